@@ -1,0 +1,261 @@
+"""Chunked gated delta rule on AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libgdr.so`` (the C ABI in ``include/gdr.h``).  It
+only marshals arguments: PyTorch provides device memory and the current HIP
+stream, every step of the operator runs in the library's HIP kernels.  There
+is no fallback: if the library is missing or the tensors are not on the GPU
+the calls raise.
+
+    o, ht = chunk_fwd(q, k, v, g, beta, scale=1.0, chunk_size=64,
+                      cu_seqlens=None, initial_state=None,
+                      output_final_state=True, use_qk_l2norm_in_kernel=False)
+
+Shapes follow the library: q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV] (or
+[B,T,HV,K] for a per-channel gate) and beta [B,T,HV] in float32; initial_state
+[N,HV,K,V] float32; cu_seqlens int32 [N+1] (then B == 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "gdr.h")
+
+GDR_BF16, GDR_FP32 = 0, 1
+STATUS = {
+    0: "GDR_OK", 1: "GDR_ERR_NULL_ARG", 2: "GDR_ERR_CHUNK_SIZE", 3: "GDR_ERR_SHAPE",
+    4: "GDR_ERR_VARLEN", 5: "GDR_ERR_DTYPE", 6: "GDR_ERR_ALIGNMENT", 7: "GDR_ERR_WORKSPACE",
+    8: "GDR_ERR_HIP", 9: "GDR_ERR_CU_SEQLENS",
+}
+
+
+class GdrProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("HV", ctypes.c_int64), ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("chunk_size", ctypes.c_int32),
+                ("gate_per_channel", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class GdrFwdLayout(ctypes.Structure):
+    _fields_ = [("nt_max", ctypes.c_int64), ("chunk_idx", ctypes.c_size_t),
+                ("chunk_off", ctypes.c_size_t), ("Tm", ctypes.c_size_t), ("w", ctypes.c_size_t),
+                ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdr.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with chunked_gated_delta_06_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        PP = ctypes.POINTER(GdrProblem)
+        L.gdr_abi_version.restype = ctypes.c_int
+        L.gdr_status_string.restype = ctypes.c_char_p
+        L.gdr_status_string.argtypes = [ctypes.c_int]
+        L.gdr_check_problem.argtypes = [PP]
+        L.gdr_validate_cu_seqlens.argtypes = [_P, ctypes.c_int64, ctypes.c_int64]
+        L.gdr_fwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.gdr_fwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrFwdLayout)]
+        L.gdr_chunk_fwd.argtypes = [PP] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
+        L.gdr_chunk_table.argtypes = [PP, _P, _P, _P, _P]
+        L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 6 + [_P]
+        L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
+        L.gdr_fwd_h.argtypes = [PP] + [_P] * 10 + [_P]
+        L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
+        for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
+                     "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
+                     "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _raise(st: int):
+    if st == 0:
+        return
+    msg = lib().gdr_status_string(st).decode()
+    if st == 8:
+        raise GdrError(st, f"{STATUS.get(st, st)}: {msg}")
+    raise ValueError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return GDR_BF16
+    if dt == torch.float32:
+        return GDR_FP32
+    return 99      # rejected by the library with GDR_ERR_DTYPE
+
+
+def make_problem(q, v, g, *, chunk_size=64, cu_seqlens=None, use_qk_l2norm=False, scale=1.0,
+                 N: Optional[int] = None) -> GdrProblem:
+    """Problem description from tensor shapes (no checks beyond the shapes)."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if N is None:
+        N = (len(cu_seqlens) - 1) if cu_seqlens is not None else B
+    return GdrProblem(B=B, T=T, H=H, HV=HV, K=K, V=V, N=N, chunk_size=int(chunk_size),
+                      gate_per_channel=int(g.dim() == 4), use_qk_l2norm=int(bool(use_qk_l2norm)),
+                      dtype=_dtype_code(q.dtype), scale=float(scale))
+
+
+def check_problem(p: GdrProblem) -> None:
+    _raise(lib().gdr_check_problem(ctypes.byref(p)))
+
+
+def fwd_layout(p: GdrProblem) -> GdrFwdLayout:
+    lay = GdrFwdLayout()
+    _raise(lib().gdr_fwd_workspace_layout(ctypes.byref(p), ctypes.byref(lay)))
+    return lay
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("gdr tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("gdr tensors must be contiguous")
+
+
+def _expect(name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def check_tensors(p: GdrProblem, q, k, v, g, beta, cu_seqlens=None, h0=None, validate_cu=True):
+    """Host-side marshalling checks: every tensor has the shape the problem
+    implies, and (optionally) cu_seqlens holds a valid table."""
+    B, T, H, HV, K, V, N = p.B, p.T, p.H, p.HV, p.K, p.V, p.N
+    _expect("q", q, (B, T, H, K))
+    _expect("k", k, (B, T, H, K))
+    _expect("v", v, (B, T, HV, V))
+    _expect("g", g, (B, T, HV, K) if p.gate_per_channel else (B, T, HV))
+    _expect("beta", beta, (B, T, HV))
+    _expect("initial_state", h0, (N, HV, K, V))
+    if cu_seqlens is not None:
+        _expect("cu_seqlens", cu_seqlens, (N + 1,))
+        if validate_cu:
+            host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+            st = lib().gdr_validate_cu_seqlens(ctypes.c_void_p(host.data_ptr()), N, T)
+            if st != 0:
+                raise ValueError(lib().gdr_status_string(st).decode())
+
+
+def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_seqlens=None,
+              initial_state=None, output_final_state: bool = True,
+              use_qk_l2norm_in_kernel: bool = False, workspace: Optional[torch.Tensor] = None,
+              return_workspace: bool = False, out=None, validate_cu: bool = True):
+    """Forward of the chunked gated delta rule.  Returns (o, ht) (ht None when
+    not requested), plus the workspace tensor when ``return_workspace``.
+    ``out=(o, ht)`` supplies the output tensors; ``validate_cu`` checks a host
+    copy of cu_seqlens first (one small device-to-host copy)."""
+    _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+    lay = fwd_layout(p)
+    check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
+    if out is not None:
+        o, ht = out
+        _need_gpu(o, ht)
+        _expect("o", o, v.shape)
+        _expect("ht", ht, (p.N, p.HV, p.K, p.V))
+        if o.dtype != q.dtype or (ht is not None and ht.dtype != torch.float32):
+            raise ValueError("o must match q's dtype and ht must be float32")
+    else:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+        ht = (torch.empty(p.N, p.HV, p.K, p.V, dtype=torch.float32, device=q.device)
+              if output_final_state else None)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gdr_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
+                             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q.device))
+    _raise(st)
+    if return_workspace:
+        return o, ht, workspace
+    return o, ht
+
+
+def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
+    """Typed views of the forward intermediates inside a workspace tensor."""
+    lay = fwd_layout(p)
+    nt, C, HV, K, V = lay.nt_max, p.chunk_size, p.HV, p.K, p.V
+    dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
+    es = 2 if p.dtype == GDR_BF16 else 4
+
+    def view(off, shape, dtype, esize):
+        n = 1
+        for s in shape:
+            n *= s
+        return ws[off:off + n * esize].view(dtype).view(*shape)
+
+    return dict(
+        chunk_idx=view(lay.chunk_idx, (nt, 4), torch.int32, 4),
+        chunk_off=view(lay.chunk_off, (p.N + 1,), torch.int32, 4),
+        Tm=view(lay.Tm, (nt, HV, C, C), dt, es),
+        w=view(lay.w, (nt, HV, C, K), dt, es),
+        u=view(lay.u, (nt, HV, V, C), dt, es),
+        h=view(lay.h, (nt, HV, V, K), dt, es),
+        v_new=view(lay.v_new, (nt, HV, V, C), dt, es),
+    )
+
+
+# ---- the forward's stages one by one (tensors allocated by the caller)
+
+def chunk_table(p: GdrProblem, cu_seqlens, chunk_idx, chunk_off):
+    _raise(lib().gdr_chunk_table(ctypes.byref(p), _ptr(cu_seqlens), _ptr(chunk_idx), _ptr(chunk_off),
+                                 _stream(chunk_off.device)))
+
+
+def fwd_kkt_solve(p, k, g, beta, chunk_idx, chunk_off, Tm):
+    _raise(lib().gdr_fwd_kkt_solve(ctypes.byref(p), _ptr(k), _ptr(g), _ptr(beta), _ptr(chunk_idx),
+                                   _ptr(chunk_off), _ptr(Tm), _stream(k.device)))
+
+
+def fwd_wy(p, k, v, g, beta, chunk_idx, chunk_off, Tm, w, u):
+    _raise(lib().gdr_fwd_wy(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(chunk_idx),
+                            _ptr(chunk_off), _ptr(Tm), _ptr(w), _ptr(u), _stream(k.device)))
+
+
+def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht):
+    _raise(lib().gdr_fwd_h(ctypes.byref(p), _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(chunk_idx),
+                           _ptr(chunk_off), _ptr(h0), _ptr(h), _ptr(v_new), _ptr(ht), _stream(k.device)))
+
+
+def fwd_o(p, q, k, v_new, h, g, chunk_idx, chunk_off, o):
+    _raise(lib().gdr_fwd_o(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g),
+                           _ptr(chunk_idx), _ptr(chunk_off), _ptr(o), _stream(q.device)))

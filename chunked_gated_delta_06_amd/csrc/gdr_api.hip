@@ -1,0 +1,286 @@
+// Host side of the C ABI declared in include/gdr.h: argument checks, the
+// workspace plan and the launch sequence of the forward stages.  Nothing here
+// allocates, frees or synchronises; every launch goes to the caller's stream.
+#include <cmath>
+#include <cstring>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+
+int64_t nt_max(const gdr_problem& p) {
+  const int64_t C = p.chunk_size;
+  if (p.T <= 0) return 0;
+  if (p.N == p.B && p.B > 1) return p.B * ((p.T + C - 1) / C);
+  // dense B = 1 and varlen use the same bound; for a single dense row it is exact
+  return (p.N == 1) ? (p.T + C - 1) / C : p.T / C + p.N;
+}
+
+}  // namespace gdr
+
+using gdr::FwdArgs;
+
+namespace {
+
+bool head_dim_ok(int64_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_size(const gdr_problem& p) { return p.dtype == GDR_BF16 ? 2 : 4; }
+
+gdr_status check(const gdr_problem* p, bool varlen) {
+  if (p == nullptr) return GDR_ERR_NULL_ARG;
+  if (p->chunk_size != 32 && p->chunk_size != 64) return GDR_ERR_CHUNK_SIZE;
+  if (p->dtype != GDR_BF16 && p->dtype != GDR_FP32) return GDR_ERR_DTYPE;
+  if (p->N < 1) return varlen ? GDR_ERR_VARLEN : GDR_ERR_SHAPE;
+  if (p->B < 1 || p->T < 0 || p->H < 1 || p->HV < 1) return GDR_ERR_SHAPE;
+  if (p->HV % p->H != 0) return GDR_ERR_SHAPE;
+  if (!head_dim_ok(p->K) || !head_dim_ok(p->V)) return GDR_ERR_SHAPE;
+  if (!std::isfinite(p->scale)) return GDR_ERR_SHAPE;
+  // fp32 with a per-channel gate at K = 256, chunk 64 does not fit one workgroup's LDS
+  if (p->dtype == GDR_FP32 && p->gate_per_channel && p->K == 256 && p->chunk_size == 64) return GDR_ERR_SHAPE;
+  // token indices are int32 in the chunk table
+  if (p->B * p->T >= (int64_t(1) << 31)) return GDR_ERR_SHAPE;
+  if (varlen) {
+    if (p->B != 1) return GDR_ERR_VARLEN;
+  } else if (p->N != p->B) {
+    return GDR_ERR_VARLEN;
+  }
+  return GDR_OK;
+}
+
+gdr::FwdArgs make_args(const gdr_problem& p) {
+  FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = p.B;
+  a.T = p.T;
+  a.H = p.H;
+  a.HV = p.HV;
+  a.K = p.K;
+  a.V = p.V;
+  a.N = p.N;
+  a.NTmax = gdr::nt_max(p);
+  a.C = p.chunk_size;
+  a.per_channel = p.gate_per_channel ? 1 : 0;
+  a.l2norm = p.use_qk_l2norm ? 1 : 0;
+  a.dtype = p.dtype;
+  a.scale = p.scale;
+  return a;
+}
+
+gdr_fwd_layout layout_of(const gdr_problem& p) {
+  gdr_fwd_layout l;
+  const int64_t nt = gdr::nt_max(p);
+  const size_t es = elem_size(p);
+  const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V;
+  size_t off = 0;
+  l.nt_max = nt;
+  l.chunk_idx = off;
+  off = round_up(off + (size_t)nt * 4 * sizeof(int32_t));
+  l.chunk_off = off;
+  off = round_up(off + ((size_t)p.N + 1) * sizeof(int32_t));
+  l.Tm = off;
+  off = round_up(off + (size_t)nt * HV * C * C * es);
+  l.w = off;
+  off = round_up(off + (size_t)nt * HV * C * K * es);
+  l.u = off;
+  off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.h = off;
+  off = round_up(off + (size_t)nt * HV * V * K * es);
+  l.v_new = off;
+  off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.total = off;
+  return l;
+}
+
+gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return 1; }
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL_ARG: return "a required pointer is NULL";
+    case GDR_ERR_CHUNK_SIZE: return "chunk_size must be either 32 or 64";
+    case GDR_ERR_SHAPE: return "unsupported shape (dims < 1, HV % H != 0, or K/V not in {32,64,128,256})";
+    case GDR_ERR_VARLEN: return "cu_seqlens requires B == 1 and N >= 1; a dense batch requires N == B";
+    case GDR_ERR_DTYPE: return "dtype must be GDR_BF16 or GDR_FP32";
+    case GDR_ERR_ALIGNMENT: return "every pointer must be 16-byte aligned";
+    case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDR_ERR_HIP: return "HIP launch failed";
+    case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
+  }
+  return "unknown status";
+}
+
+gdr_status gdr_check_problem(const gdr_problem* p) {
+  if (p == nullptr) return GDR_ERR_NULL_ARG;
+  return check(p, p->N != p->B);
+}
+
+gdr_status gdr_validate_cu_seqlens(const int32_t* cu, int64_t N, int64_t T) {
+  if (cu == nullptr) return GDR_ERR_NULL_ARG;
+  if (N < 1 || cu[0] != 0 || cu[N] != T) return GDR_ERR_CU_SEQLENS;
+  for (int64_t i = 0; i < N; ++i)
+    if (cu[i + 1] < cu[i]) return GDR_ERR_CU_SEQLENS;
+  return GDR_OK;
+}
+
+gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* out) {
+  if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
+  const gdr_status st = check(p, p->N != p->B);
+  if (st != GDR_OK) return st;
+  *out = layout_of(*p);
+  return GDR_OK;
+}
+
+gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes) {
+  gdr_fwd_layout l;
+  const gdr_status st = gdr_fwd_workspace_layout(p, &l);
+  if (st != GDR_OK) return st;
+  if (bytes == nullptr) return GDR_ERR_NULL_ARG;
+  *bytes = l.total;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check(p, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  const bool empty = p->T == 0;
+  if (!empty && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  const gdr_fwd_layout l = layout_of(*p);
+  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
+
+  FwdArgs a = make_args(*p);
+  char* ws = static_cast<char*>(workspace);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.chunk_idx);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.chunk_off);
+  a.Tm = ws + l.Tm;
+  a.w = ws + l.w;
+  a.u = ws + l.u;
+  a.h = ws + l.h;
+  a.v_new = ws + l.v_new;
+  a.o = o;
+  a.ht = ht;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_chunk_table(a, s);
+  if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+  if (e == hipSuccess) e = gdr::launch_wy(a, s);
+  if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+  if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+  return hip_status(e);
+}
+
+gdr_status gdr_chunk_table(const gdr_problem* p, const int32_t* cu_seqlens, int32_t* chunk_idx,
+                           int32_t* chunk_off, void* stream) {
+  gdr_status st = check(p, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  if (chunk_off == nullptr || (gdr::nt_max(*p) > 0 && chunk_idx == nullptr)) return GDR_ERR_NULL_ARG;
+  if (!aligned16(chunk_idx) || !aligned16(chunk_off) || !aligned16(cu_seqlens)) return GDR_ERR_ALIGNMENT;
+  FwdArgs a = make_args(*p);
+  a.cu = cu_seqlens;
+  a.chunk_idx = chunk_idx;
+  a.chunk_off = chunk_off;
+  return hip_status(gdr::launch_chunk_table(a, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+gdr_status stage_common(const gdr_problem* p, std::initializer_list<const void*> ptrs) {
+  gdr_status st = check(p, p ? p->N != p->B : false);
+  if (st != GDR_OK) return st;
+  for (const void* ptr : ptrs) {
+    if (ptr == nullptr) return GDR_ERR_NULL_ARG;
+    if (!aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  }
+  return GDR_OK;
+}
+}  // namespace
+
+gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g, const float* beta,
+                             const int32_t* chunk_idx, const int32_t* chunk_off, void* Tm, void* stream) {
+  gdr_status st = stage_common(p, {k, g, beta, chunk_idx, chunk_off, Tm});
+  if (st != GDR_OK) return st;
+  FwdArgs a = make_args(*p);
+  a.k = k;
+  a.g = g;
+  a.beta = beta;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.Tm = Tm;
+  return hip_status(gdr::launch_kkt_solve(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const float* g, const float* beta,
+                      const int32_t* chunk_idx, const int32_t* chunk_off, const void* Tm, void* w, void* u,
+                      void* stream) {
+  gdr_status st = stage_common(p, {k, v, g, beta, chunk_idx, chunk_off, Tm, w, u});
+  if (st != GDR_OK) return st;
+  FwdArgs a = make_args(*p);
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.Tm = const_cast<void*>(Tm);
+  a.w = w;
+  a.u = u;
+  return hip_status(gdr::launch_wy(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u, const float* g,
+                     const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0, void* h, void* v_new,
+                     float* ht, void* stream) {
+  gdr_status st = stage_common(p, {k, w, u, g, chunk_idx, chunk_off, h, v_new});
+  if (st != GDR_OK) return st;
+  if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_ERR_ALIGNMENT;
+  FwdArgs a = make_args(*p);
+  a.k = k;
+  a.w = const_cast<void*>(w);
+  a.u = const_cast<void*>(u);
+  a.g = g;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.h0 = h0;
+  a.h = h;
+  a.v_new = v_new;
+  a.ht = ht;
+  return hip_status(gdr::launch_fwd_h(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,
+                     const float* g, const int32_t* chunk_idx, const int32_t* chunk_off, void* o, void* stream) {
+  gdr_status st = stage_common(p, {q, k, v_new, h, g, chunk_idx, chunk_off, o});
+  if (st != GDR_OK) return st;
+  FwdArgs a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.v_new = const_cast<void*>(v_new);
+  a.h = const_cast<void*>(h);
+  a.g = g;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.o = o;
+  return hip_status(gdr::launch_fwd_o(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// K2: WY recompute.
+//
+// For one chunk and value head, from Tm = (I + A)^-1 (K1):
+//   w = Tm (beta * exp(G) * k^)      u = Tm (beta * v)
+// the WY factors of the DeltaNet chunk form P^r = I - sum_i k^i w^i^T on the
+// coverage-matrix page ("FLA operator-kernel correctness testing and coverage
+// matrix", section 2), with the gate folded into w.
+//
+// gfx950 mapping (4 waves per chunk and value head):
+//  * the k and v tiles are staged token-major in LDS with coalesced 16-byte
+//    loads and read back transposed with ds_read_b64_tr_b16, so both products
+//    contract over tokens on bf16 MFMA without a transposing copy;
+//  * w is computed as w^T = k^T (Tm diag(s))^T, so each lane ends with four
+//    consecutive features of one token (an 8-byte token-major store), and u as
+//    Tm diag(beta) v, so each lane ends with four consecutive tokens of one
+//    value column (an 8-byte store into the per-chunk transposed u);
+//  * with a scalar gate the per-token factor s_t = beta_t exp(G_t) / |k_t|
+//    multiplies the columns of Tm, leaving the raw keys exact; a per-channel
+//    gate multiplies the key tile element-wise by exp(G_td) <= 1;
+//  * blocks above the diagonal of Tm are skipped (Tm is lower triangular).
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+template <typename T, int C, int K, bool PC>
+__global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int NB = C / 16;
+  constexpr int KSC = C / 32;                       // token slabs
+  constexpr int PADE = 16 / sizeof(T) * 1;          // 16 bytes of row padding
+  constexpr int KP = K + PADE;
+  constexpr int VT = sizeof(T) == 2 ? 128 : 64;     // value columns staged per pass
+  constexpr int VP = VT + PADE;
+  constexpr int GP = K + 1;
+  constexpr int CPR = K / 8;                        // 8-element chunks per key row
+  __shared__ __attribute__((aligned(16))) T sK[C * KP];
+  __shared__ __attribute__((aligned(16))) T sV[C * VP];
+  __shared__ float sS[C], sB[C], sRn[C];
+  __shared__ float sGc[PC ? C * GP : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int64_t c = blockIdx.x, j = blockIdx.y;
+  if (c >= a.chunk_off[a.N]) return;
+  const int64_t t0 = a.chunk_idx[4 * c + 1];
+  const int L = a.chunk_idx[4 * c + 2];
+  const int64_t H = a.H, HV = a.HV, V = a.V, h = j / (HV / H);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ vp = static_cast<const T*>(a.v);
+  const T* __restrict__ Tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
+  T* __restrict__ wp = static_cast<T*>(a.w) + (c * HV + j) * (int64_t)(C * K);
+  T* __restrict__ up = static_cast<T*>(a.u) + (c * HV + j) * (int64_t)C * V;
+
+  if constexpr (PC) {
+    for (int idx = tid; idx < C * K; idx += 256) {
+      const int t = idx / K, d = idx % K;
+      sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
+    }
+    __syncthreads();
+    for (int d = tid; d < K; d += 256) {
+      float run = 0.f;
+      for (int t = 0; t < C; ++t) {
+        run += sGc[t * GP + d];
+        sGc[t * GP + d] = run;
+      }
+    }
+    __syncthreads();
+  }
+
+  // key tile (token-major), row norms of the raw keys
+  for (int idx = tid; idx < C * CPR; idx += 256) {
+    const int t = idx / CPR, d8 = (idx % CPR) * 8;
+    Frag<T> f = (t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+    f32x8 x = f.f32();
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+    sq = lanes_sum(sq, CPR);
+    if (idx % CPR == 0) sRn[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+    if constexpr (PC) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[t * GP + d8 + e]);
+      f = Frag<T>::make(x);
+    }
+    st8(&sK[t * KP + d8], f);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    float gv = 0.f, bv = 0.f;
+    if (lane < L) {
+      if (!PC) gv = a.g[(t0 + lane) * HV + j];
+      bv = a.beta[(t0 + lane) * HV + j];
+    }
+    const float G = PC ? 0.f : wave_incl_scan(gv, lane);
+    if (lane < C) {
+      sB[lane] = bv;
+      sS[lane] = bv * sRn[lane] * (PC ? 1.f : __expf(G));
+    }
+  }
+  __syncthreads();
+
+  // rows of Tm this lane feeds: row 16 rb + r16, tokens 32 ks + 8 g4 + e
+  Frag<T> tf[NB][KSC];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks)
+      tf[rb][ks] = (2 * ks <= rb) ? ld8(Tp + (16 * rb + r16) * C + 32 * ks + 8 * g4) : frag_zero<T>();
+
+  // w^T = k^T (Tm diag(s))^T
+  for (int fb = wv; fb < K / 16; fb += NW) {
+#pragma unroll
+    for (int rb = 0; rb < NB; ++rb) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        if (2 * ks > rb) continue;
+        const Frag<T> ka = lds_tr_frag(sK, KP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * fb, lane);
+        f32x8 sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = sS[32 * ks + 8 * g4 + e];
+        mma(acc, ka, Frag<T>::make(tf[rb][ks].f32() * sc));
+      }
+      st4(wp + (16 * rb + r16) * K + 16 * fb + 4 * g4, acc);
+    }
+  }
+
+  // u = Tm diag(beta) v, value columns staged VT at a time
+  for (int64_t v0 = 0; v0 < V; v0 += VT) {
+    const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
+    const int vpr = nv / 8;
+    __syncthreads();
+    for (int idx = tid; idx < C * vpr; idx += 256) {
+      const int t = idx / vpr, d8 = (idx % vpr) * 8;
+      const Frag<T> f = (t < L) ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + d8) : frag_zero<T>();
+      st8(&sV[t * VP + d8], f);
+    }
+    __syncthreads();
+    for (int vb = wv; vb < nv / 16; vb += NW) {
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) {
+          if (2 * ks > rb) continue;
+          f32x8 sc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = sB[32 * ks + 8 * g4 + e];
+          const Frag<T> vbf = lds_tr_frag(sV, VP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * vb, lane);
+          mma(acc, Frag<T>::make(tf[rb][ks].f32() * sc), vbf);
+        }
+        st4(up + (v0 + 16 * vb + r16) * C + 16 * rb + 4 * g4, acc);
+      }
+    }
+  }
+}
+
+template <typename T, int C, int K, bool PC>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k2_wy<T, C, K, PC>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int C, bool PC>
+hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+  switch (a.K) {
+    case 32: return launch_t<T, C, 32, PC>(a, s);
+    case 64: return launch_t<T, C, 64, PC>(a, s);
+    case 128: return launch_t<T, C, 128, PC>(a, s);
+    case 256: return launch_t<T, C, 256, PC>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+  if (a.C == 32) return a.per_channel ? launch_k<T, 32, true>(a, s) : launch_k<T, 32, false>(a, s);
+  return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_wy(const FwdArgs& a, hipStream_t s) {
+  if (a.NTmax == 0) return hipSuccess;
+  return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+}  // namespace gdr

@@ -1,0 +1,236 @@
+// K4: chunk output (chunk_fwd_o).
+//
+// For one chunk (L rows) and value head j, with h the state entering the chunk
+// (K3) and e its corrected values:
+//   o_r = scale * [ (exp(G_r) q^_r)^T h + sum_{t<=r} (sum_d q^_rd k^_td exp(G_rd - G_td)) e_t ]
+// i.e. O = scale (diag(exp(G)) Q h + (Q K^T o M) E), the output of the chunk
+// form on the coverage-matrix page ("FLA operator-kernel correctness testing
+// and coverage matrix", section 2) with the decay mask M folded in.
+//
+// gfx950 mapping: one workgroup per (chunk, value head), wave w owns output
+// rows 16 w .. 16 w + 15 and all value columns.  The wave computes P^T blocks
+// (K Q^T, causal blocks only) on bf16 MFMA from the raw q / k rows, scales
+// them in fp32 (norms, gate, causal mask) and feeds the accumulators straight
+// in as the B operand of O^T += e^T P^T ("chained" contraction map); the inter
+// part O^T = h^T Q^T reads h^T and the per-chunk transposed e with plain
+// 16-byte / 8-byte loads.  Producing O^T leaves each lane four consecutive
+// value columns of one token, so o is written with 8-byte stores.  A
+// per-channel gate uses a reference row per block so that every exponential
+// factor stays <= 1 (diagonal blocks: the middle row, with a per-element
+// fallback when the block's gate span is too wide).
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr float kSpanLimit = 80.f;
+
+template <typename T, int C, int K, bool PC>
+__global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
+  constexpr int NB = C / 16;
+  constexpr int KSK = K / 32;
+  constexpr int KSC = C / 32;
+  constexpr int GP = K + 1;
+  __shared__ float sG[C], sRq[C], sRk[C];
+  __shared__ float sGc[PC ? C * GP : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int64_t c = blockIdx.x, j = blockIdx.y;
+  if (c >= a.chunk_off[a.N]) return;
+  const int64_t t0 = a.chunk_idx[4 * c + 1];
+  const int L = a.chunk_idx[4 * c + 2];
+  const int64_t H = a.H, HV = a.HV, V = a.V, h = j / (HV / H);
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ hp = static_cast<const T*>(a.h) + (c * HV + j) * V * (int64_t)K;
+  const T* __restrict__ ep = static_cast<const T*>(a.v_new) + (c * HV + j) * V * (int64_t)C;
+  T* __restrict__ op = static_cast<T*>(a.o);
+
+  auto row8 = [&](const T* base, int row, int ks) -> Frag<T> {
+    if (row < L) return ld8(base + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
+    return frag_zero<T>();
+  };
+
+  // ---- gates, norms
+  if constexpr (PC) {
+    for (int idx = tid; idx < C * K; idx += 64 * NB) {
+      const int t = idx / K, d = idx % K;
+      sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
+    }
+    __syncthreads();
+    for (int d = tid; d < K; d += 64 * NB) {
+      float run = 0.f;
+      for (int t = 0; t < C; ++t) {
+        run += sGc[t * GP + d];
+        sGc[t * GP + d] = run;
+      }
+    }
+  } else {
+    if (wv == 0) {
+      const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+      const float G = wave_incl_scan(gv, lane);
+      if (lane < C) sG[lane] = G;
+    }
+  }
+  const int rr = 16 * wv + r16;               // this lane's output row
+  Frag<T> qf[KSK];
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KSK; ++ks) {
+    qf[ks] = row8(qp, rr, ks);
+    const f32x8 xq = qf[ks].f32(), xk = row8(kp, rr, ks).f32();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq += xq[e] * xq[e];
+      sk += xk[e] * xk[e];
+    }
+  }
+  sq = group4_sum(sq);
+  sk = group4_sum(sk);
+  if (g4 == 0) {
+    sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+    sRk[rr] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+  }
+  __syncthreads();
+
+  // ---- P^T blocks (t-block jb, r-block wv), jb <= wv
+  const float rq = sRq[rr];
+  f32x4 Pt[NB];
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) {
+    Pt[jb] = zero4();
+    if (jb > wv) continue;
+    if constexpr (!PC) {
+#pragma unroll
+      for (int ks = 0; ks < KSK; ++ks) mma(Pt[jb], row8(kp, 16 * jb + r16, ks), qf[ks]);
+    } else {
+      bool direct = false;
+      int m = 16 * jb + 15;
+      if (jb == wv) {
+        m = 16 * jb + 8;
+        float span = 0.f;
+        for (int d = lane; d < K; d += 64)
+          span = fmaxf(span, sGc[(16 * jb) * GP + d] - sGc[(16 * jb + 15) * GP + d]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+        direct = span > kSpanLimit;
+      }
+      if (!direct) {
+        const int tk = 16 * jb + r16;
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks) {
+          f32x8 xa = row8(kp, tk, ks).f32(), xb = qf[ks].f32();
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = 32 * ks + 8 * g4 + e;
+            const float gm = sGc[m * GP + d];
+            xa[e] *= __expf(gm - sGc[tk * GP + d]);
+            xb[e] *= __expf(sGc[rr * GP + d] - gm);
+          }
+          mma_split(Pt[jb], SplitFrag<T>::make(xa), SplitFrag<T>::make(xb));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * jb + 4 * g4 + i;
+          float s = 0.f;
+          if (t <= rr && rr < L) {
+            for (int d = 0; d < K; ++d)
+              s += to_float(kp[((t0 + t) * H + h) * K + d]) * to_float(qp[((t0 + rr) * H + h) * K + d]) *
+                   __expf(sGc[rr * GP + d] - sGc[t * GP + d]);
+          }
+          Pt[jb][i] = s;
+        }
+      }
+    }
+    // scale and mask: P^T[t][rr], t = 16 jb + 4 g4 + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * jb + 4 * g4 + i;
+      float f = 0.f;
+      if (t <= rr && rr < L) {
+        f = rq * sRk[t];
+        if (!PC) f *= __expf(sG[rr] - sG[t]);
+      }
+      Pt[jb][i] *= f;
+    }
+  }
+  // P^T as the B operand of the intra product, kept as a bf16 hi + lo pair
+  SplitFrag<T> Pf[KSC];
+#pragma unroll
+  for (int kt = 0; kt < KSC; ++kt) Pf[kt] = SplitFrag<T>::make(cat8(Pt[2 * kt], Pt[2 * kt + 1]));
+
+  // q rows for the inter part: raw q (scalar gate, exact) or exp(G_r) q_r
+  // (per-channel gate, as a hi + lo pair)
+  SplitFrag<T> qi[KSK];
+#pragma unroll
+  for (int ks = 0; ks < KSK; ++ks) {
+    f32x8 x = qf[ks].f32();
+    if constexpr (PC) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[rr * GP + 32 * ks + 8 * g4 + e]);
+      qi[ks] = SplitFrag<T>::make(x);
+    } else {
+      qi[ks].hi = qf[ks];
+      qi[ks].lo = frag_zero<T>();
+    }
+  }
+  const float inter_scale = rq * (PC ? 1.f : __expf(sG[rr]));
+  const float sc = a.scale;
+
+  // ---- O^T = h^T Q^T (scaled) + e^T P^T, 16 value columns at a time
+  for (int64_t vb = 0; vb < V / 16; ++vb) {
+    f32x4 acc = zero4();
+    const T* hrow = hp + (16 * vb + r16) * (int64_t)K;
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) {
+      if constexpr (PC) {
+        mma_split(acc, ld8(hrow + 32 * ks + 8 * g4), qi[ks]);
+      } else {
+        mma(acc, ld8(hrow + 32 * ks + 8 * g4), qi[ks].hi);
+      }
+    }
+    acc *= inter_scale;
+    const T* erow = ep + (16 * vb + r16) * (int64_t)C;
+#pragma unroll
+    for (int kt = 0; kt < KSC; ++kt) {
+      if (2 * kt > wv) continue;
+      mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), Pf[kt]);
+    }
+    if (rr < L) st4(op + ((t0 + rr) * HV + j) * V + 16 * vb + 4 * g4, acc * sc);
+  }
+}
+
+template <typename T, int C, int K, bool PC>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k4_fwd_o<T, C, K, PC>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(C * 4), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int C, bool PC>
+hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+  switch (a.K) {
+    case 32: return launch_t<T, C, 32, PC>(a, s);
+    case 64: return launch_t<T, C, 64, PC>(a, s);
+    case 128: return launch_t<T, C, 128, PC>(a, s);
+    case 256: return launch_t<T, C, 256, PC>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+  if (a.C == 32) return a.per_channel ? launch_k<T, 32, true>(a, s) : launch_k<T, 32, false>(a, s);
+  return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_o(const FwdArgs& a, hipStream_t s) {
+  if (a.NTmax == 0) return hipSuccess;
+  return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+}  // namespace gdr

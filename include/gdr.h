@@ -1,0 +1,162 @@
+/*
+ * gdr.h -- C ABI of the chunked gated delta-rule operator on AMD MI355X (gfx950).
+ *
+ * The operator (pages: "FLA operator-kernel correctness testing and coverage
+ * matrix", section 2 and section 3; "flash-linear-attention KCP precision-failure
+ * root-cause manual", section "h and dh cross-rank semantics"):
+ *
+ *   for every sequence n, value head j (q/k head h = j / (HV / H)), token t:
+ *     S' = D_t S            D_t = diag(exp(g[t, j]))  (scalar or per-channel gate)
+ *     e  = beta[t, j] * (v[t, j] - S'^T k^[t, h])
+ *     S  = S' + k^[t, h] e^T                                  (S is K x V)
+ *     o[t, j] = scale * S^T q^[t, h]
+ *   starting from h0[n, j] (or zeros) and ending in ht[n, j], where q^, k^ are
+ *   q, k divided by sqrt(sum(x^2) + 1e-6) when use_qk_l2norm is set.  It is
+ *   evaluated chunk by chunk (chunk_size 32 or 64) through the WY form
+ *   S^r = P^r S^0 + H^r of the coverage-matrix page (section 2).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are device memory owned by the caller; the library
+ *     never allocates, frees or synchronises.  Every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL = the null stream).
+ *   - Tensors are dense and row-major with the shapes given below; every
+ *     pointer must be 16-byte aligned.
+ *   - "dtype" tensors (q, k, v, o and the intermediates) are bf16 when
+ *     problem->dtype == GDR_BF16 and float32 when GDR_FP32; g, beta, h0, ht
+ *     are always float32.
+ *   - Arguments are checked on the host before any launch; a failed check
+ *     returns an error code and writes nothing.  A launch failure returns
+ *     GDR_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ *   - cu_seqlens contents (cu[0] = 0, non-decreasing, cu[N] = T) are a
+ *     precondition; gdr_validate_cu_seqlens checks a host copy.
+ *   - Every output element is written (outputs may hold garbage on entry).
+ *   - Calls that share a workspace or an output must not overlap in time.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+  GDR_ERR_CHUNK_SIZE = 2,  /* "chunk_size must be either 32 or 64" */
+  GDR_ERR_SHAPE = 3,       /* a dim < 1 (T < 0), HV % H != 0, K or V not in {32,64,128,256},
+                              B*T >= 2^31, or fp32 + per-channel gate + K = 256 + chunk 64 */
+  GDR_ERR_VARLEN = 4,      /* cu_seqlens with B != 1, N < 1, or N != B for a dense batch */
+  GDR_ERR_DTYPE = 5,       /* dtype not GDR_BF16 / GDR_FP32 */
+  GDR_ERR_ALIGNMENT = 6,   /* a pointer not 16-byte aligned */
+  GDR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than *_workspace_bytes */
+  GDR_ERR_HIP = 8,         /* a kernel launch failed */
+  GDR_ERR_CU_SEQLENS = 9   /* gdr_validate_cu_seqlens: bad table */
+} gdr_status;
+
+typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
+
+/* Problem description.  Dense batch: cu_seqlens = NULL, N = B, every row is one
+ * sequence of T tokens.  Varlen batch: B = 1, T = total tokens, N = number of
+ * sequences, sequence n spans tokens [cu_seqlens[n], cu_seqlens[n+1]). */
+typedef struct {
+  int64_t B, T, H, HV, K, V, N;
+  int32_t chunk_size;        /* 32 | 64 */
+  int32_t gate_per_channel;  /* 0: g is [B,T,HV]; 1: g is [B,T,HV,K] */
+  int32_t use_qk_l2norm;     /* 1: normalise q, k rows in the kernels */
+  int32_t dtype;             /* gdr_dtype */
+  float scale;               /* output scale */
+} gdr_problem;
+
+/* Offsets (bytes from the workspace base) of the forward intermediates that
+ * gdr_chunk_fwd keeps in its workspace; NT_max = B * ceil(T / C) for a dense
+ * batch and floor(T / C) + N for a varlen batch.
+ *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
+ *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
+ *   Tm         dtype [NT_max][HV][C][C]   (I + A)^-1 of each chunk, row-major
+ *   w          dtype [NT_max][HV][C][K]   WY keys, token-major
+ *   u          dtype [NT_max][HV][V][C]   WY values, transposed per chunk
+ *   h          dtype [NT_max][HV][V][K]   state entering each chunk, transposed (h^T)
+ *   v_new      dtype [NT_max][HV][V][C]   corrected values e, transposed per chunk
+ * Rows past the end of a partial chunk hold zeros. */
+typedef struct {
+  int64_t nt_max;
+  size_t chunk_idx, chunk_off, Tm, w, u, h, v_new, total;
+} gdr_fwd_layout;
+
+/* ABI version of this header (bumped on incompatible changes). */
+int gdr_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* gdr_status_string(gdr_status s);
+
+/* Host-side check of a problem description (no device access). */
+gdr_status gdr_check_problem(const gdr_problem* p);
+
+/* Check a host copy of cu_seqlens ([N+1] int32): cu[0] = 0, non-decreasing,
+ * cu[N] = T.  Returns GDR_OK or GDR_ERR_CU_SEQLENS (GDR_ERR_NULL_ARG if NULL). */
+gdr_status gdr_validate_cu_seqlens(const int32_t* cu_host, int64_t N, int64_t T);
+
+/* Workspace needed by gdr_chunk_fwd (bytes), and where each intermediate sits. */
+gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
+gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
+
+/* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
+ * K3 state scan -> K4 output, all on `stream`.
+ *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
+ *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
+ *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
+ *   h0    f32 [N,HV,K,V] or NULL (zeros)
+ *   o     dtype [B,T,HV,V] (output)
+ *   ht    f32 [N,HV,K,V] (output) or NULL (final state not wanted)
+ *   workspace  >= gdr_fwd_workspace_bytes bytes of device memory (contents on
+ *              entry are irrelevant; on return they hold the intermediates
+ *              listed in gdr_fwd_layout). */
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const int32_t* cu_seqlens,
+                         const float* h0, void* o, float* ht, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ---- the forward's stages, callable one by one (same layouts as above) ---- */
+
+/* K0: chunk table.  Chunks restart at every sequence start and the last chunk of
+ * a sequence may be partial (KCP page, section "why per-chunk comparison lies
+ * under varlen KCP").  Writes chunk_idx [NT_max][4] and chunk_off [N+1]; table
+ * rows past NT are left untouched. */
+gdr_status gdr_chunk_table(const gdr_problem* p, const int32_t* cu_seqlens, int32_t* chunk_idx,
+                           int32_t* chunk_off, void* stream);
+
+/* K1: per chunk and value head, G = chunk-local cumsum of g,
+ * A[r][j] = beta_r * sum_d k^_rd k^_jd exp(G_rd - G_jd) for j < r, and
+ * Tm = (I + A)^-1 (unit lower triangular; upper triangle and rows >= L are 0). */
+gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g,
+                             const float* beta, const int32_t* chunk_idx,
+                             const int32_t* chunk_off, void* Tm, void* stream);
+
+/* K2: WY recompute, w = Tm (beta exp(G) k^), u = Tm (beta v) per chunk and value head
+ * (coverage-matrix page, section 2: P^r = I - sum k^i w^i^T). */
+gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const float* g,
+                      const float* beta, const int32_t* chunk_idx, const int32_t* chunk_off,
+                      const void* Tm, void* w, void* u, void* stream);
+
+/* K3: state scan.  For each sequence, value head and chunk in order: h = S (the
+ * state entering the chunk, as on the KCP page, section "h and dh cross-rank
+ * semantics"), e = u - w S -> v_new, then
+ * S <- diag(exp(G_L)) S + sum_j (exp(G_L - G_j) k^_j) e_j^T.  S starts at h0 (or 0)
+ * and is written to ht after the last chunk (if ht != NULL). */
+gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u,
+                     const float* g, const int32_t* chunk_idx, const int32_t* chunk_off,
+                     const float* h0, void* h, void* v_new, float* ht, void* stream);
+
+/* K4: output, o_r = scale * [ (exp(G_r) q^_r)^T h + sum_{j<=r} (q^_r . exp(G_r - G_j) k^_j) e_j ]. */
+gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new,
+                     const void* h, const float* g, const int32_t* chunk_idx,
+                     const int32_t* chunk_off, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

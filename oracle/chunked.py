@@ -80,8 +80,9 @@ def forward_substitution(A: np.ndarray) -> np.ndarray:
     for r in range(L):
         row = np.zeros(A.shape[:-2] + (L,))
         row[..., r] = 1.0
-        for j in range(r):
-            row = row - A[..., r, j, None] * Tm[..., j, :]
+        if r:
+            # sum_{j<r} A[r, j] T[j] as one (batched) vector-matrix product
+            row = row - (A[..., r:r + 1, :r] @ Tm[..., :r, :])[..., 0, :]
         Tm[..., r, :] = row
     return Tm
 
@@ -113,8 +114,8 @@ def _chunk(qc, kc, vc, Gc, bc, S0, scale, per_channel):
         diff = Gh[:, :, None] - Gh[:, None, :]
         low = np.tril(np.ones((L, L)))[None] > 0
         dec = np.where(low, np.exp(np.where(low, diff, 0.0)), 0.0)
-        kk = np.einsum("hrd,hjd->hrj", kh, kh) * dec
-        qk = np.einsum("hrd,hjd->hrj", qh, kh) * dec
+        kk = (kh @ np.transpose(kh, (0, 2, 1))) * dec
+        qk = (qh @ np.transpose(kh, (0, 2, 1))) * dec
         gam = np.exp(Gh)[:, :, None]
         kg_in = gam * kh
         q_in = gam * qh

@@ -1,0 +1,360 @@
+"""GPU parity of the forward path (K0..K4) against the float64 oracle.
+
+Tolerances: err_ratio = RMS(diff) / RMS(ref) <= 1e-4 for float32 and <= 5e-3
+for bf16 on o, ht and the intermediates (the bf16 bound is the chunked-vs-
+per-token noise level the KCP page's acceptance section names); integer chunk
+tables are compared exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_06_amd as gdr
+import workloads
+from oracle import chunked, recurrent
+from oracle.metrics import err_ratio
+from fwd_helpers import TOL, check, dev, f64, gpu_fwd, oracle_fwd, slice_inputs
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+
+
+def mk(name="t", B=2, T=200, H=2, HV=4, K=64, V=64, C=64, dtype="bf16", pc=False, l2=True, h0=True,
+       slow=False, lengths=None, scale=1.0, seed=7, host_l2=False):
+    w = W(name, B=B, T=T, H=H, HV=HV, K=K, V=V, chunk_size=C, dtype=dtype, per_channel_gate=pc,
+          l2norm_in_kernel=l2, host_l2norm=host_l2, h0=h0, slow_decay=slow, scale=scale)
+    return w, workloads.make_inputs(w, seed=seed, lengths=lengths)
+
+
+# ------------------------------------------------------------------ K0
+
+@pytest.mark.parametrize("case", ["dense", "page_example", "empty_seqs", "many_seqs", "config3"])
+@pytest.mark.parametrize("C", [32, 64])
+def test_chunk_table_bit_exact(case, C):
+    rng = np.random.default_rng(0)
+    if case == "dense":
+        B, T, cu = 3, 100, None
+    else:
+        if case == "page_example":
+            lengths = [400, 624]
+        elif case == "empty_seqs":
+            lengths = [0, 5, 0, 70, 64, 1, 0]
+        elif case == "many_seqs":
+            lengths = list(rng.integers(0, 200, size=3000))
+        else:
+            g = torch.Generator().manual_seed(workloads.SEED)
+            lengths = workloads.draw_lengths(g, 24, 64, 2048)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        B, T = 1, int(cu[-1])
+    N = B if cu is None else len(cu) - 1
+    p = gdr.GdrProblem(B=B, T=T, H=1, HV=1, K=32, V=32, N=N, chunk_size=C, gate_per_channel=0,
+                       use_qk_l2norm=0, dtype=0, scale=1.0)
+    nt = gdr.fwd_layout(p).nt_max
+    idx = torch.full((nt + 1, 4), -7, dtype=torch.int32, device="cuda")    # one canary row
+    off = torch.full((N + 1,), -7, dtype=torch.int32, device="cuda")
+    gdr.chunk_table(p, dev(torch.from_numpy(cu)) if cu is not None else None, idx, off)
+    torch.cuda.synchronize()
+    ref_idx, ref_off = chunked.chunk_table(B, T, cu, C)
+    off_h = off.cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    assert np.array_equal(off_h, ref_off)
+    NT = int(ref_off[-1])
+    assert np.array_equal(idx_h[:NT, :3], ref_idx)
+    # chunk number inside the sequence
+    assert np.array_equal(idx_h[:NT, 3], np.concatenate([np.arange(ref_off[n + 1] - ref_off[n])
+                                                         for n in range(N)]).astype(np.int32)
+                          if NT else np.zeros(0, np.int32))
+    assert (idx_h[nt] == -7).all()
+    assert nt >= NT
+
+
+# ------------------------------------------------------------------ stages
+
+STAGE_CASES = [
+    dict(dtype="fp32", K=32, V=32, C=64),
+    dict(dtype="fp32", K=64, V=128, C=32, pc=True),
+    dict(dtype="bf16", K=128, V=128, C=64),
+    dict(dtype="bf16", K=128, V=256, C=32, pc=True, l2=False, host_l2=True),
+    dict(dtype="bf16", K=64, V=32, C=64, H=1, HV=4),
+]
+
+
+@pytest.mark.parametrize("cfg", STAGE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_stage_intermediates(cfg):
+    """K1 (Tm), K2 (w, u), K3 (h, v_new, ht) and K4 (o) each against the
+    oracle's per-chunk quantities, on a ragged dense batch with slow decay."""
+    w, inp = mk(T=150, slow=True, **cfg)
+    tol = TOL[w.dtype]
+    o, ht, ws = gpu_fwd(inp)
+    ro, rht, it = oracle_fwd(inp, intermediates=True)
+    NT = int(it["off"][-1])
+    assert np.array_equal(ws["chunk_idx"][:NT, :3].cpu().numpy(), it["idx"])
+    check("Tm", f64(ws["Tm"][:NT]), it["T"], tol)
+    check("w", f64(ws["w"][:NT]), it["W"], tol)
+    check("u", f64(ws["u"][:NT]).transpose(0, 1, 3, 2), it["U"], tol)
+    check("h", f64(ws["h"][:NT]).transpose(0, 1, 3, 2), it["h"], tol)
+    check("v_new", f64(ws["v_new"][:NT]).transpose(0, 1, 3, 2), it["E"], tol)
+    check("o", f64(o), ro, tol)
+    check("ht", f64(ht), rht, tol)
+
+
+# ------------------------------------------------------------------ sweep
+
+SWEEP = []
+for dtype in ("bf16", "fp32"):
+    for C in (32, 64):
+        for (K, V) in ((32, 64), (64, 64), (128, 128), (256, 64), (64, 256)):
+            for pc in (False, True):
+                if dtype == "fp32" and pc and K == 256 and C == 64:
+                    continue
+                SWEEP.append(dict(dtype=dtype, C=C, K=K, V=V, pc=pc))
+
+
+@pytest.mark.parametrize("cfg", SWEEP, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_forward_sweep(cfg):
+    """Dense GVA batch with a ragged tail, in-kernel L2 norm, h0, slow decay."""
+    w, inp = mk(B=2, T=137, H=2, HV=4, slow=True, scale=0.75, **cfg)
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[w.dtype])
+    check("ht", f64(ht), rht, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("pc", [False, True])
+@pytest.mark.parametrize("l2", [False, True])
+def test_forward_varlen(dtype, pc, l2):
+    lengths = [1, 63, 64, 65, 0, 130, 7, 200]
+    w, inp = mk(B=1, H=2, HV=4, K=64, V=128, dtype=dtype, pc=pc, l2=l2, lengths=lengths, slow=True,
+                host_l2=not l2)
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[dtype])
+    check("ht", f64(ht), rht, TOL[dtype])
+    # worst single sequence
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        if lengths[n]:
+            check(f"o[seq {n}]", f64(o)[:, cu[n]:cu[n + 1]], ro[:, cu[n]:cu[n + 1]], TOL[dtype])
+
+
+def test_forward_matches_per_token_recurrence():
+    """The GPU against the plain per-token oracle directly (not the chunked one)."""
+    w, inp = mk(B=1, T=100, H=1, HV=2, K=64, V=64, dtype="fp32", slow=True)
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = recurrent.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"],
+                                      use_qk_l2norm=True)
+    check("o", f64(o), ro, 1e-4)
+    check("ht", f64(ht), rht, 1e-4)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_empty_batch_and_no_state():
+    w, inp = mk(B=2, T=0)
+    o, ht, _ = gpu_fwd(inp)
+    assert o.numel() == 0
+    assert torch.equal(ht.cpu(), inp["h0"])
+
+
+def test_single_token_sequences():
+    w, inp = mk(B=1, lengths=[1, 1, 1, 2], dtype="fp32", K=32, V=32)
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, 1e-4)
+    check("ht", f64(ht), rht, 1e-4)
+
+
+@pytest.mark.parametrize("scale", [1.0, 128 ** -0.5])
+def test_largest_head_dims(scale):
+    w, inp = mk(B=1, T=96, H=1, HV=2, K=256, V=256, scale=scale, slow=True)
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, 5e-3)
+    check("ht", f64(ht), rht, 5e-3)
+
+
+def test_extreme_per_channel_gate_span():
+    """Gate spans above the exponential-safety limit take the per-element path
+    (diagonal blocks) and must still match."""
+    w, inp = mk(B=1, T=64, H=1, HV=1, K=64, V=64, C=64, pc=True, dtype="fp32")
+    inp["g"] = inp["g"] * 0.0 - 9.0          # ~144 of decay inside each 16-row block
+    inp["g"][0, 1::3] = -0.01
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, 1e-4)
+    check("ht", f64(ht), rht, 1e-4)
+
+
+# ------------------------------------------------------------------ invariants (bitwise)
+
+def test_varlen_equals_dense_per_sequence_bitwise():
+    lengths = [130, 64, 1, 200]
+    w, inp = mk(B=1, H=2, HV=4, K=128, V=128, lengths=lengths, slow=True)
+    o, ht, _ = gpu_fwd(inp)
+    cu = inp["cu_seqlens"].tolist()
+    for n, L in enumerate(lengths):
+        s, e = cu[n], cu[n + 1]
+        sub = dict(inp, cu_seqlens=None, B=1, N=1, T=L)
+        for key in ("q", "k", "v", "g", "beta"):
+            sub[key] = inp[key][:, s:e].contiguous()
+        sub["h0"] = inp["h0"][n:n + 1].contiguous()
+        on, hn, _ = gpu_fwd(sub)
+        assert torch.equal(o[:, s:e].cpu(), on.cpu()), f"o differs for sequence {n}"
+        assert torch.equal(ht[n:n + 1].cpu(), hn.cpu()), f"ht differs for sequence {n}"
+
+
+@pytest.mark.parametrize("split", [64, 192])
+def test_split_handoff_bitwise(split):
+    """Running [0, split) then [split, T) with ht -> h0 equals one pass, bit for
+    bit, when the split sits on a chunk boundary (KCP page, step 4 of its
+    playbook: a uniform single sequence must be bit-perfect)."""
+    w, inp = mk(B=1, T=320, H=2, HV=2, K=128, V=128, slow=True)
+    o, ht, _ = gpu_fwd(inp)
+    a = dict(inp, T=split)
+    b = dict(inp, T=320 - split)
+    for key in ("q", "k", "v", "g", "beta"):
+        a[key] = inp[key][:, :split].contiguous()
+        b[key] = inp[key][:, split:].contiguous()
+    oa, hta, _ = gpu_fwd(a)
+    b["h0"] = hta.cpu()
+    ob, htb, _ = gpu_fwd(b)
+    assert torch.equal(torch.cat([oa, ob], 1).cpu(), o.cpu())
+    assert torch.equal(htb.cpu(), ht.cpu())
+
+
+def test_split_handoff_unaligned_within_tolerance():
+    w, inp = mk(B=1, T=300, H=1, HV=2, K=64, V=64, slow=True)
+    split = 111
+    ro, rht = oracle_fwd(inp)
+    a = dict(inp, T=split)
+    b = dict(inp, T=300 - split)
+    for key in ("q", "k", "v", "g", "beta"):
+        a[key] = inp[key][:, :split].contiguous()
+        b[key] = inp[key][:, split:].contiguous()
+    oa, hta, _ = gpu_fwd(a)
+    b["h0"] = hta.cpu()
+    ob, htb, _ = gpu_fwd(b)
+    check("o", f64(torch.cat([oa, ob], 1)), ro, 5e-3)
+    check("ht", f64(htb), rht, 5e-3)
+
+
+def test_gva_equals_repeated_heads_bitwise():
+    w, inp = mk(B=2, T=150, H=2, HV=6, K=64, V=64)
+    o, ht, _ = gpu_fwd(inp)
+    rep = dict(inp, q=inp["q"].repeat_interleave(3, 2), k=inp["k"].repeat_interleave(3, 2))
+    o2, ht2, _ = gpu_fwd(rep)
+    assert torch.equal(o.cpu(), o2.cpu()) and torch.equal(ht.cpu(), ht2.cpu())
+
+
+def test_h0_none_equals_zeros_bitwise():
+    w, inp = mk(B=2, T=100)
+    o1, ht1, _ = gpu_fwd(inp, h0=False)
+    z = dict(inp, h0=torch.zeros_like(inp["h0"]))
+    o2, ht2, _ = gpu_fwd(z)
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(ht1.cpu(), ht2.cpu())
+
+
+def test_deterministic_and_nan_poison_and_canaries():
+    """Run-to-run bitwise determinism; NaN-filled outputs and workspace on entry
+    (the poisoning idea of the coverage-matrix page, section 7) leave no trace;
+    guard bands around o, ht and the workspace are untouched."""
+    w, inp = mk(B=2, T=170, H=2, HV=4, K=128, V=128, slow=True)
+    o1, ht1, _ = gpu_fwd(inp)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
+    lay = gdr.fwd_layout(p)
+    pad = 4096
+    ws_full = torch.full((lay.total + 2 * pad,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws = ws_full[pad:pad + lay.total]
+    on = o1.numel()
+    o_full = torch.full((on + 2 * pad,), float("nan"), dtype=o1.dtype, device="cuda")
+    ht_full = torch.full((ht1.numel() + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+    o = o_full[pad:pad + on].view(o1.shape)
+    ht = ht_full[pad:pad + ht1.numel()].view(ht1.shape)
+    o2, ht2, _ = gpu_fwd(inp, workspace=ws, out=(o, ht))
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(ht1.cpu(), ht2.cpu())
+    assert not torch.isnan(o2).any() and not torch.isnan(ht2).any()
+    assert torch.isnan(o_full[:pad]).all() and torch.isnan(o_full[pad + on:]).all()
+    assert torch.isnan(ht_full[:pad]).all() and torch.isnan(ht_full[pad + ht1.numel():]).all()
+    assert (ws_full[:pad] == 0xFF).all() and (ws_full[pad + lay.total:] == 0xFF).all()
+
+
+def test_int64_offsets():
+    """A varlen batch whose last sequence sits past 2^31 elements of q / k / v
+    and of the per-chunk state tensor; only that sequence is checked."""
+    H = HV = 16
+    K = V = 128
+    tail = 192
+    T_big = (1 << 20) + 64
+    lengths = [T_big - tail, tail]
+    gen = torch.Generator().manual_seed(3)
+    T = T_big
+    q = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    k = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    v = torch.zeros(1, T, HV, V, dtype=torch.bfloat16)
+    g = torch.zeros(1, T, HV)
+    beta = torch.zeros(1, T, HV)
+    s = T - tail
+    q[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    k[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    v[:, s:] = torch.randn(1, tail, HV, V, generator=gen).bfloat16()
+    g[:, s:] = torch.nn.functional.logsigmoid(torch.randn(1, tail, HV, generator=gen) + 4)
+    beta[:, s:] = torch.sigmoid(torch.randn(1, tail, HV, generator=gen))
+    h0 = 0.1 * torch.randn(2, HV, K, V, generator=gen)
+    assert (T - 1) * H * K > 2 ** 31
+    cu = torch.tensor([0, lengths[0], T], dtype=torch.int32)
+    inp = dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, scale=1.0, chunk_size=64,
+               use_qk_l2norm=True)
+    o, ht, ws = gpu_fwd(inp)
+    sub = dict(inp, cu_seqlens=None, h0=h0[1:2])
+    for key in ("q", "k", "v", "g", "beta"):
+        sub[key] = inp[key][:, s:].contiguous()
+    ro, rht = oracle_fwd(sub)
+    check("o tail", f64(o[:, s:]), ro, 5e-3)
+    check("ht tail", f64(ht[1:2]), rht, 5e-3)
+    del ws
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def _run_config(name, rows=None, heads=None):
+    w = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(w)
+    o, ht, _ = gpu_fwd(inp)
+    sub = slice_inputs(inp, rows=rows, heads=heads)
+    ro, rht = oracle_fwd(sub)
+    og, htg = o, ht
+    if rows is not None:
+        og, htg = og[rows], htg[rows]
+    if heads is not None:
+        og, htg = og[:, :, heads], htg[:, heads]
+    tol = TOL[w.dtype]
+    r1 = check("o", f64(og), ro, tol)
+    r2 = check("ht", f64(htg), rht, tol)
+    print(f"{name}: err_ratio o={r1:.2e} ht={r2:.2e}")
+    return inp, o, ht
+
+
+def test_config_tiny_fp32():
+    inp, o, ht = _run_config("tiny_fp32")
+    ro, rht = recurrent.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], h0=inp["h0"])
+    check("o (per-token)", f64(o), ro, 1e-4)
+
+
+def test_config_gdn_dense_bf16():
+    _run_config("gdn_dense_bf16")
+
+
+def test_config_varlen_gva_bf16():
+    inp, o, ht = _run_config("varlen_gva_bf16")
+    assert any(L % 64 for L in np.diff(inp["cu_seqlens"].numpy()))
+
+
+def test_config_kda_bf16():
+    _run_config("kda_bf16", rows=slice(1, 2))
+
+
+def test_config_long_bf16_forward():
+    _run_config("long_bf16", heads=[0, 21])
