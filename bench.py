@@ -182,11 +182,12 @@ def main():
     cidx, coff = views["chunk_idx"], views["chunk_off"]
     stages = {
         "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], cidx, coff),
-        "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], cidx, coff, views["Tm"]),
+        "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], cidx, coff, views["Tm"],
+                                               views["kscale"]),
         "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff, views["Tm"], views["w"],
                                  views["u"]),
         "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
-                                   views["v_new"], ht),
+                                   views["v_new"], ht, views["kscale"]),
         "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
     }
     names = list(stages)
@@ -210,7 +211,7 @@ def main():
     if args.breakdown:
         print("per-stage ms: " + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr)
 
-    T_seq = inp["T"] / inp["N"]
+    T_seq = inp["B"] * inp["T"] / inp["N"]
     per_unit = stage_bytes_per_token_head(w, T_seq)
     units = tokens * w.HV
     dom = max(per_unit, key=lambda n: avg_ms[n])

@@ -46,7 +46,7 @@ class GdrFwdLayout(ctypes.Structure):
     _fields_ = [("nt_max", ctypes.c_int64), ("chunk_idx", ctypes.c_size_t),
                 ("chunk_off", ctypes.c_size_t), ("Tm", ctypes.c_size_t), ("w", ctypes.c_size_t),
                 ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
-                ("total", ctypes.c_size_t)]
+                ("kscale", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class GdrError(RuntimeError):
@@ -76,9 +76,9 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrFwdLayout)]
         L.gdr_chunk_fwd.argtypes = [PP] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
         L.gdr_chunk_table.argtypes = [PP, _P, _P, _P, _P]
-        L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 6 + [_P]
+        L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 7 + [_P]
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
-        L.gdr_fwd_h.argtypes = [PP] + [_P] * 10 + [_P]
+        L.gdr_fwd_h.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
@@ -231,6 +231,7 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
         u=view(lay.u, (nt, HV, V, C), dt, es),
         h=view(lay.h, (nt, HV, V, K), dt, es),
         v_new=view(lay.v_new, (nt, HV, V, C), dt, es),
+        kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, C + 4), torch.float32, 4),
     )
 
 
@@ -241,9 +242,9 @@ def chunk_table(p: GdrProblem, cu_seqlens, chunk_idx, chunk_off):
                                  _stream(chunk_off.device)))
 
 
-def fwd_kkt_solve(p, k, g, beta, chunk_idx, chunk_off, Tm):
+def fwd_kkt_solve(p, k, g, beta, chunk_idx, chunk_off, Tm, kscale=None):
     _raise(lib().gdr_fwd_kkt_solve(ctypes.byref(p), _ptr(k), _ptr(g), _ptr(beta), _ptr(chunk_idx),
-                                   _ptr(chunk_off), _ptr(Tm), _stream(k.device)))
+                                   _ptr(chunk_off), _ptr(Tm), _ptr(kscale), _stream(k.device)))
 
 
 def fwd_wy(p, k, v, g, beta, chunk_idx, chunk_off, Tm, w, u):
@@ -251,9 +252,10 @@ def fwd_wy(p, k, v, g, beta, chunk_idx, chunk_off, Tm, w, u):
                             _ptr(chunk_off), _ptr(Tm), _ptr(w), _ptr(u), _stream(k.device)))
 
 
-def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht):
-    _raise(lib().gdr_fwd_h(ctypes.byref(p), _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(chunk_idx),
-                           _ptr(chunk_off), _ptr(h0), _ptr(h), _ptr(v_new), _ptr(ht), _stream(k.device)))
+def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht, kscale=None):
+    _raise(lib().gdr_fwd_h(ctypes.byref(p), _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(kscale),
+                           _ptr(chunk_idx), _ptr(chunk_off), _ptr(h0), _ptr(h), _ptr(v_new), _ptr(ht),
+                           _stream(k.device)))
 
 
 def fwd_o(p, q, k, v_new, h, g, chunk_idx, chunk_off, o):

@@ -91,6 +91,8 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * V * K * es);
   l.v_new = off;
   off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.kscale = off;
+  off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * (C + 4) * sizeof(float)));
   l.total = off;
   return l;
 }
@@ -179,6 +181,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   a.u = ws + l.u;
   a.h = ws + l.h;
   a.v_new = ws + l.v_new;
+  a.kscale = p->gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.kscale);
   a.o = o;
   a.ht = ht;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -216,9 +219,12 @@ gdr_status stage_common(const gdr_problem* p, std::initializer_list<const void*>
 }  // namespace
 
 gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g, const float* beta,
-                             const int32_t* chunk_idx, const int32_t* chunk_off, void* Tm, void* stream) {
+                             const int32_t* chunk_idx, const int32_t* chunk_off, void* Tm, float* kscale,
+                             void* stream) {
   gdr_status st = stage_common(p, {k, g, beta, chunk_idx, chunk_off, Tm});
   if (st != GDR_OK) return st;
+  if (!p->gate_per_channel && kscale == nullptr) return GDR_ERR_NULL_ARG;
+  if (kscale != nullptr && !aligned16(kscale)) return GDR_ERR_ALIGNMENT;
   FwdArgs a = make_args(*p);
   a.k = k;
   a.g = g;
@@ -226,6 +232,7 @@ gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g
   a.chunk_idx = const_cast<int32_t*>(chunk_idx);
   a.chunk_off = const_cast<int32_t*>(chunk_off);
   a.Tm = Tm;
+  a.kscale = p->gate_per_channel ? nullptr : kscale;
   return hip_status(gdr::launch_kkt_solve(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -248,16 +255,19 @@ gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const 
 }
 
 gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u, const float* g,
-                     const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0, void* h, void* v_new,
-                     float* ht, void* stream) {
-  gdr_status st = stage_common(p, {k, w, u, g, chunk_idx, chunk_off, h, v_new});
+                     const float* kscale, const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0,
+                     void* h, void* v_new, float* ht, void* stream) {
+  gdr_status st = stage_common(p, {k, w, u, chunk_idx, chunk_off, h, v_new});
   if (st != GDR_OK) return st;
+  if (p->gate_per_channel ? g == nullptr : kscale == nullptr) return GDR_ERR_NULL_ARG;
+  if ((g && !aligned16(g)) || (kscale && !aligned16(kscale))) return GDR_ERR_ALIGNMENT;
   if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_ERR_ALIGNMENT;
   FwdArgs a = make_args(*p);
   a.k = k;
   a.w = const_cast<void*>(w);
   a.u = const_cast<void*>(u);
   a.g = g;
+  a.kscale = const_cast<float*>(kscale);
   a.chunk_idx = const_cast<int32_t*>(chunk_idx);
   a.chunk_off = const_cast<int32_t*>(chunk_off);
   a.h0 = h0;

@@ -173,6 +173,16 @@ GDR_DEV Frag<T> lds_tr_frag(const T* tile, int pitch, int row_lo, int row_hi, in
 GDR_DEV float to_float(bf16 x) { return (float)x; }
 GDR_DEV float to_float(float x) { return x; }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// fences global memory, which makes the compiler wait for every outstanding
+// global load and store (s_waitcnt vmcnt(0)) and so drains software-pipelined
+// prefetches; kernels whose waves only share data through LDS use this one.
+GDR_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- waves
 
 // Inclusive prefix sum across the 64 lanes of a wave.

@@ -27,6 +27,7 @@ struct FwdArgs {
   void* u;
   void* h;
   void* v_new;
+  float* kscale;
   void* o;
   float* ht;
 };

@@ -241,6 +241,17 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
       __syncthreads();
     }
 
+    // ---- per-token factors the state scan applies to the rows of e:
+    //      kscale[t] = exp(G_L - G_t) / |k_t| (0 past L), kscale[C] = exp(G_L)
+    if constexpr (!PC) {
+      if (a.kscale != nullptr) {
+        float* ks = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+        const float GL = __shfl(Gc, 63, 64);     // padded lanes add 0, so lane 63 holds G_L
+        if (lane < C) ks[lane] = (lane < L) ? __expf(GL - Gc) * sRn[lane] : 0.f;
+        if (lane < 4) ks[C + lane] = (lane == 0) ? __expf(GL) : 0.f;
+      }
+    }
+
     // ---- store Tm (rows / cols past L and the upper triangle are zero)
     T* dst = Tout + (c * HV + j) * (int64_t)(C * C);
     for (int idx = lane; idx < C * C / 8; idx += 64) {

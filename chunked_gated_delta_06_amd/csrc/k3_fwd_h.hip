@@ -12,20 +12,23 @@
 // ("FLA operator-kernel correctness testing and coverage matrix", section 2).
 //
 // gfx950 mapping: one workgroup per (sequence, value head, BV = 16 NW value
-// columns); wave w owns 16 columns of S as eight (K/16) 16x16 fp32 MFMA
-// accumulators that never leave registers.  Per chunk:
-//  * w and the raw keys are staged token-major in LDS (coalesced 16-byte
-//    loads); u arrives straight from its per-chunk transposed layout;
+// columns); wave w owns 16 columns of S as K/16 16x16 fp32 MFMA accumulators
+// that never leave registers.
+//  * The chunk loop is software-pipelined: every chunk's w / k / u / gate data
+//    is fetched into registers two chunk steps before it is used (two register
+//    payloads, loop unrolled by two), then staged into one of two LDS buffers,
+//    so the global-load latency overlaps two steps of MFMA work instead of
+//    stalling the sequential scan.
 //  * e = u - w S on bf16 MFMA, with S fed as the B operand directly from its
-//    accumulator layout (the "chained" contraction map);
-//  * the S update k^T e reads k^T from LDS with ds_read_b64_tr_b16 and takes e
-//    from the previous MFMA's accumulators, again without a round trip;
-//  * a scalar gate and the key norm scale the rows of e in fp32, keeping the
-//    raw keys exact; a per-channel gate scales the key tile element-wise;
-//  * h is written transposed (h^T, 8-byte stores of four features) for the
-//    output kernel; e is written per-chunk transposed (v_new).
-//  * consecutive workgroups of one head are mapped to one XCD so the shared
-//    w / k tiles hit the same L2.
+//    accumulator layout (the "chained" contraction map); the S update k^T e
+//    reads k^T from LDS with ds_read_b64_tr_b16 and takes e from the previous
+//    MFMA's accumulators.
+//  * A scalar gate and the key norm scale the rows of e in fp32, keeping the
+//    raw keys exact; a per-channel gate scales the staged key tile.
+//  * h is written transposed (h^T, four features per lane) for the output
+//    kernel; e is written per-chunk transposed (v_new).
+//  * Consecutive workgroups of one head are mapped to one XCD so the shared
+//    w / k tiles are served from the same L2.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -34,22 +37,51 @@ namespace gdr {
 namespace {
 
 template <typename T, int C, int K, bool PC, int NW>
+struct K3 {
+  static constexpr int NT = 64 * NW;            // threads per workgroup
+  static constexpr int NE = C / 16;             // token blocks of e
+  static constexpr int NS = K / 16;             // feature blocks of S
+  static constexpr int KSK = K / 32;            // feature slabs
+  static constexpr int KSC = C / 32;            // token slabs
+  static constexpr int CPR = K / 8;             // 8-element pieces per key row
+  static constexpr int NLD = C * CPR / NT;      // pieces of a C x K tile per thread
+  static constexpr int WP = K + 16 / sizeof(T); // LDS pitch of w rows (+16 B)
+  static constexpr int KP = K + 32 / sizeof(T); // LDS pitch of key rows (+32 B, transposed reads)
+  static constexpr int GP = K + 1;
+  static constexpr int NG = PC ? C * K / 4 / NT : 1;   // float4 pieces of a per-channel gate tile
+  static constexpr size_t tile_bytes = (size_t)C * (WP + KP) * sizeof(T) + (PC ? K * 4 : 0);
+  static constexpr size_t fixed_bytes = PC ? (size_t)C * GP * 4 : 0;
+  static constexpr int NBUF = (2 * tile_bytes + fixed_bytes <= 160 * 1024) ? 2 : 1;
+  static constexpr bool fits = NBUF * tile_bytes + fixed_bytes <= 160 * 1024;
+
+  // one chunk's global data, held in registers between fetch and staging
+  struct Regs {
+    Frag<T> w[NLD], k[NLD];
+    v4_t<T> u[NE];
+    f32x4 ks[NE];      // scalar gate: exp(G_L - G_t) / |k_t| for this lane's rows of e
+    f32x4 gc[NG];      // per-channel gate tile piece
+    float gl;          // scalar gate: exp(G_L)
+    int64_t t0;
+    int L;
+  };
+
+  struct Smem {
+    T w[NBUF][C * WP];
+    T k[NBUF][C * KP];
+    float dec[NBUF][PC ? K : 1];   // exp(G_L,d) (per-channel gate)
+    float gc[PC ? C * GP : 1];     // per-channel cumsum scratch
+  };
+};
+
+template <typename T, int C, int K, bool PC, int NW>
 __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
-  constexpr int NE = C / 16;        // token blocks of e
-  constexpr int NS = K / 16;        // feature blocks of S
-  constexpr int KSK = K / 32;       // feature slabs
-  constexpr int KSC = C / 32;       // token slabs
-  constexpr int PADE = 16 / sizeof(T);
-  constexpr int KP = K + PADE;
-  constexpr int CPR = K / 8;
-  constexpr int GP = K + 1;
+  using Cfg = K3<T, C, K, PC, NW>;
+  using Regs = typename Cfg::Regs;
+  constexpr int NT = Cfg::NT, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
+  constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, WP = Cfg::WP, KP = Cfg::KP, GP = Cfg::GP;
+  constexpr int NG = Cfg::NG, NBUF = Cfg::NBUF;
   constexpr int BV = 16 * NW;
-  __shared__ __attribute__((aligned(16))) T sW[C * KP];
-  __shared__ __attribute__((aligned(16))) T sK[C * KP];
-  __shared__ float sSc[C], sRn[C];
-  __shared__ float sDec[PC ? K : 1];
-  __shared__ float sGc[PC ? C * GP : 1];
-  __shared__ float sGL;
+  __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
@@ -64,6 +96,89 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
   const T* __restrict__ ubase = static_cast<const T*>(a.u);
   T* __restrict__ hbase = static_cast<T*>(a.h);
   T* __restrict__ vnbase = static_cast<T*>(a.v_new);
+  const float* __restrict__ gp = a.g;
+
+  // ---- fetch chunk c into registers (no waiting here)
+  // Addresses are a wave-uniform 64-bit base plus a 32-bit per-lane offset.
+  auto fetch = [&](Regs& R, int64_t c) {
+    R.t0 = a.chunk_idx[4 * c + 1];
+    R.L = a.chunk_idx[4 * c + 2];
+    const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
+    const T* krow = kp + (R.t0 * H + h) * K;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      R.w[i] = ld8(wp + 8 * idx);
+      R.k[i] = (t < R.L) ? ld8(krow + (t * (int)(H * K) + d8)) : frag_zero<T>();
+    }
+    const T* up = ubase + ((c * HV + j) * V + v0) * (int64_t)C;
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) R.u[eb] = ld4raw(up + (r16 * C + 16 * eb + 4 * g4));
+    if constexpr (PC) {
+      const float* grow = gp + (R.t0 * HV + j) * K;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+        R.gc[i] = (t < R.L) ? *reinterpret_cast<const f32x4*>(grow + (t * (int)(HV * K) + d4)) : zero4();
+      }
+    } else {
+      const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+#pragma unroll
+      for (int eb = 0; eb < NE; ++eb) R.ks[eb] = *reinterpret_cast<const f32x4*>(ksp + 16 * eb + 4 * g4);
+      R.gl = ksp[C];
+    }
+  };
+
+  f32x4 ucur[NE];     // u of the chunk being computed (accumulator layout)
+  f32x4 kscur[NE];    // its row factors for e (scalar gate)
+  float glcur = 0.f;  // exp(G_L) (scalar gate)
+
+  // ---- stage registers into LDS buffer b (waits for the fetch to land)
+  auto stage = [&](const Regs& R, int b) {
+    if constexpr (PC) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.gc[t * GP + d4 + e] = R.gc[i][e];
+      }
+      lds_barrier();
+      for (int d = tid; d < K; d += NT) {
+        float run = 0.f;
+        for (int t = 0; t < C; ++t) {
+          run += sm.gc[t * GP + d];
+          sm.gc[t * GP + d] = run;
+        }
+        sm.dec[b][d] = __expf(run);
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      st8(&sm.w[b][t * WP + d8], R.w[i]);
+      if constexpr (PC) {
+        f32x8 x = R.k[i].f32();
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+        sq = lanes_sum(sq, CPR);
+        const float rn = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+        const float* Gl = &sm.gc[(C - 1) * GP];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= rn * __expf(Gl[d8 + e] - sm.gc[t * GP + d8 + e]);
+        st8(&sm.k[b][t * KP + d8], Frag<T>::make(x));
+      } else {
+        st8(&sm.k[b][t * KP + d8], R.k[i]);
+      }
+    }
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) {
+      ucur[eb] = to_f32<T>(R.u[eb]);
+      if constexpr (!PC) kscur[eb] = R.ks[eb];
+    }
+    if constexpr (!PC) glcur = R.gl;
+  };
 
   // S: rows 16 mb + 4 g4 + i, column v0 + r16
   f32x4 S[NS];
@@ -77,96 +192,38 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
     }
   }
 
-  const int32_t c_begin = a.chunk_off[n], c_end = a.chunk_off[n + 1];
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t t0 = a.chunk_idx[4 * c + 1];
-    const int L = a.chunk_idx[4 * c + 2];
-    const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
-
-    // ---- stage w, k and the gate factors of chunk c
-    if constexpr (PC) {
-      for (int idx = tid; idx < C * K; idx += 64 * NW) {
-        const int t = idx / K, d = idx % K;
-        sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
-      }
-      __syncthreads();
-      for (int d = tid; d < K; d += 64 * NW) {
-        float run = 0.f;
-        for (int t = 0; t < C; ++t) {
-          run += sGc[t * GP + d];
-          sGc[t * GP + d] = run;
-        }
-        sDec[d] = __expf(run);
-      }
-      __syncthreads();
-    }
-    for (int idx = tid; idx < C * CPR; idx += 64 * NW) {
-      const int t = idx / CPR, d8 = (idx % CPR) * 8;
-      st8(&sW[t * KP + d8], ld8(wp + t * K + d8));
-      Frag<T> f = (t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
-      f32x8 x = f.f32();
-      float sq = 0.f;
+  // ---- one chunk step from LDS buffer b
+  auto compute = [&](int64_t c, int b) {
+    // h[c] = S (transposed, 4 features per lane)
+    T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
-      sq = lanes_sum(sq, CPR);
-      const float rn = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
-      if (idx % CPR == 0) sRn[t] = rn;
-      if constexpr (PC) {
-        const float* Gl = &sGc[(C - 1) * GP];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= rn * __expf(Gl[d8 + e] - sGc[t * GP + d8 + e]);
-        f = Frag<T>::make(x);
-      }
-      st8(&sK[t * KP + d8], f);
-    }
-    if (!PC && wv == 0) {
-      const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
-      const float G = wave_incl_scan(gv, lane);
-      const float GL = __shfl(G, 63, 64);        // padded rows add 0, so lane 63 holds G_L
-      if (lane == 0) sGL = __expf(GL);
-      if (lane < C) sSc[lane] = __expf(GL - G);
-    }
-    __syncthreads();
-
-    // ---- h[c] = S (transposed, 4 features per lane)
-    T* hp = hbase + ((c * HV + j) * V + v0 + r16) * (int64_t)K;
-#pragma unroll
-    for (int mb = 0; mb < NS; ++mb) st4(hp + 16 * mb + 4 * g4, S[mb]);
-
-    // ---- e = u - w S
-    const T* up = ubase + ((c * HV + j) * V + v0 + r16) * (int64_t)C;
+    for (int mb = 0; mb < NS; ++mb) st4(hp + (r16 * K + 16 * mb + 4 * g4), S[mb]);
+    // e = u - w S
     f32x4 E[NE];
 #pragma unroll
-    for (int eb = 0; eb < NE; ++eb) E[eb] = ld4f(up + 16 * eb + 4 * g4);
+    for (int eb = 0; eb < NE; ++eb) E[eb] = ucur[eb];
     Frag<T> nS[KSK];
 #pragma unroll
     for (int ks = 0; ks < KSK; ++ks) nS[ks] = frag_from_halves<T>(-S[2 * ks], -S[2 * ks + 1]);
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) {
-      const T* row = &sW[(16 * eb + r16) * KP];
+      const T* row = &sm.w[b][(16 * eb + r16) * WP];
 #pragma unroll
-      for (int ks = 0; ks < KSK; ++ks) {
+      for (int ks = 0; ks < KSK; ++ks)
         mma(E[eb], ld_chain(row + 32 * ks + 4 * g4, row + 32 * ks + 16 + 4 * g4), nS[ks]);
-      }
     }
-
-    // ---- v_new = e (transposed per chunk)
-    T* vnp = vnbase + ((c * HV + j) * V + v0 + r16) * (int64_t)C;
+    // v_new = e (transposed per chunk)
+    T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
-    for (int eb = 0; eb < NE; ++eb) st4(vnp + 16 * eb + 4 * g4, E[eb]);
-
-    // ---- S <- diag(exp(G_L)) S + k^T diag(s) e
+    for (int eb = 0; eb < NE; ++eb) st4(vnp + (r16 * C + 16 * eb + 4 * g4), E[eb]);
+    // S <- diag(exp(G_L)) S + k^T diag(s) e
     Frag<T> Ef[KSC];
 #pragma unroll
     for (int kt = 0; kt < KSC; ++kt) {
       f32x4 lo = E[2 * kt], hi = E[2 * kt + 1];
       if constexpr (!PC) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t_lo = 32 * kt + 4 * g4 + i, t_hi = t_lo + 16;
-          lo[i] *= sSc[t_lo] * sRn[t_lo];
-          hi[i] *= sSc[t_hi] * sRn[t_hi];
-        }
+        lo *= kscur[2 * kt];
+        hi *= kscur[2 * kt + 1];
       }
       Ef[kt] = frag_from_halves<T>(lo, hi);
     }
@@ -174,20 +231,48 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
 #pragma unroll
       for (int mb = 0; mb < NS; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[mb][i] *= sDec[16 * mb + 4 * g4 + i];
+        for (int i = 0; i < 4; ++i) S[mb][i] *= sm.dec[b][16 * mb + 4 * g4 + i];
     } else {
-      const float dec = sGL;
 #pragma unroll
-      for (int mb = 0; mb < NS; ++mb) S[mb] *= dec;
+      for (int mb = 0; mb < NS; ++mb) S[mb] *= glcur;
     }
 #pragma unroll
-    for (int mb = 0; mb < NS; ++mb) {
+    for (int mb = 0; mb < NS; ++mb)
 #pragma unroll
-      for (int kt = 0; kt < KSC; ++kt) {
-        mma(S[mb], lds_tr_frag(sK, KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane), Ef[kt]);
-      }
+      for (int kt = 0; kt < KSC; ++kt)
+        mma(S[mb], lds_tr_frag(&sm.k[b][0], KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane), Ef[kt]);
+  };
+
+  // ---- pipelined chunk loop.  Fetches are unconditional (the chunk index is
+  // clamped to the sequence's last chunk, so the load addresses stay valid and
+  // extra copies are simply never computed): with an identical stream of
+  // memory operations on every path the compiler can wait for exactly the
+  // fetch it needs instead of draining all outstanding loads.
+  const int64_t c_begin = a.chunk_off[n];
+  const int nc = a.chunk_off[n + 1] - (int)c_begin;
+  if (nc > 0) {
+    const int64_t c_last = c_begin + nc - 1;
+    auto cl = [&](int64_t c) { return c < c_last ? c : c_last; };
+    Regs Ra, Rb;
+    fetch(Ra, c_begin);
+    fetch(Rb, cl(c_begin + 1));
+    stage(Ra, 0);
+    lds_barrier();
+    fetch(Ra, cl(c_begin + 2));
+    int i = 0;
+    for (; i + 1 < nc; i += 2) {
+      compute(c_begin + i, 0);
+      if constexpr (NBUF == 1) lds_barrier();
+      stage(Rb, NBUF - 1);
+      fetch(Rb, cl(c_begin + i + 3));
+      lds_barrier();
+      compute(c_begin + i + 1, NBUF - 1);
+      if constexpr (NBUF == 1) lds_barrier();
+      stage(Ra, 0);
+      fetch(Ra, cl(c_begin + i + 4));
+      lds_barrier();
     }
-    __syncthreads();
+    if (i < nc) compute(c_begin + i, 0);
   }
 
   if (a.ht != nullptr) {
@@ -198,25 +283,22 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
   }
 }
 
-// LDS bytes of one workgroup (the per-channel gate tile dominates in fp32)
-template <typename T, int C, int K, bool PC>
-constexpr size_t lds_bytes() {
-  return 2 * C * (K + 16 / sizeof(T)) * sizeof(T) + (PC ? C * (K + 1) * 4 + K * 4 : 0) + 3 * C * 4;
+template <typename T, int C, int K, bool PC, int NW>
+hipError_t launch_nw(const FwdArgs& a, hipStream_t s) {
+  if constexpr (!K3<T, C, K, PC, NW>::fits) {
+    return hipErrorInvalidValue;    // rejected on the host before any launch
+  } else {
+    const int64_t nblk = a.N * a.HV * (a.V / (16 * NW));
+    hipLaunchKernelGGL((k3_fwd_h<T, C, K, PC, NW>), dim3((unsigned)nblk), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  if constexpr (lds_bytes<T, C, K, PC>() > 160 * 1024) {
-    return hipErrorInvalidValue;    // rejected on the host before any launch
-  } else if (a.V % 32 == 0) {
-    // value columns per workgroup: 32 (two waves) when V allows it
-    const int64_t nblk = a.N * a.HV * (a.V / 32);
-    hipLaunchKernelGGL((k3_fwd_h<T, C, K, PC, 2>), dim3((unsigned)nblk), dim3(128), 0, s, a);
-  } else {
-    const int64_t nblk = a.N * a.HV * (a.V / 16);
-    hipLaunchKernelGGL((k3_fwd_h<T, C, K, PC, 1>), dim3((unsigned)nblk), dim3(64), 0, s, a);
-  }
-  return hipGetLastError();
+  // two waves (32 value columns) per workgroup; one wave per workgroup would
+  // double each thread's prefetch payload and spill at K = 128
+  return launch_nw<T, C, K, PC, 2>(a, s);
 }
 
 template <typename T, int C, bool PC>

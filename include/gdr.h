@@ -80,10 +80,12 @@ typedef struct {
  *   u          dtype [NT_max][HV][V][C]   WY values, transposed per chunk
  *   h          dtype [NT_max][HV][V][K]   state entering each chunk, transposed (h^T)
  *   v_new      dtype [NT_max][HV][V][C]   corrected values e, transposed per chunk
+ *   kscale     f32   [NT_max][HV][C + 4]  scalar gate only: exp(G_L - G_t) / |k_t| per
+ *                                         row t (0 past L), then exp(G_L), then 3 zeros
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;
-  size_t chunk_idx, chunk_off, Tm, w, u, h, v_new, total;
+  size_t chunk_idx, chunk_off, Tm, w, u, h, v_new, kscale, total;
 } gdr_fwd_layout;
 
 /* ABI version of this header (bumped on incompatible changes). */
@@ -130,10 +132,12 @@ gdr_status gdr_chunk_table(const gdr_problem* p, const int32_t* cu_seqlens, int3
 
 /* K1: per chunk and value head, G = chunk-local cumsum of g,
  * A[r][j] = beta_r * sum_d k^_rd k^_jd exp(G_rd - G_jd) for j < r, and
- * Tm = (I + A)^-1 (unit lower triangular; upper triangle and rows >= L are 0). */
+ * Tm = (I + A)^-1 (unit lower triangular; upper triangle and rows >= L are 0).
+ * With a scalar gate it also writes kscale (layout above; required then,
+ * ignored and may be NULL for a per-channel gate). */
 gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g,
                              const float* beta, const int32_t* chunk_idx,
-                             const int32_t* chunk_off, void* Tm, void* stream);
+                             const int32_t* chunk_off, void* Tm, float* kscale, void* stream);
 
 /* K2: WY recompute, w = Tm (beta exp(G) k^), u = Tm (beta v) per chunk and value head
  * (coverage-matrix page, section 2: P^r = I - sum k^i w^i^T). */
@@ -145,10 +149,12 @@ gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const 
  * state entering the chunk, as on the KCP page, section "h and dh cross-rank
  * semantics"), e = u - w S -> v_new, then
  * S <- diag(exp(G_L)) S + sum_j (exp(G_L - G_j) k^_j) e_j^T.  S starts at h0 (or 0)
- * and is written to ht after the last chunk (if ht != NULL). */
+ * and is written to ht after the last chunk (if ht != NULL).  A scalar gate is
+ * read through K1's kscale (g may then be NULL); a per-channel gate through g. */
 gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u,
-                     const float* g, const int32_t* chunk_idx, const int32_t* chunk_off,
-                     const float* h0, void* h, void* v_new, float* ht, void* stream);
+                     const float* g, const float* kscale, const int32_t* chunk_idx,
+                     const int32_t* chunk_off, const float* h0, void* h, void* v_new, float* ht,
+                     void* stream);
 
 /* K4: output, o_r = scale * [ (exp(G_r) q^_r)^T h + sum_{j<=r} (q^_r . exp(G_r - G_j) k^_j) e_j ]. */
 gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new,
