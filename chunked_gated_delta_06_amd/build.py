@@ -22,6 +22,9 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # keep the compiler from emitting packed fp32 arithmetic (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in architectural VGPRs (no AGPR <-> VGPR copies
+    # around the elementwise work between MFMAs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-pass-failed",
 ]
 

@@ -100,16 +100,24 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
 
   // ---- fetch chunk c into registers (no waiting here)
   // Addresses are a wave-uniform 64-bit base plus a 32-bit per-lane offset.
+  // token range of the sequence, read once (see k3_scan)
+  const int64_t c_begin = a.chunk_off[n];
+  const int nc = a.chunk_off[n + 1] - (int)c_begin;
+  const int64_t c_last = c_begin + (nc > 0 ? nc - 1 : 0);
+  const int64_t seq_t0 = nc > 0 ? a.chunk_idx[4 * c_begin + 1] : 0;
+  const int64_t seq_end = nc > 0 ? a.chunk_idx[4 * c_last + 1] + a.chunk_idx[4 * c_last + 2] : 0;
   auto fetch = [&](Regs& R, int64_t c) {
-    R.t0 = a.chunk_idx[4 * c + 1];
-    R.L = a.chunk_idx[4 * c + 2];
+    R.t0 = seq_t0 + (c - c_begin) * C;
+    R.L = (int)((seq_end - R.t0) < C ? (seq_end - R.t0) : C);
     const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
     const T* krow = kp + (R.t0 * H + h) * K;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      const int tc = t < R.L ? t : R.L - 1;
+      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
       R.w[i] = ld8(wp + 8 * idx);
-      R.k[i] = (t < R.L) ? ld8(krow + (t * (int)(H * K) + d8)) : frag_zero<T>();
+      R.k[i] = (t < R.L) ? kr : frag_zero<T>();
     }
     const T* up = ubase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
@@ -119,7 +127,9 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
-        R.gc[i] = (t < R.L) ? *reinterpret_cast<const f32x4*>(grow + (t * (int)(HV * K) + d4)) : zero4();
+        const int tc = t < R.L ? t : R.L - 1;
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(grow + (tc * (int)(HV * K) + d4));
+        R.gc[i] = (t < R.L) ? gr : zero4();
       }
     } else {
       const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
@@ -248,10 +258,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
   // extra copies are simply never computed): with an identical stream of
   // memory operations on every path the compiler can wait for exactly the
   // fetch it needs instead of draining all outstanding loads.
-  const int64_t c_begin = a.chunk_off[n];
-  const int nc = a.chunk_off[n + 1] - (int)c_begin;
   if (nc > 0) {
-    const int64_t c_last = c_begin + nc - 1;
     auto cl = [&](int64_t c) { return c < c_last ? c : c_last; };
     Regs Ra, Rb;
     fetch(Ra, c_begin);
@@ -283,6 +290,238 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Scalar-gate scan with warp specialisation.  Waves 0..NWC-1 compute (each owns
+// 16 value columns of S and runs only the MFMA chain of the step); waves
+// NWC..NWC+NWL-1 are loaders: they fetch each chunk's w / k / u / kscale into
+// registers three chunk steps ahead (three payloads, loop unrolled by three),
+// stage it into one of two LDS buffers while the compute waves work on the
+// other, and meet the compute waves at one LDS-only barrier per step.  The
+// compute waves therefore carry no prefetch registers, so the state and the
+// e tiles stay in architectural VGPRs next to the MFMAs.
+template <typename T, int C, int K, int NWC, int NWL>
+struct K3S {
+  static constexpr int NTL = 64 * NWL;          // loader threads
+  static constexpr int BV = 16 * NWC;           // value columns per workgroup
+  static constexpr int NE = C / 16, NS = K / 16, KSK = K / 32, KSC = C / 32;
+  static constexpr int CPR = K / 8;
+  static constexpr int NPW = C * CPR;           // 8-element pieces of a w (or k) tile
+  static constexpr int NPU = BV * C / 8;        // 8-element pieces of the u tile
+  static constexpr int NLD = (NPW + NTL - 1) / NTL;   // w and k pieces per loader thread
+  static constexpr int NLU = (NPU + NTL - 1) / NTL;   // u pieces per loader thread
+  static constexpr int NKS = (C + 4) / 4;       // float4 pieces of a kscale row
+  static constexpr int WP = K + 16 / sizeof(T);
+  static constexpr int KP = K + 32 / sizeof(T);
+  static constexpr int UP = C + 8 / sizeof(T);  // u rows (one per value column), +8 B
+  static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(T) + (C + 4) * 4;
+  static constexpr bool fits = 2 * buf_bytes <= 160 * 1024 && NKS <= NTL;
+
+  struct Regs {
+    Frag<T> w[NLD], k[NLD];
+    Frag<T> u[NLU];
+    f32x4 ks;
+    int64_t t0;
+    int L;
+  };
+  struct Smem {
+    T w[2][C * WP];
+    T k[2][C * KP];
+    T u[2][BV * UP];
+    float ks[2][C + 4];
+  };
+};
+
+template <typename T, int C, int K, int NWC, int NWL>
+__global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(FwdArgs a) {
+  using Cfg = K3S<T, C, K, NWC, NWL>;
+  using Regs = typename Cfg::Regs;
+  constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
+  constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
+  constexpr int WP = Cfg::WP, KP = Cfg::KP, UP = Cfg::UP;
+  __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const bool loader = wv >= NWC;
+  const int tl = tid - 64 * NWC;                 // loader thread index
+  const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
+  const int64_t nvt = V / BV;
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t vt = bid % nvt, j = (bid / nvt) % HV, n = bid / (nvt * HV);
+  if (n >= N) return;
+  const int64_t h = j / (HV / H);
+  const int64_t vw = vt * BV;                    // workgroup's first value column
+  const int64_t v0 = vw + 16 * wv;               // compute wave's first value column
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ wbase = static_cast<const T*>(a.w);
+  const T* __restrict__ ubase = static_cast<const T*>(a.u);
+  T* __restrict__ hbase = static_cast<T*>(a.h);
+  T* __restrict__ vnbase = static_cast<T*>(a.v_new);
+
+  const int64_t c_begin = a.chunk_off[n];
+  const int nc = a.chunk_off[n + 1] - (int)c_begin;
+  const int64_t c_last = c_begin + (nc > 0 ? nc - 1 : 0);
+  auto cl = [&](int64_t c) { return c < c_last ? c : c_last; };
+  // token range of the sequence, read once: chunk c_begin + x starts at
+  // seq_t0 + x C, so the loop never waits on a chunk-table load (vector-memory
+  // waits complete in order and would drain the prefetched payloads)
+  const int64_t seq_t0 = nc > 0 ? a.chunk_idx[4 * c_begin + 1] : 0;
+  const int64_t seq_end = nc > 0 ? a.chunk_idx[4 * c_last + 1] + a.chunk_idx[4 * c_last + 2] : 0;
+
+  // ---- loader side
+  auto fetch = [&](Regs& R, int64_t c) {
+    R.t0 = seq_t0 + (c - c_begin) * C;
+    R.L = (int)((seq_end - R.t0) < C ? (seq_end - R.t0) : C);
+    const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
+    const T* krow = kp + (R.t0 * H + h) * K;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      const bool in = (NPW % NTL == 0) || idx < NPW;
+      // rows past L load row L-1 (a valid address) and are zeroed by a select
+      const int tc = t < R.L ? t : R.L - 1;
+      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
+      R.w[i] = in ? ld8(wp + 8 * idx) : frag_zero<T>();
+      R.k[i] = (in && t < R.L) ? kr : frag_zero<T>();
+    }
+    const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
+#pragma unroll
+    for (int i = 0; i < NLU; ++i) {
+      const int idx = tl + NTL * i;
+      R.u[i] = ((NPU % NTL == 0) || idx < NPU) ? ld8(up + 8 * idx) : frag_zero<T>();
+    }
+    const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+    R.ks = (tl < NKS) ? *reinterpret_cast<const f32x4*>(ksp + 4 * tl) : zero4();
+  };
+  auto stage = [&](const Regs& R, int b) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      if ((NPW % NTL == 0) || idx < NPW) {
+        st8(&sm.w[b][t * WP + d8], R.w[i]);
+        st8(&sm.k[b][t * KP + d8], R.k[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NLU; ++i) {
+      const int idx = tl + NTL * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+      if ((NPU % NTL == 0) || idx < NPU) st8(&sm.u[b][v * UP + t8], R.u[i]);
+    }
+    if (tl < NKS) *reinterpret_cast<f32x4*>(&sm.ks[b][4 * tl]) = R.ks;
+  };
+
+  // The loader and compute waves run separate loops with the same sequence of
+  // barriers (one per chunk step), so neither carries the other's registers.
+  // Chunk c_begin + x lives in register slot x % 3 and LDS buffer x % 2; at
+  // step s the compute waves work on chunk s while the loaders stage chunk s + 1
+  // and fetch chunk s + 4 (indices clamped to the last chunk; extra copies are
+  // staged but never computed).
+  if (loader) {
+    if (nc > 0) {
+      Regs R0, R1, R2;
+      fetch(R0, c_begin);
+      fetch(R1, cl(c_begin + 1));
+      fetch(R2, cl(c_begin + 2));
+      stage(R0, 0);
+      fetch(R0, cl(c_begin + 3));
+      lds_barrier();
+      for (int s0 = 0; s0 < nc; s0 += 3) {
+        stage(R1, (s0 + 1) & 1);
+        fetch(R1, cl(c_begin + s0 + 4));
+        lds_barrier();
+        stage(R2, (s0 + 2) & 1);
+        fetch(R2, cl(c_begin + s0 + 5));
+        lds_barrier();
+        stage(R0, (s0 + 3) & 1);
+        fetch(R0, cl(c_begin + s0 + 6));
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves: S rows 16 mb + 4 g4 + i, column v0 + r16
+  f32x4 S[NS];
+#pragma unroll
+  for (int mb = 0; mb < NS; ++mb) {
+    if (a.h0 != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[mb][i] = a.h0[((n * HV + j) * K + 16 * mb + 4 * g4 + i) * V + v0 + r16];
+    } else {
+      S[mb] = zero4();
+    }
+  }
+  auto compute = [&](int64_t c, int b) {
+    // every LDS fragment of the step is requested up front (w rows for e, k^T
+    // columns for the S update), so the reads overlap the MFMA chain instead of
+    // each MFMA waiting on its own read
+    Frag<T> wf[KSK][NE], kf[KSC][NS];
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < NE; ++eb) {
+        const T* row = &sm.w[b][(16 * eb + r16) * WP];
+        wf[ks][eb] = ld_chain(row + 32 * ks + 4 * g4, row + 32 * ks + 16 + 4 * g4);
+      }
+#pragma unroll
+    for (int kt = 0; kt < KSC; ++kt)
+#pragma unroll
+      for (int mb = 0; mb < NS; ++mb)
+        kf[kt][mb] = lds_tr_frag(&sm.k[b][0], KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane);
+    f32x4 E[NE];
+    const T* urow = &sm.u[b][(16 * wv + r16) * UP];
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) E[eb] = ld4f(urow + 16 * eb + 4 * g4);
+    f32x4 sc[NE];
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
+    const float gl = sm.ks[b][C];
+    // h[c] = S (transposed, 4 features per lane)
+    T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb) st4(hp + (r16 * K + 16 * mb + 4 * g4), S[mb]);
+    // e = u - w S  (independent accumulators alternate between MFMAs)
+    Frag<T> nS[KSK];
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) nS[ks] = frag_from_halves<T>(-S[2 * ks], -S[2 * ks + 1]);
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < NE; ++eb) mma(E[eb], wf[ks][eb], nS[ks]);
+    // v_new = e (transposed per chunk)
+    T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) st4(vnp + (r16 * C + 16 * eb + 4 * g4), E[eb]);
+    // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e
+    Frag<T> Ef[KSC];
+#pragma unroll
+    for (int kt = 0; kt < KSC; ++kt) Ef[kt] = frag_from_halves<T>(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]);
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+#pragma unroll
+    for (int kt = 0; kt < KSC; ++kt)
+#pragma unroll
+      for (int mb = 0; mb < NS; ++mb) mma(S[mb], kf[kt][mb], Ef[kt]);
+  };
+
+  if (nc > 0) {
+    lds_barrier();
+    for (int s0 = 0; s0 < nc; s0 += 3) {
+      compute(c_begin + s0, s0 & 1);
+      lds_barrier();
+      if (s0 + 1 < nc) compute(c_begin + s0 + 1, (s0 + 1) & 1);
+      lds_barrier();
+      if (s0 + 2 < nc) compute(c_begin + s0 + 2, s0 & 1);
+      lds_barrier();
+    }
+  }
+  if (a.ht != nullptr) {
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.ht[((n * HV + j) * K + 16 * mb + 4 * g4 + i) * V + v0 + r16] = S[mb][i];
+  }
+}
+
 template <typename T, int C, int K, bool PC, int NW>
 hipError_t launch_nw(const FwdArgs& a, hipStream_t s) {
   if constexpr (!K3<T, C, K, PC, NW>::fits) {
@@ -296,8 +535,18 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t s) {
 
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  // two waves (32 value columns) per workgroup; one wave per workgroup would
-  // double each thread's prefetch payload and spill at K = 128
+  if constexpr (!PC) {
+    // warp-specialised scan: 2 compute + 2 loader waves (4 loader waves when
+    // elements are fp32 or K = 256, to keep each loader's payload in registers)
+    constexpr int NWL = (sizeof(T) == 4 || K == 256) ? 4 : 2;
+    if constexpr (K3S<T, C, K, 2, NWL>::fits) {
+      const int64_t nblk = a.N * a.HV * (a.V / 32);
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL>), dim3((unsigned)nblk), dim3(64 * (2 + NWL)), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  // per-channel gate (and shapes whose double-buffered tiles exceed LDS):
+  // two waves (32 value columns) per workgroup
   return launch_nw<T, C, K, PC, 2>(a, s);
 }
 
