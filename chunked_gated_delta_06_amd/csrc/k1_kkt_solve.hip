@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
         const int t = idx / K, d = idx % K;
         sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
       }
-      __syncthreads();
+      lds_barrier();
       for (int d = lane; d < K; d += 64) {
         float run = 0.f;
         for (int t = 0; t < C; ++t) {
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
           sGc[t * GP + d] = run;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // gated kk^T, block by block, with a reference row per block
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- A into LDS (strictly lower, fp32)
 #pragma unroll
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
           sM[r * P + cc] = val;
         }
       }
-    __syncthreads();
+    lds_barrier();
 
     // ---- diagonal 16x16 inverses by forward substitution (lane = column)
     float x[16];
@@ -199,12 +199,12 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
         x[r] = s;
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (db < NB) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sM[(16 * db + r) * P + 16 * db + r16] = x[r];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- block forward substitution: T_ib = -T_ii * sum_{m=b}^{i-1} A_im T_mb
 #pragma unroll
@@ -233,12 +233,12 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
         mma16_f32(Y, tv, xv);
         res[jb] = -Y;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int jb = 0; jb < ib; ++jb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sM[(16 * ib + 4 * g4 + i) * P + 16 * jb + r16] = res[jb][i];
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- per-token factors the state scan applies to the rows of e:
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
       }
       st8(dst + r * C + c8, Frag<T>::make(x));
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

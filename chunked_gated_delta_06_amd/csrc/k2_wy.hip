@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
       const int t = idx / K, d = idx % K;
       sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int d = tid; d < K; d += 256) {
       float run = 0.f;
       for (int t = 0; t < C; ++t) {
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
         sGc[t * GP + d] = run;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // key tile (token-major), row norms of the raw keys
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
     }
     st8(&sK[t * KP + d8], f);
   }
-  __syncthreads();
+  lds_barrier();
   if (wv == 0) {
     float gv = 0.f, bv = 0.f;
     if (lane < L) {
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
       sS[lane] = bv * sRn[lane] * (PC ? 1.f : __expf(G));
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // rows of Tm this lane feeds: row 16 rb + r16, tokens 32 ks + 8 g4 + e
   Frag<T> tf[NB][KSC];
@@ -131,13 +131,13 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
   for (int64_t v0 = 0; v0 < V; v0 += VT) {
     const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
     const int vpr = nv / 8;
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < C * vpr; idx += 256) {
       const int t = idx / vpr, d8 = (idx % vpr) * 8;
       const Frag<T> f = (t < L) ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + d8) : frag_zero<T>();
       st8(&sV[t * VP + d8], f);
     }
-    __syncthreads();
+    lds_barrier();
     for (int vb = wv; vb < nv / 16; vb += NW) {
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {

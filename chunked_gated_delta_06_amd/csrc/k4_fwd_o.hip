@@ -30,11 +30,19 @@ constexpr float kSpanLimit = 80.f;
 template <typename T, int C, int K, bool PC>
 __global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
   constexpr int NB = C / 16;
+  constexpr int NT = 64 * NB;
   constexpr int KSK = K / 32;
   constexpr int KSC = C / 32;
   constexpr int GP = K + 1;
+  constexpr int VT = sizeof(T) == 2 ? 128 : 64;   // value columns staged per pass
+  constexpr int HP = K + 16 / sizeof(T);          // LDS pitch of h^T rows
+  constexpr int EP = C + 16 / sizeof(T);          // LDS pitch of e^T rows
+  constexpr int NHP = (VT * K / 8 + NT - 1) / NT;  // 8-element h pieces per thread
+  constexpr int NEP = (VT * C / 8 + NT - 1) / NT;  // 8-element e pieces per thread
   __shared__ float sG[C], sRq[C], sRk[C];
   __shared__ float sGc[PC ? C * GP : 1];
+  __shared__ __attribute__((aligned(16))) T sH[VT * HP];
+  __shared__ __attribute__((aligned(16))) T sE[VT * EP];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int64_t c = blockIdx.x, j = blockIdx.y;
@@ -53,13 +61,45 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
     return frag_zero<T>();
   };
 
+  // ---- h^T and e^T tiles of VT value columns: fetched into registers early,
+  //      staged into LDS, then read as MFMA A operands
+  Frag<T> hreg[NHP], ereg[NEP];
+  auto fetch_tile = [&](int64_t v0) {
+    const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
+    const T* hsrc = hp + v0 * K;
+    const T* esrc = ep + v0 * C;
+#pragma unroll
+    for (int i = 0; i < NHP; ++i) {
+      const int idx = tid + NT * i;
+      hreg[i] = (idx < nv * K / 8) ? ld8(hsrc + 8 * idx) : frag_zero<T>();
+    }
+#pragma unroll
+    for (int i = 0; i < NEP; ++i) {
+      const int idx = tid + NT * i;
+      ereg[i] = (idx < nv * C / 8) ? ld8(esrc + 8 * idx) : frag_zero<T>();
+    }
+  };
+  auto stage_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NHP; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < VT * K / 8) st8(&sH[(idx / (K / 8)) * HP + (idx % (K / 8)) * 8], hreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NEP; ++i) {
+      const int idx = tid + NT * i;
+      if (idx < VT * C / 8) st8(&sE[(idx / (C / 8)) * EP + (idx % (C / 8)) * 8], ereg[i]);
+    }
+  };
+  fetch_tile(0);
+
   // ---- gates, norms
   if constexpr (PC) {
     for (int idx = tid; idx < C * K; idx += 64 * NB) {
       const int t = idx / K, d = idx % K;
       sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
     for (int d = tid; d < K; d += 64 * NB) {
       float run = 0.f;
       for (int t = 0; t < C; ++t) {
@@ -93,7 +133,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
     sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
     sRk[rr] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- P^T blocks (t-block jb, r-block wv), jb <= wv
   const float rq = sRq[rr];
@@ -181,9 +221,15 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
   const float sc = a.scale;
 
   // ---- O^T = h^T Q^T (scaled) + e^T P^T, 16 value columns at a time
-  for (int64_t vb = 0; vb < V / 16; ++vb) {
+  for (int64_t v0 = 0; v0 < V; v0 += VT) {
+  stage_tile();
+  lds_barrier();
+  if (v0 + VT < V) fetch_tile(v0 + VT);
+  const int nvb = ((V - v0) < VT ? (int)(V - v0) : VT) / 16;
+  for (int vbl = 0; vbl < nvb; ++vbl) {
+    const int64_t vb = v0 / 16 + vbl;
     f32x4 acc = zero4();
-    const T* hrow = hp + (16 * vb + r16) * (int64_t)K;
+    const T* hrow = &sH[(16 * vbl + r16) * HP];
 #pragma unroll
     for (int ks = 0; ks < KSK; ++ks) {
       if constexpr (PC) {
@@ -193,13 +239,15 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(FwdArgs a) {
       }
     }
     acc *= inter_scale;
-    const T* erow = ep + (16 * vb + r16) * (int64_t)C;
+    const T* erow = &sE[(16 * vbl + r16) * EP];
 #pragma unroll
     for (int kt = 0; kt < KSC; ++kt) {
       if (2 * kt > wv) continue;
       mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), Pf[kt]);
     }
     if (rr < L) st4(op + ((t0 + rr) * HV + j) * V + 16 * vb + 4 * g4, acc * sc);
+  }
+  lds_barrier();
   }
 }
 
