@@ -208,3 +208,171 @@ def wy_factors(k, beta, g, w, u):
             P[r] -= np.outer(dk, w[j])
             Hs[r] += np.outer(dk, u[j])
     return P, Hs
+
+
+# --------------------------------------------------------------------------
+# Chunk-wise backward (float64, NumPy).  Gradients of the chunk form above,
+# derived by matrix calculus for one chunk and written for the general
+# per-channel gate (a scalar gate is the case G_rd = G_r for every d; its dg
+# is the sum over d).  Per chunk, with S0 the entering state, dS1 the gradient
+# of the leaving state and Kt = exp(G_L - G) * K, Kg = exp(G) * K,
+# Qg = exp(G) * Q:
+#   dE  = scale P^T dO + Kt dS1                      (P: gated q.k, j <= r)
+#   dS0 = scale Qg^T dO + exp(G_L) * dS1 - W^T dE     (passed to the previous chunk)
+#   dP  = scale dO E^T,   dW = -dE S0^T,   dU = dE
+#   dT  = dW (beta Kg)^T + dU (beta V)^T,  dA = -T^T dT T^T (strictly lower)
+#   dV  = beta T^T dU,    dKg = beta T^T dW
+# then the gated bilinear forms A (k.k), P (q.k), Qg, Kg, Kt give dq, dk and
+# the per-channel gate gradient dG, and dg is the reverse cumsum of dG within
+# the chunk.  Pinned against the per-token backward in the tests.
+# --------------------------------------------------------------------------
+
+def _gated_pair(a, b, G, lower_strict):
+    """D[r, j] = sum_d a_rd b_jd exp(G_rd - G_jd) on the (strict) lower
+    triangle; a, b [HV,L,K], G [HV,L,K].  Returns D and the mask."""
+    L = a.shape[1]
+    low = np.tril(np.ones((L, L)), -1 if lower_strict else 0)[None, :, :, None] > 0
+    diff = G[:, :, None, :] - G[:, None, :, :]
+    ex = np.where(low, np.exp(np.where(low, diff, 0.0)), 0.0)       # [HV,r,j,K]
+    return np.einsum("hrd,hjd,hrjd->hrj", a, b, ex), ex
+
+
+def _gated_pair_grads(dD, a, b, ex):
+    """Gradients of D[r,j] = sum_d a_rd b_jd ex_rjd w.r.t. a, b and G
+    (ex = exp(G_r - G_j) on the mask): returns da, db, dG."""
+    da = np.einsum("hrj,hjd,hrjd->hrd", dD, b, ex)
+    db = np.einsum("hrj,hrd,hrjd->hjd", dD, a, ex)
+    dG = a * da - b * db
+    return da, db, dG
+
+
+def _chunk_bwd(qc, kc, vc, Gc, bc, S0, dO, dS1, scale):
+    """One chunk, all value heads; shapes as in _chunk plus dO [L,HV,V],
+    dS1 [HV,K,V].  G is per channel here ([L,HV,K]).  Returns a dict."""
+    q = np.transpose(qc, (1, 0, 2))
+    k = np.transpose(kc, (1, 0, 2))
+    v = np.transpose(vc, (1, 0, 2))
+    G = np.transpose(Gc, (1, 0, 2))
+    b = bc.T
+    do = np.transpose(dO, (1, 0, 2))
+    L = k.shape[1]
+    HV = k.shape[0]
+    # forward recompute
+    Abar, exA = _gated_pair(k, k, G, True)
+    A = b[:, :, None] * Abar
+    Tm = forward_substitution(A)
+    eG = np.exp(G)
+    Kg, Qg = eG * k, eG * q
+    GL = G[:, -1:, :]
+    Kt = np.exp(GL - G) * k
+    W = Tm @ (b[:, :, None] * Kg)
+    U = Tm @ (b[:, :, None] * v)
+    E = U - W @ S0
+    P, exP = _gated_pair(q, k, G, False)
+    tr = lambda x: np.transpose(x, (0, 2, 1))
+    # backward
+    dE = scale * tr(P) @ do + Kt @ dS1
+    dS0 = scale * tr(Qg) @ do + np.exp(GL[:, 0, :])[:, :, None] * dS1 - tr(W) @ dE
+    dP = scale * do @ tr(E)
+    dQg = scale * do @ tr(S0)
+    dKt = E @ tr(dS1)
+    dW = -dE @ tr(S0)
+    dU = dE
+    dT = dW @ tr(b[:, :, None] * Kg) + dU @ tr(b[:, :, None] * v)
+    TtdW = tr(Tm) @ dW
+    TtdU = tr(Tm) @ dU
+    dKg = b[:, :, None] * TtdW
+    dv = b[:, :, None] * TtdU
+    dA = np.tril(-tr(Tm) @ dT @ tr(Tm), -1)
+    dbeta = (Kg * TtdW).sum(-1) + (v * TtdU).sum(-1) + (dA * Abar).sum(-1)
+    dAbar = b[:, :, None] * dA
+    dk1, dk2, dG_A = _gated_pair_grads(dAbar, k, k, exA)
+    dq_P, dk_P, dG_P = _gated_pair_grads(dP, q, k, exP)
+    dq = dq_P + eG * dQg
+    dk = dk1 + dk2 + dk_P + eG * dKg + np.exp(GL - G) * dKt
+    dG = dG_A + dG_P + Qg * dQg + Kg * dKg - Kt * dKt
+    dG[:, -1, :] += (Kt * dKt).sum(1) + np.exp(GL[:, 0, :]) * (S0 * dS1).sum(-1)
+    dg = np.flip(np.cumsum(np.flip(dG, 1), 1), 1)           # reverse cumsum over rows
+    return dict(dq=dq, dk=dk, dv=dv, dbeta=dbeta, dg=dg, dS0=dS0, dE=dE,
+                dEi=scale * tr(P) @ do, E=E)
+
+
+def chunked_bwd(q, k, v, g, beta, do, dht=None, *, scale=1.0, h0=None, cu_seqlens=None,
+                use_qk_l2norm=False, chunk_size=64, intermediates=False):
+    """Chunk-wise backward of L = (o * do).sum() + (ht * dht).sum().
+    Returns dict dq, dk [B,T,H,K]; dv [B,T,HV,V]; dg like g; dbeta like beta;
+    dh0 [N,HV,K,V] (float64 NumPy).  With ``intermediates``: per-chunk dh
+    [NT,HV,K,V] (gradient of the state leaving the chunk), dE and dEi
+    [NT,HV,C,V] (dEi = scale P^T dO, the chunk-local part of dE)."""
+    q, k, v, g, beta, h0, do, dht = (_np64(x) for x in (q, k, v, g, beta, h0, do, dht))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    Gs = HV // H
+    C = int(chunk_size)
+    per_channel = g.ndim == 4
+    if use_qk_l2norm:
+        nq = np.sqrt((q * q).sum(-1, keepdims=True) + EPS)
+        nk = np.sqrt((k * k).sum(-1, keepdims=True) + EPS)
+        qh, kh = q / nq, k / nk
+    else:
+        qh, kh = q, k
+    qe = np.repeat(qh, Gs, axis=2).reshape(B * T, HV, K)
+    ke = np.repeat(kh, Gs, axis=2).reshape(B * T, HV, K)
+    vv = v.reshape(B * T, HV, V)
+    gg = g.reshape(B * T, HV, K) if per_channel else np.repeat(g.reshape(B * T, HV, 1), K, axis=2)
+    bb = beta.reshape(B * T, HV)
+    dov = do.reshape(B * T, HV, V)
+    idx, off = chunk_table(B, T, cu_seqlens, C)
+    N, NT = len(off) - 1, len(idx)
+    dqe = np.zeros((B * T, HV, K))
+    dke = np.zeros((B * T, HV, K))
+    dv = np.zeros((B * T, HV, V))
+    dG = np.zeros((B * T, HV, K))
+    dbeta = np.zeros((B * T, HV))
+    dh0 = np.zeros((N, HV, K, V))
+    inter = dict(dh=np.zeros((NT, HV, K, V)), dE=np.zeros((NT, HV, C, V)),
+                 dEi=np.zeros((NT, HV, C, V))) if intermediates else None
+    for n in range(N):
+        # forward pass over the chunks to get the entering states
+        S = h0[n].copy() if h0 is not None else np.zeros((HV, K, V))
+        states = []
+        for c in range(off[n], off[n + 1]):
+            _, t0, L = (int(x) for x in idx[c])
+            sl = slice(t0, t0 + L)
+            states.append(S)
+            Gc = np.cumsum(gg[sl], axis=0)
+            r = _chunk(qe[sl], ke[sl], vv[sl], Gc, bb[sl], S, scale, True)
+            S = r["S_next"]
+        dS = dht[n].copy() if dht is not None else np.zeros((HV, K, V))
+        for i, c in reversed(list(enumerate(range(off[n], off[n + 1])))):
+            _, t0, L = (int(x) for x in idx[c])
+            sl = slice(t0, t0 + L)
+            if inter is not None:
+                inter["dh"][c] = dS
+            Gc = np.cumsum(gg[sl], axis=0)
+            r = _chunk_bwd(qe[sl], ke[sl], vv[sl], Gc, bb[sl], states[i], dov[sl], dS, scale)
+            dqe[sl] = np.transpose(r["dq"], (1, 0, 2))
+            dke[sl] = np.transpose(r["dk"], (1, 0, 2))
+            dv[sl] = np.transpose(r["dv"], (1, 0, 2))
+            dbeta[sl] = r["dbeta"].T
+            dG[sl] = np.transpose(r["dg"], (1, 0, 2))
+            if inter is not None:
+                inter["dE"][c, :, :L] = r["dE"]
+                inter["dEi"][c, :, :L] = r["dEi"]
+            dS = r["dS0"]
+        dh0[n] = dS
+    dqh = dqe.reshape(B, T, H, Gs, K).sum(3)
+    dkh = dke.reshape(B, T, H, Gs, K).sum(3)
+    if use_qk_l2norm:
+        dq = (dqh - qh * (qh * dqh).sum(-1, keepdims=True)) / nq
+        dk = (dkh - kh * (kh * dkh).sum(-1, keepdims=True)) / nk
+    else:
+        dq, dk = dqh, dkh
+    dg = dG.reshape(B, T, HV, K)
+    if not per_channel:
+        dg = dg.sum(-1)
+    out = dict(dq=dq, dk=dk, dv=dv.reshape(B, T, HV, V), dg=dg, dbeta=dbeta.reshape(B, T, HV), dh0=dh0)
+    if intermediates:
+        inter["idx"], inter["off"] = idx, off
+        out["inter"] = inter
+    return out

@@ -413,3 +413,55 @@ def test_err_ratio_definition():
     assert abs(err_ratio(np.array([3.0, 4.0 + 0.5]), ref) - (0.5 / math.sqrt(2)) / (5 / math.sqrt(2))) < 1e-15
     with pytest.raises(AssertionError):
         err_ratio(np.array([np.nan, 1.0]), ref)
+
+
+# -------------------------------------------------------- chunked backward
+
+@pytest.mark.parametrize("C", [1, 3, 8, 32])
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("l2", [False, True])
+def test_chunked_backward_equals_per_token(C, per_channel, l2):
+    q, k, v, g, beta, h0, do, dht = _bwd_inputs(per_channel, 40, T=37, H=2, HV=4, K=5, V=3)
+    kw = dict(scale=0.7, h0=h0, use_qk_l2norm=l2)
+    ref = recurrent.recurrent_bwd(q, k, v, g, beta, do, dht, ckpt=8, **kw)
+    got = chunked.chunked_bwd(q, k, v, g, beta, do, dht, chunk_size=C, **kw)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert err_ratio(got[n], ref[n]) < 1e-11, n
+
+
+def test_chunked_backward_varlen_and_state_gradients():
+    lengths = [9, 0, 20, 1]
+    T = sum(lengths)
+    q, k, v, g, beta, _, do, _ = _bwd_inputs(False, 41, T=T, H=1, HV=2, K=4, V=3)
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    h0 = rnd(4, 2, 4, 3, seed=42)
+    dht = rnd(4, 2, 4, 3, seed=43)
+    kw = dict(scale=1.2, h0=h0, cu_seqlens=cu, use_qk_l2norm=True)
+    ref = recurrent.autograd_bwd(q, k, v, g, beta, do, dht, **kw)
+    got = chunked.chunked_bwd(q, k, v, g, beta, do, dht, chunk_size=8, intermediates=True, **kw)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert err_ratio(got[n], ref[n]) < 1e-11, n
+    # dh[c] is the gradient w.r.t. the state leaving chunk c: for the last chunk
+    # of a sequence it is dht
+    it = got["inter"]
+    for n in range(4):
+        if lengths[n]:
+            last = it["off"][n + 1] - 1
+            assert np.allclose(it["dh"][last], dht[n].numpy())
+    # dE is the gradient w.r.t. E = T (beta V - ...) taken as a free output, so
+    # dv = beta T^T dE per chunk (T from the forward oracle), and with dS1 = 0,
+    # dE reduces to its chunk-local part dEi for the last chunk of a sequence
+    # whose dht is zero
+    _, _, fi = chunked.chunked_fwd(q, k, v, g, beta, chunk_size=8, intermediates=True, **kw)
+    for c in range(len(it["idx"])):
+        _, t0, L = (int(x) for x in it["idx"][c])
+        dv_c = got["dv"][0, t0:t0 + L]                       # [L,HV,V]
+        be = beta[0, t0:t0 + L].numpy()[:, :, None]
+        TtdE = np.transpose(fi["T"][c, :, :L, :L], (0, 2, 1)) @ it["dE"][c, :, :L]
+        assert np.allclose(dv_c, be * np.transpose(TtdE, (1, 0, 2)), atol=1e-12)
+    got0 = chunked.chunked_bwd(q, k, v, g, beta, do, torch.zeros_like(dht), chunk_size=8,
+                               intermediates=True, **kw)
+    for n in range(4):
+        if lengths[n]:
+            last = got0["inter"]["off"][n + 1] - 1
+            assert np.allclose(got0["inter"]["dE"][last], got0["inter"]["dEi"][last], atol=1e-14)
