@@ -9,6 +9,7 @@ the calls raise.
     o, ht = chunk_fwd(q, k, v, g, beta, scale=1.0, chunk_size=64,
                       cu_seqlens=None, initial_state=None,
                       output_final_state=True, use_qk_l2norm_in_kernel=False)
+    dq, dk, dv, dg, dbeta, dh0 = chunk_bwd(q, k, v, g, beta, do, dht, ...)
 
 Shapes follow the library: q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV] (or
 [B,T,HV,K] for a per-channel gate) and beta [B,T,HV] in float32; initial_state
@@ -30,7 +31,7 @@ GDR_BF16, GDR_FP32 = 0, 1
 STATUS = {
     0: "GDR_OK", 1: "GDR_ERR_NULL_ARG", 2: "GDR_ERR_CHUNK_SIZE", 3: "GDR_ERR_SHAPE",
     4: "GDR_ERR_VARLEN", 5: "GDR_ERR_DTYPE", 6: "GDR_ERR_ALIGNMENT", 7: "GDR_ERR_WORKSPACE",
-    8: "GDR_ERR_HIP", 9: "GDR_ERR_CU_SEQLENS",
+    8: "GDR_ERR_HIP", 9: "GDR_ERR_CU_SEQLENS", 10: "GDR_ERR_UNSUPPORTED",
 }
 
 
@@ -47,6 +48,11 @@ class GdrFwdLayout(ctypes.Structure):
                 ("chunk_off", ctypes.c_size_t), ("Tm", ctypes.c_size_t), ("w", ctypes.c_size_t),
                 ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
                 ("kscale", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+class GdrBwdLayout(ctypes.Structure):
+    _fields_ = [("fwd", GdrFwdLayout), ("de_local", ctypes.c_size_t), ("qscale", ctypes.c_size_t),
+                ("dh", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class GdrError(RuntimeError):
@@ -80,9 +86,17 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
         L.gdr_fwd_h.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
+        L.gdr_bwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.gdr_bwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrBwdLayout)]
+        L.gdr_chunk_bwd.argtypes = [PP] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
+        L.gdr_bwd_intra.argtypes = [PP] + [_P] * 8 + [_P]
+        L.gdr_bwd_dh.argtypes = [PP] + [_P] * 12 + [_P]
+        L.gdr_bwd_dqkvg.argtypes = [PP] + [_P] * 17 + [_P]
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
-                     "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o"):
+                     "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o",
+                     "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
+                     "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -132,6 +146,12 @@ def check_problem(p: GdrProblem) -> None:
 def fwd_layout(p: GdrProblem) -> GdrFwdLayout:
     lay = GdrFwdLayout()
     _raise(lib().gdr_fwd_workspace_layout(ctypes.byref(p), ctypes.byref(lay)))
+    return lay
+
+
+def bwd_layout(p: GdrProblem) -> GdrBwdLayout:
+    lay = GdrBwdLayout()
+    _raise(lib().gdr_bwd_workspace_layout(ctypes.byref(p), ctypes.byref(lay)))
     return lay
 
 
@@ -261,3 +281,94 @@ def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht, kscale=None):
 def fwd_o(p, q, k, v_new, h, g, chunk_idx, chunk_off, o):
     _raise(lib().gdr_fwd_o(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g),
                            _ptr(chunk_idx), _ptr(chunk_off), _ptr(o), _stream(q.device)))
+
+
+# ---- backward
+
+def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size: int = 64,
+              cu_seqlens=None, initial_state=None, use_qk_l2norm_in_kernel: bool = False,
+              workspace: Optional[torch.Tensor] = None, return_workspace: bool = False,
+              out=None, want_dh0: bool = True, validate_cu: bool = True):
+    """Backward of the chunked gated delta rule: gradients of
+    sum(o * do) + sum(ht * dht).  Returns (dq, dk, dv, dg, dbeta, dh0) (dh0 None
+    when not wanted), plus the workspace when ``return_workspace``.  ``out``
+    supplies the six output tensors."""
+    _need_gpu(q, k, v, g, beta, do, dht, cu_seqlens, initial_state)
+    if k.dtype != q.dtype or v.dtype != q.dtype or do.dtype != q.dtype:
+        raise ValueError("q, k, v and do must share one dtype")
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("dht", dht)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+    lay = bwd_layout(p)
+    check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
+    _expect("do", do, v.shape)
+    _expect("dht", dht, (p.N, p.HV, p.K, p.V))
+    if out is not None:
+        dq, dk, dv, dg, dbeta, dh0 = out
+        _need_gpu(dq, dk, dv, dg, dbeta, dh0)
+        for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v), ("dg", dg, g), ("dbeta", dbeta, beta)):
+            _expect(name, t, ref.shape)
+            if t.dtype != ref.dtype:
+                raise ValueError(f"{name} must have dtype {ref.dtype}")
+        _expect("dh0", dh0, (p.N, p.HV, p.K, p.V))
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+        dh0 = (torch.empty(p.N, p.HV, p.K, p.V, dtype=torch.float32, device=q.device)
+               if want_dh0 else None)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gdr_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(workspace),
+                             ctypes.c_size_t(workspace.numel()), _stream(q.device))
+    _raise(st)
+    res = (dq, dk, dv, dg, dbeta, dh0)
+    if return_workspace:
+        return res + (workspace,)
+    return res
+
+
+def bwd_workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
+    """Typed views of the backward's intermediates (forward ones included)."""
+    lay = bwd_layout(p)
+    views = workspace_views(p, ws)
+    nt, C, HV, K, V = lay.fwd.nt_max, p.chunk_size, p.HV, p.K, p.V
+    dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
+    es = 2 if p.dtype == GDR_BF16 else 4
+
+    def view(off, shape, dtype, esize):
+        n = 1
+        for s_ in shape:
+            n *= s_
+        return ws[off:off + n * esize].view(dtype).view(*shape)
+
+    views.update(
+        de_local=view(lay.de_local, (nt, HV, V, C), dt, es),
+        qscale=view(lay.qscale, (nt, HV, C), torch.float32, 4),
+        dh=view(lay.dh, (nt, HV, V, K), dt, es),
+    )
+    return views
+
+
+# ---- the backward's stages one by one
+
+def bwd_intra(p, q, k, g, do, chunk_idx, chunk_off, de_local, qscale):
+    _raise(lib().gdr_bwd_intra(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(g), _ptr(do), _ptr(chunk_idx),
+                               _ptr(chunk_off), _ptr(de_local), _ptr(qscale), _stream(q.device)))
+
+
+def bwd_dh(p, q, k, w, do, de_local, qscale, kscale, chunk_idx, chunk_off, dht, dh, dh0):
+    _raise(lib().gdr_bwd_dh(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), _ptr(do), _ptr(de_local),
+                            _ptr(qscale), _ptr(kscale), _ptr(chunk_idx), _ptr(chunk_off), _ptr(dht),
+                            _ptr(dh), _ptr(dh0), _stream(q.device)))
+
+
+def bwd_dqkvg(p, q, k, v, g, beta, do, Tm, h, v_new, dh, chunk_idx, chunk_off, dq, dk, dv, dg, dbeta):
+    _raise(lib().gdr_bwd_dqkvg(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(do),
+                               _ptr(Tm), _ptr(h), _ptr(v_new), _ptr(dh), _ptr(chunk_idx), _ptr(chunk_off),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _stream(q.device)))

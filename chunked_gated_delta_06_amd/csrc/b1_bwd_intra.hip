@@ -1,0 +1,169 @@
+// B1: chunk-local part of the value gradient (bwd, intra-chunk).
+//
+// Backward of o = scale [ diag(exp(G)) Q^ h + (Q^ K^T o M) E ] with respect to
+// the corrected values E of the same chunk:
+//   de_local = scale P^T dO,   P[r][t] = q^_r . k^_t exp(G_r - G_t)  (t <= r)
+// and the row factors of the inter term that the reverse state scan needs:
+//   qscale[r] = scale exp(G_r) / |q_r|          (0 past the chunk end)
+// (chunk form of the coverage-matrix page, "FLA operator-kernel correctness
+// testing and coverage matrix", section 2, differentiated through o).
+//
+// gfx950 mapping: one workgroup per (chunk, value head), wave w owns tokens
+// t = 16 w .. 16 w + 15 of de_local.  The wave computes its column blocks of
+// P from the raw bf16 q / k rows on MFMA, applies norms, gate and causal mask
+// in fp32 and feeds the accumulators as the A operand (rows t) of
+// de_local = P^T dO in the "chained" contraction map, as a bf16 hi + lo pair;
+// dO is staged through LDS 32 value columns at a time and read with
+// transposed LDS reads.  The result leaves each lane four consecutive tokens
+// of one value column, which is the transposed per-chunk layout of
+// de_local, written with 8-byte stores.
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+template <typename T, int C, int K>
+__global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
+  constexpr int NB = C / 16;
+  constexpr int NT = 64 * NB;
+  constexpr int KSK = K / 32;
+  constexpr int KSC = C / 32;
+  constexpr int VT = 32;                          // value columns per pass
+  constexpr int DP = VT + 32 / sizeof(T);         // LDS pitch of dO rows
+  constexpr int NPD = VT * C / 8 / NT;            // 8-element dO pieces per thread (= 1)
+  static_assert(NPD * NT * 8 == VT * C, "dO tile pieces");
+  __shared__ float sG[C], sRq[C], sRk[C];
+  __shared__ __attribute__((aligned(16))) T sDO[C * DP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int64_t c = blockIdx.x, j = blockIdx.y;
+  if (c >= a.chunk_off[a.N]) return;
+  const int64_t t0 = a.chunk_idx[4 * c + 1];
+  const int L = a.chunk_idx[4 * c + 2];
+  const int64_t H = a.H, HV = a.HV, V = a.V, h = j / (HV / H);
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ dop = static_cast<const T*>(a.d_o);
+  T* __restrict__ dep = static_cast<T*>(a.de_local) + (c * HV + j) * V * (int64_t)C;
+
+  auto row8 = [&](const T* base, int row, int ks) -> Frag<T> {
+    if (row < L) return ld8(base + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
+    return frag_zero<T>();
+  };
+
+  // dO tile (rows t, VT value columns from v0), fetched into registers early
+  Frag<T> dreg[NPD];
+  auto fetch_tile = [&](int64_t v0) {
+#pragma unroll
+    for (int i = 0; i < NPD; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      dreg[i] = (t < L) ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
+    }
+  };
+  auto stage_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPD; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      st8(&sDO[t * DP + v8], dreg[i]);
+    }
+  };
+  fetch_tile(0);
+
+  // ---- gate cumsum and norms
+  if (wv == 0) {
+    const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+    const float G = wave_incl_scan(gv, lane);
+    if (lane < C) sG[lane] = G;
+  }
+  const int rr = 16 * wv + r16;
+  {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) {
+      const f32x8 xq = row8(qp, rr, ks).f32(), xk = row8(kp, rr, ks).f32();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += xq[e] * xq[e];
+        sk += xk[e] * xk[e];
+      }
+    }
+    sq = group4_sum(sq);
+    sk = group4_sum(sk);
+    if (g4 == 0) {
+      sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+      sRk[rr] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+    }
+  }
+  lds_barrier();
+  if (g4 == 0)
+    a.qscale[(c * HV + j) * C + rr] = (rr < L) ? a.scale * __expf(sG[rr]) * sRq[rr] : 0.f;
+
+  // ---- P blocks (r-block rb, t-block wv) for rb >= wv: acc[i] = P[16 rb + 4 g + i][16 wv + l % 16]
+  const int tt = 16 * wv + r16;           // this lane's token column of P
+  const float rkt = sRk[tt], Gt = sG[tt];
+  f32x4 Pa[NB];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb) {
+    Pa[rb] = zero4();
+    if (rb < wv) continue;
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) mma(Pa[rb], row8(qp, 16 * rb + r16, ks), row8(kp, tt, ks));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rb + 4 * g4 + i;
+      Pa[rb][i] *= (tt <= r && r < L) ? sRq[r] * rkt * __expf(sG[r] - Gt) : 0.f;
+    }
+  }
+  // P^T rows t as A operands over the chained r map, as hi + lo pairs
+  SplitFrag<T> Pf[KSC];
+#pragma unroll
+  for (int s = 0; s < KSC; ++s) Pf[s] = SplitFrag<T>::make(cat8(Pa[2 * s], Pa[2 * s + 1]));
+
+  // ---- de_local^T[v][t] = scale sum_r P[r][t] dO[r][v]
+  const float sc = a.scale;
+  for (int64_t v0 = 0; v0 < V; v0 += VT) {
+    stage_tile();
+    lds_barrier();
+    if (v0 + VT < V) fetch_tile(v0 + VT);
+#pragma unroll
+    for (int vb = 0; vb < VT / 16; ++vb) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (2 * s + 1 < wv) continue;     // r < 16 wv in the whole slab: P is zero
+        mma_split(acc, Pf[s], lds_tr_frag(sDO, DP, 32 * s + 4 * g4, 32 * s + 16 + 4 * g4, 16 * vb, lane));
+      }
+      // acc[i] = de_local[16 wv + 4 g + i][v0 + 16 vb + l % 16]
+      st4(dep + (v0 + 16 * vb + r16) * C + 16 * wv + 4 * g4, acc * sc);
+    }
+    lds_barrier();
+  }
+}
+
+template <typename T, int C>
+hipError_t launch_k(const Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.NTmax, (unsigned)a.HV);
+  switch (a.K) {
+    case 32: hipLaunchKernelGGL((b1_bwd_intra<T, C, 32>), grid, dim3(C * 4), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((b1_bwd_intra<T, C, 64>), grid, dim3(C * 4), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((b1_bwd_intra<T, C, 128>), grid, dim3(C * 4), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_c(const Args& a, hipStream_t s) {
+  return a.C == 32 ? launch_k<T, 32>(a, s) : launch_k<T, 64>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_intra(const Args& a, hipStream_t s) {
+  if (a.NTmax == 0) return hipSuccess;
+  return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+}  // namespace gdr

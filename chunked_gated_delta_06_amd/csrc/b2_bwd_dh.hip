@@ -1,0 +1,341 @@
+// B2: reverse state-gradient scan (bwd_dhu).
+//
+// For each sequence n and value head j, dS (K x V, fp32) starts at dht (or 0)
+// and runs over the chunks from last to first:
+//   dh[c] = dS                                   (gradient of the state leaving
+//            chunk c: the hand-off of the KCP page, "flash-linear-attention
+//            KCP precision-failure root-cause manual", section "h and dh
+//            cross-rank semantics", which passes dht back to the previous rank)
+//   dE    = de_local + diag(kscale) K dS         (gradient of the chunk's e)
+//   dS   <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE
+// and dh0 = dS at the end, with kscale[t] = exp(G_L - G_t) / |k_t| and
+// qscale[r] = scale exp(G_r) / |q_r|.  This is the transpose of the forward
+// recursion S <- exp(G_L) S + K~^T (U - W S) of the chunk form on the
+// coverage-matrix page ("FLA operator-kernel correctness testing and coverage
+// matrix", section 2) plus the inter term of o.
+//
+// gfx950 mapping (as the forward scan): one workgroup per (sequence, value
+// head, 32 value columns).  Two compute waves own 16 columns of dS each as
+// K/16 fp32 MFMA accumulators; NWL loader waves fetch each chunk's k, q, w,
+// dO, de_local and kscale into registers three steps ahead and stage them into
+// LDS (two buffers when they fit, else one with a second barrier per step);
+// dO is multiplied by qscale while it is staged.  dE = K dS takes dS straight
+// from its accumulators as the B operand (chained contraction map); the dS
+// update reads q^T and w^T with transposed LDS reads.
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+template <typename T, int C, int K, int NWL>
+struct B2S {
+  static constexpr int NWC = 2;
+  static constexpr int NTL = 64 * NWL;
+  static constexpr int BV = 16 * NWC;
+  static constexpr int NE = C / 16, NS = K / 16, KSK = K / 32, KSC = C / 32;
+  static constexpr int CPR = K / 8;
+  static constexpr int NPW = C * CPR;                   // 8-element pieces of a C x K tile
+  static constexpr int NLD = (NPW + NTL - 1) / NTL;
+  static constexpr int NPO = C * BV / 8;                // dO pieces
+  static constexpr int NLO = (NPO + NTL - 1) / NTL;
+  static constexpr int NPE = BV * C / 8;                // de_local pieces
+  static constexpr int NLE = (NPE + NTL - 1) / NTL;
+  static constexpr int NKS = (C + 4) / 4;
+  static constexpr int KR = K + 16 / sizeof(T);         // k rows (row reads)
+  static constexpr int KP = K + 32 / sizeof(T);         // q, w rows (transposed reads)
+  static constexpr int OP = BV + 32 / sizeof(T);        // scaled dO rows (transposed reads)
+  static constexpr int EP = C + 8 / sizeof(T);          // de_local rows (one per value column)
+  static constexpr size_t buf_bytes =
+      ((size_t)C * (KR + 2 * KP) + (size_t)C * OP + (size_t)BV * EP) * sizeof(T) + (C + 4) * 4;
+  static constexpr int NBUF = 2 * buf_bytes <= 160 * 1024 ? 2 : 1;
+  static constexpr bool fits = NBUF * buf_bytes <= 160 * 1024 && NKS <= NTL;
+
+  struct Regs {
+    Frag<T> k[NLD], q[NLD], w[NLD];
+    Frag<T> o[NLO];
+    float qs[NLO];
+    Frag<T> e[NLE];
+    f32x4 ks;
+  };
+  struct Smem {
+    T k[NBUF][C * KR];
+    T q[NBUF][C * KP];
+    T w[NBUF][C * KP];
+    T o[NBUF][C * OP];
+    T e[NBUF][BV * EP];
+    float ks[NBUF][C + 4];
+  };
+};
+
+template <typename T, int C, int K, int NWL>
+__global__ __launch_bounds__(64 * (2 + NWL)) void b2_bwd_dh(Args a) {
+  using Cfg = B2S<T, C, K, NWL>;
+  using Regs = typename Cfg::Regs;
+  constexpr int NWC = Cfg::NWC, NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS;
+  constexpr int KSK = Cfg::KSK, KSC = Cfg::KSC, CPR = Cfg::CPR, NLD = Cfg::NLD, NLO = Cfg::NLO;
+  constexpr int NLE = Cfg::NLE, NKS = Cfg::NKS, NPW = Cfg::NPW, NPO = Cfg::NPO, NPE = Cfg::NPE;
+  constexpr int KR = Cfg::KR, KP = Cfg::KP, OP = Cfg::OP, EP = Cfg::EP, NBUF = Cfg::NBUF;
+  __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const bool loader = wv >= NWC;
+  const int tl = tid - 64 * NWC;
+  const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
+  const int64_t nvt = V / BV;
+  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t vt = bid % nvt, j = (bid / nvt) % HV, n = bid / (nvt * HV);
+  if (n >= N) return;
+  const int64_t h = j / (HV / H);
+  const int64_t vw = vt * BV;
+  const int64_t v0 = vw + 16 * wv;
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ wbase = static_cast<const T*>(a.w);
+  const T* __restrict__ dop = static_cast<const T*>(a.d_o);
+  const T* __restrict__ debase = static_cast<const T*>(a.de_local);
+  T* __restrict__ dhbase = static_cast<T*>(a.dh);
+
+  const int64_t c_begin = a.chunk_off[n];
+  const int nc = a.chunk_off[n + 1] - (int)c_begin;
+  const int64_t c_last = c_begin + (nc > 0 ? nc - 1 : 0);
+  // step x works on chunk c_last - x; indices past the first chunk are clamped
+  // to it (those copies are staged but never computed)
+  auto chunk_at = [&](int x) -> int64_t { return x < nc ? c_last - x : c_begin; };
+  const int64_t seq_t0 = nc > 0 ? a.chunk_idx[4 * c_begin + 1] : 0;
+  const int64_t seq_end = nc > 0 ? a.chunk_idx[4 * c_last + 1] + a.chunk_idx[4 * c_last + 2] : 0;
+
+  auto fetch = [&](Regs& R, int64_t c) {
+    const int64_t t0 = seq_t0 + (c - c_begin) * C;
+    const int L = (int)((seq_end - t0) < C ? (seq_end - t0) : C);
+    const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
+    const T* krow = kp + (t0 * H + h) * K;
+    const T* qrow = qp + (t0 * H + h) * K;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      const bool in = (NPW % NTL == 0) || idx < NPW;
+      const int tc = t < L ? t : L - 1;
+      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
+      const Frag<T> qr = ld8(qrow + (tc * (int)(H * K) + d8));
+      R.w[i] = in ? ld8(wp + 8 * idx) : frag_zero<T>();
+      R.k[i] = (in && t < L) ? kr : frag_zero<T>();
+      R.q[i] = (in && t < L) ? qr : frag_zero<T>();
+    }
+    const T* orow = dop + (t0 * HV + j) * V + vw;
+    const float* qsp = a.qscale + (c * HV + j) * (int64_t)C;
+#pragma unroll
+    for (int i = 0; i < NLO; ++i) {
+      const int idx = tl + NTL * i, t = idx / (BV / 8), v8 = (idx % (BV / 8)) * 8;
+      const bool in = (NPO % NTL == 0) || idx < NPO;
+      const int tc = t < L ? t : L - 1;
+      const Frag<T> orr = ld8(orow + (tc * (int)(HV * V) + v8));
+      R.o[i] = (in && t < L) ? orr : frag_zero<T>();
+      R.qs[i] = qsp[t < C ? t : C - 1];
+    }
+    const T* ep = debase + ((c * HV + j) * V + vw) * (int64_t)C;
+#pragma unroll
+    for (int i = 0; i < NLE; ++i) {
+      const int idx = tl + NTL * i;
+      R.e[i] = ((NPE % NTL == 0) || idx < NPE) ? ld8(ep + 8 * idx) : frag_zero<T>();
+    }
+    const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+    R.ks = (tl < NKS) ? *reinterpret_cast<const f32x4*>(ksp + 4 * tl) : zero4();
+  };
+  auto stage = [&](const Regs& R, int b) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      if ((NPW % NTL == 0) || idx < NPW) {
+        st8(&sm.k[b][t * KR + d8], R.k[i]);
+        st8(&sm.q[b][t * KP + d8], R.q[i]);
+        st8(&sm.w[b][t * KP + d8], R.w[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NLO; ++i) {
+      const int idx = tl + NTL * i, t = idx / (BV / 8), v8 = (idx % (BV / 8)) * 8;
+      if ((NPO % NTL == 0) || idx < NPO) st8(&sm.o[b][t * OP + v8], Frag<T>::make(R.o[i].f32() * R.qs[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < NLE; ++i) {
+      const int idx = tl + NTL * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+      if ((NPE % NTL == 0) || idx < NPE) st8(&sm.e[b][v * EP + t8], R.e[i]);
+    }
+    if (tl < NKS) *reinterpret_cast<f32x4*>(&sm.ks[b][4 * tl]) = R.ks;
+  };
+
+  // Loader and compute waves run separate loops with the same barrier
+  // sequence.  Step x lives in register slot x % 3 and LDS buffer x % NBUF; at
+  // step s the compute waves work on step s while the loaders stage step s + 1
+  // (after a second barrier when there is one buffer) and fetch step s + 4.
+  if (loader) {
+    if (nc > 0) {
+      Regs R0, R1, R2;
+      fetch(R0, chunk_at(0));
+      fetch(R1, chunk_at(1));
+      fetch(R2, chunk_at(2));
+      stage(R0, 0);
+      fetch(R0, chunk_at(3));
+      lds_barrier();
+      for (int s0 = 0; s0 < nc; s0 += 3) {
+        if constexpr (NBUF == 1) lds_barrier();
+        stage(R1, (s0 + 1) % NBUF);
+        fetch(R1, chunk_at(s0 + 4));
+        lds_barrier();
+        if constexpr (NBUF == 1) lds_barrier();
+        stage(R2, (s0 + 2) % NBUF);
+        fetch(R2, chunk_at(s0 + 5));
+        lds_barrier();
+        if constexpr (NBUF == 1) lds_barrier();
+        stage(R0, (s0 + 3) % NBUF);
+        fetch(R0, chunk_at(s0 + 6));
+        lds_barrier();
+      }
+    }
+    return;
+  }
+
+  // ---- compute waves: dS rows 16 mb + 4 g4 + i, column v0 + r16
+  f32x4 S[NS];
+#pragma unroll
+  for (int mb = 0; mb < NS; ++mb) {
+    if (a.dht != nullptr) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[mb][i] = a.dht[((n * HV + j) * K + 16 * mb + 4 * g4 + i) * V + v0 + r16];
+    } else {
+      S[mb] = zero4();
+    }
+  }
+  auto compute = [&](int64_t c, int b) {
+    Frag<T> kf[KSK][NE];
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < NE; ++eb) {
+        const T* row = &sm.k[b][(16 * eb + r16) * KR];
+        kf[ks][eb] = ld_chain(row + 32 * ks + 4 * g4, row + 32 * ks + 16 + 4 * g4);
+      }
+    f32x4 sc[NE], dl[NE];
+    const T* erow = &sm.e[b][(16 * wv + r16) * EP];
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) {
+      sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
+      dl[eb] = ld4f(erow + 16 * eb + 4 * g4);
+    }
+    const float gl = sm.ks[b][C];
+    // dh[c] = dS (transposed, 4 features per lane)
+    T* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb) st4(hp + (r16 * K + 16 * mb + 4 * g4), S[mb]);
+    // dE = de_local + diag(kscale) K dS
+    Frag<T> Sf[KSK];
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) Sf[ks] = frag_from_halves<T>(S[2 * ks], S[2 * ks + 1]);
+    f32x4 E[NE];
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) E[eb] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < NE; ++eb) mma(E[eb], kf[ks][eb], Sf[ks]);
+    Frag<T> nE[KSC];
+#pragma unroll
+    for (int kt = 0; kt < KSC; ++kt)
+      nE[kt] = frag_from_halves<T>(-(E[2 * kt] * sc[2 * kt] + dl[2 * kt]),
+                                   -(E[2 * kt + 1] * sc[2 * kt + 1] + dl[2 * kt + 1]));
+    // dS <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb)
+#pragma unroll
+      for (int kt = 0; kt < KSC; ++kt) {
+        const int r0 = 32 * kt + 4 * g4, r1 = 32 * kt + 16 + 4 * g4;
+        mma(S[mb], lds_tr_frag(&sm.q[b][0], KP, r0, r1, 16 * mb, lane),
+            lds_tr_frag(&sm.o[b][0], OP, r0, r1, 16 * wv, lane));
+        mma(S[mb], lds_tr_frag(&sm.w[b][0], KP, r0, r1, 16 * mb, lane), nE[kt]);
+      }
+  };
+
+  if (nc > 0) {
+    lds_barrier();
+    for (int s0 = 0; s0 < nc; s0 += 3) {
+      compute(chunk_at(s0), s0 % NBUF);
+      lds_barrier();
+      if constexpr (NBUF == 1) lds_barrier();
+      if (s0 + 1 < nc) compute(chunk_at(s0 + 1), (s0 + 1) % NBUF);
+      lds_barrier();
+      if constexpr (NBUF == 1) lds_barrier();
+      if (s0 + 2 < nc) compute(chunk_at(s0 + 2), (s0 + 2) % NBUF);
+      lds_barrier();
+      if constexpr (NBUF == 1) lds_barrier();
+    }
+  }
+  if (a.dh0 != nullptr) {
+#pragma unroll
+    for (int mb = 0; mb < NS; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.dh0[((n * HV + j) * K + 16 * mb + 4 * g4 + i) * V + v0 + r16] = S[mb][i];
+  }
+}
+
+template <typename T, int C, int K>
+constexpr int loader_waves() {
+  // about 150 VGPRs of prefetch per loader thread (three payloads of three
+  // C x K tiles)
+  constexpr int x = (int)sizeof(T) * C * K / 4096;
+  return x < 2 ? 2 : (x > 8 ? 8 : x);
+}
+
+template <typename T, int C, int K>
+hipError_t launch_t(const Args& a, hipStream_t s) {
+  constexpr int NWL = loader_waves<T, C, K>();
+  if constexpr (!B2S<T, C, K, NWL>::fits) {
+    return hipErrorInvalidValue;    // rejected on the host before any launch
+  } else {
+    const int64_t nblk = a.N * a.HV * (a.V / 32);
+    hipLaunchKernelGGL((b2_bwd_dh<T, C, K, NWL>), dim3((unsigned)nblk), dim3(64 * (2 + NWL)), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int C>
+hipError_t launch_k(const Args& a, hipStream_t s) {
+  switch (a.K) {
+    case 32: return launch_t<T, C, 32>(a, s);
+    case 64: return launch_t<T, C, 64>(a, s);
+    case 128: return launch_t<T, C, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_c(const Args& a, hipStream_t s) {
+  return a.C == 32 ? launch_k<T, 32>(a, s) : launch_k<T, 64>(a, s);
+}
+
+}  // namespace
+
+bool bwd_scan_fits(int dtype, int C, int K) {
+  bool ok = false;
+#define GDR_B2_FITS(TT, CC, KK) \
+  if (C == CC && K == KK) ok = B2S<TT, CC, KK, loader_waves<TT, CC, KK>()>::fits;
+  if (dtype == GDR_BF16) {
+    GDR_B2_FITS(bf16, 32, 32) GDR_B2_FITS(bf16, 32, 64) GDR_B2_FITS(bf16, 32, 128)
+    GDR_B2_FITS(bf16, 64, 32) GDR_B2_FITS(bf16, 64, 64) GDR_B2_FITS(bf16, 64, 128)
+  } else {
+    GDR_B2_FITS(float, 32, 32) GDR_B2_FITS(float, 32, 64) GDR_B2_FITS(float, 32, 128)
+    GDR_B2_FITS(float, 64, 32) GDR_B2_FITS(float, 64, 64) GDR_B2_FITS(float, 64, 128)
+  }
+#undef GDR_B2_FITS
+  return ok;
+}
+
+hipError_t launch_bwd_dh(const Args& a, hipStream_t s) {
+  if (a.N == 0) return hipSuccess;
+  return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+}  // namespace gdr

@@ -1,0 +1,593 @@
+// B3: fused chunk-parallel backward (bwd_o + bwd_wy + bwd_dqk_intra).
+//
+// Per chunk (L rows), q/k head h and each value head j of its group, with S0 =
+// h[c] (state entering the chunk), dS1 = dh[c] (gradient of the state leaving
+// it), E = v_new, T = (I + A)^-1, gate G (chunk-local cumsum), gamma = exp(G),
+// kappa = exp(G_L - G), row norms rq, rk and P[r][t] = q^_r . k^_t exp(G_r - G_t)
+// (t <= r), the gradients of the chunk form on the coverage-matrix page ("FLA
+// operator-kernel correctness testing and coverage matrix", section 2) are
+//   dE   = scale P^T dO + diag(kappa) K^ dS1       (gradient of E)
+//   Y    = T^T dE                                  dv = diag(beta) Y
+//   dQg  = scale dO S0^T     T^T dW = -Y S0^T      dKt = E dS1^T
+//   dP   = scale dO E^T      dA = -Y E^T (strictly lower)
+// where dA = -T^T dT T^T collapses to -Y E^T because
+// beta (V - diag(gamma) K^ S0) = (I + A) E, so the WY factors' gradient dT
+// never has to be formed.  Then
+//   dq^ = gamma dQg + D K^,               D[r][t] = dP[r][t] exp(G_r - G_t)
+//   dk^ = kappa dKt + beta gamma T^T dW + D^T Q^ + Dk K^ + Dk^T K^,
+//         Dk[t][m] = beta_t dA[t][m] exp(G_t - G_m)
+//   dbeta_t = gamma_t k^_t . (T^T dW)_t + v_t . Y_t + sum_m dA[t][m] Abar[t][m]
+//   dG (per row) from every exp(G) factor, dg = reverse cumsum of dG in the
+//   chunk; finally the group sum over value heads (GVA) and the L2-norm
+//   backward dx = (dx^ - x^ (x^ . dx^)) / |x|.
+//
+// gfx950 mapping: one workgroup (4 waves) per (chunk, q/k head); value heads
+// of a GVA group run one after the other and sum dq^, dk^ in registers.
+// Every operand sits in LDS as a row-major tile; MFMA fragments use the row
+// contraction map and come from 16-byte row reads or ds_read_b64_tr_b16
+// column reads, so any product (A or A^T times B or B^T) is one code path.
+// fp32 intermediates that feed MFMAs (P, dE, Y, D, Dk) are kept as bf16 hi + lo
+// pairs.  The value dimension is streamed in tiles of 32 columns: per tile the
+// kernel stages h^T, dh^T, dO, v and e^T, forms dE and Y (writing dv) and
+// accumulates the C x K and C x C products above in registers; a wave owns a
+// fixed set of 16 x 16 output blocks for the whole chunk.
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+namespace {
+
+template <typename T, int C, int K>
+struct B3 {
+  static constexpr int NT = 256;
+  static constexpr int VT = 32;
+  static constexpr int EB = sizeof(T);
+  static constexpr int PK = K + 32 / EB;     // q, k, h^T, dh^T rows
+  static constexpr int PC = C + 32 / EB;     // T, e^T, P^T, D rows
+  static constexpr int PV = VT + 32 / EB;    // dO, v, dE, Y rows
+  static constexpr int NRB = C / 16, NKB = K / 16, NVB = VT / 16;
+  static constexpr int KSK = K / 32, KSC = C / 32;
+  static constexpr int SCK = NRB * NKB / 4;  // C x K blocks per wave
+  static constexpr int SCC = NRB * NRB / 4;  // C x C blocks per wave
+  static constexpr int SCV = NRB * NVB / 4;  // C x VT blocks per wave
+  static_assert(SCK * 4 == NRB * NKB && SCC * 4 == NRB * NRB && SCV * 4 == NRB * NVB, "block split");
+  // LDS byte offsets
+  static constexpr size_t oQ = 0;
+  static constexpr size_t oK = oQ + (size_t)C * PK * EB;
+  static constexpr size_t oT = oK + (size_t)C * PK * EB;
+  static constexpr size_t oLoop = oT + (size_t)C * PC * EB;
+  static constexpr size_t FCV = (size_t)C * PV * 4;     // fp32 operand tile C x PV (hi + lo)
+  static constexpr size_t FCC = (size_t)C * PC * 4;     // fp32 operand tile C x PC
+  static constexpr size_t lH = 0;
+  static constexpr size_t lDH = lH + (size_t)VT * PK * EB;
+  static constexpr size_t lDO = lDH + (size_t)VT * PK * EB;
+  static constexpr size_t lV = lDO + (size_t)C * PV * EB;
+  static constexpr size_t lE = lV + (size_t)C * PV * EB;
+  static constexpr size_t lDE = lE + (size_t)VT * PC * EB;
+  static constexpr size_t lY = lDE + FCV;
+  static constexpr size_t lPT = lY + FCV;
+  static constexpr size_t loop_bytes = lPT + FCC;
+  static constexpr size_t pD1 = 0, pD2 = FCC, post_bytes = 2 * FCC;
+  static constexpr size_t oRows = oLoop + (loop_bytes > post_bytes ? loop_bytes : post_bytes);
+  // rows: G, rq, rk, beta; per-wave dG, dbeta, q.dq, k.dk partials; 8 scalars
+  static constexpr size_t rows_floats = 4 * C + 4 * 4 * C + 8;
+  static constexpr size_t total = oRows + rows_floats * 4;
+  static constexpr bool fits = total <= 160 * 1024;
+};
+
+template <typename T, int P>
+GDR_DEV FTile<T> ftile(char* base, int rows) {
+  FTile<T> f;
+  f.hi = reinterpret_cast<T*>(base);
+  f.lo = FTile<T>::kSplit ? reinterpret_cast<T*>(base + (size_t)rows * P * sizeof(T)) : nullptr;
+  f.pitch = P;
+  return f;
+}
+
+template <typename T, int C, int K, bool GVA>
+__global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
+  using Cfg = B3<T, C, K>;
+  constexpr int VT = Cfg::VT, PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV;
+  constexpr int NRB = Cfg::NRB, NVB = Cfg::NVB, KSK = Cfg::KSK, KSC = Cfg::KSC;
+  constexpr int SCK = Cfg::SCK, SCC = Cfg::SCC, SCV = Cfg::SCV;
+  constexpr int CPR = K / 8;
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int64_t c = blockIdx.x, h = blockIdx.y;
+  if (c >= a.chunk_off[a.N]) return;
+  const int64_t t0 = a.chunk_idx[4 * c + 1];
+  const int L = a.chunk_idx[4 * c + 2];
+  const int64_t H = a.H, HV = a.HV, V = a.V;
+  const int ng = (int)(HV / H);
+  const float scale = a.scale;
+
+  T* sQ = reinterpret_cast<T*>(smem + Cfg::oQ);
+  T* sK = reinterpret_cast<T*>(smem + Cfg::oK);
+  T* sT = reinterpret_cast<T*>(smem + Cfg::oT);
+  char* loop = smem + Cfg::oLoop;
+  T* sH = reinterpret_cast<T*>(loop + Cfg::lH);
+  T* sDH = reinterpret_cast<T*>(loop + Cfg::lDH);
+  T* sDO = reinterpret_cast<T*>(loop + Cfg::lDO);
+  T* sV = reinterpret_cast<T*>(loop + Cfg::lV);
+  T* sE = reinterpret_cast<T*>(loop + Cfg::lE);
+  const FTile<T> fDE = ftile<T, PV>(loop + Cfg::lDE, C);
+  const FTile<T> fY = ftile<T, PV>(loop + Cfg::lY, C);
+  const FTile<T> fPT = ftile<T, PC>(loop + Cfg::lPT, C);
+  const FTile<T> fD1 = ftile<T, PC>(loop + Cfg::pD1, C);
+  const FTile<T> fD2 = ftile<T, PC>(loop + Cfg::pD2, C);
+  float* sG = reinterpret_cast<float*>(smem + Cfg::oRows);
+  float* sRq = sG + C;
+  float* sRk = sRq + C;
+  float* sB = sRk + C;
+  float* sRowG = sB + C;          // [4][C]
+  float* sRowB = sRowG + 4 * C;   // [4][C]
+  float* sDotQ = sRowB + 4 * C;   // [4][C]
+  float* sDotK = sDotQ + 4 * C;   // [4][C]
+  float* sRed = sDotK + 4 * C;    // [8]
+
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ vp = static_cast<const T*>(a.v);
+  const T* __restrict__ dop = static_cast<const T*>(a.d_o);
+
+  // ---- q, k tiles (rows past L are zero) and their row norms
+  {
+    constexpr int NP = C * CPR;
+#pragma unroll
+    for (int i = 0; i < (NP + 255) / 256; ++i) {
+      const int idx = tid + 256 * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      const bool in = idx < NP && t < L;
+      const Frag<T> q8 = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+      const Frag<T> k8 = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+      if (idx < NP) {
+        st8(&sQ[t * PK + d8], q8);
+        st8(&sK[t * PK + d8], k8);
+      }
+      const f32x8 xq = q8.f32(), xk = k8.f32();
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += xq[e] * xq[e];
+        sk += xk[e] * xk[e];
+      }
+      sq = lanes_sum(sq, CPR);
+      sk = lanes_sum(sk, CPR);
+      if (idx < NP && d8 == 0) {
+        sRq[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+        sRk[t] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+      }
+    }
+    for (int i = tid; i < 8 * C; i += 256) sDotQ[i] = 0.f;   // sDotQ and sDotK
+  }
+
+  // a wave's fixed output blocks: slot i of a product with NRB row blocks is
+  // block b = wv + 4 i, row block b % NRB (= wv % NRB), column block b / NRB
+  const int rb = wv % NRB;
+  f32x4 dq[SCK], dk[SCK];          // dq^, dk^ of the current value head
+  f32x4 sq_[GVA ? SCK : 1], sk_[GVA ? SCK : 1];
+  if constexpr (GVA) {
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) sq_[i] = sk_[i] = zero4();
+  }
+
+  for (int jj = 0; jj < ng; ++jj) {
+    const int64_t j = h * ng + jj;
+    // ---- per-head rows and the T tile
+    if (wv == 0) {
+      const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+      const float G = wave_incl_scan(gv, lane);
+      if (lane < C) sG[lane] = G;
+    }
+    for (int i = tid; i < C; i += 256) sB[i] = (i < L) ? a.beta[(t0 + i) * HV + j] : 0.f;
+    for (int i = tid; i < 8 * C; i += 256) sRowG[i] = 0.f;     // sRowG and sRowB
+    if (tid < 8) sRed[tid] = 0.f;
+    {
+      const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
+      for (int idx = tid; idx < C * C / 8; idx += 256) {
+        const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+        st8(&sT[r * PC + c8], ld8(tp + 8 * idx));
+      }
+    }
+    lds_barrier();
+    const float GL = sG[L - 1];
+
+    // ---- P^T tile: P^T[t][r] = P[r][t] (norms, gate, causal mask applied)
+#pragma unroll
+    for (int i = 0; i < SCC; ++i) {
+      const int b = wv + 4 * i, tb = b % NRB, cb = b / NRB;
+      f32x4 acc = zero4();
+      if (tb <= cb) {
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          mma(acc, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sQ[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
+      }
+      const int r = 16 * cb + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * tb + 4 * g4 + e;
+        const float f = (t <= r && r < L) ? sRq[r] * sRk[t] * __expf(sG[r] - sG[t]) : 0.f;
+        fPT.put(t, r, acc[e] * f);
+      }
+    }
+
+    f32x4 dQg[SCK], TdW[SCK], dKt[SCK], dP[SCC], dA[SCC];
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) dQg[i] = TdW[i] = dKt[i] = zero4();
+#pragma unroll
+    for (int i = 0; i < SCC; ++i) dP[i] = dA[i] = zero4();
+    float lr = 0.f;     // sum of S0 o dS1 (this thread's share)
+    lds_barrier();
+
+    const T* hbase = static_cast<const T*>(a.h) + (c * HV + j) * V * (int64_t)K;
+    const T* dhbase = static_cast<const T*>(a.dh) + (c * HV + j) * V * (int64_t)K;
+    const T* ebase = static_cast<const T*>(a.v_new) + (c * HV + j) * V * (int64_t)C;
+    for (int64_t v0 = 0; v0 < V; v0 += VT) {
+      // ---- stage the value tile
+      for (int idx = tid; idx < VT * CPR; idx += 256) {
+        const int v = idx / CPR, d8 = (idx % CPR) * 8;
+        const Frag<T> x = ld8(hbase + v0 * K + 8 * idx);
+        const Frag<T> y = ld8(dhbase + v0 * K + 8 * idx);
+        st8(&sH[v * PK + d8], x);
+        st8(&sDH[v * PK + d8], y);
+        const f32x8 fx = x.f32(), fy = y.f32();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lr += fx[e] * fy[e];
+      }
+      for (int idx = tid; idx < C * VT / 8; idx += 256) {
+        const int t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+        const bool in = t < L;
+        st8(&sDO[t * PV + v8], in ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>());
+        st8(&sV[t * PV + v8], in ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>());
+      }
+      for (int idx = tid; idx < VT * C / 8; idx += 256) {
+        const int v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+        st8(&sE[v * PC + t8], ld8(ebase + v0 * C + 8 * idx));
+      }
+      lds_barrier();
+
+      // ---- dE[t][v] = scale (P^T dO)[t][v] + kappa_t rk_t (K dS1)[t][v]
+#pragma unroll
+      for (int i = 0; i < SCV; ++i) {
+        const int b = wv + 4 * i, tb = b % NRB, vb = b / NRB;
+        f32x4 a1 = zero4(), a2 = zero4();
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          if (32 * s + 31 < 16 * tb) continue;
+          mma_split(a1, fPT.row(16 * tb + r16, 32 * s, lane), lds_col8(sDO, PV, 32 * s, 16 * vb, lane));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          mma(a2, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sDH[(16 * vb + r16) * PK + 32 * ks + 8 * g4]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * tb + 4 * g4 + e;
+          const float ks = (t < L) ? __expf(GL - sG[t]) * sRk[t] : 0.f;
+          fDE.put(t, 16 * vb + r16, scale * a1[e] + ks * a2[e]);
+        }
+      }
+      lds_barrier();
+
+      // ---- Y^T[v][t] = (dE^T T)[v][t]; dv = beta Y; dbeta += v . Y
+#pragma unroll
+      for (int i = 0; i < SCV; ++i) {
+        const int b = wv + 4 * i, vb = b % NVB, tb = b / NVB;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          if (32 * s + 31 < 16 * tb) continue;
+          mma_split(acc, fDE.col(32 * s, 16 * vb, lane), lds_col8(sT, PC, 32 * s, 16 * tb, lane));
+        }
+        const int t = 16 * tb + r16, vc = 16 * vb + 4 * g4;
+        if (t < L) st4(static_cast<T*>(a.dv) + ((t0 + t) * HV + j) * V + v0 + vc, acc * sB[t]);
+        const f32x4 vv = ld4f(&sV[t * PV + vc]);
+        const float p = group4_sum(acc[0] * vv[0] + acc[1] * vv[1] + acc[2] * vv[2] + acc[3] * vv[3]);
+        if (g4 == 0) sRowB[wv * C + t] += p;
+        fY.put4(t, vc, acc);
+      }
+      lds_barrier();
+
+      // ---- products over this tile's 32 value columns
+      {
+        const Frag<T> aO = ld8(&sDO[(16 * rb + r16) * PV + 8 * g4]);
+        const SplitFrag<T> aY = fY.row(16 * rb + r16, 0, lane);
+        const Frag<T> aE = lds_col8(sE, PC, 0, 16 * rb, lane);
+#pragma unroll
+        for (int i = 0; i < SCK; ++i) {
+          const int db = (wv + 4 * i) / NRB;
+          const Frag<T> bS = lds_col8(sH, PK, 0, 16 * db, lane);
+          const Frag<T> bD = lds_col8(sDH, PK, 0, 16 * db, lane);
+          mma(dQg[i], aO, bS);
+          mma_split(TdW[i], aY, bS);
+          mma(dKt[i], aE, bD);
+        }
+#pragma unroll
+        for (int i = 0; i < SCC; ++i) {
+          const int cb = (wv + 4 * i) / NRB;
+          const Frag<T> bE = lds_col8(sE, PC, 0, 16 * cb, lane);
+          mma(dP[i], aO, bE);
+          mma_split(dA[i], aY, bE);
+        }
+      }
+      lds_barrier();
+    }
+
+    // ---- S0 . dS1 (for the exp(G_L) factor of the state hand-off)
+    lr = lanes_sum(lr, 64);
+    if (lane == 0) sRed[wv] = lr;
+
+    // ---- D = dP o exp(G_r - G_t) (causal); dG from P
+    f32x4 Dv[SCC];
+#pragma unroll
+    for (int i = 0; i < SCC; ++i) {
+      const int cb = (wv + 4 * i) / NRB;
+      const int t = 16 * cb + r16;
+      float colsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * g4 + e;
+        const bool ok = t <= r && r < L;
+        const float dps = scale * dP[i][e];
+        Dv[i][e] = ok ? dps * __expf(sG[r] - sG[t]) : 0.f;
+        const float pd = ok ? dps * fPT.get(t, r) : 0.f;
+        const float rs = lanes_sum(pd, 16);
+        if (r16 == 0) sRowG[wv * C + r] += rs;
+        colsum += pd;
+      }
+      colsum = group4_sum(colsum);
+      if (g4 == 0) sRowG[wv * C + t] -= colsum;
+    }
+    lds_barrier();     // P^T is dead: D tiles overlay it
+
+    // ---- D tiles; row-dot terms of dG / dbeta; dq^, dk^ row-scaled parts
+#pragma unroll
+    for (int i = 0; i < SCC; ++i) {
+      const int cb = (wv + 4 * i) / NRB;
+      const int t = 16 * cb + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * g4 + e;
+        fD1.put(r, t, Dv[i][e] * sRk[t]);
+        fD2.put(r, t, Dv[i][e] * sRq[r]);
+      }
+    }
+    {
+      f32x4 qd = zero4(), kw = zero4(), kk = zero4();
+#pragma unroll
+      for (int i = 0; i < SCK; ++i) {
+        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+        dQg[i] *= scale;
+        TdW[i] = -TdW[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * g4 + e;
+          const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
+          qd[e] += qv * dQg[i][e];
+          kw[e] += kv * TdW[i][e];
+          kk[e] += kv * dKt[i][e];
+        }
+      }
+      float last = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * g4 + e;
+        const float q1 = lanes_sum(qd[e], 16), k1 = lanes_sum(kw[e], 16), k2 = lanes_sum(kk[e], 16);
+        const bool ok = r < L;
+        const float gam = __expf(sG[r]), kap = __expf(GL - sG[r]);
+        const float tw = ok ? gam * sRk[r] * k1 : 0.f;
+        const float kt = ok ? kap * sRk[r] * k2 : 0.f;
+        if (r16 == 0) {
+          sRowG[wv * C + r] += (ok ? gam * sRq[r] * q1 : 0.f) + sB[r] * tw - kt;
+          sRowB[wv * C + r] += tw;
+        }
+        last += kt;
+#pragma unroll
+        for (int i = 0; i < SCK; ++i) {
+          dq[i][e] = gam * dQg[i][e];
+          dk[i][e] = kap * dKt[i][e] + sB[r] * gam * TdW[i][e];
+        }
+      }
+      last = group4_sum(last);
+      if (lane == 0) sRed[4 + wv] = last;
+    }
+    lds_barrier();
+
+    // ---- dq^ += D~ K (D~ = D rk_t), dk^ += D^^T Q (D^ = D rq_r)
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) {
+      const int db = (wv + 4 * i) / NRB;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (32 * s <= 16 * rb + 15)
+          mma_split(dq[i], fD1.row(16 * rb + r16, 32 * s, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+        if (32 * s + 31 >= 16 * rb)
+          mma_split(dk[i], fD2.col(32 * s, 16 * rb, lane), lds_col8(sQ, PK, 32 * s, 16 * db, lane));
+      }
+    }
+    lds_barrier();
+
+    // ---- dA (strictly lower): dbeta, dG and the Dk tiles
+#pragma unroll
+    for (int i = 0; i < SCC; ++i) {
+      const int cb = (wv + 4 * i) / NRB;
+      f32x4 kk = zero4();
+      if (cb <= rb) {
+#pragma unroll
+        for (int ks = 0; ks < KSK; ++ks)
+          mma(kk, ld8(&sK[(16 * rb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sK[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
+      }
+      const int m = 16 * cb + r16;
+      float colsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rb + 4 * g4 + e;
+        const bool ok = m < t && t < L;
+        const float da = -dA[i][e];
+        const float ex = ok ? __expf(sG[t] - sG[m]) : 0.f;
+        const float abar = sRk[t] * sRk[m] * kk[e] * ex;
+        const float dbp = ok ? da * abar : 0.f;
+        const float dkv = ok ? sB[t] * da * ex : 0.f;
+        const float ad = sB[t] * dbp;
+        const float rb1 = lanes_sum(dbp, 16), rg = lanes_sum(ad, 16);
+        if (r16 == 0) {
+          sRowB[wv * C + t] += rb1;
+          sRowG[wv * C + t] += rg;
+        }
+        colsum += ad;
+        fD1.put(t, m, dkv * sRk[m]);
+        fD2.put(t, m, dkv * sRk[t]);
+      }
+      colsum = group4_sum(colsum);
+      if (g4 == 0) sRowG[wv * C + m] -= colsum;
+    }
+    lds_barrier();
+
+    // ---- dk^ += Dk~ K + Dk^^T K
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) {
+      const int db = (wv + 4 * i) / NRB;
+#pragma unroll
+      for (int s = 0; s < KSC; ++s) {
+        if (32 * s <= 16 * rb + 15)
+          mma_split(dk[i], fD1.row(16 * rb + r16, 32 * s, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+        if (32 * s + 31 >= 16 * rb)
+          mma_split(dk[i], fD2.col(32 * s, 16 * rb, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+      }
+    }
+    if constexpr (GVA) {
+#pragma unroll
+      for (int i = 0; i < SCK; ++i) {
+        sq_[i] += dq[i];
+        sk_[i] += dk[i];
+      }
+    }
+    lds_barrier();
+
+    // ---- dg = reverse cumsum of dG over the chunk, dbeta
+    if (wv == 0) {
+      const float lrt = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+      const float lst = sRed[4] + sRed[5] + sRed[6] + sRed[7];
+      const int tr = C - 1 - lane;            // this lane's row, reversed
+      float x = 0.f;
+      if (lane < C && tr < L) {
+        x = sRowG[tr] + sRowG[C + tr] + sRowG[2 * C + tr] + sRowG[3 * C + tr];
+        if (tr == L - 1) x += lst + __expf(GL) * lrt;
+      }
+      const float y = wave_incl_scan(x, lane);
+      if (lane < C && tr < L) a.dg[(t0 + tr) * HV + j] = y;
+      if (lane < L) {
+        const float db = sRowB[lane] + sRowB[C + lane] + sRowB[2 * C + lane] + sRowB[3 * C + lane];
+        a.dbeta[(t0 + lane) * HV + j] = db;
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- group sums, L2-norm backward, dq / dk
+  auto finish = [&](const f32x4 (&DQ)[SCK], const f32x4 (&DK)[SCK]) {
+    if (a.l2norm) {
+      f32x4 qd = zero4(), kd = zero4();
+#pragma unroll
+      for (int i = 0; i < SCK; ++i) {
+        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * g4 + e;
+          qd[e] += to_float(sQ[r * PK + d]) * DQ[i][e];
+          kd[e] += to_float(sK[r * PK + d]) * DK[i][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * g4 + e;
+        const float q1 = lanes_sum(qd[e], 16), k1 = lanes_sum(kd[e], 16);
+        if (r16 == 0) {
+          sDotQ[wv * C + r] = q1;
+          sDotK[wv * C + r] = k1;
+        }
+      }
+      lds_barrier();
+    }
+    T* dqp = static_cast<T*>(a.dq);
+    T* dkp = static_cast<T*>(a.dk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rb + 4 * g4 + e;
+      if (r >= L) continue;
+      float cq = 0.f, ck = 0.f;
+      const float rq = sRq[r], rk = sRk[r];
+      if (a.l2norm) {
+        cq = rq * rq * (sDotQ[r] + sDotQ[C + r] + sDotQ[2 * C + r] + sDotQ[3 * C + r]);
+        ck = rk * rk * (sDotK[r] + sDotK[C + r] + sDotK[2 * C + r] + sDotK[3 * C + r]);
+      }
+#pragma unroll
+      for (int i = 0; i < SCK; ++i) {
+        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+        const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
+        const float oq = a.l2norm ? rq * (DQ[i][e] - cq * qv) : DQ[i][e];
+        const float okv = a.l2norm ? rk * (DK[i][e] - ck * kv) : DK[i][e];
+        dqp[((t0 + r) * H + h) * K + d] = (T)oq;
+        dkp[((t0 + r) * H + h) * K + d] = (T)okv;
+      }
+    }
+  };
+  if constexpr (GVA) {
+    finish(sq_, sk_);
+  } else {
+    finish(dq, dk);
+  }
+}
+
+template <typename T, int C, int K>
+hipError_t launch_t(const Args& a, hipStream_t s) {
+  if constexpr (!B3<T, C, K>::fits) {
+    return hipErrorInvalidValue;    // rejected on the host before any launch
+  } else {
+    const dim3 grid((unsigned)a.NTmax, (unsigned)a.H);
+    if (a.HV == a.H)
+      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, true>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int C>
+hipError_t launch_k(const Args& a, hipStream_t s) {
+  switch (a.K) {
+    case 32: return launch_t<T, C, 32>(a, s);
+    case 64: return launch_t<T, C, 64>(a, s);
+    case 128: return launch_t<T, C, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_c(const Args& a, hipStream_t s) {
+  return a.C == 32 ? launch_k<T, 32>(a, s) : launch_k<T, 64>(a, s);
+}
+
+}  // namespace
+
+bool bwd_fused_fits(int dtype, int C, int K) {
+  bool ok = false;
+#define GDR_B3_FITS(TT, CC, KK) \
+  if (C == CC && K == KK) ok = B3<TT, CC, KK>::fits;
+  if (dtype == GDR_BF16) {
+    GDR_B3_FITS(bf16, 32, 32) GDR_B3_FITS(bf16, 32, 64) GDR_B3_FITS(bf16, 32, 128)
+    GDR_B3_FITS(bf16, 64, 32) GDR_B3_FITS(bf16, 64, 64) GDR_B3_FITS(bf16, 64, 128)
+  } else {
+    GDR_B3_FITS(float, 32, 32) GDR_B3_FITS(float, 32, 64) GDR_B3_FITS(float, 32, 128)
+    GDR_B3_FITS(float, 64, 32) GDR_B3_FITS(float, 64, 64) GDR_B3_FITS(float, 64, 128)
+  }
+#undef GDR_B3_FITS
+  return ok;
+}
+
+hipError_t launch_bwd_dqkvg(const Args& a, hipStream_t s) {
+  if (a.NTmax == 0) return hipSuccess;
+  return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+}  // namespace gdr

@@ -8,6 +8,12 @@
 
 namespace gdr {
 
+bool bwd_shape_ok(const gdr_problem& p) {
+  if (p.gate_per_channel) return false;
+  if (p.K != 32 && p.K != 64 && p.K != 128) return false;
+  return bwd_scan_fits(p.dtype, p.chunk_size, (int)p.K) && bwd_fused_fits(p.dtype, p.chunk_size, (int)p.K);
+}
+
 int64_t nt_max(const gdr_problem& p) {
   const int64_t C = p.chunk_size;
   if (p.T <= 0) return 0;
@@ -18,7 +24,7 @@ int64_t nt_max(const gdr_problem& p) {
 
 }  // namespace gdr
 
-using gdr::FwdArgs;
+using gdr::Args;
 
 namespace {
 
@@ -51,8 +57,8 @@ gdr_status check(const gdr_problem* p, bool varlen) {
   return GDR_OK;
 }
 
-gdr::FwdArgs make_args(const gdr_problem& p) {
-  FwdArgs a;
+gdr::Args make_args(const gdr_problem& p) {
+  Args a;
   std::memset(&a, 0, sizeof(a));
   a.B = p.B;
   a.T = p.T;
@@ -99,6 +105,29 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
 
 gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_HIP; }
 
+gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
+  gdr_bwd_layout l;
+  l.fwd = layout_of(p);
+  const int64_t nt = l.fwd.nt_max;
+  const size_t es = elem_size(p);
+  const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V;
+  size_t off = l.fwd.total;
+  l.de_local = off;
+  off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.qscale = off;
+  off = round_up(off + (size_t)nt * HV * C * sizeof(float));
+  l.dh = off;
+  off = round_up(off + (size_t)nt * HV * V * K * es);
+  l.total = off;
+  return l;
+}
+
+gdr_status check_bwd(const gdr_problem* p, bool varlen) {
+  const gdr_status st = check(p, varlen);
+  if (st != GDR_OK) return st;
+  return gdr::bwd_shape_ok(*p) ? GDR_OK : GDR_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +146,8 @@ const char* gdr_status_string(gdr_status s) {
     case GDR_ERR_WORKSPACE: return "workspace missing or too small";
     case GDR_ERR_HIP: return "HIP launch failed";
     case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
+    case GDR_ERR_UNSUPPORTED:
+      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 needs chunk_size 32)";
   }
   return "unknown status";
 }
@@ -165,7 +196,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   const gdr_fwd_layout l = layout_of(*p);
   if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
 
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   char* ws = static_cast<char*>(workspace);
   a.q = q;
   a.k = k;
@@ -199,7 +230,7 @@ gdr_status gdr_chunk_table(const gdr_problem* p, const int32_t* cu_seqlens, int3
   if (st != GDR_OK) return st;
   if (chunk_off == nullptr || (gdr::nt_max(*p) > 0 && chunk_idx == nullptr)) return GDR_ERR_NULL_ARG;
   if (!aligned16(chunk_idx) || !aligned16(chunk_off) || !aligned16(cu_seqlens)) return GDR_ERR_ALIGNMENT;
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   a.cu = cu_seqlens;
   a.chunk_idx = chunk_idx;
   a.chunk_off = chunk_off;
@@ -225,7 +256,7 @@ gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g
   if (st != GDR_OK) return st;
   if (!p->gate_per_channel && kscale == nullptr) return GDR_ERR_NULL_ARG;
   if (kscale != nullptr && !aligned16(kscale)) return GDR_ERR_ALIGNMENT;
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   a.k = k;
   a.g = g;
   a.beta = beta;
@@ -241,7 +272,7 @@ gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const 
                       void* stream) {
   gdr_status st = stage_common(p, {k, v, g, beta, chunk_idx, chunk_off, Tm, w, u});
   if (st != GDR_OK) return st;
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   a.k = k;
   a.v = v;
   a.g = g;
@@ -262,7 +293,7 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
   if (p->gate_per_channel ? g == nullptr : kscale == nullptr) return GDR_ERR_NULL_ARG;
   if ((g && !aligned16(g)) || (kscale && !aligned16(kscale))) return GDR_ERR_ALIGNMENT;
   if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_ERR_ALIGNMENT;
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   a.k = k;
   a.w = const_cast<void*>(w);
   a.u = const_cast<void*>(u);
@@ -281,7 +312,7 @@ gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const v
                      const float* g, const int32_t* chunk_idx, const int32_t* chunk_off, void* o, void* stream) {
   gdr_status st = stage_common(p, {q, k, v_new, h, g, chunk_idx, chunk_off, o});
   if (st != GDR_OK) return st;
-  FwdArgs a = make_args(*p);
+  Args a = make_args(*p);
   a.q = q;
   a.k = k;
   a.v_new = const_cast<void*>(v_new);
@@ -291,6 +322,160 @@ gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const v
   a.chunk_off = const_cast<int32_t*>(chunk_off);
   a.o = o;
   return hip_status(gdr::launch_fwd_o(a, static_cast<hipStream_t>(stream)));
+}
+
+
+gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* out) {
+  if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
+  const gdr_status st = check_bwd(p, p->N != p->B);
+  if (st != GDR_OK) return st;
+  *out = bwd_layout_of(*p);
+  return GDR_OK;
+}
+
+gdr_status gdr_bwd_workspace_bytes(const gdr_problem* p, size_t* bytes) {
+  gdr_bwd_layout l;
+  const gdr_status st = gdr_bwd_workspace_layout(p, &l);
+  if (st != GDR_OK) return st;
+  if (bytes == nullptr) return GDR_ERR_NULL_ARG;
+  *bytes = l.total;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, const void* d_o,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check_bwd(p, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  if (p->T > 0) {
+    const void* req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta};
+    for (const void* ptr : req)
+      if (ptr == nullptr) return GDR_ERR_NULL_ARG;
+  }
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  const gdr_bwd_layout l = bwd_layout_of(*p);
+  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
+
+  Args a = make_args(*p);
+  char* ws = static_cast<char*>(workspace);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
+  a.Tm = ws + l.fwd.Tm;
+  a.w = ws + l.fwd.w;
+  a.u = ws + l.fwd.u;
+  a.h = ws + l.fwd.h;
+  a.v_new = ws + l.fwd.v_new;
+  a.kscale = reinterpret_cast<float*>(ws + l.fwd.kscale);
+  a.ht = nullptr;
+  a.d_o = d_o;
+  a.dht = dht;
+  a.de_local = ws + l.de_local;
+  a.qscale = reinterpret_cast<float*>(ws + l.qscale);
+  a.dh = ws + l.dh;
+  a.dh0 = dh0;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gdr::launch_chunk_table(a, s);
+  if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+  if (e == hipSuccess) e = gdr::launch_wy(a, s);
+  if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+  if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
+  if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
+  if (e == hipSuccess) e = gdr::launch_bwd_dqkvg(a, s);
+  return hip_status(e);
+}
+
+namespace {
+gdr_status bwd_stage_common(const gdr_problem* p, std::initializer_list<const void*> ptrs) {
+  gdr_status st = check_bwd(p, p ? p->N != p->B : false);
+  if (st != GDR_OK) return st;
+  for (const void* ptr : ptrs) {
+    if (ptr == nullptr) return GDR_ERR_NULL_ARG;
+    if (!aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  }
+  return GDR_OK;
+}
+}  // namespace
+
+gdr_status gdr_bwd_intra(const gdr_problem* p, const void* q, const void* k, const float* g, const void* d_o,
+                         const int32_t* chunk_idx, const int32_t* chunk_off, void* de_local, float* qscale,
+                         void* stream) {
+  gdr_status st = bwd_stage_common(p, {q, k, g, d_o, chunk_idx, chunk_off, de_local, qscale});
+  if (st != GDR_OK) return st;
+  Args a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.g = g;
+  a.d_o = d_o;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.de_local = de_local;
+  a.qscale = qscale;
+  return hip_status(gdr::launch_bwd_intra(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_bwd_dh(const gdr_problem* p, const void* q, const void* k, const void* w, const void* d_o,
+                      const void* de_local, const float* qscale, const float* kscale, const int32_t* chunk_idx,
+                      const int32_t* chunk_off, const float* dht, void* dh, float* dh0, void* stream) {
+  gdr_status st = bwd_stage_common(p, {q, k, w, d_o, de_local, qscale, kscale, chunk_idx, chunk_off, dh});
+  if (st != GDR_OK) return st;
+  if ((dht && !aligned16(dht)) || (dh0 && !aligned16(dh0))) return GDR_ERR_ALIGNMENT;
+  Args a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.w = const_cast<void*>(w);
+  a.d_o = d_o;
+  a.de_local = const_cast<void*>(de_local);
+  a.qscale = const_cast<float*>(qscale);
+  a.kscale = const_cast<float*>(kscale);
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.dht = dht;
+  a.dh = dh;
+  a.dh0 = dh0;
+  return hip_status(gdr::launch_bwd_dh(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_bwd_dqkvg(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const void* d_o, const void* Tm, const void* h, const void* v_new,
+                         const void* dh, const int32_t* chunk_idx, const int32_t* chunk_off, void* dq, void* dk,
+                         void* dv, float* dg, float* dbeta, void* stream) {
+  gdr_status st = bwd_stage_common(
+      p, {q, k, v, g, beta, d_o, Tm, h, v_new, dh, chunk_idx, chunk_off, dq, dk, dv, dg, dbeta});
+  if (st != GDR_OK) return st;
+  Args a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.d_o = d_o;
+  a.Tm = const_cast<void*>(Tm);
+  a.h = const_cast<void*>(h);
+  a.v_new = const_cast<void*>(v_new);
+  a.dh = const_cast<void*>(dh);
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  return hip_status(gdr::launch_bwd_dqkvg(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -114,6 +114,10 @@ template <typename T> GDR_DEV void mma_split(f32x4& acc, const Frag<T>& a, const
   mma(acc, a, b.hi);
   if constexpr (SplitFrag<T>::kSplit) mma(acc, a, b.lo);
 }
+template <typename T> GDR_DEV void mma_split(f32x4& acc, const SplitFrag<T>& a, const Frag<T>& b) {
+  mma(acc, a.hi, b);
+  if constexpr (SplitFrag<T>::kSplit) mma(acc, a.lo, b);
+}
 
 // ---------------------------------------------------------------- memory
 
@@ -172,6 +176,56 @@ GDR_DEV Frag<T> lds_tr_frag(const T* tile, int pitch, int row_lo, int row_hi, in
 
 GDR_DEV float to_float(bf16 x) { return (float)x; }
 GDR_DEV float to_float(float x) { return x; }
+
+// Row-map fragment (contraction index 8 g + e) taken down a column of a
+// row-major LDS tile: rows row0 + 8 g .. row0 + 8 g + 7 of column col0 + l % 16.
+template <typename T>
+GDR_DEV Frag<T> lds_col8(const T* tile, int pitch, int row0, int col0, int lane) {
+  const int r = row0 + 8 * (lane >> 4);
+  return lds_tr_frag(tile, pitch, r, r + 4, col0, lane);
+}
+
+// An fp32 operand tile in LDS.  For bf16 problems each value is kept as a
+// bf16 pair hi + lo (about 16 mantissa bits), so MFMA operands come out as
+// SplitFrag through the same 16-byte row reads and transposed column reads as
+// plain bf16 tiles; for fp32 problems it is one float tile (lo unused).
+template <typename T> struct FTile {
+  static constexpr bool kSplit = sizeof(T) == 2;
+  T* hi;
+  T* lo;
+  int pitch;
+  GDR_DEV void put(int r, int c, float x) const {
+    const T h = (T)x;
+    hi[r * pitch + c] = h;
+    if constexpr (kSplit) lo[r * pitch + c] = (T)(x - to_float(h));
+  }
+  // columns c .. c + 3 of row r (c a multiple of 4)
+  GDR_DEV void put4(int r, int c, f32x4 x) const {
+    const v4_t<T> h = cvt4<T>(x);
+    *reinterpret_cast<v4_t<T>*>(hi + r * pitch + c) = h;
+    if constexpr (kSplit) *reinterpret_cast<v4_t<T>*>(lo + r * pitch + c) = cvt4<T>(x - to_f32<T>(h));
+  }
+  GDR_DEV float get(int r, int c) const {
+    float x = to_float(hi[r * pitch + c]);
+    if constexpr (kSplit) x += to_float(lo[r * pitch + c]);
+    return x;
+  }
+  // row r, contraction columns c0 + 8 g .. + 7
+  GDR_DEV SplitFrag<T> row(int r, int c0, int lane) const {
+    SplitFrag<T> f;
+    const int o = r * pitch + c0 + 8 * (lane >> 4);
+    f.hi = ld8(hi + o);
+    if constexpr (kSplit) f.lo = ld8(lo + o);
+    return f;
+  }
+  // column c0 + l % 16, contraction rows r0 + 8 g .. + 7
+  GDR_DEV SplitFrag<T> col(int r0, int c0, int lane) const {
+    SplitFrag<T> f;
+    f.hi = lds_col8(hi, pitch, r0, c0, lane);
+    if constexpr (kSplit) f.lo = lds_col8(lo, pitch, r0, c0, lane);
+    return f;
+  }
+};
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // fences global memory, which makes the compiler wait for every outstanding

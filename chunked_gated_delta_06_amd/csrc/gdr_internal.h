@@ -8,8 +8,9 @@
 
 namespace gdr {
 
-// Everything a forward stage needs: the problem and plain device pointers.
-struct FwdArgs {
+// Everything a stage needs: the problem and plain device pointers (forward
+// stages leave the backward fields NULL).
+struct Args {
   int64_t B, T, H, HV, K, V, N, NTmax;
   int32_t C, per_channel, l2norm, dtype;
   float scale;
@@ -30,14 +31,35 @@ struct FwdArgs {
   float* kscale;
   void* o;
   float* ht;
+  // backward
+  const void* d_o;
+  const float* dht;
+  void* de_local;
+  float* qscale;
+  void* dh;
+  float* dh0;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
 };
 
 int64_t nt_max(const gdr_problem& p);
 
-hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s);
-hipError_t launch_kkt_solve(const FwdArgs& a, hipStream_t s);
-hipError_t launch_wy(const FwdArgs& a, hipStream_t s);
-hipError_t launch_fwd_h(const FwdArgs& a, hipStream_t s);
-hipError_t launch_fwd_o(const FwdArgs& a, hipStream_t s);
+hipError_t launch_chunk_table(const Args& a, hipStream_t s);
+hipError_t launch_kkt_solve(const Args& a, hipStream_t s);
+hipError_t launch_wy(const Args& a, hipStream_t s);
+hipError_t launch_fwd_h(const Args& a, hipStream_t s);
+hipError_t launch_fwd_o(const Args& a, hipStream_t s);
+hipError_t launch_bwd_intra(const Args& a, hipStream_t s);
+hipError_t launch_bwd_dh(const Args& a, hipStream_t s);
+hipError_t launch_bwd_dqkvg(const Args& a, hipStream_t s);
+
+// Shapes the backward kernels take (scalar gate; LDS limits of the fused
+// kernel and of the reverse scan).
+bool bwd_shape_ok(const gdr_problem& p);
+bool bwd_scan_fits(int dtype, int C, int K);
+bool bwd_fused_fits(int dtype, int C, int K);
 
 }  // namespace gdr

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(1024) void k0_varlen(const int32_t* __restrict__ cu
   if (tid == 0) off[N] = tile_base;
 }
 
-hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
   if (a.cu == nullptr) {
     const int64_t NC = (a.T + a.C - 1) / a.C;
     const int64_t work = (a.B * NC > a.B + 1) ? a.B * NC : a.B + 1;

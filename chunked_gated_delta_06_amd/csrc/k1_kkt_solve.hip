@@ -32,7 +32,7 @@ namespace {
 constexpr float kSpanLimit = 80.f;
 
 template <typename T, int C, int K, bool PC>
-__global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
+__global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   constexpr int NB = C / 16;                 // 16-row blocks per chunk
   constexpr int KS = K / 32;                 // contraction slabs
   constexpr int NLB = NB * (NB + 1) / 2;     // lower-triangular blocks
@@ -269,14 +269,14 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(FwdArgs a) {
 }
 
 template <typename T, int C, int K, bool PC>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_t(const Args& a, hipStream_t s) {
   const unsigned gy = (unsigned)(PC ? a.HV : a.H);
   hipLaunchKernelGGL((k1_kkt_solve<T, C, K, PC>), dim3((unsigned)a.NTmax, gy), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T, int C, bool PC>
-hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_k(const Args& a, hipStream_t s) {
   switch (a.K) {
     case 32: return launch_t<T, C, 32, PC>(a, s);
     case 64: return launch_t<T, C, 64, PC>(a, s);
@@ -287,14 +287,14 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_c(const Args& a, hipStream_t s) {
   if (a.C == 32) return a.per_channel ? launch_k<T, 32, true>(a, s) : launch_k<T, 32, false>(a, s);
   return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_kkt_solve(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_kkt_solve(const Args& a, hipStream_t s) {
   if (a.NTmax == 0) return hipSuccess;
   return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
 }

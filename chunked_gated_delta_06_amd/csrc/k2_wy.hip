@@ -26,7 +26,7 @@ namespace gdr {
 namespace {
 
 template <typename T, int C, int K, bool PC>
-__global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
+__global__ __launch_bounds__(256) void k2_wy(Args a) {
   constexpr int NW = 4;
   constexpr int NB = C / 16;
   constexpr int KSC = C / 32;                       // token slabs
@@ -158,13 +158,13 @@ __global__ __launch_bounds__(256) void k2_wy(FwdArgs a) {
 }
 
 template <typename T, int C, int K, bool PC>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_t(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL((k2_wy<T, C, K, PC>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename T, int C, bool PC>
-hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_k(const Args& a, hipStream_t s) {
   switch (a.K) {
     case 32: return launch_t<T, C, 32, PC>(a, s);
     case 64: return launch_t<T, C, 64, PC>(a, s);
@@ -175,14 +175,14 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_c(const Args& a, hipStream_t s) {
   if (a.C == 32) return a.per_channel ? launch_k<T, 32, true>(a, s) : launch_k<T, 32, false>(a, s);
   return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_wy(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_wy(const Args& a, hipStream_t s) {
   if (a.NTmax == 0) return hipSuccess;
   return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
 }

@@ -74,7 +74,7 @@ struct K3 {
 };
 
 template <typename T, int C, int K, bool PC, int NW>
-__global__ __launch_bounds__(64 * NW) void k3_fwd_h(FwdArgs a) {
+__global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
   using Cfg = K3<T, C, K, PC, NW>;
   using Regs = typename Cfg::Regs;
   constexpr int NT = Cfg::NT, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
@@ -332,7 +332,7 @@ struct K3S {
 };
 
 template <typename T, int C, int K, int NWC, int NWL>
-__global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(FwdArgs a) {
+__global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
   using Cfg = K3S<T, C, K, NWC, NWL>;
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(FwdArgs a) {
 }
 
 template <typename T, int C, int K, bool PC, int NW>
-hipError_t launch_nw(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_nw(const Args& a, hipStream_t s) {
   if constexpr (!K3<T, C, K, PC, NW>::fits) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
@@ -534,7 +534,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int C, int K, bool PC>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_t(const Args& a, hipStream_t s) {
   if constexpr (!PC) {
     // warp-specialised scan: 2 compute + 2 loader waves (4 loader waves when
     // elements are fp32 or K = 256, to keep each loader's payload in registers)
@@ -551,7 +551,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int C, bool PC>
-hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_k(const Args& a, hipStream_t s) {
   switch (a.K) {
     case 32: return launch_t<T, C, 32, PC>(a, s);
     case 64: return launch_t<T, C, 64, PC>(a, s);
@@ -562,14 +562,14 @@ hipError_t launch_k(const FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_c(const Args& a, hipStream_t s) {
   if (a.C == 32) return a.per_channel ? launch_k<T, 32, true>(a, s) : launch_k<T, 32, false>(a, s);
   return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_h(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_h(const Args& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
 }

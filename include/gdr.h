@@ -53,7 +53,9 @@ typedef enum {
   GDR_ERR_ALIGNMENT = 6,   /* a pointer not 16-byte aligned */
   GDR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than *_workspace_bytes */
   GDR_ERR_HIP = 8,         /* a kernel launch failed */
-  GDR_ERR_CU_SEQLENS = 9   /* gdr_validate_cu_seqlens: bad table */
+  GDR_ERR_CU_SEQLENS = 9,  /* gdr_validate_cu_seqlens: bad table */
+  GDR_ERR_UNSUPPORTED = 10 /* backward: per-channel gate, K = 256, or fp32 with K = 128 and
+                              chunk 64 (see gdr_chunk_bwd) */
 } gdr_status;
 
 typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
@@ -160,6 +162,78 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
 gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new,
                      const void* h, const float* g, const int32_t* chunk_idx,
                      const int32_t* chunk_off, void* o, void* stream);
+
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradients of L = sum(o * d_o) + sum(ht * dht) with respect to q, k, v, g,
+ * beta and h0, for the same operator as gdr_chunk_fwd (scalar gate).  dq, dk
+ * are gradients with respect to q, k as passed (through the in-kernel L2 norm
+ * when use_qk_l2norm is set), summed over the value heads of each GVA group;
+ * dg is the gradient with respect to the per-token log gate g (not its cumsum).
+ *
+ * Backward workspace: the forward intermediates at the offsets of `fwd`
+ * (recomputed by the backward, so a forward workspace is not needed), plus
+ *   de_local  dtype [NT_max][HV][V][C]  scale * P^T dO per chunk, transposed, with
+ *                                       P[r][t] = q^_r . k^_t exp(G_r - G_t), t <= r
+ *   qscale    f32   [NT_max][HV][C]     scale * exp(G_r) / |q_r| (0 past L)
+ *   dh        dtype [NT_max][HV][V][K]  gradient of the state leaving each chunk,
+ *                                       transposed (dh^T) */
+typedef struct {
+  gdr_fwd_layout fwd;
+  size_t de_local, qscale, dh, total;
+} gdr_bwd_layout;
+
+gdr_status gdr_bwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
+gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* layout);
+
+/* Full backward: recompute K0-K3 (chunk table, T and kscale, w / u, h and
+ * v_new), then B1 de_local -> B2 reverse state-gradient scan -> B3 fused
+ * gradients, all on `stream`.  The pages' backward likewise recomputes the
+ * forward state scan before its own stages ("flash-linear-attention KCP
+ * precision-failure root-cause manual", sections "pitfall 2" and "debug script
+ * layout"); the state gradient follows the hand-off of section "h and dh
+ * cross-rank semantics" (dht in, dh0 out).
+ *   q, k, v, g, beta, cu_seqlens, h0   as gdr_chunk_fwd (h0 may be NULL = zeros)
+ *   d_o   dtype [B,T,HV,V]            gradient of o
+ *   dht   f32 [N,HV,K,V] or NULL       gradient of ht (NULL = zeros)
+ *   dq, dk  dtype [B,T,H,K]   dv dtype [B,T,HV,V]   dg f32 [B,T,HV]   dbeta f32 [B,T,HV]
+ *   dh0   f32 [N,HV,K,V] or NULL       gradient of h0 (not wanted if NULL)
+ *   workspace  >= gdr_bwd_workspace_bytes bytes (contents on entry irrelevant).
+ * Supported: scalar gate (gate_per_channel = 0), K in {32, 64, 128}, any V;
+ * fp32 additionally needs chunk_size 32 when K = 128.  Other problems return
+ * GDR_ERR_UNSUPPORTED before any launch. */
+gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const int32_t* cu_seqlens,
+                         const float* h0, const void* d_o, const float* dht, void* dq, void* dk,
+                         void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ---- the backward's stages (after K0-K3 of the forward, same layouts) ---- */
+
+/* B1: de_local = scale P^T dO and qscale for every chunk and value head
+ * (differentiating o through the intra-chunk term of the chunk form on the
+ * coverage-matrix page, section 2). */
+gdr_status gdr_bwd_intra(const gdr_problem* p, const void* q, const void* k, const float* g,
+                         const void* d_o, const int32_t* chunk_idx, const int32_t* chunk_off,
+                         void* de_local, float* qscale, void* stream);
+
+/* B2: reverse state-gradient scan.  For each sequence and value head, dS starts
+ * at dht (or 0); for the chunks from last to first: dh = dS,
+ * dE = de_local + diag(kscale) K dS, dS <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE;
+ * finally dh0 = dS (if dh0 != NULL).  kscale is K1's. */
+gdr_status gdr_bwd_dh(const gdr_problem* p, const void* q, const void* k, const void* w,
+                      const void* d_o, const void* de_local, const float* qscale,
+                      const float* kscale, const int32_t* chunk_idx, const int32_t* chunk_off,
+                      const float* dht, void* dh, float* dh0, void* stream);
+
+/* B3: per chunk and q/k head, every remaining gradient: dq, dk (group sums and
+ * L2-norm backward included), dv, dbeta and dg, from q, k, v, g, beta, d_o, Tm
+ * (K1), h and v_new (K3) and dh (B2). */
+gdr_status gdr_bwd_dqkvg(const gdr_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const void* d_o, const void* Tm,
+                         const void* h, const void* v_new, const void* dh,
+                         const int32_t* chunk_idx, const int32_t* chunk_off, void* dq, void* dk,
+                         void* dv, float* dg, float* dbeta, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,281 @@
+"""GPU parity of the backward path (K0-K3 recompute, B1 de_local, B2 reverse
+state-gradient scan, B3 fused gradients) against the float64 chunk-wise
+backward oracle, which is itself pinned to the per-token backward, autograd and
+finite differences (tests/test_oracle.py).
+
+Tolerances as for the forward: err_ratio = RMS(diff) / RMS(ref) <= 1e-4 for
+float32 and <= 5e-3 for bf16 on every gradient (the per-gradient acceptance
+line of the KCP page, "flash-linear-attention KCP precision-failure root-cause
+manual", acceptance section) and on the intermediates de_local and dh.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_06_amd as gdr
+import workloads
+from oracle import chunked, recurrent
+from fwd_helpers import TOL, check, dev, f64, slice_inputs
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def mk(name="b", B=2, T=200, H=2, HV=2, K=64, V=64, C=64, dtype="bf16", l2=True, h0=True,
+       slow=False, lengths=None, scale=1.0, seed=11, host_l2=False):
+    w = W(name, B=B, T=T, H=H, HV=HV, K=K, V=V, chunk_size=C, dtype=dtype, per_channel_gate=False,
+          l2norm_in_kernel=l2, host_l2norm=host_l2, h0=h0, slow_decay=slow, scale=scale, backward=True)
+    return w, workloads.make_inputs(w, seed=seed, lengths=lengths)
+
+
+def gpu_bwd(inp, *, h0=True, dht=True, workspace=None, out=None):
+    """Library backward; returns (dict of gradients as CPU float64 arrays or
+    None, workspace views, raw device outputs)."""
+    res = gdr.chunk_bwd(
+        dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]), dev(inp["do"]),
+        dev(inp["dht"]) if dht else None, scale=inp["scale"], chunk_size=inp["chunk_size"],
+        cu_seqlens=dev(inp["cu_seqlens"]), initial_state=dev(inp["h0"]) if h0 else None,
+        use_qk_l2norm_in_kernel=inp["use_qk_l2norm"], workspace=workspace, return_workspace=True,
+        out=out)
+    torch.cuda.synchronize()
+    *grads, ws = res
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=inp["chunk_size"],
+                         cu_seqlens=inp["cu_seqlens"], use_qk_l2norm=inp["use_qk_l2norm"],
+                         scale=inp["scale"])
+    views = gdr.bwd_workspace_views(p, ws)
+    got = {n: (None if t is None else f64(t)) for n, t in zip(GRADS, grads)}
+    return got, views, grads
+
+
+def oracle_bwd(inp, *, h0=True, dht=True, intermediates=False):
+    return chunked.chunked_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"],
+                               inp["dht"] if dht else None, scale=inp["scale"],
+                               h0=inp["h0"] if h0 else None, cu_seqlens=inp["cu_seqlens"],
+                               use_qk_l2norm=inp["use_qk_l2norm"], chunk_size=inp["chunk_size"],
+                               intermediates=intermediates)
+
+
+def compare(got, ref, tol, names=GRADS):
+    out = {}
+    for n in names:
+        if got.get(n) is None:
+            continue
+        out[n] = check(n, got[n], ref[n], tol)
+    return out
+
+
+# ------------------------------------------------------------------ stages
+
+STAGE_CASES = [
+    dict(dtype="fp32", K=32, V=32, C=64),
+    dict(dtype="fp32", K=128, V=64, C=32),
+    dict(dtype="bf16", K=128, V=128, C=64),
+    dict(dtype="bf16", K=64, V=32, C=64, H=1, HV=4),
+    dict(dtype="bf16", K=128, V=256, C=32, l2=False, host_l2=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(STAGE_CASES)))
+def test_bwd_stage_intermediates(case):
+    kw = STAGE_CASES[case]
+    w, inp = mk(**kw, slow=True)
+    tol = TOL[w.dtype]
+    got, views, _ = gpu_bwd(inp)
+    ref = oracle_bwd(inp, intermediates=True)
+    it = ref["inter"]
+    NT = int(it["off"][-1])
+    C = w.chunk_size
+    # chunk table (recomputed by the backward)
+    assert np.array_equal(views["chunk_idx"][:NT, :3].cpu().numpy(), it["idx"])
+    # de_local = scale P^T dO, stored transposed per chunk
+    de = f64(views["de_local"][:NT].transpose(-1, -2))
+    check("de_local", de, it["dEi"], tol)
+    # qscale = scale exp(G_r) / |q_r| on valid rows, 0 past the chunk end
+    _, _, fi = chunked.chunked_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   scale=inp["scale"], h0=inp["h0"], chunk_size=C,
+                                   use_qk_l2norm=inp["use_qk_l2norm"], intermediates=True)
+    q64 = inp["q"].double()
+    rq = (1.0 / torch.sqrt((q64 * q64).sum(-1) + 1e-6)) if inp["use_qk_l2norm"] else torch.ones(q64.shape[:-1], dtype=torch.float64)
+    rq = rq.reshape(-1, w.H).repeat_interleave(w.HV // w.H, dim=1).numpy()     # [B*T, HV]
+    ref_qs = np.zeros((NT, w.HV, C))
+    for c in range(NT):
+        _, t0, L = (int(x) for x in it["idx"][c])
+        ref_qs[c, :, :L] = inp["scale"] * np.exp(fi["G"][c, :, :L]) * rq[t0:t0 + L].T
+    qs = f64(views["qscale"][:NT])
+    check("qscale", qs, ref_qs, 1e-5)
+    assert np.all(qs[ref_qs == 0] == 0)
+    # dh: gradient of the state leaving each chunk (transposed per chunk)
+    check("dh", f64(views["dh"][:NT].transpose(-1, -2)), it["dh"], tol)
+    compare(got, ref, tol)
+
+
+# ------------------------------------------------------------------ sweep
+
+SWEEP = [
+    dict(dtype="fp32", K=32, V=32, C=32),
+    dict(dtype="fp32", K=64, V=128, C=64),
+    dict(dtype="fp32", K=128, V=32, C=32, H=1, HV=2),
+    dict(dtype="bf16", K=32, V=32, C=32),
+    dict(dtype="bf16", K=32, V=64, C=32, H=2, HV=4),
+    dict(dtype="bf16", K=64, V=64, C=64),
+    dict(dtype="bf16", K=64, V=128, C=32),
+    dict(dtype="bf16", K=128, V=64, C=32, H=2, HV=4),
+    dict(dtype="bf16", K=128, V=128, C=64, l2=False, host_l2=True),
+    dict(dtype="bf16", K=128, V=256, C=64, H=1, HV=2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_bwd_sweep(case):
+    kw = SWEEP[case]
+    w, inp = mk(**kw, scale=kw["K"] ** -0.5, seed=20 + case)
+    got, _, _ = gpu_bwd(inp)
+    compare(got, oracle_bwd(inp), TOL[w.dtype])
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_matches_per_token_backward(dtype):
+    """End to end against the hand-derived per-token reverse recurrence."""
+    w, inp = mk(dtype=dtype, B=1, T=150, K=32, V=32, C=32, slow=True, seed=3)
+    got, _, _ = gpu_bwd(inp)
+    ref = recurrent.recurrent_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["do"],
+                                  inp["dht"], scale=inp["scale"], h0=inp["h0"],
+                                  use_qk_l2norm=inp["use_qk_l2norm"])
+    compare(got, {n: f64(t) if torch.is_tensor(t) else t for n, t in ref.items()}, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_varlen_ragged(dtype):
+    lengths = [0, 1, 63, 64, 65, 200, 0, 7, 130]
+    w, inp = mk(dtype=dtype, B=1, T=sum(lengths), H=2, HV=4, K=64, V=32, C=64, lengths=lengths,
+                seed=5)
+    got, _, _ = gpu_bwd(inp)
+    ref = oracle_bwd(inp)
+    tol = TOL[dtype]
+    compare(got, ref, tol)
+    # every sequence on its own (per-sequence ratios, as on the KCP page)
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lengths)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e - s < 16:
+            continue
+        for name in ("dq", "dk", "dv"):
+            check(f"{name} seq {n}", got[name][:, s:e], ref[name][:, s:e], tol)
+    check("dh0 of empty sequences", got["dh0"][[0, 6]], inp["dht"][[0, 6]].double().numpy(), 0.0)
+
+
+@pytest.mark.parametrize("h0,dht", [(False, True), (True, False), (False, False)])
+def test_bwd_optional_states(h0, dht):
+    w, inp = mk(T=130, K=64, V=64, C=32, seed=9)
+    got, _, _ = gpu_bwd(inp, h0=h0, dht=dht)
+    compare(got, oracle_bwd(inp, h0=h0, dht=dht), TOL["bf16"])
+
+
+def test_bwd_no_dh0_wanted():
+    w, inp = mk(T=100, K=32, V=32, C=32, seed=13)
+    res = gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                        dev(inp["do"]), dev(inp["dht"]), chunk_size=32, initial_state=dev(inp["h0"]),
+                        use_qk_l2norm_in_kernel=True, want_dh0=False)
+    torch.cuda.synchronize()
+    assert res[5] is None
+    ref = oracle_bwd(inp)
+    for n, t in zip(GRADS[:5], res[:5]):
+        check(n, f64(t), ref[n], TOL["bf16"])
+
+
+def test_bwd_empty_batch():
+    """T = 0: no token gradients; dh0 = dht for every sequence."""
+    w, inp = mk(B=1, T=0, lengths=[0, 0, 0], K=32, V=32, C=64)
+    got, _, _ = gpu_bwd(inp)
+    assert np.array_equal(got["dh0"], inp["dht"].double().numpy())
+
+
+def test_bwd_single_tokens():
+    lengths = [1] * 9
+    w, inp = mk(B=1, T=9, lengths=lengths, K=32, V=64, C=32, seed=17)
+    got, _, _ = gpu_bwd(inp)
+    compare(got, oracle_bwd(inp), TOL["bf16"])
+
+
+def test_bwd_beta_zero_closed_form():
+    """beta = 0: pure decay, dh0 = sum_t scale exp(Gabs_t) q^_t do_t^T + exp(Gabs_T) dht,
+    dk = dv = 0 (a closed form independent of the chunk algebra)."""
+    w, inp = mk(B=1, T=90, H=1, HV=1, K=32, V=32, C=32, dtype="fp32", seed=19)
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    got, _, _ = gpu_bwd(inp)
+    q = inp["q"].double()[0, :, 0]
+    qh = q / torch.sqrt((q * q).sum(-1, keepdim=True) + 1e-6)
+    Gabs = torch.cumsum(inp["g"].double()[0, :, 0], 0)
+    do = inp["do"].double()[0, :, 0]
+    ref = inp["scale"] * torch.einsum("t,tk,tv->kv", torch.exp(Gabs), qh, do) + torch.exp(Gabs[-1]) * inp["dht"].double()[0, 0]
+    check("dh0 (beta=0)", got["dh0"][0, 0], ref.numpy(), 1e-4)
+    assert np.abs(got["dk"]).max() == 0 and np.abs(got["dv"]).max() == 0
+
+
+def test_bwd_deterministic_and_poisoned():
+    """Two runs are bitwise equal; NaN-poisoned workspace and outputs are fully
+    overwritten."""
+    w, inp = mk(B=1, T=333, H=2, HV=4, K=128, V=64, C=64, seed=23)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
+    lay = gdr.bwd_layout(p)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
+    ws.view(torch.int8).fill_(-1)     # 0xFF bytes: NaN in bf16 and fp32
+    outs = tuple(torch.full_like(dev(x), float("nan")) for x in
+                 (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"]))
+    dh0 = torch.full((1, 4, 128, 64), float("nan"), device="cuda")
+    got1, _, raw1 = gpu_bwd(inp, workspace=ws, out=outs + (dh0,))
+    for n in GRADS:
+        assert np.isfinite(got1[n]).all(), n
+    got2, _, _ = gpu_bwd(inp)
+    for n in GRADS:
+        assert np.array_equal(got1[n], got2[n]), n
+    compare(got1, oracle_bwd(inp), TOL["bf16"])
+
+
+def test_bwd_unsupported_shapes_raise():
+    w, inp = mk(T=64, K=64, V=64, C=64)
+    gpc = torch.zeros(2, 64, 2, 64, device="cuda")
+    with pytest.raises(ValueError, match="backward supports"):
+        gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), gpc, dev(inp["beta"]),
+                      dev(inp["do"]), None, chunk_size=64)
+
+
+def test_bwd_varlen_equals_dense_rows():
+    """A varlen batch of equal-length sequences gives bitwise the gradients of the
+    dense batch with those rows."""
+    w, inp = mk(B=3, T=150, K=64, V=64, C=64, seed=29)
+    gd, _, _ = gpu_bwd(inp)
+    vl = dict(inp)
+    for n in ("q", "k", "v", "g", "beta", "do"):
+        vl[n] = inp[n].reshape(1, 3 * 150, *inp[n].shape[2:]).contiguous()
+    vl["cu_seqlens"] = torch.tensor([0, 150, 300, 450], dtype=torch.int32)
+    gv, _, _ = gpu_bwd(vl)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.array_equal(gv[n].reshape(gd[n].shape), gd[n]), n
+    assert np.array_equal(gv["dh0"], gd["dh0"])
+
+
+# ------------------------------------------------------------------ full-size workload
+
+@pytest.mark.timeout(300)
+def test_config_long_bf16_backward():
+    """The long single-sequence workload (B=1, T=65536, H=HV=32, K=V=128,
+    fwd+bwd) at full size on the GPU, checked on a sampled head against the
+    chunk-wise oracle run on that head (H == HV, so the head's dq / dk have no
+    other contributions)."""
+    w = workloads.CONFIGS["long_bf16"]
+    inp = workloads.make_inputs(w)
+    res = gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                        dev(inp["do"]), dev(inp["dht"]), scale=inp["scale"], chunk_size=w.chunk_size,
+                        initial_state=dev(inp["h0"]), use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    heads = [21]
+    for n, t in zip(GRADS, res):
+        assert bool(torch.isfinite(t).all()), n
+    got = {n: f64(t[:, :, heads] if n != "dh0" else t[:, heads]) for n, t in zip(GRADS, res)}
+    del res
+    torch.cuda.empty_cache()
+    ref = oracle_bwd(slice_inputs(inp, heads=heads))
+    compare(got, ref, TOL[w.dtype])
