@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
-"""Throughput of the chunked gated delta-rule forward on one MI355X.
+"""Throughput of the chunked gated delta-rule operator on one MI355X.
 
 One step = one full forward (K0 chunk table, K1 kk^T + triangular inverse,
 K2 WY recompute, K3 state scan, K4 output) over one batch of the workload,
-inputs resident in HBM.  Prints one JSON line:
+inputs resident in HBM; for a workload with a backward (long_bf16) a step is
+the forward plus the full backward (K0-K3 recompute, B1 de_local, B2 reverse
+state-gradient scan, B3 fused gradients).  Prints one JSON line:
 
-  value        tokens/s of the whole forward (B*T / seconds per step)
+  value        tokens/s of one step (B*T / seconds per step)
   roofline     the dominant kernel's algorithmic HBM bytes per launch / its
                average launch time (HIP events on the launch stream), against
                8 TB/s; traffic = measured HBM bytes per launch from rocprofv3
                counters (profiles/), null when the kernel changed since
   cpu_baseline the float64 per-token oracle timed on a bounded sample
+  backward     (default run) the same measurement for the long-sequence
+               forward + backward workload
 
-The bench first checks a sample of its own output against the oracle and
-refuses to report numbers when that check fails.
+Each leg first checks a sample of its own output against the oracle and the
+bench refuses to report numbers when that check fails.
 """
 import argparse
 import ctypes
@@ -47,9 +51,30 @@ def stage_bytes_per_token_head(w, T_seq):
     }
 
 
+def bwd_stage_bytes_per_token_head(w, T_seq):
+    """Same accounting for the backward's own stages (the K1-K3 recompute is
+    counted with the forward model, without the ht write)."""
+    e = 2 if w.dtype == "bf16" else 4
+    r = w.H / w.HV
+    K, V, C = w.K, w.V, w.chunk_size
+    fwd = stage_bytes_per_token_head(w, T_seq)
+    return {
+        "kkt_solve": fwd["kkt_solve"],
+        "wy": fwd["wy"],
+        "fwd_h": fwd["fwd_h"] - 4 * K * V / T_seq,
+        # q, k, g, dO -> de_local, qscale
+        "bwd_intra": 2 * r * K * e + 4 + V * e + V * e + 4,
+        # q, k, w, dO, de_local, qscale, kscale, dht -> dh, dh0
+        "bwd_dh": 2 * r * K * e + K * e + 2 * V * e + 8 + e * K * V / C + 8 * K * V / T_seq,
+        # q, k, v, g, beta, dO, Tm, h, v_new, dh -> dq, dk, dv, dg, dbeta
+        "bwd_dqkvg": 4 * r * K * e + 4 * V * e + 16 + e * C + 2 * e * K * V / C,
+    }
+
+
 def kernel_source_hash(stage):
     fname = {"kkt_solve": "k1_kkt_solve.hip", "wy": "k2_wy.hip", "fwd_h": "k3_fwd_h.hip",
-             "fwd_o": "k4_fwd_o.hip"}[stage]
+             "fwd_o": "k4_fwd_o.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
+             "bwd_dqkvg": "b3_bwd_dqkvg.hip"}[stage]
     h = hashlib.sha256()
     for f in (fname, "gdr_device.h"):
         with open(os.path.join(ROOT, "chunked_gated_delta_06_amd", "csrc", f), "rb") as fh:
@@ -115,6 +140,198 @@ def parity_gate(w, inp, o, ht):
     return eo, eh, tol
 
 
+def event_stage_ms(stream, stages, reps):
+    """Average milliseconds per launch of each stage (HIP events recorded on
+    the launch stream around every launch, stages run in order)."""
+    import torch
+    names = list(stages)
+    for _ in range(2):
+        for n in names:
+            stages[n]()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(stream)
+        for i, n in enumerate(names):
+            stages[n]()
+            evs[r][i + 1].record(stream)
+    torch.cuda.synchronize()
+    acc = {n: 0.0 for n in names}
+    for r in range(reps):
+        for i, n in enumerate(names):
+            acc[n] += evs[r][i].elapsed_time(evs[r][i + 1])
+    return {n: acc[n] / reps for n in names}
+
+
+def wall_ms_per_step(step, warmup, steps):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def roofline(per_unit, avg_ms, units, workload, stages):
+    dom = max(stages, key=lambda n: avg_ms[n])
+    alg_bytes = per_unit[dom] * units
+    achieved = alg_bytes / (avg_ms[dom] * 1e-3) / 1e9
+    return {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(dom, workload),
+            "bytes_per_unit": per_unit[dom], "units": units, "avg_launch_ms": avg_ms[dom]}
+
+
+def to_dev(inp, dev, names):
+    import torch
+    return {k: (inp[k].to(dev) if isinstance(inp.get(k), torch.Tensor) else inp.get(k)) for k in names}
+
+
+def bwd_parity_gate(gdr, w, inp, dev, o, T=2048, heads=(0, 21)):
+    """The timed forward's o on the first T tokens of two value heads, and the
+    backward (same kernels, same per-head shapes) run on those tokens and
+    heads, against the chunk-wise oracle."""
+    import torch
+    from oracle import chunked
+    from oracle.metrics import err_ratio
+    hs = list(heads)
+    sub = {n: inp[n][:, :T][:, :, hs].contiguous() for n in ("q", "k", "v", "g", "beta", "do")}
+    sub["h0"] = inp["h0"][:, hs].contiguous()
+    sub["dht"] = inp["dht"][:, hs].contiguous()
+    d = to_dev(sub, dev, list(sub))
+    res = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["dht"], scale=inp["scale"],
+                        chunk_size=inp["chunk_size"], initial_state=d["h0"],
+                        use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    torch.cuda.synchronize()
+    ref = chunked.chunked_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"], sub["dht"],
+                              scale=inp["scale"], h0=sub["h0"], use_qk_l2norm=inp["use_qk_l2norm"],
+                              chunk_size=inp["chunk_size"])
+    errs = {n: err_ratio(t.cpu(), ref[n]) for n, t in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), res)}
+    ro, _ = chunked.chunked_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale=inp["scale"],
+                                h0=sub["h0"], use_qk_l2norm=inp["use_qk_l2norm"], chunk_size=inp["chunk_size"])
+    errs["o"] = err_ratio(o[:, :T][:, :, hs].cpu(), ro)
+    return errs, (5e-3 if w.dtype == "bf16" else 1e-4)
+
+
+def measure(gdr, w, steps, warmup, breakdown, label):
+    """Time one workload; returns the fields of its JSON record."""
+    import torch
+    dev = torch.device("cuda:0")
+    inp = workloads_inputs(w)
+    backward = bool(w.backward)
+    d = to_dev(inp, dev, ("q", "k", "v", "g", "beta", "h0", "cu_seqlens", "do", "dht"))
+    kw = dict(scale=inp["scale"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
+              initial_state=d["h0"], output_final_state=True,
+              use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    o, ht, ws = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], return_workspace=True, **kw)
+    torch.cuda.synchronize()
+    if backward:
+        errs, tol = bwd_parity_gate(gdr, w, inp, dev, o)
+        parity = {**{f"{n} (first 2048 tokens, heads 0 and 21)": v for n, v in errs.items()}, "tol": tol}
+        ok = all(v <= tol for v in errs.values())
+    else:
+        eo, eh, tol = parity_gate(w, inp, o.cpu(), ht.cpu())
+        parity = {"o": eo, "ht": eh, "tol": tol}
+        ok = eo <= tol and eh <= tol
+    print(f"parity gate ({label}): " + ", ".join(f"{k}={v:.2e}" for k, v in parity.items()),
+          file=sys.stderr, flush=True)
+    if not ok:
+        print("parity check failed: refusing to report throughput", file=sys.stderr)
+        sys.exit(1)
+
+    L = gdr.lib()
+    p = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fwd_args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]),
+                P(d["h0"]), P(o), P(ht), P(ws), ctypes.c_size_t(ws.numel()), sp)
+    if backward:
+        blay = gdr.bwd_layout(p)
+        bws = torch.empty(blay.total, dtype=torch.uint8, device=dev)
+        grads = [torch.empty_like(d[n]) for n in ("q", "k", "v", "g", "beta")]
+        dh0 = torch.empty_like(d["h0"])
+        bwd_args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]),
+                    P(d["cu_seqlens"]), P(d["h0"]), P(d["do"]), P(d["dht"]), *[P(t) for t in grads], P(dh0),
+                    P(bws), ctypes.c_size_t(bws.numel()), sp)
+
+    def step():
+        st = L.gdr_chunk_fwd(*fwd_args)
+        if st == 0 and backward:
+            st = L.gdr_chunk_bwd(*bwd_args)
+        if st != 0:
+            raise RuntimeError(L.gdr_status_string(st).decode())
+
+    ms_per_step = wall_ms_per_step(step, warmup, steps)
+    tokens = inp["B"] * inp["T"]
+    value = tokens / (ms_per_step * 1e-3)
+
+    # per-stage launch times with events on the launch stream, same kernels and order
+    views = gdr.workspace_views(p, ws)
+    cidx, coff = views["chunk_idx"], views["chunk_off"]
+    fstages = {
+        "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], cidx, coff),
+        "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], cidx, coff, views["Tm"],
+                                               views["kscale"]),
+        "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff, views["Tm"], views["w"],
+                                 views["u"]),
+        "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
+                                   views["v_new"], ht, views["kscale"]),
+        "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
+    }
+    reps = max(5, min(steps, 50))
+    fwd_ms = event_stage_ms(stream, fstages, reps)
+    T_seq = inp["B"] * inp["T"] / inp["N"]
+    units = tokens * w.HV
+    per_unit = stage_bytes_per_token_head(w, T_seq)
+    fwd_total_ms = sum(fwd_ms.values())
+    rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
+           "stage_ms": {"forward": fwd_ms}, "parity": parity,
+           "forward_hbm_frac": sum(per_unit.values()) * units / (fwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    rec["roofline"] = roofline(per_unit, fwd_ms, units, w.name, list(per_unit))
+    if backward:
+        bv = gdr.bwd_workspace_views(p, bws)
+        bidx, boff = bv["chunk_idx"], bv["chunk_off"]
+        bstages = {
+            "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], bidx, boff),
+            "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], bidx, boff, bv["Tm"],
+                                                   bv["kscale"]),
+            "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], bidx, boff, bv["Tm"], bv["w"],
+                                     bv["u"]),
+            "fwd_h": lambda: gdr.fwd_h(p, d["k"], bv["w"], bv["u"], d["g"], bidx, boff, d["h0"], bv["h"],
+                                       bv["v_new"], None, bv["kscale"]),
+            "bwd_intra": lambda: gdr.bwd_intra(p, d["q"], d["k"], d["g"], d["do"], bidx, boff, bv["de_local"],
+                                               bv["qscale"]),
+            "bwd_dh": lambda: gdr.bwd_dh(p, d["q"], d["k"], bv["w"], d["do"], bv["de_local"], bv["qscale"],
+                                         bv["kscale"], bidx, boff, d["dht"], bv["dh"], dh0),
+            "bwd_dqkvg": lambda: gdr.bwd_dqkvg(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], bv["Tm"],
+                                               bv["h"], bv["v_new"], bv["dh"], bidx, boff, *grads),
+        }
+        bwd_ms = event_stage_ms(stream, bstages, reps)
+        bper = bwd_stage_bytes_per_token_head(w, T_seq)
+        rec["stage_ms"]["backward"] = bwd_ms
+        bwd_total_ms = sum(bwd_ms.values())
+        rec["backward_hbm_frac"] = sum(bper.values()) * units / (bwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
+        rec["backward_ms"] = bwd_total_ms
+        # the dominant kernel of a forward + backward step is taken among the
+        # backward's own stages (the forward's stages are reported separately)
+        rec["roofline"] = roofline(bper, bwd_ms, units, w.name, [n for n in bper if n.startswith("bwd_")])
+        rec["forward_roofline"] = roofline(per_unit, fwd_ms, units, w.name, list(per_unit))
+    if breakdown:
+        for part, ms in rec["stage_ms"].items():
+            print(f"{label} {part} per-stage ms: " + ", ".join(f"{n}={v:.4f}" for n, v in ms.items()),
+                  file=sys.stderr)
+    return rec, inp
+
+
+def workloads_inputs(w):
+    import workloads
+    return workloads.make_inputs(w)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +339,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gdn_dense_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the long-sequence forward + backward record of the default run")
     ap.add_argument("--breakdown", action="store_true", help="per-stage times on stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (known bytes, to scale the "
@@ -148,109 +367,31 @@ def main():
     import workloads
 
     w = workloads.CONFIGS[args.workload]
-    inp = workloads.make_inputs(w)
-    dev = torch.device("cuda:0")
-    d = {k: (inp[k].to(dev) if isinstance(inp.get(k), torch.Tensor) else inp.get(k))
-         for k in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
-    kw = dict(scale=inp["scale"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
-              initial_state=d["h0"], output_final_state=True,
-              use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
-    o, ht, ws = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], return_workspace=True, **kw)
-    torch.cuda.synchronize()
-    eo, eh, tol = parity_gate(w, inp, o.cpu(), ht.cpu())
-    print(f"parity gate ({args.workload}, sequence 0): err_ratio o={eo:.2e} ht={eh:.2e} (tol {tol:.0e})",
-          file=sys.stderr, flush=True)
-    if not (eo <= tol and eh <= tol):
-        print("parity check failed: refusing to report throughput", file=sys.stderr)
-        sys.exit(1)
-
-    L = gdr.lib()
-    p = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
-                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
-    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
-    stream = torch.cuda.current_stream(dev)
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    fwd_args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]),
-                P(d["h0"]), P(o), P(ht), P(ws), ctypes.c_size_t(ws.numel()), sp)
-
-    def step():
-        st = L.gdr_chunk_fwd(*fwd_args)
-        if st != 0:
-            raise RuntimeError(L.gdr_status_string(st).decode())
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-    tokens = inp["B"] * inp["T"]
-    value = tokens / (wall / args.steps)
-
-    # per-stage launch times with events on the launch stream, same kernels and order
-    views = gdr.workspace_views(p, ws)
-    cidx, coff = views["chunk_idx"], views["chunk_off"]
-    stages = {
-        "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], cidx, coff),
-        "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], cidx, coff, views["Tm"],
-                                               views["kscale"]),
-        "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff, views["Tm"], views["w"],
-                                 views["u"]),
-        "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
-                                   views["v_new"], ht, views["kscale"]),
-        "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
-    }
-    names = list(stages)
-    acc = {n: 0.0 for n in names}
-    reps = max(5, args.steps)
-    for _ in range(2):
-        for n in names:
-            stages[n]()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
-    for r in range(reps):
-        evs[r][0].record(stream)
-        for i, n in enumerate(names):
-            stages[n]()
-            evs[r][i + 1].record(stream)
-    torch.cuda.synchronize()
-    for r in range(reps):
-        for i, n in enumerate(names):
-            acc[n] += evs[r][i].elapsed_time(evs[r][i + 1])
-    avg_ms = {n: acc[n] / reps for n in names}
-    if args.breakdown:
-        print("per-stage ms: " + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr)
-
-    T_seq = inp["B"] * inp["T"] / inp["N"]
-    per_unit = stage_bytes_per_token_head(w, T_seq)
-    units = tokens * w.HV
-    dom = max(per_unit, key=lambda n: avg_ms[n])
-    alg_bytes = per_unit[dom] * units
-    achieved = alg_bytes / (avg_ms[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(dom, w.name)
-    fwd_bytes = sum(per_unit.values()) * units
-
+    rec, inp = measure(gdr, w, args.steps, args.warmup, args.breakdown, w.name)
     line = {
         "metric": "tokens/sec and % HBM/MFMA roofline, chunk GDN fwd (+bwd) on 1 MI355X",
-        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, logsigmoid gates, sigmoid beta)",
         "config": {"workload": w.name, "B": inp["B"], "T": inp["T"], "H": w.H, "HV": w.HV, "K": w.K,
-                   "V": w.V, "chunk_size": w.chunk_size, "pass": "forward",
+                   "V": w.V, "chunk_size": w.chunk_size,
+                   "pass": "forward+backward" if w.backward else "forward",
                    "gate": "per-channel" if w.per_channel_gate else "scalar",
                    "l2norm_in_kernel": w.l2norm_in_kernel, "parallelism": "single GPU"},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "bytes_per_unit": per_unit[dom], "units": units, "avg_launch_ms": avg_ms[dom]},
-        "stage_ms": avg_ms,
-        "forward_hbm_frac": fwd_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "parity": {"o": eo, "ht": eh, "tol": tol},
     }
+    line.update({k: v for k, v in rec.items() if k not in ("value", "ms_per_step", "tokens")})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
+    del inp
+    if not w.backward and not args.no_backward:
+        torch.cuda.empty_cache()
+        wb = workloads.CONFIGS["long_bf16"]
+        brec, binp = measure(gdr, wb, max(3, args.steps // 5), max(2, args.warmup // 5), args.breakdown,
+                             wb.name)
+        line["backward"] = {"workload": wb.name, "pass": "forward+backward", "B": binp["B"], "T": binp["T"],
+                            "H": wb.H, "HV": wb.HV, "K": wb.K, "V": wb.V, "chunk_size": wb.chunk_size,
+                            "tokens_per_s": brec["value"], "ms_per_step": brec["ms_per_step"],
+                            **{k: v for k, v in brec.items() if k not in ("value", "ms_per_step")}}
     print(json.dumps(line))
 
 
