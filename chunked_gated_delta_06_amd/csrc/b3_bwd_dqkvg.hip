@@ -30,7 +30,10 @@
 // pairs.  The value dimension is streamed in tiles of 32 columns: per tile the
 // kernel stages h^T, dh^T, dO, v and e^T, forms dE and Y (writing dv) and
 // accumulates the C x K and C x C products above in registers; a wave owns a
-// fixed set of 16 x 16 output blocks for the whole chunk.
+// fixed set of 16 x 16 output blocks (one row block) for the whole chunk.  The
+// next head's T tile, gate and beta are fetched into registers while the
+// current head's last value tile is computed; dq and dk leave through an LDS
+// tile as 16-byte row pieces.  Cross-lane sums use DPP row permutations.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -38,20 +41,29 @@ namespace gdr {
 
 namespace {
 
-template <typename T, int C, int K>
+template <typename T, int C, int K, int NW>
 struct B3 {
-  static constexpr int NT = 256;
+  static constexpr int NT = 64 * NW;
   static constexpr int VT = 32;
   static constexpr int EB = sizeof(T);
-  static constexpr int PK = K + 32 / EB;     // q, k, h^T, dh^T rows
+  static constexpr int CPR = K / 8;
+  static constexpr int PK = K + 32 / EB;     // q, k, h^T, dh^T, dq / dk out rows
   static constexpr int PC = C + 32 / EB;     // T, e^T, P^T, D rows
   static constexpr int PV = VT + 32 / EB;    // dO, v, dE, Y rows
   static constexpr int NRB = C / 16, NKB = K / 16, NVB = VT / 16;
   static constexpr int KSK = K / 32, KSC = C / 32;
-  static constexpr int SCK = NRB * NKB / 4;  // C x K blocks per wave
-  static constexpr int SCC = NRB * NRB / 4;  // C x C blocks per wave
-  static constexpr int SCV = NRB * NVB / 4;  // C x VT blocks per wave
-  static_assert(SCK * 4 == NRB * NKB && SCC * 4 == NRB * NRB && SCV * 4 == NRB * NVB, "block split");
+  static_assert(NW % NRB == 0, "a wave owns one row block");
+  // 16 x 16 blocks per wave: block b = wave + NW * slot
+  static constexpr int NBK = NRB * NKB, NBC = NRB * NRB, NBV = NRB * NVB;
+  static constexpr int SCK = (NBK + NW - 1) / NW;
+  static constexpr int SCC = (NBC + NW - 1) / NW;
+  static constexpr int SCV = (NBV + NW - 1) / NW;
+  // 8-element pieces per thread of the staged tiles
+  static constexpr int NPQ = (C * CPR + NT - 1) / NT;        // q / k tiles
+  static constexpr int NPT = (C * C / 8 + NT - 1) / NT;      // T tile
+  static constexpr int NPH = (VT * CPR + NT - 1) / NT;       // h^T / dh^T tiles
+  static constexpr int NPO = (C * VT / 8 + NT - 1) / NT;     // dO / v tiles
+  static constexpr int NPE = (VT * C / 8 + NT - 1) / NT;     // e^T tile
   // LDS byte offsets
   static constexpr size_t oQ = 0;
   static constexpr size_t oK = oQ + (size_t)C * PK * EB;
@@ -68,10 +80,12 @@ struct B3 {
   static constexpr size_t lY = lDE + FCV;
   static constexpr size_t lPT = lY + FCV;
   static constexpr size_t loop_bytes = lPT + FCC;
-  static constexpr size_t pD1 = 0, pD2 = FCC, post_bytes = 2 * FCC;
+  static constexpr size_t pD1 = 0, pD2 = FCC;
+  static constexpr size_t pOq = 0, pOk = (size_t)C * PK * EB;
+  static constexpr size_t post_bytes = 2 * FCC > 2 * pOk ? 2 * FCC : 2 * pOk;
   static constexpr size_t oRows = oLoop + (loop_bytes > post_bytes ? loop_bytes : post_bytes);
-  // rows: G, rq, rk, beta; per-wave dG, dbeta, q.dq, k.dk partials; 8 scalars
-  static constexpr size_t rows_floats = 4 * C + 4 * 4 * C + 8;
+  // rows: G, rq, rk, beta; per-wave dG, dbeta, q.dq, k.dk partials; 2 NW scalars
+  static constexpr size_t rows_floats = 4 * C + 4 * NW * C + 2 * NW;
   static constexpr size_t total = oRows + rows_floats * 4;
   static constexpr bool fits = total <= 160 * 1024;
 };
@@ -85,13 +99,14 @@ GDR_DEV FTile<T> ftile(char* base, int rows) {
   return f;
 }
 
-template <typename T, int C, int K, bool GVA>
-__global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
-  using Cfg = B3<T, C, K>;
-  constexpr int VT = Cfg::VT, PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV;
+template <typename T, int C, int K, bool GVA, int NW>
+__global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
+  using Cfg = B3<T, C, K, NW>;
+  constexpr int NT = Cfg::NT, VT = Cfg::VT, PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, CPR = Cfg::CPR;
   constexpr int NRB = Cfg::NRB, NVB = Cfg::NVB, KSK = Cfg::KSK, KSC = Cfg::KSC;
+  constexpr int NBK = Cfg::NBK, NBC = Cfg::NBC, NBV = Cfg::NBV;
   constexpr int SCK = Cfg::SCK, SCC = Cfg::SCC, SCV = Cfg::SCV;
-  constexpr int CPR = K / 8;
+  constexpr int NPQ = Cfg::NPQ, NPT = Cfg::NPT, NPH = Cfg::NPH, NPO = Cfg::NPO, NPE = Cfg::NPE;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
@@ -117,53 +132,132 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
   const FTile<T> fPT = ftile<T, PC>(loop + Cfg::lPT, C);
   const FTile<T> fD1 = ftile<T, PC>(loop + Cfg::pD1, C);
   const FTile<T> fD2 = ftile<T, PC>(loop + Cfg::pD2, C);
+  T* sOq = reinterpret_cast<T*>(loop + Cfg::pOq);
+  T* sOk = reinterpret_cast<T*>(loop + Cfg::pOk);
   float* sG = reinterpret_cast<float*>(smem + Cfg::oRows);
   float* sRq = sG + C;
   float* sRk = sRq + C;
   float* sB = sRk + C;
-  float* sRowG = sB + C;          // [4][C]
-  float* sRowB = sRowG + 4 * C;   // [4][C]
-  float* sDotQ = sRowB + 4 * C;   // [4][C]
-  float* sDotK = sDotQ + 4 * C;   // [4][C]
-  float* sRed = sDotK + 4 * C;    // [8]
+  float* sRowG = sB + C;           // [NW][C]
+  float* sRowB = sRowG + NW * C;   // [NW][C]
+  float* sDotQ = sRowB + NW * C;   // [NW][C]
+  float* sDotK = sDotQ + NW * C;   // [NW][C]
+  float* sRed = sDotK + NW * C;    // [2 NW]
 
   const T* __restrict__ qp = static_cast<const T*>(a.q);
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ vp = static_cast<const T*>(a.v);
   const T* __restrict__ dop = static_cast<const T*>(a.d_o);
 
-  // ---- q, k tiles (rows past L are zero) and their row norms
-  {
-    constexpr int NP = C * CPR;
+  // ---- global fetches into registers (staged into LDS later)
+  struct HeadRegs {
+    Frag<T> t[NPT];
+    float g, b;
+  };
+  struct TileRegs {
+    Frag<T> h[NPH], dh[NPH], o[NPO], v[NPO], e[NPE];
+  };
+  auto fetch_head = [&](HeadRegs& R, int64_t j) {
+    const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
 #pragma unroll
-    for (int i = 0; i < (NP + 255) / 256; ++i) {
-      const int idx = tid + 256 * i, t = idx / CPR, d8 = (idx % CPR) * 8;
-      const bool in = idx < NP && t < L;
-      const Frag<T> q8 = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
-      const Frag<T> k8 = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
-      if (idx < NP) {
-        st8(&sQ[t * PK + d8], q8);
-        st8(&sK[t * PK + d8], k8);
+    for (int i = 0; i < NPT; ++i) {
+      const int idx = tid + NT * i;
+      R.t[i] = (idx < C * C / 8) ? ld8(tp + 8 * idx) : frag_zero<T>();
+    }
+    R.g = (tid < L) ? a.g[(t0 + tid) * HV + j] : 0.f;
+    R.b = (tid < L) ? a.beta[(t0 + tid) * HV + j] : 0.f;
+  };
+  auto fetch_tile = [&](TileRegs& R, int64_t j, int64_t v0) {
+    const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
+    const T* dhb = static_cast<const T*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
+    const T* eb = static_cast<const T*>(a.v_new) + ((c * HV + j) * V + v0) * (int64_t)C;
+#pragma unroll
+    for (int i = 0; i < NPH; ++i) {
+      const int idx = tid + NT * i;
+      const bool in = idx < VT * CPR;
+      R.h[i] = in ? ld8(hb + 8 * idx) : frag_zero<T>();
+      R.dh[i] = in ? ld8(dhb + 8 * idx) : frag_zero<T>();
+    }
+#pragma unroll
+    for (int i = 0; i < NPO; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      const bool in = idx < C * VT / 8 && t < L;
+      R.o[i] = in ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
+      R.v[i] = in ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
+    }
+#pragma unroll
+    for (int i = 0; i < NPE; ++i) {
+      const int idx = tid + NT * i;
+      R.e[i] = (idx < VT * C / 8) ? ld8(eb + 8 * idx) : frag_zero<T>();
+    }
+  };
+  float lr = 0.f;     // sum of S0 o dS1 over the head (this thread's share)
+  auto stage_tile = [&](const TileRegs& R) {
+#pragma unroll
+    for (int i = 0; i < NPH; ++i) {
+      const int idx = tid + NT * i, v = idx / CPR, d8 = (idx % CPR) * 8;
+      if (idx < VT * CPR) {
+        st8(&sH[v * PK + d8], R.h[i]);
+        st8(&sDH[v * PK + d8], R.dh[i]);
       }
-      const f32x8 xq = q8.f32(), xk = k8.f32();
+      const f32x8 fx = R.h[i].f32(), fy = R.dh[i].f32();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lr += fx[e] * fy[e];
+    }
+#pragma unroll
+    for (int i = 0; i < NPO; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      if (idx < C * VT / 8) {
+        st8(&sDO[t * PV + v8], R.o[i]);
+        st8(&sV[t * PV + v8], R.v[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPE; ++i) {
+      const int idx = tid + NT * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+      if (idx < VT * C / 8) st8(&sE[v * PC + t8], R.e[i]);
+    }
+  };
+
+  HeadRegs HR;
+  {
+    // q, k tiles (rows past L are zero) and their row norms, with the first
+    // head's T tile, gate and beta already on the way
+    Frag<T> qr[NPQ], kr[NPQ];
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      const bool in = idx < C * CPR && t < L;
+      qr[i] = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+      kr[i] = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+    }
+    fetch_head(HR, h * ng);
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      if (idx < C * CPR) {
+        st8(&sQ[t * PK + d8], qr[i]);
+        st8(&sK[t * PK + d8], kr[i]);
+      }
+      const f32x8 xq = qr[i].f32(), xk = kr[i].f32();
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         sq += xq[e] * xq[e];
         sk += xk[e] * xk[e];
       }
-      sq = lanes_sum(sq, CPR);
-      sk = lanes_sum(sk, CPR);
-      if (idx < NP && d8 == 0) {
+      sq = lanes_sum_t<CPR>(sq);
+      sk = lanes_sum_t<CPR>(sk);
+      if (idx < C * CPR && d8 == 0) {
         sRq[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
         sRk[t] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
       }
     }
-    for (int i = tid; i < 8 * C; i += 256) sDotQ[i] = 0.f;   // sDotQ and sDotK
+    for (int i = tid; i < 2 * NW * C; i += NT) sDotQ[i] = 0.f;   // sDotQ and sDotK
   }
 
-  // a wave's fixed output blocks: slot i of a product with NRB row blocks is
-  // block b = wv + 4 i, row block b % NRB (= wv % NRB), column block b / NRB
+  // a wave's fixed output blocks: slot i of a product is block b = wv + NW i,
+  // row block b % NRB (= wv % NRB), column block b / NRB
   const int rb = wv % NRB;
   f32x4 dq[SCK], dk[SCK];          // dq^, dk^ of the current value head
   f32x4 sq_[GVA ? SCK : 1], sk_[GVA ? SCK : 1];
@@ -175,28 +269,27 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
   for (int jj = 0; jj < ng; ++jj) {
     const int64_t j = h * ng + jj;
     // ---- per-head rows and the T tile
-    if (wv == 0) {
-      const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
-      const float G = wave_incl_scan(gv, lane);
-      if (lane < C) sG[lane] = G;
-    }
-    for (int i = tid; i < C; i += 256) sB[i] = (i < L) ? a.beta[(t0 + i) * HV + j] : 0.f;
-    for (int i = tid; i < 8 * C; i += 256) sRowG[i] = 0.f;     // sRowG and sRowB
-    if (tid < 8) sRed[tid] = 0.f;
     {
-      const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
-      for (int idx = tid; idx < C * C / 8; idx += 256) {
-        const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
-        st8(&sT[r * PC + c8], ld8(tp + 8 * idx));
+      const float G = wave_incl_scan(HR.g, lane);
+      if (wv == 0 && lane < C) sG[lane] = G;
+      if (tid < C) sB[tid] = HR.b;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const int idx = tid + NT * i, r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+        if (idx < C * C / 8) st8(&sT[r * PC + c8], HR.t[i]);
       }
     }
+    for (int i = tid; i < 2 * NW * C; i += NT) sRowG[i] = 0.f;     // sRowG and sRowB
+    if (tid < 2 * NW) sRed[tid] = 0.f;
+    lr = 0.f;
     lds_barrier();
     const float GL = sG[L - 1];
 
     // ---- P^T tile: P^T[t][r] = P[r][t] (norms, gate, causal mask applied)
 #pragma unroll
     for (int i = 0; i < SCC; ++i) {
-      const int b = wv + 4 * i, tb = b % NRB, cb = b / NRB;
+      const int b = wv + NW * i, tb = b % NRB, cb = b / NRB;
+      if (b >= NBC) continue;
       f32x4 acc = zero4();
       if (tb <= cb) {
 #pragma unroll
@@ -217,40 +310,24 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
     for (int i = 0; i < SCK; ++i) dQg[i] = TdW[i] = dKt[i] = zero4();
 #pragma unroll
     for (int i = 0; i < SCC; ++i) dP[i] = dA[i] = zero4();
-    float lr = 0.f;     // sum of S0 o dS1 (this thread's share)
-    lds_barrier();
 
-    const T* hbase = static_cast<const T*>(a.h) + (c * HV + j) * V * (int64_t)K;
-    const T* dhbase = static_cast<const T*>(a.dh) + (c * HV + j) * V * (int64_t)K;
-    const T* ebase = static_cast<const T*>(a.v_new) + (c * HV + j) * V * (int64_t)C;
     for (int64_t v0 = 0; v0 < V; v0 += VT) {
-      // ---- stage the value tile
-      for (int idx = tid; idx < VT * CPR; idx += 256) {
-        const int v = idx / CPR, d8 = (idx % CPR) * 8;
-        const Frag<T> x = ld8(hbase + v0 * K + 8 * idx);
-        const Frag<T> y = ld8(dhbase + v0 * K + 8 * idx);
-        st8(&sH[v * PK + d8], x);
-        st8(&sDH[v * PK + d8], y);
-        const f32x8 fx = x.f32(), fy = y.f32();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lr += fx[e] * fy[e];
-      }
-      for (int idx = tid; idx < C * VT / 8; idx += 256) {
-        const int t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
-        const bool in = t < L;
-        st8(&sDO[t * PV + v8], in ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>());
-        st8(&sV[t * PV + v8], in ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>());
-      }
-      for (int idx = tid; idx < VT * C / 8; idx += 256) {
-        const int v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
-        st8(&sE[v * PC + t8], ld8(ebase + v0 * C + 8 * idx));
+      {
+        // all of the tile's loads are issued before the first LDS store; a
+        // register prefetch of the next tile across the compute phases would
+        // not fit the register budget (about 500 live registers per lane)
+        TileRegs TR;
+        fetch_tile(TR, j, v0);
+        stage_tile(TR);
       }
       lds_barrier();
+      if (v0 + VT >= V && jj + 1 < ng) fetch_head(HR, j + 1);
 
       // ---- dE[t][v] = scale (P^T dO)[t][v] + kappa_t rk_t (K dS1)[t][v]
 #pragma unroll
       for (int i = 0; i < SCV; ++i) {
-        const int b = wv + 4 * i, tb = b % NRB, vb = b / NRB;
+        const int b = wv + NW * i, tb = b % NRB, vb = b / NRB;
+        if (b >= NBV) continue;
         f32x4 a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int s = 0; s < KSC; ++s) {
@@ -272,7 +349,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
       // ---- Y^T[v][t] = (dE^T T)[v][t]; dv = beta Y; dbeta += v . Y
 #pragma unroll
       for (int i = 0; i < SCV; ++i) {
-        const int b = wv + 4 * i, vb = b % NVB, tb = b / NVB;
+        const int b = wv + NW * i, vb = b % NVB, tb = b / NVB;
+        if (b >= NBV) continue;
         f32x4 acc = zero4();
 #pragma unroll
         for (int s = 0; s < KSC; ++s) {
@@ -295,7 +373,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
         const Frag<T> aE = lds_col8(sE, PC, 0, 16 * rb, lane);
 #pragma unroll
         for (int i = 0; i < SCK; ++i) {
-          const int db = (wv + 4 * i) / NRB;
+          const int b = wv + NW * i, db = b / NRB;
+          if (b >= NBK) continue;
           const Frag<T> bS = lds_col8(sH, PK, 0, 16 * db, lane);
           const Frag<T> bD = lds_col8(sDH, PK, 0, 16 * db, lane);
           mma(dQg[i], aO, bS);
@@ -304,7 +383,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
         }
 #pragma unroll
         for (int i = 0; i < SCC; ++i) {
-          const int cb = (wv + 4 * i) / NRB;
+          const int b = wv + NW * i, cb = b / NRB;
+          if (b >= NBC) continue;
           const Frag<T> bE = lds_col8(sE, PC, 0, 16 * cb, lane);
           mma(dP[i], aO, bE);
           mma_split(dA[i], aY, bE);
@@ -314,14 +394,16 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
     }
 
     // ---- S0 . dS1 (for the exp(G_L) factor of the state hand-off)
-    lr = lanes_sum(lr, 64);
+    lr = lanes_sum_t<64>(lr);
     if (lane == 0) sRed[wv] = lr;
 
     // ---- D = dP o exp(G_r - G_t) (causal); dG from P
     f32x4 Dv[SCC];
 #pragma unroll
     for (int i = 0; i < SCC; ++i) {
-      const int cb = (wv + 4 * i) / NRB;
+      const int b = wv + NW * i, cb = b / NRB;
+      Dv[i] = zero4();
+      if (b >= NBC) continue;
       const int t = 16 * cb + r16;
       float colsum = 0.f;
 #pragma unroll
@@ -331,7 +413,7 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
         const float dps = scale * dP[i][e];
         Dv[i][e] = ok ? dps * __expf(sG[r] - sG[t]) : 0.f;
         const float pd = ok ? dps * fPT.get(t, r) : 0.f;
-        const float rs = lanes_sum(pd, 16);
+        const float rs = lanes_sum_t<16>(pd);
         if (r16 == 0) sRowG[wv * C + r] += rs;
         colsum += pd;
       }
@@ -343,7 +425,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
     // ---- D tiles; row-dot terms of dG / dbeta; dq^, dk^ row-scaled parts
 #pragma unroll
     for (int i = 0; i < SCC; ++i) {
-      const int cb = (wv + 4 * i) / NRB;
+      const int b = wv + NW * i, cb = b / NRB;
+      if (b >= NBC) continue;
       const int t = 16 * cb + r16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -356,9 +439,10 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
       f32x4 qd = zero4(), kw = zero4(), kk = zero4();
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
         dQg[i] *= scale;
         TdW[i] = -TdW[i];
+        if (b >= NBK) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rb + 4 * g4 + e;
@@ -372,7 +456,7 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * g4 + e;
-        const float q1 = lanes_sum(qd[e], 16), k1 = lanes_sum(kw[e], 16), k2 = lanes_sum(kk[e], 16);
+        const float q1 = lanes_sum_t<16>(qd[e]), k1 = lanes_sum_t<16>(kw[e]), k2 = lanes_sum_t<16>(kk[e]);
         const bool ok = r < L;
         const float gam = __expf(sG[r]), kap = __expf(GL - sG[r]);
         const float tw = ok ? gam * sRk[r] * k1 : 0.f;
@@ -389,14 +473,15 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
         }
       }
       last = group4_sum(last);
-      if (lane == 0) sRed[4 + wv] = last;
+      if (lane == 0) sRed[NW + wv] = last;
     }
     lds_barrier();
 
     // ---- dq^ += D~ K (D~ = D rk_t), dk^ += D^^T Q (D^ = D rq_r)
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
-      const int db = (wv + 4 * i) / NRB;
+      const int b = wv + NW * i, db = b / NRB;
+      if (b >= NBK) continue;
 #pragma unroll
       for (int s = 0; s < KSC; ++s) {
         if (32 * s <= 16 * rb + 15)
@@ -410,7 +495,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
     // ---- dA (strictly lower): dbeta, dG and the Dk tiles
 #pragma unroll
     for (int i = 0; i < SCC; ++i) {
-      const int cb = (wv + 4 * i) / NRB;
+      const int b = wv + NW * i, cb = b / NRB;
+      if (b >= NBC) continue;
       f32x4 kk = zero4();
       if (cb <= rb) {
 #pragma unroll
@@ -429,7 +515,7 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
         const float dbp = ok ? da * abar : 0.f;
         const float dkv = ok ? sB[t] * da * ex : 0.f;
         const float ad = sB[t] * dbp;
-        const float rb1 = lanes_sum(dbp, 16), rg = lanes_sum(ad, 16);
+        const float rb1 = lanes_sum_t<16>(dbp), rg = lanes_sum_t<16>(ad);
         if (r16 == 0) {
           sRowB[wv * C + t] += rb1;
           sRowG[wv * C + t] += rg;
@@ -446,7 +532,8 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
     // ---- dk^ += Dk~ K + Dk^^T K
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
-      const int db = (wv + 4 * i) / NRB;
+      const int b = wv + NW * i, db = b / NRB;
+      if (b >= NBK) continue;
 #pragma unroll
       for (int s = 0; s < KSC; ++s) {
         if (32 * s <= 16 * rb + 15)
@@ -466,31 +553,39 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
 
     // ---- dg = reverse cumsum of dG over the chunk, dbeta
     if (wv == 0) {
-      const float lrt = sRed[0] + sRed[1] + sRed[2] + sRed[3];
-      const float lst = sRed[4] + sRed[5] + sRed[6] + sRed[7];
+      float lrt = 0.f, lst = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        lrt += sRed[w];
+        lst += sRed[NW + w];
+      }
       const int tr = C - 1 - lane;            // this lane's row, reversed
       float x = 0.f;
       if (lane < C && tr < L) {
-        x = sRowG[tr] + sRowG[C + tr] + sRowG[2 * C + tr] + sRowG[3 * C + tr];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += sRowG[w * C + tr];
         if (tr == L - 1) x += lst + __expf(GL) * lrt;
       }
       const float y = wave_incl_scan(x, lane);
       if (lane < C && tr < L) a.dg[(t0 + tr) * HV + j] = y;
       if (lane < L) {
-        const float db = sRowB[lane] + sRowB[C + lane] + sRowB[2 * C + lane] + sRowB[3 * C + lane];
+        float db = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += sRowB[w * C + lane];
         a.dbeta[(t0 + lane) * HV + j] = db;
       }
     }
     lds_barrier();
   }
 
-  // ---- group sums, L2-norm backward, dq / dk
+  // ---- group sums, L2-norm backward, dq / dk through LDS as 16-byte rows
   auto finish = [&](const f32x4 (&DQ)[SCK], const f32x4 (&DK)[SCK]) {
     if (a.l2norm) {
       f32x4 qd = zero4(), kd = zero4();
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
+        if (b >= NBK) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rb + 4 * g4 + e;
@@ -501,7 +596,7 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * g4 + e;
-        const float q1 = lanes_sum(qd[e], 16), k1 = lanes_sum(kd[e], 16);
+        const float q1 = lanes_sum_t<16>(qd[e]), k1 = lanes_sum_t<16>(kd[e]);
         if (r16 == 0) {
           sDotQ[wv * C + r] = q1;
           sDotK[wv * C + r] = k1;
@@ -509,26 +604,40 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
       }
       lds_barrier();
     }
-    T* dqp = static_cast<T*>(a.dq);
-    T* dkp = static_cast<T*>(a.dk);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * rb + 4 * g4 + e;
-      if (r >= L) continue;
       float cq = 0.f, ck = 0.f;
       const float rq = sRq[r], rk = sRk[r];
       if (a.l2norm) {
-        cq = rq * rq * (sDotQ[r] + sDotQ[C + r] + sDotQ[2 * C + r] + sDotQ[3 * C + r]);
-        ck = rk * rk * (sDotK[r] + sDotK[C + r] + sDotK[2 * C + r] + sDotK[3 * C + r]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          cq += sDotQ[w * C + r];
+          ck += sDotK[w * C + r];
+        }
+        cq *= rq * rq;
+        ck *= rk * rk;
       }
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int d = 16 * ((wv + 4 * i) / NRB) + r16;
+        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
+        if (b >= NBK) continue;
         const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
         const float oq = a.l2norm ? rq * (DQ[i][e] - cq * qv) : DQ[i][e];
         const float okv = a.l2norm ? rk * (DK[i][e] - ck * kv) : DK[i][e];
-        dqp[((t0 + r) * H + h) * K + d] = (T)oq;
-        dkp[((t0 + r) * H + h) * K + d] = (T)okv;
+        sOq[r * PK + d] = (T)oq;
+        sOk[r * PK + d] = (T)okv;
+      }
+    }
+    lds_barrier();
+    T* dqp = static_cast<T*>(a.dq);
+    T* dkp = static_cast<T*>(a.dk);
+#pragma unroll
+    for (int i = 0; i < NPQ; ++i) {
+      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      if (idx < C * CPR && t < L) {
+        st8(dqp + ((t0 + t) * H + h) * K + d8, ld8(&sOq[t * PK + d8]));
+        st8(dkp + ((t0 + t) * H + h) * K + d8, ld8(&sOk[t * PK + d8]));
       }
     }
   };
@@ -539,16 +648,25 @@ __global__ __launch_bounds__(256) void b3_bwd_dqkvg(Args a) {
   }
 }
 
+// Four waves (one per SIMD): the kernel holds about 400 live registers per
+// lane at chunk 64, which two waves per SIMD (256 each) cannot hold without
+// spilling.
+template <typename T, int C, int K>
+constexpr int b3_waves() {
+  return 4;
+}
+
 template <typename T, int C, int K>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  if constexpr (!B3<T, C, K>::fits) {
+  constexpr int NW = b3_waves<T, C, K>();
+  if constexpr (!B3<T, C, K, NW>::fits) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
     const dim3 grid((unsigned)a.NTmax, (unsigned)a.H);
     if (a.HV == a.H)
-      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, false, NW>), grid, dim3(64 * NW), 0, s, a);
     else
-      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, true>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, true, NW>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
   }
 }
@@ -573,7 +691,7 @@ hipError_t launch_c(const Args& a, hipStream_t s) {
 bool bwd_fused_fits(int dtype, int C, int K) {
   bool ok = false;
 #define GDR_B3_FITS(TT, CC, KK) \
-  if (C == CC && K == KK) ok = B3<TT, CC, KK>::fits;
+  if (C == CC && K == KK) ok = B3<TT, CC, KK, b3_waves<TT, CC, KK>()>::fits;
   if (dtype == GDR_BF16) {
     GDR_B3_FITS(bf16, 32, 32) GDR_B3_FITS(bf16, 32, 64) GDR_B3_FITS(bf16, 32, 128)
     GDR_B3_FITS(bf16, 64, 32) GDR_B3_FITS(bf16, 64, 64) GDR_B3_FITS(bf16, 64, 128)

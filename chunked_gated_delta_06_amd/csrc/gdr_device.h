@@ -249,16 +249,40 @@ GDR_DEV float wave_incl_scan(float x, int lane) {
   return x;
 }
 
+// Cross-lane sums.  Inside each 16-lane row they stay in the vector ALU: DPP
+// quad swaps, then the half-row and row mirrors (after each step every lane of
+// a group holds its group's sum).  Across rows they use __shfl_xor.  Every
+// lane of the wave must be active.
+template <int CTRL> GDR_DEV float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N a power of two <= 64).
+template <int N> GDR_DEV float lanes_sum_t(float x) {
+  if constexpr (N >= 2) x += dpp_f<0xB1>(x);     // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_f<0x4E>(x);     // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_f<0x141>(x);    // row_half_mirror
+  if constexpr (N >= 16) x += dpp_f<0x140>(x);   // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+GDR_DEV float lanes_sum(float x, int n) {
+  switch (n) {
+    case 1: return x;
+    case 2: return lanes_sum_t<2>(x);
+    case 4: return lanes_sum_t<4>(x);
+    case 8: return lanes_sum_t<8>(x);
+    case 16: return lanes_sum_t<16>(x);
+    case 32: return lanes_sum_t<32>(x);
+    default: return lanes_sum_t<64>(x);
+  }
+}
+
 // Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
 GDR_DEV float group4_sum(float x) {
   x += __shfl_xor(x, 16, 64);
   x += __shfl_xor(x, 32, 64);
-  return x;
-}
-
-// Sum over aligned groups of n lanes (n a power of two <= 64).
-GDR_DEV float lanes_sum(float x, int n) {
-  for (int o = 1; o < n; o <<= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
 
