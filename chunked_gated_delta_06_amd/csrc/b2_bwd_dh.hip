@@ -15,7 +15,8 @@
 // matrix", section 2) plus the inter term of o.
 //
 // gfx950 mapping (as the forward scan): one workgroup per (sequence, value
-// head, 32 value columns).  Two compute waves own 16 columns of dS each as
+// head, 32 value columns, or 16 when that fills the chip better).  Each
+// compute wave owns 16 columns of dS as
 // K/16 fp32 MFMA accumulators; NWL loader waves fetch each chunk's k, q, w,
 // dO, de_local and kscale into registers three steps ahead and stage them into
 // LDS (two buffers when they fit, else one with a second barrier per step);
@@ -29,9 +30,9 @@ namespace gdr {
 
 namespace {
 
-template <typename T, int C, int K, int NWL>
+template <typename T, int C, int K, int NWC_, int NWL>
 struct B2S {
-  static constexpr int NWC = 2;
+  static constexpr int NWC = NWC_;
   static constexpr int NTL = 64 * NWL;
   static constexpr int BV = 16 * NWC;
   static constexpr int NE = C / 16, NS = K / 16, KSK = K / 32, KSC = C / 32;
@@ -69,9 +70,9 @@ struct B2S {
   };
 };
 
-template <typename T, int C, int K, int NWL>
-__global__ __launch_bounds__(64 * (2 + NWL)) void b2_bwd_dh(Args a) {
-  using Cfg = B2S<T, C, K, NWL>;
+template <typename T, int C, int K, int NWC_, int NWL>
+__global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
+  using Cfg = B2S<T, C, K, NWC_, NWL>;
   using Regs = typename Cfg::Regs;
   constexpr int NWC = Cfg::NWC, NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS;
   constexpr int KSK = Cfg::KSK, KSC = Cfg::KSC, CPR = Cfg::CPR, NLD = Cfg::NLD, NLO = Cfg::NLO;
@@ -292,11 +293,17 @@ constexpr int loader_waves() {
 template <typename T, int C, int K>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   constexpr int NWL = loader_waves<T, C, K>();
-  if constexpr (!B2S<T, C, K, NWL>::fits) {
+  if constexpr (!B2S<T, C, K, 2, NWL>::fits) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
-    const int64_t nblk = a.N * a.HV * (a.V / 32);
-    hipLaunchKernelGGL((b2_bwd_dh<T, C, K, NWL>), dim3((unsigned)nblk), dim3(64 * (2 + NWL)), 0, s, a);
+    // 32 value columns per workgroup, or 16 when the 32-column grid would
+    // leave compute units idle (as the forward scan)
+    const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+    if (nblk32 < kNumCUs) {
+      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 1, NWL>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 2, NWL>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+    }
     return hipGetLastError();
   }
 }
@@ -321,7 +328,7 @@ hipError_t launch_c(const Args& a, hipStream_t s) {
 bool bwd_scan_fits(int dtype, int C, int K) {
   bool ok = false;
 #define GDR_B2_FITS(TT, CC, KK) \
-  if (C == CC && K == KK) ok = B2S<TT, CC, KK, loader_waves<TT, CC, KK>()>::fits;
+  if (C == CC && K == KK) ok = B2S<TT, CC, KK, 2, loader_waves<TT, CC, KK>()>::fits;
   if (dtype == GDR_BF16) {
     GDR_B2_FITS(bf16, 32, 32) GDR_B2_FITS(bf16, 32, 64) GDR_B2_FITS(bf16, 32, 128)
     GDR_B2_FITS(bf16, 64, 32) GDR_B2_FITS(bf16, 64, 64) GDR_B2_FITS(bf16, 64, 128)

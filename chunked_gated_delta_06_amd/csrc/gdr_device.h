@@ -288,6 +288,9 @@ GDR_DEV float group4_sum(float x) {
 
 constexpr float kL2Eps = 1e-6f;
 
+// Compute units of one MI355X (8 XCDs x 32).
+constexpr int64_t kNumCUs = 256;
+
 // Workgroup index remap so that consecutive logical indices run on the same
 // XCD (MI355X dispatches workgroups to its 8 XCDs round-robin); blocks that
 // share input tiles then share an L2.

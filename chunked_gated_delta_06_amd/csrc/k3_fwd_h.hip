@@ -12,7 +12,8 @@
 // ("FLA operator-kernel correctness testing and coverage matrix", section 2).
 //
 // gfx950 mapping: one workgroup per (sequence, value head, BV = 16 NW value
-// columns); wave w owns 16 columns of S as K/16 16x16 fp32 MFMA accumulators
+// columns; the scalar-gate scan below uses 32, or 16 when that fills the chip
+// better); wave w owns 16 columns of S as K/16 16x16 fp32 MFMA accumulators
 // that never leave registers.
 //  * The chunk loop is software-pipelined: every chunk's w / k / u / gate data
 //    is fetched into registers two chunk steps before it is used (two register
@@ -540,8 +541,16 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
     // elements are fp32 or K = 256, to keep each loader's payload in registers)
     constexpr int NWL = (sizeof(T) == 4 || K == 256) ? 4 : 2;
     if constexpr (K3S<T, C, K, 2, NWL>::fits) {
-      const int64_t nblk = a.N * a.HV * (a.V / 32);
-      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL>), dim3((unsigned)nblk), dim3(64 * (2 + NWL)), 0, s, a);
+      // 32 value columns (two compute waves) per workgroup, or 16 (one) when
+      // the 32-column grid would leave compute units idle: the scan's step
+      // latency does not shrink with fewer columns, so more workgroups is the
+      // only way to use the whole chip on few long sequences
+      const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+      if (nblk32 < kNumCUs) {
+        hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+      }
       return hipGetLastError();
     }
   }
