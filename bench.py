@@ -93,28 +93,74 @@ def measured_traffic(stage, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=12.0):
-    """The per-token float64 oracle on a bounded sample of the workload: the
-    first sequence, all value heads, as many tokens as fit the time budget."""
+def cpu_baseline(w, inp, budget_s=20.0):
+    """The per-token float64 oracle on a bounded sample of the workload: whole
+    sequences in order, all value heads, until the time budget or the
+    workload ends; the chunked/WY oracle is timed on the first sequence."""
+    import torch
+    from oracle import chunked, recurrent
+    threads = torch.get_num_threads()
+    B, N = inp["B"], inp["N"]
+    cu = inp["cu_seqlens"]
+    step = 512
+    tokens, spent, seqs = 0, 0.0, 0
+    for n in range(N):
+        if spent >= budget_s:
+            break
+        if cu is None:
+            b, s0, e0 = n, 0, inp["T"]
+        else:
+            b, s0, e0 = 0, int(cu[n]), int(cu[n + 1])
+        S = inp["h0"][n:n + 1] if inp["h0"] is not None else None
+        for s in range(s0, e0, step):
+            if spent >= budget_s:
+                break
+            sl = slice(s, min(s + step, e0))
+            t0 = time.perf_counter()
+            _, S = recurrent.recurrent_fwd(inp["q"][b:b + 1, sl], inp["k"][b:b + 1, sl], inp["v"][b:b + 1, sl],
+                                           inp["g"][b:b + 1, sl], inp["beta"][b:b + 1, sl], scale=inp["scale"],
+                                           h0=S, use_qk_l2norm=inp["use_qk_l2norm"])
+            spent += time.perf_counter() - t0
+            tokens += sl.stop - sl.start
+        seqs += 1
+    # chunked/WY oracle on the first sequence (or its first 4096 tokens)
+    if cu is None:
+        b, s0, e0 = 0, 0, min(inp["T"], 4096)
+    else:
+        b, s0, e0 = 0, int(cu[0]), min(int(cu[1]), int(cu[0]) + 4096)
+    sl = slice(s0, e0)
+    t0 = time.perf_counter()
+    chunked.chunked_fwd(inp["q"][b:b + 1, sl], inp["k"][b:b + 1, sl], inp["v"][b:b + 1, sl],
+                        inp["g"][b:b + 1, sl], inp["beta"][b:b + 1, sl], scale=inp["scale"],
+                        h0=inp["h0"][0:1] if inp["h0"] is not None else None,
+                        use_qk_l2norm=inp["use_qk_l2norm"], chunk_size=inp["chunk_size"])
+    tc = time.perf_counter() - t0
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"per-token float64 recurrence, {seqs} of {N} sequences in order (the last possibly "
+                      f"cut at the {budget_s:.0f} s budget), all {w.HV} value heads, {tokens} tokens in "
+                      f"{spent:.1f} s",
+            "chunked_oracle_tokens_per_s": (e0 - s0) / tc,
+            "chunked_oracle_sample": f"chunked/WY float64 evaluation, sequence 0, {e0 - s0} tokens, "
+                                     f"all {w.HV} value heads, {tc:.1f} s"}
+
+
+def cpu_baseline_bwd(w, inp, T=4096, heads=(0, 21)):
+    """The per-token float64 oracle forward + hand-derived backward on the first
+    T tokens of the given value heads, scaled to all value heads."""
     import torch
     from oracle import recurrent
-    threads = torch.get_num_threads()
-    T = inp["T"] if inp["cu_seqlens"] is None else int(inp["cu_seqlens"][1])
-    tokens, spent = 0, 0.0
-    step = 256
-    S0 = inp["h0"][0:1] if inp["h0"] is not None else None
-    while spent < budget_s and tokens < T:
-        n = min(step, T - tokens)
-        sl = slice(tokens, tokens + n)
-        t0 = time.perf_counter()
-        _, S0 = recurrent.recurrent_fwd(inp["q"][0:1, sl], inp["k"][0:1, sl], inp["v"][0:1, sl],
-                                        inp["g"][0:1, sl], inp["beta"][0:1, sl], scale=inp["scale"],
-                                        h0=S0, use_qk_l2norm=inp["use_qk_l2norm"])
-        spent += time.perf_counter() - t0
-        tokens += n
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"per-token float64 recurrence, sequence 0, all {w.HV} value heads, "
-                      f"first {tokens} tokens ({spent:.1f} s)"}
+    hs = list(heads)
+    sub = {n: inp[n][:, :T][:, :, hs].contiguous() for n in ("q", "k", "v", "g", "beta", "do")}
+    t0 = time.perf_counter()
+    recurrent.recurrent_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"],
+                            inp["dht"][:, hs], scale=inp["scale"], h0=inp["h0"][:, hs],
+                            use_qk_l2norm=inp["use_qk_l2norm"])
+    spent = time.perf_counter() - t0
+    per_head_s = spent / len(hs)
+    return {"value": T / (per_head_s * w.HV), "unit": "tokens/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"per-token float64 forward replay + reverse recurrence, first {T} tokens of value "
+                      f"head(s) {hs} ({spent:.1f} s), rate scaled to all {w.HV} value heads"}
 
 
 def parity_gate(w, inp, o, ht):
@@ -392,6 +438,8 @@ def main():
                             "H": wb.H, "HV": wb.HV, "K": wb.K, "V": wb.V, "chunk_size": wb.chunk_size,
                             "tokens_per_s": brec["value"], "ms_per_step": brec["ms_per_step"],
                             **{k: v for k, v in brec.items() if k not in ("value", "ms_per_step")}}
+        if not args.no_cpu_baseline:
+            line["backward"]["cpu_baseline"] = cpu_baseline_bwd(wb, binp)
     print(json.dumps(line))
 
 
