@@ -17,7 +17,10 @@
 //  * with a scalar gate the per-token factor s_t = beta_t exp(G_t) / |k_t|
 //    multiplies the columns of Tm, leaving the raw keys exact; a per-channel
 //    gate multiplies the key tile element-wise by exp(G_td) <= 1;
-//  * blocks above the diagonal of Tm are skipped (Tm is lower triangular).
+//  * blocks above the diagonal of Tm are skipped (Tm is lower triangular);
+//  * every global load of a chunk (keys, the first value pass, Tm rows, g,
+//    beta) is issued before the first wait, so a workgroup pays one memory
+//    round trip, not four.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -28,6 +31,7 @@ namespace {
 template <typename T, int C, int K, bool PC>
 __global__ __launch_bounds__(256) void k2_wy(Args a) {
   constexpr int NW = 4;
+  constexpr int NT = 256;
   constexpr int NB = C / 16;
   constexpr int KSC = C / 32;                       // token slabs
   constexpr int PADE = 16 / sizeof(T) * 1;          // 16 bytes of row padding
@@ -36,6 +40,8 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   constexpr int VP = VT + PADE;
   constexpr int GP = K + 1;
   constexpr int CPR = K / 8;                        // 8-element chunks per key row
+  constexpr int NKP = (C * CPR + NT - 1) / NT;      // key pieces per thread
+  constexpr int NVP = (C * VT / 8 + NT - 1) / NT;   // value pieces per thread and pass
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
   __shared__ __attribute__((aligned(16))) T sV[C * VP];
   __shared__ float sS[C], sB[C], sRn[C];
@@ -53,13 +59,44 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   T* __restrict__ wp = static_cast<T*>(a.w) + (c * HV + j) * (int64_t)(C * K);
   T* __restrict__ up = static_cast<T*>(a.u) + (c * HV + j) * (int64_t)C * V;
 
+  // ---- every global load of the chunk is issued up front (one round trip):
+  //      key rows, the first value pass, the rows of Tm this lane feeds, g, beta
+  Frag<T> kr[NKP], vr[NVP];
+  auto fetch_v = [&](int64_t v0) {
+    const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
+    const int vpr = nv / 8;
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int idx = tid + NT * i, t = idx / vpr, d8 = (idx % vpr) * 8;
+      vr[i] = (idx < C * vpr && t < L) ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + d8) : frag_zero<T>();
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NKP; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    kr[i] = (idx < C * CPR && t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+  }
+  fetch_v(0);
+  // rows of Tm this lane feeds: row 16 rb + r16, tokens 32 ks + 8 g4 + e
+  Frag<T> tf[NB][KSC];
+#pragma unroll
+  for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks)
+      tf[rb][ks] = (2 * ks <= rb) ? ld8(Tp + (16 * rb + r16) * C + 32 * ks + 8 * g4) : frag_zero<T>();
+  float gv = 0.f, bv = 0.f;
+  if (wv == 0 && lane < L) {
+    if (!PC) gv = a.g[(t0 + lane) * HV + j];
+    bv = a.beta[(t0 + lane) * HV + j];
+  }
+
   if constexpr (PC) {
-    for (int idx = tid; idx < C * K; idx += 256) {
+    for (int idx = tid; idx < C * K; idx += NT) {
       const int t = idx / K, d = idx % K;
       sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
     }
     lds_barrier();
-    for (int d = tid; d < K; d += 256) {
+    for (int d = tid; d < K; d += NT) {
       float run = 0.f;
       for (int t = 0; t < C; ++t) {
         run += sGc[t * GP + d];
@@ -70,29 +107,27 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   }
 
   // key tile (token-major), row norms of the raw keys
-  for (int idx = tid; idx < C * CPR; idx += 256) {
-    const int t = idx / CPR, d8 = (idx % CPR) * 8;
-    Frag<T> f = (t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
-    f32x8 x = f.f32();
+#pragma unroll
+  for (int i = 0; i < NKP; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    f32x8 x = kr[i].f32();
     float sq = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
-    sq = lanes_sum(sq, CPR);
-    if (idx % CPR == 0) sRn[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
-    if constexpr (PC) {
+    sq = lanes_sum_t<CPR>(sq);
+    if (idx < C * CPR) {
+      if (d8 == 0) sRn[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+      Frag<T> f = kr[i];
+      if constexpr (PC) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[t * GP + d8 + e]);
-      f = Frag<T>::make(x);
+        for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[t * GP + d8 + e]);
+        f = Frag<T>::make(x);
+      }
+      st8(&sK[t * KP + d8], f);
     }
-    st8(&sK[t * KP + d8], f);
   }
   lds_barrier();
   if (wv == 0) {
-    float gv = 0.f, bv = 0.f;
-    if (lane < L) {
-      if (!PC) gv = a.g[(t0 + lane) * HV + j];
-      bv = a.beta[(t0 + lane) * HV + j];
-    }
     const float G = PC ? 0.f : wave_incl_scan(gv, lane);
     if (lane < C) {
       sB[lane] = bv;
@@ -100,14 +135,6 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     }
   }
   lds_barrier();
-
-  // rows of Tm this lane feeds: row 16 rb + r16, tokens 32 ks + 8 g4 + e
-  Frag<T> tf[NB][KSC];
-#pragma unroll
-  for (int rb = 0; rb < NB; ++rb)
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
-      tf[rb][ks] = (2 * ks <= rb) ? ld8(Tp + (16 * rb + r16) * C + 32 * ks + 8 * g4) : frag_zero<T>();
 
   // w^T = k^T (Tm diag(s))^T
   for (int fb = wv; fb < K / 16; fb += NW) {
@@ -127,17 +154,19 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     }
   }
 
-  // u = Tm diag(beta) v, value columns staged VT at a time
+  // u = Tm diag(beta) v, value columns staged VT at a time (the next pass's
+  // loads are issued while this one is computed)
   for (int64_t v0 = 0; v0 < V; v0 += VT) {
     const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
     const int vpr = nv / 8;
     lds_barrier();
-    for (int idx = tid; idx < C * vpr; idx += 256) {
-      const int t = idx / vpr, d8 = (idx % vpr) * 8;
-      const Frag<T> f = (t < L) ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + d8) : frag_zero<T>();
-      st8(&sV[t * VP + d8], f);
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int idx = tid + NT * i, t = idx / vpr, d8 = (idx % vpr) * 8;
+      if (idx < C * vpr) st8(&sV[t * VP + d8], vr[i]);
     }
     lds_barrier();
+    if (v0 + VT < V) fetch_v(v0 + VT);
     for (int vb = wv; vb < nv / 16; vb += NW) {
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {

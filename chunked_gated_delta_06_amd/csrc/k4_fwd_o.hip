@@ -34,15 +34,19 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   constexpr int KSK = K / 32;
   constexpr int KSC = C / 32;
   constexpr int GP = K + 1;
-  constexpr int VT = sizeof(T) == 2 ? 128 : 64;   // value columns staged per pass
+  constexpr int CPR = K / 8;
+  constexpr int VT = sizeof(T) == 2 ? 64 : (K == 256 ? 16 : 32);   // value columns staged per pass
   constexpr int HP = K + 16 / sizeof(T);          // LDS pitch of h^T rows
   constexpr int EP = C + 16 / sizeof(T);          // LDS pitch of e^T rows
+  constexpr int KP = K + 16 / sizeof(T);          // LDS pitch of key rows
   constexpr int NHP = (VT * K / 8 + NT - 1) / NT;  // 8-element h pieces per thread
   constexpr int NEP = (VT * C / 8 + NT - 1) / NT;  // 8-element e pieces per thread
+  constexpr int NKP = (C * CPR + NT - 1) / NT;     // 8-element key pieces per thread
   __shared__ float sG[C], sRq[C], sRk[C];
   __shared__ float sGc[PC ? C * GP : 1];
   __shared__ __attribute__((aligned(16))) T sH[VT * HP];
   __shared__ __attribute__((aligned(16))) T sE[VT * EP];
+  __shared__ __attribute__((aligned(16))) T sK[C * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int64_t c = blockIdx.x, j = blockIdx.y;
@@ -60,6 +64,22 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
     if (row < L) return ld8(base + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
     return frag_zero<T>();
   };
+
+  // ---- every global load the chunk needs before its first MFMA is issued up
+  //      front, in the order it is consumed (vector-memory waits complete in
+  //      order): the scalar gate, the key tile, this lane's q row, the first
+  //      h^T / e^T tile
+  const float gv = (!PC && wv == 0 && lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+  Frag<T> kreg[NKP];
+#pragma unroll
+  for (int i = 0; i < NKP; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    kreg[i] = (idx < C * CPR && t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+  }
+  const int rr = 16 * wv + r16;               // this lane's output row
+  Frag<T> qf[KSK];
+#pragma unroll
+  for (int ks = 0; ks < KSK; ++ks) qf[ks] = row8(qp, rr, ks);
 
   // ---- h^T and e^T tiles of VT value columns: fetched into registers early,
   //      staged into LDS, then read as MFMA A operands
@@ -93,7 +113,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   };
   fetch_tile(0);
 
-  // ---- gates, norms
+  // ---- gates, norms, key tile
   if constexpr (PC) {
     for (int idx = tid; idx < C * K; idx += 64 * NB) {
       const int t = idx / K, d = idx % K;
@@ -109,31 +129,36 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
     }
   } else {
     if (wv == 0) {
-      const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
       const float G = wave_incl_scan(gv, lane);
       if (lane < C) sG[lane] = G;
     }
   }
-  const int rr = 16 * wv + r16;               // this lane's output row
-  Frag<T> qf[KSK];
-  float sq = 0.f, sk = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < KSK; ++ks) {
-    qf[ks] = row8(qp, rr, ks);
-    const f32x8 xq = qf[ks].f32(), xk = row8(kp, rr, ks).f32();
+  for (int i = 0; i < NKP; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    const f32x8 x = kreg[i].f32();
+    float sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sq += xq[e] * xq[e];
-      sk += xk[e] * xk[e];
+    for (int e = 0; e < 8; ++e) sk += x[e] * x[e];
+    sk = lanes_sum_t<CPR>(sk);
+    if (idx < C * CPR) {
+      if (d8 == 0) sRk[t] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+      st8(&sK[t * KP + d8], kreg[i]);
     }
   }
-  sq = group4_sum(sq);
-  sk = group4_sum(sk);
-  if (g4 == 0) {
-    sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
-    sRk[rr] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+  {
+    float sq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSK; ++ks) {
+      const f32x8 xq = qf[ks].f32();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += xq[e] * xq[e];
+    }
+    sq = group4_sum(sq);
+    if (g4 == 0) sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
   }
   lds_barrier();
+  auto krow8 = [&](int row, int ks) -> Frag<T> { return ld8(&sK[row * KP + 32 * ks + 8 * g4]); };
 
   // ---- P^T blocks (t-block jb, r-block wv), jb <= wv
   const float rq = sRq[rr];
@@ -144,7 +169,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
     if (jb > wv) continue;
     if constexpr (!PC) {
 #pragma unroll
-      for (int ks = 0; ks < KSK; ++ks) mma(Pt[jb], row8(kp, 16 * jb + r16, ks), qf[ks]);
+      for (int ks = 0; ks < KSK; ++ks) mma(Pt[jb], krow8(16 * jb + r16, ks), qf[ks]);
     } else {
       bool direct = false;
       int m = 16 * jb + 15;
@@ -161,7 +186,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
         const int tk = 16 * jb + r16;
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks) {
-          f32x8 xa = row8(kp, tk, ks).f32(), xb = qf[ks].f32();
+          f32x8 xa = krow8(tk, ks).f32(), xb = qf[ks].f32();
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int d = 32 * ks + 8 * g4 + e;
@@ -178,7 +203,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
           float s = 0.f;
           if (t <= rr && rr < L) {
             for (int d = 0; d < K; ++d)
-              s += to_float(kp[((t0 + t) * H + h) * K + d]) * to_float(qp[((t0 + rr) * H + h) * K + d]) *
+              s += to_float(sK[t * KP + d]) * to_float(qp[((t0 + rr) * H + h) * K + d]) *
                    __expf(sGc[rr * GP + d] - sGc[t * GP + d]);
           }
           Pt[jb][i] = s;
