@@ -61,6 +61,24 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
     return frag_zero<T>();
   };
 
+  // the first value head's gate and beta are requested together with the
+  // keys, so their latency overlaps the kk^T products
+  auto fetch_gb = [&](int64_t j, float& gv, float& bv) {
+    gv = (!PC && lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+    bv = (lane < L) ? a.beta[(t0 + lane) * HV + j] : 0.f;
+  };
+  // (scalar gate: all key fragments at once; a per-channel gate re-reads the
+  // keys block by block below and loads them per slab here)
+  Frag<T> kf[PC ? 1 : KS][NB];
+  if constexpr (!PC) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) kf[ks][rb] = krow(16 * rb + r16, ks);
+  }
+  float gnext, bnext;
+  fetch_gb(jfirst, gnext, bnext);
+
   // ---- raw kk^T (scalar gate) and row norms
   f32x4 acc[NLB];
 #pragma unroll
@@ -73,7 +91,11 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
     Frag<T> f[NB];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      f[rb] = krow(16 * rb + r16, ks);
+      if constexpr (PC) {
+        f[rb] = krow(16 * rb + r16, ks);
+      } else {
+        f[rb] = kf[ks][rb];
+      }
       const f32x8 x = f[rb].f32();
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss[rb] += x[e] * x[e];
@@ -94,10 +116,9 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   for (int64_t jj = 0; jj < jcount; ++jj) {
     const int64_t j = jfirst + jj;
     // ---- gates: chunk-local inclusive cumsum, one token per lane
-    float gv = 0.f;
-    if (!PC && lane < L) gv = a.g[(t0 + lane) * HV + j];
+    const float gv = gnext, bv = bnext;
+    if (jj + 1 < jcount) fetch_gb(j + 1, gnext, bnext);
     const float Gc = PC ? 0.f : wave_incl_scan(gv, lane);
-    const float bv = (lane < L) ? a.beta[(t0 + lane) * HV + j] : 0.f;
     if (lane < C) {
       sG[lane] = Gc;
       sBeta[lane] = bv;
