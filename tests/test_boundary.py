@@ -29,6 +29,7 @@ def test_exports_every_declared_function():
     L = gdr.lib()
     names = header_functions()
     assert "gdr_chunk_fwd" in names and "gdr_fwd_h" in names
+    assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
     assert L.gdr_abi_version() == 1
@@ -37,8 +38,9 @@ def test_exports_every_declared_function():
 def test_status_strings():
     L = gdr.lib()
     assert L.gdr_status_string(2).decode() == "chunk_size must be either 32 or 64"
-    for s in range(10):
+    for s in range(11):
         assert L.gdr_status_string(s)
+    assert "backward supports" in L.gdr_status_string(10).decode()
 
 
 @pytest.mark.parametrize("kw,msg", [
@@ -129,3 +131,73 @@ def test_python_wrapper_refuses_cpu_tensors():
     g = torch.zeros(1, 64, 1)
     with pytest.raises(ValueError, match="GPU"):
         gdr.chunk_fwd(x, x, x, g, g)
+
+
+@pytest.mark.parametrize("kw,ok", [
+    (dict(), True),
+    (dict(K=128, V=256, chunk_size=32), True),
+    (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=32), True),
+    (dict(dtype=gdr.GDR_FP32, K=64, chunk_size=64), True),
+    (dict(gate_per_channel=1), False),
+    (dict(K=256), False),
+    (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64), False),
+])
+def test_bwd_supported_shapes(kw, ok):
+    p = problem(**kw)
+    gdr.check_problem(p)                 # every case is a valid forward problem
+    if ok:
+        lay = gdr.bwd_layout(p)
+        assert lay.total > 0
+    else:
+        with pytest.raises(ValueError, match="backward supports"):
+            gdr.bwd_layout(p)
+
+
+def test_bwd_workspace_layout():
+    p = problem(B=1, T=65536, H=32, HV=32, K=128, V=128, N=1)
+    lay = gdr.bwd_layout(p)
+    f = gdr.fwd_layout(p)
+    assert lay.fwd.total == f.total and lay.fwd.h == f.h
+    nt, C, HV, K, V = 1024, 64, 32, 128, 128
+    assert lay.fwd.nt_max == nt
+    offs = [lay.fwd.total, lay.de_local, lay.qscale, lay.dh, lay.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.qscale - lay.de_local >= nt * HV * V * C * 2
+    assert lay.dh - lay.qscale >= nt * HV * C * 4
+    assert lay.total - lay.dh >= nt * HV * V * K * 2
+    size = ctypes.c_size_t(0)
+    assert gdr.lib().gdr_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(size)) == 0
+    assert size.value == lay.total
+
+
+def test_bwd_rejects_before_launch():
+    """Backward argument errors come back as codes before any launch."""
+    L = gdr.lib()
+    p = problem()
+    P = ctypes.c_void_p
+    a = P(0x1000)
+    big = ctypes.c_size_t(1 << 40)
+    # q, k, v, g, beta, cu, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, ws
+    # (every call below fails a host check, so nothing is launched even where a
+    # GPU is present: the fake addresses are never dereferenced)
+    base = [a, a, a, a, a, None, None, a, None, a, a, a, a, a, None]
+    args = list(base)
+    args[7] = None                       # null d_o
+    assert L.gdr_chunk_bwd(ctypes.byref(p), *args, a, big, None) == 1
+    args = list(base)
+    args[12] = P(0x1004)                 # misaligned dg
+    assert L.gdr_chunk_bwd(ctypes.byref(p), *args, a, big, None) == 6
+    assert L.gdr_chunk_bwd(ctypes.byref(p), *base, a, ctypes.c_size_t(64), None) == 7
+    assert L.gdr_chunk_bwd(ctypes.byref(p), *base, None, big, None) == 7
+    ppc = problem(gate_per_channel=1)
+    assert L.gdr_chunk_bwd(ctypes.byref(ppc), *base, a, big, None) == 10
+    p16 = problem(chunk_size=16)
+    assert L.gdr_chunk_bwd(ctypes.byref(p16), *base, a, big, None) == 2
+
+
+def test_bwd_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 1, 32, dtype=torch.bfloat16)
+    g = torch.zeros(1, 64, 1)
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.chunk_bwd(x, x, x, g, g, x)
