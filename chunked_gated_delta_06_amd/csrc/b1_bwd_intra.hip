@@ -9,9 +9,11 @@
 // testing and coverage matrix", section 2, differentiated through o).
 //
 // gfx950 mapping: one workgroup per (chunk, value head), wave w owns tokens
-// t = 16 w .. 16 w + 15 of de_local.  The wave computes its column blocks of
-// P from the raw bf16 q / k rows on MFMA, applies norms, gate and causal mask
-// in fp32 and feeds the accumulators as the A operand (rows t) of
+// t = 16 w .. 16 w + 15 of de_local.  The q and k tiles are read once per
+// workgroup (all loads issued before the first wait) and staged in LDS; the
+// wave computes its column blocks of P from the raw bf16 q / k rows on MFMA,
+// applies norms, gate and causal mask in fp32 and feeds the accumulators as
+// the A operand (rows t) of
 // de_local = P^T dO in the "chained" contraction map, as a bf16 hi + lo pair;
 // dO is staged through LDS 32 value columns at a time and read with
 // transposed LDS reads.  The result leaves each lane four consecutive tokens
@@ -30,12 +32,17 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   constexpr int NT = 64 * NB;
   constexpr int KSK = K / 32;
   constexpr int KSC = C / 32;
+  constexpr int CPR = K / 8;
   constexpr int VT = 32;                          // value columns per pass
   constexpr int DP = VT + 32 / sizeof(T);         // LDS pitch of dO rows
+  constexpr int KP = K + 16 / sizeof(T);          // LDS pitch of q / k rows
   constexpr int NPD = VT * C / 8 / NT;            // 8-element dO pieces per thread (= 1)
+  constexpr int NPK = (C * CPR + NT - 1) / NT;     // 8-element q / k pieces per thread
   static_assert(NPD * NT * 8 == VT * C, "dO tile pieces");
   __shared__ float sG[C], sRq[C], sRk[C];
   __shared__ __attribute__((aligned(16))) T sDO[C * DP];
+  __shared__ __attribute__((aligned(16))) T sQ[C * KP];
+  __shared__ __attribute__((aligned(16))) T sK[C * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int64_t c = blockIdx.x, j = blockIdx.y;
@@ -48,12 +55,18 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   const T* __restrict__ dop = static_cast<const T*>(a.d_o);
   T* __restrict__ dep = static_cast<T*>(a.de_local) + (c * HV + j) * V * (int64_t)C;
 
-  auto row8 = [&](const T* base, int row, int ks) -> Frag<T> {
-    if (row < L) return ld8(base + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
-    return frag_zero<T>();
-  };
-
-  // dO tile (rows t, VT value columns from v0), fetched into registers early
+  // ---- every global load of the chunk is issued up front: the gate, the q
+  //      and k tiles (each read once, coalesced) and the first dO tile
+  const float gv = (wv == 0 && lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
+  Frag<T> qreg[NPK], kreg[NPK];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    const bool in = idx < C * CPR && t < L;
+    qreg[i] = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+    kreg[i] = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+  }
+  // dO tile (rows t, VT value columns from v0)
   Frag<T> dreg[NPD];
   auto fetch_tile = [&](int64_t v0) {
 #pragma unroll
@@ -71,32 +84,34 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   };
   fetch_tile(0);
 
-  // ---- gate cumsum and norms
+  // ---- gate cumsum; q / k tiles into LDS with their row norms
   if (wv == 0) {
-    const float gv = (lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
     const float G = wave_incl_scan(gv, lane);
     if (lane < C) sG[lane] = G;
   }
-  const int rr = 16 * wv + r16;
-  {
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    const f32x8 xq = qreg[i].f32(), xk = kreg[i].f32();
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSK; ++ks) {
-      const f32x8 xq = row8(qp, rr, ks).f32(), xk = row8(kp, rr, ks).f32();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sq += xq[e] * xq[e];
-        sk += xk[e] * xk[e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      sq += xq[e] * xq[e];
+      sk += xk[e] * xk[e];
     }
-    sq = group4_sum(sq);
-    sk = group4_sum(sk);
-    if (g4 == 0) {
-      sRq[rr] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
-      sRk[rr] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+    sq = lanes_sum_t<CPR>(sq);
+    sk = lanes_sum_t<CPR>(sk);
+    if (idx < C * CPR) {
+      st8(&sQ[t * KP + d8], qreg[i]);
+      st8(&sK[t * KP + d8], kreg[i]);
+      if (d8 == 0) {
+        sRq[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+        sRk[t] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+      }
     }
   }
   lds_barrier();
+  const int rr = 16 * wv + r16;
   if (g4 == 0)
     a.qscale[(c * HV + j) * C + rr] = (rr < L) ? a.scale * __expf(sG[rr]) * sRq[rr] : 0.f;
 
@@ -109,7 +124,8 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
     Pa[rb] = zero4();
     if (rb < wv) continue;
 #pragma unroll
-    for (int ks = 0; ks < KSK; ++ks) mma(Pa[rb], row8(qp, 16 * rb + r16, ks), row8(kp, tt, ks));
+    for (int ks = 0; ks < KSK; ++ks)
+      mma(Pa[rb], ld8(&sQ[(16 * rb + r16) * KP + 32 * ks + 8 * g4]), ld8(&sK[tt * KP + 32 * ks + 8 * g4]));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rb + 4 * g4 + i;
