@@ -177,6 +177,41 @@ GDR_DEV Frag<T> lds_tr_frag(const T* tile, int pitch, int row_lo, int row_hi, in
 GDR_DEV float to_float(bf16 x) { return (float)x; }
 GDR_DEV float to_float(float x) { return x; }
 
+// Store of two stacked 16-row accumulator blocks X (rows 4g..4g+3 of block 0)
+// and Y (same rows of block 1), column l % 16, into the row of a transposed
+// tile where the 32 rows are consecutive elements: v_permlane16_swap
+// exchanges X of lane rows 1 / 3 with Y of rows 0 / 2, after which lane row g
+// holds 8 consecutive elements starting at 16 (g & 1) + 8 (g >> 1) -- one
+// 16-byte store per lane instead of two 8-byte ones.  `row` points at element
+// 0 of the 32.
+template <typename T>
+GDR_DEV void st_pair(T* row, f32x4 X, f32x4 Y, int lane) {
+  const int g = lane >> 4;
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 xb = cvt4<bf16>(X), yb = cvt4<bf16>(Y);
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 xu = __builtin_bit_cast(u32x2, xb), yu = __builtin_bit_cast(u32x2, yb);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(xu[0], yu[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(xu[1], yu[1], false, false);
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 out = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    *reinterpret_cast<u32x4*>(row + 16 * (g & 1) + 8 * (g >> 1)) = out;
+  } else {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 xu = __builtin_bit_cast(u32x4, X), yu = __builtin_bit_cast(u32x4, Y);
+    u32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(xu[e], yu[e], false, false);
+      a[e] = sw[0];
+      b[e] = sw[1];
+    }
+    float* dst = reinterpret_cast<float*>(row) + 16 * (g & 1) + 8 * (g >> 1);
+    *reinterpret_cast<u32x4*>(dst) = a;
+    *reinterpret_cast<u32x4*>(dst + 4) = b;
+  }
+}
+
 // Row-map fragment (contraction index 8 g + e) taken down a column of a
 // row-major LDS tile: rows row0 + 8 g .. row0 + 8 g + 7 of column col0 + l % 16.
 template <typename T>

@@ -479,7 +479,7 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
     // h[c] = S (transposed, 4 features per lane)
     T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
-    for (int mb = 0; mb < NS; ++mb) st4(hp + (r16 * K + 16 * mb + 4 * g4), S[mb]);
+    for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
     // e = u - w S  (independent accumulators alternate between MFMAs)
     Frag<T> nS[KSK];
 #pragma unroll
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
     // v_new = e (transposed per chunk)
     T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
-    for (int eb = 0; eb < NE; ++eb) st4(vnp + (r16 * C + 16 * eb + 4 * g4), E[eb]);
+    for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
     // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e
     Frag<T> Ef[KSC];
 #pragma unroll
