@@ -226,10 +226,10 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       dl[eb] = ld4f(erow + 16 * eb + 4 * g4);
     }
     const float gl = sm.ks[b][C];
-    // dh[c] = dS (transposed, 4 features per lane)
+    // dh[c] = dS (transposed; feature blocks paired into 16-byte stores)
     T* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
-    for (int mb = 0; mb < NS; ++mb) st4(hp + (r16 * K + 16 * mb + 4 * g4), S[mb]);
+    for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
     // dE = de_local + diag(kscale) K dS
     Frag<T> Sf[KSK];
 #pragma unroll

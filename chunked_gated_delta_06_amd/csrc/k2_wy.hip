@@ -136,21 +136,31 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   }
   lds_barrier();
 
-  // w^T = k^T (Tm diag(s))^T
-  for (int fb = wv; fb < K / 16; fb += NW) {
+  // w^T = k^T (Tm diag(s))^T; with K / 32 feature pairs per wave or more, the
+  // blocks (2 p, 2 p + 1) are computed together and leave as 16-byte stores
+  auto w_block = [&](int fb, int rb) {
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int rb = 0; rb < NB; ++rb) {
-      f32x4 acc = zero4();
+    for (int ks = 0; ks < KSC; ++ks) {
+      if (2 * ks > rb) continue;
+      const Frag<T> ka = lds_tr_frag(sK, KP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * fb, lane);
+      f32x8 sc;
 #pragma unroll
-      for (int ks = 0; ks < KSC; ++ks) {
-        if (2 * ks > rb) continue;
-        const Frag<T> ka = lds_tr_frag(sK, KP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * fb, lane);
-        f32x8 sc;
+      for (int e = 0; e < 8; ++e) sc[e] = sS[32 * ks + 8 * g4 + e];
+      mma(acc, ka, Frag<T>::make(tf[rb][ks].f32() * sc));
+    }
+    return acc;
+  };
+  if constexpr (K / 32 >= NW) {
+    for (int fp = wv; fp < K / 32; fp += NW) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = sS[32 * ks + 8 * g4 + e];
-        mma(acc, ka, Frag<T>::make(tf[rb][ks].f32() * sc));
-      }
-      st4(wp + (16 * rb + r16) * K + 16 * fb + 4 * g4, acc);
+      for (int rb = 0; rb < NB; ++rb)
+        st_pair(wp + (16 * rb + r16) * K + 32 * fp, w_block(2 * fp, rb), w_block(2 * fp + 1, rb), lane);
+    }
+  } else {
+    for (int fb = wv; fb < K / 16; fb += NW) {
+#pragma unroll
+      for (int rb = 0; rb < NB; ++rb) st4(wp + (16 * rb + r16) * K + 16 * fb + 4 * g4, w_block(fb, rb));
     }
   }
 
@@ -168,9 +178,10 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     lds_barrier();
     if (v0 + VT < V) fetch_v(v0 + VT);
     for (int vb = wv; vb < nv / 16; vb += NW) {
+      f32x4 acc[NB];
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
-        f32x4 acc = zero4();
+        acc[rb] = zero4();
 #pragma unroll
         for (int ks = 0; ks < KSC; ++ks) {
           if (2 * ks > rb) continue;
@@ -178,10 +189,13 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) sc[e] = sB[32 * ks + 8 * g4 + e];
           const Frag<T> vbf = lds_tr_frag(sV, VP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * vb, lane);
-          mma(acc, Frag<T>::make(tf[rb][ks].f32() * sc), vbf);
+          mma(acc[rb], Frag<T>::make(tf[rb][ks].f32() * sc), vbf);
         }
-        st4(up + (v0 + 16 * vb + r16) * C + 16 * rb + 4 * g4, acc);
       }
+      // token blocks paired into 16-byte stores of the transposed u rows
+#pragma unroll
+      for (int m = 0; m < NB / 2; ++m)
+        st_pair(up + (v0 + 16 * vb + r16) * C + 32 * m, acc[2 * m], acc[2 * m + 1], lane);
     }
   }
 }

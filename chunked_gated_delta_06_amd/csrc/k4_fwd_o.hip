@@ -251,8 +251,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   lds_barrier();
   if (v0 + VT < V) fetch_tile(v0 + VT);
   const int nvb = ((V - v0) < VT ? (int)(V - v0) : VT) / 16;
-  for (int vbl = 0; vbl < nvb; ++vbl) {
-    const int64_t vb = v0 / 16 + vbl;
+  auto o_block = [&](int vbl) {
     f32x4 acc = zero4();
     const T* hrow = &sH[(16 * vbl + r16) * HP];
 #pragma unroll
@@ -270,7 +269,20 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
       if (2 * kt > wv) continue;
       mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), Pf[kt]);
     }
-    if (rr < L) st4(op + ((t0 + rr) * HV + j) * V + 16 * vb + 4 * g4, acc * sc);
+    return acc * sc;
+  };
+  T* orow = op + ((t0 + rr) * HV + j) * V + v0;
+  if constexpr (VT >= 32) {
+    // value blocks paired into 16-byte stores (nvb is even: V is a multiple of 32)
+    for (int vbl = 0; vbl < nvb; vbl += 2) {
+      const f32x4 x = o_block(vbl), y = o_block(vbl + 1);
+      if (rr < L) st_pair(orow + 16 * vbl, x, y, lane);
+    }
+  } else {
+    for (int vbl = 0; vbl < nvb; ++vbl) {
+      const f32x4 x = o_block(vbl);
+      if (rr < L) st4(orow + 16 * vbl + 4 * g4, x);
+    }
   }
   lds_barrier();
   }
