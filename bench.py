@@ -48,6 +48,8 @@ def stage_bytes_per_token_head(w, T_seq):
         "wy": r * K * e + V * e + e * C + gb + 4 + e * K + e * V,
         "fwd_h": e * K + e * V + r * K * e + gb + e * V + e * K * V / C + 8 * K * V / T_seq,
         "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
+        # fused scan + output: w, u, k, kscale, q, g -> o, ht (h and v_new stay on chip)
+        "fwd_h_o": e * K + e * V + r * K * e + 4 + r * K * e + 4 + e * V + 8 * K * V / T_seq,
     }
 
 
@@ -73,7 +75,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
 
 def kernel_source_hash(stage):
     fname = {"kkt_solve": "k1_kkt_solve.hip", "wy": "k2_wy.hip", "fwd_h": "k3_fwd_h.hip",
-             "fwd_o": "k4_fwd_o.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
+             "fwd_o": "k4_fwd_o.hip", "fwd_h_o": "k3_fwd_h.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
              "bwd_dqkvg": "b3_bwd_dqkvg.hip"}[stage]
     h = hashlib.sha256()
     for f in (fname, "gdr_device.h"):
@@ -271,7 +273,11 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     kw = dict(scale=inp["scale"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
               initial_state=d["h0"], output_final_state=True,
               use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
-    o, ht, ws = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], return_workspace=True, **kw)
+    # the same forward path the timed step runs (fused scan + output where the
+    # shape has it); the workspace still holds the K0-K2 intermediates the
+    # per-stage timing below reads
+    o, ht, ws = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], return_workspace=True,
+                              keep_states=False, **kw)
     torch.cuda.synchronize()
     if backward:
         errs, tol = bwd_parity_gate(gdr, w, inp, dev, o)
@@ -327,12 +333,18 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
                                    views["v_new"], ht, views["kscale"]),
         "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
+        "fwd_h_o": lambda: gdr.fwd_h_o(p, d["q"], d["k"], views["w"], views["u"], d["g"], views["kscale"],
+                                       cidx, coff, d["h0"], o, ht),
     }
+    # the stages the timed step runs: the fused scan + output where the shape has it
+    fused = gdr.fwd_h_o_supported(p)
+    for name in (("fwd_h", "fwd_o") if fused else ("fwd_h_o",)):
+        del fstages[name]
     reps = max(5, min(steps, 50))
     fwd_ms = event_stage_ms(stream, fstages, reps)
     T_seq = inp["B"] * inp["T"] / inp["N"]
     units = tokens * w.HV
-    per_unit = stage_bytes_per_token_head(w, T_seq)
+    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq).items() if k in fstages}
     fwd_total_ms = sum(fwd_ms.values())
     rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
            "stage_ms": {"forward": fwd_ms}, "parity": parity,

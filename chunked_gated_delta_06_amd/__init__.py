@@ -40,7 +40,7 @@ class GdrProblem(ctypes.Structure):
                 ("HV", ctypes.c_int64), ("K", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("N", ctypes.c_int64), ("chunk_size", ctypes.c_int32),
                 ("gate_per_channel", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("keep_states", ctypes.c_int32)]
 
 
 class GdrFwdLayout(ctypes.Structure):
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
         L.gdr_fwd_h.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
+        L.gdr_fwd_h_o_supported.argtypes = [PP]
+        L.gdr_fwd_h_o_supported.restype = ctypes.c_int
+        L.gdr_fwd_h_o.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_bwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_bwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrBwdLayout)]
         L.gdr_chunk_bwd.argtypes = [PP] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
@@ -94,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_bwd_dqkvg.argtypes = [PP] + [_P] * 17 + [_P]
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
-                     "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o",
+                     "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
                      "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
                      "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
@@ -128,15 +131,17 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_problem(q, v, g, *, chunk_size=64, cu_seqlens=None, use_qk_l2norm=False, scale=1.0,
-                 N: Optional[int] = None) -> GdrProblem:
-    """Problem description from tensor shapes (no checks beyond the shapes)."""
+                 N: Optional[int] = None, keep_states: bool = False) -> GdrProblem:
+    """Problem description from tensor shapes (no checks beyond the shapes).
+    ``keep_states`` makes gdr_chunk_fwd leave h and v_new in its workspace
+    (separate scan and output stages instead of the fused one)."""
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
     if N is None:
         N = (len(cu_seqlens) - 1) if cu_seqlens is not None else B
     return GdrProblem(B=B, T=T, H=H, HV=HV, K=K, V=V, N=N, chunk_size=int(chunk_size),
                       gate_per_channel=int(g.dim() == 4), use_qk_l2norm=int(bool(use_qk_l2norm)),
-                      dtype=_dtype_code(q.dtype), scale=float(scale))
+                      dtype=_dtype_code(q.dtype), scale=float(scale), keep_states=int(bool(keep_states)))
 
 
 def check_problem(p: GdrProblem) -> None:
@@ -191,11 +196,14 @@ def check_tensors(p: GdrProblem, q, k, v, g, beta, cu_seqlens=None, h0=None, val
 def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_seqlens=None,
               initial_state=None, output_final_state: bool = True,
               use_qk_l2norm_in_kernel: bool = False, workspace: Optional[torch.Tensor] = None,
-              return_workspace: bool = False, out=None, validate_cu: bool = True):
+              return_workspace: bool = False, out=None, validate_cu: bool = True,
+              keep_states: Optional[bool] = None):
     """Forward of the chunked gated delta rule.  Returns (o, ht) (ht None when
     not requested), plus the workspace tensor when ``return_workspace``.
     ``out=(o, ht)`` supplies the output tensors; ``validate_cu`` checks a host
-    copy of cu_seqlens first (one small device-to-host copy)."""
+    copy of cu_seqlens first (one small device-to-host copy).  ``keep_states``
+    (default: ``return_workspace``) keeps h and v_new in the workspace;
+    otherwise the fused scan + output stage runs where the shape allows it."""
     _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k and v must share one dtype")
@@ -204,8 +212,10 @@ def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_
             raise ValueError(f"{name} must be float32")
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
+    if keep_states is None:
+        keep_states = return_workspace
     p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=keep_states)
     lay = fwd_layout(p)
     check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
     if out is not None:
@@ -281,6 +291,16 @@ def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht, kscale=None):
 def fwd_o(p, q, k, v_new, h, g, chunk_idx, chunk_off, o):
     _raise(lib().gdr_fwd_o(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g),
                            _ptr(chunk_idx), _ptr(chunk_off), _ptr(o), _stream(q.device)))
+
+
+def fwd_h_o_supported(p) -> bool:
+    return bool(lib().gdr_fwd_h_o_supported(ctypes.byref(p)))
+
+
+def fwd_h_o(p, q, k, w, u, g, kscale, chunk_idx, chunk_off, h0, o, ht):
+    _raise(lib().gdr_fwd_h_o(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(kscale),
+                             _ptr(chunk_idx), _ptr(chunk_off), _ptr(h0), _ptr(o), _ptr(ht),
+                             _stream(q.device)))
 
 
 # ---- backward

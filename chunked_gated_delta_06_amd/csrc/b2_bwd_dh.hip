@@ -59,6 +59,7 @@ struct B2S {
     float qs[NLO];
     Frag<T> e[NLE];
     f32x4 ks;
+    int L;
   };
   struct Smem {
     T k[NBUF][C * KR];
@@ -117,12 +118,14 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
     for (int i = 0; i < NLD; ++i) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       const bool in = (NPW % NTL == 0) || idx < NPW;
+      // Only loads here (the payload is first read when staged, so the
+      // in-order vector-memory counter leaves the later payloads in flight);
+      // rows past L load row L-1 and are zeroed when staged, pieces past the
+      // tile load piece 0 and are never staged.
       const int tc = t < L ? t : L - 1;
-      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
-      const Frag<T> qr = ld8(qrow + (tc * (int)(H * K) + d8));
-      R.w[i] = in ? ld8(wp + 8 * idx) : frag_zero<T>();
-      R.k[i] = (in && t < L) ? kr : frag_zero<T>();
-      R.q[i] = (in && t < L) ? qr : frag_zero<T>();
+      R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));
+      R.q[i] = ld8(qrow + (tc * (int)(H * K) + d8));
+      R.w[i] = ld8(wp + 8 * (in ? idx : 0));
     }
     const T* orow = dop + (t0 * HV + j) * V + vw;
     const float* qsp = a.qscale + (c * HV + j) * (int64_t)C;
@@ -131,33 +134,35 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       const int idx = tl + NTL * i, t = idx / (BV / 8), v8 = (idx % (BV / 8)) * 8;
       const bool in = (NPO % NTL == 0) || idx < NPO;
       const int tc = t < L ? t : L - 1;
-      const Frag<T> orr = ld8(orow + (tc * (int)(HV * V) + v8));
-      R.o[i] = (in && t < L) ? orr : frag_zero<T>();
-      R.qs[i] = qsp[t < C ? t : C - 1];
+      R.o[i] = ld8(orow + (tc * (int)(HV * V) + v8));
+      R.qs[i] = qsp[tc];
     }
     const T* ep = debase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
     for (int i = 0; i < NLE; ++i) {
       const int idx = tl + NTL * i;
-      R.e[i] = ((NPE % NTL == 0) || idx < NPE) ? ld8(ep + 8 * idx) : frag_zero<T>();
+      R.e[i] = ld8(ep + 8 * (((NPE % NTL == 0) || idx < NPE) ? idx : 0));
     }
     const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
-    R.ks = (tl < NKS) ? *reinterpret_cast<const f32x4*>(ksp + 4 * tl) : zero4();
+    R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
+    R.L = L;
   };
   auto stage = [&](const Regs& R, int b) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       if ((NPW % NTL == 0) || idx < NPW) {
-        st8(&sm.k[b][t * KR + d8], R.k[i]);
-        st8(&sm.q[b][t * KP + d8], R.q[i]);
+        st8(&sm.k[b][t * KR + d8], t < R.L ? R.k[i] : frag_zero<T>());
+        st8(&sm.q[b][t * KP + d8], t < R.L ? R.q[i] : frag_zero<T>());
         st8(&sm.w[b][t * KP + d8], R.w[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < NLO; ++i) {
       const int idx = tl + NTL * i, t = idx / (BV / 8), v8 = (idx % (BV / 8)) * 8;
-      if ((NPO % NTL == 0) || idx < NPO) st8(&sm.o[b][t * OP + v8], Frag<T>::make(R.o[i].f32() * R.qs[i]));
+      // rows past L: a zero row factor (the loaded row is a finite copy of row L-1)
+      const float qs = t < R.L ? R.qs[i] : 0.f;
+      if ((NPO % NTL == 0) || idx < NPO) st8(&sm.o[b][t * OP + v8], Frag<T>::make(R.o[i].f32() * qs));
     }
 #pragma unroll
     for (int i = 0; i < NLE; ++i) {

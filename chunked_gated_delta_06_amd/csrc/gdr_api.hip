@@ -132,7 +132,7 @@ gdr_status check_bwd(const gdr_problem* p, bool varlen) {
 
 extern "C" {
 
-int gdr_abi_version(void) { return 1; }
+int gdr_abi_version(void) { return 2; }
 
 const char* gdr_status_string(gdr_status s) {
   switch (s) {
@@ -219,8 +219,13 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   hipError_t e = gdr::launch_chunk_table(a, s);
   if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
   if (e == hipSuccess) e = gdr::launch_wy(a, s);
-  if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
-  if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+  if (!p->keep_states && gdr::fwd_h_o_supported(a)) {
+    // fused scan + output: h and v_new never leave the chip
+    if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
+  } else {
+    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+    if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+  }
   return hip_status(e);
 }
 
@@ -306,6 +311,33 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
   a.v_new = v_new;
   a.ht = ht;
   return hip_status(gdr::launch_fwd_h(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdr_fwd_h_o_supported(const gdr_problem* p) {
+  if (check(p, p ? p->N != p->B : false) != GDR_OK) return 0;
+  return gdr::fwd_h_o_supported(make_args(*p)) ? 1 : 0;
+}
+
+gdr_status gdr_fwd_h_o(const gdr_problem* p, const void* q, const void* k, const void* w, const void* u,
+                       const float* g, const float* kscale, const int32_t* chunk_idx, const int32_t* chunk_off,
+                       const float* h0, void* o, float* ht, void* stream) {
+  gdr_status st = stage_common(p, {q, k, w, u, g, kscale, chunk_idx, chunk_off, o});
+  if (st != GDR_OK) return st;
+  if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return GDR_ERR_ALIGNMENT;
+  Args a = make_args(*p);
+  if (!gdr::fwd_h_o_supported(a)) return GDR_ERR_UNSUPPORTED;
+  a.q = q;
+  a.k = k;
+  a.w = const_cast<void*>(w);
+  a.u = const_cast<void*>(u);
+  a.g = g;
+  a.kscale = const_cast<float*>(kscale);
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.h0 = h0;
+  a.o = o;
+  a.ht = ht;
+  return hip_status(gdr::launch_fwd_h_o(a, static_cast<hipStream_t>(stream)));
 }
 
 gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new, const void* h,

@@ -51,6 +51,10 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_kkt_solve(const Args& a, hipStream_t s);
 hipError_t launch_wy(const Args& a, hipStream_t s);
 hipError_t launch_fwd_h(const Args& a, hipStream_t s);
+// fused state scan + output (no h / v_new); fwd_h_o_supported says whether the
+// shape has an instantiation (scalar gate, staged tiles fit in LDS)
+bool fwd_h_o_supported(const Args& a);
+hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s);

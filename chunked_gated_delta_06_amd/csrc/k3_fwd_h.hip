@@ -116,9 +116,8 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     for (int i = 0; i < NLD; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       const int tc = t < R.L ? t : R.L - 1;
-      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
+      R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));   // rows past L: zeroed when staged
       R.w[i] = ld8(wp + 8 * idx);
-      R.k[i] = (t < R.L) ? kr : frag_zero<T>();
     }
     const T* up = ubase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
@@ -129,8 +128,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
       for (int i = 0; i < NG; ++i) {
         const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
         const int tc = t < R.L ? t : R.L - 1;
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(grow + (tc * (int)(HV * K) + d4));
-        R.gc[i] = (t < R.L) ? gr : zero4();
+        R.gc[i] = *reinterpret_cast<const f32x4*>(grow + (tc * (int)(HV * K) + d4));
       }
     } else {
       const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
@@ -150,8 +148,9 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+        const f32x4 gr = (t < R.L) ? R.gc[i] : zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.gc[t * GP + d4 + e] = R.gc[i][e];
+        for (int e = 0; e < 4; ++e) sm.gc[t * GP + d4 + e] = gr[e];
       }
       lds_barrier();
       for (int d = tid; d < K; d += NT) {
@@ -168,8 +167,9 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     for (int i = 0; i < NLD; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       st8(&sm.w[b][t * WP + d8], R.w[i]);
+      const Frag<T> kr = (t < R.L) ? R.k[i] : frag_zero<T>();
       if constexpr (PC) {
-        f32x8 x = R.k[i].f32();
+        f32x8 x = kr.f32();
         float sq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
         for (int e = 0; e < 8; ++e) x[e] *= rn * __expf(Gl[d8 + e] - sm.gc[t * GP + d8 + e]);
         st8(&sm.k[b][t * KP + d8], Frag<T>::make(x));
       } else {
-        st8(&sm.k[b][t * KP + d8], R.k[i]);
+        st8(&sm.k[b][t * KP + d8], kr);
       }
     }
 #pragma unroll
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
 // other, and meet the compute waves at one LDS-only barrier per step.  The
 // compute waves therefore carry no prefetch registers, so the state and the
 // e tiles stay in architectural VGPRs next to the MFMAs.
-template <typename T, int C, int K, int NWC, int NWL>
+template <typename T, int C, int K, int NWC, int NWL, int NWO = 0>
 struct K3S {
   static constexpr int NTL = 64 * NWL;          // loader threads
   static constexpr int BV = 16 * NWC;           // value columns per workgroup
@@ -316,11 +316,29 @@ struct K3S {
   static constexpr int UP = C + 8 / sizeof(T);  // u rows (one per value column), +8 B
   static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(T) + (C + 4) * 4;
   static constexpr bool fits = 2 * buf_bytes <= 160 * 1024 && NKS <= NTL;
+  // Output staging: the compute waves leave h and e of a step in LDS and the
+  // loader waves store them during the next step, so the compute waves issue
+  // no vector-memory instructions at all (their stores would queue behind the
+  // loaders' loads in the CU's memory pipeline and stall the MFMA chain).
+  // Used when the two extra buffers fit next to the double-buffered tiles.
+  static constexpr int HSP = K + 16 / sizeof(T);  // staged h rows (one per value column)
+  static constexpr int VSP = C + 16 / sizeof(T);  // staged e rows
+  static constexpr size_t stg_bytes = (size_t)BV * (HSP + VSP) * sizeof(T);
+  static constexpr bool STG = 2 * (buf_bytes + stg_bytes) <= 160 * 1024;
+  static constexpr int NDH = (BV * K / 8 + NTL - 1) / NTL;   // staged h pieces per loader thread
+  static constexpr int NDV = (BV * C / 8 + NTL - 1) / NTL;   // staged e pieces per loader thread
+  // fused output: the loaders also stage each chunk's q tile and gates
+  static constexpr bool OUT = NWO > 0;
+  static constexpr int QP = K + 16 / sizeof(T);   // staged q rows
+  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 3 * C * 4 : 0;
+  static constexpr bool fits_out = STG && 2 * (buf_bytes + stg_bytes + q_bytes) <= 160 * 1024;
 
   struct Regs {
     Frag<T> w[NLD], k[NLD];
+    Frag<T> q[OUT ? NLD : 1];
     Frag<T> u[NLU];
     f32x4 ks;
+    float g;
     int64_t t0;
     int L;
   };
@@ -329,21 +347,36 @@ struct K3S {
     T k[2][C * KP];
     T u[2][BV * UP];
     float ks[2][C + 4];
+    T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
+    T es[STG ? 2 : 1][STG ? BV * VSP : 8];
+    T q[OUT ? 2 : 1][OUT ? C * QP : 8];
+    // per token of the staged chunk: gate cumsum G_t, 1 / |k_t|, 1 / |q_t|
+    __attribute__((aligned(16))) float gq[OUT ? 2 : 1][OUT ? C : 4];
+    __attribute__((aligned(16))) float rk[OUT ? 2 : 1][OUT ? C : 4];
+    __attribute__((aligned(16))) float rq[OUT ? 2 : 1][OUT ? C : 4];
   };
 };
 
-template <typename T, int C, int K, int NWC, int NWL>
-__global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
-  using Cfg = K3S<T, C, K, NWC, NWL>;
+template <typename T, int C, int K, int NWC, int NWL, int NWO>
+__global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
+  using Cfg = K3S<T, C, K, NWC, NWL, NWO>;
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
   constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
   constexpr int WP = Cfg::WP, KP = Cfg::KP, UP = Cfg::UP;
+  constexpr bool STG = Cfg::STG;
+  constexpr int HSP = Cfg::HSP, VSP = Cfg::VSP, NDH = Cfg::NDH, NDV = Cfg::NDV;
   __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
 
+  // fused output: NWO output waves compute o from the staged h / e, and
+  // neither h nor v_new is written
+  constexpr bool OUT = Cfg::OUT;
+  constexpr int QP = Cfg::QP;
+  static_assert(!OUT || (Cfg::fits_out && Cfg::NTL >= C), "the fused output reads the staged h / e / q");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
-  const bool loader = wv >= NWC;
-  const int tl = tid - 64 * NWC;                 // loader thread index
+  const bool loader = wv >= NWC + NWO;
+  const bool outw = !loader && wv >= NWC;
+  const int tl = tid - 64 * (NWC + NWO);         // loader thread index
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
   const int64_t nvt = V / BV;
   const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -378,20 +411,24 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
     for (int i = 0; i < NLD; ++i) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       const bool in = (NPW % NTL == 0) || idx < NPW;
-      // rows past L load row L-1 (a valid address) and are zeroed by a select
+      // Only loads here: nothing reads the payload until it is staged, so the
+      // in-order vector-memory counter lets the later payloads stay in flight.
+      // Rows past L load row L-1 (a valid address) and are zeroed when staged;
+      // pieces past the tile load piece 0 and are never staged.
       const int tc = t < R.L ? t : R.L - 1;
-      const Frag<T> kr = ld8(krow + (tc * (int)(H * K) + d8));
-      R.w[i] = in ? ld8(wp + 8 * idx) : frag_zero<T>();
-      R.k[i] = (in && t < R.L) ? kr : frag_zero<T>();
+      R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));
+      R.w[i] = ld8(wp + 8 * (in ? idx : 0));
+      if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
     }
+    if constexpr (OUT) R.g = a.g[(R.t0 + (tl < R.L ? tl : R.L - 1)) * HV + j];
     const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
     for (int i = 0; i < NLU; ++i) {
       const int idx = tl + NTL * i;
-      R.u[i] = ((NPU % NTL == 0) || idx < NPU) ? ld8(up + 8 * idx) : frag_zero<T>();
+      R.u[i] = ld8(up + 8 * (((NPU % NTL == 0) || idx < NPU) ? idx : 0));
     }
     const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
-    R.ks = (tl < NKS) ? *reinterpret_cast<const f32x4*>(ksp + 4 * tl) : zero4();
+    R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
   };
   auto stage = [&](const Regs& R, int b) {
 #pragma unroll
@@ -399,7 +436,35 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
       if ((NPW % NTL == 0) || idx < NPW) {
         st8(&sm.w[b][t * WP + d8], R.w[i]);
-        st8(&sm.k[b][t * KP + d8], R.k[i]);
+        st8(&sm.k[b][t * KP + d8], t < R.L ? R.k[i] : frag_zero<T>());
+        if constexpr (OUT) st8(&sm.q[b][t * QP + d8], t < R.L ? R.q[i] : frag_zero<T>());
+      }
+    }
+    if constexpr (OUT) {
+      // row norms of the staged k / q rows (the CPR consecutive threads that
+      // hold a row sum their pieces), and the chunk's gate cumsum (first
+      // loader wave, one token per lane); rows past L are zero
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+        const f32x8 xk = R.k[i].f32(), xq = R.q[i].f32();
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sk += xk[e] * xk[e];
+          sq += xq[e] * xq[e];
+        }
+        sk = lanes_sum_t<CPR>(sk);
+        sq = lanes_sum_t<CPR>(sq);
+        if (((NPW % NTL == 0) || idx < NPW) && d8 == 0) {
+          const bool live = t < R.L;
+          sm.rk[b][t] = a.l2norm ? 1.f / sqrtf((live ? sk : 0.f) + kL2Eps) : 1.f;
+          sm.rq[b][t] = a.l2norm ? 1.f / sqrtf((live ? sq : 0.f) + kL2Eps) : 1.f;
+        }
+      }
+      if (tl < 64) {
+        const float G = wave_incl_scan(tl < R.L ? R.g : 0.f, tl);
+        if (tl < C) sm.gq[b][tl] = G;
       }
     }
 #pragma unroll
@@ -410,12 +475,43 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
     if (tl < NKS) *reinterpret_cast<f32x4*>(&sm.ks[b][4 * tl]) = R.ks;
   };
 
+  // staged h / e of step x (buffer x % 2) to global memory, 16 contiguous
+  // bytes per lane: h^T rows of K features and e^T rows of C tokens are
+  // contiguous for the workgroup's BV value columns
+  auto drain = [&](int x) {
+    const int64_t c = c_begin + x;
+    T* hp = hbase + ((c * HV + j) * V + vw) * (int64_t)K;
+    T* vnp = vnbase + ((c * HV + j) * V + vw) * (int64_t)C;
+    Frag<T> hv[NDH], ev[NDV];
+#pragma unroll
+    for (int i = 0; i < NDH; ++i) {
+      const int idx = tl + NTL * i, v = idx / (K / 8), d8 = (idx % (K / 8)) * 8;
+      if ((BV * K / 8) % NTL == 0 || idx < BV * K / 8) hv[i] = ld8(&sm.hs[x & 1][v * HSP + d8]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) {
+      const int idx = tl + NTL * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+      if ((BV * C / 8) % NTL == 0 || idx < BV * C / 8) ev[i] = ld8(&sm.es[x & 1][v * VSP + t8]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDH; ++i) {
+      const int idx = tl + NTL * i;
+      if ((BV * K / 8) % NTL == 0 || idx < BV * K / 8) st8(hp + 8 * idx, hv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDV; ++i) {
+      const int idx = tl + NTL * i;
+      if ((BV * C / 8) % NTL == 0 || idx < BV * C / 8) st8(vnp + 8 * idx, ev[i]);
+    }
+  };
+
   // The loader and compute waves run separate loops with the same sequence of
   // barriers (one per chunk step), so neither carries the other's registers.
   // Chunk c_begin + x lives in register slot x % 3 and LDS buffer x % 2; at
   // step s the compute waves work on chunk s while the loaders stage chunk s + 1
   // and fetch chunk s + 4 (indices clamped to the last chunk; extra copies are
-  // staged but never computed).
+  // staged but never computed) and, with output staging, store the h / e that
+  // step s - 1 left in LDS.
   if (loader) {
     if (nc > 0) {
       Regs R0, R1, R2;
@@ -428,13 +524,173 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
       for (int s0 = 0; s0 < nc; s0 += 3) {
         stage(R1, (s0 + 1) & 1);
         fetch(R1, cl(c_begin + s0 + 4));
+        if constexpr (STG && !OUT) {
+          if (s0 > 0) drain(s0 - 1);
+        }
         lds_barrier();
         stage(R2, (s0 + 2) & 1);
         fetch(R2, cl(c_begin + s0 + 5));
+        if constexpr (STG && !OUT) {
+          if (s0 < nc) drain(s0);
+        }
         lds_barrier();
         stage(R0, (s0 + 3) & 1);
         fetch(R0, cl(c_begin + s0 + 6));
+        if constexpr (STG && !OUT) {
+          if (s0 + 1 < nc) drain(s0 + 1);
+        }
         lds_barrier();
+      }
+      // the last step's output when the loop ended right after it
+      if constexpr (STG && !OUT) {
+        if (nc % 3 == 0) drain(nc - 1);
+      }
+    }
+    return;
+  }
+
+  // ---- output waves (fused output).  During step x an output wave computes o
+  // of chunk x - 1 from the h / e the compute waves staged in LDS during step
+  // x - 1, then the P^T blocks of chunk x from the key tile staged for step x,
+  // as the output stage does: O^T = scale (h^T Q^T diag(exp(G) / |q|) +
+  // e^T P^T), P^T[t][r] = k^_t . q^_r exp(G_r - G_t) for t <= r.  q rows are
+  // read straight into MFMA operand registers one step ahead; o leaves as
+  // 16-byte stores of four consecutive value columns per lane and block pair.
+  if (outw) {
+    if constexpr (OUT) {
+      constexpr int NB = C / 16;                 // token blocks of a chunk
+      constexpr int TPW = NB / NWO;              // token blocks per output wave (1 or 2)
+      constexpr int NVB = BV / 16;               // value blocks of the workgroup
+      static_assert(TPW >= 1 && TPW <= 2 && TPW * NWO == NB, "output-wave token split");
+      // wave-uniform in a scalar register: the causal-block conditions below
+      // then compile to scalar branches.  Under a lane mask the compiler may
+      // leave a one-MFMA block without a skip branch, and an MFMA does not
+      // honour the lane mask, so a masked-off wave would still accumulate.
+      const int ow = __builtin_amdgcn_readfirstlane(wv - NWC);
+      // token blocks {ow, NB - 1 - ow}: equal causal work for both waves
+      auto tbk = [&](int m) { return m == 0 ? ow : NB - 1 - ow; };
+      const int tbmax = tbk(TPW - 1);
+      T* __restrict__ op = static_cast<T*>(a.o);
+      // operands of one chunk's output, carried from its P^T step to its o step
+      struct ORegs {
+        Frag<T> q[TPW][KSK];        // q rows of this wave's token blocks
+        SplitFrag<T> f[TPW][KSC];   // P^T as the chained B operand
+        float isc[TPW];             // exp(G_r) / |q_r|
+      };
+      auto chunk_t0 = [&](int x) { return seq_t0 + (int64_t)x * C; };
+      auto chunk_L = [&](int x) {
+        const int64_t r = seq_end - chunk_t0(x);
+        return (int)(r < C ? r : C);
+      };
+      // P^T blocks of chunk x from the staged keys, queries and gates
+      // (buffer x % 2; rows past L are zero there)
+      auto pphase = [&](ORegs& P, int x) {
+        const int L = chunk_L(x);
+        const int b = x & 1;
+        float rq[TPW], Gr[TPW];
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          const int rr = 16 * tbk(m) + r16;
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
+          rq[m] = sm.rq[b][rr];
+          Gr[m] = sm.gq[b][rr];
+        }
+        f32x4 Pt[TPW][NB];
+#pragma unroll
+        for (int m = 0; m < TPW; ++m)
+#pragma unroll
+          for (int jb = 0; jb < NB; ++jb) Pt[m][jb] = zero4();
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+          if (jb > tbmax) continue;
+          Frag<T> kf[KSK];
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) kf[ks] = ld8(&sm.k[b][(16 * jb + r16) * KP + 32 * ks + 8 * g4]);
+#pragma unroll
+          for (int m = 0; m < TPW; ++m) {
+            if (jb > tbk(m)) continue;
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) mma(Pt[m][jb], kf[ks], P.q[m][ks]);
+          }
+          // P^T[t][rr] with t = 16 jb + 4 g4 + i: the four tokens' factors in one read each
+          const f32x4 rk4 = *reinterpret_cast<const f32x4*>(&sm.rk[b][16 * jb + 4 * g4]);
+          const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sm.gq[b][16 * jb + 4 * g4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * jb + 4 * g4 + i;
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+              if (jb > tbk(m)) continue;
+              const int rr = 16 * tbk(m) + r16;
+              Pt[m][jb][i] *= (t <= rr && rr < L) ? rq[m] * rk4[i] * __expf(Gr[m] - G4[i]) : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+#pragma unroll
+          for (int kt = 0; kt < KSC; ++kt) P.f[m][kt] = SplitFrag<T>::make(cat8(Pt[m][2 * kt], Pt[m][2 * kt + 1]));
+          P.isc[m] = rq[m] * __expf(Gr[m]);
+        }
+      };
+      // o of chunk x from the staged h / e (buffer x % 2) and its P^T step's operands
+      auto ophase = [&](const ORegs& P, int x) {
+        const int64_t t0 = chunk_t0(x);
+        const int L = chunk_L(x);
+        const T* hsb = sm.hs[x & 1];
+        const T* esb = sm.es[x & 1];
+        f32x4 O[TPW][NVB];
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          Frag<T> hf[KSK];
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) hf[ks] = ld8(&hsb[(16 * vb + r16) * HSP + 32 * ks + 8 * g4]);
+          const T* erow = &esb[(16 * vb + r16) * VSP];
+#pragma unroll
+          for (int m = 0; m < TPW; ++m) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) mma(acc, hf[ks], P.q[m][ks]);
+            acc *= P.isc[m];
+#pragma unroll
+            for (int kt = 0; kt < KSC; ++kt) {
+              if (2 * kt > tbk(m)) continue;
+              mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), P.f[m][kt]);
+            }
+            O[m][vb] = acc * a.scale;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          const int rr = 16 * tbk(m) + r16;
+          T* orow = op + ((t0 + rr) * HV + j) * V + vw;
+          if (rr < L) {
+            if constexpr (NVB % 2 == 0) {
+#pragma unroll
+              for (int pb = 0; pb < NVB / 2; ++pb) st_pair(orow + 32 * pb, O[m][2 * pb], O[m][2 * pb + 1], lane);
+            } else {
+#pragma unroll
+              for (int vb = 0; vb < NVB; ++vb) st4(orow + 16 * vb + 4 * g4, O[m][vb]);
+            }
+          }
+        }
+      };
+
+      // Same barrier sequence as the other roles: one per chunk step over
+      // 3 ceil(nc / 3) steps.  Step x: o of chunk x - 1, then P^T of chunk x
+      // (whose operands stay in registers for the next step's o).
+      if (nc > 0) {
+        ORegs P;
+        lds_barrier();
+        const int nsteps = 3 * ((nc + 2) / 3);
+        for (int x = 0; x < nsteps; ++x) {
+          if (x >= 1 && x - 1 < nc) ophase(P, x - 1);
+          if (x < nc) pphase(P, x);
+          lds_barrier();
+        }
+        // the last chunk's o when the loop ended right after its step
+        if (nsteps == nc) ophase(P, nc - 1);
       }
     }
     return;
@@ -476,10 +732,17 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
     const float gl = sm.ks[b][C];
-    // h[c] = S (transposed, 4 features per lane)
-    T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
+    // h[c] = S (transposed): staged in LDS for the loaders, or stored directly
+    // with feature blocks paired into 16-byte stores
+    if constexpr (STG) {
+      T* hs = &sm.hs[b][(16 * wv + r16) * HSP];
 #pragma unroll
-    for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
+      for (int mb = 0; mb < NS; ++mb) st4(hs + 16 * mb + 4 * g4, S[mb]);
+    } else {
+      T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
+#pragma unroll
+      for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
+    }
     // e = u - w S  (independent accumulators alternate between MFMAs)
     Frag<T> nS[KSK];
 #pragma unroll
@@ -489,9 +752,15 @@ __global__ __launch_bounds__(64 * (NWC + NWL)) void k3_scan(Args a) {
 #pragma unroll
       for (int eb = 0; eb < NE; ++eb) mma(E[eb], wf[ks][eb], nS[ks]);
     // v_new = e (transposed per chunk)
-    T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
+    if constexpr (STG) {
+      T* es = &sm.es[b][(16 * wv + r16) * VSP];
 #pragma unroll
-    for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
+      for (int eb = 0; eb < NE; ++eb) st4(es + 16 * eb + 4 * g4, E[eb]);
+    } else {
+      T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
+#pragma unroll
+      for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
+    }
     // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e
     Frag<T> Ef[KSC];
 #pragma unroll
@@ -547,9 +816,9 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       // only way to use the whole chip on few long sequences
       const int64_t nblk32 = a.N * a.HV * (a.V / 32);
       if (nblk32 < kNumCUs) {
-        hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+        hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
       } else {
-        hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+        hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
       }
       return hipGetLastError();
     }
@@ -576,11 +845,70 @@ hipError_t launch_c(const Args& a, hipStream_t s) {
   return a.per_channel ? launch_k<T, 64, true>(a, s) : launch_k<T, 64, false>(a, s);
 }
 
+// ---- fused state scan + output (scalar gate): 1 or 2 compute waves, 2 output
+// waves, 4 loader waves (the output waves' registers leave room for only half
+// a loader payload per thread).  Shapes qualify when the staged h / e fit in
+// LDS next to the double-buffered tiles and no role spills.
+template <typename T, int C, int K>
+constexpr bool fused_ok() {
+  return K3S<T, C, K, 2, 4, 2>::fits && K3S<T, C, K, 2, 4, 2>::fits_out && K3S<T, C, K, 1, 4, 2>::fits_out &&
+         K <= 128;
+}
+
+template <typename T, int C, int K>
+hipError_t launch_fused_t(const Args& a, hipStream_t s) {
+  if constexpr (fused_ok<T, C, K>()) {
+    const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+    if (nblk32 < kNumCUs) {
+      hipLaunchKernelGGL((k3_scan<T, C, K, 1, 4, 2>), dim3((unsigned)(2 * nblk32)), dim3(64 * 7), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, 4, 2>), dim3((unsigned)nblk32), dim3(64 * 8), 0, s, a);
+    }
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int C>
+bool fused_ok_k(int64_t K) {
+  switch (K) {
+    case 32: return fused_ok<T, C, 32>();
+    case 64: return fused_ok<T, C, 64>();
+    case 128: return fused_ok<T, C, 128>();
+    case 256: return fused_ok<T, C, 256>();
+  }
+  return false;
+}
+
+template <typename T, int C>
+hipError_t launch_fused_k(const Args& a, hipStream_t s) {
+  switch (a.K) {
+    case 32: return launch_fused_t<T, C, 32>(a, s);
+    case 64: return launch_fused_t<T, C, 64>(a, s);
+    case 128: return launch_fused_t<T, C, 128>(a, s);
+    case 256: return launch_fused_t<T, C, 256>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_h(const Args& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
+}
+
+bool fwd_h_o_supported(const Args& a) {
+  if (a.per_channel) return false;
+  if (a.dtype == GDR_BF16) return a.C == 32 ? fused_ok_k<bf16, 32>(a.K) : fused_ok_k<bf16, 64>(a.K);
+  return a.C == 32 ? fused_ok_k<float, 32>(a.K) : fused_ok_k<float, 64>(a.K);
+}
+
+hipError_t launch_fwd_h_o(const Args& a, hipStream_t s) {
+  if (a.N == 0) return hipSuccess;
+  if (a.dtype == GDR_BF16) return a.C == 32 ? launch_fused_k<bf16, 32>(a, s) : launch_fused_k<bf16, 64>(a, s);
+  return a.C == 32 ? launch_fused_k<float, 32>(a, s) : launch_fused_k<float, 64>(a, s);
 }
 
 }  // namespace gdr

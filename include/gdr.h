@@ -55,7 +55,8 @@ typedef enum {
   GDR_ERR_HIP = 8,         /* a kernel launch failed */
   GDR_ERR_CU_SEQLENS = 9,  /* gdr_validate_cu_seqlens: bad table */
   GDR_ERR_UNSUPPORTED = 10 /* backward: per-channel gate, K = 256, or fp32 with K = 128 and
-                              chunk 64 (see gdr_chunk_bwd) */
+                              chunk 64 (see gdr_chunk_bwd); gdr_fwd_h_o: a shape without
+                              the fused stage (see gdr_fwd_h_o_supported) */
 } gdr_status;
 
 typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
@@ -70,6 +71,10 @@ typedef struct {
   int32_t use_qk_l2norm;     /* 1: normalise q, k rows in the kernels */
   int32_t dtype;             /* gdr_dtype */
   float scale;               /* output scale */
+  int32_t keep_states;       /* gdr_chunk_fwd only: 1 = run the separate K3 and K4 stages and
+                                leave h and v_new in the workspace; 0 = use the fused
+                                scan + output stage where gdr_fwd_h_o_supported (h and
+                                v_new are then not written) */
 } gdr_problem;
 
 /* Offsets (bytes from the workspace base) of the forward intermediates that
@@ -108,7 +113,10 @@ gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
- * K3 state scan -> K4 output, all on `stream`.
+ * K3 state scan -> K4 output, all on `stream`; with p->keep_states == 0 and a
+ * shape that gdr_fwd_h_o_supported accepts, K3 and K4 run as the one fused
+ * stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
+ * untouched.
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
@@ -162,6 +170,20 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
 gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const void* v_new,
                      const void* h, const float* g, const int32_t* chunk_idx,
                      const int32_t* chunk_off, void* o, void* stream);
+
+/* K3 + K4 fused (scalar gate): the state scan of gdr_fwd_h and the output of
+ * gdr_fwd_o in one pass, o computed from each chunk's h and e while they are
+ * on chip, so neither is written (same operator as the two stages: the chunk
+ * form of the coverage-matrix page, section 2, with h as on the KCP page,
+ * section "h and dh cross-rank semantics").  g (scalar gate [B,T,HV]) and
+ * K1's kscale are both required; h0 / ht as gdr_fwd_h.  Returns
+ * GDR_ERR_UNSUPPORTED for a per-channel gate or a shape without an
+ * instantiation; gdr_fwd_h_o_supported tells in advance (1 = supported). */
+int gdr_fwd_h_o_supported(const gdr_problem* p);
+gdr_status gdr_fwd_h_o(const gdr_problem* p, const void* q, const void* k, const void* w,
+                       const void* u, const float* g, const float* kscale,
+                       const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0,
+                       void* o, float* ht, void* stream);
 
 /* ------------------------------------------------------------------ backward
  *

@@ -18,16 +18,18 @@ def dev(x):
     return None if x is None else x.cuda()
 
 
-def gpu_fwd(inp, *, h0=True, ht=True, workspace=None, out=None):
+def gpu_fwd(inp, *, h0=True, ht=True, workspace=None, out=None, keep_states=False):
     """Library forward on the inputs of ``workloads.make_inputs``; returns
-    (o, ht, workspace views) with o / ht on the CPU as float64."""
+    (o, ht, workspace views).  ``keep_states`` runs the separate scan and
+    output stages (h and v_new kept in the workspace); otherwise the library
+    picks the fused scan + output stage where the shape has one."""
     cu = dev(inp["cu_seqlens"])
     o, htd, ws = gdr.chunk_fwd(
         dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
         scale=inp["scale"], chunk_size=inp["chunk_size"], cu_seqlens=cu,
         initial_state=dev(inp["h0"]) if h0 else None, output_final_state=ht,
         use_qk_l2norm_in_kernel=inp["use_qk_l2norm"], workspace=workspace, return_workspace=True,
-        out=out)
+        out=out, keep_states=keep_states)
     torch.cuda.synchronize()
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=inp["chunk_size"],
                          cu_seqlens=inp["cu_seqlens"], use_qk_l2norm=inp["use_qk_l2norm"],

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdr_abi_version() == 1
+    assert L.gdr_abi_version() == 2
 
 
 def test_status_strings():
@@ -123,6 +123,30 @@ def test_fwd_rejects_before_launch():
     st = L.gdr_chunk_fwd(ctypes.byref(p), *args[:5], P(0x1000), None, P(0x1000), None, P(0x1000),
                          ctypes.c_size_t(1 << 40), None)
     assert st == 4
+
+
+def test_fused_stage_support_and_host_rejections():
+    """Which shapes have the fused scan + output stage, and its host-side
+    errors (no call here reaches a launch)."""
+    L = gdr.lib()
+    sup = lambda **kw: L.gdr_fwd_h_o_supported(ctypes.byref(problem(**kw)))
+    assert sup(K=128, V=128) == 1                       # the dense bf16 workload's shape
+    assert sup(K=64, V=256, chunk_size=32) == 1
+    assert sup(K=64, dtype=gdr.GDR_FP32) == 1
+    assert sup(K=128, gate_per_channel=1) == 0           # per-channel gate: separate stages
+    assert sup(K=256) == 0
+    assert sup(K=128, dtype=gdr.GDR_FP32) == 0          # staged tiles exceed LDS
+    assert sup(chunk_size=16) == 0
+    P = ctypes.c_void_p
+    args = [P(0x1000)] * 11
+    p = problem()
+    assert L.gdr_fwd_h_o(ctypes.byref(p), None, *args[1:], None) == 1       # null q
+    assert L.gdr_fwd_h_o(ctypes.byref(p), *args[:5], None, *args[6:], None) == 1   # null kscale
+    assert L.gdr_fwd_h_o(ctypes.byref(p), P(0x1008), *args[1:], None) == 6  # misaligned q
+    pc = problem(gate_per_channel=1)
+    assert L.gdr_fwd_h_o(ctypes.byref(pc), *args, None) == 10
+    pk = problem(K=256)
+    assert L.gdr_fwd_h_o(ctypes.byref(pk), *args, None) == 10
 
 
 def test_python_wrapper_refuses_cpu_tensors():

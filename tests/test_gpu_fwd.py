@@ -86,7 +86,7 @@ def test_stage_intermediates(cfg):
     oracle's per-chunk quantities, on a ragged dense batch with slow decay."""
     w, inp = mk(T=150, slow=True, **cfg)
     tol = TOL[w.dtype]
-    o, ht, ws = gpu_fwd(inp)
+    o, ht, ws = gpu_fwd(inp, keep_states=True)
     ro, rht, it = oracle_fwd(inp, intermediates=True)
     NT = int(it["off"][-1])
     assert np.array_equal(ws["chunk_idx"][:NT, :3].cpu().numpy(), it["idx"])
@@ -99,6 +99,54 @@ def test_stage_intermediates(cfg):
     check("ht", f64(ht), rht, tol)
 
 
+# ------------------------------------------------------------------ fused scan + output
+
+FUSED_CASES = [
+    dict(dtype="bf16", K=128, V=128, C=64),
+    dict(dtype="bf16", K=64, V=256, C=32, H=1, HV=4),
+    dict(dtype="fp32", K=64, V=64, C=64),
+    dict(dtype="bf16", K=32, V=64, C=64, l2=False, host_l2=True),
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_fused_stage_against_separate_stages(cfg):
+    """gdr_fwd_h_o on the K0-K2 intermediates of a keep-states forward: ht is
+    bit-identical to the separate scan's (the scan arithmetic is the same), o
+    agrees with the separate output stage, and both match the oracle."""
+    w, inp = mk(T=150, slow=True, **cfg)
+    tol = TOL[w.dtype]
+    o_sep, ht_sep, ws = gpu_fwd(inp, keep_states=True)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=inp["chunk_size"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    assert gdr.fwd_h_o_supported(p)
+    o_f = torch.full_like(o_sep, float("nan"))
+    ht_f = torch.full_like(ht_sep, float("nan"))
+    gdr.fwd_h_o(p, dev(inp["q"]), dev(inp["k"]), ws["w"], ws["u"], dev(inp["g"]), ws["kscale"],
+                ws["chunk_idx"], ws["chunk_off"], dev(inp["h0"]), o_f, ht_f)
+    torch.cuda.synchronize()
+    assert torch.equal(ht_f, ht_sep)
+    ro, rht = oracle_fwd(inp)
+    check("o fused", f64(o_f), ro, tol)
+    check("o separate", f64(o_sep), ro, tol)
+    check("ht", f64(ht_f), rht, tol)
+    assert err_ratio(f64(o_f), f64(o_sep)) <= tol / 4
+
+
+def test_fused_default_leaves_states_untouched():
+    """Without keep_states the forward takes the fused stage: o / ht match the
+    oracle and the h / v_new regions of the workspace keep their fill."""
+    w, inp = mk(B=2, T=170, H=2, HV=4, K=128, V=128, slow=True)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
+    lay = gdr.fwd_layout(p)
+    ws = torch.full((lay.total,), 0x5A, dtype=torch.uint8, device="cuda")
+    o, ht, views = gpu_fwd(inp, workspace=ws)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL["bf16"])
+    check("ht", f64(ht), rht, TOL["bf16"])
+    assert (ws[lay.h:lay.v_new] == 0x5A).all() and (ws[lay.v_new:lay.kscale] == 0x5A).all()
+
+
 # ------------------------------------------------------------------ sweep
 
 SWEEP = []
@@ -109,13 +157,19 @@ for dtype in ("bf16", "fp32"):
                 if dtype == "fp32" and pc and K == 256 and C == 64:
                     continue
                 SWEEP.append(dict(dtype=dtype, C=C, K=K, V=V, pc=pc))
+                if not pc:
+                    # the separate scan and output stages too (the default is the
+                    # fused stage wherever the shape has one)
+                    SWEEP.append(dict(dtype=dtype, C=C, K=K, V=V, pc=pc, keep=True))
 
 
 @pytest.mark.parametrize("cfg", SWEEP, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_forward_sweep(cfg):
     """Dense GVA batch with a ragged tail, in-kernel L2 norm, h0, slow decay."""
+    cfg = dict(cfg)
+    keep = cfg.pop("keep", False)
     w, inp = mk(B=2, T=137, H=2, HV=4, slow=True, scale=0.75, **cfg)
-    o, ht, _ = gpu_fwd(inp)
+    o, ht, _ = gpu_fwd(inp, keep_states=keep)
     ro, rht = oracle_fwd(inp)
     check("o", f64(o), ro, TOL[w.dtype])
     check("ht", f64(ht), rht, TOL[w.dtype])
@@ -306,15 +360,16 @@ def test_int64_offsets():
     cu = torch.tensor([0, lengths[0], T], dtype=torch.int32)
     inp = dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, scale=1.0, chunk_size=64,
                use_qk_l2norm=True)
-    o, ht, ws = gpu_fwd(inp)
     sub = dict(inp, cu_seqlens=None, h0=h0[1:2])
     for key in ("q", "k", "v", "g", "beta"):
         sub[key] = inp[key][:, s:].contiguous()
     ro, rht = oracle_fwd(sub)
-    check("o tail", f64(o[:, s:]), ro, 5e-3)
-    check("ht tail", f64(ht[1:2]), rht, 5e-3)
-    del ws
-    torch.cuda.empty_cache()
+    for keep in (True, False):     # separate stages (h offsets past 2^31), then fused
+        o, ht, ws = gpu_fwd(inp, keep_states=keep)
+        check(f"o tail keep={keep}", f64(o[:, s:]), ro, 5e-3)
+        check(f"ht tail keep={keep}", f64(ht[1:2]), rht, 5e-3)
+        del o, ht, ws
+        torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ the five workloads
