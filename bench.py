@@ -337,7 +337,7 @@ def measure(gdr, w, steps, warmup, breakdown, label):
                                        cidx, coff, d["h0"], o, ht),
     }
     # the stages the timed step runs: the fused scan + output where the shape has it
-    fused = gdr.fwd_h_o_supported(p)
+    fused = gdr.chunk_fwd_fused(p)
     for name in (("fwd_h", "fwd_o") if fused else ("fwd_h_o",)):
         del fstages[name]
     reps = max(5, min(steps, 50))

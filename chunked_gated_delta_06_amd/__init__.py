@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
         L.gdr_fwd_h_o_supported.argtypes = [PP]
         L.gdr_fwd_h_o_supported.restype = ctypes.c_int
+        L.gdr_chunk_fwd_fused.argtypes = [PP]
+        L.gdr_chunk_fwd_fused.restype = ctypes.c_int
         L.gdr_fwd_h_o.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_bwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_bwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrBwdLayout)]
@@ -261,7 +263,7 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
         u=view(lay.u, (nt, HV, V, C), dt, es),
         h=view(lay.h, (nt, HV, V, K), dt, es),
         v_new=view(lay.v_new, (nt, HV, V, C), dt, es),
-        kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, C + 4), torch.float32, 4),
+        kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, 3 * C + 4), torch.float32, 4),
     )
 
 
@@ -295,6 +297,11 @@ def fwd_o(p, q, k, v_new, h, g, chunk_idx, chunk_off, o):
 
 def fwd_h_o_supported(p) -> bool:
     return bool(lib().gdr_fwd_h_o_supported(ctypes.byref(p)))
+
+
+def chunk_fwd_fused(p) -> bool:
+    """Whether gdr_chunk_fwd runs the fused scan + output stage for ``p``."""
+    return bool(lib().gdr_chunk_fwd_fused(ctypes.byref(p)))
 
 
 def fwd_h_o(p, q, k, w, u, g, kscale, chunk_idx, chunk_off, h0, o, ht):

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       const int idx = tl + NTL * i;
       R.e[i] = ld8(ep + 8 * (((NPE % NTL == 0) || idx < NPE) ? idx : 0));
     }
-    const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+    const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
     R.L = L;
   };

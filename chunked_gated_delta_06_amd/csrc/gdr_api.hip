@@ -98,7 +98,7 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   l.v_new = off;
   off = round_up(off + (size_t)nt * HV * V * C * es);
   l.kscale = off;
-  off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * (C + 4) * sizeof(float)));
+  off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float)));
   l.total = off;
   return l;
 }
@@ -219,7 +219,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   hipError_t e = gdr::launch_chunk_table(a, s);
   if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
   if (e == hipSuccess) e = gdr::launch_wy(a, s);
-  if (!p->keep_states && gdr::fwd_h_o_supported(a)) {
+  if (!p->keep_states && gdr::fwd_h_o_preferred(a)) {
     // fused scan + output: h and v_new never leave the chip
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
   } else {
@@ -311,6 +311,11 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
   a.v_new = v_new;
   a.ht = ht;
   return hip_status(gdr::launch_fwd_h(a, static_cast<hipStream_t>(stream)));
+}
+
+int gdr_chunk_fwd_fused(const gdr_problem* p) {
+  if (check(p, p ? p->N != p->B : false) != GDR_OK) return 0;
+  return !p->keep_states && gdr::fwd_h_o_preferred(make_args(*p)) ? 1 : 0;
 }
 
 int gdr_fwd_h_o_supported(const gdr_problem* p) {

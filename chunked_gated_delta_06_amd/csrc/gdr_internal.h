@@ -8,6 +8,14 @@
 
 namespace gdr {
 
+// Per-chunk token factors written by K1 (scalar gate), one row of
+// kscale_pitch(C) floats per chunk and value head:
+//   [0, C)         exp(G_L - G_t) / |k_t|   (0 past L)
+//   [C, C + 4)     exp(G_L), 0, 0, 0
+//   [C + 4, 2C + 4)   G_t, the chunk-local gate cumsum   (0 past L)
+//   [2C + 4, 3C + 4)  1 / |k_t| (1 without the in-kernel norm; 0 past L)
+constexpr int64_t kscale_pitch(int64_t C) { return 3 * C + 4; }
+
 // Everything a stage needs: the problem and plain device pointers (forward
 // stages leave the backward fields NULL).
 struct Args {
@@ -54,6 +62,7 @@ hipError_t launch_fwd_h(const Args& a, hipStream_t s);
 // fused state scan + output (no h / v_new); fwd_h_o_supported says whether the
 // shape has an instantiation (scalar gate, staged tiles fit in LDS)
 bool fwd_h_o_supported(const Args& a);
+bool fwd_h_o_preferred(const Args& a);   // the full forward's choice
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s);

@@ -262,13 +262,18 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
       lds_barrier();
     }
 
-    // ---- per-token factors the state scan applies to the rows of e:
-    //      kscale[t] = exp(G_L - G_t) / |k_t| (0 past L), kscale[C] = exp(G_L)
+    // ---- per-token factors of the chunk (layout at kscale_pitch): the ones
+    //      the state scan applies to the rows of e, kscale[t] = exp(G_L - G_t)
+    //      / |k_t| and exp(G_L), then G_t and 1 / |k_t| for the fused output
     if constexpr (!PC) {
       if (a.kscale != nullptr) {
-        float* ks = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+        float* ks = a.kscale + (c * HV + j) * kscale_pitch(C);
         const float GL = __shfl(Gc, 63, 64);     // padded lanes add 0, so lane 63 holds G_L
-        if (lane < C) ks[lane] = (lane < L) ? __expf(GL - Gc) * sRn[lane] : 0.f;
+        if (lane < C) {
+          ks[lane] = (lane < L) ? __expf(GL - Gc) * sRn[lane] : 0.f;
+          ks[C + 4 + lane] = (lane < L) ? Gc : 0.f;
+          ks[2 * C + 4 + lane] = (lane < L) ? sRn[lane] : 0.f;
+        }
         if (lane < 4) ks[C + lane] = (lane == 0) ? __expf(GL) : 0.f;
       }
     }

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
         R.gc[i] = *reinterpret_cast<const f32x4*>(grow + (tc * (int)(HV * K) + d4));
       }
     } else {
-      const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+      const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
 #pragma unroll
       for (int eb = 0; eb < NE; ++eb) R.ks[eb] = *reinterpret_cast<const f32x4*>(ksp + 16 * eb + 4 * g4);
       R.gl = ksp[C];
@@ -313,7 +313,7 @@ struct K3S {
   static constexpr int NKS = (C + 4) / 4;       // float4 pieces of a kscale row
   static constexpr int WP = K + 16 / sizeof(T);
   static constexpr int KP = K + 32 / sizeof(T);
-  static constexpr int UP = C + 8 / sizeof(T);  // u rows (one per value column), +8 B
+  static constexpr int UP = C + 16 / sizeof(T); // u rows (one per value column), +16 B
   static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(T) + (C + 4) * 4;
   static constexpr bool fits = 2 * buf_bytes <= 160 * 1024 && NKS <= NTL;
   // Output staging: the compute waves leave h and e of a step in LDS and the
@@ -330,7 +330,7 @@ struct K3S {
   // fused output: the loaders also stage each chunk's q tile and gates
   static constexpr bool OUT = NWO > 0;
   static constexpr int QP = K + 16 / sizeof(T);   // staged q rows
-  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 3 * C * 4 : 0;
+  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 2 * C * 4 : 0;
   static constexpr bool fits_out = STG && 2 * (buf_bytes + stg_bytes + q_bytes) <= 160 * 1024;
 
   struct Regs {
@@ -338,7 +338,7 @@ struct K3S {
     Frag<T> q[OUT ? NLD : 1];
     Frag<T> u[NLU];
     f32x4 ks;
-    float g;
+    float g2;                 // G_t (threads < C) or 1 / |k_t| (threads C .. 2C - 1)
     int64_t t0;
     int L;
   };
@@ -350,10 +350,9 @@ struct K3S {
     T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
     T es[STG ? 2 : 1][STG ? BV * VSP : 8];
     T q[OUT ? 2 : 1][OUT ? C * QP : 8];
-    // per token of the staged chunk: gate cumsum G_t, 1 / |k_t|, 1 / |q_t|
+    // per token of the staged chunk: gate cumsum G_t and 1 / |k_t|
     __attribute__((aligned(16))) float gq[OUT ? 2 : 1][OUT ? C : 4];
     __attribute__((aligned(16))) float rk[OUT ? 2 : 1][OUT ? C : 4];
-    __attribute__((aligned(16))) float rq[OUT ? 2 : 1][OUT ? C : 4];
   };
 };
 
@@ -372,7 +371,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   // neither h nor v_new is written
   constexpr bool OUT = Cfg::OUT;
   constexpr int QP = Cfg::QP;
-  static_assert(!OUT || (Cfg::fits_out && Cfg::NTL >= C), "the fused output reads the staged h / e / q");
+  static_assert(!OUT || (Cfg::fits_out && Cfg::NTL >= 2 * C), "the fused output reads the staged h / e / q");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const bool loader = wv >= NWC + NWO;
   const bool outw = !loader && wv >= NWC;
@@ -420,15 +419,16 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
       if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
     }
-    if constexpr (OUT) R.g = a.g[(R.t0 + (tl < R.L ? tl : R.L - 1)) * HV + j];
     const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
     for (int i = 0; i < NLU; ++i) {
       const int idx = tl + NTL * i;
       R.u[i] = ld8(up + 8 * (((NPU % NTL == 0) || idx < NPU) ? idx : 0));
     }
-    const float* ksp = a.kscale + (c * HV + j) * (int64_t)(C + 4);
+    const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
+    // fused output: G_t and 1 / |k_t| of the chunk (K1's token factors)
+    if constexpr (OUT) R.g2 = ksp[C + 4 + (tl < 2 * C ? tl : 0)];
   };
   auto stage = [&](const Regs& R, int b) {
 #pragma unroll
@@ -441,31 +441,8 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       }
     }
     if constexpr (OUT) {
-      // row norms of the staged k / q rows (the CPR consecutive threads that
-      // hold a row sum their pieces), and the chunk's gate cumsum (first
-      // loader wave, one token per lane); rows past L are zero
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
-        const f32x8 xk = R.k[i].f32(), xq = R.q[i].f32();
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sk += xk[e] * xk[e];
-          sq += xq[e] * xq[e];
-        }
-        sk = lanes_sum_t<CPR>(sk);
-        sq = lanes_sum_t<CPR>(sq);
-        if (((NPW % NTL == 0) || idx < NPW) && d8 == 0) {
-          const bool live = t < R.L;
-          sm.rk[b][t] = a.l2norm ? 1.f / sqrtf((live ? sk : 0.f) + kL2Eps) : 1.f;
-          sm.rq[b][t] = a.l2norm ? 1.f / sqrtf((live ? sq : 0.f) + kL2Eps) : 1.f;
-        }
-      }
-      if (tl < 64) {
-        const float G = wave_incl_scan(tl < R.L ? R.g : 0.f, tl);
-        if (tl < C) sm.gq[b][tl] = G;
-      }
+      if (tl < C) sm.gq[b][tl] = R.g2;
+      else if (tl < 2 * C) sm.rk[b][tl - C] = R.g2;
     }
 #pragma unroll
     for (int i = 0; i < NLU; ++i) {
@@ -591,9 +568,16 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
           const int rr = 16 * tbk(m) + r16;
+          float sq = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < KSK; ++ks) P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
-          rq[m] = sm.rq[b][rr];
+          for (int ks = 0; ks < KSK; ++ks) {
+            P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
+            const f32x8 xq = P.q[m][ks].f32();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq += xq[e] * xq[e];
+          }
+          sq = group4_sum(sq);
+          rq[m] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
           Gr[m] = sm.gq[b][rr];
         }
         f32x4 Pt[TPW][NB];
@@ -903,6 +887,13 @@ bool fwd_h_o_supported(const Args& a) {
   if (a.per_channel) return false;
   if (a.dtype == GDR_BF16) return a.C == 32 ? fused_ok_k<bf16, 32>(a.K) : fused_ok_k<bf16, 64>(a.K);
   return a.C == 32 ? fused_ok_k<float, 32>(a.K) : fused_ok_k<float, 64>(a.K);
+}
+
+bool fwd_h_o_preferred(const Args& a) {
+  // with fewer 32-column tiles than compute units the scan runs one compute
+  // wave (16 columns) per workgroup, and the output waves would recompute a
+  // chunk's causal block for every 16 columns: the separate stages are faster
+  return fwd_h_o_supported(a) && a.N * a.HV * (a.V / 32) >= kNumCUs;
 }
 
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s) {

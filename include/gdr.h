@@ -87,8 +87,11 @@ typedef struct {
  *   u          dtype [NT_max][HV][V][C]   WY values, transposed per chunk
  *   h          dtype [NT_max][HV][V][K]   state entering each chunk, transposed (h^T)
  *   v_new      dtype [NT_max][HV][V][C]   corrected values e, transposed per chunk
- *   kscale     f32   [NT_max][HV][C + 4]  scalar gate only: exp(G_L - G_t) / |k_t| per
- *                                         row t (0 past L), then exp(G_L), then 3 zeros
+ *   kscale     f32   [NT_max][HV][3C + 4] scalar gate only, per chunk token factors:
+ *                                         exp(G_L - G_t) / |k_t| per row t, then exp(G_L)
+ *                                         and 3 zeros, then G_t (chunk-local gate cumsum),
+ *                                         then 1 / |k_t| (1 without the in-kernel norm);
+ *                                         0 past L
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;
@@ -113,10 +116,11 @@ gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
- * K3 state scan -> K4 output, all on `stream`; with p->keep_states == 0 and a
- * shape that gdr_fwd_h_o_supported accepts, K3 and K4 run as the one fused
- * stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
- * untouched.
+ * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0, a
+ * shape that gdr_fwd_h_o_supported accepts and at least one 32-column value
+ * tile per compute unit (N * HV * V / 32 >= 256), K3 and K4 run as the one
+ * fused stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
+ * untouched; gdr_chunk_fwd_fused(p) returns 1 exactly then.
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
@@ -180,6 +184,7 @@ gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const v
  * GDR_ERR_UNSUPPORTED for a per-channel gate or a shape without an
  * instantiation; gdr_fwd_h_o_supported tells in advance (1 = supported). */
 int gdr_fwd_h_o_supported(const gdr_problem* p);
+int gdr_chunk_fwd_fused(const gdr_problem* p);
 gdr_status gdr_fwd_h_o(const gdr_problem* p, const void* q, const void* k, const void* w,
                        const void* u, const float* g, const float* kscale,
                        const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0,

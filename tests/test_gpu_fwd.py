@@ -102,10 +102,16 @@ def test_stage_intermediates(cfg):
 # ------------------------------------------------------------------ fused scan + output
 
 FUSED_CASES = [
+    # few value tiles: one compute wave (16 value columns) per workgroup
     dict(dtype="bf16", K=128, V=128, C=64),
     dict(dtype="bf16", K=64, V=256, C=32, H=1, HV=4),
     dict(dtype="fp32", K=64, V=64, C=64),
     dict(dtype="bf16", K=32, V=64, C=64, l2=False, host_l2=True),
+    # >= 256 tiles of 32 value columns: two compute waves per workgroup (the
+    # variant the full forward picks)
+    dict(dtype="bf16", K=128, V=128, C=64, H=8, HV=32),
+    dict(dtype="bf16", K=64, V=256, C=32, B=1, H=4, HV=32),
+    dict(dtype="fp32", K=64, V=64, C=64, H=16, HV=64),
 ]
 
 
@@ -136,8 +142,9 @@ def test_fused_stage_against_separate_stages(cfg):
 def test_fused_default_leaves_states_untouched():
     """Without keep_states the forward takes the fused stage: o / ht match the
     oracle and the h / v_new regions of the workspace keep their fill."""
-    w, inp = mk(B=2, T=170, H=2, HV=4, K=128, V=128, slow=True)
+    w, inp = mk(B=2, T=170, H=8, HV=32, K=128, V=128, slow=True)
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
+    assert gdr.chunk_fwd_fused(p)
     lay = gdr.fwd_layout(p)
     ws = torch.full((lay.total,), 0x5A, dtype=torch.uint8, device="cuda")
     o, ht, views = gpu_fwd(inp, workspace=ws)
