@@ -43,13 +43,17 @@ def stage_bytes_per_token_head(w, T_seq):
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
     gb = 4 * K if w.per_channel_gate else 4
+    # K1's per-chunk token factors (scalar gate): 3C + 4 floats per chunk and
+    # value head, of which the separate scan reads the first C + 4
+    kf_row = 0 if w.per_channel_gate else 4 * (3 * C + 4) / C
+    kf_scan = gb if w.per_channel_gate else 4 * (C + 4) / C
     return {
-        "kkt_solve": r * K * e + gb + 4 + e * C,
+        "kkt_solve": r * K * e + gb + 4 + e * C + kf_row,
         "wy": r * K * e + V * e + e * C + gb + 4 + e * K + e * V,
-        "fwd_h": e * K + e * V + r * K * e + gb + e * V + e * K * V / C + 8 * K * V / T_seq,
+        "fwd_h": e * K + e * V + r * K * e + kf_scan + e * V + e * K * V / C + 8 * K * V / T_seq,
         "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
-        # fused scan + output: w, u, k, kscale, q, g -> o, ht (h and v_new stay on chip)
-        "fwd_h_o": e * K + e * V + r * K * e + 4 + r * K * e + 4 + e * V + 8 * K * V / T_seq,
+        # fused scan + output: w, u, k, q, token factors -> o, ht (h and v_new stay on chip)
+        "fwd_h_o": e * K + e * V + r * K * e + r * K * e + kf_row + e * V + 8 * K * V / T_seq,
     }
 
 
