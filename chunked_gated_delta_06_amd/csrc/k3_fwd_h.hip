@@ -30,6 +30,8 @@
 //    kernel; e is written per-chunk transposed (v_new).
 //  * Consecutive workgroups of one head are mapped to one XCD so the shared
 //    w / k tiles are served from the same L2.
+#include <type_traits>
+
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -539,14 +541,18 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       constexpr int TPW = NB / NWO;              // token blocks per output wave (1 or 2)
       constexpr int NVB = BV / 16;               // value blocks of the workgroup
       static_assert(TPW >= 1 && TPW <= 2 && TPW * NWO == NB, "output-wave token split");
-      // wave-uniform in a scalar register: the causal-block conditions below
-      // then compile to scalar branches.  Under a lane mask the compiler may
-      // leave a one-MFMA block without a skip branch, and an MFMA does not
-      // honour the lane mask, so a masked-off wave would still accumulate.
-      const int ow = __builtin_amdgcn_readfirstlane(wv - NWC);
-      // token blocks {ow, NB - 1 - ow}: equal causal work for both waves
-      auto tbk = [&](int m) { return m == 0 ? ow : NB - 1 - ow; };
-      const int tbmax = tbk(TPW - 1);
+      // The wave index is a compile-time constant inside `run` (one
+      // instantiation per output wave, selected by a scalar branch): every
+      // causal-block condition below folds away, so the loops unroll without
+      // branches and LDS reads and independent MFMA chains interleave.  (A
+      // runtime condition would split the code into small blocks, and held in
+      // a vector register it would become a lane mask, which an MFMA ignores.)
+      auto run = [&](auto owc) {
+      constexpr int OW = decltype(owc)::value;
+      // token blocks {OW, NB - 1 - OW}: equal causal work for both waves
+      constexpr int TB0 = OW, TB1 = NB - 1 - OW;
+      auto tbk = [](int m) constexpr { return m == 0 ? TB0 : TB1; };
+      constexpr int tbmax = TPW == 1 ? TB0 : TB1;
       T* __restrict__ op = static_cast<T*>(a.o);
       // operands of one chunk's output, carried from its P^T step to its o step
       struct ORegs {
@@ -675,6 +681,12 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         }
         // the last chunk's o when the loop ended right after its step
         if (nsteps == nc) ophase(P, nc - 1);
+      }
+      };
+      if (__builtin_amdgcn_readfirstlane(wv - NWC) == 0) {
+        run(std::integral_constant<int, 0>{});
+      } else {
+        run(std::integral_constant<int, 1>{});
       }
     }
     return;
