@@ -109,7 +109,12 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   constexpr int NPQ = Cfg::NPQ, NPT = Cfg::NPT, NPH = Cfg::NPH, NPO = Cfg::NPO, NPE = Cfg::NPE;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::total];
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  // the body below runs with its wave index as a compile-time constant
+  // (with_wave_index): each wave's output-block slots and causal conditions
+  // fold, so the MFMA loops unroll without runtime branches
+  auto body = [&](auto wvc) {
+  constexpr int wv = decltype(wvc)::value;
+  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int64_t c = blockIdx.x, h = blockIdx.y;
   if (c >= a.chunk_off[a.N]) return;
   const int64_t t0 = a.chunk_idx[4 * c + 1];
@@ -646,6 +651,8 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   } else {
     finish(dq, dk);
   }
+  };
+  with_wave_index<NW>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), body);
 }
 
 // Four waves (one per SIMD): the kernel holds about 400 live registers per

@@ -16,6 +16,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace gdr {
@@ -329,6 +330,25 @@ constexpr int64_t kNumCUs = 256;
 // Workgroup index remap so that consecutive logical indices run on the same
 // XCD (MI355X dispatches workgroups to its 8 XCDs round-robin); blocks that
 // share input tiles then share an L2.
+// Calls f(std::integral_constant<int, w>{}) for the wave index w in [0, N)
+// (pass a scalar, e.g. __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)).
+// Each wave then runs a body in which its index is a compile-time constant:
+// per-wave block assignments and causal conditions fold away, so MFMA loops
+// unroll without branches.  Shared-memory arrays belong outside the body (a
+// __shared__ array declared in it would exist once per instantiation).
+template <int N, typename F>
+GDR_DEV void with_wave_index(int w, F&& f) {
+  if constexpr (N > 1) {
+    if (w == N - 1) {
+      f(std::integral_constant<int, N - 1>{});
+      return;
+    }
+    with_wave_index<N - 1>(w, f);
+  } else {
+    f(std::integral_constant<int, 0>{});
+  }
+}
+
 GDR_DEV int64_t xcd_remap(int64_t bid, int64_t nblk) {
   if (nblk % 8 != 0) return bid;
   return (bid % 8) * (nblk / 8) + bid / 8;
