@@ -902,10 +902,10 @@ bool fwd_h_o_supported(const Args& a) {
 }
 
 bool fwd_h_o_preferred(const Args& a) {
-  // with fewer 32-column tiles than compute units the scan runs one compute
-  // wave (16 columns) per workgroup, and the output waves would recompute a
-  // chunk's causal block for every 16 columns: the separate stages are faster
-  return fwd_h_o_supported(a) && a.N * a.HV * (a.V / 32) >= kNumCUs;
+  // measured faster than the separate scan and output stages on both grid
+  // shapes (one 16-column compute wave per workgroup on few long sequences:
+  // 1.78 vs 1.95 ms; two compute waves on 4 x 16 heads: 145 vs 222 us)
+  return fwd_h_o_supported(a);
 }
 
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s) {

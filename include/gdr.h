@@ -116,10 +116,9 @@ gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
- * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0, a
- * shape that gdr_fwd_h_o_supported accepts and at least one 32-column value
- * tile per compute unit (N * HV * V / 32 >= 256), K3 and K4 run as the one
- * fused stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
+ * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0 and a
+ * shape that gdr_fwd_h_o_supported accepts, K3 and K4 run as the one fused
+ * stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
  * untouched; gdr_chunk_fwd_fused(p) returns 1 exactly then.
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]

@@ -140,7 +140,7 @@ def test_fused_stage_support_and_host_rejections():
     fused = lambda **kw: L.gdr_chunk_fwd_fused(ctypes.byref(problem(**kw)))
     assert fused(B=4, N=4, HV=16, H=16, K=128, V=128) == 1     # 4 * 16 * 128 / 32 = 256 tiles
     assert fused(B=4, N=4, HV=16, H=16, K=128, V=128, keep_states=1) == 0
-    assert fused(B=1, N=1, HV=32, H=32, K=128, V=128) == 0     # 128 tiles: separate stages
+    assert fused(B=1, N=1, HV=32, H=32, K=128, V=128) == 1     # 16-column workgroups
     assert fused(B=4, N=4, HV=16, H=16, K=256, V=128) == 0
     P = ctypes.c_void_p
     args = [P(0x1000)] * 11
