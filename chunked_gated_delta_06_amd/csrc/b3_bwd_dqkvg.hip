@@ -70,6 +70,8 @@ struct B3 {
   static constexpr size_t oT = oK + (size_t)C * PK * EB;
   static constexpr size_t oLoop = oT + (size_t)C * PC * EB;
   static constexpr size_t FCV = (size_t)C * PV * 4;     // fp32 operand tile C x PV (hi + lo)
+  static_assert((size_t)VT * PC * (sizeof(T) == 2 ? 2 : 1) * sizeof(T) <= FCV, "dE^T (VT x PC) fits the dE slot");
+  static_assert(C % 4 == 0, "16-byte row-factor reads");
   static constexpr size_t FCC = (size_t)C * PC * 4;     // fp32 operand tile C x PC
   static constexpr size_t lH = 0;
   static constexpr size_t lDH = lH + (size_t)VT * PK * EB;
@@ -87,6 +89,7 @@ struct B3 {
   // rows: G, rq, rk, beta; per-wave dG, dbeta, q.dq, k.dk partials; 2 NW scalars
   static constexpr size_t rows_floats = 4 * C + 4 * NW * C + 2 * NW;
   static constexpr size_t total = oRows + rows_floats * 4;
+  static_assert(oRows % 16 == 0, "row factors start 16-byte aligned");
   static constexpr bool fits = total <= 160 * 1024;
 };
 
@@ -132,9 +135,13 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   T* sDO = reinterpret_cast<T*>(loop + Cfg::lDO);
   T* sV = reinterpret_cast<T*>(loop + Cfg::lV);
   T* sE = reinterpret_cast<T*>(loop + Cfg::lE);
-  const FTile<T> fDE = ftile<T, PV>(loop + Cfg::lDE, C);
+  // fp32 operand tiles (bf16 hi + lo in LDS), stored in the orientation that
+  // lets each lane write its accumulator's four consecutive elements as one
+  // 8-byte store: fDE holds dE^T [v][t], fP holds P [r][t], fD1 / fD2 hold the
+  // transposes of the D products' operands
+  const FTile<T> fDE = ftile<T, PC>(loop + Cfg::lDE, VT);
   const FTile<T> fY = ftile<T, PV>(loop + Cfg::lY, C);
-  const FTile<T> fPT = ftile<T, PC>(loop + Cfg::lPT, C);
+  const FTile<T> fP = ftile<T, PC>(loop + Cfg::lPT, C);
   const FTile<T> fD1 = ftile<T, PC>(loop + Cfg::pD1, C);
   const FTile<T> fD2 = ftile<T, PC>(loop + Cfg::pD2, C);
   T* sOq = reinterpret_cast<T*>(loop + Cfg::pOq);
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     lds_barrier();
     const float GL = sG[L - 1];
 
-    // ---- P^T tile: P^T[t][r] = P[r][t] (norms, gate, causal mask applied)
+    // ---- P tile, P[r][t] (norms, gate, causal mask applied)
 #pragma unroll
     for (int i = 0; i < SCC; ++i) {
       const int b = wv + NW * i, tb = b % NRB, cb = b / NRB;
@@ -302,12 +309,14 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
           mma(acc, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sQ[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
       }
       const int r = 16 * cb + r16;
+      f32x4 pv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * tb + 4 * g4 + e;
         const float f = (t <= r && r < L) ? sRq[r] * sRk[t] * __expf(sG[r] - sG[t]) : 0.f;
-        fPT.put(t, r, acc[e] * f);
+        pv[e] = acc[e] * f;
       }
+      fP.put4(r, 16 * tb + 4 * g4, pv);
     }
 
     f32x4 dQg[SCK], TdW[SCK], dKt[SCK], dP[SCC], dA[SCC];
@@ -337,17 +346,19 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
         for (int s = 0; s < KSC; ++s) {
           if (32 * s + 31 < 16 * tb) continue;
-          mma_split(a1, fPT.row(16 * tb + r16, 32 * s, lane), lds_col8(sDO, PV, 32 * s, 16 * vb, lane));
+          mma_split(a1, fP.col(32 * s, 16 * tb, lane), lds_col8(sDO, PV, 32 * s, 16 * vb, lane));
         }
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
           mma(a2, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sDH[(16 * vb + r16) * PK + 32 * ks + 8 * g4]));
+        f32x4 dv4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * tb + 4 * g4 + e;
           const float ks = (t < L) ? __expf(GL - sG[t]) * sRk[t] : 0.f;
-          fDE.put(t, 16 * vb + r16, scale * a1[e] + ks * a2[e]);
+          dv4[e] = scale * a1[e] + ks * a2[e];
         }
+        fDE.put4(16 * vb + r16, 16 * tb + 4 * g4, dv4);
       }
       lds_barrier();
 
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
         for (int s = 0; s < KSC; ++s) {
           if (32 * s + 31 < 16 * tb) continue;
-          mma_split(acc, fDE.col(32 * s, 16 * vb, lane), lds_col8(sT, PC, 32 * s, 16 * tb, lane));
+          mma_split(acc, fDE.row(16 * vb + r16, 32 * s, lane), lds_col8(sT, PC, 32 * s, 16 * tb, lane));
         }
         const int t = 16 * tb + r16, vc = 16 * vb + 4 * g4;
         if (t < L) st4(static_cast<T*>(a.dv) + ((t0 + t) * HV + j) * V + v0 + vc, acc * sB[t]);
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
         const bool ok = t <= r && r < L;
         const float dps = scale * dP[i][e];
         Dv[i][e] = ok ? dps * __expf(sG[r] - sG[t]) : 0.f;
-        const float pd = ok ? dps * fPT.get(t, r) : 0.f;
+        const float pd = ok ? dps * fP.get(r, t) : 0.f;
         const float rs = lanes_sum_t<16>(pd);
         if (r16 == 0) sRowG[wv * C + r] += rs;
         colsum += pd;
@@ -433,12 +444,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       const int b = wv + NW * i, cb = b / NRB;
       if (b >= NBC) continue;
       const int t = 16 * cb + r16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
-        fD1.put(r, t, Dv[i][e] * sRk[t]);
-        fD2.put(r, t, Dv[i][e] * sRq[r]);
-      }
+      const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sRq[16 * rb + 4 * g4]);
+      fD1.put4(t, 16 * rb + 4 * g4, Dv[i] * sRk[t]);
+      fD2.put4(t, 16 * rb + 4 * g4, Dv[i] * rq4);
     }
     {
       f32x4 qd = zero4(), kw = zero4(), kk = zero4();
@@ -490,9 +498,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int s = 0; s < KSC; ++s) {
         if (32 * s <= 16 * rb + 15)
-          mma_split(dq[i], fD1.row(16 * rb + r16, 32 * s, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+          mma_split(dq[i], fD1.col(32 * s, 16 * rb, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
         if (32 * s + 31 >= 16 * rb)
-          mma_split(dk[i], fD2.col(32 * s, 16 * rb, lane), lds_col8(sQ, PK, 32 * s, 16 * db, lane));
+          mma_split(dk[i], fD2.row(16 * rb + r16, 32 * s, lane), lds_col8(sQ, PK, 32 * s, 16 * db, lane));
       }
     }
     lds_barrier();
@@ -510,6 +518,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       }
       const int m = 16 * cb + r16;
       float colsum = 0.f;
+      f32x4 d1v, d2v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * rb + 4 * g4 + e;
@@ -526,9 +535,11 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
           sRowG[wv * C + t] += rg;
         }
         colsum += ad;
-        fD1.put(t, m, dkv * sRk[m]);
-        fD2.put(t, m, dkv * sRk[t]);
+        d1v[e] = dkv * sRk[m];
+        d2v[e] = dkv * sRk[t];
       }
+      fD1.put4(m, 16 * rb + 4 * g4, d1v);
+      fD2.put4(m, 16 * rb + 4 * g4, d2v);
       colsum = group4_sum(colsum);
       if (g4 == 0) sRowG[wv * C + m] -= colsum;
     }
@@ -542,9 +553,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int s = 0; s < KSC; ++s) {
         if (32 * s <= 16 * rb + 15)
-          mma_split(dk[i], fD1.row(16 * rb + r16, 32 * s, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+          mma_split(dk[i], fD1.col(32 * s, 16 * rb, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
         if (32 * s + 31 >= 16 * rb)
-          mma_split(dk[i], fD2.col(32 * s, 16 * rb, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
+          mma_split(dk[i], fD2.row(16 * rb + r16, 32 * s, lane), lds_col8(sK, PK, 32 * s, 16 * db, lane));
       }
     }
     if constexpr (GVA) {
