@@ -36,9 +36,14 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   constexpr int NB = C / 16;                 // 16-row blocks per chunk
   constexpr int KS = K / 32;                 // contraction slabs
   constexpr int NLB = NB * (NB + 1) / 2;     // lower-triangular blocks
-  constexpr int P = C + 1;                   // LDS pitch of the fp32 C x C matrix
   constexpr int GP = K + 1;                  // LDS pitch of the per-channel gate tile
-  __shared__ float sM[C * P];
+  // A, then T, in fp32: only the lower-triangular 16 x 16 blocks are ever
+  // touched, so they are stored packed (block (rb, cb <= rb) at index
+  // rb (rb + 1) / 2 + cb, rows of 17 floats), which keeps the workgroup's LDS
+  // small enough for more single-wave workgroups per CU
+  __shared__ float sM[NLB * 16 * 17];
+  // block (rb, cb) base; element (i, k) of a block at base + 17 i + k
+  auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * (16 * 17); };
   __shared__ float sG[C], sBeta[C], sRn[C];
   __shared__ float sGc[PC ? C * GP : 1];
 
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
             val = sBeta[r] * s[i] * sRn[r] * sRn[cc];
             if (!PC) val *= __expf(sG[r] - sG[cc]);
           }
-          sM[r * P + cc] = val;
+          sM[blk(rb, cb) + (4 * g4 + i) * 17 + r16] = val;
         }
       }
     lds_barrier();
@@ -211,19 +216,20 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
     // ---- diagonal 16x16 inverses by forward substitution (lane = column)
     float x[16];
     const int db = g4;
+    float* Md = sM + blk(db < NB ? db : 0, db < NB ? db : 0);
     if (db < NB) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float s = (r == r16) ? 1.f : 0.f;
 #pragma unroll
-        for (int q = 0; q < r; ++q) s -= sM[(16 * db + r) * P + 16 * db + q] * x[q];
+        for (int q = 0; q < r; ++q) s -= Md[r * 17 + q] * x[q];
         x[r] = s;
       }
     }
     lds_barrier();
     if (db < NB) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sM[(16 * db + r) * P + 16 * db + r16] = x[r];
+      for (int r = 0; r < 16; ++r) Md[r * 17 + r16] = x[r];
     }
     lds_barrier();
 
@@ -239,15 +245,15 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
           float av[4], bvv[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            av[s] = sM[(16 * ib + r16) * P + 16 * mb + 4 * g4 + s];
-            bvv[s] = sM[(16 * mb + 4 * g4 + s) * P + 16 * jb + r16];
+            av[s] = sM[blk(ib, mb) + r16 * 17 + 4 * g4 + s];
+            bvv[s] = sM[blk(mb, jb) + (4 * g4 + s) * 17 + r16];
           }
           mma16_f32(X, av, bvv);
         }
         float tv[4], xv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          tv[s] = sM[(16 * ib + r16) * P + 16 * ib + 4 * g4 + s];
+          tv[s] = sM[blk(ib, ib) + r16 * 17 + 4 * g4 + s];
           xv[s] = X[s];
         }
         f32x4 Y = zero4();
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
 #pragma unroll
       for (int jb = 0; jb < ib; ++jb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sM[(16 * ib + 4 * g4 + i) * P + 16 * jb + r16] = res[jb][i];
+        for (int i = 0; i < 4; ++i) sM[blk(ib, jb) + (4 * g4 + i) * 17 + r16] = res[jb][i];
       lds_barrier();
     }
 
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int cc = c8 + e;
-        x[e] = (r < L && cc <= r) ? sM[r * P + cc] : 0.f;
+        x[e] = (r < L && cc <= r) ? sM[blk(r >> 4, cc >> 4) + (r & 15) * 17 + (cc & 15)] : 0.f;
       }
       st8(dst + r * C + c8, Frag<T>::make(x));
     }
