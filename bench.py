@@ -80,7 +80,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
 def kernel_source_hash(stage):
     fname = {"kkt_solve": "k1_kkt_solve.hip", "wy": "k2_wy.hip", "fwd_h": "k3_fwd_h.hip",
              "fwd_o": "k4_fwd_o.hip", "fwd_h_o": "k3_fwd_h.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
-             "bwd_dqkvg": "b3_bwd_dqkvg.hip"}[stage]
+             "bwd_dqkvg": "b3_bwd_dqkvg.hip", "recurrent": "k5_recurrent.hip"}[stage]
     h = hashlib.sha256()
     for f in (fname, "gdr_device.h"):
         with open(os.path.join(ROOT, "chunked_gated_delta_06_amd", "csrc", f), "rb") as fh:
@@ -389,6 +389,66 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     return rec, inp
 
 
+def decode_bytes_per_token_head(w):
+    """Algorithmic HBM bytes per (token, value head) of the token-by-token
+    kernel over one decoding step (T tokens per sequence): q, k (shared by the
+    value heads of a group), v, g, beta and o per token, plus the fp32 state
+    read from h0 and written to ht once per sequence."""
+    e = 2 if w.dtype == "bf16" else 4
+    r = w.H / w.HV
+    gb = 4 * w.K if w.per_channel_gate else 4
+    return 2 * r * w.K * e + w.V * e + gb + 4 + w.V * e + 8 * w.K * w.V / w.T
+
+
+def measure_decode(gdr, w, steps, warmup):
+    """Time one decoding step of the token-by-token forward
+    (gdr_fused_recurrent_fwd) on workload ``w``; returns its JSON record."""
+    import torch
+    from oracle import recurrent
+    from oracle.metrics import err_ratio
+    dev = torch.device("cuda:0")
+    inp = workloads_inputs(w)
+    d = to_dev(inp, dev, ("q", "k", "v", "g", "beta", "h0", "cu_seqlens"))
+    kw = dict(scale=inp["scale"], cu_seqlens=d["cu_seqlens"], initial_state=d["h0"],
+              use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    o, ht = gdr.fused_recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], **kw)
+    torch.cuda.synchronize()
+    seqs = [0, 1, inp["N"] // 2, inp["N"] - 1]
+    ro, rht = recurrent.recurrent_fwd(inp["q"][seqs], inp["k"][seqs], inp["v"][seqs], inp["g"][seqs],
+                                      inp["beta"][seqs], scale=inp["scale"], h0=inp["h0"][seqs],
+                                      use_qk_l2norm=inp["use_qk_l2norm"])
+    tol = 5e-3 if w.dtype == "bf16" else 1e-4
+    parity = {"o (4 sequences, all heads)": err_ratio(o[seqs].cpu(), ro),
+              "ht (4 sequences, all heads)": err_ratio(ht[seqs].cpu(), rht), "tol": tol}
+    print(f"parity gate ({w.name}): " + ", ".join(f"{k}={v:.2e}" for k, v in parity.items()),
+          file=sys.stderr, flush=True)
+    if not all(v <= tol for k, v in parity.items() if k != "tol"):
+        print("parity check failed: refusing to report throughput", file=sys.stderr)
+        sys.exit(1)
+    L = gdr.lib()
+    p = gdr.make_problem(d["q"], d["v"], d["g"], cu_seqlens=d["cu_seqlens"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream(dev)
+    args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["cu_seqlens"]),
+            P(d["h0"]), P(o), P(ht), ctypes.c_void_p(stream.cuda_stream))
+
+    def step():
+        st = L.gdr_fused_recurrent_fwd(*args)
+        if st != 0:
+            raise RuntimeError(L.gdr_status_string(st).decode())
+
+    ms_per_step = wall_ms_per_step(step, warmup, steps)
+    ev_ms = event_stage_ms(stream, {"recurrent": step}, max(5, min(steps, 50)))
+    tokens = inp["B"] * inp["T"]
+    units = tokens * w.HV
+    per_unit = {"recurrent": decode_bytes_per_token_head(w)}
+    rec = {"value": tokens / (ms_per_step * 1e-3), "ms_per_step": ms_per_step, "tokens": tokens,
+           "stage_ms": {"forward": ev_ms}, "parity": parity,
+           "roofline": roofline(per_unit, ev_ms, units, w.name, ["recurrent"])}
+    return rec, inp
+
+
 def workloads_inputs(w):
     import workloads
     return workloads.make_inputs(w)
@@ -429,7 +489,10 @@ def main():
     import workloads
 
     w = workloads.CONFIGS[args.workload]
-    rec, inp = measure(gdr, w, args.steps, args.warmup, args.breakdown, w.name)
+    if w.T == 1:
+        rec, inp = measure_decode(gdr, w, args.steps, args.warmup)
+    else:
+        rec, inp = measure(gdr, w, args.steps, args.warmup, args.breakdown, w.name)
     line = {
         "metric": "tokens/sec and % HBM/MFMA roofline, chunk GDN fwd (+bwd) on 1 MI355X",
         "value": rec["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -437,7 +500,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, logsigmoid gates, sigmoid beta)",
         "config": {"workload": w.name, "B": inp["B"], "T": inp["T"], "H": w.H, "HV": w.HV, "K": w.K,
                    "V": w.V, "chunk_size": w.chunk_size,
-                   "pass": "forward+backward" if w.backward else "forward",
+                   "pass": ("forward+backward" if w.backward else
+                            "token-by-token forward (one decoding step)" if w.T == 1 else "forward"),
                    "gate": "per-channel" if w.per_channel_gate else "scalar",
                    "l2norm_in_kernel": w.l2norm_in_kernel, "parallelism": "single GPU"},
     }
@@ -456,6 +520,14 @@ def main():
                             **{k: v for k, v in brec.items() if k not in ("value", "ms_per_step")}}
         if not args.no_cpu_baseline:
             line["backward"]["cpu_baseline"] = cpu_baseline_bwd(wb, binp)
+        del binp
+        torch.cuda.empty_cache()
+        wd = workloads.CONFIGS["decode_gva_bf16"]
+        drec, dinp = measure_decode(gdr, wd, args.steps, args.warmup)
+        line["decode"] = {"workload": wd.name, "pass": "token-by-token forward (one decoding step)",
+                          "B": dinp["B"], "T": dinp["T"], "H": wd.H, "HV": wd.HV, "K": wd.K, "V": wd.V,
+                          "tokens_per_s": drec["value"], "ms_per_step": drec["ms_per_step"],
+                          **{k: v for k, v in drec.items() if k not in ("value", "ms_per_step")}}
     print(json.dumps(line))
 
 

@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_chunk_fwd_fused.argtypes = [PP]
         L.gdr_chunk_fwd_fused.restype = ctypes.c_int
         L.gdr_fwd_h_o.argtypes = [PP] + [_P] * 11 + [_P]
+        L.gdr_fused_recurrent_fwd.argtypes = [PP] + [_P] * 9 + [_P]
         L.gdr_bwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_bwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrBwdLayout)]
         L.gdr_chunk_bwd.argtypes = [PP] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
                      "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
+                     "gdr_fused_recurrent_fwd",
                      "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
                      "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
@@ -308,6 +310,42 @@ def fwd_h_o(p, q, k, w, u, g, kscale, chunk_idx, chunk_off, h0, o, ht):
     _raise(lib().gdr_fwd_h_o(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(kscale),
                              _ptr(chunk_idx), _ptr(chunk_off), _ptr(h0), _ptr(o), _ptr(ht),
                              _stream(q.device)))
+
+
+def fused_recurrent_fwd(q, k, v, g, beta, *, scale: float = 1.0, cu_seqlens=None, initial_state=None,
+                        output_final_state: bool = True, use_qk_l2norm_in_kernel: bool = False,
+                        out=None, validate_cu: bool = True):
+    """Token-by-token forward of the same operator (gdr_fused_recurrent_fwd):
+    no chunk table and no workspace, for decoding and short sequences.
+    Returns (o, ht) (ht None when not requested); ``out=(o, ht)`` supplies the
+    output tensors."""
+    _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    p = make_problem(q, v, g, chunk_size=64, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+    check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
+    if out is not None:
+        o, ht = out
+        _need_gpu(o, ht)
+        _expect("o", o, v.shape)
+        _expect("ht", ht, (p.N, p.HV, p.K, p.V))
+        if o.dtype != q.dtype or (ht is not None and ht.dtype != torch.float32):
+            raise ValueError("o must match q's dtype and ht must be float32")
+    else:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+        ht = (torch.empty(p.N, p.HV, p.K, p.V, dtype=torch.float32, device=q.device)
+              if output_final_state else None)
+    st = lib().gdr_fused_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
+                                       _stream(q.device))
+    _raise(st)
+    return o, ht
 
 
 # ---- backward

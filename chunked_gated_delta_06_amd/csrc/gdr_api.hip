@@ -16,7 +16,7 @@ bool bwd_shape_ok(const gdr_problem& p) {
 
 int64_t nt_max(const gdr_problem& p) {
   const int64_t C = p.chunk_size;
-  if (p.T <= 0) return 0;
+  if (p.T <= 0 || C <= 0) return 0;
   if (p.N == p.B && p.B > 1) return p.B * ((p.T + C - 1) / C);
   // dense B = 1 and varlen use the same bound; for a single dense row it is exact
   return (p.N == 1) ? (p.T + C - 1) / C : p.T / C + p.N;
@@ -36,24 +36,33 @@ size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t elem_size(const gdr_problem& p) { return p.dtype == GDR_BF16 ? 2 : 4; }
 
-gdr_status check(const gdr_problem* p, bool varlen) {
+// Checks shared by the chunked and the token-by-token paths (chunk_size is
+// not read here).
+gdr_status check_dims(const gdr_problem* p, bool varlen) {
   if (p == nullptr) return GDR_ERR_NULL_ARG;
-  if (p->chunk_size != 32 && p->chunk_size != 64) return GDR_ERR_CHUNK_SIZE;
   if (p->dtype != GDR_BF16 && p->dtype != GDR_FP32) return GDR_ERR_DTYPE;
   if (p->N < 1) return varlen ? GDR_ERR_VARLEN : GDR_ERR_SHAPE;
   if (p->B < 1 || p->T < 0 || p->H < 1 || p->HV < 1) return GDR_ERR_SHAPE;
   if (p->HV % p->H != 0) return GDR_ERR_SHAPE;
   if (!head_dim_ok(p->K) || !head_dim_ok(p->V)) return GDR_ERR_SHAPE;
   if (!std::isfinite(p->scale)) return GDR_ERR_SHAPE;
-  // fp32 with a per-channel gate at K = 256, chunk 64 does not fit one workgroup's LDS
-  if (p->dtype == GDR_FP32 && p->gate_per_channel && p->K == 256 && p->chunk_size == 64) return GDR_ERR_SHAPE;
-  // token indices are int32 in the chunk table
-  if (p->B * p->T >= (int64_t(1) << 31)) return GDR_ERR_SHAPE;
   if (varlen) {
     if (p->B != 1) return GDR_ERR_VARLEN;
   } else if (p->N != p->B) {
     return GDR_ERR_VARLEN;
   }
+  return GDR_OK;
+}
+
+gdr_status check(const gdr_problem* p, bool varlen) {
+  if (p == nullptr) return GDR_ERR_NULL_ARG;
+  if (p->chunk_size != 32 && p->chunk_size != 64) return GDR_ERR_CHUNK_SIZE;
+  const gdr_status st = check_dims(p, varlen);
+  if (st != GDR_OK) return st;
+  // fp32 with a per-channel gate at K = 256, chunk 64 does not fit one workgroup's LDS
+  if (p->dtype == GDR_FP32 && p->gate_per_channel && p->K == 256 && p->chunk_size == 64) return GDR_ERR_SHAPE;
+  // token indices are int32 in the chunk table
+  if (p->B * p->T >= (int64_t(1) << 31)) return GDR_ERR_SHAPE;
   return GDR_OK;
 }
 
@@ -361,6 +370,30 @@ gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const v
   return hip_status(gdr::launch_fwd_o(a, static_cast<hipStream_t>(stream)));
 }
 
+
+gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* h0, void* o, float* ht, void* stream) {
+  const gdr_status st = check_dims(p, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  if (p->T > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  if (p->T == 0 && ht == nullptr) return GDR_OK;
+  Args a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.o = o;
+  a.ht = ht;
+  return hip_status(gdr::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
 
 gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* out) {
   if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;

@@ -65,6 +65,8 @@ bool fwd_h_o_supported(const Args& a);
 bool fwd_h_o_preferred(const Args& a);   // the full forward's choice
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
+// token-by-token forward (no chunk table, no workspace)
+hipError_t launch_recurrent(const Args& a, hipStream_t s);
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dqkvg(const Args& a, hipStream_t s);

@@ -189,6 +189,28 @@ gdr_status gdr_fwd_h_o(const gdr_problem* p, const void* q, const void* k, const
                        const int32_t* chunk_idx, const int32_t* chunk_off, const float* h0,
                        void* o, float* ht, void* stream);
 
+/* Token-by-token ("fused recurrent") forward of the same operator: the
+ * recurrence at the top of this header applied one token at a time with the
+ * state in registers, the per-token form that the chunk form of the
+ * coverage-matrix page (section 2) reorganises; that page's coverage matrix
+ * (section 3) tests such a fused_recurrent entry point beside the chunked one.
+ * It needs no chunk table and no workspace, which suits decoding (T of one or a
+ * few tokens per sequence, the state handed over through h0 / ht) and short
+ * sequences.  Same problem description, layouts and pointer rules as
+ * gdr_chunk_fwd; chunk_size and keep_states are not read, and the chunked
+ * path's int32 token limit (B*T < 2^31) does not apply.
+ *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
+ *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
+ *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
+ *   h0    f32 [N,HV,K,V] or NULL (zeros)
+ *   o     dtype [B,T,HV,V] (output)
+ *   ht    f32 [N,HV,K,V] (output) or NULL
+ * State and arithmetic are fp32; o is rounded to the input dtype.  Errors as
+ * gdr_chunk_fwd (never GDR_ERR_CHUNK_SIZE or GDR_ERR_WORKSPACE). */
+gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* h0, void* o, float* ht, void* stream);
+
 /* ------------------------------------------------------------------ backward
  *
  * Gradients of L = sum(o * d_o) + sum(ht * dht) with respect to q, k, v, g,

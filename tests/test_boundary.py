@@ -230,3 +230,34 @@ def test_bwd_wrapper_refuses_cpu_tensors():
     g = torch.zeros(1, 64, 1)
     with pytest.raises(ValueError, match="GPU"):
         gdr.chunk_bwd(x, x, x, g, g, x)
+
+
+def test_fused_recurrent_rejects_before_launch():
+    """The token-by-token forward: host-side errors, and chunk_size is not read
+    (no call here reaches a launch)."""
+    L = gdr.lib()
+    P = ctypes.c_void_p
+    A = P(0x1000)
+    p = problem()
+    # null q
+    assert L.gdr_fused_recurrent_fwd(ctypes.byref(p), None, A, A, A, A, None, None, A, None, None) == 1
+    # misaligned v
+    assert L.gdr_fused_recurrent_fwd(ctypes.byref(p), A, A, P(0x1004), A, A, None, None, A, None, None) == 6
+    # cu_seqlens with B != 1
+    assert L.gdr_fused_recurrent_fwd(ctypes.byref(p), A, A, A, A, A, A, None, A, None, None) == 4
+    # shapes and dtype
+    for kw, st in ((dict(HV=3), 3), (dict(K=96), 3), (dict(dtype=7), 5), (dict(N=3), 4)):
+        assert L.gdr_fused_recurrent_fwd(ctypes.byref(problem(**kw)), A, A, A, A, A, None, None, A,
+                                         None, None) == st, kw
+    # an empty batch without a final state launches nothing; chunk_size is not read
+    for cs in (0, 16, 64):
+        assert L.gdr_fused_recurrent_fwd(ctypes.byref(problem(T=0, chunk_size=cs)), None, None, None,
+                                         None, None, None, None, None, None, None) == 0
+
+
+def test_fused_recurrent_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
+    g = torch.zeros(1, 8, 1)
+    with pytest.raises(ValueError, match="GPU"):
+        gdr.fused_recurrent_fwd(x, x, x, g, g)
