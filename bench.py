@@ -52,6 +52,8 @@ def stage_bytes_per_token_head(w, T_seq):
         "wy": r * K * e + V * e + e * C + gb + 4 + e * K + e * V,
         "fwd_h": e * K + e * V + r * K * e + kf_scan + e * V + e * K * V / C + 8 * K * V / T_seq,
         "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
+        # fused K1 + K2: k, v, g, beta -> w, u, token factors (Tm stays on chip)
+        "kkt_wy": r * K * e + V * e + gb + 4 + e * K + e * V + kf_row,
         # fused scan + output: w, u, k, q, token factors -> o, ht (h and v_new stay on chip)
         "fwd_h_o": e * K + e * V + r * K * e + r * K * e + kf_row + e * V + 8 * K * V / T_seq,
     }
@@ -79,7 +81,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
 
 def kernel_source_hash(stage):
     fname = {"kkt_solve": "k1_kkt_solve.hip", "wy": "k2_wy.hip", "fwd_h": "k3_fwd_h.hip",
-             "fwd_o": "k4_fwd_o.hip", "fwd_h_o": "k3_fwd_h.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
+             "fwd_o": "k4_fwd_o.hip", "fwd_h_o": "k3_fwd_h.hip", "kkt_wy": "k12_kkt_wy.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
              "bwd_dqkvg": "b3_bwd_dqkvg.hip", "recurrent": "k5_recurrent.hip"}[stage]
     h = hashlib.sha256()
     for f in (fname, "gdr_device.h"):
@@ -340,10 +342,16 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         "fwd_h_o": lambda: gdr.fwd_h_o(p, d["q"], d["k"], views["w"], views["u"], d["g"], views["kscale"],
                                        cidx, coff, d["h0"], o, ht),
     }
-    # the stages the timed step runs: the fused scan + output where the shape has it
+    if not w.per_channel_gate:
+        fstages["kkt_wy"] = lambda: gdr.fwd_kkt_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff,
+                                                   views["w"], views["u"], views["kscale"])
+    # the stages the timed step runs: the fused K1 + K2 and scan + output
+    # stages where the shape has them
     fused = gdr.chunk_fwd_fused(p)
-    for name in (("fwd_h", "fwd_o") if fused else ("fwd_h_o",)):
-        del fstages[name]
+    for name in (("kkt_solve", "wy", "fwd_h", "fwd_o") if fused else ("kkt_wy", "fwd_h_o")):
+        fstages.pop(name, None)
+    fstages = {n: fstages[n] for n in ("chunk_table", "kkt_solve", "wy", "kkt_wy", "fwd_h", "fwd_o", "fwd_h_o")
+               if n in fstages}
     reps = max(5, min(steps, 50))
     fwd_ms = event_stage_ms(stream, fstages, reps)
     T_seq = inp["B"] * inp["T"] / inp["N"]

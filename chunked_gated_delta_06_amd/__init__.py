@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_chunk_table.argtypes = [PP, _P, _P, _P, _P]
         L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 7 + [_P]
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
+        L.gdr_fwd_kkt_wy.argtypes = [PP] + [_P] * 9 + [_P]
         L.gdr_fwd_h.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fwd_o.argtypes = [PP] + [_P] * 8 + [_P]
         L.gdr_fwd_h_o_supported.argtypes = [PP]
@@ -101,7 +102,7 @@ def lib() -> ctypes.CDLL:
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
                      "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
-                     "gdr_fused_recurrent_fwd",
+                     "gdr_fused_recurrent_fwd", "gdr_fwd_kkt_wy",
                      "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
                      "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
@@ -284,6 +285,12 @@ def fwd_kkt_solve(p, k, g, beta, chunk_idx, chunk_off, Tm, kscale=None):
 def fwd_wy(p, k, v, g, beta, chunk_idx, chunk_off, Tm, w, u):
     _raise(lib().gdr_fwd_wy(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(chunk_idx),
                             _ptr(chunk_off), _ptr(Tm), _ptr(w), _ptr(u), _stream(k.device)))
+
+
+def fwd_kkt_wy(p, k, v, g, beta, chunk_idx, chunk_off, w, u, kscale):
+    """K1 + K2 fused (scalar gate): w, u and kscale without writing Tm."""
+    _raise(lib().gdr_fwd_kkt_wy(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(chunk_idx),
+                                _ptr(chunk_off), _ptr(w), _ptr(u), _ptr(kscale), _stream(k.device)))
 
 
 def fwd_h(p, k, w, u, g, chunk_idx, chunk_off, h0, h, v_new, ht, kscale=None):

@@ -226,12 +226,14 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   a.ht = ht;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = gdr::launch_chunk_table(a, s);
-  if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-  if (e == hipSuccess) e = gdr::launch_wy(a, s);
   if (!p->keep_states && gdr::fwd_h_o_preferred(a)) {
-    // fused scan + output: h and v_new never leave the chip
+    // fused K1 + K2 (Tm stays on chip) and fused scan + output (h and v_new
+    // stay on chip)
+    if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
   } else {
+    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    if (e == hipSuccess) e = gdr::launch_wy(a, s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
     if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
   }
@@ -297,6 +299,25 @@ gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const 
   a.w = w;
   a.u = u;
   return hip_status(gdr::launch_wy(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_fwd_kkt_wy(const gdr_problem* p, const void* k, const void* v, const float* g, const float* beta,
+                          const int32_t* chunk_idx, const int32_t* chunk_off, void* w, void* u, float* kscale,
+                          void* stream) {
+  gdr_status st = stage_common(p, {k, v, g, beta, chunk_idx, chunk_off, w, u, kscale});
+  if (st != GDR_OK) return st;
+  if (p->gate_per_channel) return GDR_ERR_UNSUPPORTED;
+  Args a = make_args(*p);
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.chunk_idx = const_cast<int32_t*>(chunk_idx);
+  a.chunk_off = const_cast<int32_t*>(chunk_off);
+  a.w = w;
+  a.u = u;
+  a.kscale = kscale;
+  return hip_status(gdr::launch_kkt_wy(a, static_cast<hipStream_t>(stream)));
 }
 
 gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u, const float* g,

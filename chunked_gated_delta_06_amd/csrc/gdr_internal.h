@@ -58,6 +58,8 @@ int64_t nt_max(const gdr_problem& p);
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_kkt_solve(const Args& a, hipStream_t s);
 hipError_t launch_wy(const Args& a, hipStream_t s);
+// K1 + K2 fused (scalar gate; w, u and kscale, no Tm)
+hipError_t launch_kkt_wy(const Args& a, hipStream_t s);
 hipError_t launch_fwd_h(const Args& a, hipStream_t s);
 // fused state scan + output (no h / v_new); fwd_h_o_supported says whether the
 // shape has an instantiation (scalar gate, staged tiles fit in LDS)

@@ -117,9 +117,10 @@ gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
  * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0 and a
- * shape that gdr_fwd_h_o_supported accepts, K3 and K4 run as the one fused
- * stage gdr_fwd_h_o and the h / v_new regions of the workspace are left
- * untouched; gdr_chunk_fwd_fused(p) returns 1 exactly then.
+ * shape that gdr_fwd_h_o_supported accepts, K1 and K2 run as the one fused
+ * stage gdr_fwd_kkt_wy and K3 and K4 as the one fused stage gdr_fwd_h_o, and
+ * the Tm, h and v_new regions of the workspace are left untouched;
+ * gdr_chunk_fwd_fused(p) returns 1 exactly then.
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
@@ -157,6 +158,15 @@ gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g
 gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const float* g,
                       const float* beta, const int32_t* chunk_idx, const int32_t* chunk_off,
                       const void* Tm, void* w, void* u, void* stream);
+
+/* K1 + K2 fused (scalar gate): the results of gdr_fwd_kkt_solve and gdr_fwd_wy
+ * (w, u and kscale, same layouts) in one pass per chunk and value head, with
+ * (I + A)^-1 kept on chip and not written.  gdr_chunk_fwd runs it in place of
+ * the two stages whenever it runs the fused scan + output stage.  Returns
+ * GDR_ERR_UNSUPPORTED for a per-channel gate. */
+gdr_status gdr_fwd_kkt_wy(const gdr_problem* p, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* chunk_idx, const int32_t* chunk_off,
+                          void* w, void* u, float* kscale, void* stream);
 
 /* K3: state scan.  For each sequence, value head and chunk in order: h = S (the
  * state entering the chunk, as on the KCP page, section "h and dh cross-rank

@@ -139,9 +139,51 @@ def test_fused_stage_against_separate_stages(cfg):
     assert err_ratio(f64(o_f), f64(o_sep)) <= tol / 4
 
 
+KKT_WY_CASES = [
+    dict(dtype="bf16", K=128, V=128, C=64),
+    dict(dtype="bf16", K=256, V=64, C=64, H=1, HV=2),
+    dict(dtype="bf16", K=64, V=256, C=32, H=1, HV=4),
+    dict(dtype="bf16", K=32, V=32, C=32, l2=False, host_l2=True),
+    dict(dtype="fp32", K=32, V=64, C=64),
+    dict(dtype="fp32", K=128, V=128, C=32),
+    dict(dtype="fp32", K=256, V=32, C=64, H=1, HV=1),
+]
+
+
+@pytest.mark.parametrize("cfg", KKT_WY_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_fused_kkt_wy_against_oracle(cfg):
+    """gdr_fwd_kkt_wy (K1 + K2 in one kernel, Tm kept on chip) on a ragged
+    dense GVA batch: w, u against the oracle's per-chunk W and U, the token
+    factors against the separate K1's, and it leaves Tm's region alone."""
+    w, inp = mk(T=150, slow=True, **cfg)
+    tol = TOL[w.dtype]
+    o_sep, ht_sep, ws = gpu_fwd(inp, keep_states=True)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=inp["chunk_size"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    ro, rht, it = oracle_fwd(inp, intermediates=True)
+    NT = int(it["off"][-1])
+    wf = torch.full_like(ws["w"], float("nan"))
+    uf = torch.full_like(ws["u"], float("nan"))
+    kf = torch.full_like(ws["kscale"], float("nan"))
+    tm_before = ws["Tm"].clone()
+    gdr.fwd_kkt_wy(p, dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]), ws["chunk_idx"],
+                   ws["chunk_off"], wf, uf, kf)
+    torch.cuda.synchronize()
+    assert torch.equal(ws["Tm"], tm_before)
+    check("w", f64(wf[:NT]), it["W"], tol)
+    check("u", f64(uf[:NT]).transpose(0, 1, 3, 2), it["U"], tol)
+    assert err_ratio(f64(wf[:NT]), f64(ws["w"][:NT])) <= tol
+    assert not torch.isnan(kf[:NT]).any()
+    np.testing.assert_allclose(f64(kf[:NT]), f64(ws["kscale"][:NT]), rtol=1e-5, atol=1e-6)
+    # the fused stages end to end (the default forward) against the oracle
+    o, ht, _ = gpu_fwd(inp)
+    check("o", f64(o), ro, tol)
+    check("ht", f64(ht), rht, tol)
+
+
 def test_fused_default_leaves_states_untouched():
-    """Without keep_states the forward takes the fused stage: o / ht match the
-    oracle and the h / v_new regions of the workspace keep their fill."""
+    """Without keep_states the forward takes the fused stages: o / ht match the
+    oracle and the Tm, h and v_new regions of the workspace keep their fill."""
     w, inp = mk(B=2, T=170, H=8, HV=32, K=128, V=128, slow=True)
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
     assert gdr.chunk_fwd_fused(p)
@@ -152,6 +194,7 @@ def test_fused_default_leaves_states_untouched():
     check("o", f64(o), ro, TOL["bf16"])
     check("ht", f64(ht), rht, TOL["bf16"])
     assert (ws[lay.h:lay.v_new] == 0x5A).all() and (ws[lay.v_new:lay.kscale] == 0x5A).all()
+    assert (ws[lay.Tm:lay.w] == 0x5A).all()
 
 
 # ------------------------------------------------------------------ sweep
