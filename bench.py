@@ -457,6 +457,74 @@ def measure_decode(gdr, w, steps, warmup):
     return rec, inp
 
 
+def measure_segmented(gdr, w, R, steps, warmup):
+    """The long sequence of ``w`` split into R equal segments and run as the
+    single-device segment hand-off (gdr_chunk_fwd_segmented: local end states
+    and transitions, merge, re-run), beside the single pass over the whole
+    sequence (gdr_chunk_fwd).  Parity: o and ht against the single pass, and o
+    on the first 2048 tokens of two heads against the chunked oracle."""
+    import torch
+    from oracle import chunked
+    from oracle.metrics import err_ratio
+    dev = torch.device("cuda:0")
+    inp = workloads_inputs(w)
+    T = inp["T"]
+    cu = torch.arange(0, T + 1, T // R, dtype=torch.int32)
+    d = to_dev(inp, dev, ("q", "k", "v", "g", "beta", "h0"))
+    d["cu"] = cu.to(dev)
+    o, ht, states, _ = gdr.chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
+                                               scale=inp["scale"], chunk_size=inp["chunk_size"],
+                                               initial_state=d["h0"],
+                                               use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    o1, ht1, ws1 = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp["scale"],
+                                 chunk_size=inp["chunk_size"], initial_state=d["h0"],
+                                 use_qk_l2norm_in_kernel=inp["use_qk_l2norm"], return_workspace=True)
+    torch.cuda.synchronize()
+    hs = [0, w.HV // 2]
+    sub = {n: inp[n][:, :2048][:, :, hs].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    ro, _ = chunked.chunked_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale=inp["scale"],
+                                h0=inp["h0"][:, hs], use_qk_l2norm=inp["use_qk_l2norm"],
+                                chunk_size=inp["chunk_size"])
+    tol = 5e-3 if w.dtype == "bf16" else 1e-4
+    parity = {"o vs single pass": err_ratio(o.cpu(), o1.cpu()), "ht vs single pass": err_ratio(ht.cpu(), ht1.cpu()),
+              "o (first 2048 tokens, 2 heads) vs oracle": err_ratio(o[:, :2048][:, :, hs].cpu(), ro), "tol": tol}
+    print(f"parity gate ({w.name}, {R} segments): " + ", ".join(f"{k}={v:.2e}" for k, v in parity.items()),
+          file=sys.stderr, flush=True)
+    if not all(v <= tol for k, v in parity.items() if k != "tol"):
+        print("parity check failed: refusing to report throughput", file=sys.stderr)
+        sys.exit(1)
+    L = gdr.lib()
+    p = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    lay = gdr.seg_layout(p)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["cu"]), P(d["h0"]),
+            P(o), P(ht), P(states), None, P(ws), ctypes.c_size_t(ws.numel()), sp)
+    p1 = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"],
+                          use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    args1 = (ctypes.byref(p1), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), None, P(d["h0"]),
+             P(o1), P(ht1), P(ws1), ctypes.c_size_t(ws1.numel()), sp)
+
+    def seg_step():
+        st = L.gdr_chunk_fwd_segmented(*args)
+        if st != 0:
+            raise RuntimeError(L.gdr_status_string(st).decode())
+
+    def one_step():
+        st = L.gdr_chunk_fwd(*args1)
+        if st != 0:
+            raise RuntimeError(L.gdr_status_string(st).decode())
+
+    ms = wall_ms_per_step(seg_step, warmup, steps)
+    ms1 = wall_ms_per_step(one_step, warmup, steps)
+    return {"workload": w.name, "pass": f"forward, one sequence as {R} segments (segment hand-off on one GPU)",
+            "B": 1, "T": T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V, "chunk_size": w.chunk_size, "segments": R,
+            "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "single_pass_ms_per_step": ms1,
+            "parity": parity}
+
+
 def workloads_inputs(w):
     import workloads
     return workloads.make_inputs(w)
@@ -529,6 +597,8 @@ def main():
         if not args.no_cpu_baseline:
             line["backward"]["cpu_baseline"] = cpu_baseline_bwd(wb, binp)
         del binp
+        torch.cuda.empty_cache()
+        line["segmented"] = measure_segmented(gdr, wb, 8, max(3, args.steps // 5), max(2, args.warmup // 5))
         torch.cuda.empty_cache()
         wd = workloads.CONFIGS["decode_gva_bf16"]
         drec, dinp = measure_decode(gdr, wd, args.steps, args.warmup)

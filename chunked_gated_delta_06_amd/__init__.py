@@ -55,6 +55,12 @@ class GdrBwdLayout(ctypes.Structure):
                 ("dh", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
+class GdrSegLayout(ctypes.Structure):
+    _fields_ = [("fwd", GdrFwdLayout), ("u_zero", ctypes.c_size_t), ("h_tr", ctypes.c_size_t),
+                ("v_tr", ctypes.c_size_t), ("eye", ctypes.c_size_t), ("s_ext", ctypes.c_size_t),
+                ("trans", ctypes.c_size_t), ("s_in", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
@@ -93,6 +99,9 @@ def lib() -> ctypes.CDLL:
         L.gdr_chunk_fwd_fused.restype = ctypes.c_int
         L.gdr_fwd_h_o.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fused_recurrent_fwd.argtypes = [PP] + [_P] * 9 + [_P]
+        L.gdr_segmented_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
+        L.gdr_segmented_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrSegLayout)]
+        L.gdr_chunk_fwd_segmented.argtypes = [PP] + [_P] * 11 + [_P, ctypes.c_size_t, _P]
         L.gdr_bwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_bwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrBwdLayout)]
         L.gdr_chunk_bwd.argtypes = [PP] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
@@ -102,7 +111,8 @@ def lib() -> ctypes.CDLL:
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
                      "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
-                     "gdr_fused_recurrent_fwd", "gdr_fwd_kkt_wy",
+                     "gdr_fused_recurrent_fwd", "gdr_fwd_kkt_wy", "gdr_segmented_workspace_bytes",
+                     "gdr_segmented_workspace_layout", "gdr_chunk_fwd_segmented",
                      "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
                      "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
@@ -353,6 +363,49 @@ def fused_recurrent_fwd(q, k, v, g, beta, *, scale: float = 1.0, cu_seqlens=None
                                        _stream(q.device))
     _raise(st)
     return o, ht
+
+
+def seg_layout(p: GdrProblem) -> GdrSegLayout:
+    lay = GdrSegLayout()
+    _raise(lib().gdr_segmented_workspace_layout(ctypes.byref(p), ctypes.byref(lay)))
+    return lay
+
+
+def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, *, scale: float = 1.0, chunk_size: int = 64,
+                        initial_state=None, use_qk_l2norm_in_kernel: bool = False,
+                        want_transitions: bool = False, validate_cu: bool = True):
+    """Forward of ONE sequence (q, k [1,T,H,K] ...) split into the segments
+    ``cu_seqlens`` bounds, run as the context-parallel scheme on one device
+    (gdr_chunk_fwd_segmented): every segment's local end state and transition,
+    the merge of the entering states, a re-run of every segment.  Returns
+    (o, ht, seg_states [N+1,HV,K,V], transitions [N,HV,K,K] or None);
+    ``initial_state`` is the sequence's [1,HV,K,V] initial state."""
+    _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is None or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens (int32 segment bounds) is required")
+    p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+    lay = seg_layout(p)
+    check_tensors(p, q, k, v, g, beta, cu_seqlens, None, validate_cu)
+    _expect("initial_state", initial_state, (1, p.HV, p.K, p.V))
+    dev = q.device
+    o = torch.empty(v.shape, dtype=q.dtype, device=dev)
+    ht = torch.empty(1, p.HV, p.K, p.V, dtype=torch.float32, device=dev)
+    states = torch.empty(p.N + 1, p.HV, p.K, p.V, dtype=torch.float32, device=dev)
+    trans = (torch.empty(p.N, p.HV, p.K, p.K, dtype=torch.float32, device=dev)
+             if want_transitions else None)
+    ws = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=dev)
+    st = lib().gdr_chunk_fwd_segmented(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
+                                       _ptr(states), _ptr(trans), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                       _stream(dev))
+    _raise(st)
+    return o, ht, states, trans
 
 
 # ---- backward

@@ -131,6 +131,31 @@ gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
   return l;
 }
 
+gdr_seg_layout seg_layout_of(const gdr_problem& p) {
+  gdr_seg_layout l;
+  l.fwd = layout_of(p);
+  const int64_t nt = l.fwd.nt_max;
+  const size_t es = elem_size(p);
+  const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V, N = (size_t)p.N;
+  size_t off = l.fwd.total;
+  l.u_zero = off;
+  off = round_up(off + (size_t)nt * HV * K * C * es);
+  l.h_tr = off;
+  off = round_up(off + (size_t)nt * HV * K * K * es);
+  l.v_tr = off;
+  off = round_up(off + (size_t)nt * HV * K * C * es);
+  l.eye = off;
+  off = round_up(off + N * HV * K * K * sizeof(float));
+  l.s_ext = off;
+  off = round_up(off + N * HV * K * V * sizeof(float));
+  l.trans = off;
+  off = round_up(off + N * HV * K * K * sizeof(float));
+  l.s_in = off;
+  off = round_up(off + (N + 1) * HV * K * V * sizeof(float));
+  l.total = off;
+  return l;
+}
+
 gdr_status check_bwd(const gdr_problem* p, bool varlen) {
   const gdr_status st = check(p, varlen);
   if (st != GDR_OK) return st;
@@ -414,6 +439,105 @@ gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const vo
   a.o = o;
   a.ht = ht;
   return hip_status(gdr::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
+
+gdr_status gdr_segmented_workspace_layout(const gdr_problem* p, gdr_seg_layout* out) {
+  if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
+  const gdr_status st = check(p, true);
+  if (st != GDR_OK) return st;
+  *out = seg_layout_of(*p);
+  return GDR_OK;
+}
+
+gdr_status gdr_segmented_workspace_bytes(const gdr_problem* p, size_t* bytes) {
+  gdr_seg_layout l;
+  const gdr_status st = gdr_segmented_workspace_layout(p, &l);
+  if (st != GDR_OK) return st;
+  if (bytes == nullptr) return GDR_ERR_NULL_ARG;
+  *bytes = l.total;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* h0, void* o, float* ht, float* seg_states, float* transitions,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (cu_seqlens == nullptr) return GDR_ERR_NULL_ARG;
+  gdr_status st = check(p, true);
+  if (st != GDR_OK) return st;
+  if (p->T > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht, seg_states, transitions, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  const gdr_seg_layout l = seg_layout_of(*p);
+  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  const int64_t HV = p->HV, K = p->K, V = p->V, N = p->N;
+  float* s_ext = reinterpret_cast<float*>(ws + l.s_ext);
+  float* trans = transitions ? transitions : reinterpret_cast<float*>(ws + l.trans);
+  float* s_in = seg_states ? seg_states : reinterpret_cast<float*>(ws + l.s_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  Args a = make_args(*p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
+  a.Tm = ws + l.fwd.Tm;
+  a.w = ws + l.fwd.w;
+  a.u = ws + l.fwd.u;
+  a.h = ws + l.fwd.h;
+  a.v_new = ws + l.fwd.v_new;
+  a.kscale = p->gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.fwd.kscale);
+
+  // chunk tables over the segments, then w, u (and the token factors)
+  hipError_t e = gdr::launch_chunk_table(a, s);
+  if (!p->gate_per_channel) {
+    if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
+  } else {
+    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    if (e == hipSuccess) e = gdr::launch_wy(a, s);
+  }
+  // pre-process 1: every segment's local end state from a zero state
+  Args pre = a;
+  pre.h0 = nullptr;
+  pre.ht = s_ext;
+  if (e == hipSuccess) e = gdr::launch_fwd_h(pre, s);
+  // pre-process 2: every segment's transition, the same scan over the K x K
+  // identity with no values (u = 0): S <- diag(e^{G_L}) S - K'^T (W S)
+  Args tr = a;
+  tr.V = K;
+  tr.u = ws + l.u_zero;
+  tr.h = ws + l.h_tr;
+  tr.v_new = ws + l.v_tr;
+  tr.h0 = reinterpret_cast<float*>(ws + l.eye);
+  tr.ht = trans;
+  if (e == hipSuccess) e = gdr::launch_zero(ws + l.u_zero, l.h_tr - l.u_zero, s);
+  if (e == hipSuccess) e = gdr::launch_identity(N * HV, K, reinterpret_cast<float*>(ws + l.eye), s);
+  if (e == hipSuccess) e = gdr::launch_fwd_h(tr, s);
+  // merge along the segments
+  if (e == hipSuccess) e = gdr::launch_merge(N, HV, K, V, trans, s_ext, h0, s_in, s);
+  // re-run every segment from its entering state; the last segment's end state is ht
+  Args re = a;
+  re.h0 = s_in;
+  re.o = o;
+  re.ht = s_ext;
+  if (gdr::fwd_h_o_supported(re)) {
+    if (e == hipSuccess) e = gdr::launch_fwd_h_o(re, s);
+  } else {
+    if (e == hipSuccess) e = gdr::launch_fwd_h(re, s);
+    if (e == hipSuccess) e = gdr::launch_fwd_o(re, s);
+  }
+  if (e == hipSuccess && ht != nullptr)
+    e = hipMemcpyAsync(ht, s_ext + (N - 1) * HV * K * V, (size_t)(HV * K * V) * sizeof(float),
+                       hipMemcpyDeviceToDevice, s);
+  return hip_status(e);
 }
 
 gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* out) {

@@ -70,6 +70,11 @@ hipError_t launch_fwd_o(const Args& a, hipStream_t s);
 // token-by-token forward (no chunk table, no workspace)
 hipError_t launch_recurrent(const Args& a, hipStream_t s);
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s);
+// segment hand-off: fills and the merge S_in[r + 1] = M[r] S_in[r] + S_ext[r]
+hipError_t launch_identity(int64_t count, int64_t K, float* out, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_merge(int64_t R, int64_t HV, int64_t K, int64_t V, const float* M, const float* Sext,
+                        const float* h0, float* Sin, hipStream_t s);
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dqkvg(const Args& a, hipStream_t s);
 

@@ -221,6 +221,45 @@ gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const vo
                                    const float* g, const float* beta, const int32_t* cu_seqlens,
                                    const float* h0, void* o, float* ht, void* stream);
 
+/* Segment hand-off on one device: the context-parallel forward of the KCP
+ * page ("flash-linear-attention KCP precision-failure root-cause manual",
+ * sections on the pre-process and merge kernels and "h and dh cross-rank
+ * semantics") with every segment in the same launches instead of on its own
+ * rank.  The problem is a varlen batch (B = 1) whose N sequences are the
+ * consecutive segments of ONE sequence of T tokens, cu_seqlens (required) their
+ * bounds.  Per segment r, with the chunk scan of gdr_fwd_h:
+ *   S_ext[r]  = the segment's end state from a zero state,
+ *   M[r]      = its transition, the product of the per-token maps
+ *               D_t (I - beta_t k^_t k^_t^T) over its tokens (the same scan
+ *               started from the K x K identity with no values),
+ * then the merge S_in[0] = h0, S_in[r + 1] = M[r] S_in[r] + S_ext[r] (fp32, in
+ * segment order), and a re-run of every segment from S_in[r] that writes o.
+ * The result is that of gdr_chunk_fwd on the whole sequence (B = 1, dense) up
+ * to rounding.
+ *   q, k, v, g, beta   as gdr_chunk_fwd with B = 1
+ *   h0          f32 [1,HV,K,V] or NULL (zeros): the sequence's initial state
+ *   o           dtype [1,T,HV,V] (output)
+ *   ht          f32 [1,HV,K,V] or NULL: the final state (the last segment's re-run)
+ *   seg_states  f32 [N+1,HV,K,V] or NULL: S_in, the state entering each segment,
+ *               and S_in[N] = the merged final state
+ *   transitions f32 [N,HV,K,K] or NULL: M
+ *   workspace   >= gdr_segmented_workspace_bytes bytes; gdr_segmented_workspace_layout
+ *               gives the offsets (the forward intermediates of the segment batch
+ *               first, as gdr_fwd_layout, then the scratch of the transition scan).
+ * Errors as gdr_chunk_fwd; cu_seqlens NULL returns GDR_ERR_NULL_ARG. */
+typedef struct {
+  gdr_fwd_layout fwd;
+  size_t u_zero, h_tr, v_tr, eye, s_ext, trans, s_in, total;
+} gdr_seg_layout;
+
+gdr_status gdr_segmented_workspace_bytes(const gdr_problem* p, size_t* bytes);
+gdr_status gdr_segmented_workspace_layout(const gdr_problem* p, gdr_seg_layout* layout);
+gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* h0, void* o, float* ht, float* seg_states,
+                                   float* transitions, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* ------------------------------------------------------------------ backward
  *
  * Gradients of L = sum(o * d_o) + sum(ht * dht) with respect to q, k, v, g,

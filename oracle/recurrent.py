@@ -292,3 +292,35 @@ def recurrent_bwd(q, k, v, g, beta, do, dht=None, *, scale=1.0, h0=None, cu_seql
     else:
         dq, dk = dqh, dkh
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0 if h0 is not None else dh0)
+
+
+def transition(k, g, beta, *, cu_seqlens=None, use_qk_l2norm: bool = False):
+    """Transition of every sequence (or segment): the product of its per-token
+    maps A_t = (I - beta_t k_t k_t^T) D_t, last token leftmost, so that the
+    recurrence above gives S_end = M S_start + (the end state from a zero
+    start).  This is the matrix the KCP page's pre-process hands to the merge
+    ("flash-linear-attention KCP precision-failure root-cause manual",
+    pre-process and merge sections); at g = 0 over one chunk it is the page
+    "FLA operator-kernel correctness testing and coverage matrix" section 2's
+    P^r.  Returns M [N,HV,K,K] in float64."""
+    k, g, beta = (_f64(x) for x in (k, g, beta))
+    B, T, H, K = k.shape
+    HV = beta.shape[2]
+    per_channel = g.dim() == 4
+    if use_qk_l2norm:
+        k = l2norm(k)
+    k = _expand_heads(k, HV)
+    segs = sequences(B, T, cu_seqlens)
+    M = torch.zeros(len(segs), HV, K, K, dtype=torch.float64)
+    eye = torch.eye(K, dtype=torch.float64)
+    for n, (b, s, e) in enumerate(segs):
+        for j in range(HV):
+            P = eye.clone()
+            for t in range(s, e):
+                d = torch.exp(g[b, t, j])
+                D = torch.diag(d) if per_channel else d * eye
+                kt = k[b, t, j]
+                A = (eye - beta[b, t, j] * torch.outer(kt, kt)) @ D
+                P = A @ P
+            M[n, j] = P
+    return M

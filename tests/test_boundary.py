@@ -261,3 +261,25 @@ def test_fused_recurrent_wrapper_refuses_cpu_tensors():
     g = torch.zeros(1, 8, 1)
     with pytest.raises(ValueError, match="GPU"):
         gdr.fused_recurrent_fwd(x, x, x, g, g)
+
+
+def test_segmented_rejects_before_launch():
+    """The segment hand-off forward needs cu_seqlens and a large enough
+    workspace; errors come back before any launch."""
+    L = gdr.lib()
+    P = ctypes.c_void_p
+    A = P(0x1000)
+    p = problem(B=1, N=3, T=300)
+    lay = gdr.seg_layout(p)
+    assert lay.total > lay.fwd.total and lay.s_in > lay.trans > lay.s_ext
+    # no cu_seqlens
+    assert L.gdr_chunk_fwd_segmented(ctypes.byref(p), A, A, A, A, A, None, None, A, None, None, None, A,
+                                     ctypes.c_size_t(1 << 40), None) == 1
+    # workspace too small
+    assert L.gdr_chunk_fwd_segmented(ctypes.byref(p), A, A, A, A, A, A, None, A, None, None, None, A,
+                                     ctypes.c_size_t(lay.total - 1), None) == 7
+    # chunk size and a dense batch (B != 1 with cu_seqlens)
+    assert L.gdr_chunk_fwd_segmented(ctypes.byref(problem(B=1, N=3, T=300, chunk_size=16)), A, A, A, A, A, A,
+                                     None, A, None, None, None, A, ctypes.c_size_t(1 << 40), None) == 2
+    assert L.gdr_chunk_fwd_segmented(ctypes.byref(problem()), A, A, A, A, A, A, None, A, None, None, None, A,
+                                     ctypes.c_size_t(1 << 40), None) == 4

@@ -16,6 +16,7 @@ import torch
 import torch.nn.functional as F
 
 from oracle import chunked, recurrent
+import workloads
 from oracle.metrics import err_ratio
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -465,3 +466,41 @@ def test_chunked_backward_varlen_and_state_gradients():
         if lengths[n]:
             last = got0["inter"]["off"][n + 1] - 1
             assert np.allclose(got0["inter"]["dE"][last], got0["inter"]["dEi"][last], atol=1e-14)
+
+
+@pytest.mark.parametrize("pc", [False, True])
+def test_transition_chains_segments(pc):
+    """The segment transition M is pinned by the property that defines it:
+    for any start state S0, running the per-token recurrence over the segment
+    from S0 ends in M S0 + (the end state from zero).  Checked on random S0
+    for two unaligned segments of a GVA batch, and M of the concatenation is
+    the product of the two segments' transitions."""
+    w = workloads.Workload("tr", B=1, T=0, H=1, HV=2, K=8, V=5, chunk_size=64, dtype="fp32",
+                           per_channel_gate=pc, l2norm_in_kernel=True, slow_decay=True)
+    inp = workloads.make_inputs(w, lengths=[9, 14])
+    q, k, v, g, beta = (inp[n] for n in ("q", "k", "v", "g", "beta"))
+    cu = inp["cu_seqlens"]
+    M = recurrent.transition(k, g, beta, cu_seqlens=cu, use_qk_l2norm=True)
+    S0 = torch.randn(2, 2, 8, 5, generator=torch.Generator().manual_seed(3), dtype=torch.float64)
+    _, ht = recurrent.recurrent_fwd(q, k, v, g, beta, h0=S0, cu_seqlens=cu, use_qk_l2norm=True)
+    _, ht0 = recurrent.recurrent_fwd(q, k, v, g, beta, h0=None, cu_seqlens=cu, use_qk_l2norm=True)
+    np.testing.assert_allclose((M @ S0 + ht0).numpy(), ht.numpy(), rtol=1e-12, atol=1e-12)
+    whole = torch.tensor([0, 23], dtype=torch.int32)
+    Mw = recurrent.transition(k, g, beta, cu_seqlens=whole, use_qk_l2norm=True)
+    np.testing.assert_allclose(Mw[0].numpy(), (M[1] @ M[0]).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_transition_at_zero_gate_is_the_wy_product():
+    """At g = 0 the transition of one chunk is the page's P^r = I - sum_i k^i w^i^T
+    with w from the chunked oracle's WY factors (a separate code path)."""
+    w = workloads.Workload("trwy", B=1, T=12, H=1, HV=1, K=6, V=4, chunk_size=64, dtype="fp32",
+                           host_l2norm=True)
+    inp = workloads.make_inputs(w)
+    g0 = torch.zeros_like(inp["g"])
+    M = recurrent.transition(inp["k"], g0, inp["beta"])
+    _, _, it = chunked.chunked_fwd(inp["q"], inp["k"], inp["v"], g0, inp["beta"], chunk_size=64,
+                                   intermediates=True)
+    kk = inp["k"][0, :, 0].double().numpy()
+    W = it["W"][0, 0][:12]
+    P = np.eye(6) - kk.T @ W
+    np.testing.assert_allclose(M[0, 0].numpy(), P, rtol=1e-12, atol=1e-12)
