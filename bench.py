@@ -540,6 +540,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the long-sequence forward + backward record of the default run")
     ap.add_argument("--breakdown", action="store_true", help="per-stage times on stderr")
+    ap.add_argument("--segments", type=int, default=0, metavar="R",
+                    help="only time the workload's first sequence as R segments (segment hand-off) "
+                         "beside its single pass, print that record and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (known bytes, to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -565,6 +568,9 @@ def main():
     import workloads
 
     w = workloads.CONFIGS[args.workload]
+    if args.segments:
+        print(json.dumps(measure_segmented(gdr, w, args.segments, args.steps, args.warmup)))
+        return
     if w.T == 1:
         rec, inp = measure_decode(gdr, w, args.steps, args.warmup)
     else:
