@@ -350,6 +350,9 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     fused = gdr.chunk_fwd_fused(p)
     for name in (("kkt_solve", "wy", "fwd_h", "fwd_o") if fused else ("kkt_wy", "fwd_h_o")):
         fstages.pop(name, None)
+    if fused and d["cu_seqlens"] is None:
+        # a dense batch's fused K1 + K2 stage writes the chunk table itself
+        fstages.pop("chunk_table")
     fstages = {n: fstages[n] for n in ("chunk_table", "kkt_solve", "wy", "kkt_wy", "fwd_h", "fwd_o", "fwd_h_o")
                if n in fstages}
     reps = max(5, min(steps, 50))

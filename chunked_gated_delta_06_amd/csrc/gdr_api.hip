@@ -250,13 +250,20 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   a.o = o;
   a.ht = ht;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gdr::launch_chunk_table(a, s);
+  hipError_t e = hipSuccess;
   if (!p->keep_states && gdr::fwd_h_o_preferred(a)) {
     // fused K1 + K2 (Tm stays on chip) and fused scan + output (h and v_new
-    // stay on chip)
+    // stay on chip); for a dense batch the first writes the chunk table too
+    if (cu_seqlens == nullptr && a.NTmax > 0) {
+      a.table_from_dims = 1;
+    } else {
+      e = gdr::launch_chunk_table(a, s);
+    }
     if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
+    a.table_from_dims = 0;
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
   } else {
+    e = gdr::launch_chunk_table(a, s);
     if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
     if (e == hipSuccess) e = gdr::launch_wy(a, s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);

@@ -21,6 +21,9 @@ constexpr int64_t kscale_pitch(int64_t C) { return 3 * C + 4; }
 struct Args {
   int64_t B, T, H, HV, K, V, N, NTmax;
   int32_t C, per_channel, l2norm, dtype;
+  // dense batch only: the first stage derives every chunk from B, T and C and
+  // writes the chunk table itself (no separate table launch)
+  int32_t table_from_dims;
   float scale;
   const void* q;
   const void* k;

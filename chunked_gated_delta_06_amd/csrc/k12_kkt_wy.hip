@@ -60,9 +60,24 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t c = blockIdx.x, j = blockIdx.y;
-  if (c >= a.chunk_off[a.N]) return;
-  const int64_t t0 = a.chunk_idx[4 * c + 1];
-  const int L = a.chunk_idx[4 * c + 2];
+  int64_t t0;
+  int L;
+  if (a.table_from_dims) {
+    // dense batch: chunk c is chunk c % NC of row c / NC; the first value
+    // head's workgroups also write the table for the stages that follow
+    const int64_t NC = (a.T + C - 1) / C, n = c / NC, cl = c % NC;
+    t0 = n * a.T + cl * C;
+    L = (int)((a.T - cl * C) < C ? (a.T - cl * C) : C);
+    if (j == 0 && tid == 0) {
+      reinterpret_cast<int4*>(a.chunk_idx)[c] = int4{(int32_t)n, (int32_t)t0, L, (int32_t)cl};
+      if (c == 0)
+        for (int64_t b = 0; b <= a.B; ++b) a.chunk_off[b] = (int32_t)(b * NC);
+    }
+  } else {
+    if (c >= a.chunk_off[a.N]) return;
+    t0 = a.chunk_idx[4 * c + 1];
+    L = a.chunk_idx[4 * c + 2];
+  }
   const int64_t H = a.H, HV = a.HV, V = a.V, h = j / (HV / H);
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ vp = static_cast<const T*>(a.v);
