@@ -22,43 +22,46 @@ constexpr int kMB = 16;    // state columns per merge workgroup
 constexpr int kMT = 256;   // merge threads
 
 // S_in for every segment boundary, for one value head and 16 state columns.
-// The running state sits in LDS; output (k, c) of a step is
+// The running state tile sits in LDS; thread t owns row k = t / (256 / K) and
+// K / 16 consecutive columns of it, reads its row of M[r] as 16-byte vectors
+// and the tile rows as broadcast LDS reads.  Output (k, c) of a step is
 // S_ext[r][k][c] + sum_m M[r][k][m] S[m][c] in fp32, summed in order of m.
 template <int K>
 __global__ __launch_bounds__(kMT) void k6_merge(int64_t R, int64_t HV, int64_t V, const float* __restrict__ M,
                                                 const float* __restrict__ Sext, const float* __restrict__ h0,
                                                 float* __restrict__ Sin) {
-  constexpr int PER = K * kMB / kMT;   // outputs per thread
-  __shared__ float sX[K * kMB];
-  const int tid = threadIdx.x;
+  constexpr int TPR = kMT / K;        // threads per row
+  constexpr int CPT = kMB / TPR;      // columns per thread
+  __shared__ __attribute__((aligned(16))) float sX[K * kMB];
+  const int tid = threadIdx.x, k = tid / TPR, c0 = (tid % TPR) * CPT;
   const int64_t nvt = V / kMB;
   const int64_t j = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * kMB;
 
+  float x[CPT];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int idx = tid + kMT * m, k = idx / kMB, c = idx % kMB;
-    const int64_t off = (j * K + k) * V + v0 + c;
-    const float x = h0 != nullptr ? h0[off] : 0.f;
-    sX[idx] = x;
-    Sin[off] = x;
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t off = (j * K + k) * V + v0 + c0 + c;
+    x[c] = h0 != nullptr ? h0[off] : 0.f;
+    sX[k * kMB + c0 + c] = x[c];
+    Sin[off] = x[c];
   }
   for (int64_t r = 0; r < R; ++r) {
     __syncthreads();
-    float acc[PER];
-    const float* Mr = M + (r * HV + j) * K * K;
+    const float* Mrow = M + ((r * HV + j) * K + k) * (int64_t)K;
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int idx = tid + kMT * m, k = idx / kMB, c = idx % kMB;
-      float s = Sext[((r * HV + j) * K + k) * V + v0 + c];
-      for (int mm = 0; mm < K; ++mm) s = __builtin_fmaf(Mr[(int64_t)k * K + mm], sX[mm * kMB + c], s);
-      acc[m] = s;
+    for (int c = 0; c < CPT; ++c) x[c] = Sext[((r * HV + j) * K + k) * V + v0 + c0 + c];
+    for (int mm = 0; mm < K; mm += 4) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mrow + mm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) x[c] = __builtin_fmaf(m4[e], sX[(mm + e) * kMB + c0 + c], x[c]);
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int idx = tid + kMT * m, k = idx / kMB, c = idx % kMB;
-      sX[idx] = acc[m];
-      Sin[(((r + 1) * HV + j) * K + k) * V + v0 + c] = acc[m];
+    for (int c = 0; c < CPT; ++c) {
+      sX[k * kMB + c0 + c] = x[c];
+      Sin[(((r + 1) * HV + j) * K + k) * V + v0 + c0 + c] = x[c];
     }
   }
 }

@@ -137,3 +137,54 @@ def test_decode_step_many_sequences():
     idx = [cu[n] for n in seqs]
     check("o", f64(o)[:, idx], ro[:, idx], 5e-3)
     check("ht", f64(ht)[seqs], rht[seqs], 5e-3)
+
+
+def test_recurrent_nan_poison_canaries_deterministic():
+    """NaN-filled outputs on entry leave no trace, guard bands around o and ht
+    stay untouched, and two runs agree bitwise."""
+    w, inp = mk(B=3, T=45, K=128, V=128)
+    o1, ht1 = gpu_rec(inp)
+    pad = 4096
+    on, hn = o1.numel(), ht1.numel()
+    o_full = torch.full((on + 2 * pad,), float("nan"), dtype=o1.dtype, device="cuda")
+    ht_full = torch.full((hn + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+    o = o_full[pad:pad + on].view(o1.shape)
+    ht = ht_full[pad:pad + hn].view(ht1.shape)
+    gdr.fused_recurrent_fwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                            scale=inp["scale"], initial_state=dev(inp["h0"]), use_qk_l2norm_in_kernel=True,
+                            out=(o, ht))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(ht, ht1)
+    assert torch.isnan(o_full[:pad]).all() and torch.isnan(o_full[pad + on:]).all()
+    assert torch.isnan(ht_full[:pad]).all() and torch.isnan(ht_full[pad + hn:]).all()
+
+
+def test_recurrent_int64_offsets():
+    """A varlen batch whose last sequence sits past 2^31 elements of q / k / v;
+    only that sequence is checked against the oracle."""
+    H = HV = 16
+    K = V = 128
+    tail = 40
+    T = (1 << 20) + 64
+    gen = torch.Generator().manual_seed(4)
+    q = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    k = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
+    v = torch.zeros(1, T, HV, V, dtype=torch.bfloat16)
+    g = torch.zeros(1, T, HV)
+    beta = torch.zeros(1, T, HV)
+    s = T - tail
+    q[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    k[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    v[:, s:] = torch.randn(1, tail, HV, V, generator=gen).bfloat16()
+    g[:, s:] = torch.nn.functional.logsigmoid(torch.randn(1, tail, HV, generator=gen) + 4)
+    beta[:, s:] = torch.sigmoid(torch.randn(1, tail, HV, generator=gen))
+    h0 = 0.1 * torch.randn(2, HV, K, V, generator=gen)
+    assert (T - 1) * H * K > 2 ** 31
+    cu = torch.tensor([0, s, T], dtype=torch.int32)
+    o, ht = gdr.fused_recurrent_fwd(q.cuda(), k.cuda(), v.cuda(), g.cuda(), beta.cuda(), cu_seqlens=cu.cuda(),
+                                    initial_state=h0.cuda(), use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    ro, rht = recurrent.recurrent_fwd(q[:, s:], k[:, s:], v[:, s:], g[:, s:], beta[:, s:], h0=h0[1:2],
+                                      use_qk_l2norm=True)
+    check("o tail", f64(o[:, s:]), ro.numpy(), 5e-3)
+    check("ht tail", f64(ht[1:2]), rht.numpy(), 5e-3)
