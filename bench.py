@@ -4,8 +4,9 @@
 One step = one full forward (K0 chunk table, K1 kk^T + triangular inverse,
 K2 WY recompute, K3 state scan, K4 output) over one batch of the workload,
 inputs resident in HBM; for a workload with a backward (long_bf16) a step is
-the forward plus the full backward (K0-K3 recompute, B1 de_local, B2 reverse
-state-gradient scan, B3 fused gradients).  Prints one JSON line:
+the forward, keeping its intermediates, plus the full backward reading them
+(B1 de_local, B2 reverse state-gradient scan, B3 fused gradients); the record
+also times the alternative that recomputes K0-K3 in the backward.  Prints one JSON line:
 
   value        tokens/s of one step (B*T / seconds per step)
   roofline     the dominant kernel's algorithmic HBM bytes per launch / its
@@ -316,14 +317,31 @@ def measure(gdr, w, steps, warmup, breakdown, label):
                     P(d["cu_seqlens"]), P(d["h0"]), P(d["do"]), P(d["dht"]), *[P(t) for t in grads], P(dh0),
                     P(bws), ctypes.c_size_t(bws.numel()), sp)
 
-    def step():
-        st = L.gdr_chunk_fwd(*fwd_args)
-        if st == 0 and backward:
-            st = L.gdr_chunk_bwd(*bwd_args)
+        # a training step keeps the forward's intermediates for the backward:
+        # the forward runs its separate stages into the backward's workspace
+        # and the backward skips its recompute of K0-K3
+        pk = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
+                              use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"], keep_states=True)
+        fwd_keep_args = (ctypes.byref(pk), *fwd_args[1:10], P(bws), ctypes.c_size_t(bws.numel()), sp)
+        bwd_keep_args = (ctypes.byref(pk), *bwd_args[1:])
+
+    def check_st(st):
         if st != 0:
             raise RuntimeError(L.gdr_status_string(st).decode())
 
+    def step():
+        if backward:
+            check_st(L.gdr_chunk_fwd(*fwd_keep_args))
+            check_st(L.gdr_chunk_bwd(*bwd_keep_args))
+        else:
+            check_st(L.gdr_chunk_fwd(*fwd_args))
+
+    def step_recompute():
+        check_st(L.gdr_chunk_fwd(*fwd_args))
+        check_st(L.gdr_chunk_bwd(*bwd_args))
+
     ms_per_step = wall_ms_per_step(step, warmup, steps)
+    recompute_ms = wall_ms_per_step(step_recompute, warmup, steps) if backward else None
     tokens = inp["B"] * inp["T"]
     value = tokens / (ms_per_step * 1e-3)
 
@@ -347,7 +365,7 @@ def measure(gdr, w, steps, warmup, breakdown, label):
                                                    views["w"], views["u"], views["kscale"])
     # the stages the timed step runs: the fused K1 + K2 and scan + output
     # stages where the shape has them
-    fused = gdr.chunk_fwd_fused(p)
+    fused = gdr.chunk_fwd_fused(p) and not backward
     for name in (("kkt_solve", "wy", "fwd_h", "fwd_o") if fused else ("kkt_wy", "fwd_h_o")):
         fstages.pop(name, None)
     if fused and d["cu_seqlens"] is None:
@@ -368,14 +386,9 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     if backward:
         bv = gdr.bwd_workspace_views(p, bws)
         bidx, boff = bv["chunk_idx"], bv["chunk_off"]
+        # the backward's own stages (the step's forward leaves K0-K3's
+        # intermediates in this workspace)
         bstages = {
-            "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], bidx, boff),
-            "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], bidx, boff, bv["Tm"],
-                                                   bv["kscale"]),
-            "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], bidx, boff, bv["Tm"], bv["w"],
-                                     bv["u"]),
-            "fwd_h": lambda: gdr.fwd_h(p, d["k"], bv["w"], bv["u"], d["g"], bidx, boff, d["h0"], bv["h"],
-                                       bv["v_new"], None, bv["kscale"]),
             "bwd_intra": lambda: gdr.bwd_intra(p, d["q"], d["k"], d["g"], d["do"], bidx, boff, bv["de_local"],
                                                bv["qscale"]),
             "bwd_dh": lambda: gdr.bwd_dh(p, d["q"], d["k"], bv["w"], d["do"], bv["de_local"], bv["qscale"],
@@ -384,11 +397,14 @@ def measure(gdr, w, steps, warmup, breakdown, label):
                                                bv["h"], bv["v_new"], bv["dh"], bidx, boff, *grads),
         }
         bwd_ms = event_stage_ms(stream, bstages, reps)
-        bper = bwd_stage_bytes_per_token_head(w, T_seq)
+        bper = {k: v for k, v in bwd_stage_bytes_per_token_head(w, T_seq).items() if k in bstages}
         rec["stage_ms"]["backward"] = bwd_ms
         bwd_total_ms = sum(bwd_ms.values())
         rec["backward_hbm_frac"] = sum(bper.values()) * units / (bwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
         rec["backward_ms"] = bwd_total_ms
+        rec["recompute_ms_per_step"] = recompute_ms
+        rec["step"] = ("forward with its intermediates kept (separate stages) + backward reading them; "
+                       "recompute_ms_per_step: fused forward + backward that recomputes K0-K3")
         # the dominant kernel of a forward + backward step is taken among the
         # backward's own stages (the forward's stages are reported separately)
         rec["roofline"] = roofline(bper, bwd_ms, units, w.name, [n for n in bper if n.startswith("bwd_")])

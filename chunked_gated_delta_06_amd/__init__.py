@@ -413,11 +413,14 @@ def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, *, scale: float = 1.0, chu
 def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size: int = 64,
               cu_seqlens=None, initial_state=None, use_qk_l2norm_in_kernel: bool = False,
               workspace: Optional[torch.Tensor] = None, return_workspace: bool = False,
-              out=None, want_dh0: bool = True, validate_cu: bool = True):
+              out=None, want_dh0: bool = True, validate_cu: bool = True, reuse_forward: bool = False):
     """Backward of the chunked gated delta rule: gradients of
     sum(o * do) + sum(ht * dht).  Returns (dq, dk, dv, dg, dbeta, dh0) (dh0 None
     when not wanted), plus the workspace when ``return_workspace``.  ``out``
-    supplies the six output tensors."""
+    supplies the six output tensors.  ``reuse_forward`` skips the recompute of
+    the forward intermediates: ``workspace`` must be the backward-sized
+    workspace a ``chunk_fwd(..., keep_states=True, workspace=workspace)`` call
+    on the same inputs has just filled."""
     _need_gpu(q, k, v, g, beta, do, dht, cu_seqlens, initial_state)
     if k.dtype != q.dtype or v.dtype != q.dtype or do.dtype != q.dtype:
         raise ValueError("q, k, v and do must share one dtype")
@@ -427,8 +430,10 @@ def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size:
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=reuse_forward)
     lay = bwd_layout(p)
+    if reuse_forward and (workspace is None or workspace.numel() < lay.total):
+        raise ValueError("reuse_forward needs the backward-sized workspace the forward filled")
     check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
     _expect("do", do, v.shape)
     _expect("dht", dht, (p.N, p.HV, p.K, p.V))

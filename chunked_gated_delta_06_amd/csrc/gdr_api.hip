@@ -611,10 +611,14 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   a.dg = dg;
   a.dbeta = dbeta;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = gdr::launch_chunk_table(a, s);
-  if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-  if (e == hipSuccess) e = gdr::launch_wy(a, s);
-  if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+  hipError_t e = hipSuccess;
+  if (!p->keep_states) {
+    // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
+    e = gdr::launch_chunk_table(a, s);
+    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    if (e == hipSuccess) e = gdr::launch_wy(a, s);
+    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+  }
   if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
   if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
   if (e == hipSuccess) e = gdr::launch_bwd_dqkvg(a, s);

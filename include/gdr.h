@@ -71,10 +71,12 @@ typedef struct {
   int32_t use_qk_l2norm;     /* 1: normalise q, k rows in the kernels */
   int32_t dtype;             /* gdr_dtype */
   float scale;               /* output scale */
-  int32_t keep_states;       /* gdr_chunk_fwd only: 1 = run the separate K3 and K4 stages and
-                                leave h and v_new in the workspace; 0 = use the fused
-                                scan + output stage where gdr_fwd_h_o_supported (h and
-                                v_new are then not written) */
+  int32_t keep_states;       /* gdr_chunk_fwd: 1 = run the separate K1..K4 stages and leave
+                                Tm, h and v_new in the workspace; 0 = use the fused stages
+                                where gdr_fwd_h_o_supported (Tm, h and v_new are then not
+                                written).  gdr_chunk_bwd: 1 = take those intermediates
+                                from its workspace instead of recomputing them (see
+                                gdr_chunk_bwd) */
 } gdr_problem;
 
 /* Offsets (bytes from the workspace base) of the forward intermediates that
@@ -298,7 +300,14 @@ gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* layout
  *   workspace  >= gdr_bwd_workspace_bytes bytes (contents on entry irrelevant).
  * Supported: scalar gate (gate_per_channel = 0), K in {32, 64, 128}, any V;
  * fp32 additionally needs chunk_size 32 when K = 128.  Other problems return
- * GDR_ERR_UNSUPPORTED before any launch. */
+ * GDR_ERR_UNSUPPORTED before any launch.
+ * Saved forward states: with p->keep_states = 1 the recompute is skipped and
+ * the forward intermediates are taken from the workspace as they stand, which
+ * requires that gdr_chunk_fwd ran with keep_states = 1, the same problem and
+ * inputs, and this same workspace (its leading gdr_fwd_layout part) before this
+ * call, with nothing written to that part in between.  The gradients are then
+ * bitwise those of the recomputing call (the same kernels produced the
+ * intermediates). */
 gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, const void* d_o, const float* dht, void* dq, void* dk,

@@ -234,6 +234,34 @@ def test_bwd_deterministic_and_poisoned():
     compare(got1, oracle_bwd(inp), TOL["bf16"])
 
 
+@pytest.mark.parametrize("varlen", [False, True])
+def test_bwd_reuses_saved_forward_states(varlen):
+    """A forward with keep_states on the backward-sized workspace, then the
+    backward with reuse_forward: the same gradients, bitwise, as the backward
+    that recomputes the forward intermediates (the same kernels made them), and
+    within tolerance of the oracle."""
+    lengths = [70, 0, 129, 64] if varlen else None
+    w, inp = mk(B=1 if varlen else 2, T=170, H=2, HV=4, K=128, V=64, slow=True, lengths=lengths)
+    ref_got, _, _ = gpu_bwd(inp)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, cu_seqlens=inp["cu_seqlens"],
+                         use_qk_l2norm=True)
+    lay = gdr.bwd_layout(p)
+    ws = torch.full((lay.total,), 0xFF, dtype=torch.uint8, device="cuda")   # poisoned
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "do", "dht", "h0", "cu_seqlens")}
+    o, ht = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                          initial_state=d["h0"], use_qk_l2norm_in_kernel=True, workspace=ws, keep_states=True)
+    grads = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["dht"],
+                          cu_seqlens=d["cu_seqlens"], initial_state=d["h0"], use_qk_l2norm_in_kernel=True,
+                          workspace=ws, reuse_forward=True)
+    torch.cuda.synchronize()
+    for n, t in zip(GRADS, grads):
+        assert np.array_equal(f64(t), ref_got[n]), n
+    compare(ref_got, oracle_bwd(inp), TOL["bf16"])
+    with pytest.raises(ValueError, match="reuse_forward"):
+        gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["dht"], cu_seqlens=d["cu_seqlens"],
+                      initial_state=d["h0"], use_qk_l2norm_in_kernel=True, reuse_forward=True)
+
+
 def test_bwd_unsupported_shapes_raise():
     w, inp = mk(T=64, K=64, V=64, C=64)
     gpc = torch.zeros(2, 64, 2, 64, device="cuda")
