@@ -544,6 +544,52 @@ def measure_segmented(gdr, w, R, steps, warmup):
             "parity": parity}
 
 
+def measure_simple_gla(gdr, w, steps, warmup):
+    """The simple GLA forward (gdr_simple_gla_fwd) on workload ``w``'s inputs
+    (beta unused): parity of the first sequence's first 512 tokens on two
+    heads against the per-token oracle, then the timed call."""
+    import torch
+    from oracle import recurrent
+    from oracle.metrics import err_ratio
+    dev = torch.device("cuda:0")
+    inp = workloads_inputs(w)
+    d = to_dev(inp, dev, ("q", "k", "v", "g", "h0", "cu_seqlens"))
+    kw = dict(scale=inp["scale"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"], initial_state=d["h0"],
+              use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    o, ht = gdr.simple_gla_fwd(d["q"], d["k"], d["v"], d["g"], **kw)
+    torch.cuda.synchronize()
+    hs = [0, w.HV - 1]
+    sub = {n: inp[n][:1, :512][:, :, hs].contiguous() for n in ("q", "k", "v", "g")}
+    ro, _ = recurrent.simple_gla_fwd(sub["q"], sub["k"], sub["v"], sub["g"], scale=inp["scale"],
+                                     h0=inp["h0"][:1, hs], use_qk_l2norm=inp["use_qk_l2norm"])
+    tol = 5e-3 if w.dtype == "bf16" else 1e-4
+    parity = {"o (sequence 0, first 512 tokens, 2 heads)": err_ratio(o[:1, :512][:, :, hs].cpu(), ro), "tol": tol}
+    print(f"parity gate ({w.name}, simple GLA): " + ", ".join(f"{k}={v:.2e}" for k, v in parity.items()),
+          file=sys.stderr, flush=True)
+    if not all(v <= tol for k, v in parity.items() if k != "tol"):
+        print("parity check failed: refusing to report throughput", file=sys.stderr)
+        sys.exit(1)
+    L = gdr.lib()
+    p = gdr.make_problem(d["q"], d["v"], d["g"], chunk_size=inp["chunk_size"], cu_seqlens=d["cu_seqlens"],
+                         use_qk_l2norm=inp["use_qk_l2norm"], scale=inp["scale"])
+    lay = gdr.fwd_layout(p)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["cu_seqlens"]), P(d["h0"]), P(o),
+            P(ht), P(ws), ctypes.c_size_t(ws.numel()), sp)
+
+    def step():
+        st = L.gdr_simple_gla_fwd(*args)
+        if st != 0:
+            raise RuntimeError(L.gdr_status_string(st).decode())
+
+    ms = wall_ms_per_step(step, warmup, steps)
+    tokens = inp["B"] * inp["T"]
+    return {"workload": w.name, "pass": "simple GLA forward (same chunked stages, w = 0, u = v)",
+            "tokens_per_s": tokens / (ms * 1e-3), "ms_per_step": ms, "parity": parity}
+
+
 def workloads_inputs(w):
     import workloads
     return workloads.make_inputs(w)
@@ -610,6 +656,8 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     del inp
+    if not w.backward and not args.no_backward and w.T > 1 and not w.per_channel_gate:
+        line["simple_gla"] = measure_simple_gla(gdr, w, args.steps, args.warmup)
     if not w.backward and not args.no_backward:
         torch.cuda.empty_cache()
         wb = workloads.CONFIGS["long_bf16"]

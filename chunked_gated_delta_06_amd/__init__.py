@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_chunk_fwd_fused.restype = ctypes.c_int
         L.gdr_fwd_h_o.argtypes = [PP] + [_P] * 11 + [_P]
         L.gdr_fused_recurrent_fwd.argtypes = [PP] + [_P] * 9 + [_P]
+        L.gdr_simple_gla_fwd.argtypes = [PP] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
         L.gdr_segmented_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_segmented_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrSegLayout)]
         L.gdr_chunk_fwd_segmented.argtypes = [PP] + [_P] * 11 + [_P, ctypes.c_size_t, _P]
@@ -112,7 +113,7 @@ def lib() -> ctypes.CDLL:
                      "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
                      "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
                      "gdr_fused_recurrent_fwd", "gdr_fwd_kkt_wy", "gdr_segmented_workspace_bytes",
-                     "gdr_segmented_workspace_layout", "gdr_chunk_fwd_segmented",
+                     "gdr_segmented_workspace_layout", "gdr_chunk_fwd_segmented", "gdr_simple_gla_fwd",
                      "gdr_bwd_workspace_bytes", "gdr_bwd_workspace_layout", "gdr_chunk_bwd",
                      "gdr_bwd_intra", "gdr_bwd_dh", "gdr_bwd_dqkvg"):
             getattr(L, name).restype = ctypes.c_int
@@ -361,6 +362,35 @@ def fused_recurrent_fwd(q, k, v, g, beta, *, scale: float = 1.0, cu_seqlens=None
     st = lib().gdr_fused_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                        _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
                                        _stream(q.device))
+    _raise(st)
+    return o, ht
+
+
+def simple_gla_fwd(q, k, v, g, *, scale: float = 1.0, chunk_size: int = 64, cu_seqlens=None,
+                   initial_state=None, output_final_state: bool = True, use_qk_l2norm_in_kernel: bool = False,
+                   workspace: Optional[torch.Tensor] = None, validate_cu: bool = True):
+    """Simple GLA forward (gdr_simple_gla_fwd): S_t = exp(g_t) S_{t-1} + k_t v_t^T,
+    o_t = scale S_t^T q_t, through the same chunked stages.  Returns (o, ht)."""
+    _need_gpu(q, k, v, g, cu_seqlens, initial_state)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    for name, t in (("g", g), ("initial_state", initial_state)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+    lay = fwd_layout(p)
+    check_tensors(p, q, k, v, g, g if g.dim() == 3 else g[..., 0], cu_seqlens, initial_state, validate_cu)
+    o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    ht = (torch.empty(p.N, p.HV, p.K, p.V, dtype=torch.float32, device=q.device)
+          if output_final_state else None)
+    if workspace is None or workspace.numel() < lay.total:
+        workspace = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=q.device)
+    st = lib().gdr_simple_gla_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(cu_seqlens),
+                                  _ptr(initial_state), _ptr(o), _ptr(ht), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel()), _stream(q.device))
     _raise(st)
     return o, ht
 

@@ -448,6 +448,58 @@ gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const vo
   return hip_status(gdr::launch_recurrent(a, static_cast<hipStream_t>(stream)));
 }
 
+gdr_status gdr_simple_gla_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                              const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  gdr_status st = check(p, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  if (p->gate_per_channel) return GDR_ERR_UNSUPPORTED;
+  if (p->T > 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, cu_seqlens, h0, o, ht, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  const gdr_fwd_layout l = layout_of(*p);
+  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
+
+  Args a = make_args(*p);
+  char* ws = static_cast<char*>(workspace);
+  a.gla = 1;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = nullptr;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.chunk_idx);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.chunk_off);
+  a.w = ws + l.w;
+  a.u = ws + l.u;
+  a.h = ws + l.h;
+  a.v_new = ws + l.v_new;
+  a.kscale = reinterpret_cast<float*>(ws + l.kscale);
+  a.o = o;
+  a.ht = ht;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (cu_seqlens == nullptr && a.NTmax > 0) {
+    a.table_from_dims = 1;
+  } else {
+    e = gdr::launch_chunk_table(a, s);
+  }
+  if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
+  a.table_from_dims = 0;
+  a.gla = 0;   // the scan and output stages see an ordinary w / u pair
+  if (gdr::fwd_h_o_supported(a)) {
+    if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
+  } else {
+    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+    if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+  }
+  return hip_status(e);
+}
+
 gdr_status gdr_segmented_workspace_layout(const gdr_problem* p, gdr_seg_layout* out) {
   if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
   const gdr_status st = check(p, true);

@@ -24,6 +24,10 @@ struct Args {
   // dense batch only: the first stage derives every chunk from B, T and C and
   // writes the chunk table itself (no separate table launch)
   int32_t table_from_dims;
+  // simple GLA (no delta correction): the fused K1 + K2 stage produces
+  // Tm = I, w = 0 and u = v, so the scan and output stages compute
+  // S_t = exp(g_t) S_{t-1} + k_t v_t^T
+  int32_t gla;
   float scale;
   const void* q;
   const void* k;

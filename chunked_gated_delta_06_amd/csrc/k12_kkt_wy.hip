@@ -10,7 +10,9 @@
 // the coverage-matrix page ("FLA operator-kernel correctness testing and
 // coverage matrix", section 2) with the gate folded in.  Same results as the
 // K1 and K2 stages, except that Tm is not written (the forward does not need
-// it; the backward runs the separate stages, whose Tm it reads).
+// it; the backward runs the separate stages, whose Tm it reads).  For simple
+// GLA (no delta correction) it yields Tm = I, w = 0 and u = v, so the same scan
+// and output stages evaluate S_t = exp(g_t) S_{t-1} + k_t v_t^T.
 //
 // gfx950 mapping (4 waves per chunk and value head):
 //  * the key tile is staged token-major in LDS once (coalesced 16-byte loads)
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   float gv = 0.f, bv = 0.f;
   if (wv == 0 && lane < L) {
     gv = a.g[(t0 + lane) * HV + j];
-    bv = a.beta[(t0 + lane) * HV + j];
+    bv = a.gla ? 1.f : a.beta[(t0 + lane) * HV + j];
   }
 
   // ---- key tile (token-major) and the row norms of the raw keys
@@ -129,8 +131,9 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
     const float Gc = wave_incl_scan(gv, lane);
     if (lane < C) {
       sG[lane] = Gc;
-      sB[lane] = bv;
-      sS[lane] = bv * sRn[lane] * __expf(Gc);
+      // simple GLA: u = v (beta = 1 on the chunk's rows) and w = 0
+      sB[lane] = a.gla ? (lane < L ? 1.f : 0.f) : bv;
+      sS[lane] = a.gla ? 0.f : bv * sRn[lane] * __expf(Gc);
     }
     // kscale row of the chunk (the state scan's and the fused output's
     // factors): exp(G_L - G_t) / |k_t|, exp(G_L) and 3 zeros, G_t, 1 / |k_t|
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * g4 + i, cc = 16 * cb + r16;
-        const float val = (cc < r && r < L) ? sB[r] * s[i] * sRn[r] * sRn[cc] * __expf(sG[r] - sG[cc]) : 0.f;
+        const float val = (!a.gla && cc < r && r < L) ? sB[r] * s[i] * sRn[r] * sRn[cc] * __expf(sG[r] - sG[cc]) : 0.f;
         sM[blk(rb, cb) + (4 * g4 + i) * 17 + r16] = val;
       }
     }

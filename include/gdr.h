@@ -223,6 +223,20 @@ gdr_status gdr_fused_recurrent_fwd(const gdr_problem* p, const void* q, const vo
                                    const float* g, const float* beta, const int32_t* cu_seqlens,
                                    const float* h0, void* o, float* ht, void* stream);
 
+/* Simple GLA forward: the same chunked pipeline without the delta correction,
+ *   S_t = exp(g_t) S_{t-1} + k^_t v_t^T,   o_t = scale * S_t^T q^_t,
+ * the variant the coverage-matrix page lists beside the delta rule (section 2,
+ * simple-gla) that shares the state-scan and output stages (chunk_fwd_h,
+ * chunk_fwd_o in fla/ops/common on the contributor guide's layout page).  The
+ * fused K1 + K2 stage produces Tm = I, w = 0 and u = v, then the fused scan +
+ * output stage (or K3 and K4 where it has no instantiation) runs unchanged.
+ * Scalar gate only (GDR_ERR_UNSUPPORTED for a per-channel gate); no beta.
+ * Arguments, layouts and the workspace (gdr_fwd_workspace_bytes) as
+ * gdr_chunk_fwd; keep_states is not read. */
+gdr_status gdr_simple_gla_fwd(const gdr_problem* p, const void* q, const void* k, const void* v,
+                              const float* g, const int32_t* cu_seqlens, const float* h0, void* o,
+                              float* ht, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Segment hand-off on one device: the context-parallel forward of the KCP
  * page ("flash-linear-attention KCP precision-failure root-cause manual",
  * sections on the pre-process and merge kernels and "h and dh cross-rank

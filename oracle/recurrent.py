@@ -324,3 +324,30 @@ def transition(k, g, beta, *, cu_seqlens=None, use_qk_l2norm: bool = False):
                 P = A @ P
             M[n, j] = P
     return M
+
+
+def simple_gla_fwd(q, k, v, g, *, scale: float = 1.0, h0=None, cu_seqlens=None, use_qk_l2norm: bool = False):
+    """Simple GLA, per token (the variant the coverage-matrix page lists beside
+    the delta rule, "FLA operator-kernel correctness testing and coverage
+    matrix", section 2): a scalar per-token gate and no delta correction,
+
+        S_t = exp(g_t) S_{t-1} + k_t v_t^T,    o_t = scale * S_t^T q_t,
+
+    with the same layouts, L2 norm, GVA mapping and sequences as
+    ``recurrent_fwd``.  Returns (o [B,T,HV,V], ht [N,HV,K,V]) in float64."""
+    q, k, v, g, h0 = (_f64(x) for x in (q, k, v, g, h0))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if use_qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
+    q, k = _expand_heads(q, HV), _expand_heads(k, HV)
+    segs = sequences(B, T, cu_seqlens)
+    o = torch.zeros(B, T, HV, V, dtype=torch.float64)
+    ht = torch.zeros(len(segs), HV, K, V, dtype=torch.float64)
+    for n, (b, s, e) in enumerate(segs):
+        S = h0[n].clone() if h0 is not None else torch.zeros(HV, K, V, dtype=torch.float64)
+        for t in range(s, e):
+            S = torch.exp(g[b, t])[:, None, None] * S + k[b, t][:, :, None] * v[b, t][:, None, :]
+            o[b, t] = scale * torch.einsum("hkv,hk->hv", S, q[b, t])
+        ht[n] = S
+    return o, ht

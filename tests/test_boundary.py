@@ -283,3 +283,17 @@ def test_segmented_rejects_before_launch():
                                      None, A, None, None, None, A, ctypes.c_size_t(1 << 40), None) == 2
     assert L.gdr_chunk_fwd_segmented(ctypes.byref(problem()), A, A, A, A, A, A, None, A, None, None, None, A,
                                      ctypes.c_size_t(1 << 40), None) == 4
+
+
+def test_simple_gla_rejects_before_launch():
+    L = gdr.lib()
+    P = ctypes.c_void_p
+    A = P(0x1000)
+    big = ctypes.c_size_t(1 << 40)
+    assert L.gdr_simple_gla_fwd(ctypes.byref(problem(gate_per_channel=1)), A, A, A, A, None, None, A, None, A,
+                                big, None) == 10
+    assert L.gdr_simple_gla_fwd(ctypes.byref(problem()), None, A, A, A, None, None, A, None, A, big, None) == 1
+    assert L.gdr_simple_gla_fwd(ctypes.byref(problem()), A, A, A, A, None, None, A, None, A,
+                                ctypes.c_size_t(16), None) == 7
+    assert L.gdr_simple_gla_fwd(ctypes.byref(problem(chunk_size=16)), A, A, A, A, None, None, A, None, A, big,
+                                None) == 2

@@ -504,3 +504,34 @@ def test_transition_at_zero_gate_is_the_wy_product():
     W = it["W"][0, 0][:12]
     P = np.eye(6) - kk.T @ W
     np.testing.assert_allclose(M[0, 0].numpy(), P, rtol=1e-12, atol=1e-12)
+
+
+def test_simple_gla_matches_its_parallel_form():
+    """The per-token simple GLA oracle against its closed (attention) form,
+    written out independently: o_t = scale [exp(G_t) q_t^T S0 +
+    sum_{s<=t} exp(G_t - G_s) (q_t . k_s) v_s] and
+    ht = exp(G_T) S0 + sum_s exp(G_T - G_s) k_s v_s^T, G the inclusive cumsum,
+    on a varlen GVA batch with an empty sequence."""
+    w = workloads.Workload("gla", B=1, T=0, H=1, HV=2, K=5, V=3, chunk_size=64, dtype="fp32",
+                           l2norm_in_kernel=True, slow_decay=True, scale=0.7)
+    inp = workloads.make_inputs(w, lengths=[7, 0, 11])
+    q, k, v, g, h0, cu = (inp[n] for n in ("q", "k", "v", "g", "h0", "cu_seqlens"))
+    o, ht = recurrent.simple_gla_fwd(q, k, v, g, scale=0.7, h0=h0, cu_seqlens=cu, use_qk_l2norm=True)
+    qd, kd = q.double(), k.double()
+    qn = qd / torch.sqrt((qd * qd).sum(-1, keepdim=True) + 1e-6)
+    kn = kd / torch.sqrt((kd * kd).sum(-1, keepdim=True) + 1e-6)
+    for n in range(3):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for j in range(2):
+            G = torch.cumsum(g[0, s:e, j].double(), 0)
+            L = e - s
+            for t in range(L):
+                ref = torch.exp(G[t]) * (h0[n, j].double().T @ qn[0, s + t, 0])
+                for u in range(t + 1):
+                    ref = ref + torch.exp(G[t] - G[u]) * (qn[0, s + t, 0] @ kn[0, s + u, 0]) * v[0, s + u, j].double()
+                np.testing.assert_allclose(o[0, s + t, j].numpy(), 0.7 * ref.numpy(), rtol=1e-12, atol=1e-12)
+            Gt = G[-1] if L else torch.tensor(0.0, dtype=torch.float64)
+            hr = torch.exp(Gt) * h0[n, j].double()
+            for u in range(L):
+                hr = hr + torch.exp(Gt - G[u]) * torch.outer(kn[0, s + u, 0], v[0, s + u, j].double())
+            np.testing.assert_allclose(ht[n, j].numpy(), hr.numpy(), rtol=1e-12, atol=1e-12)
