@@ -12,7 +12,8 @@ the calls raise.
     dq, dk, dv, dg, dbeta, dh0 = chunk_bwd(q, k, v, g, beta, do, dht, ...)
 
 Shapes follow the library: q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV] (or
-[B,T,HV,K] for a per-channel gate) and beta [B,T,HV] in float32; initial_state
+[B,T,HV,K] for a per-channel gate) and beta [B,T,HV] in float32 (``beta_logits=True``:
+beta holds logits and the kernels apply the sigmoid); initial_state
 [N,HV,K,V] float32; cu_seqlens int32 [N+1] (then B == 1).
 """
 from __future__ import annotations
@@ -40,7 +41,8 @@ class GdrProblem(ctypes.Structure):
                 ("HV", ctypes.c_int64), ("K", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("N", ctypes.c_int64), ("chunk_size", ctypes.c_int32),
                 ("gate_per_channel", ctypes.c_int32), ("use_qk_l2norm", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("keep_states", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("keep_states", ctypes.c_int32),
+                ("beta_logits", ctypes.c_int32)]
 
 
 class GdrFwdLayout(ctypes.Structure):
@@ -147,7 +149,7 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_problem(q, v, g, *, chunk_size=64, cu_seqlens=None, use_qk_l2norm=False, scale=1.0,
-                 N: Optional[int] = None, keep_states: bool = False) -> GdrProblem:
+                 N: Optional[int] = None, keep_states: bool = False, beta_logits: bool = False) -> GdrProblem:
     """Problem description from tensor shapes (no checks beyond the shapes).
     ``keep_states`` makes gdr_chunk_fwd leave h and v_new in its workspace
     (separate scan and output stages instead of the fused one)."""
@@ -157,7 +159,8 @@ def make_problem(q, v, g, *, chunk_size=64, cu_seqlens=None, use_qk_l2norm=False
         N = (len(cu_seqlens) - 1) if cu_seqlens is not None else B
     return GdrProblem(B=B, T=T, H=H, HV=HV, K=K, V=V, N=N, chunk_size=int(chunk_size),
                       gate_per_channel=int(g.dim() == 4), use_qk_l2norm=int(bool(use_qk_l2norm)),
-                      dtype=_dtype_code(q.dtype), scale=float(scale), keep_states=int(bool(keep_states)))
+                      dtype=_dtype_code(q.dtype), scale=float(scale), keep_states=int(bool(keep_states)),
+                      beta_logits=int(bool(beta_logits)))
 
 
 def check_problem(p: GdrProblem) -> None:
@@ -213,7 +216,7 @@ def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_
               initial_state=None, output_final_state: bool = True,
               use_qk_l2norm_in_kernel: bool = False, workspace: Optional[torch.Tensor] = None,
               return_workspace: bool = False, out=None, validate_cu: bool = True,
-              keep_states: Optional[bool] = None):
+              keep_states: Optional[bool] = None, beta_logits: bool = False):
     """Forward of the chunked gated delta rule.  Returns (o, ht) (ht None when
     not requested), plus the workspace tensor when ``return_workspace``.
     ``out=(o, ht)`` supplies the output tensors; ``validate_cu`` checks a host
@@ -231,7 +234,8 @@ def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_
     if keep_states is None:
         keep_states = return_workspace
     p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=keep_states)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=keep_states,
+                     beta_logits=beta_logits)
     lay = fwd_layout(p)
     check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
     if out is not None:
@@ -332,7 +336,7 @@ def fwd_h_o(p, q, k, w, u, g, kscale, chunk_idx, chunk_off, h0, o, ht):
 
 def fused_recurrent_fwd(q, k, v, g, beta, *, scale: float = 1.0, cu_seqlens=None, initial_state=None,
                         output_final_state: bool = True, use_qk_l2norm_in_kernel: bool = False,
-                        out=None, validate_cu: bool = True):
+                        out=None, validate_cu: bool = True, beta_logits: bool = False):
     """Token-by-token forward of the same operator (gdr_fused_recurrent_fwd):
     no chunk table and no workspace, for decoding and short sequences.
     Returns (o, ht) (ht None when not requested); ``out=(o, ht)`` supplies the
@@ -346,7 +350,7 @@ def fused_recurrent_fwd(q, k, v, g, beta, *, scale: float = 1.0, cu_seqlens=None
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     p = make_problem(q, v, g, chunk_size=64, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, beta_logits=beta_logits)
     check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu)
     if out is not None:
         o, ht = out
@@ -403,7 +407,7 @@ def seg_layout(p: GdrProblem) -> GdrSegLayout:
 
 def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, *, scale: float = 1.0, chunk_size: int = 64,
                         initial_state=None, use_qk_l2norm_in_kernel: bool = False,
-                        want_transitions: bool = False, validate_cu: bool = True):
+                        want_transitions: bool = False, validate_cu: bool = True, beta_logits: bool = False):
     """Forward of ONE sequence (q, k [1,T,H,K] ...) split into the segments
     ``cu_seqlens`` bounds, run as the context-parallel scheme on one device
     (gdr_chunk_fwd_segmented): every segment's local end state and transition,
@@ -419,7 +423,7 @@ def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, *, scale: float = 1.0, chu
     if cu_seqlens is None or cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens (int32 segment bounds) is required")
     p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, beta_logits=beta_logits)
     lay = seg_layout(p)
     check_tensors(p, q, k, v, g, beta, cu_seqlens, None, validate_cu)
     _expect("initial_state", initial_state, (1, p.HV, p.K, p.V))
@@ -443,7 +447,8 @@ def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, *, scale: float = 1.0, chu
 def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size: int = 64,
               cu_seqlens=None, initial_state=None, use_qk_l2norm_in_kernel: bool = False,
               workspace: Optional[torch.Tensor] = None, return_workspace: bool = False,
-              out=None, want_dh0: bool = True, validate_cu: bool = True, reuse_forward: bool = False):
+              out=None, want_dh0: bool = True, validate_cu: bool = True, reuse_forward: bool = False,
+              beta_logits: bool = False):
     """Backward of the chunked gated delta rule: gradients of
     sum(o * do) + sum(ht * dht).  Returns (dq, dk, dv, dg, dbeta, dh0) (dh0 None
     when not wanted), plus the workspace when ``return_workspace``.  ``out``
@@ -460,7 +465,8 @@ def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size:
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
     p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=reuse_forward)
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, keep_states=reuse_forward,
+                     beta_logits=beta_logits)
     lay = bwd_layout(p)
     if reuse_forward and (workspace is None or workspace.numel() < lay.total):
         raise ValueError("reuse_forward needs the backward-sized workspace the forward filled")

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       R.t[i] = (idx < C * C / 8) ? ld8(tp + 8 * idx) : frag_zero<T>();
     }
     R.g = (tid < L) ? a.g[(t0 + tid) * HV + j] : 0.f;
-    R.b = (tid < L) ? a.beta[(t0 + tid) * HV + j] : 0.f;
+    R.b = (tid < L) ? beta_value(a.beta[(t0 + tid) * HV + j], a.beta_logits) : 0.f;
   };
   auto fetch_tile = [&](TileRegs& R, int64_t j, int64_t v0) {
     const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
@@ -588,7 +588,8 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
         float db = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) db += sRowB[w * C + lane];
-        a.dbeta[(t0 + lane) * HV + j] = db;
+        // with logits, d/dx sigmoid(x) = beta (1 - beta)
+        a.dbeta[(t0 + lane) * HV + j] = a.beta_logits ? db * sB[lane] * (1.f - sB[lane]) : db;
       }
     }
     lds_barrier();

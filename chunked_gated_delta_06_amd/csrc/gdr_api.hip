@@ -80,6 +80,7 @@ gdr::Args make_args(const gdr_problem& p) {
   a.C = p.chunk_size;
   a.per_channel = p.gate_per_channel ? 1 : 0;
   a.l2norm = p.use_qk_l2norm ? 1 : 0;
+  a.beta_logits = p.beta_logits ? 1 : 0;
   a.dtype = p.dtype;
   a.scale = p.scale;
   return a;
@@ -166,7 +167,7 @@ gdr_status check_bwd(const gdr_problem* p, bool varlen) {
 
 extern "C" {
 
-int gdr_abi_version(void) { return 2; }
+int gdr_abi_version(void) { return 3; }
 
 const char* gdr_status_string(gdr_status s) {
   switch (s) {

@@ -324,6 +324,10 @@ GDR_DEV float group4_sum(float x) {
 
 constexpr float kL2Eps = 1e-6f;
 
+// beta as the operator uses it: the value passed, or its sigmoid when the
+// caller passes logits.
+GDR_DEV float beta_value(float x, int32_t logits) { return logits ? 1.f / (1.f + __expf(-x)) : x; }
+
 // Compute units of one MI355X (8 XCDs x 32).
 constexpr int64_t kNumCUs = 256;
 

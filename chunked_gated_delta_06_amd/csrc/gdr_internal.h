@@ -28,6 +28,8 @@ struct Args {
   // Tm = I, w = 0 and u = v, so the scan and output stages compute
   // S_t = exp(g_t) S_{t-1} + k_t v_t^T
   int32_t gla;
+  // beta holds logits: the kernels use sigmoid(beta) (see beta_value)
+  int32_t beta_logits;
   float scale;
   const void* q;
   const void* k;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   float gv = 0.f, bv = 0.f;
   if (wv == 0 && lane < L) {
     gv = a.g[(t0 + lane) * HV + j];
-    bv = a.gla ? 1.f : a.beta[(t0 + lane) * HV + j];
+    bv = a.gla ? 1.f : beta_value(a.beta[(t0 + lane) * HV + j], a.beta_logits);
   }
 
   // ---- key tile (token-major) and the row norms of the raw keys

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   // keys, so their latency overlaps the kk^T products
   auto fetch_gb = [&](int64_t j, float& gv, float& bv) {
     gv = (!PC && lane < L) ? a.g[(t0 + lane) * HV + j] : 0.f;
-    bv = (lane < L) ? a.beta[(t0 + lane) * HV + j] : 0.f;
+    bv = (lane < L) ? beta_value(a.beta[(t0 + lane) * HV + j], a.beta_logits) : 0.f;
   };
   // (scalar gate: all key fragments at once; a per-channel gate re-reads the
   // keys block by block below and loads them per slab here)

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   float gv = 0.f, bv = 0.f;
   if (wv == 0 && lane < L) {
     if (!PC) gv = a.g[(t0 + lane) * HV + j];
-    bv = a.beta[(t0 + lane) * HV + j];
+    bv = beta_value(a.beta[(t0 + lane) * HV + j], a.beta_logits);
   }
 
   if constexpr (PC) {

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(64) void k5_recurrent(Args a) {
       const int row = lane & (kTB - 1);
       const int64_t t = bos + blk * kTB + (row <= last ? row : last);
       if (lane < kTB) b.gb = PC ? 0.f : a.g[t * HV + j];
-      else if (lane < 2 * kTB) b.gb = a.beta[t * HV + j];
+      else if (lane < 2 * kTB) b.gb = beta_value(a.beta[t * HV + j], a.beta_logits);
       else b.gb = 0.f;
     }
     if constexpr (PC) {

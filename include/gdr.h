@@ -77,6 +77,10 @@ typedef struct {
                                 written).  gdr_chunk_bwd: 1 = take those intermediates
                                 from its workspace instead of recomputing them (see
                                 gdr_chunk_bwd) */
+  int32_t beta_logits;       /* 1: beta holds logits and every kernel uses sigmoid(beta) (the
+                                beta-mode axis of the coverage-matrix page, section 3); the
+                                backward's dbeta is then the gradient with respect to the
+                                logits.  0: beta is used as given */
 } gdr_problem;
 
 /* Offsets (bytes from the workspace base) of the forward intermediates that

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdr_abi_version() == 2
+    assert L.gdr_abi_version() == 3
 
 
 def test_status_strings():

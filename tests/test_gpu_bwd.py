@@ -307,3 +307,33 @@ def test_config_long_bf16_backward():
     torch.cuda.empty_cache()
     ref = oracle_bwd(slice_inputs(inp, heads=heads))
     compare(got, ref, TOL[w.dtype])
+
+
+def test_beta_logits_mode():
+    """beta passed as logits (the kernels apply the sigmoid): forward (fused and
+    separate stages, token by token) and backward against the oracle run on
+    sigmoid(logits); the logits' gradient is dbeta * beta (1 - beta)."""
+    w, inp = mk(B=2, T=150, H=2, HV=4, K=128, V=64, slow=True)
+    x = torch.logit(inp["beta"])                     # the logits the kernels read
+    b = torch.sigmoid(x.double())
+    ref_inp = dict(inp, beta=b)
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "do", "dht", "h0")}
+    xd = dev(x.contiguous())
+    ro, rht = chunked.chunked_fwd(inp["q"], inp["k"], inp["v"], inp["g"], b, h0=inp["h0"], use_qk_l2norm=True,
+                                  chunk_size=64)
+    for keep in (False, True):
+        o, ht = gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], xd, initial_state=d["h0"],
+                              use_qk_l2norm_in_kernel=True, keep_states=keep, beta_logits=True)
+        torch.cuda.synchronize()
+        check(f"o keep={keep}", f64(o), ro, TOL["bf16"])
+        check(f"ht keep={keep}", f64(ht), rht, TOL["bf16"])
+    o, ht = gdr.fused_recurrent_fwd(d["q"], d["k"], d["v"], d["g"], xd, initial_state=d["h0"],
+                                    use_qk_l2norm_in_kernel=True, beta_logits=True)
+    torch.cuda.synchronize()
+    check("o token-by-token", f64(o), ro, TOL["bf16"])
+    grads = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], xd, d["do"], d["dht"], initial_state=d["h0"],
+                          use_qk_l2norm_in_kernel=True, beta_logits=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(ref_inp)
+    ref["dbeta"] = ref["dbeta"] * (b * (1 - b)).numpy()
+    compare({n: f64(t) for n, t in zip(GRADS, grads)}, ref, TOL["bf16"])

@@ -535,3 +535,21 @@ def test_simple_gla_matches_its_parallel_form():
             for u in range(L):
                 hr = hr + torch.exp(Gt - G[u]) * torch.outer(kn[0, s + u, 0], v[0, s + u, j].double())
             np.testing.assert_allclose(ht[n, j].numpy(), hr.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_beta_logits_chain_rule():
+    """The beta-logits mode (beta = sigmoid(x), the beta-mode axis of the
+    coverage-matrix page, section 3) composes the oracle with a sigmoid; the
+    gradient with respect to x is dbeta * beta * (1 - beta).  Pinned by
+    autograd through the per-token oracle with the sigmoid inside."""
+    w = workloads.Workload("bl", B=1, T=13, H=1, HV=2, K=6, V=4, chunk_size=64, dtype="fp32",
+                           l2norm_in_kernel=True, slow_decay=True, backward=True)
+    inp = workloads.make_inputs(w)
+    x = torch.logit(inp["beta"]).double().requires_grad_(True)
+    o, ht = recurrent.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], torch.sigmoid(x), h0=inp["h0"],
+                                    use_qk_l2norm=True)
+    ((o * inp["do"].double()).sum() + (ht * inp["dht"].double()).sum()).backward()
+    b = torch.sigmoid(x.detach())
+    ref = chunked.chunked_bwd(inp["q"], inp["k"], inp["v"], inp["g"], b, inp["do"], inp["dht"], h0=inp["h0"],
+                              use_qk_l2norm=True, chunk_size=8)
+    np.testing.assert_allclose(x.grad.numpy(), ref["dbeta"] * (b * (1 - b)).numpy(), rtol=1e-9, atol=1e-12)
