@@ -38,13 +38,26 @@ size_t elem_size(const gdr_problem& p) { return p.dtype == GDR_BF16 ? 2 : 4; }
 
 // Checks shared by the chunked and the token-by-token paths (chunk_size is
 // not read here).
-gdr_status check_dims(const gdr_problem* p, bool varlen) {
+// Head dims the full forward / backward take by zero padding: any size up to
+// 256 runs as the next instantiated one.
+int64_t pad_dim(int64_t d) { return d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : 256; }
+bool pad_dims_ok(int64_t d) { return d >= 1 && d <= 256; }
+bool needs_pad(const gdr_problem& p) { return !head_dim_ok(p.K) || !head_dim_ok(p.V); }
+gdr_problem padded_problem(const gdr_problem& p) {
+  gdr_problem r = p;
+  r.K = pad_dim(p.K);
+  r.V = pad_dim(p.V);
+  return r;
+}
+
+gdr_status check_dims(const gdr_problem* p, bool varlen, bool allow_pad = false) {
   if (p == nullptr) return GDR_ERR_NULL_ARG;
   if (p->dtype != GDR_BF16 && p->dtype != GDR_FP32) return GDR_ERR_DTYPE;
   if (p->N < 1) return varlen ? GDR_ERR_VARLEN : GDR_ERR_SHAPE;
   if (p->B < 1 || p->T < 0 || p->H < 1 || p->HV < 1) return GDR_ERR_SHAPE;
   if (p->HV % p->H != 0) return GDR_ERR_SHAPE;
-  if (!head_dim_ok(p->K) || !head_dim_ok(p->V)) return GDR_ERR_SHAPE;
+  if (allow_pad ? !(pad_dims_ok(p->K) && pad_dims_ok(p->V)) : !(head_dim_ok(p->K) && head_dim_ok(p->V)))
+    return GDR_ERR_SHAPE;
   if (!std::isfinite(p->scale)) return GDR_ERR_SHAPE;
   if (varlen) {
     if (p->B != 1) return GDR_ERR_VARLEN;
@@ -54,13 +67,14 @@ gdr_status check_dims(const gdr_problem* p, bool varlen) {
   return GDR_OK;
 }
 
-gdr_status check(const gdr_problem* p, bool varlen) {
+gdr_status check(const gdr_problem* p, bool varlen, bool allow_pad = false) {
   if (p == nullptr) return GDR_ERR_NULL_ARG;
   if (p->chunk_size != 32 && p->chunk_size != 64) return GDR_ERR_CHUNK_SIZE;
-  const gdr_status st = check_dims(p, varlen);
+  const gdr_status st = check_dims(p, varlen, allow_pad);
   if (st != GDR_OK) return st;
   // fp32 with a per-channel gate at K = 256, chunk 64 does not fit one workgroup's LDS
-  if (p->dtype == GDR_FP32 && p->gate_per_channel && p->K == 256 && p->chunk_size == 64) return GDR_ERR_SHAPE;
+  if (p->dtype == GDR_FP32 && p->gate_per_channel && pad_dim(p->K) == 256 && p->chunk_size == 64)
+    return GDR_ERR_SHAPE;
   // token indices are int32 in the chunk table
   if (p->B * p->T >= (int64_t(1) << 31)) return GDR_ERR_SHAPE;
   return GDR_OK;
@@ -157,82 +171,53 @@ gdr_seg_layout seg_layout_of(const gdr_problem& p) {
   return l;
 }
 
-gdr_status check_bwd(const gdr_problem* p, bool varlen) {
-  const gdr_status st = check(p, varlen);
+gdr_status check_bwd(const gdr_problem* p, bool varlen, bool allow_pad = false) {
+  const gdr_status st = check(p, varlen, allow_pad);
   if (st != GDR_OK) return st;
-  return gdr::bwd_shape_ok(*p) ? GDR_OK : GDR_ERR_UNSUPPORTED;
+  return gdr::bwd_shape_ok(padded_problem(*p)) ? GDR_OK : GDR_ERR_UNSUPPORTED;
 }
 
-}  // namespace
+// Padded copies of the inputs and outputs of a problem whose head dims are not
+// instantiated, placed after the padded problem's own workspace (base).
+struct PadLayout {
+  size_t q, k, v, g, h0, o, ht, d_o, dht, dq, dk, dv, dh0, total;
+};
 
-extern "C" {
-
-int gdr_abi_version(void) { return 3; }
-
-const char* gdr_status_string(gdr_status s) {
-  switch (s) {
-    case GDR_OK: return "ok";
-    case GDR_ERR_NULL_ARG: return "a required pointer is NULL";
-    case GDR_ERR_CHUNK_SIZE: return "chunk_size must be either 32 or 64";
-    case GDR_ERR_SHAPE: return "unsupported shape (dims < 1, HV % H != 0, or K/V not in {32,64,128,256})";
-    case GDR_ERR_VARLEN: return "cu_seqlens requires B == 1 and N >= 1; a dense batch requires N == B";
-    case GDR_ERR_DTYPE: return "dtype must be GDR_BF16 or GDR_FP32";
-    case GDR_ERR_ALIGNMENT: return "every pointer must be 16-byte aligned";
-    case GDR_ERR_WORKSPACE: return "workspace missing or too small";
-    case GDR_ERR_HIP: return "HIP launch failed";
-    case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
-    case GDR_ERR_UNSUPPORTED:
-      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 needs chunk_size 32)";
-  }
-  return "unknown status";
+PadLayout pad_layout(const gdr_problem& p, size_t base, bool bwd) {
+  PadLayout l;
+  const gdr_problem pp = padded_problem(p);
+  const size_t es = elem_size(p);
+  const size_t BT = (size_t)(p.B * p.T), H = (size_t)p.H, HV = (size_t)p.HV, N = (size_t)p.N;
+  const size_t Kp = (size_t)pp.K, Vp = (size_t)pp.V;
+  size_t off = base;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes);
+    return at;
+  };
+  l.q = take(BT * H * Kp * es);
+  l.k = take(BT * H * Kp * es);
+  l.v = take(BT * HV * Vp * es);
+  l.g = take(p.gate_per_channel ? BT * HV * Kp * sizeof(float) : 0);
+  l.h0 = take(N * HV * Kp * Vp * sizeof(float));
+  l.o = take(bwd ? 0 : BT * HV * Vp * es);
+  l.ht = take(bwd ? 0 : N * HV * Kp * Vp * sizeof(float));
+  l.d_o = take(bwd ? BT * HV * Vp * es : 0);
+  l.dht = take(bwd ? N * HV * Kp * Vp * sizeof(float) : 0);
+  l.dq = take(bwd ? BT * H * Kp * es : 0);
+  l.dk = take(bwd ? BT * H * Kp * es : 0);
+  l.dv = take(bwd ? BT * HV * Vp * es : 0);
+  l.dh0 = take(bwd ? N * HV * Kp * Vp * sizeof(float) : 0);
+  l.total = off;
+  return l;
 }
 
-gdr_status gdr_check_problem(const gdr_problem* p) {
-  if (p == nullptr) return GDR_ERR_NULL_ARG;
-  return check(p, p->N != p->B);
-}
-
-gdr_status gdr_validate_cu_seqlens(const int32_t* cu, int64_t N, int64_t T) {
-  if (cu == nullptr) return GDR_ERR_NULL_ARG;
-  if (N < 1 || cu[0] != 0 || cu[N] != T) return GDR_ERR_CU_SEQLENS;
-  for (int64_t i = 0; i < N; ++i)
-    if (cu[i + 1] < cu[i]) return GDR_ERR_CU_SEQLENS;
-  return GDR_OK;
-}
-
-gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* out) {
-  if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
-  const gdr_status st = check(p, p->N != p->B);
-  if (st != GDR_OK) return st;
-  *out = layout_of(*p);
-  return GDR_OK;
-}
-
-gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes) {
-  gdr_fwd_layout l;
-  const gdr_status st = gdr_fwd_workspace_layout(p, &l);
-  if (st != GDR_OK) return st;
-  if (bytes == nullptr) return GDR_ERR_NULL_ARG;
-  *bytes = l.total;
-  return GDR_OK;
-}
-
-gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
-                         void* workspace, size_t workspace_bytes, void* stream) {
-  gdr_status st = check(p, cu_seqlens != nullptr);
-  if (st != GDR_OK) return st;
-  const bool empty = p->T == 0;
-  if (!empty && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
-    return GDR_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht, workspace};
-  for (const void* ptr : ptrs)
-    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
-  const gdr_fwd_layout l = layout_of(*p);
-  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
-
-  Args a = make_args(*p);
-  char* ws = static_cast<char*>(workspace);
+// The forward's launch sequence for a problem with instantiated head dims;
+// the intermediates go to the workspace at the offsets of l.
+hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht, char* ws,
+                   const gdr_fwd_layout& l, hipStream_t s) {
+  Args a = make_args(p);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -247,12 +232,11 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   a.u = ws + l.u;
   a.h = ws + l.h;
   a.v_new = ws + l.v_new;
-  a.kscale = p->gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.kscale);
+  a.kscale = p.gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.kscale);
   a.o = o;
   a.ht = ht;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (!p->keep_states && gdr::fwd_h_o_preferred(a)) {
+  if (!p.keep_states && gdr::fwd_h_o_preferred(a)) {
     // fused K1 + K2 (Tm stays on chip) and fused scan + output (h and v_new
     // stay on chip); for a dense batch the first writes the chunk table too
     if (cu_seqlens == nullptr && a.NTmax > 0) {
@@ -270,6 +254,148 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
     if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
   }
+  return e;
+}
+
+// The backward's launch sequence for a problem with instantiated head dims.
+hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
+                   void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, char* ws,
+                   const gdr_bwd_layout& l, hipStream_t s) {
+  Args a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.cu = cu_seqlens;
+  a.h0 = h0;
+  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
+  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
+  a.Tm = ws + l.fwd.Tm;
+  a.w = ws + l.fwd.w;
+  a.u = ws + l.fwd.u;
+  a.h = ws + l.fwd.h;
+  a.v_new = ws + l.fwd.v_new;
+  a.kscale = reinterpret_cast<float*>(ws + l.fwd.kscale);
+  a.ht = nullptr;
+  a.d_o = d_o;
+  a.dht = dht;
+  a.de_local = ws + l.de_local;
+  a.qscale = reinterpret_cast<float*>(ws + l.qscale);
+  a.dh = ws + l.dh;
+  a.dh0 = dh0;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  hipError_t e = hipSuccess;
+  if (!p.keep_states) {
+    // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
+    e = gdr::launch_chunk_table(a, s);
+    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    if (e == hipSuccess) e = gdr::launch_wy(a, s);
+    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+  }
+  if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
+  if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
+  if (e == hipSuccess) e = gdr::launch_bwd_dqkvg(a, s);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return 3; }
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL_ARG: return "a required pointer is NULL";
+    case GDR_ERR_CHUNK_SIZE: return "chunk_size must be either 32 or 64";
+    case GDR_ERR_SHAPE:
+      return "unsupported shape (dims < 1, HV % H != 0, K/V outside 1..256, or, for a single stage, "
+             "K/V not in {32,64,128,256})";
+    case GDR_ERR_VARLEN: return "cu_seqlens requires B == 1 and N >= 1; a dense batch requires N == B";
+    case GDR_ERR_DTYPE: return "dtype must be GDR_BF16 or GDR_FP32";
+    case GDR_ERR_ALIGNMENT: return "every pointer must be 16-byte aligned";
+    case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDR_ERR_HIP: return "HIP launch failed";
+    case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
+    case GDR_ERR_UNSUPPORTED:
+      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 needs chunk_size 32)";
+  }
+  return "unknown status";
+}
+
+gdr_status gdr_check_problem(const gdr_problem* p) {
+  if (p == nullptr) return GDR_ERR_NULL_ARG;
+  return check(p, p->N != p->B, true);
+}
+
+gdr_status gdr_validate_cu_seqlens(const int32_t* cu, int64_t N, int64_t T) {
+  if (cu == nullptr) return GDR_ERR_NULL_ARG;
+  if (N < 1 || cu[0] != 0 || cu[N] != T) return GDR_ERR_CU_SEQLENS;
+  for (int64_t i = 0; i < N; ++i)
+    if (cu[i + 1] < cu[i]) return GDR_ERR_CU_SEQLENS;
+  return GDR_OK;
+}
+
+gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* out) {
+  if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
+  const gdr_status st = check(p, p->N != p->B, true);
+  if (st != GDR_OK) return st;
+  *out = layout_of(padded_problem(*p));
+  if (needs_pad(*p)) out->total = pad_layout(*p, out->total, false).total;
+  return GDR_OK;
+}
+
+gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes) {
+  gdr_fwd_layout l;
+  const gdr_status st = gdr_fwd_workspace_layout(p, &l);
+  if (st != GDR_OK) return st;
+  if (bytes == nullptr) return GDR_ERR_NULL_ARG;
+  *bytes = l.total;
+  return GDR_OK;
+}
+
+gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check(p, cu_seqlens != nullptr, true);
+  if (st != GDR_OK) return st;
+  const bool empty = p->T == 0;
+  if (!empty && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  const gdr_problem pp = padded_problem(*p);
+  const gdr_fwd_layout l = layout_of(pp);
+  const bool pad = needs_pad(*p);
+  const PadLayout pl = pad_layout(*p, l.total, false);
+  if (workspace == nullptr || workspace_bytes < (pad ? pl.total : l.total)) return GDR_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!pad) return hip_status(fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, ws, l, s));
+
+  // head dims without an instantiation: zero-padded copies in, padded problem, copies out
+  const int es = (int)elem_size(*p);
+  const int64_t BT = p->B * p->T, H = p->H, HV = p->HV, N = p->N, K = p->K, V = p->V, Kp = pp.K, Vp = pp.V;
+  hipError_t e = gdr::launch_pad(q, ws + pl.q, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(k, ws + pl.k, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(v, ws + pl.v, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && p->gate_per_channel) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
+  if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
+  if (e == hipSuccess)
+    e = fwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v,
+                p->gate_per_channel ? reinterpret_cast<const float*>(ws + pl.g) : g, beta, cu_seqlens,
+                h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.o,
+                ht != nullptr ? reinterpret_cast<float*>(ws + pl.ht) : nullptr, ws, l, s);
+  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.o, o, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && ht != nullptr) e = gdr::launch_unpad(ws + pl.ht, ht, N * HV, K, V, Kp, Vp, 4, s);
   return hip_status(e);
 }
 
@@ -377,8 +503,8 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
 }
 
 int gdr_chunk_fwd_fused(const gdr_problem* p) {
-  if (check(p, p ? p->N != p->B : false) != GDR_OK) return 0;
-  return !p->keep_states && gdr::fwd_h_o_preferred(make_args(*p)) ? 1 : 0;
+  if (check(p, p ? p->N != p->B : false, true) != GDR_OK) return 0;
+  return !p->keep_states && gdr::fwd_h_o_preferred(make_args(padded_problem(*p))) ? 1 : 0;
 }
 
 int gdr_fwd_h_o_supported(const gdr_problem* p) {
@@ -602,9 +728,10 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
 
 gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* out) {
   if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
-  const gdr_status st = check_bwd(p, p->N != p->B);
+  const gdr_status st = check_bwd(p, p->N != p->B, true);
   if (st != GDR_OK) return st;
-  *out = bwd_layout_of(*p);
+  *out = bwd_layout_of(padded_problem(*p));
+  if (needs_pad(*p)) out->total = pad_layout(*p, out->total, true).total;
   return GDR_OK;
 }
 
@@ -621,7 +748,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                          const float* beta, const int32_t* cu_seqlens, const float* h0, const void* d_o,
                          const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  gdr_status st = check_bwd(p, cu_seqlens != nullptr);
+  gdr_status st = check_bwd(p, cu_seqlens != nullptr, true);
   if (st != GDR_OK) return st;
   if (p->T > 0) {
     const void* req[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta};
@@ -631,50 +758,34 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
   for (const void* ptr : ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
-  const gdr_bwd_layout l = bwd_layout_of(*p);
-  if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
-
-  Args a = make_args(*p);
+  const gdr_problem pp = padded_problem(*p);
+  const gdr_bwd_layout l = bwd_layout_of(pp);
+  const bool pad = needs_pad(*p);
+  const PadLayout pl = pad_layout(*p, l.total, true);
+  if (workspace == nullptr || workspace_bytes < (pad ? pl.total : l.total)) return GDR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = g;
-  a.beta = beta;
-  a.cu = cu_seqlens;
-  a.h0 = h0;
-  a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
-  a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
-  a.Tm = ws + l.fwd.Tm;
-  a.w = ws + l.fwd.w;
-  a.u = ws + l.fwd.u;
-  a.h = ws + l.fwd.h;
-  a.v_new = ws + l.fwd.v_new;
-  a.kscale = reinterpret_cast<float*>(ws + l.fwd.kscale);
-  a.ht = nullptr;
-  a.d_o = d_o;
-  a.dht = dht;
-  a.de_local = ws + l.de_local;
-  a.qscale = reinterpret_cast<float*>(ws + l.qscale);
-  a.dh = ws + l.dh;
-  a.dh0 = dh0;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.dg = dg;
-  a.dbeta = dbeta;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (!p->keep_states) {
-    // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
-    e = gdr::launch_chunk_table(a, s);
-    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-    if (e == hipSuccess) e = gdr::launch_wy(a, s);
-    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
-  }
-  if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
-  if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
-  if (e == hipSuccess) e = gdr::launch_bwd_dqkvg(a, s);
+  if (!pad)
+    return hip_status(bwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, ws, l, s));
+
+  // head dims without an instantiation: zero-padded copies in, padded problem, copies out
+  const int es = (int)elem_size(*p);
+  const int64_t BT = p->B * p->T, H = p->H, HV = p->HV, N = p->N, K = p->K, V = p->V, Kp = pp.K, Vp = pp.V;
+  hipError_t e = gdr::launch_pad(q, ws + pl.q, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(k, ws + pl.k, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(v, ws + pl.v, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(d_o, ws + pl.d_o, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
+  if (e == hipSuccess && dht != nullptr) e = gdr::launch_pad(dht, ws + pl.dht, N * HV, K, V, Kp, Vp, 4, s);
+  if (e == hipSuccess)
+    e = bwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v, g, beta, cu_seqlens,
+                h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.d_o,
+                dht != nullptr ? reinterpret_cast<const float*>(ws + pl.dht) : nullptr, ws + pl.dq, ws + pl.dk,
+                ws + pl.dv, dg, dbeta, dh0 != nullptr ? reinterpret_cast<float*>(ws + pl.dh0) : nullptr, ws, l, s);
+  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dq, dq, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dk, dk, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dv, dv, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && dh0 != nullptr) e = gdr::launch_unpad(ws + pl.dh0, dh0, N * HV, K, V, Kp, Vp, 4, s);
   return hip_status(e);
 }
 

@@ -82,6 +82,11 @@ hipError_t launch_bwd_intra(const Args& a, hipStream_t s);
 // segment hand-off: fills and the merge S_in[r + 1] = M[r] S_in[r] + S_ext[r]
 hipError_t launch_identity(int64_t count, int64_t K, float* out, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// zero padding of head dims: M matrices R x C inside Rp x Cp, 2- or 4-byte words
+hipError_t launch_pad(const void* src, void* dst, int64_t M, int64_t R, int64_t C, int64_t Rp, int64_t Cp,
+                      int esize, hipStream_t s);
+hipError_t launch_unpad(const void* src, void* dst, int64_t M, int64_t R, int64_t C, int64_t Rp, int64_t Cp,
+                        int esize, hipStream_t s);
 hipError_t launch_merge(int64_t R, int64_t HV, int64_t K, int64_t V, const float* M, const float* Sext,
                         const float* h0, float* Sin, hipStream_t s);
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s);

@@ -46,8 +46,10 @@ typedef enum {
   GDR_OK = 0,
   GDR_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
   GDR_ERR_CHUNK_SIZE = 2,  /* "chunk_size must be either 32 or 64" */
-  GDR_ERR_SHAPE = 3,       /* a dim < 1 (T < 0), HV % H != 0, K or V not in {32,64,128,256},
-                              B*T >= 2^31, or fp32 + per-channel gate + K = 256 + chunk 64 */
+  GDR_ERR_SHAPE = 3,       /* a dim < 1 (T < 0), HV % H != 0, K or V above 256 (or, for a single
+                              stage, the token-by-token, segmented and simple GLA paths, not in
+                              {32,64,128,256}), B*T >= 2^31, or fp32 + per-channel gate + K > 128
+                              + chunk 64 */
   GDR_ERR_VARLEN = 4,      /* cu_seqlens with B != 1, N < 1, or N != B for a dense batch */
   GDR_ERR_DTYPE = 5,       /* dtype not GDR_BF16 / GDR_FP32 */
   GDR_ERR_ALIGNMENT = 6,   /* a pointer not 16-byte aligned */
@@ -120,6 +122,15 @@ gdr_status gdr_validate_cu_seqlens(const int32_t* cu_host, int64_t N, int64_t T)
 /* Workspace needed by gdr_chunk_fwd (bytes), and where each intermediate sits. */
 gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
+
+/* Head dims: the stages are instantiated for K, V in {32, 64, 128, 256}.
+ * gdr_chunk_fwd and gdr_chunk_bwd also take any K, V in 1..256 (the coverage-
+ * matrix page's non-power-of-two D, section 3): they copy q, k, v (a
+ * per-channel g, h0, d_o, dht) into zero-padded tensors of the next
+ * instantiated size inside the workspace, run the padded problem and copy o, ht
+ * (dq, dk, dv, dh0) back.  Zero features add only exact zeros to every norm and
+ * contraction.  The workspace sizes include the padded copies, and the
+ * intermediates of gdr_fwd_layout / gdr_bwd_layout then have the padded dims. */
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
  * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0 and a

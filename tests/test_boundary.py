@@ -47,8 +47,8 @@ def test_status_strings():
     (dict(chunk_size=16), "chunk_size must be either 32 or 64"),
     (dict(chunk_size=128), "chunk_size must be either 32 or 64"),
     (dict(HV=3), "unsupported shape"),
-    (dict(K=96), "unsupported shape"),
-    (dict(V=48), "unsupported shape"),
+    (dict(K=300), "unsupported shape"),
+    (dict(V=257), "unsupported shape"),
     (dict(H=0), "unsupported shape"),
     (dict(T=-1), "unsupported shape"),
     (dict(dtype=7), "dtype"),
@@ -297,3 +297,28 @@ def test_simple_gla_rejects_before_launch():
                                 ctypes.c_size_t(16), None) == 7
     assert L.gdr_simple_gla_fwd(ctypes.byref(problem(chunk_size=16)), A, A, A, A, None, None, A, None, A, big,
                                 None) == 2
+
+
+def test_padded_head_dims():
+    """Head dims without an instantiation (the coverage-matrix page's D = 60)
+    are taken by the full forward / backward through zero padding: the problem
+    check and the workspace sizes accept them (the workspace grows by the
+    padded copies); a single stage, the token-by-token forward and the
+    segmented / simple GLA paths still reject them."""
+    L = gdr.lib()
+    P = ctypes.c_void_p
+    A = P(0x1000)
+    p60 = problem(K=60, V=60)
+    gdr.check_problem(p60)
+    lay = gdr.fwd_layout(p60)
+    lay64 = gdr.fwd_layout(problem(K=64, V=64))
+    assert lay.total > lay64.total and lay.w == lay64.w
+    assert gdr.bwd_layout(p60).total > gdr.bwd_layout(problem(K=64, V=64)).total
+    assert L.gdr_fwd_kkt_solve(ctypes.byref(p60), A, A, A, A, A, A, A, None) == 3
+    assert L.gdr_fused_recurrent_fwd(ctypes.byref(p60), A, A, A, A, A, None, None, A, None, None) == 3
+    assert L.gdr_simple_gla_fwd(ctypes.byref(p60), A, A, A, A, None, None, A, None, A, ctypes.c_size_t(1 << 40),
+                                None) == 3
+    # the full forward checks the workspace against the padded size
+    st = L.gdr_chunk_fwd(ctypes.byref(p60), A, A, A, A, A, None, None, A, None, A,
+                         ctypes.c_size_t(lay64.total), None)
+    assert st == 7

@@ -463,3 +463,40 @@ def test_config_kda_bf16():
 
 def test_config_long_bf16_forward():
     _run_config("long_bf16", heads=[0, 21])
+
+
+# ------------------------------------------------------------------ head dims without an instantiation
+
+PAD_CASES = [
+    dict(B=2, T=512, H=2, HV=4, K=60, V=60, C=64),                        # the page's GVA shape with D = 60
+    dict(B=1, T=150, H=2, HV=2, K=60, V=100, C=32, pc=True, l2=False, host_l2=True),
+    dict(B=2, T=90, H=1, HV=2, K=60, V=36, C=64, dtype="fp32"),
+    dict(B=1, T=70, H=2, HV=2, K=200, V=24, C=32),
+]
+
+
+@pytest.mark.parametrize("cfg", PAD_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_forward_padded_head_dims(cfg):
+    """Non-power-of-two head dims run zero-padded to the next instantiated size;
+    inputs sit between NaN guard bands (and a per-channel gate between 1e30
+    bands, the page's right-padding trick) so a read past a tensor shows."""
+    w, inp = mk(slow=True, scale=0.75, **cfg)
+    pad = 4096
+
+    def guarded(t, fill):
+        flat = torch.full((t.numel() + 2 * pad,), fill, dtype=t.dtype, device="cuda")
+        flat[pad:pad + t.numel()] = t.reshape(-1).cuda()
+        return flat[pad:pad + t.numel()].view(t.shape)
+
+    q, k, v = (guarded(inp[n], float("nan")) for n in ("q", "k", "v"))
+    g = guarded(inp["g"], 1e30 if w.per_channel_gate else float("nan"))
+    beta, h0 = guarded(inp["beta"], float("nan")), guarded(inp["h0"], float("nan"))
+    o, ht = gdr.chunk_fwd(q, k, v, g, beta, scale=inp["scale"], chunk_size=w.chunk_size, initial_state=h0,
+                          use_qk_l2norm_in_kernel=inp["use_qk_l2norm"])
+    torch.cuda.synchronize()
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[w.dtype])
+    check("ht", f64(ht), rht, TOL[w.dtype])
+    if not w.per_channel_gate:
+        o2, ht2, _ = gpu_fwd(inp, keep_states=True)
+        check("o separate stages", f64(o2), ro, TOL[w.dtype])
