@@ -45,7 +45,8 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x, j = blockIdx.y;
+  const ChunkHead ch = chunk_head(a.HV);
+  const int64_t c = ch.c, j = ch.j;
   if (c >= a.chunk_off[a.N]) return;
   const int64_t t0 = a.chunk_idx[4 * c + 1];
   const int L = a.chunk_idx[4 * c + 2];
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
 
 template <typename T, int C>
 hipError_t launch_k(const Args& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.NTmax, (unsigned)a.HV);
+  const dim3 grid((unsigned)(a.NTmax * a.HV));
   switch (a.K) {
     case 32: hipLaunchKernelGGL((b1_bwd_intra<T, C, 32>), grid, dim3(C * 4), 0, s, a); break;
     case 64: hipLaunchKernelGGL((b1_bwd_intra<T, C, 64>), grid, dim3(C * 4), 0, s, a); break;

@@ -358,4 +358,17 @@ GDR_DEV int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return (bid % 8) * (nblk / 8) + bid / 8;
 }
 
+// Chunk-parallel grids (one workgroup per chunk and head, launched as a 1-D
+// grid of chunks x nheads): the heads of one chunk get consecutive logical
+// indices on one XCD, so the per-token rows of g and beta (all heads of a
+// token share one line) and a GVA group's key rows are fetched into one L2
+// and shared instead of once per XCD.
+struct ChunkHead {
+  int64_t c, j;
+};
+GDR_DEV ChunkHead chunk_head(int64_t nheads) {
+  const int64_t id = xcd_remap(blockIdx.x, (int64_t)gridDim.x);
+  return ChunkHead{id / nheads, id % nheads};
+}
+
 }  // namespace gdr

@@ -61,7 +61,8 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   // below is a scalar branch around whole MFMA sequences
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t c = blockIdx.x, j = blockIdx.y;
+  const ChunkHead ch = chunk_head(a.HV);
+  const int64_t c = ch.c, j = ch.j;
   int64_t t0;
   int L;
   if (a.table_from_dims) {
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
 
 template <typename T, int C, int K>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k12_kkt_wy<T, C, K>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k12_kkt_wy<T, C, K>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

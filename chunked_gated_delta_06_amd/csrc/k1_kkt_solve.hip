@@ -48,7 +48,9 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   __shared__ float sGc[PC ? C * GP : 1];
 
   const int lane = threadIdx.x, r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x;
+  const int64_t NG = PC ? a.HV : a.H;    // workgroups per chunk
+  const ChunkHead ch = chunk_head(NG);
+  const int64_t c = ch.c;
   if (c >= a.chunk_off[a.N]) return;
   const int64_t t0 = a.chunk_idx[4 * c + 1];
   const int L = a.chunk_idx[4 * c + 2];
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   T* __restrict__ Tout = static_cast<T*>(a.Tm);
 
   // value heads handled by this workgroup: the whole GVA group (scalar gate) or one
-  const int64_t jfirst = PC ? (int64_t)blockIdx.y : (int64_t)blockIdx.y * GR;
+  const int64_t jfirst = PC ? ch.j : ch.j * GR;
   const int64_t jcount = PC ? 1 : GR;
   const int64_t h = jfirst / GR;
 
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   const unsigned gy = (unsigned)(PC ? a.HV : a.H);
-  hipLaunchKernelGGL((k1_kkt_solve<T, C, K, PC>), dim3((unsigned)a.NTmax, gy), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((k1_kkt_solve<T, C, K, PC>), dim3((unsigned)(a.NTmax * gy)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

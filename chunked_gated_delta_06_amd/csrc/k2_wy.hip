@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   __shared__ float sGc[PC ? C * GP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x, j = blockIdx.y;
+  const ChunkHead ch = chunk_head(a.HV);
+  const int64_t c = ch.c, j = ch.j;
   if (c >= a.chunk_off[a.N]) return;
   const int64_t t0 = a.chunk_idx[4 * c + 1];
   const int L = a.chunk_idx[4 * c + 2];
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
 
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k2_wy<T, C, K, PC>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k2_wy<T, C, K, PC>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x, j = blockIdx.y;
+  const ChunkHead ch = chunk_head(a.HV);
+  const int64_t c = ch.c, j = ch.j;
   if (c >= a.chunk_off[a.N]) return;
   const int64_t t0 = a.chunk_idx[4 * c + 1];
   const int L = a.chunk_idx[4 * c + 2];
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
 
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k4_fwd_o<T, C, K, PC>), dim3((unsigned)a.NTmax, (unsigned)a.HV), dim3(C * 4), 0, s, a);
+  hipLaunchKernelGGL((k4_fwd_o<T, C, K, PC>), dim3((unsigned)(a.NTmax * a.HV)), dim3(C * 4), 0, s, a);
   return hipGetLastError();
 }
 
