@@ -47,7 +47,8 @@ class GdrProblem(ctypes.Structure):
 
 class GdrFwdLayout(ctypes.Structure):
     _fields_ = [("nt_max", ctypes.c_int64), ("chunk_idx", ctypes.c_size_t),
-                ("chunk_off", ctypes.c_size_t), ("Tm", ctypes.c_size_t), ("w", ctypes.c_size_t),
+                ("chunk_off", ctypes.c_size_t), ("seq_order", ctypes.c_size_t), ("Tm", ctypes.c_size_t),
+                ("w", ctypes.c_size_t),
                 ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
                 ("kscale", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
@@ -276,6 +277,7 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
     return dict(
         chunk_idx=view(lay.chunk_idx, (nt, 4), torch.int32, 4),
         chunk_off=view(lay.chunk_off, (p.N + 1,), torch.int32, 4),
+        seq_order=view(lay.seq_order, (p.N,), torch.int32, 4),
         Tm=view(lay.Tm, (nt, HV, C, C), dt, es),
         w=view(lay.w, (nt, HV, C, K), dt, es),
         u=view(lay.u, (nt, HV, V, C), dt, es),

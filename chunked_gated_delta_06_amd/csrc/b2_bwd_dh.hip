@@ -86,8 +86,8 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
   const int tl = tid - 64 * NWC;
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
   const int64_t nvt = V / BV;
-  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t vt = bid % nvt, j = (bid / nvt) % HV, n = bid / (nvt * HV);
+  const ScanUnit su = scan_unit(a.seq_order, N, HV, nvt);
+  const int64_t vt = su.vt, j = su.j, n = su.n;
   if (n >= N) return;
   const int64_t h = j / (HV / H);
   const int64_t vw = vt * BV;

@@ -111,6 +111,8 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * 4 * sizeof(int32_t));
   l.chunk_off = off;
   off = round_up(off + ((size_t)p.N + 1) * sizeof(int32_t));
+  l.seq_order = off;
+  off = round_up(off + (size_t)p.N * sizeof(int32_t));
   l.Tm = off;
   off = round_up(off + (size_t)nt * HV * C * C * es);
   l.w = off;
@@ -227,6 +229,7 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.h0 = h0;
   a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.chunk_idx);
   a.chunk_off = reinterpret_cast<int32_t*>(ws + l.chunk_off);
+  a.seq_order = (a.cu != nullptr && a.N <= gdr::kMaxOrdered) ? reinterpret_cast<int32_t*>(ws + l.seq_order) : nullptr;
   a.Tm = ws + l.Tm;
   a.w = ws + l.w;
   a.u = ws + l.u;
@@ -272,6 +275,7 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.h0 = h0;
   a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
   a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
+  a.seq_order = (a.cu != nullptr && a.N <= gdr::kMaxOrdered) ? reinterpret_cast<int32_t*>(ws + l.fwd.seq_order) : nullptr;
   a.Tm = ws + l.fwd.Tm;
   a.w = ws + l.fwd.w;
   a.u = ws + l.fwd.u;
@@ -601,6 +605,7 @@ gdr_status gdr_simple_gla_fwd(const gdr_problem* p, const void* q, const void* k
   a.h0 = h0;
   a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.chunk_idx);
   a.chunk_off = reinterpret_cast<int32_t*>(ws + l.chunk_off);
+  a.seq_order = (a.cu != nullptr && a.N <= gdr::kMaxOrdered) ? reinterpret_cast<int32_t*>(ws + l.seq_order) : nullptr;
   a.w = ws + l.w;
   a.u = ws + l.u;
   a.h = ws + l.h;
@@ -675,6 +680,7 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
   a.cu = cu_seqlens;
   a.chunk_idx = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_idx);
   a.chunk_off = reinterpret_cast<int32_t*>(ws + l.fwd.chunk_off);
+  a.seq_order = (a.cu != nullptr && a.N <= gdr::kMaxOrdered) ? reinterpret_cast<int32_t*>(ws + l.fwd.seq_order) : nullptr;
   a.Tm = ws + l.fwd.Tm;
   a.w = ws + l.fwd.w;
   a.u = ws + l.fwd.u;

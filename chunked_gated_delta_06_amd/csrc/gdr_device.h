@@ -358,6 +358,28 @@ GDR_DEV int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return (bid % 8) * (nblk / 8) + bid / 8;
 }
 
+// State-scan grids: the (sequence, value head, value tile) of a hardware
+// block.  Without an order table, xcd_remap keeps a head's value tiles (which
+// share w, k and q) on one XCD.  With seq_order (the sequences by decreasing
+// chunk count), the (sequence, head) units are dealt round-robin over the 8
+// XCDs in that order, each unit's tiles consecutive on its XCD: the longest
+// scans start first and every XCD gets an equal share (longest-first list
+// scheduling, which matters when a varlen batch mixes short and long
+// sequences).
+struct ScanUnit {
+  int64_t n, j, vt;
+};
+GDR_DEV ScanUnit scan_unit(const int32_t* seq_order, int64_t N, int64_t HV, int64_t nvt) {
+  const int64_t nblk = (int64_t)gridDim.x, b = (int64_t)blockIdx.x;
+  if (seq_order == nullptr || (N * HV) % 8 != 0 || nblk != N * HV * nvt) {
+    const int64_t bid = xcd_remap(b, nblk);
+    return ScanUnit{bid / (nvt * HV), (bid / nvt) % HV, bid % nvt};
+  }
+  const int64_t x = b % 8, q = b / 8;
+  const int64_t pos = x + 8 * (q / nvt);   // position in the ordered list of units
+  return ScanUnit{(int64_t)seq_order[pos / HV], pos % HV, q % nvt};
+}
+
 // Chunk-parallel grids (one workgroup per chunk and head, launched as a 1-D
 // grid of chunks x nheads): the heads of one chunk get consecutive logical
 // indices on one XCD, so the per-token rows of g and beta (all heads of a

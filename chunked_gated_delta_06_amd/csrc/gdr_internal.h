@@ -40,6 +40,10 @@ struct Args {
   const float* h0;
   int32_t* chunk_idx;
   int32_t* chunk_off;
+  // varlen batches of at most kMaxOrdered sequences: the sequences by
+  // decreasing chunk count, written by the chunk-table stage and read by the
+  // state scans' workgroup mapping (NULL: natural order)
+  int32_t* seq_order;
   void* Tm;
   void* w;
   void* u;
@@ -63,6 +67,7 @@ struct Args {
 };
 
 int64_t nt_max(const gdr_problem& p);
+constexpr int64_t kMaxOrdered = 1024;
 
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_kkt_solve(const Args& a, hipStream_t s);

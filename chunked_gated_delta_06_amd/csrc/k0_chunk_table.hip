@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void k0_dense(int32_t* __restrict__ idx, int32
 // One workgroup of 1024 threads walks the sequences in tiles of 1024 with a
 // block-wide exclusive scan of the per-sequence chunk counts.
 __global__ __launch_bounds__(1024) void k0_varlen(const int32_t* __restrict__ cu, int32_t* __restrict__ idx,
-                                                  int32_t* __restrict__ off, int64_t N, int32_t C) {
+                                                  int32_t* __restrict__ off, int32_t* __restrict__ order, int64_t N,
+                                                  int32_t C) {
   __shared__ int32_t wave_tot[16];
   __shared__ int32_t tile_base;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -77,6 +78,22 @@ __global__ __launch_bounds__(1024) void k0_varlen(const int32_t* __restrict__ cu
     __syncthreads();
   }
   if (tid == 0) off[N] = tile_base;
+  // sequences by decreasing chunk count (ties by index): rank of sequence n
+  // = the number of sequences that come before it
+  if (order != nullptr && N <= kMaxOrdered) {
+    __shared__ int32_t cnts[kMaxOrdered];
+    if (tid < N) cnts[tid] = (cu[tid + 1] - cu[tid] + C - 1) / C;
+    __syncthreads();
+    if (tid < N) {
+      const int32_t mine = cnts[tid];
+      int32_t rank = 0;
+      for (int m = 0; m < (int)N; ++m) {
+        const int32_t other = cnts[m];
+        rank += (other > mine || (other == mine && m < tid)) ? 1 : 0;
+      }
+      order[rank] = tid;
+    }
+  }
 }
 
 hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
@@ -87,7 +104,8 @@ hipError_t launch_chunk_table(const Args& a, hipStream_t s) {
     hipLaunchKernelGGL(k0_dense, dim3((unsigned)blocks), dim3(256), 0, s, a.chunk_idx, a.chunk_off, a.B, a.T,
                        a.C);
   } else {
-    hipLaunchKernelGGL(k0_varlen, dim3(1), dim3(1024), 0, s, a.cu, a.chunk_idx, a.chunk_off, a.N, a.C);
+    hipLaunchKernelGGL(k0_varlen, dim3(1), dim3(1024), 0, s, a.cu, a.chunk_idx, a.chunk_off, a.seq_order, a.N,
+                       a.C);
   }
   return hipGetLastError();
 }

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
   const int64_t nvt = V / BV;
-  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t vt = bid % nvt, j = (bid / nvt) % HV, n = bid / (nvt * HV);
+  const ScanUnit su = scan_unit(a.seq_order, N, HV, nvt);
+  const int64_t vt = su.vt, j = su.j, n = su.n;
   if (n >= N) return;
   const int64_t h = j / (HV / H);
   const int64_t v0 = vt * BV + 16 * wv;     // this wave's first value column
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   const int tl = tid - 64 * (NWC + NWO);         // loader thread index
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
   const int64_t nvt = V / BV;
-  const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t vt = bid % nvt, j = (bid / nvt) % HV, n = bid / (nvt * HV);
+  const ScanUnit su = scan_unit(a.seq_order, N, HV, nvt);
+  const int64_t vt = su.vt, j = su.j, n = su.n;
   if (n >= N) return;
   const int64_t h = j / (HV / H);
   const int64_t vw = vt * BV;                    // workgroup's first value column

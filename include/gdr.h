@@ -90,6 +90,9 @@ typedef struct {
  * batch and floor(T / C) + N for a varlen batch.
  *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
  *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
+ *   seq_order  int32 [N]           varlen batches of at most 1024 sequences: the sequences
+ *                                  by decreasing chunk count (ties by index), the order in
+ *                                  which the state scans start them; unused otherwise
  *   Tm         dtype [NT_max][HV][C][C]   (I + A)^-1 of each chunk, row-major
  *   w          dtype [NT_max][HV][C][K]   WY keys, token-major
  *   u          dtype [NT_max][HV][V][C]   WY values, transposed per chunk
@@ -103,7 +106,7 @@ typedef struct {
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;
-  size_t chunk_idx, chunk_off, Tm, w, u, h, v_new, kscale, total;
+  size_t chunk_idx, chunk_off, seq_order, Tm, w, u, h, v_new, kscale, total;
 } gdr_fwd_layout;
 
 /* ABI version of this header (bumped on incompatible changes). */

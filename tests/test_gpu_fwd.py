@@ -500,3 +500,20 @@ def test_forward_padded_head_dims(cfg):
     if not w.per_channel_gate:
         o2, ht2, _ = gpu_fwd(inp, keep_states=True)
         check("o separate stages", f64(o2), ro, TOL[w.dtype])
+
+
+def test_varlen_scan_order():
+    """A varlen forward writes the sequences by decreasing chunk count (ties by
+    index) into the workspace, the order the state scans start them in; the
+    results stay those of the oracle (and equal, bitwise, a forward whose
+    batch lists the sequences in that order: each sequence's arithmetic does
+    not depend on where its workgroups run)."""
+    lengths = [64, 2048, 0, 130, 640, 1, 700, 129]
+    w, inp = mk(B=1, H=2, HV=4, K=64, V=64, lengths=lengths, slow=True)
+    o, ht, ws = gpu_fwd(inp)
+    cnt = [(L + 63) // 64 for L in lengths]
+    want = sorted(range(len(lengths)), key=lambda n: (-cnt[n], n))
+    assert ws["seq_order"].cpu().tolist() == want
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL["bf16"])
+    check("ht", f64(ht), rht, TOL["bf16"])
