@@ -137,12 +137,16 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
         sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
       }
       lds_barrier();
+      // chunk-local cumsum down each feature column: all C reads first, the
+      // running sum in registers (same order of additions), then the writes
       for (int d = lane; d < K; d += 64) {
-        float run = 0.f;
-        for (int t = 0; t < C; ++t) {
-          run += sGc[t * GP + d];
-          sGc[t * GP + d] = run;
-        }
+        float col[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t) col[t] = sGc[t * GP + d];
+#pragma unroll
+        for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+        for (int t = 0; t < C; ++t) sGc[t * GP + d] = col[t];
       }
       lds_barrier();
       // gated kk^T, block by block, with a reference row per block

@@ -97,12 +97,16 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
       sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
     }
     lds_barrier();
+    // chunk-local cumsum down each feature column: all C reads first, the
+    // running sum in registers (same order of additions), then the writes
     for (int d = tid; d < K; d += NT) {
-      float run = 0.f;
-      for (int t = 0; t < C; ++t) {
-        run += sGc[t * GP + d];
-        sGc[t * GP + d] = run;
-      }
+      float col[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) col[t] = sGc[t * GP + d];
+#pragma unroll
+      for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+      for (int t = 0; t < C; ++t) sGc[t * GP + d] = col[t];
     }
     lds_barrier();
   }

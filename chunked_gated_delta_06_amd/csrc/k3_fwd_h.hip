@@ -155,13 +155,17 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
         for (int e = 0; e < 4; ++e) sm.gc[t * GP + d4 + e] = gr[e];
       }
       lds_barrier();
+      // chunk-local cumsum down each feature column: all C reads issued
+      // first, the running sum in registers, then the writes
       for (int d = tid; d < K; d += NT) {
-        float run = 0.f;
-        for (int t = 0; t < C; ++t) {
-          run += sm.gc[t * GP + d];
-          sm.gc[t * GP + d] = run;
-        }
-        sm.dec[b][d] = __expf(run);
+        float col[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t) col[t] = sm.gc[t * GP + d];
+#pragma unroll
+        for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+        for (int t = 0; t < C; ++t) sm.gc[t * GP + d] = col[t];
+        sm.dec[b][d] = __expf(col[C - 1]);
       }
       lds_barrier();
     }

@@ -121,12 +121,16 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
       sGc[t * GP + d] = (t < L) ? a.g[((t0 + t) * HV + j) * K + d] : 0.f;
     }
     lds_barrier();
+    // chunk-local cumsum down each feature column: all C reads first, the
+    // running sum in registers (same order of additions), then the writes
     for (int d = tid; d < K; d += 64 * NB) {
-      float run = 0.f;
-      for (int t = 0; t < C; ++t) {
-        run += sGc[t * GP + d];
-        sGc[t * GP + d] = run;
-      }
+      float col[C];
+#pragma unroll
+      for (int t = 0; t < C; ++t) col[t] = sGc[t * GP + d];
+#pragma unroll
+      for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+      for (int t = 0; t < C; ++t) sGc[t * GP + d] = col[t];
     }
   } else {
     if (wv == 0) {
