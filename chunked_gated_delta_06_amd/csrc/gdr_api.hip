@@ -173,10 +173,25 @@ gdr_seg_layout seg_layout_of(const gdr_problem& p) {
   return l;
 }
 
+// The problem the full backward runs: padded head dims, and chunk 32 where the
+// requested chunk 64 has no instantiation of the backward kernels (fp32 with
+// K = 128).  The chunk form is exact at any chunk size, so the gradients are
+// the same up to rounding; a saved-state backward (keep_states) cannot switch,
+// because the forward's intermediates were chunked as requested.
+gdr_problem bwd_problem(const gdr_problem& p) {
+  gdr_problem r = padded_problem(p);
+  if (!gdr::bwd_shape_ok(r) && r.chunk_size == 64 && !r.keep_states) {
+    gdr_problem c32 = r;
+    c32.chunk_size = 32;
+    if (gdr::bwd_shape_ok(c32)) return c32;
+  }
+  return r;
+}
+
 gdr_status check_bwd(const gdr_problem* p, bool varlen, bool allow_pad = false) {
   const gdr_status st = check(p, varlen, allow_pad);
   if (st != GDR_OK) return st;
-  return gdr::bwd_shape_ok(padded_problem(*p)) ? GDR_OK : GDR_ERR_UNSUPPORTED;
+  return gdr::bwd_shape_ok(allow_pad ? bwd_problem(*p) : *p) ? GDR_OK : GDR_ERR_UNSUPPORTED;
 }
 
 // Padded copies of the inputs and outputs of a problem whose head dims are not
@@ -329,7 +344,8 @@ const char* gdr_status_string(gdr_status s) {
     case GDR_ERR_HIP: return "HIP launch failed";
     case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
     case GDR_ERR_UNSUPPORTED:
-      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 needs chunk_size 32)";
+      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 runs at chunk_size 32, "
+             "so a saved-state backward there needs a chunk_size 32 forward)";
   }
   return "unknown status";
 }
@@ -736,7 +752,7 @@ gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* out) {
   if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
   const gdr_status st = check_bwd(p, p->N != p->B, true);
   if (st != GDR_OK) return st;
-  *out = bwd_layout_of(padded_problem(*p));
+  *out = bwd_layout_of(bwd_problem(*p));
   if (needs_pad(*p)) out->total = pad_layout(*p, out->total, true).total;
   return GDR_OK;
 }
@@ -764,7 +780,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, workspace};
   for (const void* ptr : ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
-  const gdr_problem pp = padded_problem(*p);
+  const gdr_problem pp = bwd_problem(*p);
   const gdr_bwd_layout l = bwd_layout_of(pp);
   const bool pad = needs_pad(*p);
   const PadLayout pl = pad_layout(*p, l.total, true);
@@ -772,7 +788,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!pad)
-    return hip_status(bwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, ws, l, s));
+    return hip_status(bwd_run(pp, q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, ws, l, s));
 
   // head dims without an instantiation: zero-padded copies in, padded problem, copies out
   const int es = (int)elem_size(*p);

@@ -56,9 +56,11 @@ typedef enum {
   GDR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than *_workspace_bytes */
   GDR_ERR_HIP = 8,         /* a kernel launch failed */
   GDR_ERR_CU_SEQLENS = 9,  /* gdr_validate_cu_seqlens: bad table */
-  GDR_ERR_UNSUPPORTED = 10 /* backward: per-channel gate, K = 256, or fp32 with K = 128 and
-                              chunk 64 (see gdr_chunk_bwd); gdr_fwd_h_o: a shape without
-                              the fused stage (see gdr_fwd_h_o_supported) */
+  GDR_ERR_UNSUPPORTED = 10 /* backward: per-channel gate, K above 128, or a saved-state
+                              backward for fp32 with K = 128 and chunk 64 (see
+                              gdr_chunk_bwd); gdr_fwd_h_o: a shape without the fused stage
+                              (see gdr_fwd_h_o_supported); gdr_simple_gla_fwd: a per-channel
+                              gate */
 } gdr_status;
 
 typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
@@ -330,9 +332,12 @@ gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* layout
  *   dq, dk  dtype [B,T,H,K]   dv dtype [B,T,HV,V]   dg f32 [B,T,HV]   dbeta f32 [B,T,HV]
  *   dh0   f32 [N,HV,K,V] or NULL       gradient of h0 (not wanted if NULL)
  *   workspace  >= gdr_bwd_workspace_bytes bytes (contents on entry irrelevant).
- * Supported: scalar gate (gate_per_channel = 0), K in {32, 64, 128}, any V;
- * fp32 additionally needs chunk_size 32 when K = 128.  Other problems return
- * GDR_ERR_UNSUPPORTED before any launch.
+ * Supported: scalar gate (gate_per_channel = 0), K up to 128 (padded to 32, 64 or
+ * 128), any V up to 256.  fp32 with K = 128 at chunk_size 64 runs the backward at
+ * chunk 32 (the chunk form is exact at any chunk size; the workspace size
+ * follows); with keep_states that switch is impossible and it returns
+ * GDR_ERR_UNSUPPORTED.  Other problems return GDR_ERR_UNSUPPORTED before any
+ * launch.
  * Saved forward states: with p->keep_states = 1 the recompute is skipped and
  * the forward intermediates are taken from the workspace as they stand, which
  * requires that gdr_chunk_fwd ran with keep_states = 1, the same problem and

@@ -169,7 +169,8 @@ def test_python_wrapper_refuses_cpu_tensors():
     (dict(dtype=gdr.GDR_FP32, K=64, chunk_size=64), True),
     (dict(gate_per_channel=1), False),
     (dict(K=256), False),
-    (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64), False),
+    (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64), True),     # runs at chunk 32 inside
+    (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64, keep_states=1), False),
 ])
 def test_bwd_supported_shapes(kw, ok):
     p = problem(**kw)

@@ -351,3 +351,12 @@ def test_bwd_padded_head_dims(cfg):
     w, inp = mk(slow=True, **cfg)
     got, _, _ = gpu_bwd(inp)
     compare(got, oracle_bwd(inp), TOL[w.dtype])
+
+
+def test_bwd_fp32_k128_chunk64_runs_at_chunk32():
+    """fp32 with K = 128 at chunk 64 has no backward instantiation; the library
+    runs that backward at chunk 32 (the chunk form is exact at any chunk size)
+    and matches the oracle at the fp32 bound."""
+    w, inp = mk(B=1, T=150, H=2, HV=2, K=128, V=64, C=64, dtype="fp32", slow=True)
+    got, _, _ = gpu_bwd(inp)
+    compare(got, oracle_bwd(inp), TOL["fp32"])
