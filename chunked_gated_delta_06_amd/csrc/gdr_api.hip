@@ -716,6 +716,9 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
   Args pre = a;
   pre.h0 = nullptr;
   pre.ht = s_ext;
+  // the warp-specialised scan skips h and v_new when they are not wanted
+  // (the other variants write them to the workspace regardless)
+  if (gdr::fwd_h_states_optional(pre)) pre.h = pre.v_new = nullptr;
   if (e == hipSuccess) e = gdr::launch_fwd_h(pre, s);
   // pre-process 2: every segment's transition, the same scan over the K x K
   // identity with no values (u = 0): S <- diag(e^{G_L}) S - K'^T (W S)
@@ -726,6 +729,7 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
   tr.v_new = ws + l.v_tr;
   tr.h0 = reinterpret_cast<float*>(ws + l.eye);
   tr.ht = trans;
+  if (gdr::fwd_h_states_optional(tr)) tr.h = tr.v_new = nullptr;
   if (e == hipSuccess) e = gdr::launch_zero(ws + l.u_zero, l.h_tr - l.u_zero, s);
   if (e == hipSuccess) e = gdr::launch_identity(N * HV, K, reinterpret_cast<float*>(ws + l.eye), s);
   if (e == hipSuccess) e = gdr::launch_fwd_h(tr, s);

@@ -362,7 +362,9 @@ struct K3S {
   };
 };
 
-template <typename T, int C, int K, int NWC, int NWL, int NWO>
+// KEEP = false: a scan that only needs the end states (the segment hand-off's
+// pre-process) writes neither h nor v_new.
+template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   using Cfg = K3S<T, C, K, NWC, NWL, NWO>;
   using Regs = typename Cfg::Regs;
@@ -507,25 +509,25 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       for (int s0 = 0; s0 < nc; s0 += 3) {
         stage(R1, (s0 + 1) & 1);
         fetch(R1, cl(c_begin + s0 + 4));
-        if constexpr (STG && !OUT) {
+        if constexpr (STG && !OUT && KEEP) {
           if (s0 > 0) drain(s0 - 1);
         }
         lds_barrier();
         stage(R2, (s0 + 2) & 1);
         fetch(R2, cl(c_begin + s0 + 5));
-        if constexpr (STG && !OUT) {
+        if constexpr (STG && !OUT && KEEP) {
           if (s0 < nc) drain(s0);
         }
         lds_barrier();
         stage(R0, (s0 + 3) & 1);
         fetch(R0, cl(c_begin + s0 + 6));
-        if constexpr (STG && !OUT) {
+        if constexpr (STG && !OUT && KEEP) {
           if (s0 + 1 < nc) drain(s0 + 1);
         }
         lds_barrier();
       }
       // the last step's output when the loop ended right after it
-      if constexpr (STG && !OUT) {
+      if constexpr (STG && !OUT && KEEP) {
         if (nc % 3 == 0) drain(nc - 1);
       }
     }
@@ -734,11 +736,11 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     const float gl = sm.ks[b][C];
     // h[c] = S (transposed): staged in LDS for the loaders, or stored directly
     // with feature blocks paired into 16-byte stores
-    if constexpr (STG) {
+    if constexpr (STG && (OUT || KEEP)) {
       T* hs = &sm.hs[b][(16 * wv + r16) * HSP];
 #pragma unroll
       for (int mb = 0; mb < NS; ++mb) st4(hs + 16 * mb + 4 * g4, S[mb]);
-    } else {
+    } else if constexpr (KEEP) {
       T* hp = hbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
       for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
@@ -752,11 +754,11 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
       for (int eb = 0; eb < NE; ++eb) mma(E[eb], wf[ks][eb], nS[ks]);
     // v_new = e (transposed per chunk)
-    if constexpr (STG) {
+    if constexpr (STG && (OUT || KEEP)) {
       T* es = &sm.es[b][(16 * wv + r16) * VSP];
 #pragma unroll
       for (int eb = 0; eb < NE; ++eb) st4(es + 16 * eb + 4 * g4, E[eb]);
-    } else {
+    } else if constexpr (KEEP) {
       T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
       for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
@@ -815,10 +817,19 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       // latency does not shrink with fewer columns, so more workgroups is the
       // only way to use the whole chip on few long sequences
       const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+      const bool keep = a.h != nullptr;
       if (nblk32 < kNumCUs) {
-        hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+        if (keep)
+          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+        else
+          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)),
+                             0, s, a);
       } else {
-        hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+        if (keep)
+          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+        else
+          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s,
+                             a);
       }
       return hipGetLastError();
     }
@@ -893,6 +904,31 @@ hipError_t launch_fused_k(const Args& a, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace {
+// the condition launch_t uses to pick the warp-specialised scan
+template <typename T, int C, int K>
+constexpr bool specialised_fits() {
+  constexpr int NWL = (sizeof(T) == 4 || K == 256) ? 4 : 2;
+  return K3S<T, C, K, 2, NWL>::fits;
+}
+template <typename T, int C>
+bool specialised_k(int64_t K) {
+  switch (K) {
+    case 32: return specialised_fits<T, C, 32>();
+    case 64: return specialised_fits<T, C, 64>();
+    case 128: return specialised_fits<T, C, 128>();
+    case 256: return specialised_fits<T, C, 256>();
+  }
+  return false;
+}
+}  // namespace
+
+bool fwd_h_states_optional(const Args& a) {
+  if (a.per_channel) return false;
+  if (a.dtype == GDR_BF16) return a.C == 32 ? specialised_k<bf16, 32>(a.K) : specialised_k<bf16, 64>(a.K);
+  return a.C == 32 ? specialised_k<float, 32>(a.K) : specialised_k<float, 64>(a.K);
+}
 
 hipError_t launch_fwd_h(const Args& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
