@@ -729,8 +729,13 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
   tr.v_new = ws + l.v_tr;
   tr.h0 = reinterpret_cast<float*>(ws + l.eye);
   tr.ht = trans;
-  if (gdr::fwd_h_states_optional(tr)) tr.h = tr.v_new = nullptr;
-  if (e == hipSuccess) e = gdr::launch_zero(ws + l.u_zero, l.h_tr - l.u_zero, s);
+  const bool tr_states_only = gdr::fwd_h_states_optional(tr);
+  if (tr_states_only) {
+    tr.h = tr.v_new = nullptr;
+    tr.u = nullptr;   // u = 0: neither read nor staged
+  } else if (e == hipSuccess) {
+    e = gdr::launch_zero(ws + l.u_zero, l.h_tr - l.u_zero, s);
+  }
   if (e == hipSuccess) e = gdr::launch_identity(N * HV, K, reinterpret_cast<float*>(ws + l.eye), s);
   if (e == hipSuccess) e = gdr::launch_fwd_h(tr, s);
   // merge along the segments

@@ -75,8 +75,8 @@ hipError_t launch_wy(const Args& a, hipStream_t s);
 // K1 + K2 fused (scalar gate; w, u and kscale, no Tm)
 hipError_t launch_kkt_wy(const Args& a, hipStream_t s);
 hipError_t launch_fwd_h(const Args& a, hipStream_t s);
-// whether launch_fwd_h takes h = v_new = NULL (then writes neither): the
-// scalar-gate warp-specialised scan
+// whether launch_fwd_h takes h = v_new = NULL (then writes neither) and, with
+// them, u = NULL for u = 0: the scalar-gate warp-specialised scan
 bool fwd_h_states_optional(const Args& a);
 // fused state scan + output (no h / v_new); fwd_h_o_supported says whether the
 // shape has an instantiation (scalar gate, staged tiles fit in LDS)

@@ -363,8 +363,9 @@ struct K3S {
 };
 
 // KEEP = false: a scan that only needs the end states (the segment hand-off's
-// pre-process) writes neither h nor v_new.
-template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true>
+// pre-process) writes neither h nor v_new.  ZU: u is zero (the transition
+// scan), so it is neither read nor staged.
+template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   using Cfg = K3S<T, C, K, NWC, NWL, NWO>;
   using Regs = typename Cfg::Regs;
@@ -427,11 +428,13 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
       if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
     }
-    const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
+    if constexpr (!ZU) {
+      const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
-    for (int i = 0; i < NLU; ++i) {
-      const int idx = tl + NTL * i;
-      R.u[i] = ld8(up + 8 * (((NPU % NTL == 0) || idx < NPU) ? idx : 0));
+      for (int i = 0; i < NLU; ++i) {
+        const int idx = tl + NTL * i;
+        R.u[i] = ld8(up + 8 * (((NPU % NTL == 0) || idx < NPU) ? idx : 0));
+      }
     }
     const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
@@ -452,10 +455,12 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       if (tl < C) sm.gq[b][tl] = R.g2;
       else if (tl < 2 * C) sm.rk[b][tl - C] = R.g2;
     }
+    if constexpr (!ZU) {
 #pragma unroll
-    for (int i = 0; i < NLU; ++i) {
-      const int idx = tl + NTL * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
-      if ((NPU % NTL == 0) || idx < NPU) st8(&sm.u[b][v * UP + t8], R.u[i]);
+      for (int i = 0; i < NLU; ++i) {
+        const int idx = tl + NTL * i, v = idx / (C / 8), t8 = (idx % (C / 8)) * 8;
+        if ((NPU % NTL == 0) || idx < NPU) st8(&sm.u[b][v * UP + t8], R.u[i]);
+      }
     }
     if (tl < NKS) *reinterpret_cast<f32x4*>(&sm.ks[b][4 * tl]) = R.ks;
   };
@@ -729,7 +734,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     f32x4 E[NE];
     const T* urow = &sm.u[b][(16 * wv + r16) * UP];
 #pragma unroll
-    for (int eb = 0; eb < NE; ++eb) E[eb] = ld4f(urow + 16 * eb + 4 * g4);
+    for (int eb = 0; eb < NE; ++eb) E[eb] = ZU ? zero4() : ld4f(urow + 16 * eb + 4 * g4);
     f32x4 sc[NE];
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
@@ -817,19 +822,24 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       // latency does not shrink with fewer columns, so more workgroups is the
       // only way to use the whole chip on few long sequences
       const int64_t nblk32 = a.N * a.HV * (a.V / 32);
-      const bool keep = a.h != nullptr;
+      // h == NULL: end states only; u == NULL too: u is zero (transition scan)
+      const bool keep = a.h != nullptr, zu = !keep && a.u == nullptr;
       if (nblk32 < kNumCUs) {
+        const dim3 g((unsigned)(2 * nblk32)), b(64 * (1 + NWL));
         if (keep)
-          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), g, b, 0, s, a);
+        else if (!zu)
+          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false>), g, b, 0, s, a);
         else
-          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)),
-                             0, s, a);
+          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false, true>), g, b, 0, s, a);
       } else {
+        const dim3 g((unsigned)nblk32), b(64 * (2 + NWL));
         if (keep)
-          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), g, b, 0, s, a);
+        else if (!zu)
+          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false>), g, b, 0, s, a);
         else
-          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s,
-                             a);
+          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false, true>), g, b, 0, s, a);
       }
       return hipGetLastError();
     }
