@@ -517,3 +517,16 @@ def test_varlen_scan_order():
     ro, rht = oracle_fwd(inp)
     check("o", f64(o), ro, TOL["bf16"])
     check("ht", f64(ht), rht, TOL["bf16"])
+
+
+def test_padded_head_dims_varlen_without_states():
+    """Zero-padded head dims (K = 60, V = 40) on a varlen batch with empty and
+    one-token sequences, no h0 and no ht requested."""
+    w, inp = mk(B=1, H=2, HV=4, K=60, V=40, lengths=[0, 1, 65, 0, 130], slow=True, h0=False)
+    o, ht = gdr.chunk_fwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                          cu_seqlens=dev(inp["cu_seqlens"]), output_final_state=False,
+                          use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    assert ht is None
+    ro, _ = oracle_fwd(inp, h0=False)
+    check("o", f64(o), ro, TOL["bf16"])

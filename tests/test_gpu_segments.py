@@ -117,3 +117,20 @@ def test_segmented_long_sequence_fast_decay():
                                       h0=S_lo, use_qk_l2norm=True)
     check("o last 256 tokens", f64(o)[:, lo:][:, :, hs], ro.numpy(), 5e-3)
     check("ht", f64(ht)[:, hs], rht.numpy(), 5e-3)
+
+
+def test_one_segment_is_the_single_pass():
+    """One segment: the merge hands h0 through, the transition is that of the
+    whole sequence, and o / ht match the oracle."""
+    w, inp = mk([173], K=64, V=64)
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+    o, ht, states, trans = gdr.chunk_fwd_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                                   scale=inp["scale"], initial_state=d["h0"],
+                                                   use_qk_l2norm_in_kernel=True, want_transitions=True)
+    torch.cuda.synchronize()
+    assert torch.equal(states[0:1], d["h0"])
+    ro, rht = recurrent.recurrent_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], scale=inp["scale"],
+                                      h0=inp["h0"], use_qk_l2norm=True)
+    check("o", f64(o), ro.numpy(), 5e-3)
+    check("ht", f64(ht), rht.numpy(), 5e-3)
+    check("merged end state", f64(states[1:2]), rht.numpy(), 5e-3)
