@@ -43,13 +43,20 @@ __global__ __launch_bounds__(64) void k5_recurrent(Args a) {
   constexpr int NGL = PC ? kTB * K / 4 / 64 : 1;   // per-channel gate quads per lane
   static_assert(NKL >= 1 && (kTB * KV8) % 64 == 0, "key pieces must tile the wave");
 
-  __shared__ __attribute__((aligned(16))) T sK[kTB * K];
-  __shared__ __attribute__((aligned(16))) T sQ[kTB * K];
+  // The state tile (h0 in, ht out) is live only before the first block is
+  // staged and after the last one is computed, so it shares its LDS with the
+  // key / query tiles: a one-wave workgroup then holds about 10 KB of LDS
+  // (K = 128, bf16) and a CU keeps twice as many decoding waves resident.
+  constexpr int kKQBytes = 2 * kTB * K * (int)sizeof(T);
+  constexpr int kSBytes = K * kBV * 4;
+  __shared__ __attribute__((aligned(16))) char sKQS[kKQBytes > kSBytes ? kKQBytes : kSBytes];
+  T* const sK = reinterpret_cast<T*>(sKQS);
+  T* const sQ = sK + kTB * K;
+  float* const sS = reinterpret_cast<float*>(sKQS);
   __shared__ __attribute__((aligned(16))) float sG[PC ? kTB * K : kTB];   // exp(g)
   __shared__ __attribute__((aligned(16))) float sV[kTB * kBV];
   __shared__ __attribute__((aligned(16))) float sO[kTB * kBV];
   __shared__ float sB[kTB], sRk[kTB], sRq[kTB];
-  __shared__ __attribute__((aligned(16))) float sS[K * kBV];   // state tile (h0 in, ht out)
 
   const int lane = threadIdx.x, kq = lane & 3, vc = lane >> 2;
   const int64_t NVT = a.V / kBV;
@@ -69,32 +76,6 @@ __global__ __launch_bounds__(64) void k5_recurrent(Args a) {
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ vp = static_cast<const T*>(a.v);
   T* __restrict__ op = static_cast<T*>(a.o);
-
-  // state: rows kq * KR + i, column v0 + vc, in fp32
-  // h0 / ht pass through an LDS tile so that HBM sees 16-byte accesses (four
-  // consecutive columns per lane, 64 contiguous bytes per row)
-  constexpr int NSL = K * kBV / 4 / 64;   // state quads per lane
-  const int64_t hbase = (n * HV + j) * K * V + v0;
-  float S[KR];
-  if (a.h0 != nullptr) {
-    f32x4 hq4[NSL];
-#pragma unroll
-    for (int m = 0; m < NSL; ++m) {
-      const int idx = lane + 64 * m, r = idx >> 2, c4 = 4 * (idx & 3);
-      hq4[m] = *reinterpret_cast<const f32x4*>(a.h0 + hbase + (int64_t)r * V + c4);
-    }
-#pragma unroll
-    for (int m = 0; m < NSL; ++m) {
-      const int idx = lane + 64 * m, r = idx >> 2, c4 = 4 * (idx & 3);
-      *reinterpret_cast<f32x4*>(sS + r * kBV + c4) = hq4[m];
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < KR; ++i) S[i] = sS[(kq * KR + i) * kBV + vc];
-  } else {
-#pragma unroll
-    for (int i = 0; i < KR; ++i) S[i] = 0.f;
-  }
 
   // ---- block loads into registers (addresses clamped to the sequence; rows
   // past its end are zeroed when staged, never at the load)
@@ -188,9 +169,38 @@ __global__ __launch_bounds__(64) void k5_recurrent(Args a) {
     }
   };
 
+  // the first block's loads are issued before the state's, so a decoding
+  // step pays one memory round trip for both
   const int64_t nblk = (len + kTB - 1) / kTB;
   Blk cur;
   if (nblk > 0) load(0, cur);
+
+  // state: rows kq * KR + i, column v0 + vc, in fp32
+  // h0 / ht pass through an LDS tile so that HBM sees 16-byte accesses (four
+  // consecutive columns per lane, 64 contiguous bytes per row)
+  constexpr int NSL = K * kBV / 4 / 64;   // state quads per lane
+  const int64_t hbase = (n * HV + j) * K * V + v0;
+  float S[KR];
+  if (a.h0 != nullptr) {
+    f32x4 hq4[NSL];
+#pragma unroll
+    for (int m = 0; m < NSL; ++m) {
+      const int idx = lane + 64 * m, r = idx >> 2, c4 = 4 * (idx & 3);
+      hq4[m] = *reinterpret_cast<const f32x4*>(a.h0 + hbase + (int64_t)r * V + c4);
+    }
+#pragma unroll
+    for (int m = 0; m < NSL; ++m) {
+      const int idx = lane + 64 * m, r = idx >> 2, c4 = 4 * (idx & 3);
+      *reinterpret_cast<f32x4*>(sS + r * kBV + c4) = hq4[m];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < KR; ++i) S[i] = sS[(kq * KR + i) * kBV + vc];
+  } else {
+#pragma unroll
+    for (int i = 0; i < KR; ++i) S[i] = 0.f;
+  }
+
   for (int64_t blk = 0; blk < nblk; ++blk) {
     lds_barrier();                 // the previous block's reads of LDS are done
     stage(blk, cur);
