@@ -26,7 +26,11 @@
 //  * w and u as in K2, with the rows of Tm read from LDS in fp32 and scaled by
 //    the per-token factors before the single rounding to the MFMA operand;
 //  * every global load of the chunk (keys, first value pass, g, beta) is
-//    issued before the first wait.
+//    issued before the first wait;
+//  * the value tile shares its LDS with Tm: the rows of Tm go to registers
+//    before the first value pass is staged, so with bf16 and chunk 64 a
+//    workgroup holds 35 KB of LDS and 128 registers per lane, and four
+//    workgroups share a CU (a dense batch's chunks run in whole rounds).
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -35,7 +39,7 @@ namespace gdr {
 namespace {
 
 template <typename T, int C, int K>
-__global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a) {
   constexpr int NW = 4;
   constexpr int NT = 256;
   constexpr int NB = C / 16;                        // 16-row blocks per chunk
@@ -50,10 +54,13 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   constexpr int NKP = (C * CPR + NT - 1) / NT;      // key pieces per thread
   constexpr int NVP = (C * VT / 8 + NT - 1) / NT;   // value pieces per thread and pass
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
-  __shared__ __attribute__((aligned(16))) T sV[C * VP];
   // A, then Tm, in fp32: the lower-triangular blocks only, packed (block
-  // (rb, cb <= rb) at rb (rb + 1) / 2 + cb, rows of 17 floats)
-  __shared__ float sM[NLB * 16 * 17];
+  // (rb, cb <= rb) at rb (rb + 1) / 2 + cb, rows of 17 floats); the value
+  // tile reuses the same bytes once Tm is in registers
+  constexpr int kVBytes = C * VP * (int)sizeof(T), kMBytes = NLB * 16 * 17 * 4;
+  __shared__ __attribute__((aligned(16))) char sVM[kVBytes > kMBytes ? kVBytes : kMBytes];
+  T* const sV = reinterpret_cast<T*>(sVM);
+  float* const sM = reinterpret_cast<float*>(sVM);
   auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * (16 * 17); };
   __shared__ float sS[C], sB[C], sRn[C], sG[C];
 
@@ -246,6 +253,20 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
       }
     }
 
+  // the first value pass goes to LDS now (its registers are free during the w
+  // products); sV shares its LDS with Tm, whose rows every wave has read
+  auto stage_v = [&](int64_t v0) {
+    const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
+    const int vpr = nv / 8;
+#pragma unroll
+    for (int i = 0; i < NVP; ++i) {
+      const int idx = tid + NT * i, t = idx / vpr, d8 = (idx % vpr) * 8;
+      if (idx < C * vpr) st8(&sV[t * VP + d8], vr[i]);
+    }
+  };
+  lds_barrier();
+  stage_v(0);
+
   // w^T = k^T (Tm diag(s))^T, s_t = beta_t exp(G_t) / |k_t|
   auto w_block = [&](int fb, int rb) {
     f32x4 acc = zero4();
@@ -277,12 +298,9 @@ __global__ __launch_bounds__(256) void k12_kkt_wy(Args a) {
   // loads are issued while this one is computed)
   for (int64_t v0 = 0; v0 < V; v0 += VT) {
     const int nv = (V - v0) < VT ? (int)(V - v0) : VT;
-    const int vpr = nv / 8;
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NVP; ++i) {
-      const int idx = tid + NT * i, t = idx / vpr, d8 = (idx % vpr) * 8;
-      if (idx < C * vpr) st8(&sV[t * VP + d8], vr[i]);
+    if (v0 > 0) {
+      lds_barrier();
+      stage_v(v0);
     }
     lds_barrier();
     if (v0 + VT < V) fetch_v(v0 + VT);
