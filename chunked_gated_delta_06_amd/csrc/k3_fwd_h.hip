@@ -844,8 +844,13 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  // per-channel gate (and shapes whose double-buffered tiles exceed LDS):
-  // two waves (32 value columns) per workgroup
+  // per-channel gate: each workgroup forms the chunk's gate cumsum and decayed
+  // keys itself, so four waves (64 value columns) share that work when the
+  // grid still gives every compute unit a workgroup; otherwise (and for
+  // shapes whose double-buffered tiles exceed LDS) two waves, 32 columns
+  if constexpr (PC && K3<T, C, K, PC, 4>::fits) {
+    if (a.V % 64 == 0 && a.N * a.HV * (a.V / 64) >= kNumCUs) return launch_nw<T, C, K, PC, 4>(a, s);
+  }
   return launch_nw<T, C, K, PC, 2>(a, s);
 }
 
