@@ -530,3 +530,16 @@ def test_padded_head_dims_varlen_without_states():
     assert ht is None
     ro, _ = oracle_fwd(inp, h0=False)
     check("o", f64(o), ro, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_per_channel_scan_four_wave_grid(dtype):
+    """Per-channel gate with N * HV * V / 64 = 256: the scan runs four waves
+    (64 value columns) per workgroup. GVA (8 q/k heads, 64 value heads),
+    a ragged tail (T = 77, chunk 32), h0 and slow decay."""
+    w, inp = mk(B=2, T=77, H=8, HV=64, K=64, V=128, C=32, dtype=dtype, pc=True, slow=True, scale=0.5)
+    assert w.B * w.HV * (w.V // 64) >= 256
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[dtype])
+    check("ht", f64(ht), rht, TOL[dtype])
