@@ -43,9 +43,13 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   constexpr int NKP = (C * CPR + NT - 1) / NT;      // key pieces per thread
   constexpr int NVP = (C * VT / 8 + NT - 1) / NT;   // value pieces per thread and pass
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
-  __shared__ __attribute__((aligned(16))) T sV[C * VP];
+  // a per-channel gate's cumsum tile is dead once the decayed key tile is
+  // staged, before the first value pass: the value tile reuses its bytes
+  constexpr int kVBytes = C * VP * (int)sizeof(T), kGBytes = PC ? C * GP * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char sVG[kVBytes > kGBytes ? kVBytes : kGBytes];
+  T* const sV = reinterpret_cast<T*>(sVG);
+  float* const sGc = reinterpret_cast<float*>(sVG);
   __shared__ float sS[C], sB[C], sRn[C];
-  __shared__ float sGc[PC ? C * GP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const ChunkHead ch = chunk_head(a.HV);
