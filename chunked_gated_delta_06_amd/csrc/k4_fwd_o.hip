@@ -43,10 +43,20 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   constexpr int NEP = (VT * C / 8 + NT - 1) / NT;  // 8-element e pieces per thread
   constexpr int NKP = (C * CPR + NT - 1) / NT;     // 8-element key pieces per thread
   __shared__ float sG[C], sRq[C], sRk[C];
-  __shared__ float sGc[PC ? C * GP : 1];
-  __shared__ __attribute__((aligned(16))) T sH[VT * HP];
-  __shared__ __attribute__((aligned(16))) T sE[VT * EP];
-  __shared__ __attribute__((aligned(16))) T sK[C * KP];
+  // Per-channel gate: the key tile and the gate's cumsum tile are dead once
+  // the P^T blocks and the q rows are in registers, so the h^T / e^T tiles of
+  // the value loop reuse their bytes (chunk 32, K = 128: 26 KB of LDS instead
+  // of 48 KB, 4 workgroups per CU instead of 3).  With a scalar gate the tiles
+  // stay apart (sharing measured slower there).
+  constexpr int kKBytes = C * KP * (int)sizeof(T), kGBytes = PC ? C * GP * 4 : 0;
+  constexpr int kHBytes = VT * HP * (int)sizeof(T), kEBytes = VT * EP * (int)sizeof(T);
+  constexpr int kPre = kKBytes + kGBytes, kLoop = kHBytes + kEBytes;
+  constexpr int kBytes = PC ? (kPre > kLoop ? kPre : kLoop) : kLoop + kKBytes;
+  __shared__ __attribute__((aligned(16))) char sBuf[kBytes];
+  T* const sH = reinterpret_cast<T*>(sBuf);
+  T* const sE = reinterpret_cast<T*>(sBuf + kHBytes);
+  T* const sK = reinterpret_cast<T*>(sBuf + (PC ? 0 : kLoop));
+  float* const sGc = reinterpret_cast<float*>(sBuf + kKBytes);   // per-channel gate only
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const ChunkHead ch = chunk_head(a.HV);
@@ -251,6 +261,7 @@ __global__ __launch_bounds__(C * 4) void k4_fwd_o(Args a) {
   const float sc = a.scale;
 
   // ---- O^T = h^T Q^T (scaled) + e^T P^T, 16 value columns at a time
+  if constexpr (PC) lds_barrier();   // every wave's reads of the key and gate tiles are done
   for (int64_t v0 = 0; v0 < V; v0 += VT) {
   stage_tile();
   lds_barrier();
