@@ -41,11 +41,16 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   // touched, so they are stored packed (block (rb, cb <= rb) at index
   // rb (rb + 1) / 2 + cb, rows of 17 floats), which keeps the workgroup's LDS
   // small enough for more single-wave workgroups per CU
-  __shared__ float sM[NLB * 16 * 17];
+  // A per-channel gate's cumsum tile is last read by the kk^T products, and A
+  // is held in registers until then, so A / T reuse the tile's bytes (one
+  // value head per workgroup: the tile is never needed again)
+  constexpr int kMFloats = NLB * 16 * 17, kGFloats = PC ? C * GP : 0;
+  __shared__ float sMG[kMFloats > kGFloats ? kMFloats : kGFloats];
+  float* const sM = sMG;
+  float* const sGc = sMG;   // per-channel gate only
   // block (rb, cb) base; element (i, k) of a block at base + 17 i + k
   auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * (16 * 17); };
   __shared__ float sG[C], sBeta[C], sRn[C];
-  __shared__ float sGc[PC ? C * GP : 1];
 
   const int lane = threadIdx.x, r16 = lane & 15, g4 = lane >> 4;
   const int64_t NG = PC ? a.HV : a.H;    // workgroups per chunk
