@@ -55,13 +55,19 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
   constexpr int NVP = (C * VT / 8 + NT - 1) / NT;   // value pieces per thread and pass
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
   // A, then Tm, in fp32: the lower-triangular blocks only, packed (block
-  // (rb, cb <= rb) at rb (rb + 1) / 2 + cb, rows of 17 floats); the value
+  // (rb, cb <= rb) at rb (rb + 1) / 2 + cb, rows of MP floats); the value
   // tile reuses the same bytes once Tm is in registers
-  constexpr int kVBytes = C * VP * (int)sizeof(T), kMBytes = NLB * 16 * 17 * 4;
+  // Rows of MP = 20 floats keep every row 16-byte aligned (T's rows leave as
+  // 16-byte reads) and make the column-wise writes of a 64-lane block and the
+  // 8-lane phases of those reads bank-conflict free; blocks start MB floats
+  // apart, MB = 16 MP + 16, so the four diagonal blocks inverted side by side
+  // sit on different banks.
+  constexpr int MP = 20, MB = 16 * MP + 16;
+  constexpr int kVBytes = C * VP * (int)sizeof(T), kMBytes = NLB * MB * 4;
   __shared__ __attribute__((aligned(16))) char sVM[kVBytes > kMBytes ? kVBytes : kMBytes];
   T* const sV = reinterpret_cast<T*>(sVM);
   float* const sM = reinterpret_cast<float*>(sVM);
-  auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * (16 * 17); };
+  auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * MB; };
   __shared__ float sS[C], sB[C], sRn[C], sG[C];
 
   // the wave index is read into a scalar register, so every per-wave choice
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rb + 4 * g4 + i, cc = 16 * cb + r16;
         const float val = (!a.gla && cc < r && r < L) ? sB[r] * s[i] * sRn[r] * sRn[cc] * __expf(sG[r] - sG[cc]) : 0.f;
-        sM[blk(rb, cb) + (4 * g4 + i) * 17 + r16] = val;
+        sM[blk(rb, cb) + (4 * g4 + i) * MP + r16] = val;
       }
     }
   }
@@ -190,14 +196,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
       for (int r = 0; r < 16; ++r) {
         float s = (r == r16) ? 1.f : 0.f;
 #pragma unroll
-        for (int q = 0; q < r; ++q) s -= Md[r * 17 + q] * x[q];
+        for (int q = 0; q < r; ++q) s -= Md[r * MP + q] * x[q];
         x[r] = s;
       }
     }
     lds_barrier();
     if (act) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Md[r * 17 + r16] = x[r];
+      for (int r = 0; r < 16; ++r) Md[r * MP + r16] = x[r];
     }
     lds_barrier();
   }
@@ -214,15 +220,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
         float av[4], bvv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          av[s] = sM[blk(ib, mb) + r16 * 17 + 4 * g4 + s];
-          bvv[s] = sM[blk(mb, jb) + (4 * g4 + s) * 17 + r16];
+          av[s] = sM[blk(ib, mb) + r16 * MP + 4 * g4 + s];
+          bvv[s] = sM[blk(mb, jb) + (4 * g4 + s) * MP + r16];
         }
         mma16_f32(X, av, bvv);
       }
       float tv[4], xv[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        tv[s] = sM[blk(ib, ib) + r16 * 17 + 4 * g4 + s];
+        tv[s] = sM[blk(ib, ib) + r16 * MP + 4 * g4 + s];
         xv[s] = X[s];
       }
       f32x4 Y = zero4();
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
     lds_barrier();
     if (jb < ib) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sM[blk(ib, jb) + (4 * g4 + i) * 17 + r16] = res[i];
+      for (int i = 0; i < 4; ++i) sM[blk(ib, jb) + (4 * g4 + i) * MP + r16] = res[i];
     }
     lds_barrier();
   }
@@ -246,10 +252,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
     for (int ks = 0; ks < KSC; ++ks) {
       const int cb = 2 * ks + (g4 >> 1);
       const int cbs = cb <= rb ? cb : rb;
+      const float* src = sM + blk(rb, cbs) + r16 * MP + 8 * (g4 & 1);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(src), x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = sM[blk(rb, cbs) + r16 * 17 + 8 * (g4 & 1) + e];
-        tf[rb][ks][e] = cb <= rb ? x : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        tf[rb][ks][e] = cb <= rb ? x0[e] : 0.f;
+        tf[rb][ks][4 + e] = cb <= rb ? x1[e] : 0.f;
       }
     }
 
