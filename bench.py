@@ -6,19 +6,32 @@ K2 WY recompute, K3 state scan, K4 output) over one batch of the workload,
 inputs resident in HBM; for a workload with a backward (long_bf16) a step is
 the forward, keeping its intermediates, plus the full backward reading them
 (B1 de_local, B2 reverse state-gradient scan, B3 fused gradients); the record
-also times the alternative that recomputes K0-K3 in the backward.  Prints one JSON line:
+also times the alternative that recomputes K0-K3 in the backward.
 
-  value        tokens/s of one step (B*T / seconds per step)
-  roofline     the dominant kernel's algorithmic HBM bytes per launch / its
-               average launch time (HIP events on the launch stream), against
-               8 TB/s; traffic = measured HBM bytes per launch from rocprofv3
-               counters (profiles/), null when the kernel changed since
-  cpu_baseline the float64 per-token oracle timed on a bounded sample
-  backward     (default run) the same measurement for the long-sequence
-               forward + backward workload
+Timing: HIP events recorded on the launch stream around every whole call
+(gdr_chunk_fwd, or gdr_chunk_fwd + gdr_chunk_bwd), after the warm-up calls;
+the median over the timed calls is the step time.  The wall clock around the
+same timed calls (one synchronisation on each side) is kept beside it.
 
-Each leg first checks a sample of its own output against the oracle and the
-bench refuses to report numbers when that check fails.
+Prints one JSON line for the dense GDN workload (the headline) with, for every
+workload of the default run, a record under "configs":
+
+  value / ms_per_step   tokens/s and the median step time (events)
+  hbm_frac_four_stage   the four-stage byte model (every K1..K4 tensor once
+                        written and once per reading stage) / time / 8 TB/s
+  hbm_frac_moved        the bytes the timed path's own stages move (same
+                        rules, only the stages that run) / time / 8 TB/s
+  hbm_frac_operator_min operator inputs and outputs only / time / 8 TB/s
+  mfma_frac             matrix-product FLOPs of the timed stages / time /
+                        dense MFMA peak of the dtype (bf16 2.5 PF, fp32 157.3 TF)
+  roofline              the dominant kernel's algorithmic HBM bytes per launch /
+                        its average launch time (events), against 8 TB/s;
+                        traffic = measured HBM bytes per launch from rocprofv3
+                        counters (profiles/), null when the kernel changed since
+  cpu_baseline          the float64 per-token oracle timed on a bounded sample
+
+Each record first checks a sample of its own output against the oracle and
+the bench refuses to report numbers when that check fails.
 """
 import argparse
 import ctypes
@@ -32,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -58,6 +72,56 @@ def stage_bytes_per_token_head(w, T_seq):
         # fused scan + output: w, u, k, q, token factors -> o, ht (h and v_new stay on chip)
         "fwd_h_o": e * K + e * V + r * K * e + r * K * e + kf_row + e * V + 8 * K * V / T_seq,
     }
+
+
+def four_stage_bytes_per_token_head(w, T_seq):
+    """The four-stage byte model of the chunk method (K1 kk^T + inverse, K2
+    WY, K3 state scan, K4 output), per (token, value head): every tensor the
+    four stages materialise is counted once when written and once per reading
+    stage, at the fixed storage dtypes (T, w, u, v_new, h in the input dtype;
+    g, beta fp32; h0 / ht fp32).  It is independent of how this library fuses
+    the stages."""
+    e = 2 if w.dtype == "bf16" else 4
+    r = w.H / w.HV
+    K, V, C = w.K, w.V, w.chunk_size
+    gb = 4 * K if w.per_channel_gate else 4
+    k1 = r * K * e + gb + 4 + e * C
+    k2 = r * K * e + V * e + e * C + gb + 4 + e * K + e * V
+    k3 = e * K + e * V + r * K * e + gb + e * V + e * K * V / C + 8 * K * V / T_seq
+    k4 = 2 * r * K * e + gb + e * V + e * K * V / C + V * e
+    return k1 + k2 + k3 + k4
+
+
+def operator_min_bytes_per_token_head(w, T_seq, backward=False):
+    """The operator's own inputs and outputs only, per (token, value head):
+    q, k (shared by a GVA group), v, g, beta, o, h0 / ht; the backward adds
+    do, dht and the gradients dq, dk, dv, dg, dbeta, dh0."""
+    e = 2 if w.dtype == "bf16" else 4
+    r = w.H / w.HV
+    K, V = w.K, w.V
+    gb = 4 * K if w.per_channel_gate else 4
+    fwd = 2 * r * K * e + 2 * V * e + gb + 4 + 8 * K * V / T_seq
+    if not backward:
+        return fwd
+    # inputs q, k, v, g, beta, do, h0, dht; outputs dq, dk, dv, dg, dbeta, dh0
+    return 2 * r * K * e + V * e + gb + 4 + V * e + 2 * r * K * e + V * e + gb + 4 + 12 * K * V / T_seq
+
+
+def flops_per_token_head(w, part):
+    """Matrix-product FLOPs per (token, value head) (2 per multiply-add,
+    causal C x C products at half, the triangular inverse at C^2 / 3):
+      forward  kk^T CK, inverse C^2/3, W CK, U CV, E = U - W S 2KV, state
+               update 2KV, Q S0 2KV, Q K^T CK, P E CV
+               = 3CK + 2CV + 6KV + C^2/3
+      bwd      (B1..B3, the backward's own stages) P CK + P^T dO CV (B1);
+               K dS, Q^T dO, W^T dE 6KV (B2); B3: P CK, P^T dO CV, K dS1 2KV,
+               Y = T^T dE CV, dQg / T^T dW / dKt 6KV, dP CV, dA CV, and five
+               C x C by C x K products (D K, D^T Q, kk^T, Dk K, Dk^T K) 5CK
+               = 7CK + 5CV + 14KV"""
+    K, V, C = w.K, w.V, w.chunk_size
+    fwd = 3 * C * K + 2 * C * V + 6 * K * V + C * C / 3
+    bwd = 7 * C * K + 5 * C * V + 14 * K * V
+    return {"forward": fwd, "bwd": bwd}[part]
 
 
 def bwd_stage_bytes_per_token_head(w, T_seq):
@@ -172,27 +236,38 @@ def cpu_baseline_bwd(w, inp, T=4096, heads=(0, 21)):
                       f"head(s) {hs} ({spent:.1f} s), rate scaled to all {w.HV} value heads"}
 
 
-def parity_gate(w, inp, o, ht):
-    """Sequence 0 (all heads) of the GPU output against the chunked oracle."""
-    import torch
+def parity_gate(w, inp, o, ht, max_tokens=2048, ht_heads=(0, -1)):
+    """The first sequence against the chunked oracle: o on its first
+    ``max_tokens`` tokens for every value head, and ht after the whole
+    sequence (all heads when the sequence is no longer than max_tokens,
+    otherwise the value heads ``ht_heads``, which needs H == HV)."""
     from oracle import chunked
     from oracle.metrics import err_ratio
-    if inp["cu_seqlens"] is None:
-        sl = slice(0, 1)
-        sub = {k: (inp[k][sl] if inp.get(k) is not None else None) for k in ("q", "k", "v", "g", "beta", "h0")}
-        go, ght = o[sl], (ht[sl] if ht is not None else None)
-    else:
-        e = int(inp["cu_seqlens"][1])
-        sub = {k: inp[k][:, :e] for k in ("q", "k", "v", "g", "beta")}
-        sub["h0"] = inp["h0"][0:1] if inp["h0"] is not None else None
-        go, ght = o[:, :e], (ht[0:1] if ht is not None else None)
-    ro, rht = chunked.chunked_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], scale=inp["scale"],
-                                  h0=sub["h0"], use_qk_l2norm=inp["use_qk_l2norm"],
-                                  chunk_size=inp["chunk_size"])
-    tol = 5e-3 if w.dtype == "bf16" else 1e-4
-    eo = err_ratio(go, ro)
-    eh = err_ratio(ght, rht) if ght is not None else 0.0
-    return eo, eh, tol
+    cu = inp["cu_seqlens"]
+    s0, e0 = (0, inp["T"]) if cu is None else (int(cu[0]), int(cu[1]))
+    Tp = min(e0 - s0, max_tokens)
+
+    def run(t_end, heads):
+        d = {}
+        for n in ("q", "k", "v", "g", "beta"):
+            x = inp[n][0:1, s0:t_end]
+            d[n] = x if heads is None else x[:, :, heads].contiguous()
+        h0 = inp["h0"]
+        d["h0"] = None if h0 is None else (h0[0:1] if heads is None else h0[0:1, heads].contiguous())
+        return chunked.chunked_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp["scale"], h0=d["h0"],
+                                   use_qk_l2norm=inp["use_qk_l2norm"], chunk_size=inp["chunk_size"])
+
+    ro, rht = run(s0 + Tp, None)
+    eo = err_ratio(o[0:1, s0:s0 + Tp], ro)
+    label_o = f"o (sequence 0, first {Tp} tokens, all heads)"
+    if ht is None:
+        return {label_o: eo}
+    if Tp == e0 - s0:
+        return {label_o: eo, "ht (sequence 0, all heads)": err_ratio(ht[0:1], rht)}
+    assert w.H == w.HV, "a head subset of the final state needs H == HV"
+    hs = sorted({h % w.HV for h in ht_heads})
+    _, rht = run(e0, hs)
+    return {label_o: eo, f"ht (sequence 0, heads {hs})": err_ratio(ht[0:1, hs], rht)}
 
 
 def event_stage_ms(stream, stages, reps):
@@ -218,16 +293,49 @@ def event_stage_ms(stream, stages, reps):
     return {n: acc[n] / reps for n in names}
 
 
-def wall_ms_per_step(step, warmup, steps):
+def timed_calls(step, warmup, steps, stream):
+    """Run ``warmup`` untimed steps, then ``steps`` timed steps with HIP events
+    recorded on the launch stream around each whole step.  Returns the median
+    and mean event time per step and the wall-clock time per step over the
+    timed steps (one synchronisation on each side), in milliseconds."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for a, b in evs:
+        a.record(stream)
         step()
+        b.record(stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    n = len(ms)
+    med = ms[n // 2] if n % 2 else 0.5 * (ms[n // 2 - 1] + ms[n // 2])
+    return {"median_ms": med, "mean_event_ms": sum(ms) / n, "wall_ms": wall, "min_ms": ms[0], "max_ms": ms[-1]}
+
+
+def fractions(w, T_seq, units, ms, moved_per_unit, backward):
+    """HBM and MFMA fractions of one step of ``ms`` milliseconds over ``units``
+    (token, value head) pairs."""
+    sec = ms * 1e-3
+    out = {}
+    if not backward:
+        four = four_stage_bytes_per_token_head(w, T_seq)
+        out["four_stage_bytes"] = four * units
+        out["hbm_frac_four_stage"] = four * units / sec / (PEAK_HBM_GBS * 1e9)
+        flops = flops_per_token_head(w, "forward") * units
+    else:
+        flops = (flops_per_token_head(w, "forward") + flops_per_token_head(w, "bwd")) * units
+    out["moved_bytes"] = moved_per_unit * units
+    out["hbm_frac_moved"] = moved_per_unit * units / sec / (PEAK_HBM_GBS * 1e9)
+    omin = operator_min_bytes_per_token_head(w, T_seq, backward)
+    out["operator_min_bytes"] = omin * units
+    out["hbm_frac_operator_min"] = omin * units / sec / (PEAK_HBM_GBS * 1e9)
+    out["flops"] = flops
+    out["mfma_frac"] = flops / sec / PEAK_MFMA_FLOPS[w.dtype]
+    return out
 
 
 def roofline(per_unit, avg_ms, units, workload, stages):
@@ -291,9 +399,9 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         parity = {**{f"{n} (first 2048 tokens, heads 0 and 21)": v for n, v in errs.items()}, "tol": tol}
         ok = all(v <= tol for v in errs.values())
     else:
-        eo, eh, tol = parity_gate(w, inp, o.cpu(), ht.cpu())
-        parity = {"o": eo, "ht": eh, "tol": tol}
-        ok = eo <= tol and eh <= tol
+        tol = 5e-3 if w.dtype == "bf16" else 1e-4
+        parity = {**parity_gate(w, inp, o.cpu(), ht.cpu()), "tol": tol}
+        ok = all(v <= tol for k, v in parity.items() if k != "tol")
     print(f"parity gate ({label}): " + ", ".join(f"{k}={v:.2e}" for k, v in parity.items()),
           file=sys.stderr, flush=True)
     if not ok:
@@ -340,8 +448,9 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         check_st(L.gdr_chunk_fwd(*fwd_args))
         check_st(L.gdr_chunk_bwd(*bwd_args))
 
-    ms_per_step = wall_ms_per_step(step, warmup, steps)
-    recompute_ms = wall_ms_per_step(step_recompute, warmup, steps) if backward else None
+    timing = timed_calls(step, warmup, steps, stream)
+    ms_per_step = timing["median_ms"]
+    recompute = timed_calls(step_recompute, warmup, steps, stream) if backward else None
     tokens = inp["B"] * inp["T"]
     value = tokens / (ms_per_step * 1e-3)
 
@@ -378,10 +487,12 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     T_seq = inp["B"] * inp["T"] / inp["N"]
     units = tokens * w.HV
     per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq).items() if k in fstages}
-    fwd_total_ms = sum(fwd_ms.values())
     rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
-           "stage_ms": {"forward": fwd_ms}, "parity": parity,
-           "forward_hbm_frac": sum(per_unit.values()) * units / (fwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+           "timing": {**timing, "what": "HIP events around each whole call on the launch stream; "
+                                        "ms_per_step = median_ms; wall_ms = wall clock per step"},
+           "stage_ms": {"forward": fwd_ms}, "parity": parity}
+    if not backward:
+        rec.update(fractions(w, T_seq, units, ms_per_step, sum(per_unit.values()), False))
     rec["roofline"] = roofline(per_unit, fwd_ms, units, w.name, list(per_unit))
     if backward:
         bv = gdr.bwd_workspace_views(p, bws)
@@ -402,7 +513,8 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         bwd_total_ms = sum(bwd_ms.values())
         rec["backward_hbm_frac"] = sum(bper.values()) * units / (bwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
         rec["backward_ms"] = bwd_total_ms
-        rec["recompute_ms_per_step"] = recompute_ms
+        rec["recompute_ms_per_step"] = recompute["median_ms"]
+        rec.update(fractions(w, T_seq, units, ms_per_step, sum(per_unit.values()) + sum(bper.values()), True))
         rec["step"] = ("forward with its intermediates kept (separate stages) + backward reading them; "
                        "recompute_ms_per_step: fused forward + backward that recomputes K0-K3")
         # the dominant kernel of a forward + backward step is taken among the
@@ -465,13 +577,14 @@ def measure_decode(gdr, w, steps, warmup):
         if st != 0:
             raise RuntimeError(L.gdr_status_string(st).decode())
 
-    ms_per_step = wall_ms_per_step(step, warmup, steps)
+    timing = timed_calls(step, warmup, steps, stream)
+    ms_per_step = timing["median_ms"]
     ev_ms = event_stage_ms(stream, {"recurrent": step}, max(5, min(steps, 50)))
     tokens = inp["B"] * inp["T"]
     units = tokens * w.HV
     per_unit = {"recurrent": decode_bytes_per_token_head(w)}
     rec = {"value": tokens / (ms_per_step * 1e-3), "ms_per_step": ms_per_step, "tokens": tokens,
-           "stage_ms": {"forward": ev_ms}, "parity": parity,
+           "timing": timing, "stage_ms": {"forward": ev_ms}, "parity": parity,
            "roofline": roofline(per_unit, ev_ms, units, w.name, ["recurrent"])}
     return rec, inp
 
@@ -536,8 +649,9 @@ def measure_segmented(gdr, w, R, steps, warmup):
         if st != 0:
             raise RuntimeError(L.gdr_status_string(st).decode())
 
-    ms = wall_ms_per_step(seg_step, warmup, steps)
-    ms1 = wall_ms_per_step(one_step, warmup, steps)
+    stream = torch.cuda.current_stream(dev)
+    ms = timed_calls(seg_step, warmup, steps, stream)["median_ms"]
+    ms1 = timed_calls(one_step, warmup, steps, stream)["median_ms"]
     return {"workload": w.name, "pass": f"forward, one sequence as {R} segments (segment hand-off on one GPU)",
             "B": 1, "T": T, "H": w.H, "HV": w.HV, "K": w.K, "V": w.V, "chunk_size": w.chunk_size, "segments": R,
             "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "single_pass_ms_per_step": ms1,
@@ -584,10 +698,22 @@ def measure_simple_gla(gdr, w, steps, warmup):
         if st != 0:
             raise RuntimeError(L.gdr_status_string(st).decode())
 
-    ms = wall_ms_per_step(step, warmup, steps)
+    ms = timed_calls(step, warmup, steps, torch.cuda.current_stream(dev))["median_ms"]
     tokens = inp["B"] * inp["T"]
     return {"workload": w.name, "pass": "simple GLA forward (same chunked stages, w = 0, u = v)",
             "tokens_per_s": tokens / (ms * 1e-3), "ms_per_step": ms, "parity": parity}
+
+
+def config_record(w, inp, rec):
+    """One workload's record: its dimensions, then the measured fields."""
+    return {"workload": w.name,
+            "pass": ("forward+backward" if w.backward else
+                     "token-by-token forward (one decoding step)" if w.T == 1 else "forward"),
+            "B": inp["B"], "T": inp["T"], "N": inp["N"], "H": w.H, "HV": w.HV, "K": w.K, "V": w.V,
+            "chunk_size": w.chunk_size, "dtype": w.dtype,
+            "gate": "per-channel" if w.per_channel_gate else "scalar",
+            "tokens_per_s": rec["value"], "ms_per_step": rec["ms_per_step"],
+            **{k: v for k, v in rec.items() if k not in ("value", "ms_per_step")}}
 
 
 def workloads_inputs(w):
@@ -658,27 +784,27 @@ def main():
     del inp
     if not w.backward and not args.no_backward and w.T > 1 and not w.per_channel_gate:
         line["simple_gla"] = measure_simple_gla(gdr, w, args.steps, args.warmup)
-    if not w.backward and not args.no_backward:
+    if not args.no_backward and w.name == "gdn_dense_bf16":
+        # every other configuration of the operator: forward records for the
+        # tiny fp32, varlen GVA and per-channel (KDA) workloads, and the long
+        # sequence's forward + backward step (median of 50 event-timed calls
+        # after 10 warm-ups each, the workload's own parity gate first)
+        line["configs"] = {}
+        for name in ("tiny_fp32", "varlen_gva_bf16", "kda_bf16", "long_bf16"):
+            torch.cuda.empty_cache()
+            wc = workloads.CONFIGS[name]
+            crec, cinp = measure(gdr, wc, 50, 10, args.breakdown, wc.name)
+            line["configs"][name] = config_record(wc, cinp, crec)
+            if wc.backward and not args.no_cpu_baseline:
+                line["configs"][name]["cpu_baseline"] = cpu_baseline_bwd(wc, cinp)
+            del cinp
         torch.cuda.empty_cache()
         wb = workloads.CONFIGS["long_bf16"]
-        brec, binp = measure(gdr, wb, max(3, args.steps // 5), max(2, args.warmup // 5), args.breakdown,
-                             wb.name)
-        line["backward"] = {"workload": wb.name, "pass": "forward+backward", "B": binp["B"], "T": binp["T"],
-                            "H": wb.H, "HV": wb.HV, "K": wb.K, "V": wb.V, "chunk_size": wb.chunk_size,
-                            "tokens_per_s": brec["value"], "ms_per_step": brec["ms_per_step"],
-                            **{k: v for k, v in brec.items() if k not in ("value", "ms_per_step")}}
-        if not args.no_cpu_baseline:
-            line["backward"]["cpu_baseline"] = cpu_baseline_bwd(wb, binp)
-        del binp
-        torch.cuda.empty_cache()
-        line["segmented"] = measure_segmented(gdr, wb, 8, max(3, args.steps // 5), max(2, args.warmup // 5))
+        line["segmented"] = measure_segmented(gdr, wb, 8, 20, 5)
         torch.cuda.empty_cache()
         wd = workloads.CONFIGS["decode_gva_bf16"]
-        drec, dinp = measure_decode(gdr, wd, args.steps, args.warmup)
-        line["decode"] = {"workload": wd.name, "pass": "token-by-token forward (one decoding step)",
-                          "B": dinp["B"], "T": dinp["T"], "H": wd.H, "HV": wd.HV, "K": wd.K, "V": wd.V,
-                          "tokens_per_s": drec["value"], "ms_per_step": drec["ms_per_step"],
-                          **{k: v for k, v in drec.items() if k not in ("value", "ms_per_step")}}
+        drec, dinp = measure_decode(gdr, wd, 50, 10)
+        line["decode"] = config_record(wd, dinp, drec)
     print(json.dumps(line))
 
 

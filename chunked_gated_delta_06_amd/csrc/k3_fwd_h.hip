@@ -47,11 +47,13 @@ struct K3 {
   static constexpr int KSK = K / 32;            // feature slabs
   static constexpr int KSC = C / 32;            // token slabs
   static constexpr int CPR = K / 8;             // 8-element pieces per key row
-  static constexpr int NLD = C * CPR / NT;      // pieces of a C x K tile per thread
+  static constexpr int NPW = C * CPR;           // 8-element pieces of a C x K tile
+  static constexpr int NLD = (NPW + NT - 1) / NT;   // pieces per thread (the last round may be partial)
   static constexpr int WP = K + 16 / sizeof(T); // LDS pitch of w rows (+16 B)
   static constexpr int KP = K + 32 / sizeof(T); // LDS pitch of key rows (+32 B, transposed reads)
   static constexpr int GP = K + 1;
   static constexpr int NG = PC ? C * K / 4 / NT : 1;   // float4 pieces of a per-channel gate tile
+  static_assert(!PC || NG * NT == C * K / 4, "every thread stages whole gate pieces");
   static constexpr size_t tile_bytes = (size_t)C * (WP + KP) * sizeof(T) + (PC ? K * 4 : 0);
   static constexpr size_t fixed_bytes = PC ? (size_t)C * GP * 4 : 0;
   static constexpr int NBUF = (2 * tile_bytes + fixed_bytes <= 160 * 1024) ? 2 : 1;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
   using Cfg = K3<T, C, K, PC, NW>;
   using Regs = typename Cfg::Regs;
   constexpr int NT = Cfg::NT, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
-  constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, WP = Cfg::WP, KP = Cfg::KP, GP = Cfg::GP;
+  constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NPW = Cfg::NPW, WP = Cfg::WP, KP = Cfg::KP, GP = Cfg::GP;
   constexpr int NG = Cfg::NG, NBUF = Cfg::NBUF;
   constexpr int BV = 16 * NW;
   __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
@@ -116,7 +118,9 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     const T* krow = kp + (R.t0 * H + h) * K;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      // pieces past the tile (K = 32 with four waves) load piece 0 and are never staged
+      const int idx = ((NPW % NT == 0) || tid + NT * i < NPW) ? tid + NT * i : 0;
+      const int t = idx / CPR, d8 = (idx % CPR) * 8;
       const int tc = t < R.L ? t : R.L - 1;
       R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));   // rows past L: zeroed when staged
       R.w[i] = ld8(wp + 8 * idx);
@@ -172,6 +176,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+      if (NPW % NT != 0 && idx >= NPW) continue;
       st8(&sm.w[b][t * WP + d8], R.w[i]);
       const Frag<T> kr = (t < R.L) ? R.k[i] : frag_zero<T>();
       if constexpr (PC) {

@@ -543,3 +543,17 @@ def test_per_channel_scan_four_wave_grid(dtype):
     ro, rht = oracle_fwd(inp)
     check("o", f64(o), ro, TOL[dtype])
     check("ht", f64(ht), rht, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_per_channel_scan_four_wave_grid_k32(dtype):
+    """Per-channel gate, K = 32 at chunk 32 on a four-wave grid (B = 2, HV = 32,
+    V = 256: N * HV * V / 64 = 256). A 32 x 32 key tile has 128 eight-element
+    pieces, fewer than the workgroup's 256 threads, so only the first two waves
+    fetch and stage the w and key tiles."""
+    w, inp = mk(B=2, T=77, H=32, HV=32, K=32, V=256, C=32, dtype=dtype, pc=True, slow=True, scale=0.5)
+    assert w.B * w.HV * (w.V // 64) >= 256
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[dtype])
+    check("ht", f64(ht), rht, TOL[dtype])
