@@ -52,8 +52,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def stage_bytes_per_token_head(w, T_seq):
     """Algorithmic HBM bytes per (token, value head) of each forward stage:
     every tensor counted once when written and once per reading stage, at the
-    library's storage dtypes (q/k/v/o/intermediates in the input dtype, g and
-    beta in fp32, h0/ht fp32)."""
+    library's storage dtypes (q/k/v/o and the intermediates in the input dtype,
+    except the separate WY stage's u, which is fp32; g and beta in fp32, h0/ht
+    fp32)."""
     e = 2 if w.dtype == "bf16" else 4
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
@@ -64,8 +65,8 @@ def stage_bytes_per_token_head(w, T_seq):
     kf_scan = gb if w.per_channel_gate else 4 * (C + 4) / C
     return {
         "kkt_solve": r * K * e + gb + 4 + e * C + kf_row,
-        "wy": r * K * e + V * e + e * C + gb + 4 + e * K + e * V,
-        "fwd_h": e * K + e * V + r * K * e + kf_scan + e * V + e * K * V / C + 8 * K * V / T_seq,
+        "wy": r * K * e + V * e + e * C + gb + 4 + e * K + 4 * V,
+        "fwd_h": e * K + 4 * V + r * K * e + kf_scan + e * V + e * K * V / C + 8 * K * V / T_seq,
         "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
         # fused K1 + K2: k, v, g, beta -> w, u, token factors (Tm stays on chip)
         "kkt_wy": r * K * e + V * e + gb + 4 + e * K + e * V + kf_row,
@@ -137,10 +138,10 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
         "fwd_h": fwd["fwd_h"] - 4 * K * V / T_seq,
         # q, k, g, dO -> de_local, qscale
         "bwd_intra": 2 * r * K * e + 4 + V * e + V * e + 4,
-        # q, k, w, dO, de_local, qscale, kscale, dht -> dh, dh0
-        "bwd_dh": 2 * r * K * e + K * e + 2 * V * e + 8 + e * K * V / C + 8 * K * V / T_seq,
-        # q, k, v, g, beta, dO, Tm, h, v_new, dh -> dq, dk, dv, dg, dbeta
-        "bwd_dqkvg": 4 * r * K * e + 4 * V * e + 16 + e * C + 2 * e * K * V / C,
+        # q, k, w, dO, de_local, qscale, kscale, dht -> dh (fp32), dh0
+        "bwd_dh": 2 * r * K * e + K * e + 2 * V * e + 8 + 4 * K * V / C + 8 * K * V / T_seq,
+        # q, k, v, g, beta, dO, Tm, h, v_new, dh (fp32) -> dq, dk, dv, dg, dbeta
+        "bwd_dqkvg": 4 * r * K * e + 4 * V * e + 16 + e * C + e * K * V / C + 4 * K * V / C,
     }
 
 
@@ -466,12 +467,12 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
                                    views["v_new"], ht, views["kscale"]),
         "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
-        "fwd_h_o": lambda: gdr.fwd_h_o(p, d["q"], d["k"], views["w"], views["u"], d["g"], views["kscale"],
+        "fwd_h_o": lambda: gdr.fwd_h_o(p, d["q"], d["k"], views["w"], views["u_fused"], d["g"], views["kscale"],
                                        cidx, coff, d["h0"], o, ht),
     }
     if not w.per_channel_gate:
         fstages["kkt_wy"] = lambda: gdr.fwd_kkt_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff,
-                                                   views["w"], views["u"], views["kscale"])
+                                                   views["w"], views["u_fused"], views["kscale"])
     # the stages the timed step runs: the fused K1 + K2 and scan + output
     # stages where the shape has them
     fused = gdr.chunk_fwd_fused(p) and not backward

@@ -280,7 +280,10 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
         seq_order=view(lay.seq_order, (p.N,), torch.int32, 4),
         Tm=view(lay.Tm, (nt, HV, C, C), dt, es),
         w=view(lay.w, (nt, HV, C, K), dt, es),
-        u=view(lay.u, (nt, HV, V, C), dt, es),
+        # u as the separate WY stage writes it (fp32), and the same region as the
+        # fused K1 + K2 stage writes it (input dtype)
+        u=view(lay.u, (nt, HV, V, C), torch.float32, 4),
+        u_fused=view(lay.u, (nt, HV, V, C), dt, es),
         h=view(lay.h, (nt, HV, V, K), dt, es),
         v_new=view(lay.v_new, (nt, HV, V, C), dt, es),
         kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, 3 * C + 4), torch.float32, 4),
@@ -518,7 +521,7 @@ def bwd_workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
     views.update(
         de_local=view(lay.de_local, (nt, HV, V, C), dt, es),
         qscale=view(lay.qscale, (nt, HV, C), torch.float32, 4),
-        dh=view(lay.dh, (nt, HV, V, K), dt, es),
+        dh=view(lay.dh, (nt, HV, V, K), torch.float32, 4),   # fp32
     )
     return views
 

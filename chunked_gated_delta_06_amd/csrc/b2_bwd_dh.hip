@@ -12,7 +12,10 @@
 // qscale[r] = scale exp(G_r) / |q_r|.  This is the transpose of the forward
 // recursion S <- exp(G_L) S + K~^T (U - W S) of the chunk form on the
 // coverage-matrix page ("FLA operator-kernel correctness testing and coverage
-// matrix", section 2) plus the inter term of o.
+// matrix", section 2) plus the inter term of o.  dh is stored in fp32 for
+// every input dtype: the gate gradient sums products of h and dh over whole
+// K x V states, where a bf16 dh would cost it about a third of its error
+// budget.
 //
 // gfx950 mapping (as the forward scan): one workgroup per (sequence, value
 // head, 32 value columns, or 16 when that fills the chip better).  Each
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
   const T* __restrict__ wbase = static_cast<const T*>(a.w);
   const T* __restrict__ dop = static_cast<const T*>(a.d_o);
   const T* __restrict__ debase = static_cast<const T*>(a.de_local);
-  T* __restrict__ dhbase = static_cast<T*>(a.dh);
+  float* __restrict__ dhbase = static_cast<float*>(a.dh);
 
   const int64_t c_begin = a.chunk_off[n];
   const int nc = a.chunk_off[n + 1] - (int)c_begin;
@@ -231,8 +234,8 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       dl[eb] = ld4f(erow + 16 * eb + 4 * g4);
     }
     const float gl = sm.ks[b][C];
-    // dh[c] = dS (transposed; feature blocks paired into 16-byte stores)
-    T* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
+    // dh[c] = dS (fp32, transposed; feature blocks paired into 16-byte stores)
+    float* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
     for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
     // dE = de_local + diag(kscale) K dS

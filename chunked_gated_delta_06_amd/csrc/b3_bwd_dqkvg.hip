@@ -26,8 +26,8 @@
 // Every operand sits in LDS as a row-major tile; MFMA fragments use the row
 // contraction map and come from 16-byte row reads or ds_read_b64_tr_b16
 // column reads, so any product (A or A^T times B or B^T) is one code path.
-// fp32 intermediates that feed MFMAs (P, dE, Y, D, Dk) are kept as bf16 hi + lo
-// pairs.  The value dimension is streamed in tiles of 32 columns: per tile the
+// fp32 intermediates that feed MFMAs (P, dE, Y, D, Dk, and dS1, which the
+// reverse scan stores in fp32) are kept as bf16 hi + lo pairs.  The value dimension is streamed in tiles of 32 columns: per tile the
 // kernel stages h^T, dh^T, dO, v and e^T, forms dE and Y (writing dv) and
 // accumulates the C x K and C x C products above in registers; a wave owns a
 // fixed set of 16 x 16 output blocks (one row block) for the whole chunk.  The
@@ -74,8 +74,8 @@ struct B3 {
   static_assert(C % 4 == 0, "16-byte row-factor reads");
   static constexpr size_t FCC = (size_t)C * PC * 4;     // fp32 operand tile C x PC
   static constexpr size_t lH = 0;
-  static constexpr size_t lDH = lH + (size_t)VT * PK * EB;
-  static constexpr size_t lDO = lDH + (size_t)VT * PK * EB;
+  static constexpr size_t lDH = lH + (size_t)VT * PK * EB;                    // dS1^T, hi (+ lo) tiles
+  static constexpr size_t lDO = lDH + (size_t)VT * PK * EB * (sizeof(T) == 2 ? 2 : 1);
   static constexpr size_t lV = lDO + (size_t)C * PV * EB;
   static constexpr size_t lE = lV + (size_t)C * PV * EB;
   static constexpr size_t lDE = lE + (size_t)VT * PC * EB;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   T* sT = reinterpret_cast<T*>(smem + Cfg::oT);
   char* loop = smem + Cfg::oLoop;
   T* sH = reinterpret_cast<T*>(loop + Cfg::lH);
-  T* sDH = reinterpret_cast<T*>(loop + Cfg::lDH);
+  const FTile<T> fDH = ftile<T, PK>(loop + Cfg::lDH, VT);   // dS1^T [v][d]
   T* sDO = reinterpret_cast<T*>(loop + Cfg::lDO);
   T* sV = reinterpret_cast<T*>(loop + Cfg::lV);
   T* sE = reinterpret_cast<T*>(loop + Cfg::lE);
@@ -167,7 +167,8 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     float g, b;
   };
   struct TileRegs {
-    Frag<T> h[NPH], dh[NPH], o[NPO], v[NPO], e[NPE];
+    Frag<T> h[NPH], o[NPO], v[NPO], e[NPE];
+    Frag<float> dh[NPH];     // dS1 (fp32)
   };
   auto fetch_head = [&](HeadRegs& R, int64_t j) {
     const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
@@ -181,14 +182,14 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   };
   auto fetch_tile = [&](TileRegs& R, int64_t j, int64_t v0) {
     const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
-    const T* dhb = static_cast<const T*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
+    const float* dhb = static_cast<const float*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
     const T* eb = static_cast<const T*>(a.v_new) + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
     for (int i = 0; i < NPH; ++i) {
       const int idx = tid + NT * i;
       const bool in = idx < VT * CPR;
       R.h[i] = in ? ld8(hb + 8 * idx) : frag_zero<T>();
-      R.dh[i] = in ? ld8(dhb + 8 * idx) : frag_zero<T>();
+      R.dh[i] = in ? ld8(dhb + 8 * idx) : frag_zero<float>();
     }
 #pragma unroll
     for (int i = 0; i < NPO; ++i) {
@@ -208,11 +209,13 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
     for (int i = 0; i < NPH; ++i) {
       const int idx = tid + NT * i, v = idx / CPR, d8 = (idx % CPR) * 8;
+      const f32x8 fx = R.h[i].f32(), fy = R.dh[i].f32();
       if (idx < VT * CPR) {
         st8(&sH[v * PK + d8], R.h[i]);
-        st8(&sDH[v * PK + d8], R.dh[i]);
+        const Frag<T> hi = Frag<T>::make(fy);
+        st8(&fDH.hi[v * PK + d8], hi);
+        if constexpr (FTile<T>::kSplit) st8(&fDH.lo[v * PK + d8], Frag<T>::make(fy - hi.f32()));
       }
-      const f32x8 fx = R.h[i].f32(), fy = R.dh[i].f32();
 #pragma unroll
       for (int e = 0; e < 8; ++e) lr += fx[e] * fy[e];
     }
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
         }
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
-          mma(a2, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sDH[(16 * vb + r16) * PK + 32 * ks + 8 * g4]));
+          mma_split(a2, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), fDH.row(16 * vb + r16, 32 * ks, lane));
         f32x4 dv4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -392,10 +395,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
           const int b = wv + NW * i, db = b / NRB;
           if (b >= NBK) continue;
           const Frag<T> bS = lds_col8(sH, PK, 0, 16 * db, lane);
-          const Frag<T> bD = lds_col8(sDH, PK, 0, 16 * db, lane);
           mma(dQg[i], aO, bS);
           mma_split(TdW[i], aY, bS);
-          mma(dKt[i], aE, bD);
+          mma_split(dKt[i], aE, fDH.col(0, 16 * db, lane));
         }
 #pragma unroll
         for (int i = 0; i < SCC; ++i) {

@@ -117,8 +117,8 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * C * C * es);
   l.w = off;
   off = round_up(off + (size_t)nt * HV * C * K * es);
-  l.u = off;
-  off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.u = off;   // fp32 from the separate WY stage, input dtype from the fused K1 + K2 stage
+  off = round_up(off + (size_t)nt * HV * V * C * sizeof(float));
   l.h = off;
   off = round_up(off + (size_t)nt * HV * V * K * es);
   l.v_new = off;
@@ -142,8 +142,8 @@ gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * V * C * es);
   l.qscale = off;
   off = round_up(off + (size_t)nt * HV * C * sizeof(float));
-  l.dh = off;
-  off = round_up(off + (size_t)nt * HV * V * K * es);
+  l.dh = off;  // fp32
+  off = round_up(off + (size_t)nt * HV * V * K * sizeof(float));
   l.total = off;
   return l;
 }
@@ -155,8 +155,8 @@ gdr_seg_layout seg_layout_of(const gdr_problem& p) {
   const size_t es = elem_size(p);
   const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V, N = (size_t)p.N;
   size_t off = l.fwd.total;
-  l.u_zero = off;
-  off = round_up(off + (size_t)nt * HV * K * C * es);
+  l.u_zero = off;   // read as the WY stage's u (fp32 with a per-channel gate)
+  off = round_up(off + (size_t)nt * HV * K * C * sizeof(float));
   l.h_tr = off;
   off = round_up(off + (size_t)nt * HV * K * K * es);
   l.v_tr = off;
@@ -266,6 +266,7 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
     a.table_from_dims = 0;
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
   } else {
+    a.u_f32 = 1;   // the separate WY stage writes u in fp32
     e = gdr::launch_chunk_table(a, s);
     if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
     if (e == hipSuccess) e = gdr::launch_wy(a, s);
@@ -309,6 +310,7 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.dv = dv;
   a.dg = dg;
   a.dbeta = dbeta;
+  a.u_f32 = 1;   // u from the separate WY stage (recomputed here, or kept by the forward)
   hipError_t e = hipSuccess;
   if (!p.keep_states) {
     // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
@@ -327,7 +329,7 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
 
 extern "C" {
 
-int gdr_abi_version(void) { return 3; }
+int gdr_abi_version(void) { return 4; }
 
 const char* gdr_status_string(gdr_status s) {
   switch (s) {
@@ -519,6 +521,7 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
   a.h = h;
   a.v_new = v_new;
   a.ht = ht;
+  a.u_f32 = 1;   // u as gdr_fwd_wy writes it
   return hip_status(gdr::launch_fwd_h(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -703,6 +706,8 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
   a.h = ws + l.fwd.h;
   a.v_new = ws + l.fwd.v_new;
   a.kscale = p->gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.fwd.kscale);
+  // u from the fused K1 + K2 stage (scalar gate, input dtype) or the separate WY stage (fp32)
+  a.u_f32 = p->gate_per_channel ? 1 : 0;
 
   // chunk tables over the segments, then w, u (and the token factors)
   hipError_t e = gdr::launch_chunk_table(a, s);

@@ -30,6 +30,9 @@ struct Args {
   int32_t gla;
   // beta holds logits: the kernels use sigmoid(beta) (see beta_value)
   int32_t beta_logits;
+  // u is fp32 (written by the separate WY stage) rather than the input dtype
+  // (written by the fused K1 + K2 stage); the state scans read it accordingly
+  int32_t u_f32;
   float scale;
   const void* q;
   const void* k;

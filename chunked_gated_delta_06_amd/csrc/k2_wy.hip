@@ -2,6 +2,10 @@
 //
 // For one chunk and value head, from Tm = (I + A)^-1 (K1):
 //   w = Tm (beta * exp(G) * k^)      u = Tm (beta * v)
+// (u in fp32 for every input dtype, its operand Tm diag(beta) as a bf16 hi + lo
+// pair: the state scan forms e = u - w S from it, and e is much smaller than u
+// once the state predicts the values, so a bf16 rounding of u, or of Tm beta,
+// lands in e, and from there in every gradient, at a large relative size)
 // the WY factors of the DeltaNet chunk form P^r = I - sum_i k^i w^i^T on the
 // coverage-matrix page ("FLA operator-kernel correctness testing and coverage
 // matrix", section 2), with the gate folded into w.
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   const T* __restrict__ vp = static_cast<const T*>(a.v);
   const T* __restrict__ Tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
   T* __restrict__ wp = static_cast<T*>(a.w) + (c * HV + j) * (int64_t)(C * K);
-  T* __restrict__ up = static_cast<T*>(a.u) + (c * HV + j) * (int64_t)C * V;
+  float* __restrict__ up = static_cast<float*>(a.u) + (c * HV + j) * (int64_t)C * V;
 
   // ---- every global load of the chunk is issued up front (one round trip):
   //      key rows, the first value pass, the rows of Tm this lane feeds, g, beta
@@ -198,10 +202,11 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) sc[e] = sB[32 * ks + 8 * g4 + e];
           const Frag<T> vbf = lds_tr_frag(sV, VP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * vb, lane);
-          mma(acc[rb], Frag<T>::make(tf[rb][ks].f32() * sc), vbf);
+          // the scaled rows of Tm as a hi + lo pair: u keeps ~16 mantissa bits
+          mma_split(acc[rb], SplitFrag<T>::make(tf[rb][ks].f32() * sc), vbf);
         }
       }
-      // token blocks paired into 16-byte stores of the transposed u rows
+      // token blocks paired into 16-byte stores of the transposed fp32 u rows
 #pragma unroll
       for (int m = 0; m < NB / 2; ++m)
         st_pair(up + (v0 + 16 * vb + r16) * C + 32 * m, acc[2 * m], acc[2 * m + 1], lane);

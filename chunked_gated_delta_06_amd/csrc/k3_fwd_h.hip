@@ -26,6 +26,11 @@
 //    MFMA's accumulators.
 //  * A scalar gate and the key norm scale the rows of e in fp32, keeping the
 //    raw keys exact; a per-channel gate scales the staged key tile.
+//  * u written by the separate WY stage is fp32; the S update takes its e
+//    operand as a bf16 hi + lo pair (two MFMAs), so the state, and the h,
+//    v_new and gradients the backward derives from it, carry about 16
+//    mantissa bits of e instead of 8.  The fused scan + output stage keeps
+//    the single bf16 operand and the input-dtype u of the fused K1 + K2 stage.
 //  * h is written transposed (h^T, four features per lane) for the output
 //    kernel; e is written per-chunk transposed (v_new).
 //  * Consecutive workgroups of one head are mapped to one XCD so the shared
@@ -62,7 +67,7 @@ struct K3 {
   // one chunk's global data, held in registers between fetch and staging
   struct Regs {
     Frag<T> w[NLD], k[NLD];
-    v4_t<T> u[NE];
+    f32x4 u[NE];       // u (fp32, from the separate WY stage)
     f32x4 ks[NE];      // scalar gate: exp(G_L - G_t) / |k_t| for this lane's rows of e
     f32x4 gc[NG];      // per-channel gate tile piece
     float gl;          // scalar gate: exp(G_L)
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
   const int64_t v0 = vt * BV + 16 * wv;     // this wave's first value column
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ wbase = static_cast<const T*>(a.w);
-  const T* __restrict__ ubase = static_cast<const T*>(a.u);
+  const float* __restrict__ ubase = static_cast<const float*>(a.u);
   T* __restrict__ hbase = static_cast<T*>(a.h);
   T* __restrict__ vnbase = static_cast<T*>(a.v_new);
   const float* __restrict__ gp = a.g;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
       R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));   // rows past L: zeroed when staged
       R.w[i] = ld8(wp + 8 * idx);
     }
-    const T* up = ubase + ((c * HV + j) * V + v0) * (int64_t)C;
+    const float* up = ubase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) R.u[eb] = ld4raw(up + (r16 * C + 16 * eb + 4 * g4));
     if constexpr (PC) {
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     }
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) {
-      ucur[eb] = to_f32<T>(R.u[eb]);
+      ucur[eb] = R.u[eb];
       if constexpr (!PC) kscur[eb] = R.ks[eb];
     }
     if constexpr (!PC) glcur = R.gl;
@@ -238,8 +243,8 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     T* vnp = vnbase + ((c * HV + j) * V + v0) * (int64_t)C;
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) st4(vnp + (r16 * C + 16 * eb + 4 * g4), E[eb]);
-    // S <- diag(exp(G_L)) S + k^T diag(s) e
-    Frag<T> Ef[KSC];
+    // S <- diag(exp(G_L)) S + k^T diag(s) e  (e as a hi + lo pair)
+    SplitFrag<T> Ef[KSC];
 #pragma unroll
     for (int kt = 0; kt < KSC; ++kt) {
       f32x4 lo = E[2 * kt], hi = E[2 * kt + 1];
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
         lo *= kscur[2 * kt];
         hi *= kscur[2 * kt + 1];
       }
-      Ef[kt] = frag_from_halves<T>(lo, hi);
+      Ef[kt] = SplitFrag<T>::make(cat8(lo, hi));
     }
     if constexpr (PC) {
 #pragma unroll
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
     for (int mb = 0; mb < NS; ++mb)
 #pragma unroll
       for (int kt = 0; kt < KSC; ++kt)
-        mma(S[mb], lds_tr_frag(&sm.k[b][0], KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane), Ef[kt]);
+        mma_split(S[mb], lds_tr_frag(&sm.k[b][0], KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane), Ef[kt]);
   };
 
   // ---- pipelined chunk loop.  Fetches are unconditional (the chunk index is
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
 // other, and meet the compute waves at one LDS-only barrier per step.  The
 // compute waves therefore carry no prefetch registers, so the state and the
 // e tiles stay in architectural VGPRs next to the MFMAs.
-template <typename T, int C, int K, int NWC, int NWL, int NWO = 0>
+template <typename T, int C, int K, int NWC, int NWL, int NWO = 0, typename UT = T>
 struct K3S {
   static constexpr int NTL = 64 * NWL;          // loader threads
   static constexpr int BV = 16 * NWC;           // value columns per workgroup
@@ -324,8 +329,8 @@ struct K3S {
   static constexpr int NKS = (C + 4) / 4;       // float4 pieces of a kscale row
   static constexpr int WP = K + 16 / sizeof(T);
   static constexpr int KP = K + 32 / sizeof(T);
-  static constexpr int UP = C + 16 / sizeof(T); // u rows (one per value column), +16 B
-  static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(T) + (C + 4) * 4;
+  static constexpr int UP = C + 16 / sizeof(UT); // u rows (one per value column), +16 B
+  static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(UT) + (C + 4) * 4;
   static constexpr bool fits = 2 * buf_bytes <= 160 * 1024 && NKS <= NTL;
   // Output staging: the compute waves leave h and e of a step in LDS and the
   // loader waves store them during the next step, so the compute waves issue
@@ -347,7 +352,7 @@ struct K3S {
   struct Regs {
     Frag<T> w[NLD], k[NLD];
     Frag<T> q[OUT ? NLD : 1];
-    Frag<T> u[NLU];
+    Frag<UT> u[NLU];
     f32x4 ks;
     float g2;                 // G_t (threads < C) or 1 / |k_t| (threads C .. 2C - 1)
     int64_t t0;
@@ -356,7 +361,7 @@ struct K3S {
   struct Smem {
     T w[2][C * WP];
     T k[2][C * KP];
-    T u[2][BV * UP];
+    UT u[2][BV * UP];
     float ks[2][C + 4];
     T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
     T es[STG ? 2 : 1][STG ? BV * VSP : 8];
@@ -369,10 +374,11 @@ struct K3S {
 
 // KEEP = false: a scan that only needs the end states (the segment hand-off's
 // pre-process) writes neither h nor v_new.  ZU: u is zero (the transition
-// scan), so it is neither read nor staged.
-template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false>
+// scan), so it is neither read nor staged.  UT: u's storage type (fp32 from
+// the separate WY stage, the input dtype from the fused K1 + K2 stage).
+template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
-  using Cfg = K3S<T, C, K, NWC, NWL, NWO>;
+  using Cfg = K3S<T, C, K, NWC, NWL, NWO, UT>;
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
   constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   const int64_t v0 = vw + 16 * wv;               // compute wave's first value column
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ wbase = static_cast<const T*>(a.w);
-  const T* __restrict__ ubase = static_cast<const T*>(a.u);
+  const UT* __restrict__ ubase = static_cast<const UT*>(a.u);
   T* __restrict__ hbase = static_cast<T*>(a.h);
   T* __restrict__ vnbase = static_cast<T*>(a.v_new);
 
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
     }
     if constexpr (!ZU) {
-      const T* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
+      const UT* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
       for (int i = 0; i < NLU; ++i) {
         const int idx = tl + NTL * i;
@@ -737,7 +743,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       for (int mb = 0; mb < NS; ++mb)
         kf[kt][mb] = lds_tr_frag(&sm.k[b][0], KP, 32 * kt + 4 * g4, 32 * kt + 16 + 4 * g4, 16 * mb, lane);
     f32x4 E[NE];
-    const T* urow = &sm.u[b][(16 * wv + r16) * UP];
+    const UT* urow = &sm.u[b][(16 * wv + r16) * UP];
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) E[eb] = ZU ? zero4() : ld4f(urow + 16 * eb + 4 * g4);
     f32x4 sc[NE];
@@ -773,16 +779,27 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
       for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
     }
-    // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e
-    Frag<T> Ef[KSC];
-#pragma unroll
-    for (int kt = 0; kt < KSC; ++kt) Ef[kt] = frag_from_halves<T>(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]);
+    // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e: e as a hi + lo
+    // pair except in the fused scan + output stage
 #pragma unroll
     for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+    if constexpr (OUT) {
+      Frag<T> Ef[KSC];
 #pragma unroll
-    for (int kt = 0; kt < KSC; ++kt)
+      for (int kt = 0; kt < KSC; ++kt) Ef[kt] = frag_from_halves<T>(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]);
 #pragma unroll
-      for (int mb = 0; mb < NS; ++mb) mma(S[mb], kf[kt][mb], Ef[kt]);
+      for (int kt = 0; kt < KSC; ++kt)
+#pragma unroll
+        for (int mb = 0; mb < NS; ++mb) mma(S[mb], kf[kt][mb], Ef[kt]);
+    } else {
+      SplitFrag<T> Ef[KSC];
+#pragma unroll
+      for (int kt = 0; kt < KSC; ++kt) Ef[kt] = SplitFrag<T>::make(cat8(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]));
+#pragma unroll
+      for (int kt = 0; kt < KSC; ++kt)
+#pragma unroll
+        for (int mb = 0; mb < NS; ++mb) mma_split(S[mb], kf[kt][mb], Ef[kt]);
+    }
   };
 
   if (nc > 0) {
@@ -815,13 +832,38 @@ hipError_t launch_nw(const Args& a, hipStream_t s) {
   }
 }
 
+// The warp-specialised scan reading u of type UT: 2 compute + 2 loader waves
+// (4 loader waves when elements or u are fp32 or K = 256, to keep each
+// loader's payload in registers), or 1 + NWL (below).
+template <typename T, int C, int K, typename UT>
+constexpr int scan_loaders() {
+  return (sizeof(T) == 4 || sizeof(UT) == 4 || K == 256) ? 4 : 2;
+}
+
+template <typename T, int C, int K, typename UT>
+hipError_t launch_keep(const Args& a, hipStream_t s) {
+  constexpr int NWL = scan_loaders<T, C, K, UT>();
+  if constexpr (!K3S<T, C, K, 2, NWL, 0, UT>::fits) {
+    return hipErrorInvalidValue;
+  } else {
+    const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+    if (nblk32 < kNumCUs)
+      hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, true, false, UT>), dim3((unsigned)(2 * nblk32)),
+                         dim3(64 * (1 + NWL)), 0, s, a);
+    else
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, true, false, UT>), dim3((unsigned)nblk32),
+                         dim3(64 * (2 + NWL)), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   if constexpr (!PC) {
     // warp-specialised scan: 2 compute + 2 loader waves (4 loader waves when
     // elements are fp32 or K = 256, to keep each loader's payload in registers)
-    constexpr int NWL = (sizeof(T) == 4 || K == 256) ? 4 : 2;
-    if constexpr (K3S<T, C, K, 2, NWL>::fits) {
+    constexpr int NWL = scan_loaders<T, C, K, T>();
+    if constexpr (K3S<T, C, K, 2, NWL>::fits && K3S<T, C, K, 2, scan_loaders<T, C, K, float>(), 0, float>::fits) {
       // 32 value columns (two compute waves) per workgroup, or 16 (one) when
       // the 32-column grid would leave compute units idle: the scan's step
       // latency does not shrink with fewer columns, so more workgroups is the
@@ -829,19 +871,16 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       const int64_t nblk32 = a.N * a.HV * (a.V / 32);
       // h == NULL: end states only; u == NULL too: u is zero (transition scan)
       const bool keep = a.h != nullptr, zu = !keep && a.u == nullptr;
+      if (keep) return a.u_f32 ? launch_keep<T, C, K, float>(a, s) : launch_keep<T, C, K, T>(a, s);
       if (nblk32 < kNumCUs) {
         const dim3 g((unsigned)(2 * nblk32)), b(64 * (1 + NWL));
-        if (keep)
-          hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0>), g, b, 0, s, a);
-        else if (!zu)
+        if (!zu)
           hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false>), g, b, 0, s, a);
         else
           hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, false, true>), g, b, 0, s, a);
       } else {
         const dim3 g((unsigned)nblk32), b(64 * (2 + NWL));
-        if (keep)
-          hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0>), g, b, 0, s, a);
-        else if (!zu)
+        if (!zu)
           hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false>), g, b, 0, s, a);
         else
           hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, false, true>), g, b, 0, s, a);
@@ -849,10 +888,13 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  // per-channel gate: each workgroup forms the chunk's gate cumsum and decayed
-  // keys itself, so four waves (64 value columns) share that work when the
-  // grid still gives every compute unit a workgroup; otherwise (and for
-  // shapes whose double-buffered tiles exceed LDS) two waves, 32 columns
+  // per-channel gate (and a scalar gate whose warp-specialised scan does not
+  // fit): u comes from the separate WY stage, in fp32.  Each workgroup forms
+  // the chunk's gate cumsum and decayed keys itself, so four waves (64 value
+  // columns) share that work when the grid still gives every compute unit a
+  // workgroup; otherwise (and for shapes whose double-buffered tiles exceed
+  // LDS) two waves, 32 columns
+  if (sizeof(T) == 2 && !a.u_f32 && a.u != nullptr) return hipErrorInvalidValue;
   if constexpr (PC && K3<T, C, K, PC, 4>::fits) {
     if (a.V % 64 == 0 && a.N * a.HV * (a.V / 64) >= kNumCUs) return launch_nw<T, C, K, PC, 4>(a, s);
   }
@@ -929,8 +971,8 @@ namespace {
 // the condition launch_t uses to pick the warp-specialised scan
 template <typename T, int C, int K>
 constexpr bool specialised_fits() {
-  constexpr int NWL = (sizeof(T) == 4 || K == 256) ? 4 : 2;
-  return K3S<T, C, K, 2, NWL>::fits;
+  return K3S<T, C, K, 2, scan_loaders<T, C, K, T>()>::fits &&
+         K3S<T, C, K, 2, scan_loaders<T, C, K, float>(), 0, float>::fits;
 }
 template <typename T, int C>
 bool specialised_k(int64_t K) {

@@ -97,7 +97,9 @@ typedef struct {
  *                                  which the state scans start them; unused otherwise
  *   Tm         dtype [NT_max][HV][C][C]   (I + A)^-1 of each chunk, row-major
  *   w          dtype [NT_max][HV][C][K]   WY keys, token-major
- *   u          dtype [NT_max][HV][V][C]   WY values, transposed per chunk
+ *   u          f32   [NT_max][HV][V][C]   WY values, transposed per chunk, as gdr_fwd_wy
+ *                                         writes them (fp32 for every dtype); the fused
+ *                                         stage gdr_fwd_kkt_wy writes them in `dtype`
  *   h          dtype [NT_max][HV][V][K]   state entering each chunk, transposed (h^T)
  *   v_new      dtype [NT_max][HV][V][C]   corrected values e, transposed per chunk
  *   kscale     f32   [NT_max][HV][3C + 4] scalar gate only, per chunk token factors:
@@ -176,13 +178,16 @@ gdr_status gdr_fwd_kkt_solve(const gdr_problem* p, const void* k, const float* g
                              const int32_t* chunk_off, void* Tm, float* kscale, void* stream);
 
 /* K2: WY recompute, w = Tm (beta exp(G) k^), u = Tm (beta v) per chunk and value head
- * (coverage-matrix page, section 2: P^r = I - sum k^i w^i^T). */
+ * (coverage-matrix page, section 2: P^r = I - sum k^i w^i^T).  w is written in
+ * `dtype`, u in fp32 (layout above): the scan's e = u - w S is small next to u,
+ * and a bf16 u would carry its rounding into e, h and every gradient. */
 gdr_status gdr_fwd_wy(const gdr_problem* p, const void* k, const void* v, const float* g,
                       const float* beta, const int32_t* chunk_idx, const int32_t* chunk_off,
                       const void* Tm, void* w, void* u, void* stream);
 
 /* K1 + K2 fused (scalar gate): the results of gdr_fwd_kkt_solve and gdr_fwd_wy
- * (w, u and kscale, same layouts) in one pass per chunk and value head, with
+ * (w, u and kscale, same layouts, but u in `dtype`: it feeds gdr_fwd_h_o) in one
+ * pass per chunk and value head, with
  * (I + A)^-1 kept on chip and not written.  gdr_chunk_fwd runs it in place of
  * the two stages whenever it runs the fused scan + output stage.  Returns
  * GDR_ERR_UNSUPPORTED for a per-channel gate. */
@@ -195,7 +200,8 @@ gdr_status gdr_fwd_kkt_wy(const gdr_problem* p, const void* k, const void* v, co
  * semantics"), e = u - w S -> v_new, then
  * S <- diag(exp(G_L)) S + sum_j (exp(G_L - G_j) k^_j) e_j^T.  S starts at h0 (or 0)
  * and is written to ht after the last chunk (if ht != NULL).  A scalar gate is
- * read through K1's kscale (g may then be NULL); a per-channel gate through g. */
+ * read through K1's kscale (g may then be NULL); a per-channel gate through g.
+ * u is fp32, as gdr_fwd_wy writes it. */
 gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const void* u,
                      const float* g, const float* kscale, const int32_t* chunk_idx,
                      const int32_t* chunk_off, const float* h0, void* h, void* v_new, float* ht,
@@ -211,7 +217,8 @@ gdr_status gdr_fwd_o(const gdr_problem* p, const void* q, const void* k, const v
  * on chip, so neither is written (same operator as the two stages: the chunk
  * form of the coverage-matrix page, section 2, with h as on the KCP page,
  * section "h and dh cross-rank semantics").  g (scalar gate [B,T,HV]) and
- * K1's kscale are both required; h0 / ht as gdr_fwd_h.  Returns
+ * K1's kscale are both required; h0 / ht as gdr_fwd_h; u in `dtype`, as
+ * gdr_fwd_kkt_wy writes it.  Returns
  * GDR_ERR_UNSUPPORTED for a per-channel gate or a shape without an
  * instantiation; gdr_fwd_h_o_supported tells in advance (1 = supported). */
 int gdr_fwd_h_o_supported(const gdr_problem* p);
@@ -309,7 +316,7 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
  *   de_local  dtype [NT_max][HV][V][C]  scale * P^T dO per chunk, transposed, with
  *                                       P[r][t] = q^_r . k^_t exp(G_r - G_t), t <= r
  *   qscale    f32   [NT_max][HV][C]     scale * exp(G_r) / |q_r| (0 past L)
- *   dh        dtype [NT_max][HV][V][K]  gradient of the state leaving each chunk,
+ *   dh        f32   [NT_max][HV][V][K]  gradient of the state leaving each chunk,
  *                                       transposed (dh^T) */
 typedef struct {
   gdr_fwd_layout fwd;
@@ -363,7 +370,8 @@ gdr_status gdr_bwd_intra(const gdr_problem* p, const void* q, const void* k, con
 /* B2: reverse state-gradient scan.  For each sequence and value head, dS starts
  * at dht (or 0); for the chunks from last to first: dh = dS,
  * dE = de_local + diag(kscale) K dS, dS <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE;
- * finally dh0 = dS (if dh0 != NULL).  kscale is K1's. */
+ * finally dh0 = dS (if dh0 != NULL).  kscale is K1's; dh is written in fp32
+ * (workspace layout above). */
 gdr_status gdr_bwd_dh(const gdr_problem* p, const void* q, const void* k, const void* w,
                       const void* d_o, const void* de_local, const float* qscale,
                       const float* kscale, const int32_t* chunk_idx, const int32_t* chunk_off,
@@ -371,7 +379,7 @@ gdr_status gdr_bwd_dh(const gdr_problem* p, const void* q, const void* k, const 
 
 /* B3: per chunk and q/k head, every remaining gradient: dq, dk (group sums and
  * L2-norm backward included), dv, dbeta and dg, from q, k, v, g, beta, d_o, Tm
- * (K1), h and v_new (K3) and dh (B2). */
+ * (K1), h and v_new (K3) and dh (B2, fp32). */
 gdr_status gdr_bwd_dqkvg(const gdr_problem* p, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const void* d_o, const void* Tm,
                          const void* h, const void* v_new, const void* dh,

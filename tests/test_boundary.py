@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdr_abi_version() == 3
+    assert L.gdr_abi_version() == 4
 
 
 def test_status_strings():
@@ -88,8 +88,10 @@ def test_workspace_layout():
     offs = [lay.chunk_idx, lay.chunk_off, lay.Tm, lay.w, lay.u, lay.h, lay.v_new, lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     nt, C, HV, K, V = 256, 64, 16, 128, 128
-    assert lay.h - lay.u >= nt * HV * V * C * 2
+    assert lay.h - lay.u >= nt * HV * V * C * 4      # u in fp32 (the separate WY stage's)
     assert lay.total - lay.v_new >= nt * HV * V * C * 2
+    blay = gdr.bwd_layout(p)
+    assert blay.total - blay.dh >= nt * HV * V * K * 4   # dh in fp32
     # varlen bound floor(T / C) + N
     pv = problem(B=1, T=25344, H=16, HV=32, K=128, V=128, N=24)
     assert gdr.fwd_layout(pv).nt_max == 25344 // 64 + 24

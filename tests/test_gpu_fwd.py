@@ -117,9 +117,10 @@ FUSED_CASES = [
 
 @pytest.mark.parametrize("cfg", FUSED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_fused_stage_against_separate_stages(cfg):
-    """gdr_fwd_h_o on the K0-K2 intermediates of a keep-states forward: ht is
-    bit-identical to the separate scan's (the scan arithmetic is the same), o
-    agrees with the separate output stage, and both match the oracle."""
+    """gdr_fwd_h_o on the w, u and token factors of the fused K1 + K2 stage,
+    beside the separate stages of a keep-states forward (whose scan reads the
+    fp32 u of the separate WY stage and takes e as a hi + lo pair): both
+    match the oracle, and each other within the tolerance."""
     w, inp = mk(T=150, slow=True, **cfg)
     tol = TOL[w.dtype]
     o_sep, ht_sep, ws = gpu_fwd(inp, keep_states=True)
@@ -128,15 +129,17 @@ def test_fused_stage_against_separate_stages(cfg):
     assert gdr.fwd_h_o_supported(p)
     o_f = torch.full_like(o_sep, float("nan"))
     ht_f = torch.full_like(ht_sep, float("nan"))
-    gdr.fwd_h_o(p, dev(inp["q"]), dev(inp["k"]), ws["w"], ws["u"], dev(inp["g"]), ws["kscale"],
+    gdr.fwd_kkt_wy(p, dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]), ws["chunk_idx"],
+                   ws["chunk_off"], ws["w"], ws["u_fused"], ws["kscale"])
+    gdr.fwd_h_o(p, dev(inp["q"]), dev(inp["k"]), ws["w"], ws["u_fused"], dev(inp["g"]), ws["kscale"],
                 ws["chunk_idx"], ws["chunk_off"], dev(inp["h0"]), o_f, ht_f)
     torch.cuda.synchronize()
-    assert torch.equal(ht_f, ht_sep)
     ro, rht = oracle_fwd(inp)
     check("o fused", f64(o_f), ro, tol)
     check("o separate", f64(o_sep), ro, tol)
-    check("ht", f64(ht_f), rht, tol)
-    assert err_ratio(f64(o_f), f64(o_sep)) <= tol / 4
+    check("ht fused", f64(ht_f), rht, tol)
+    check("ht separate", f64(ht_sep), rht, tol)
+    assert err_ratio(f64(o_f), f64(o_sep)) <= tol
 
 
 KKT_WY_CASES = [
@@ -163,7 +166,7 @@ def test_fused_kkt_wy_against_oracle(cfg):
     ro, rht, it = oracle_fwd(inp, intermediates=True)
     NT = int(it["off"][-1])
     wf = torch.full_like(ws["w"], float("nan"))
-    uf = torch.full_like(ws["u"], float("nan"))
+    uf = torch.full_like(ws["u_fused"], float("nan"))
     kf = torch.full_like(ws["kscale"], float("nan"))
     tm_before = ws["Tm"].clone()
     gdr.fwd_kkt_wy(p, dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]), ws["chunk_idx"],
