@@ -32,7 +32,7 @@ GDR_BF16, GDR_FP32 = 0, 1
 STATUS = {
     0: "GDR_OK", 1: "GDR_ERR_NULL_ARG", 2: "GDR_ERR_CHUNK_SIZE", 3: "GDR_ERR_SHAPE",
     4: "GDR_ERR_VARLEN", 5: "GDR_ERR_DTYPE", 6: "GDR_ERR_ALIGNMENT", 7: "GDR_ERR_WORKSPACE",
-    8: "GDR_ERR_HIP", 9: "GDR_ERR_CU_SEQLENS", 10: "GDR_ERR_UNSUPPORTED",
+    8: "GDR_ERR_HIP", 9: "GDR_ERR_CU_SEQLENS", 10: "GDR_ERR_UNSUPPORTED", 11: "GDR_ERR_SCRATCH_LIMIT",
 }
 
 
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_size_t)]
         L.gdr_fwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrFwdLayout)]
         L.gdr_chunk_fwd.argtypes = [PP] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
+        L.gdr_chunk_fwd_noalloc.argtypes = [PP] + [_P] * 9 + [_P]
         L.gdr_chunk_table.argtypes = [PP, _P, _P, _P, _P]
         L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 7 + [_P]
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
@@ -113,7 +114,7 @@ def lib() -> ctypes.CDLL:
         L.gdr_bwd_dh.argtypes = [PP] + [_P] * 12 + [_P]
         L.gdr_bwd_dqkvg.argtypes = [PP] + [_P] * 17 + [_P]
         for name in ("gdr_check_problem", "gdr_validate_cu_seqlens", "gdr_fwd_workspace_bytes",
-                     "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_table",
+                     "gdr_fwd_workspace_layout", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc", "gdr_chunk_table",
                      "gdr_fwd_kkt_solve", "gdr_fwd_wy", "gdr_fwd_h", "gdr_fwd_o", "gdr_fwd_h_o",
                      "gdr_fused_recurrent_fwd", "gdr_fwd_kkt_wy", "gdr_segmented_workspace_bytes",
                      "gdr_segmented_workspace_layout", "gdr_chunk_fwd_segmented", "gdr_simple_gla_fwd",
@@ -258,6 +259,33 @@ def chunk_fwd(q, k, v, g, beta, *, scale: float = 1.0, chunk_size: int = 64, cu_
     _raise(st)
     if return_workspace:
         return o, ht, workspace
+    return o, ht
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, *, out, scale: float = 1.0, chunk_size: int = 64, cu_seqlens=None,
+                      initial_state=None, use_qk_l2norm_in_kernel: bool = False, beta_logits: bool = False):
+    """The full forward through gdr_chunk_fwd_noalloc: no workspace, the
+    library's fixed per-device scratch instead; ``out=(o, ht)`` are the
+    caller's output tensors (ht may be None), so this call allocates nothing.
+    Calls that overlap on one device race on the scratch."""
+    _need_gpu(q, k, v, g, beta, cu_seqlens, initial_state)
+    o, ht = out
+    _need_gpu(o, ht)
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise ValueError("q, k, v and o must share one dtype")
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("ht", ht)):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    p = make_problem(q, v, g, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                     use_qk_l2norm=use_qk_l2norm_in_kernel, scale=scale, beta_logits=beta_logits)
+    check_tensors(p, q, k, v, g, beta, cu_seqlens, initial_state, validate_cu=False)
+    _expect("o", o, v.shape)
+    _expect("ht", ht, (p.N, p.HV, p.K, p.V))
+    _raise(lib().gdr_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
+                                       _stream(q.device)))
     return o, ht
 
 

@@ -3,6 +3,7 @@
 // allocates, frees or synchronises; every launch goes to the caller's stream.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "gdr_internal.h"
 
@@ -125,6 +126,34 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * V * C * es);
   l.kscale = off;
   off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float)));
+  l.total = off;
+  return l;
+}
+
+// The regions the fused path touches (chunk tables, w, u in the input dtype,
+// kscale): Tm, h and v_new get no bytes (their offsets are the next region's).
+gdr_fwd_layout fused_layout_of(const gdr_problem& p) {
+  gdr_fwd_layout l;
+  const int64_t nt = gdr::nt_max(p);
+  const size_t es = elem_size(p);
+  const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V;
+  size_t off = 0;
+  l.nt_max = nt;
+  l.chunk_idx = off;
+  off = round_up(off + (size_t)nt * 4 * sizeof(int32_t));
+  l.chunk_off = off;
+  off = round_up(off + ((size_t)p.N + 1) * sizeof(int32_t));
+  l.seq_order = off;
+  off = round_up(off + (size_t)p.N * sizeof(int32_t));
+  l.Tm = off;
+  l.w = off;
+  off = round_up(off + (size_t)nt * HV * C * K * es);
+  l.u = off;
+  off = round_up(off + (size_t)nt * HV * V * C * es);
+  l.h = off;
+  l.v_new = off;
+  l.kscale = off;
+  off = round_up(off + (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float));
   l.total = off;
   return l;
 }
@@ -325,6 +354,76 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   return e;
 }
 
+// Argument checks of the full forward (everything but the workspace).
+gdr_status check_fwd_args(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const int32_t* cu_seqlens, const float* h0, const void* o,
+                          const float* ht) {
+  const gdr_status st = check(p, cu_seqlens != nullptr, true);
+  if (st != GDR_OK) return st;
+  if (p->T != 0 && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  return GDR_OK;
+}
+
+// ---- fixed scratch of the no-allocation forward (gdr_chunk_fwd_noalloc).
+// One array per device, created with the code object and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the per-device address that
+// hipGetSymbolAddress returns, fetched once per device with that device
+// current.
+constexpr size_t kScratchBytes = GDR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on the first call there).
+gdr_status scratch_on_current_device(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return GDR_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
+}
+
+// The full forward on workspace `ws` laid out as `l` (the padded problem's
+// layout; zero-padded copies of the inputs and outputs follow it when the head
+// dims have no instantiation).
+gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
+                         char* ws, const gdr_fwd_layout& l, hipStream_t s) {
+  const gdr_problem* p = &p0;
+  const gdr_problem pp = padded_problem(*p);
+  if (!needs_pad(*p)) return hip_status(fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, ws, l, s));
+  const PadLayout pl = pad_layout(*p, l.total, false);
+  // head dims without an instantiation: zero-padded copies in, padded problem, copies out
+  const int es = (int)elem_size(*p);
+  const int64_t BT = p->B * p->T, H = p->H, HV = p->HV, N = p->N, K = p->K, V = p->V, Kp = pp.K, Vp = pp.V;
+  hipError_t e = gdr::launch_pad(q, ws + pl.q, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(k, ws + pl.k, BT * H, 1, K, 1, Kp, es, s);
+  if (e == hipSuccess) e = gdr::launch_pad(v, ws + pl.v, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && p->gate_per_channel) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
+  if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
+  if (e == hipSuccess)
+    e = fwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v,
+                p->gate_per_channel ? reinterpret_cast<const float*>(ws + pl.g) : g, beta, cu_seqlens,
+                h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.o,
+                ht != nullptr ? reinterpret_cast<float*>(ws + pl.ht) : nullptr, ws, l, s);
+  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.o, o, BT * HV, 1, V, 1, Vp, es, s);
+  if (e == hipSuccess && ht != nullptr) e = gdr::launch_unpad(ws + pl.ht, ht, N * HV, K, V, Kp, Vp, 4, s);
+  return hip_status(e);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +444,9 @@ const char* gdr_status_string(gdr_status s) {
     case GDR_ERR_WORKSPACE: return "workspace missing or too small";
     case GDR_ERR_HIP: return "HIP launch failed";
     case GDR_ERR_CU_SEQLENS: return "cu_seqlens must start at 0, be non-decreasing and end at T";
+    case GDR_ERR_SCRATCH_LIMIT:
+      return "gdr_chunk_fwd_noalloc: the problem needs more than the fixed scratch of GDR_NOALLOC_SCRATCH_BYTES "
+             "(use gdr_chunk_fwd with a workspace)";
     case GDR_ERR_UNSUPPORTED:
       return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 runs at chunk_size 32, "
              "so a saved-state backward there needs a chunk_size 32 forward)";
@@ -386,39 +488,32 @@ gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes) {
 gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const int32_t* cu_seqlens, const float* h0, void* o, float* ht,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  gdr_status st = check(p, cu_seqlens != nullptr, true);
+  const gdr_status st = check_fwd_args(p, q, k, v, g, beta, cu_seqlens, h0, o, ht);
   if (st != GDR_OK) return st;
-  const bool empty = p->T == 0;
-  if (!empty && (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr))
-    return GDR_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, cu_seqlens, h0, o, ht, workspace};
-  for (const void* ptr : ptrs)
-    if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
+  if (workspace != nullptr && !aligned16(workspace)) return GDR_ERR_ALIGNMENT;
   const gdr_problem pp = padded_problem(*p);
   const gdr_fwd_layout l = layout_of(pp);
-  const bool pad = needs_pad(*p);
-  const PadLayout pl = pad_layout(*p, l.total, false);
-  if (workspace == nullptr || workspace_bytes < (pad ? pl.total : l.total)) return GDR_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!pad) return hip_status(fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, ws, l, s));
+  const size_t need = needs_pad(*p) ? pad_layout(*p, l.total, false).total : l.total;
+  if (workspace == nullptr || workspace_bytes < need) return GDR_ERR_WORKSPACE;
+  return chunk_fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, static_cast<char*>(workspace), l,
+                       static_cast<hipStream_t>(stream));
+}
 
-  // head dims without an instantiation: zero-padded copies in, padded problem, copies out
-  const int es = (int)elem_size(*p);
-  const int64_t BT = p->B * p->T, H = p->H, HV = p->HV, N = p->N, K = p->K, V = p->V, Kp = pp.K, Vp = pp.V;
-  hipError_t e = gdr::launch_pad(q, ws + pl.q, BT * H, 1, K, 1, Kp, es, s);
-  if (e == hipSuccess) e = gdr::launch_pad(k, ws + pl.k, BT * H, 1, K, 1, Kp, es, s);
-  if (e == hipSuccess) e = gdr::launch_pad(v, ws + pl.v, BT * HV, 1, V, 1, Vp, es, s);
-  if (e == hipSuccess && p->gate_per_channel) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
-  if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
-  if (e == hipSuccess)
-    e = fwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v,
-                p->gate_per_channel ? reinterpret_cast<const float*>(ws + pl.g) : g, beta, cu_seqlens,
-                h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.o,
-                ht != nullptr ? reinterpret_cast<float*>(ws + pl.ht) : nullptr, ws, l, s);
-  if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.o, o, BT * HV, 1, V, 1, Vp, es, s);
-  if (e == hipSuccess && ht != nullptr) e = gdr::launch_unpad(ws + pl.ht, ht, N * HV, K, V, Kp, Vp, 4, s);
-  return hip_status(e);
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const int32_t* cu_seqlens, const float* h0,
+                                 void* o, float* ht, void* stream) {
+  const gdr_status st = check_fwd_args(p, q, k, v, g, beta, cu_seqlens, h0, o, ht);
+  if (st != GDR_OK) return st;
+  // the fused path touches only the chunk tables, w, u and kscale
+  const gdr_problem pp = padded_problem(*p);
+  const bool fused = !pp.keep_states && gdr::fwd_h_o_preferred(make_args(pp));
+  const gdr_fwd_layout l = fused ? fused_layout_of(pp) : layout_of(pp);
+  const size_t need = needs_pad(*p) ? pad_layout(*p, l.total, false).total : l.total;
+  if (need > kScratchBytes) return GDR_ERR_SCRATCH_LIMIT;
+  char* ws = nullptr;
+  const gdr_status sst = scratch_on_current_device(&ws);
+  if (sst != GDR_OK) return sst;
+  return chunk_fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, ws, l, static_cast<hipStream_t>(stream));
 }
 
 gdr_status gdr_chunk_table(const gdr_problem* p, const int32_t* cu_seqlens, int32_t* chunk_idx,

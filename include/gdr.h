@@ -56,11 +56,13 @@ typedef enum {
   GDR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than *_workspace_bytes */
   GDR_ERR_HIP = 8,         /* a kernel launch failed */
   GDR_ERR_CU_SEQLENS = 9,  /* gdr_validate_cu_seqlens: bad table */
-  GDR_ERR_UNSUPPORTED = 10 /* backward: per-channel gate, K above 128, or a saved-state
+  GDR_ERR_UNSUPPORTED = 10, /* backward: per-channel gate, K above 128, or a saved-state
                               backward for fp32 with K = 128 and chunk 64 (see
                               gdr_chunk_bwd); gdr_fwd_h_o: a shape without the fused stage
                               (see gdr_fwd_h_o_supported); gdr_simple_gla_fwd: a per-channel
                               gate */
+  GDR_ERR_SCRATCH_LIMIT = 11 /* gdr_chunk_fwd_noalloc: the problem needs more than
+                                GDR_NOALLOC_SCRATCH_BYTES of scratch */
 } gdr_status;
 
 typedef enum { GDR_BF16 = 0, GDR_FP32 = 1 } gdr_dtype;
@@ -158,6 +160,28 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
                          const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, void* o, float* ht, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Full forward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same operator, arguments (minus the
+ * workspace), kernels and results as gdr_chunk_fwd; the intermediates live in
+ * a fixed scratch array of GDR_NOALLOC_SCRATCH_BYTES per device, part of the
+ * library's code object (allocated when the library is loaded on a device and
+ * held until the process ends).  With the fused stages (gdr_chunk_fwd_fused)
+ * the scratch holds the chunk tables, w, u and kscale (about 524 bytes per
+ * token and value head for bf16 with K = V = 128 at chunk 64), so such a
+ * problem fits up to about 500 k (token, value head) pairs (4 x 4096 tokens x
+ * 16 heads take half); a larger problem returns GDR_ERR_SCRATCH_LIMIT before
+ * any launch.  Nothing in the scratch has to start at zero.  Every call on a
+ * device shares that device's scratch: calls that overlap in time on one
+ * device (other streams, other host threads) race and must be serialised by
+ * the caller.  `stream` must belong to the current device.  The only HIP call
+ * besides the launches is one hipGetSymbolAddress on the first call on each
+ * device. */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const int32_t* cu_seqlens,
+                                 const float* h0, void* o, float* ht, void* stream);
 
 /* ---- the forward's stages, callable one by one (same layouts as above) ---- */
 

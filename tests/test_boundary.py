@@ -38,7 +38,7 @@ def test_exports_every_declared_function():
 def test_status_strings():
     L = gdr.lib()
     assert L.gdr_status_string(2).decode() == "chunk_size must be either 32 or 64"
-    for s in range(11):
+    for s in range(12):
         assert L.gdr_status_string(s)
     assert "backward supports" in L.gdr_status_string(10).decode()
 
@@ -125,6 +125,24 @@ def test_fwd_rejects_before_launch():
     st = L.gdr_chunk_fwd(ctypes.byref(p), *args[:5], P(0x1000), None, P(0x1000), None, P(0x1000),
                          ctypes.c_size_t(1 << 40), None)
     assert st == 4
+
+
+def test_noalloc_forward_rejects_before_launch():
+    """gdr_chunk_fwd_noalloc checks its arguments and the scratch limit on the
+    host before it touches the device (these calls run on the CPU host)."""
+    L = gdr.lib()
+    P = ctypes.c_void_p
+    a = [P(0x1000)] * 5
+    p = problem()
+    assert L.gdr_chunk_fwd_noalloc(ctypes.byref(p), None, *a[1:5], None, None, P(0x1000), None, None) == 1
+    assert L.gdr_chunk_fwd_noalloc(ctypes.byref(p), P(0x1000), P(0x1008), *a[2:5], None, None, P(0x1000),
+                                   None, None) == 6
+    assert L.gdr_chunk_fwd_noalloc(ctypes.byref(problem(chunk_size=16)), *a, None, None, P(0x1000), None,
+                                   None) == 2
+    # 32768 tokens x 32 heads at K = V = 128: w, u and the token factors exceed the scratch
+    big = problem(B=1, T=32768, H=32, HV=32, K=128, V=128, N=1)
+    assert L.gdr_chunk_fwd_noalloc(ctypes.byref(big), *a, None, None, P(0x1000), None, None) == 11
+    assert "fixed scratch" in L.gdr_status_string(11).decode()
 
 
 def test_fused_stage_support_and_host_rejections():
