@@ -54,8 +54,10 @@ class GdrFwdLayout(ctypes.Structure):
 
 
 class GdrBwdLayout(ctypes.Structure):
-    _fields_ = [("fwd", GdrFwdLayout), ("de_local", ctypes.c_size_t), ("qscale", ctypes.c_size_t),
-                ("dh", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+    _fields_ = [("fwd", GdrFwdLayout), ("chunk_size", ctypes.c_int64), ("de_local", ctypes.c_size_t),
+                ("qscale", ctypes.c_size_t),
+                ("dh", ctypes.c_size_t), ("kt", ctypes.c_size_t), ("qg", ctypes.c_size_t),
+                ("dl", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class GdrSegLayout(ctypes.Structure):
@@ -535,8 +537,12 @@ def chunk_bwd(q, k, v, g, beta, do, dht=None, *, scale: float = 1.0, chunk_size:
 def bwd_workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
     """Typed views of the backward's intermediates (forward ones included)."""
     lay = bwd_layout(p)
-    views = workspace_views(p, ws)
-    nt, C, HV, K, V = lay.fwd.nt_max, p.chunk_size, p.HV, p.K, p.V
+    # the chunk size the backward runs at (a per-channel gate, and fp32 with
+    # K = 128, run chunk 64 problems at 32)
+    pe = GdrProblem.from_buffer_copy(p)
+    pe.chunk_size = int(lay.chunk_size)
+    views = workspace_views(pe, ws)
+    nt, C, HV, K, V = lay.fwd.nt_max, pe.chunk_size, p.HV, p.K, p.V
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 
@@ -551,6 +557,9 @@ def bwd_workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
         qscale=view(lay.qscale, (nt, HV, C), torch.float32, 4),
         dh=view(lay.dh, (nt, HV, V, K), torch.float32, 4),   # fp32
     )
+    if p.gate_per_channel:
+        views.update(kt=view(lay.kt, (nt, HV, C, K), dt, es), qg=view(lay.qg, (nt, HV, C, K), dt, es),
+                     dl=view(lay.dl, (nt, HV, K), torch.float32, 4))
     return views
 
 

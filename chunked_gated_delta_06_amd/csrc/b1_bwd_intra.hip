@@ -159,6 +159,189 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   }
 }
 
+// Per-channel gate (chunk 32): the same de_local, with
+//   P[r][t] = sum_d q^_rd k^_td exp(G_rd - G_td)        (t <= r)
+// formed on the vector ALU with the exact exponent of every difference
+// (G_rd - G_td <= 0 for a decay gate: no overflow, no reference row needed),
+// and, for the reverse scan, the chunk's gated operand rows and decay
+//   kt[t][d] = exp(G_Ld - G_td) k^_td      qg[t][d] = scale exp(G_td) q^_td
+//   dl[d]    = exp(G_Ld)
+// ([NT][HV][C][K] in the input dtype, zero past L; [NT][HV][K] fp32), which
+// take the place of the raw rows and the row factors of the scalar gate.
+// Four waves: P is split over the threads by (row, token group); de_local
+// blocks (token block w % 2, value blocks (w / 2) + 2 i) on MFMA with P^T as a
+// bf16 hi + lo pair.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void b1_bwd_intra_pc(Args a) {
+  constexpr int C = 32;
+  constexpr int NT = 256;
+  constexpr int CPR = K / 8;
+  constexpr int VT = 32;
+  constexpr int DP = VT + 32 / sizeof(T);
+  constexpr int KP = K + 16 / sizeof(T);
+  constexpr int GP = K + 1;
+  constexpr int PP = C + 32 / sizeof(T);          // P^T rows (hi / lo tiles)
+  constexpr int NPK = (C * CPR + NT - 1) / NT;
+  constexpr int NPD = (VT * C / 8 + NT - 1) / NT;
+  __shared__ float sRq[C], sRk[C];
+  __shared__ __attribute__((aligned(16))) float sG[C * GP];
+  __shared__ __attribute__((aligned(16))) T sQ[C * KP];
+  __shared__ __attribute__((aligned(16))) T sK[C * KP];
+  __shared__ __attribute__((aligned(16))) T sDO[C * DP];
+  __shared__ __attribute__((aligned(16))) T sPT[2 * C * PP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const ChunkHead ch = chunk_head(a.HV);
+  const int64_t c = ch.c, j = ch.j;
+  if (c >= a.chunk_off[a.N]) return;
+  const int64_t t0 = a.chunk_idx[4 * c + 1];
+  const int L = a.chunk_idx[4 * c + 2];
+  const int64_t H = a.H, HV = a.HV, V = a.V, h = j / (HV / H);
+  const T* __restrict__ qp = static_cast<const T*>(a.q);
+  const T* __restrict__ kp = static_cast<const T*>(a.k);
+  const T* __restrict__ dop = static_cast<const T*>(a.d_o);
+  T* __restrict__ dep = static_cast<T*>(a.de_local) + (c * HV + j) * V * (int64_t)C;
+  T* __restrict__ ktp = static_cast<T*>(a.kt) + (c * HV + j) * (int64_t)(C * K);
+  T* __restrict__ qgp = static_cast<T*>(a.qg) + (c * HV + j) * (int64_t)(C * K);
+  float* __restrict__ dlp = a.dl + (c * HV + j) * (int64_t)K;
+  const FTile<T> fPT = ftile<T, PP>(reinterpret_cast<char*>(sPT), C);
+
+  // ---- loads: q, k rows, the gate tile, the first dO tile
+  Frag<T> qreg[NPK], kreg[NPK];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    const bool in = idx < C * CPR && t < L;
+    qreg[i] = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+    kreg[i] = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+  }
+  for (int idx = tid; idx < C * K / 4; idx += NT) {
+    const int t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+    const f32x4 gv = (t < L) ? *reinterpret_cast<const f32x4*>(a.g + ((t0 + t) * HV + j) * K + d4) : zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sG[t * GP + d4 + e] = gv[e];
+  }
+  Frag<T> dreg[NPD];
+  auto fetch_tile = [&](int64_t v0) {
+#pragma unroll
+    for (int i = 0; i < NPD; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      dreg[i] = (idx < VT * C / 8 && t < L) ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
+    }
+  };
+  fetch_tile(0);
+
+  // ---- q / k tiles and their row norms; the gate cumsum down each column
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    const f32x8 xq = qreg[i].f32(), xk = kreg[i].f32();
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq += xq[e] * xq[e];
+      sk += xk[e] * xk[e];
+    }
+    sq = lanes_sum_t<CPR>(sq);
+    sk = lanes_sum_t<CPR>(sk);
+    if (idx < C * CPR) {
+      st8(&sQ[t * KP + d8], qreg[i]);
+      st8(&sK[t * KP + d8], kreg[i]);
+      if (d8 == 0) {
+        sRq[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+        sRk[t] = a.l2norm ? 1.f / sqrtf(sk + kL2Eps) : 1.f;
+      }
+    }
+  }
+  lds_barrier();
+  for (int d = tid; d < K; d += NT) {
+    float col[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) col[t] = sG[t * GP + d];
+#pragma unroll
+    for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+    for (int t = 0; t < C; ++t) sG[t * GP + d] = col[t];
+  }
+  lds_barrier();
+
+  // ---- the reverse scan's operands: kt, qg (zero past L) and dl
+  const float* GL = &sG[(L - 1) * GP];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) {
+    const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
+    if (idx < C * CPR) {
+      f32x8 xk = kreg[i].f32(), xq = qreg[i].f32();
+      const float rk = sRk[t], rq = sRq[t] * a.scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gt = sG[t * GP + d8 + e];
+        xk[e] = (t < L) ? xk[e] * rk * __expf(GL[d8 + e] - gt) : 0.f;
+        xq[e] = (t < L) ? xq[e] * rq * __expf(gt) : 0.f;
+      }
+      st8(ktp + t * K + d8, Frag<T>::make(xk));
+      st8(qgp + t * K + d8, Frag<T>::make(xq));
+    }
+  }
+  for (int d = tid; d < K; d += NT) dlp[d] = __expf(GL[d]);
+
+  // ---- P^T[t][r] = rq_r rk_t sum_d q_rd k_td exp(G_rd - G_td), t <= r < L:
+  //      thread (r = tid / 8, token group tid % 8) owns t = group + 8 m
+  {
+    const int r = tid >> 3, tg = tid & 7;
+    float acc[C / 8];
+#pragma unroll
+    for (int m = 0; m < C / 8; ++m) acc[m] = 0.f;
+    if (r < L) {
+      for (int d = 0; d < K; ++d) {
+        const float qv = to_float(sQ[r * KP + d]), gr = sG[r * GP + d];
+#pragma unroll
+        for (int m = 0; m < C / 8; ++m) {
+          const int t = tg + 8 * m;
+          if (t <= r) acc[m] += qv * to_float(sK[t * KP + d]) * __expf(gr - sG[t * GP + d]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < C / 8; ++m) {
+      const int t = tg + 8 * m;
+      fPT.put(t, r, (t <= r && r < L) ? acc[m] * sRq[r] * sRk[t] : 0.f);
+    }
+  }
+
+  // ---- de_local^T[v][t] = scale sum_r P^T[t][r] dO[r][v]
+  const int tb = wv & 1;
+  const float sc = a.scale;
+  for (int64_t v0 = 0; v0 < V; v0 += VT) {
+#pragma unroll
+    for (int i = 0; i < NPD; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      if (idx < VT * C / 8) st8(&sDO[t * DP + v8], dreg[i]);
+    }
+    lds_barrier();
+    if (v0 + VT < V) fetch_tile(v0 + VT);
+    {
+      const int vb = wv >> 1;
+      f32x4 acc = zero4();
+      mma_split(acc, fPT.row(16 * tb + r16, 0, lane), lds_col8(sDO, DP, 0, 16 * vb, lane));
+      st4(dep + (v0 + 16 * vb + r16) * C + 16 * tb + 4 * g4, acc * sc);
+    }
+    lds_barrier();
+  }
+}
+
+template <typename T>
+hipError_t launch_pc(const Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.NTmax * a.HV));
+  switch (a.K) {
+    case 32: hipLaunchKernelGGL((b1_bwd_intra_pc<T, 32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((b1_bwd_intra_pc<T, 64>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((b1_bwd_intra_pc<T, 128>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int C>
 hipError_t launch_k(const Args& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.NTmax * a.HV));
@@ -180,6 +363,10 @@ hipError_t launch_c(const Args& a, hipStream_t s) {
 
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s) {
   if (a.NTmax == 0) return hipSuccess;
+  if (a.per_channel) {
+    if (a.C != 32) return hipErrorInvalidValue;
+    return a.dtype == GDR_BF16 ? launch_pc<bf16>(a, s) : launch_pc<float>(a, s);
+  }
   return a.dtype == GDR_BF16 ? launch_c<bf16>(a, s) : launch_c<float>(a, s);
 }
 

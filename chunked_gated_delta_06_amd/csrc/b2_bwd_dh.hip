@@ -26,6 +26,12 @@
 // dO is multiplied by qscale while it is staged.  dE = K dS takes dS straight
 // from its accumulators as the B operand (chained contraction map); the dS
 // update reads q^T and w^T with transposed LDS reads.
+//
+// Per-channel gate (PC): the chunk's gate enters every feature separately,
+//   dE = de_local + Kt dS,   dS <- diag(exp(G_L)) dS + Qg^T dO - W^T dE,
+// with the gated rows kt = exp(G_L - G_t) k^_t and qg = scale exp(G_t) q^_t and
+// the decay dl = exp(G_L) that the intra-chunk stage wrote per chunk; they take
+// the place of the raw rows and the row factors kscale / qscale.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -33,7 +39,7 @@ namespace gdr {
 
 namespace {
 
-template <typename T, int C, int K, int NWC_, int NWL>
+template <typename T, int C, int K, int NWC_, int NWL, bool PC = false>
 struct B2S {
   static constexpr int NWC = NWC_;
   static constexpr int NTL = 64 * NWL;
@@ -46,13 +52,14 @@ struct B2S {
   static constexpr int NLO = (NPO + NTL - 1) / NTL;
   static constexpr int NPE = BV * C / 8;                // de_local pieces
   static constexpr int NLE = (NPE + NTL - 1) / NTL;
-  static constexpr int NKS = (C + 4) / 4;
+  static constexpr int NKS = PC ? K / 4 : (C + 4) / 4;   // float4 pieces of the row factors / decay
+  static constexpr int KSN = PC ? K : C + 4;
   static constexpr int KR = K + 16 / sizeof(T);         // k rows (row reads)
   static constexpr int KP = K + 32 / sizeof(T);         // q, w rows (transposed reads)
   static constexpr int OP = BV + 32 / sizeof(T);        // scaled dO rows (transposed reads)
   static constexpr int EP = C + 8 / sizeof(T);          // de_local rows (one per value column)
   static constexpr size_t buf_bytes =
-      ((size_t)C * (KR + 2 * KP) + (size_t)C * OP + (size_t)BV * EP) * sizeof(T) + (C + 4) * 4;
+      ((size_t)C * (KR + 2 * KP) + (size_t)C * OP + (size_t)BV * EP) * sizeof(T) + KSN * 4;
   static constexpr int NBUF = 2 * buf_bytes <= 160 * 1024 ? 2 : 1;
   static constexpr bool fits = NBUF * buf_bytes <= 160 * 1024 && NKS <= NTL;
 
@@ -70,13 +77,13 @@ struct B2S {
     T w[NBUF][C * KP];
     T o[NBUF][C * OP];
     T e[NBUF][BV * EP];
-    float ks[NBUF][C + 4];
+    float ks[NBUF][KSN];
   };
 };
 
-template <typename T, int C, int K, int NWC_, int NWL>
+template <typename T, int C, int K, int NWC_, int NWL, bool PC = false>
 __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
-  using Cfg = B2S<T, C, K, NWC_, NWL>;
+  using Cfg = B2S<T, C, K, NWC_, NWL, PC>;
   using Regs = typename Cfg::Regs;
   constexpr int NWC = Cfg::NWC, NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS;
   constexpr int KSK = Cfg::KSK, KSC = Cfg::KSC, CPR = Cfg::CPR, NLD = Cfg::NLD, NLO = Cfg::NLO;
@@ -115,8 +122,10 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
     const int64_t t0 = seq_t0 + (c - c_begin) * C;
     const int L = (int)((seq_end - t0) < C ? (seq_end - t0) : C);
     const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
-    const T* krow = kp + (t0 * H + h) * K;
-    const T* qrow = qp + (t0 * H + h) * K;
+    // scalar gate: raw rows of the input; per-channel: the chunk's gated rows
+    const T* krow = PC ? static_cast<const T*>(a.kt) + (c * HV + j) * (int64_t)(C * K) : kp + (t0 * H + h) * K;
+    const T* qrow = PC ? static_cast<const T*>(a.qg) + (c * HV + j) * (int64_t)(C * K) : qp + (t0 * H + h) * K;
+    const int rstride = PC ? K : (int)(H * K);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -126,8 +135,8 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       // rows past L load row L-1 and are zeroed when staged, pieces past the
       // tile load piece 0 and are never staged.
       const int tc = t < L ? t : L - 1;
-      R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));
-      R.q[i] = ld8(qrow + (tc * (int)(H * K) + d8));
+      R.k[i] = ld8(krow + (tc * rstride + d8));
+      R.q[i] = ld8(qrow + (tc * rstride + d8));
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
     }
     const T* orow = dop + (t0 * HV + j) * V + vw;
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       const bool in = (NPO % NTL == 0) || idx < NPO;
       const int tc = t < L ? t : L - 1;
       R.o[i] = ld8(orow + (tc * (int)(HV * V) + v8));
-      R.qs[i] = qsp[tc];
+      R.qs[i] = PC ? 1.f : qsp[tc];
     }
     const T* ep = debase + ((c * HV + j) * V + vw) * (int64_t)C;
 #pragma unroll
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       const int idx = tl + NTL * i;
       R.e[i] = ld8(ep + 8 * (((NPE % NTL == 0) || idx < NPE) ? idx : 0));
     }
-    const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
+    const float* ksp = PC ? a.dl + (c * HV + j) * (int64_t)K : a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
     R.L = L;
   };
@@ -163,9 +172,10 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
 #pragma unroll
     for (int i = 0; i < NLO; ++i) {
       const int idx = tl + NTL * i, t = idx / (BV / 8), v8 = (idx % (BV / 8)) * 8;
-      // rows past L: a zero row factor (the loaded row is a finite copy of row L-1)
+      // rows past L: a zero row factor (the loaded row is a finite copy of row
+      // L-1); per-channel: the gated q rows past L are zero instead
       const float qs = t < R.L ? R.qs[i] : 0.f;
-      if ((NPO % NTL == 0) || idx < NPO) st8(&sm.o[b][t * OP + v8], Frag<T>::make(R.o[i].f32() * qs));
+      if ((NPO % NTL == 0) || idx < NPO) st8(&sm.o[b][t * OP + v8], PC ? R.o[i] : Frag<T>::make(R.o[i].f32() * qs));
     }
 #pragma unroll
     for (int i = 0; i < NLE; ++i) {
@@ -230,10 +240,10 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
     const T* erow = &sm.e[b][(16 * wv + r16) * EP];
 #pragma unroll
     for (int eb = 0; eb < NE; ++eb) {
-      sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
+      sc[eb] = PC ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
       dl[eb] = ld4f(erow + 16 * eb + 4 * g4);
     }
-    const float gl = sm.ks[b][C];
+    const float gl = PC ? 1.f : sm.ks[b][C];
     // dh[c] = dS (fp32, transposed; feature blocks paired into 16-byte stores)
     float* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
 #pragma unroll
@@ -254,9 +264,15 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
     for (int kt = 0; kt < KSC; ++kt)
       nE[kt] = frag_from_halves<T>(-(E[2 * kt] * sc[2 * kt] + dl[2 * kt]),
                                    -(E[2 * kt + 1] * sc[2 * kt + 1] + dl[2 * kt + 1]));
-    // dS <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE
+    // dS <- exp(G_L) dS + Q^T diag(qscale) dO - W^T dE (per-channel: row d of
+    // dS decays by exp(G_Ld))
+    if constexpr (PC) {
 #pragma unroll
-    for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+      for (int mb = 0; mb < NS; ++mb) S[mb] *= *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * mb + 4 * g4]);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+    }
 #pragma unroll
     for (int mb = 0; mb < NS; ++mb)
 #pragma unroll
@@ -298,19 +314,20 @@ constexpr int loader_waves() {
   return x < 2 ? 2 : (x > 8 ? 8 : x);
 }
 
-template <typename T, int C, int K>
+template <typename T, int C, int K, bool PC = false>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   constexpr int NWL = loader_waves<T, C, K>();
-  if constexpr (!B2S<T, C, K, 2, NWL>::fits) {
+  if constexpr (!B2S<T, C, K, 2, NWL, PC>::fits) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
     // 32 value columns per workgroup, or 16 when the 32-column grid would
     // leave compute units idle (as the forward scan)
     const int64_t nblk32 = a.N * a.HV * (a.V / 32);
     if (nblk32 < kNumCUs) {
-      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 1, NWL>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s, a);
+      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 1, NWL, PC>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s,
+                         a);
     } else {
-      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 2, NWL>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
+      hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 2, NWL, PC>), dim3((unsigned)nblk32), dim3(64 * (2 + NWL)), 0, s, a);
     }
     return hipGetLastError();
   }
@@ -326,8 +343,21 @@ hipError_t launch_k(const Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// per-channel gate: chunk 32 (the backward runs a chunk-64 problem at 32)
+template <typename T>
+hipError_t launch_pc(const Args& a, hipStream_t s) {
+  if (a.C != 32) return hipErrorInvalidValue;
+  switch (a.K) {
+    case 32: return launch_t<T, 32, 32, true>(a, s);
+    case 64: return launch_t<T, 32, 64, true>(a, s);
+    case 128: return launch_t<T, 32, 128, true>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T>
 hipError_t launch_c(const Args& a, hipStream_t s) {
+  if (a.per_channel) return launch_pc<T>(a, s);
   return a.C == 32 ? launch_k<T, 32>(a, s) : launch_k<T, 64>(a, s);
 }
 
@@ -346,6 +376,16 @@ bool bwd_scan_fits(int dtype, int C, int K) {
   }
 #undef GDR_B2_FITS
   return ok;
+}
+
+bool bwd_scan_pc_fits(int dtype, int K) {
+  if (dtype == GDR_BF16)
+    return K == 32 ? B2S<bf16, 32, 32, 2, loader_waves<bf16, 32, 32>(), true>::fits
+         : K == 64 ? B2S<bf16, 32, 64, 2, loader_waves<bf16, 32, 64>(), true>::fits
+         : K == 128 ? B2S<bf16, 32, 128, 2, loader_waves<bf16, 32, 128>(), true>::fits : false;
+  return K == 32 ? B2S<float, 32, 32, 2, loader_waves<float, 32, 32>(), true>::fits
+       : K == 64 ? B2S<float, 32, 64, 2, loader_waves<float, 32, 64>(), true>::fits
+       : K == 128 ? B2S<float, 32, 128, 2, loader_waves<float, 32, 128>(), true>::fits : false;
 }
 
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s) {

@@ -93,15 +93,6 @@ struct B3 {
   static constexpr bool fits = total <= 160 * 1024;
 };
 
-template <typename T, int P>
-GDR_DEV FTile<T> ftile(char* base, int rows) {
-  FTile<T> f;
-  f.hi = reinterpret_cast<T*>(base);
-  f.lo = FTile<T>::kSplit ? reinterpret_cast<T*>(base + (size_t)rows * P * sizeof(T)) : nullptr;
-  f.pitch = P;
-  return f;
-}
-
 template <typename T, int C, int K, bool GVA, int NW>
 __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   using Cfg = B3<T, C, K, NW>;

@@ -10,8 +10,9 @@
 namespace gdr {
 
 bool bwd_shape_ok(const gdr_problem& p) {
-  if (p.gate_per_channel) return false;
   if (p.K != 32 && p.K != 64 && p.K != 128) return false;
+  if (p.gate_per_channel)
+    return p.chunk_size == 32 && bwd_scan_pc_fits(p.dtype, (int)p.K) && bwd_pc_fits(p.dtype, (int)p.K);
   return bwd_scan_fits(p.dtype, p.chunk_size, (int)p.K) && bwd_fused_fits(p.dtype, p.chunk_size, (int)p.K);
 }
 
@@ -163,6 +164,7 @@ gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_
 gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
   gdr_bwd_layout l;
   l.fwd = layout_of(p);
+  l.chunk_size = p.chunk_size;
   const int64_t nt = l.fwd.nt_max;
   const size_t es = elem_size(p);
   const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V;
@@ -173,6 +175,14 @@ gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * C * sizeof(float));
   l.dh = off;  // fp32
   off = round_up(off + (size_t)nt * HV * V * K * sizeof(float));
+  // per-channel gate: the chunk's gated rows and decay for the reverse scan
+  const size_t pc = p.gate_per_channel ? 1 : 0;
+  l.kt = off;
+  off = round_up(off + pc * (size_t)nt * HV * C * K * es);
+  l.qg = off;
+  off = round_up(off + pc * (size_t)nt * HV * C * K * es);
+  l.dl = off;
+  off = round_up(off + pc * (size_t)nt * HV * K * sizeof(float));
   l.total = off;
   return l;
 }
@@ -226,7 +236,7 @@ gdr_status check_bwd(const gdr_problem* p, bool varlen, bool allow_pad = false) 
 // Padded copies of the inputs and outputs of a problem whose head dims are not
 // instantiated, placed after the padded problem's own workspace (base).
 struct PadLayout {
-  size_t q, k, v, g, h0, o, ht, d_o, dht, dq, dk, dv, dh0, total;
+  size_t q, k, v, g, h0, o, ht, d_o, dht, dq, dk, dv, dh0, dg, total;
 };
 
 PadLayout pad_layout(const gdr_problem& p, size_t base, bool bwd) {
@@ -254,6 +264,7 @@ PadLayout pad_layout(const gdr_problem& p, size_t base, bool bwd) {
   l.dk = take(bwd ? BT * H * Kp * es : 0);
   l.dv = take(bwd ? BT * HV * Vp * es : 0);
   l.dh0 = take(bwd ? N * HV * Kp * Vp * sizeof(float) : 0);
+  l.dg = take(bwd && p.gate_per_channel ? BT * HV * Kp * sizeof(float) : 0);
   l.total = off;
   return l;
 }
@@ -340,6 +351,13 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.dg = dg;
   a.dbeta = dbeta;
   a.u_f32 = 1;   // u from the separate WY stage (recomputed here, or kept by the forward)
+  if (p.gate_per_channel) {
+    a.kscale = nullptr;
+    a.qscale = nullptr;
+    a.kt = ws + l.kt;
+    a.qg = ws + l.qg;
+    a.dl = reinterpret_cast<float*>(ws + l.dl);
+  }
   hipError_t e = hipSuccess;
   if (!p.keep_states) {
     // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
@@ -350,7 +368,7 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   }
   if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
   if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
-  if (e == hipSuccess) e = gdr::launch_bwd_dqkvg(a, s);
+  if (e == hipSuccess) e = p.gate_per_channel ? gdr::launch_bwd_dqkvg_pc(a, s) : gdr::launch_bwd_dqkvg(a, s);
   return e;
 }
 
@@ -448,8 +466,9 @@ const char* gdr_status_string(gdr_status s) {
       return "gdr_chunk_fwd_noalloc: the problem needs more than the fixed scratch of GDR_NOALLOC_SCRATCH_BYTES "
              "(use gdr_chunk_fwd with a workspace)";
     case GDR_ERR_UNSUPPORTED:
-      return "backward supports a scalar gate with K in {32, 64, 128} (fp32 with K = 128 runs at chunk_size 32, "
-             "so a saved-state backward there needs a chunk_size 32 forward)";
+      return "backward supports K in {32, 64, 128} (a per-channel gate, and fp32 with K = 128, run at chunk_size "
+             "32, so a saved-state backward there needs a chunk_size 32 forward; the per-stage backward entry "
+             "points take a scalar gate only)";
   }
   return "unknown status";
 }
@@ -908,11 +927,15 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (e == hipSuccess) e = gdr::launch_pad(d_o, ws + pl.d_o, BT * HV, 1, V, 1, Vp, es, s);
   if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
   if (e == hipSuccess && dht != nullptr) e = gdr::launch_pad(dht, ws + pl.dht, N * HV, K, V, Kp, Vp, 4, s);
+  const bool pc = p->gate_per_channel != 0;
+  if (e == hipSuccess && pc) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
   if (e == hipSuccess)
-    e = bwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v, g, beta, cu_seqlens,
-                h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.d_o,
+    e = bwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v, pc ? reinterpret_cast<const float*>(ws + pl.g) : g, beta,
+                cu_seqlens, h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.d_o,
                 dht != nullptr ? reinterpret_cast<const float*>(ws + pl.dht) : nullptr, ws + pl.dq, ws + pl.dk,
-                ws + pl.dv, dg, dbeta, dh0 != nullptr ? reinterpret_cast<float*>(ws + pl.dh0) : nullptr, ws, l, s);
+                ws + pl.dv, pc ? reinterpret_cast<float*>(ws + pl.dg) : dg, dbeta,
+                dh0 != nullptr ? reinterpret_cast<float*>(ws + pl.dh0) : nullptr, ws, l, s);
+  if (e == hipSuccess && pc) e = gdr::launch_unpad(ws + pl.dg, dg, BT * HV, 1, K, 1, Kp, 4, s);
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dq, dq, BT * H, 1, K, 1, Kp, es, s);
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dk, dk, BT * H, 1, K, 1, Kp, es, s);
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dv, dv, BT * HV, 1, V, 1, Vp, es, s);
@@ -937,6 +960,7 @@ gdr_status gdr_bwd_intra(const gdr_problem* p, const void* q, const void* k, con
                          void* stream) {
   gdr_status st = bwd_stage_common(p, {q, k, g, d_o, chunk_idx, chunk_off, de_local, qscale});
   if (st != GDR_OK) return st;
+  if (p->gate_per_channel) return GDR_ERR_UNSUPPORTED;
   Args a = make_args(*p);
   a.q = q;
   a.k = k;
@@ -954,6 +978,7 @@ gdr_status gdr_bwd_dh(const gdr_problem* p, const void* q, const void* k, const 
                       const int32_t* chunk_off, const float* dht, void* dh, float* dh0, void* stream) {
   gdr_status st = bwd_stage_common(p, {q, k, w, d_o, de_local, qscale, kscale, chunk_idx, chunk_off, dh});
   if (st != GDR_OK) return st;
+  if (p->gate_per_channel) return GDR_ERR_UNSUPPORTED;
   if ((dht && !aligned16(dht)) || (dh0 && !aligned16(dh0))) return GDR_ERR_ALIGNMENT;
   Args a = make_args(*p);
   a.q = q;
@@ -978,6 +1003,7 @@ gdr_status gdr_bwd_dqkvg(const gdr_problem* p, const void* q, const void* k, con
   gdr_status st = bwd_stage_common(
       p, {q, k, v, g, beta, d_o, Tm, h, v_new, dh, chunk_idx, chunk_off, dq, dk, dv, dg, dbeta});
   if (st != GDR_OK) return st;
+  if (p->gate_per_channel) return GDR_ERR_UNSUPPORTED;
   Args a = make_args(*p);
   a.q = q;
   a.k = k;

@@ -263,6 +263,17 @@ template <typename T> struct FTile {
   }
 };
 
+// An FTile of `rows` rows of pitch P at `base` (the lo tile, when there is
+// one, follows the hi tile).
+template <typename T, int P>
+GDR_DEV FTile<T> ftile(char* base, int rows) {
+  FTile<T> f;
+  f.hi = reinterpret_cast<T*>(base);
+  f.lo = FTile<T>::kSplit ? reinterpret_cast<T*>(base + (size_t)rows * P * sizeof(T)) : nullptr;
+  f.pitch = P;
+  return f;
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // fences global memory, which makes the compiler wait for every outstanding
 // global load and store (s_waitcnt vmcnt(0)) and so drains software-pipelined

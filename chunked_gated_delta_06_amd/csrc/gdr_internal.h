@@ -67,6 +67,12 @@ struct Args {
   void* dv;
   float* dg;
   float* dbeta;
+  // backward with a per-channel gate: the chunk's gated operand rows for the
+  // reverse scan and B3, kt = exp(G_L - G_t) k^_t and qg = scale exp(G_t) q^_t
+  // ([NT][HV][C][K], input dtype), and the decay dl = exp(G_L) ([NT][HV][K])
+  void* kt;
+  void* qg;
+  float* dl;
 };
 
 int64_t nt_max(const gdr_problem& p);
@@ -102,11 +108,16 @@ hipError_t launch_merge(int64_t R, int64_t HV, int64_t K, int64_t V, const float
                         const float* h0, float* Sin, hipStream_t s);
 hipError_t launch_bwd_dh(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dqkvg(const Args& a, hipStream_t s);
+// per-channel gate (chunk 32): every gradient but dh / dh0 (reads kt from the
+// intra-chunk stage)
+hipError_t launch_bwd_dqkvg_pc(const Args& a, hipStream_t s);
 
-// Shapes the backward kernels take (scalar gate; LDS limits of the fused
-// kernel and of the reverse scan).
+// Shapes the backward kernels take (LDS limits of the fused kernel and of the
+// reverse scan; a per-channel gate at chunk 32).
 bool bwd_shape_ok(const gdr_problem& p);
 bool bwd_scan_fits(int dtype, int C, int K);
+bool bwd_scan_pc_fits(int dtype, int K);   // per-channel reverse scan at chunk 32
 bool bwd_fused_fits(int dtype, int C, int K);
+bool bwd_pc_fits(int dtype, int K);        // per-channel B3 at chunk 32
 
 }  // namespace gdr

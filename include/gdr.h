@@ -330,21 +330,27 @@ gdr_status gdr_chunk_fwd_segmented(const gdr_problem* p, const void* q, const vo
 /* ------------------------------------------------------------------ backward
  *
  * Gradients of L = sum(o * d_o) + sum(ht * dht) with respect to q, k, v, g,
- * beta and h0, for the same operator as gdr_chunk_fwd (scalar gate).  dq, dk
+ * beta and h0, for the same operator as gdr_chunk_fwd (scalar or per-channel gate).  dq, dk
  * are gradients with respect to q, k as passed (through the in-kernel L2 norm
  * when use_qk_l2norm is set), summed over the value heads of each GVA group;
- * dg is the gradient with respect to the per-token log gate g (not its cumsum).
+ * dg is the gradient with respect to the per-token log gate g (not its cumsum), per
+ * channel ([B,T,HV,K]) for a per-channel gate.
  *
  * Backward workspace: the forward intermediates at the offsets of `fwd`
  * (recomputed by the backward, so a forward workspace is not needed), plus
  *   de_local  dtype [NT_max][HV][V][C]  scale * P^T dO per chunk, transposed, with
  *                                       P[r][t] = q^_r . k^_t exp(G_r - G_t), t <= r
  *   qscale    f32   [NT_max][HV][C]     scale * exp(G_r) / |q_r| (0 past L)
+ *   kt, qg    dtype [NT_max][HV][C][K]  per-channel gate only: exp(G_L - G_t) k^_t and
+ *                                       scale exp(G_t) q^_t per chunk (zero past L)
+ *   dl        f32   [NT_max][HV][K]     per-channel gate only: exp(G_L) per chunk
  *   dh        f32   [NT_max][HV][V][K]  gradient of the state leaving each chunk,
  *                                       transposed (dh^T) */
 typedef struct {
   gdr_fwd_layout fwd;
-  size_t de_local, qscale, dh, total;
+  int64_t chunk_size;   /* the chunk size the backward runs at (32 where it switches, see
+                           gdr_chunk_bwd); the per-chunk layouts above use it */
+  size_t de_local, qscale, dh, kt, qg, dl, total;
 } gdr_bwd_layout;
 
 gdr_status gdr_bwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
@@ -360,14 +366,14 @@ gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* layout
  *   q, k, v, g, beta, cu_seqlens, h0   as gdr_chunk_fwd (h0 may be NULL = zeros)
  *   d_o   dtype [B,T,HV,V]            gradient of o
  *   dht   f32 [N,HV,K,V] or NULL       gradient of ht (NULL = zeros)
- *   dq, dk  dtype [B,T,H,K]   dv dtype [B,T,HV,V]   dg f32 [B,T,HV]   dbeta f32 [B,T,HV]
+ *   dq, dk  dtype [B,T,H,K]   dv dtype [B,T,HV,V]   dg f32 like g   dbeta f32 [B,T,HV]
  *   dh0   f32 [N,HV,K,V] or NULL       gradient of h0 (not wanted if NULL)
  *   workspace  >= gdr_bwd_workspace_bytes bytes (contents on entry irrelevant).
- * Supported: scalar gate (gate_per_channel = 0), K up to 128 (padded to 32, 64 or
- * 128), any V up to 256.  fp32 with K = 128 at chunk_size 64 runs the backward at
- * chunk 32 (the chunk form is exact at any chunk size; the workspace size
- * follows); with keep_states that switch is impossible and it returns
- * GDR_ERR_UNSUPPORTED.  Other problems return GDR_ERR_UNSUPPORTED before any
+ * Supported: K up to 128 (padded to 32, 64 or 128), any V up to 256, scalar or
+ * per-channel gate.  A per-channel gate, and fp32 with K = 128, at chunk_size 64
+ * run the backward at chunk 32 (the chunk form is exact at any chunk size; the
+ * workspace size follows); with keep_states that switch is impossible and it
+ * returns GDR_ERR_UNSUPPORTED.  Other problems return GDR_ERR_UNSUPPORTED before any
  * launch.
  * Saved forward states: with p->keep_states = 1 the recompute is skipped and
  * the forward intermediates are taken from the workspace as they stand, which
@@ -382,7 +388,8 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
                          void* dv, float* dg, float* dbeta, float* dh0, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* ---- the backward's stages (after K0-K3 of the forward, same layouts) ---- */
+/* ---- the backward's stages (after K0-K3 of the forward, same layouts; scalar
+ * gate only: with a per-channel gate they return GDR_ERR_UNSUPPORTED) ---- */
 
 /* B1: de_local = scale P^T dO and qscale for every chunk and value head
  * (differentiating o through the intra-chunk term of the chunk form on the

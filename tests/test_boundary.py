@@ -187,7 +187,9 @@ def test_python_wrapper_refuses_cpu_tensors():
     (dict(K=128, V=256, chunk_size=32), True),
     (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=32), True),
     (dict(dtype=gdr.GDR_FP32, K=64, chunk_size=64), True),
-    (dict(gate_per_channel=1), False),
+    (dict(gate_per_channel=1), True),                            # per-channel: runs at chunk 32 inside
+    (dict(gate_per_channel=1, chunk_size=32, K=128, V=256), True),
+    (dict(gate_per_channel=1, keep_states=1), False),            # chunk 64 kept states cannot switch
     (dict(K=256), False),
     (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64), True),     # runs at chunk 32 inside
     (dict(dtype=gdr.GDR_FP32, K=128, chunk_size=64, keep_states=1), False),
@@ -201,6 +203,13 @@ def test_bwd_supported_shapes(kw, ok):
     else:
         with pytest.raises(ValueError, match="backward supports"):
             gdr.bwd_layout(p)
+
+
+def test_bwd_layout_reports_the_chunk_size_it_runs_at():
+    assert gdr.bwd_layout(problem()).chunk_size == 64
+    assert gdr.bwd_layout(problem(gate_per_channel=1)).chunk_size == 32
+    assert gdr.bwd_layout(problem(dtype=gdr.GDR_FP32, K=128)).chunk_size == 32
+    assert gdr.bwd_layout(problem(gate_per_channel=1, chunk_size=32)).chunk_size == 32
 
 
 def test_bwd_workspace_layout():
@@ -239,7 +248,7 @@ def test_bwd_rejects_before_launch():
     assert L.gdr_chunk_bwd(ctypes.byref(p), *args, a, big, None) == 6
     assert L.gdr_chunk_bwd(ctypes.byref(p), *base, a, ctypes.c_size_t(64), None) == 7
     assert L.gdr_chunk_bwd(ctypes.byref(p), *base, None, big, None) == 7
-    ppc = problem(gate_per_channel=1)
+    ppc = problem(K=256)                       # no backward instantiation: refused on the host
     assert L.gdr_chunk_bwd(ctypes.byref(ppc), *base, a, big, None) == 10
     p16 = problem(chunk_size=16)
     assert L.gdr_chunk_bwd(ctypes.byref(p16), *base, a, big, None) == 2

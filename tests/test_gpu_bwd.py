@@ -24,8 +24,8 @@ GRADS = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
 def mk(name="b", B=2, T=200, H=2, HV=2, K=64, V=64, C=64, dtype="bf16", l2=True, h0=True,
-       slow=False, lengths=None, scale=1.0, seed=11, host_l2=False):
-    w = W(name, B=B, T=T, H=H, HV=HV, K=K, V=V, chunk_size=C, dtype=dtype, per_channel_gate=False,
+       slow=False, lengths=None, scale=1.0, seed=11, host_l2=False, pc=False):
+    w = W(name, B=B, T=T, H=H, HV=HV, K=K, V=V, chunk_size=C, dtype=dtype, per_channel_gate=pc,
           l2norm_in_kernel=l2, host_l2norm=host_l2, h0=h0, slow_decay=slow, scale=scale, backward=True)
     return w, workloads.make_inputs(w, seed=seed, lengths=lengths)
 
@@ -263,11 +263,17 @@ def test_bwd_reuses_saved_forward_states(varlen):
 
 
 def test_bwd_unsupported_shapes_raise():
-    w, inp = mk(T=64, K=64, V=64, C=64)
-    gpc = torch.zeros(2, 64, 2, 64, device="cuda")
+    """K = 256 has no backward instantiation; a per-channel gate through the
+    per-stage entry points (which take no gated rows) is refused too."""
+    w, inp = mk(T=64, K=256, V=64, C=64)
     with pytest.raises(ValueError, match="backward supports"):
-        gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), gpc, dev(inp["beta"]),
+        gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
                       dev(inp["do"]), None, chunk_size=64)
+    w, inp = mk(T=64, K=64, V=64, C=32, pc=True)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, use_qk_l2norm=True)
+    x = torch.zeros(1024, device="cuda")
+    with pytest.raises(ValueError, match="backward supports"):
+        gdr.bwd_intra(p, dev(inp["q"]), dev(inp["k"]), dev(inp["g"]), dev(inp["do"]), x, x, x, x)
 
 
 def test_bwd_varlen_equals_dense_rows():
@@ -395,3 +401,92 @@ def test_bwd_fp32_k128_chunk64_runs_at_chunk32():
     w, inp = mk(B=1, T=150, H=2, HV=2, K=128, V=64, C=64, dtype="fp32", slow=True)
     got, _, _ = gpu_bwd(inp)
     compare(got, oracle_bwd(inp), TOL["fp32"])
+
+
+# ------------------------------------------------------------------ per-channel gate (KDA-style)
+
+PC_SWEEP = [
+    dict(dtype="bf16", K=128, V=256, C=32, H=2, HV=2),
+    dict(dtype="bf16", K=64, V=32, C=32, H=1, HV=4),
+    dict(dtype="bf16", K=32, V=64, C=32, H=2, HV=2, l2=False, host_l2=True),
+    dict(dtype="bf16", K=128, V=64, C=64, H=2, HV=4),                      # chunk 64 runs at 32
+    dict(dtype="fp32", K=64, V=128, C=32, H=2, HV=2),
+    dict(dtype="fp32", K=128, V=32, C=32, H=1, HV=2),
+    dict(dtype="fp32", K=32, V=32, C=64, H=2, HV=2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PC_SWEEP)))
+def test_bwd_per_channel_sweep(case):
+    """The per-channel gate's backward (dg per channel, [B,T,HV,K]) on a ragged
+    dense batch with slow decay and h0 / dht, against the chunk-wise oracle."""
+    kw = PC_SWEEP[case]
+    w, inp = mk(**kw, T=150, pc=True, slow=True, scale=kw["K"] ** -0.5, seed=40 + case)
+    got, _, _ = gpu_bwd(inp)
+    assert got["dg"].shape == tuple(inp["g"].shape)
+    compare(got, oracle_bwd(inp), TOL[w.dtype])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_per_channel_varlen(dtype):
+    lengths = [0, 1, 31, 32, 33, 100, 0, 7, 70]
+    w, inp = mk(dtype=dtype, B=1, T=sum(lengths), H=2, HV=4, K=64, V=64, C=32, lengths=lengths, pc=True,
+                slow=True, seed=6)
+    got, _, _ = gpu_bwd(inp)
+    ref = oracle_bwd(inp)
+    compare(got, ref, TOL[dtype])
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lengths)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e - s < 16:
+            continue
+        for name in ("dq", "dk", "dv", "dg"):
+            check(f"{name} seq {n}", got[name][:, s:e], ref[name][:, s:e], TOL[dtype])
+
+
+def test_bwd_per_channel_intermediates():
+    """The per-channel intra-chunk stage's de_local and the reverse scan's dh
+    against the oracle's chunk-wise intermediates."""
+    w, inp = mk(B=1, T=100, H=2, HV=2, K=64, V=64, C=32, pc=True, slow=True, seed=8)
+    got, views, _ = gpu_bwd(inp)
+    ref = oracle_bwd(inp, intermediates=True)
+    it = ref["inter"]
+    NT = int(it["off"][-1])
+    check("de_local", f64(views["de_local"][:NT].transpose(-1, -2)), it["dEi"], TOL["bf16"])
+    check("dh", f64(views["dh"][:NT].transpose(-1, -2)), it["dh"], TOL["bf16"])
+    compare(got, ref, TOL["bf16"])
+
+
+def test_bwd_per_channel_gate_equal_channels_is_scalar():
+    """A per-channel gate whose channels are all equal is the scalar gate: its
+    dg summed over the channels equals the scalar backward's dg, and the other
+    gradients agree, within the bf16 tolerance."""
+    w, inp = mk(B=2, T=130, H=2, HV=2, K=64, V=64, C=32, slow=True, seed=12)
+    got_s, _, _ = gpu_bwd(inp)
+    pinp = dict(inp, g=inp["g"][..., None].expand(*inp["g"].shape, 64).contiguous())
+    got_p, _, _ = gpu_bwd(pinp)
+    for n in ("dq", "dk", "dv", "dbeta", "dh0"):
+        check(n, got_p[n], got_s[n], TOL["bf16"])
+    check("dg (channel sum)", got_p["dg"].sum(-1), got_s["dg"], TOL["bf16"])
+
+
+@pytest.mark.timeout(300)
+def test_config_kda_shaped_backward():
+    """The KDA workload's shape (H = HV = 32, K = 128, V = 256, chunk 32, per-
+    channel gate, host-normalised q / k, no h0) with 2 x 1024 tokens, do and
+    dht ~ N(0, 1), against the chunk-wise oracle on two sampled heads."""
+    base = workloads.CONFIGS["kda_bf16"]
+    w = workloads.small(base, T=1024, backward=True)
+    inp = workloads.make_inputs(w)
+    res = gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                        dev(inp["do"]), dev(inp["dht"]), scale=inp["scale"], chunk_size=w.chunk_size,
+                        initial_state=None, use_qk_l2norm_in_kernel=False)
+    torch.cuda.synchronize()
+    for n, t in zip(GRADS, res):
+        assert bool(torch.isfinite(t).all()), n
+    heads = [3, 30]
+    got = {n: f64(t[:, :, heads] if n != "dh0" else t[:, heads]) for n, t in zip(GRADS, res)}
+    sub = slice_inputs(inp, heads=heads)
+    ref = chunked.chunked_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"], sub["dht"],
+                              scale=inp["scale"], h0=None, use_qk_l2norm=False, chunk_size=w.chunk_size)
+    compare(got, ref, TOL[w.dtype])
