@@ -122,6 +122,12 @@ def flops_per_token_head(w, part):
     K, V, C = w.K, w.V, w.chunk_size
     fwd = 3 * C * K + 2 * C * V + 6 * K * V + C * C / 3
     bwd = 7 * C * K + 5 * C * V + 14 * K * V
+    if w.per_channel_gate:
+        # the gated pair sums (P in the intra-chunk stage; dq, dk through P and
+        # A in B3) run on the vector ALU and are not matrix-core FLOPs:
+        # P^T dO CV (B1); 6KV (B2); Kt dS1 2KV, Y CV, dQg / TdW / dKt 6KV,
+        # dP CV, dA CV (B3)
+        bwd = 4 * C * V + 14 * K * V
     return {"forward": fwd, "bwd": bwd}[part]
 
 
@@ -132,6 +138,18 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
     fwd = stage_bytes_per_token_head(w, T_seq)
+    if w.per_channel_gate:
+        return {
+            "kkt_solve": fwd["kkt_solve"],
+            "wy": fwd["wy"],
+            "fwd_h": fwd["fwd_h"] - 4 * K * V / T_seq,
+            # q, k, g, dO -> de_local, the gated rows kt, qg and the decay dl
+            "bwd_intra": 2 * r * K * e + 4 * K + V * e + V * e + 2 * K * e + 4 * K / C,
+            # kt, qg, w, dO, de_local, dl, dht -> dh (fp32), dh0
+            "bwd_dh": 3 * K * e + 2 * V * e + 4 * K / C + 4 * K * V / C + 8 * K * V / T_seq,
+            # q, k, v, g, beta, dO, Tm, h, v_new, dh (fp32), de_local, kt -> dq, dk, dv, dg, dbeta
+            "bwd_dqkvg": 4 * r * K * e + 5 * V * e + 8 * K + 8 + e * C + e * K * V / C + 4 * K * V / C + K * e,
+        }
     return {
         "kkt_solve": fwd["kkt_solve"],
         "wy": fwd["wy"],
@@ -227,7 +245,8 @@ def cpu_baseline_bwd(w, inp, T=4096, heads=(0, 21)):
     sub = {n: inp[n][:, :T][:, :, hs].contiguous() for n in ("q", "k", "v", "g", "beta", "do")}
     t0 = time.perf_counter()
     recurrent.recurrent_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["do"],
-                            inp["dht"][:, hs], scale=inp["scale"], h0=inp["h0"][:, hs],
+                            inp["dht"][:, hs], scale=inp["scale"],
+                            h0=inp["h0"][:, hs] if inp["h0"] is not None else None,
                             use_qk_l2norm=inp["use_qk_l2norm"])
     spent = time.perf_counter() - t0
     per_head_s = spent / len(hs)
@@ -292,6 +311,29 @@ def event_stage_ms(stream, stages, reps):
         for i, n in enumerate(names):
             acc[n] += evs[r][i].elapsed_time(evs[r][i + 1])
     return {n: acc[n] / reps for n in names}
+
+
+def call_stage_ms(gdr, call, reps):
+    """Average milliseconds per launch of each stage of a full library call,
+    from the HIP events the library records on its launch stream after every
+    stage (gdr_stage_timing), over ``reps`` calls run back to back after two
+    untimed ones, so that each interval is the stage's own GPU time."""
+    import torch
+    call()
+    call()
+    torch.cuda.synchronize()
+    gdr.stage_timing(True)
+    try:
+        for _ in range(reps):
+            call()
+        rec = gdr.stage_times()
+    finally:
+        gdr.stage_timing(False)
+    acc, cnt = {}, {}
+    for n, ms in rec:
+        acc[n] = acc.get(n, 0.0) + ms
+        cnt[n] = cnt.get(n, 0) + 1
+    return {n: acc[n] / cnt[n] for n in acc}
 
 
 def timed_calls(step, warmup, steps, stream):
@@ -362,7 +404,7 @@ def bwd_parity_gate(gdr, w, inp, dev, o, T=2048, heads=(0, 21)):
     from oracle.metrics import err_ratio
     hs = list(heads)
     sub = {n: inp[n][:, :T][:, :, hs].contiguous() for n in ("q", "k", "v", "g", "beta", "do")}
-    sub["h0"] = inp["h0"][:, hs].contiguous()
+    sub["h0"] = inp["h0"][:, hs].contiguous() if inp["h0"] is not None else None
     sub["dht"] = inp["dht"][:, hs].contiguous()
     d = to_dev(sub, dev, list(sub))
     res = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], d["dht"], scale=inp["scale"],
@@ -421,7 +463,7 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         blay = gdr.bwd_layout(p)
         bws = torch.empty(blay.total, dtype=torch.uint8, device=dev)
         grads = [torch.empty_like(d[n]) for n in ("q", "k", "v", "g", "beta")]
-        dh0 = torch.empty_like(d["h0"])
+        dh0 = torch.empty(inp["N"], w.HV, w.K, w.V, dtype=torch.float32, device=dev)
         bwd_args = (ctypes.byref(p), P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]),
                     P(d["cu_seqlens"]), P(d["h0"]), P(d["do"]), P(d["dht"]), *[P(t) for t in grads], P(dh0),
                     P(bws), ctypes.c_size_t(bws.numel()), sp)
@@ -455,39 +497,15 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     tokens = inp["B"] * inp["T"]
     value = tokens / (ms_per_step * 1e-3)
 
-    # per-stage launch times with events on the launch stream, same kernels and order
-    views = gdr.workspace_views(p, ws)
-    cidx, coff = views["chunk_idx"], views["chunk_off"]
-    fstages = {
-        "chunk_table": lambda: gdr.chunk_table(p, d["cu_seqlens"], cidx, coff),
-        "kkt_solve": lambda: gdr.fwd_kkt_solve(p, d["k"], d["g"], d["beta"], cidx, coff, views["Tm"],
-                                               views["kscale"]),
-        "wy": lambda: gdr.fwd_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff, views["Tm"], views["w"],
-                                 views["u"]),
-        "fwd_h": lambda: gdr.fwd_h(p, d["k"], views["w"], views["u"], d["g"], cidx, coff, d["h0"], views["h"],
-                                   views["v_new"], ht, views["kscale"]),
-        "fwd_o": lambda: gdr.fwd_o(p, d["q"], d["k"], views["v_new"], views["h"], d["g"], cidx, coff, o),
-        "fwd_h_o": lambda: gdr.fwd_h_o(p, d["q"], d["k"], views["w"], views["u_fused"], d["g"], views["kscale"],
-                                       cidx, coff, d["h0"], o, ht),
-    }
-    if not w.per_channel_gate:
-        fstages["kkt_wy"] = lambda: gdr.fwd_kkt_wy(p, d["k"], d["v"], d["g"], d["beta"], cidx, coff,
-                                                   views["w"], views["u_fused"], views["kscale"])
-    # the stages the timed step runs: the fused K1 + K2 and scan + output
-    # stages where the shape has them
-    fused = gdr.chunk_fwd_fused(p) and not backward
-    for name in (("kkt_solve", "wy", "fwd_h", "fwd_o") if fused else ("kkt_wy", "fwd_h_o")):
-        fstages.pop(name, None)
-    if fused and d["cu_seqlens"] is None:
-        # a dense batch's fused K1 + K2 stage writes the chunk table itself
-        fstages.pop("chunk_table")
-    fstages = {n: fstages[n] for n in ("chunk_table", "kkt_solve", "wy", "kkt_wy", "fwd_h", "fwd_o", "fwd_h_o")
-               if n in fstages}
+    # per-stage launch times: the library's own HIP events on the launch
+    # stream, inside the same calls the step makes
     reps = max(5, min(steps, 50))
-    fwd_ms = event_stage_ms(stream, fstages, reps)
+    fwd_call = (lambda: check_st(L.gdr_chunk_fwd(*fwd_keep_args))) if backward else \
+        (lambda: check_st(L.gdr_chunk_fwd(*fwd_args)))
+    fwd_ms = call_stage_ms(gdr, fwd_call, reps)
     T_seq = inp["B"] * inp["T"] / inp["N"]
     units = tokens * w.HV
-    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq).items() if k in fstages}
+    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq).items() if k in fwd_ms}
     rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
            "timing": {**timing, "what": "HIP events around each whole call on the launch stream; "
                                         "ms_per_step = median_ms; wall_ms = wall clock per step"},
@@ -496,20 +514,10 @@ def measure(gdr, w, steps, warmup, breakdown, label):
         rec.update(fractions(w, T_seq, units, ms_per_step, sum(per_unit.values()), False))
     rec["roofline"] = roofline(per_unit, fwd_ms, units, w.name, list(per_unit))
     if backward:
-        bv = gdr.bwd_workspace_views(p, bws)
-        bidx, boff = bv["chunk_idx"], bv["chunk_off"]
         # the backward's own stages (the step's forward leaves K0-K3's
         # intermediates in this workspace)
-        bstages = {
-            "bwd_intra": lambda: gdr.bwd_intra(p, d["q"], d["k"], d["g"], d["do"], bidx, boff, bv["de_local"],
-                                               bv["qscale"]),
-            "bwd_dh": lambda: gdr.bwd_dh(p, d["q"], d["k"], bv["w"], d["do"], bv["de_local"], bv["qscale"],
-                                         bv["kscale"], bidx, boff, d["dht"], bv["dh"], dh0),
-            "bwd_dqkvg": lambda: gdr.bwd_dqkvg(p, d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], bv["Tm"],
-                                               bv["h"], bv["v_new"], bv["dh"], bidx, boff, *grads),
-        }
-        bwd_ms = event_stage_ms(stream, bstages, reps)
-        bper = {k: v for k, v in bwd_stage_bytes_per_token_head(w, T_seq).items() if k in bstages}
+        bwd_ms = call_stage_ms(gdr, lambda: check_st(L.gdr_chunk_bwd(*bwd_keep_args)), reps)
+        bper = {k: v for k, v in bwd_stage_bytes_per_token_head(w, T_seq).items() if k in bwd_ms}
         rec["stage_ms"]["backward"] = bwd_ms
         bwd_total_ms = sum(bwd_ms.values())
         rec["backward_hbm_frac"] = sum(bper.values()) * units / (bwd_total_ms * 1e-3) / 1e9 / PEAK_HBM_GBS
@@ -787,11 +795,12 @@ def main():
         line["simple_gla"] = measure_simple_gla(gdr, w, args.steps, args.warmup)
     if not args.no_backward and w.name == "gdn_dense_bf16":
         # every other configuration of the operator: forward records for the
-        # tiny fp32, varlen GVA and per-channel (KDA) workloads, and the long
-        # sequence's forward + backward step (median of 50 event-timed calls
-        # after 10 warm-ups each, the workload's own parity gate first)
+        # tiny fp32, varlen GVA and per-channel (KDA) workloads, the long
+        # sequence's forward + backward step, and a forward + backward step on
+        # the KDA workload's shape (median of 50 event-timed calls after 10
+        # warm-ups each, the workload's own parity gate first)
         line["configs"] = {}
-        for name in ("tiny_fp32", "varlen_gva_bf16", "kda_bf16", "long_bf16"):
+        for name in ("tiny_fp32", "varlen_gva_bf16", "kda_bf16", "long_bf16", "kda_train_bf16"):
             torch.cuda.empty_cache()
             wc = workloads.CONFIGS[name]
             crec, cinp = measure(gdr, wc, 50, 10, args.breakdown, wc.name)

@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.gdr_fwd_workspace_layout.argtypes = [PP, ctypes.POINTER(GdrFwdLayout)]
         L.gdr_chunk_fwd.argtypes = [PP] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
         L.gdr_chunk_fwd_noalloc.argtypes = [PP] + [_P] * 9 + [_P]
+        L.gdr_stage_timing.argtypes = [ctypes.c_int]
+        L.gdr_stage_timing.restype = ctypes.c_int
+        L.gdr_stage_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.gdr_stage_times.restype = ctypes.c_int
         L.gdr_chunk_table.argtypes = [PP, _P, _P, _P, _P]
         L.gdr_fwd_kkt_solve.argtypes = [PP] + [_P] * 7 + [_P]
         L.gdr_fwd_wy.argtypes = [PP] + [_P] * 9 + [_P]
@@ -289,6 +293,24 @@ def chunk_fwd_noalloc(q, k, v, g, beta, *, out, scale: float = 1.0, chunk_size: 
                                        _ptr(cu_seqlens), _ptr(initial_state), _ptr(o), _ptr(ht),
                                        _stream(q.device)))
     return o, ht
+
+
+def stage_timing(enable: bool) -> None:
+    """Turn the library's per-stage HIP-event timing on (clearing what was
+    recorded) or off, for this thread."""
+    _raise(lib().gdr_stage_timing(int(bool(enable))))
+
+
+def stage_times(max_stages: int = 8192) -> list:
+    """[(stage name, milliseconds)] of every full forward / backward call timed
+    on this thread since stage_timing(True), in launch order (waits for the
+    last recorded event)."""
+    names = (ctypes.c_char_p * max_stages)()
+    ms = (ctypes.c_float * max_stages)()
+    n = lib().gdr_stage_times(names, ms, max_stages)
+    if n < 0:
+        raise GdrError(8, "stage timing: HIP error")
+    return [(names[i].decode(), float(ms[i])) for i in range(n)]
 
 
 def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:

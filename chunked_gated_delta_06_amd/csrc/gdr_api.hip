@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "gdr_internal.h"
 
@@ -29,6 +30,41 @@ int64_t nt_max(const gdr_problem& p) {
 using gdr::Args;
 
 namespace {
+
+// ---- stage timing (measurement only, off by default; gdr_stage_timing): the
+// full forward and backward record a HIP event on their stream before their
+// first launch and after each stage, per host thread, into events created on
+// first use and kept; gdr_stage_times reads every stage interval recorded
+// since timing was (re)enabled.  names[i] is the stage that ends at event i,
+// or NULL where event i starts a call.
+constexpr size_t kMaxTimedEvents = 8192;
+struct StageTimer {
+  bool on = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> names;
+  size_t used = 0;
+};
+thread_local StageTimer t_timer;
+
+bool timer_record(hipStream_t s, const char* name) {
+  if (t_timer.used == kMaxTimedEvents) return false;
+  if (t_timer.used == t_timer.ev.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return false;
+    t_timer.ev.push_back(e);
+    t_timer.names.push_back(nullptr);
+  }
+  if (hipEventRecord(t_timer.ev[t_timer.used], s) != hipSuccess) return false;
+  t_timer.names[t_timer.used++] = name;
+  return true;
+}
+void timer_start(hipStream_t s) {
+  if (t_timer.on) timer_record(s, nullptr);
+}
+// the stage that ends here (after a successful launch)
+void timer_mark(hipError_t e, const char* name, hipStream_t s) {
+  if (t_timer.on && e == hipSuccess && t_timer.used > 0) timer_record(s, name);
+}
 
 bool head_dim_ok(int64_t d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -301,17 +337,25 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
       a.table_from_dims = 1;
     } else {
       e = gdr::launch_chunk_table(a, s);
+      timer_mark(e, "chunk_table", s);
     }
     if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
+    timer_mark(e, "kkt_wy", s);
     a.table_from_dims = 0;
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
+    timer_mark(e, "fwd_h_o", s);
   } else {
     a.u_f32 = 1;   // the separate WY stage writes u in fp32
     e = gdr::launch_chunk_table(a, s);
+    timer_mark(e, "chunk_table", s);
     if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    timer_mark(e, "kkt_solve", s);
     if (e == hipSuccess) e = gdr::launch_wy(a, s);
+    timer_mark(e, "wy", s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+    timer_mark(e, "fwd_h", s);
     if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+    timer_mark(e, "fwd_o", s);
   }
   return e;
 }
@@ -362,13 +406,20 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   if (!p.keep_states) {
     // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
     e = gdr::launch_chunk_table(a, s);
+    timer_mark(e, "chunk_table", s);
     if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    timer_mark(e, "kkt_solve", s);
     if (e == hipSuccess) e = gdr::launch_wy(a, s);
+    timer_mark(e, "wy", s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+    timer_mark(e, "fwd_h", s);
   }
   if (e == hipSuccess) e = gdr::launch_bwd_intra(a, s);
+  timer_mark(e, "bwd_intra", s);
   if (e == hipSuccess) e = gdr::launch_bwd_dh(a, s);
+  timer_mark(e, "bwd_dh", s);
   if (e == hipSuccess) e = p.gate_per_channel ? gdr::launch_bwd_dqkvg_pc(a, s) : gdr::launch_bwd_dqkvg(a, s);
+  timer_mark(e, "bwd_dqkvg", s);
   return e;
 }
 
@@ -421,6 +472,7 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
                          char* ws, const gdr_fwd_layout& l, hipStream_t s) {
   const gdr_problem* p = &p0;
   const gdr_problem pp = padded_problem(*p);
+  timer_start(s);
   if (!needs_pad(*p)) return hip_status(fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, ws, l, s));
   const PadLayout pl = pad_layout(*p, l.total, false);
   // head dims without an instantiation: zero-padded copies in, padded problem, copies out
@@ -431,6 +483,7 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
   if (e == hipSuccess) e = gdr::launch_pad(v, ws + pl.v, BT * HV, 1, V, 1, Vp, es, s);
   if (e == hipSuccess && p->gate_per_channel) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
   if (e == hipSuccess && h0 != nullptr) e = gdr::launch_pad(h0, ws + pl.h0, N * HV, K, V, Kp, Vp, 4, s);
+  timer_mark(e, "pad", s);
   if (e == hipSuccess)
     e = fwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v,
                 p->gate_per_channel ? reinterpret_cast<const float*>(ws + pl.g) : g, beta, cu_seqlens,
@@ -438,6 +491,7 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
                 ht != nullptr ? reinterpret_cast<float*>(ws + pl.ht) : nullptr, ws, l, s);
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.o, o, BT * HV, 1, V, 1, Vp, es, s);
   if (e == hipSuccess && ht != nullptr) e = gdr::launch_unpad(ws + pl.ht, ht, N * HV, K, V, Kp, Vp, 4, s);
+  timer_mark(e, "unpad", s);
   return hip_status(e);
 }
 
@@ -447,6 +501,26 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
 extern "C" {
 
 int gdr_abi_version(void) { return 4; }
+
+gdr_status gdr_stage_timing(int enable) {
+  t_timer.on = enable != 0;
+  t_timer.used = 0;
+  return GDR_OK;
+}
+
+int gdr_stage_times(const char** names, float* ms, int max_stages) {
+  if (!t_timer.on || t_timer.used < 2 || names == nullptr || ms == nullptr) return 0;
+  if (hipEventSynchronize(t_timer.ev[t_timer.used - 1]) != hipSuccess) return -1;
+  int n = 0;
+  for (size_t i = 1; i < t_timer.used && n < max_stages; ++i) {
+    if (t_timer.names[i] == nullptr) continue;   // a call starts here
+    float x = 0.f;
+    if (hipEventElapsedTime(&x, t_timer.ev[i - 1], t_timer.ev[i]) != hipSuccess) return -1;
+    names[n] = t_timer.names[i];
+    ms[n++] = x;
+  }
+  return n;
+}
 
 const char* gdr_status_string(gdr_status s) {
   switch (s) {
@@ -915,6 +989,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (workspace == nullptr || workspace_bytes < (pad ? pl.total : l.total)) return GDR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  timer_start(s);
   if (!pad)
     return hip_status(bwd_run(pp, q, k, v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg, dbeta, dh0, ws, l, s));
 
@@ -929,6 +1004,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (e == hipSuccess && dht != nullptr) e = gdr::launch_pad(dht, ws + pl.dht, N * HV, K, V, Kp, Vp, 4, s);
   const bool pc = p->gate_per_channel != 0;
   if (e == hipSuccess && pc) e = gdr::launch_pad(g, ws + pl.g, BT * HV, 1, K, 1, Kp, 4, s);
+  timer_mark(e, "pad", s);
   if (e == hipSuccess)
     e = bwd_run(pp, ws + pl.q, ws + pl.k, ws + pl.v, pc ? reinterpret_cast<const float*>(ws + pl.g) : g, beta,
                 cu_seqlens, h0 != nullptr ? reinterpret_cast<const float*>(ws + pl.h0) : nullptr, ws + pl.d_o,
@@ -940,6 +1016,7 @@ gdr_status gdr_chunk_bwd(const gdr_problem* p, const void* q, const void* k, con
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dk, dk, BT * H, 1, K, 1, Kp, es, s);
   if (e == hipSuccess) e = gdr::launch_unpad(ws + pl.dv, dv, BT * HV, 1, V, 1, Vp, es, s);
   if (e == hipSuccess && dh0 != nullptr) e = gdr::launch_unpad(ws + pl.dh0, dh0, N * HV, K, V, Kp, Vp, 4, s);
+  timer_mark(e, "unpad", s);
   return hip_status(e);
 }
 

@@ -118,6 +118,21 @@ typedef struct {
 /* ABI version of this header (bumped on incompatible changes). */
 int gdr_abi_version(void);
 
+/* Stage timing, for measurement: gdr_stage_timing(1) turns it on (and clears
+ * what was recorded), 0 turns it off.  While on, every gdr_chunk_fwd,
+ * gdr_chunk_fwd_noalloc and gdr_chunk_bwd call on this host thread records a
+ * HIP event on its stream before its first launch and after each stage (events
+ * created on first use and kept; at most 8192 per recording).  gdr_stage_times
+ * waits for the last recorded event and writes, in launch order, up to
+ * max_stages (stage name, milliseconds) pairs of every call since timing was
+ * turned on: names are static strings ("chunk_table", "kkt_solve", "wy",
+ * "kkt_wy", "fwd_h", "fwd_o", "fwd_h_o", "bwd_intra", "bwd_dh", "bwd_dqkvg",
+ * "pad", "unpad").  It returns the count (0 when off or nothing was recorded,
+ * -1 on a HIP error).  Calls timed back to back keep the stream busy, so each
+ * interval is the stage's own time on the GPU. */
+gdr_status gdr_stage_timing(int enable);
+int gdr_stage_times(const char** names, float* ms, int max_stages);
+
 /* Human-readable name of a status code (static string). */
 const char* gdr_status_string(gdr_status s);
 

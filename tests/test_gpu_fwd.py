@@ -560,3 +560,27 @@ def test_per_channel_scan_four_wave_grid_k32(dtype):
     ro, rht = oracle_fwd(inp)
     check("o", f64(o), ro, TOL[dtype])
     check("ht", f64(ht), rht, TOL[dtype])
+
+
+def test_stage_timing_reports_the_stages_each_call_runs():
+    """gdr_stage_timing / gdr_stage_times: the stages of every call since
+    timing was turned on, in launch order, with positive durations; nothing
+    once it is off."""
+    w, inp = mk(B=2, T=200, H=2, HV=2, K=128, V=128, C=64)
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "beta", "h0")}
+    kw = dict(chunk_size=64, initial_state=d["h0"], use_qk_l2norm_in_kernel=True)
+    gdr.stage_timing(True)
+    try:
+        for _ in range(2):
+            gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], **kw)
+        fused = gdr.stage_times()
+        gdr.stage_timing(True)
+        gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], keep_states=True, **kw)
+        sep = gdr.stage_times()
+    finally:
+        gdr.stage_timing(False)
+    assert [n for n, _ in fused] == ["kkt_wy", "fwd_h_o"] * 2
+    assert [n for n, _ in sep] == ["chunk_table", "kkt_solve", "wy", "fwd_h", "fwd_o"]
+    assert all(ms > 0 for _, ms in fused + sep)
+    gdr.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], **kw)
+    assert gdr.stage_times() == []

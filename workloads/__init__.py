@@ -78,6 +78,11 @@ CONFIGS = {
                          dtype="bf16", per_channel_gate=True, host_l2norm=True, h0=False),
     "long_bf16": Workload("long_bf16", B=1, T=65536, H=32, HV=32, K=128, V=128, chunk_size=64,
                           dtype="bf16", l2norm_in_kernel=True, backward=True),
+    # a training step (forward + backward) on the per-channel workload's shape,
+    # with do, dht ~ N(0, 1) drawn after the inputs as for the long workload
+    "kda_train_bf16": Workload("kda_train_bf16", B=2, T=8192, H=32, HV=32, K=128, V=256, chunk_size=32,
+                               dtype="bf16", per_channel_gate=True, host_l2norm=True, h0=False,
+                               backward=True),
     # one decoding step of the token-by-token path: 256 sequences of one token,
     # each continuing from its own state (the varlen workload's head layout)
     "decode_gva_bf16": Workload("decode_gva_bf16", B=256, T=1, H=16, HV=32, K=128, V=128,
