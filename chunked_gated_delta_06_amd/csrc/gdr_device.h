@@ -335,6 +335,10 @@ GDR_DEV float group4_sum(float x) {
 
 constexpr float kL2Eps = 1e-6f;
 
+// log2(e): gates kept in log2 units go straight to the hardware 2^x
+constexpr float kLog2e = 1.4426950408889634f;
+GDR_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // beta as the operator uses it: the value passed, or its sigmoid when the
 // caller passes logits.
 GDR_DEV float beta_value(float x, int32_t logits) { return logits ? 1.f / (1.f + __expf(-x)) : x; }

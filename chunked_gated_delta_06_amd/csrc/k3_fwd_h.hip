@@ -337,7 +337,10 @@ struct K3S {
   // no vector-memory instructions at all (their stores would queue behind the
   // loaders' loads in the CU's memory pipeline and stall the MFMA chain).
   // Used when the two extra buffers fit next to the double-buffered tiles.
-  static constexpr int HSP = K + 16 / sizeof(T);  // staged h rows (one per value column)
+  // staged h rows (one per value column); the fused output reads them as
+  // 16-byte row pieces, which a 32-byte pad keeps free of bank conflicts (bf16;
+  // fp32 keeps 16 bytes so that its fused shapes still fit)
+  static constexpr int HSP = K + (NWO > 0 && sizeof(T) == 2 ? 32 : 16) / sizeof(T);
   static constexpr int VSP = C + 16 / sizeof(T);  // staged e rows
   static constexpr size_t stg_bytes = (size_t)BV * (HSP + VSP) * sizeof(T);
   static constexpr bool STG = 2 * (buf_bytes + stg_bytes) <= 160 * 1024;
@@ -345,8 +348,8 @@ struct K3S {
   static constexpr int NDV = (BV * C / 8 + NTL - 1) / NTL;   // staged e pieces per loader thread
   // fused output: the loaders also stage each chunk's q tile and gates
   static constexpr bool OUT = NWO > 0;
-  static constexpr int QP = K + 16 / sizeof(T);   // staged q rows
-  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 2 * C * 4 : 0;
+  static constexpr int QP = K + (sizeof(T) == 2 ? 32 : 16) / sizeof(T);   // staged q rows, padded as h
+  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 3 * C * 4 : 0;
   static constexpr bool fits_out = STG && 2 * (buf_bytes + stg_bytes + q_bytes) <= 160 * 1024;
 
   struct Regs {
@@ -355,6 +358,7 @@ struct K3S {
     Frag<UT> u[NLU];
     f32x4 ks;
     float g2;                 // G_t (threads < C) or 1 / |k_t| (threads C .. 2C - 1)
+    float rk2, gref;          // threads < C: 1 / |k_t| and G at the end of t's key block
     int64_t t0;
     int L;
   };
@@ -366,9 +370,12 @@ struct K3S {
     T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
     T es[STG ? 2 : 1][STG ? BV * VSP : 8];
     T q[OUT ? 2 : 1][OUT ? C * QP : 8];
-    // per token of the staged chunk: gate cumsum G_t and 1 / |k_t|
+    // per token of the staged chunk: gate cumsum G_t in log2 units, 1 / |k_t|
+    // and the column factor exp(G_e - G_t) / |k_t|, e the last token of t's
+    // key block (zero past L)
     __attribute__((aligned(16))) float gq[OUT ? 2 : 1][OUT ? C : 4];
     __attribute__((aligned(16))) float rk[OUT ? 2 : 1][OUT ? C : 4];
+    __attribute__((aligned(16))) float cf[OUT ? 2 : 1][OUT ? C : 4];
   };
 };
 
@@ -395,6 +402,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const bool loader = wv >= NWC + NWO;
   const bool outw = !loader && wv >= NWC;
+  const int oi = wv - NWC;                       // output wave index
   const int tl = tid - 64 * (NWC + NWO);         // loader thread index
   const int64_t H = a.H, HV = a.HV, V = a.V, N = a.N;
   const int64_t nvt = V / BV;
@@ -449,8 +457,16 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     }
     const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
-    // fused output: G_t and 1 / |k_t| of the chunk (K1's token factors)
-    if constexpr (OUT) R.g2 = ksp[C + 4 + (tl < 2 * C ? tl : 0)];
+    // fused output: G_t and 1 / |k_t| of the chunk (K1's token factors), and
+    // for the column factor G at the end of t's key block (the chunk's last
+    // token when the block runs past it)
+    if constexpr (OUT) {
+      R.g2 = ksp[C + 4 + (tl < 2 * C ? tl : 0)];
+      const int tc = tl < C ? tl : 0;
+      const int te = (tc | 15) < R.L - 1 ? (tc | 15) : R.L - 1;
+      R.rk2 = ksp[2 * C + 4 + tc];
+      R.gref = ksp[C + 4 + te];
+    }
   };
   auto stage = [&](const Regs& R, int b) {
 #pragma unroll
@@ -463,8 +479,13 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       }
     }
     if constexpr (OUT) {
-      if (tl < C) sm.gq[b][tl] = R.g2;
-      else if (tl < 2 * C) sm.rk[b][tl - C] = R.g2;
+      if (tl < C) {
+        // past L: G of the chunk's last token, so every staged factor stays finite
+        sm.gq[b][tl] = (tl < R.L ? R.g2 : R.gref) * kLog2e;
+        sm.cf[b][tl] = tl < R.L ? R.rk2 * exp2_fast((R.gref - R.g2) * kLog2e) : 0.f;
+      } else if (tl < 2 * C) {
+        sm.rk[b][tl - C] = R.g2;
+      }
     }
     if constexpr (!ZU) {
 #pragma unroll
@@ -580,7 +601,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       struct ORegs {
         Frag<T> q[TPW][KSK];        // q rows of this wave's token blocks
         SplitFrag<T> f[TPW][KSC];   // P^T as the chained B operand
-        float isc[TPW];             // exp(G_r) / |q_r|
+        float isc[TPW];             // scale exp(G_r) / |q_r|
       };
       auto chunk_t0 = [&](int x) { return seq_t0 + (int64_t)x * C; };
       auto chunk_L = [&](int x) {
@@ -588,24 +609,29 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         return (int)(r < C ? r : C);
       };
       // P^T blocks of chunk x from the staged keys, queries and gates
-      // (buffer x % 2; rows past L are zero there)
+      // (buffer x % 2; rows past L are zero there).  On a diagonal block
+      // exp(G_r - G_t) is taken directly; below it, it is the row factor
+      // exp(G_r - G_e) times the staged column factor exp(G_e - G_t) / |k_t|,
+      // e the last token of t's key block (for non-positive gates both are at
+      // most 1).  |q_r|^2 is the diagonal of the block's Q Q^T product, and the
+      // output scale rides on the row factors.  A column r >= L of P^T only
+      // reaches row r of o, which is never stored.
       auto pphase = [&](ORegs& P, int x) {
-        const int L = chunk_L(x);
         const int b = x & 1;
-        float rq[TPW], Gr[TPW];
+        float rs[TPW], Gr[TPW];      // scale / |q_r| and G_r (log2 units)
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
           const int rr = 16 * tbk(m) + r16;
-          float sq = 0.f;
+          f32x4 d = zero4();
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) {
             P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
-            const f32x8 xq = P.q[m][ks].f32();
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sq += xq[e] * xq[e];
+            mma(d, P.q[m][ks], P.q[m][ks]);
           }
-          sq = group4_sum(sq);
-          rq[m] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+          // Q Q^T[i][r16] sits in lane r16 + 16 (i >> 2), element i & 3
+          const float d01 = (r16 & 1) ? d[1] : d[0], d23 = (r16 & 1) ? d[3] : d[2];
+          const float sq = __shfl((r16 & 2) ? d23 : d01, r16 + 16 * (r16 >> 2), 64);
+          rs[m] = a.l2norm ? a.scale * __builtin_amdgcn_rsqf(sq + kL2Eps) : a.scale;
           Gr[m] = sm.gq[b][rr];
         }
         f32x4 Pt[TPW][NB];
@@ -626,16 +652,30 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
             for (int ks = 0; ks < KSK; ++ks) mma(Pt[m][jb], kf[ks], P.q[m][ks]);
           }
           // P^T[t][rr] with t = 16 jb + 4 g4 + i: the four tokens' factors in one read each
-          const f32x4 rk4 = *reinterpret_cast<const f32x4*>(&sm.rk[b][16 * jb + 4 * g4]);
-          const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sm.gq[b][16 * jb + 4 * g4]);
+          bool below = false, diag = false;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * jb + 4 * g4 + i;
+          for (int m = 0; m < TPW; ++m) {
+            below |= jb < tbk(m);
+            diag |= jb == tbk(m);
+          }
+          if (below) {
+            const f32x4 cf4 = *reinterpret_cast<const f32x4*>(&sm.cf[b][16 * jb + 4 * g4]);
+            const float Ge = sm.gq[b][16 * jb + 15];
 #pragma unroll
             for (int m = 0; m < TPW; ++m) {
-              if (jb > tbk(m)) continue;
-              const int rr = 16 * tbk(m) + r16;
-              Pt[m][jb][i] *= (t <= rr && rr < L) ? rq[m] * rk4[i] * __expf(Gr[m] - G4[i]) : 0.f;
+              if (jb >= tbk(m)) continue;
+              Pt[m][jb] *= cf4 * (rs[m] * exp2_fast(Gr[m] - Ge));
+            }
+          }
+          if (diag) {
+            const f32x4 rk4 = *reinterpret_cast<const f32x4*>(&sm.rk[b][16 * jb + 4 * g4]);
+            const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sm.gq[b][16 * jb + 4 * g4]);
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) {
+              if (jb != tbk(m)) continue;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                Pt[m][jb][i] *= 4 * g4 + i <= r16 ? rs[m] * rk4[i] * exp2_fast(Gr[m] - G4[i]) : 0.f;
             }
           }
         }
@@ -643,7 +683,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         for (int m = 0; m < TPW; ++m) {
 #pragma unroll
           for (int kt = 0; kt < KSC; ++kt) P.f[m][kt] = SplitFrag<T>::make(cat8(Pt[m][2 * kt], Pt[m][2 * kt + 1]));
-          P.isc[m] = rq[m] * __expf(Gr[m]);
+          P.isc[m] = rs[m] * exp2_fast(Gr[m]);
         }
       };
       // o of chunk x from the staged h / e (buffer x % 2) and its P^T step's operands
@@ -670,7 +710,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
               if (2 * kt > tbk(m)) continue;
               mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), P.f[m][kt]);
             }
-            O[m][vb] = acc * a.scale;
+            O[m][vb] = acc;
           }
         }
 #pragma unroll
@@ -691,7 +731,9 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 
       // Same barrier sequence as the other roles: one per chunk step over
       // 3 ceil(nc / 3) steps.  Step x: o of chunk x - 1, then P^T of chunk x
-      // (whose operands stay in registers for the next step's o).
+      // (whose operands stay in registers for the next step's o).  (Merging
+      // the two phases into one branch-free block, so that they interleave,
+      // measured slower.)
       if (nc > 0) {
         ORegs P;
         lds_barrier();
@@ -705,7 +747,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         if (nsteps == nc) ophase(P, nc - 1);
       }
       };
-      if (__builtin_amdgcn_readfirstlane(wv - NWC) == 0) {
+      if (__builtin_amdgcn_readfirstlane(oi) == 0) {
         run(std::integral_constant<int, 0>{});
       } else {
         run(std::integral_constant<int, 1>{});

@@ -294,6 +294,22 @@ def test_extreme_per_channel_gate_span():
     check("ht", f64(ht), rht, 1e-4)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_scalar_gate_span_fused_output(dtype):
+    """Scalar gates of -9 per token (about 144 of decay inside a 16-token
+    block, so every decay factor between blocks underflows), with a few
+    near-zero gates, a ragged last chunk and the fused scan + output stage:
+    the output's factored decays (row factor times column factor) must still
+    match the plain exp(G_r - G_t)."""
+    w, inp = mk(B=1, T=150, H=2, HV=2, K=128 if dtype == "bf16" else 64, V=64, C=64, dtype=dtype)
+    inp["g"] = inp["g"] * 0.0 - 9.0
+    inp["g"][0, 1::5] = -0.01
+    o, ht, _ = gpu_fwd(inp)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL[dtype])
+    check("ht", f64(ht), rht, TOL[dtype])
+
+
 # ------------------------------------------------------------------ invariants (bitwise)
 
 def test_varlen_equals_dense_per_sequence_bitwise():
