@@ -313,10 +313,15 @@ def stage_times(max_stages: int = 8192) -> list:
     return [(names[i].decode(), float(ms[i])) for i in range(n)]
 
 
-def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
-    """Typed views of the forward intermediates inside a workspace tensor."""
-    lay = fwd_layout(p)
+def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout] = None) -> dict:
+    """Typed views of the forward intermediates inside a workspace tensor (of
+    the layout ``lay``, by default the one gdr_chunk_fwd uses for ``p``).  The
+    compact layout of the fused stages has no Tm, h or v_new and keeps u in the
+    input dtype: those views are None there."""
+    if lay is None:
+        lay = fwd_layout(p)
     nt, C, HV, K, V = lay.nt_max, p.chunk_size, p.HV, p.K, p.V
+    compact = nt > 0 and lay.Tm == lay.w
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 
@@ -330,14 +335,14 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
         chunk_idx=view(lay.chunk_idx, (nt, 4), torch.int32, 4),
         chunk_off=view(lay.chunk_off, (p.N + 1,), torch.int32, 4),
         seq_order=view(lay.seq_order, (p.N,), torch.int32, 4),
-        Tm=view(lay.Tm, (nt, HV, C, C), dt, es),
+        Tm=None if compact else view(lay.Tm, (nt, HV, C, C), dt, es),
         w=view(lay.w, (nt, HV, C, K), dt, es),
         # u as the separate WY stage writes it (fp32), and the same region as the
         # fused K1 + K2 stage writes it (input dtype)
-        u=view(lay.u, (nt, HV, V, C), torch.float32, 4),
+        u=None if compact else view(lay.u, (nt, HV, V, C), torch.float32, 4),
         u_fused=view(lay.u, (nt, HV, V, C), dt, es),
-        h=view(lay.h, (nt, HV, V, K), dt, es),
-        v_new=view(lay.v_new, (nt, HV, V, C), dt, es),
+        h=None if compact else view(lay.h, (nt, HV, V, K), dt, es),
+        v_new=None if compact else view(lay.v_new, (nt, HV, V, C), dt, es),
         kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, 3 * C + 4), torch.float32, 4),
     )
 
@@ -563,7 +568,7 @@ def bwd_workspace_views(p: GdrProblem, ws: torch.Tensor) -> dict:
     # K = 128, run chunk 64 problems at 32)
     pe = GdrProblem.from_buffer_copy(p)
     pe.chunk_size = int(lay.chunk_size)
-    views = workspace_views(pe, ws)
+    views = workspace_views(pe, ws, lay.fwd)
     nt, C, HV, K, V = lay.fwd.nt_max, pe.chunk_size, p.HV, p.K, p.V
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4

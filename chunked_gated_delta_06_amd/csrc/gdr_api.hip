@@ -195,6 +195,13 @@ gdr_fwd_layout fused_layout_of(const gdr_problem& p) {
   return l;
 }
 
+// The layout gdr_chunk_fwd works in: the compact one when the fused stages run
+// (no keep_states and a shape with the fused scan + output stage), else the
+// full one with Tm, h and v_new.
+gdr_fwd_layout fwd_layout_for(const gdr_problem& pp) {
+  return (!pp.keep_states && gdr::fwd_h_o_preferred(make_args(pp))) ? fused_layout_of(pp) : layout_of(pp);
+}
+
 gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_HIP; }
 
 gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
@@ -564,7 +571,7 @@ gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* out) {
   if (p == nullptr || out == nullptr) return GDR_ERR_NULL_ARG;
   const gdr_status st = check(p, p->N != p->B, true);
   if (st != GDR_OK) return st;
-  *out = layout_of(padded_problem(*p));
+  *out = fwd_layout_for(padded_problem(*p));
   if (needs_pad(*p)) out->total = pad_layout(*p, out->total, false).total;
   return GDR_OK;
 }
@@ -585,7 +592,7 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
   if (st != GDR_OK) return st;
   if (workspace != nullptr && !aligned16(workspace)) return GDR_ERR_ALIGNMENT;
   const gdr_problem pp = padded_problem(*p);
-  const gdr_fwd_layout l = layout_of(pp);
+  const gdr_fwd_layout l = fwd_layout_for(pp);
   const size_t need = needs_pad(*p) ? pad_layout(*p, l.total, false).total : l.total;
   if (workspace == nullptr || workspace_bytes < need) return GDR_ERR_WORKSPACE;
   return chunk_fwd_run(*p, q, k, v, g, beta, cu_seqlens, h0, o, ht, static_cast<char*>(workspace), l,
@@ -599,8 +606,7 @@ gdr_status gdr_chunk_fwd_noalloc(const gdr_problem* p, const void* q, const void
   if (st != GDR_OK) return st;
   // the fused path touches only the chunk tables, w, u and kscale
   const gdr_problem pp = padded_problem(*p);
-  const bool fused = !pp.keep_states && gdr::fwd_h_o_preferred(make_args(pp));
-  const gdr_fwd_layout l = fused ? fused_layout_of(pp) : layout_of(pp);
+  const gdr_fwd_layout l = fwd_layout_for(pp);
   const size_t need = needs_pad(*p) ? pad_layout(*p, l.total, false).total : l.total;
   if (need > kScratchBytes) return GDR_ERR_SCRATCH_LIMIT;
   char* ws = nullptr;
@@ -797,7 +803,9 @@ gdr_status gdr_simple_gla_fwd(const gdr_problem* p, const void* q, const void* k
   const void* ptrs[] = {q, k, v, g, cu_seqlens, h0, o, ht, workspace};
   for (const void* ptr : ptrs)
     if (ptr != nullptr && !aligned16(ptr)) return GDR_ERR_ALIGNMENT;
-  const gdr_fwd_layout l = layout_of(*p);
+  // the same layout rule as gdr_fwd_workspace_layout (simple GLA runs the fused
+  // scan + output stage wherever the shape has it)
+  const gdr_fwd_layout l = gdr::fwd_h_o_supported(make_args(*p)) ? fused_layout_of(*p) : layout_of(*p);
   if (workspace == nullptr || workspace_bytes < l.total) return GDR_ERR_WORKSPACE;
 
   Args a = make_args(*p);

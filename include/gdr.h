@@ -56,9 +56,11 @@ typedef enum {
   GDR_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than *_workspace_bytes */
   GDR_ERR_HIP = 8,         /* a kernel launch failed */
   GDR_ERR_CU_SEQLENS = 9,  /* gdr_validate_cu_seqlens: bad table */
-  GDR_ERR_UNSUPPORTED = 10, /* backward: per-channel gate, K above 128, or a saved-state
-                              backward for fp32 with K = 128 and chunk 64 (see
-                              gdr_chunk_bwd); gdr_fwd_h_o: a shape without the fused stage
+  GDR_ERR_UNSUPPORTED = 10, /* backward: K above 128, or a saved-state backward that
+                              would have to switch to chunk 32 (per-channel gate, or fp32
+                              with K = 128, at chunk 64; see gdr_chunk_bwd); the backward
+                              stage entry points: a per-channel gate; gdr_fwd_h_o: a shape
+                              without the fused stage
                               (see gdr_fwd_h_o_supported); gdr_simple_gla_fwd: a per-channel
                               gate */
   GDR_ERR_SCRATCH_LIMIT = 11 /* gdr_chunk_fwd_noalloc: the problem needs more than
@@ -91,7 +93,10 @@ typedef struct {
 
 /* Offsets (bytes from the workspace base) of the forward intermediates that
  * gdr_chunk_fwd keeps in its workspace; NT_max = B * ceil(T / C) for a dense
- * batch and floor(T / C) + N for a varlen batch.
+ * batch and floor(T / C) + N for a varlen batch.  When the forward takes the
+ * fused stages (keep_states = 0 and a shape gdr_chunk_fwd_fused reports), the
+ * layout is the compact one those stages use: Tm, h and v_new get no bytes
+ * (their offsets equal the next region's) and u is in `dtype`.
  *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
  *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
  *   seq_order  int32 [N]           varlen batches of at most 1024 sequences: the sequences
@@ -140,10 +145,20 @@ const char* gdr_status_string(gdr_status s);
 gdr_status gdr_check_problem(const gdr_problem* p);
 
 /* Check a host copy of cu_seqlens ([N+1] int32): cu[0] = 0, non-decreasing,
- * cu[N] = T.  Returns GDR_OK or GDR_ERR_CU_SEQLENS (GDR_ERR_NULL_ARG if NULL). */
+ * cu[N] = T.  Returns GDR_OK or GDR_ERR_CU_SEQLENS (GDR_ERR_NULL_ARG if NULL).
+ * The varlen offsets are the coverage-matrix page's cu_seqlens axis (section
+ * 3); the KCP manual's chunk-boundary section ("why per-chunk comparison lies
+ * under varlen KCP") is why a bad table must be refused before any chunk is
+ * formed.  The kernels trust cu_seqlens, so a caller that cannot vouch for it
+ * checks a host copy here (the Python binding does by default). */
 gdr_status gdr_validate_cu_seqlens(const int32_t* cu_host, int64_t N, int64_t T);
 
-/* Workspace needed by gdr_chunk_fwd (bytes), and where each intermediate sits. */
+/* Workspace needed by gdr_chunk_fwd (bytes), and where each intermediate sits.
+ * Library plumbing, not an operation of the pages: it holds the intermediates
+ * of the chunk form's stages (the coverage-matrix page, section 2; the KCP
+ * manual's debug-script stage order) between launches, since the library never
+ * allocates.  The size is written through `bytes` so that an invalid problem
+ * returns its status instead of a size. */
 gdr_status gdr_fwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout);
 
@@ -368,6 +383,9 @@ typedef struct {
   size_t de_local, qscale, dh, kt, qg, dl, total;
 } gdr_bwd_layout;
 
+/* Workspace needed by gdr_chunk_bwd (bytes), and where each intermediate sits;
+ * plumbing like gdr_fwd_workspace_bytes.  Its leading part is the keep-states
+ * forward's layout, so a saved-state backward can read what that forward left. */
 gdr_status gdr_bwd_workspace_bytes(const gdr_problem* p, size_t* bytes);
 gdr_status gdr_bwd_workspace_layout(const gdr_problem* p, gdr_bwd_layout* layout);
 

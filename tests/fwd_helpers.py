@@ -33,7 +33,7 @@ def gpu_fwd(inp, *, h0=True, ht=True, workspace=None, out=None, keep_states=Fals
     torch.cuda.synchronize()
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=inp["chunk_size"],
                          cu_seqlens=inp["cu_seqlens"], use_qk_l2norm=inp["use_qk_l2norm"],
-                         scale=inp["scale"])
+                         scale=inp["scale"], keep_states=keep_states)
     views = gdr.workspace_views(p, ws)
     return o, htd, views
 

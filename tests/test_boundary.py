@@ -82,16 +82,28 @@ def test_validate_cu_seqlens():
 
 
 def test_workspace_layout():
-    p = problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4)
+    # the separate stages (keep_states): every intermediate has its region
+    p = problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, keep_states=1)
     lay = gdr.fwd_layout(p)
     assert lay.nt_max == 4 * 64
     offs = [lay.chunk_idx, lay.chunk_off, lay.Tm, lay.w, lay.u, lay.h, lay.v_new, lay.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     nt, C, HV, K, V = 256, 64, 16, 128, 128
+    assert lay.w - lay.Tm >= nt * HV * C * C * 2
     assert lay.h - lay.u >= nt * HV * V * C * 4      # u in fp32 (the separate WY stage's)
     assert lay.total - lay.v_new >= nt * HV * V * C * 2
     blay = gdr.bwd_layout(p)
     assert blay.total - blay.dh >= nt * HV * V * K * 4   # dh in fp32
+    # the fused stages (the default): no Tm, h or v_new, u in the input dtype
+    pf = problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4)
+    f = gdr.fwd_layout(pf)
+    assert f.Tm == f.w and f.h == f.v_new == f.kscale
+    assert f.u - f.w >= nt * HV * C * K * 2 and f.kscale - f.u >= nt * HV * V * C * 2
+    assert f.kscale - f.u < nt * HV * V * C * 4
+    assert f.total < lay.total // 2
+    # a shape without the fused scan + output stage (per-channel gate) keeps the full layout
+    pc = gdr.fwd_layout(problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1))
+    assert pc.w - pc.Tm >= nt * HV * C * C * 2 and pc.v_new > pc.h
     # varlen bound floor(T / C) + N
     pv = problem(B=1, T=25344, H=16, HV=32, K=128, V=128, N=24)
     assert gdr.fwd_layout(pv).nt_max == 25344 // 64 + 24
@@ -215,7 +227,8 @@ def test_bwd_layout_reports_the_chunk_size_it_runs_at():
 def test_bwd_workspace_layout():
     p = problem(B=1, T=65536, H=32, HV=32, K=128, V=128, N=1)
     lay = gdr.bwd_layout(p)
-    f = gdr.fwd_layout(p)
+    # the backward's leading part is the keep-states forward's layout
+    f = gdr.fwd_layout(problem(B=1, T=65536, H=32, HV=32, K=128, V=128, N=1, keep_states=1))
     assert lay.fwd.total == f.total and lay.fwd.h == f.h
     nt, C, HV, K, V = 1024, 64, 32, 128, 128
     assert lay.fwd.nt_max == nt

@@ -5,6 +5,8 @@ for bf16 on o, ht and the intermediates (the bf16 bound is the chunked-vs-
 per-token noise level the KCP page's acceptance section names); integer chunk
 tables are compared exactly.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -184,20 +186,34 @@ def test_fused_kkt_wy_against_oracle(cfg):
     check("ht", f64(ht), rht, tol)
 
 
-def test_fused_default_leaves_states_untouched():
-    """Without keep_states the forward takes the fused stages: o / ht match the
-    oracle and the Tm, h and v_new regions of the workspace keep their fill."""
+def test_fused_default_uses_the_compact_workspace():
+    """Without keep_states the forward takes the fused stages in the compact
+    workspace layout (no Tm, h or v_new regions): o / ht match the oracle, and a
+    workspace of exactly that size, inside guard bands, is enough and is not
+    overrun; with keep_states the full layout is required."""
     w, inp = mk(B=2, T=170, H=8, HV=32, K=128, V=128, slow=True)
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True)
     assert gdr.chunk_fwd_fused(p)
     lay = gdr.fwd_layout(p)
-    ws = torch.full((lay.total,), 0x5A, dtype=torch.uint8, device="cuda")
+    full = gdr.fwd_layout(gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True,
+                                           keep_states=True))
+    assert lay.Tm == lay.w and lay.h == lay.kscale and lay.total < full.total
+    pad = 4096
+    ws_full = torch.full((lay.total + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = ws_full[pad:pad + lay.total]
     o, ht, views = gpu_fwd(inp, workspace=ws)
     ro, rht = oracle_fwd(inp)
     check("o", f64(o), ro, TOL["bf16"])
     check("ht", f64(ht), rht, TOL["bf16"])
-    assert (ws[lay.h:lay.v_new] == 0x5A).all() and (ws[lay.v_new:lay.kscale] == 0x5A).all()
-    assert (ws[lay.Tm:lay.w] == 0x5A).all()
+    assert views["Tm"] is None and views["h"] is None and views["v_new"] is None
+    assert (ws_full[:pad] == 0x5A).all() and (ws_full[pad + lay.total:] == 0x5A).all()
+    # the C ABI refuses that workspace for the separate stages
+    pk = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=64, use_qk_l2norm=True, keep_states=True)
+    P = lambda t: ctypes.c_void_p(dev(t).data_ptr())
+    st = gdr.lib().gdr_chunk_fwd(ctypes.byref(pk), P(inp["q"]), P(inp["k"]), P(inp["v"]), P(inp["g"]),
+                                 P(inp["beta"]), None, None, ctypes.c_void_p(o.data_ptr()), None,
+                                 ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(lay.total), None)
+    assert st == 7   # GDR_ERR_WORKSPACE
 
 
 # ------------------------------------------------------------------ sweep
