@@ -406,28 +406,44 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     lr = lanes_sum_t<64>(lr);
     if (lane == 0) sRed[wv] = lr;
 
-    // ---- D = dP o exp(G_r - G_t) (causal); dG from P
+    // ---- D = dP o exp(G_r - G_t) (causal); dG from P.  The wave's rows
+    //      r = 16 rb + 4 g4 + e are the same in every slot: their factors are
+    //      read once and their sums over t stay in registers until one
+    //      reduction after the slots; blocks above the diagonal are zero.
+    const int r4 = 16 * rb + 4 * g4;
+    const f32x4 Gr4 = *reinterpret_cast<const f32x4*>(&sG[r4]);
+    const f32x4 Rq4 = *reinterpret_cast<const f32x4*>(&sRq[r4]);
+    const f32x4 Rk4 = *reinterpret_cast<const f32x4*>(&sRk[r4]);
+    const f32x4 B4 = *reinterpret_cast<const f32x4*>(&sB[r4]);
     f32x4 Dv[SCC];
+    {
+      f32x4 rowP = zero4();
 #pragma unroll
-    for (int i = 0; i < SCC; ++i) {
-      const int b = wv + NW * i, cb = b / NRB;
-      Dv[i] = zero4();
-      if (b >= NBC) continue;
-      const int t = 16 * cb + r16;
-      float colsum = 0.f;
+      for (int i = 0; i < SCC; ++i) {
+        const int b = wv + NW * i, cb = b / NRB;
+        Dv[i] = zero4();
+        if (b >= NBC || cb > rb) continue;
+        const int t = 16 * cb + r16;
+        const float Gt = sG[t];
+        const f32x4 P4 = fP.get4(r4, 16 * cb, lane);
+        float colsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = t <= r4 + e && r4 + e < L;
+          const float dps = scale * dP[i][e];
+          Dv[i][e] = ok ? dps * __expf(Gr4[e] - Gt) : 0.f;
+          const float pd = ok ? dps * P4[e] : 0.f;
+          rowP[e] += pd;
+          colsum += pd;
+        }
+        colsum = group4_sum(colsum);
+        if (g4 == 0) sRowG[wv * C + t] -= colsum;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
-        const bool ok = t <= r && r < L;
-        const float dps = scale * dP[i][e];
-        Dv[i][e] = ok ? dps * __expf(sG[r] - sG[t]) : 0.f;
-        const float pd = ok ? dps * fP.get(r, t) : 0.f;
-        const float rs = lanes_sum_t<16>(pd);
-        if (r16 == 0) sRowG[wv * C + r] += rs;
-        colsum += pd;
+        const float rs = lanes_sum_t<16>(rowP[e]);
+        if (r16 == 0) sRowG[wv * C + r4 + e] += rs;
       }
-      colsum = group4_sum(colsum);
-      if (g4 == 0) sRowG[wv * C + t] -= colsum;
     }
     lds_barrier();     // P^T is dead: D tiles overlay it
 
@@ -437,45 +453,40 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       const int b = wv + NW * i, cb = b / NRB;
       if (b >= NBC) continue;
       const int t = 16 * cb + r16;
-      const f32x4 rq4 = *reinterpret_cast<const f32x4*>(&sRq[16 * rb + 4 * g4]);
-      fD1.put4(t, 16 * rb + 4 * g4, Dv[i] * sRk[t]);
-      fD2.put4(t, 16 * rb + 4 * g4, Dv[i] * rq4);
+      fD1.put4(t, r4, Dv[i] * sRk[t]);
+      fD2.put4(t, r4, Dv[i] * Rq4);
     }
     {
       f32x4 qd = zero4(), kw = zero4(), kk = zero4();
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
+        const int b = wv + NW * i, db = b / NRB;
         dQg[i] *= scale;
         TdW[i] = -TdW[i];
         if (b >= NBK) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * g4 + e;
-          const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
-          qd[e] += qv * dQg[i][e];
-          kw[e] += kv * TdW[i][e];
-          kk[e] += kv * dKt[i][e];
-        }
+        const f32x4 q4 = lds_rows4(sQ, PK, r4, 16 * db, lane), k4 = lds_rows4(sK, PK, r4, 16 * db, lane);
+        qd += q4 * dQg[i];
+        kw += k4 * TdW[i];
+        kk += k4 * dKt[i];
       }
       float last = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
+        const int r = r4 + e;
         const float q1 = lanes_sum_t<16>(qd[e]), k1 = lanes_sum_t<16>(kw[e]), k2 = lanes_sum_t<16>(kk[e]);
         const bool ok = r < L;
-        const float gam = __expf(sG[r]), kap = __expf(GL - sG[r]);
-        const float tw = ok ? gam * sRk[r] * k1 : 0.f;
-        const float kt = ok ? kap * sRk[r] * k2 : 0.f;
+        const float gam = __expf(Gr4[e]), kap = __expf(GL - Gr4[e]);
+        const float tw = ok ? gam * Rk4[e] * k1 : 0.f;
+        const float kt = ok ? kap * Rk4[e] * k2 : 0.f;
         if (r16 == 0) {
-          sRowG[wv * C + r] += (ok ? gam * sRq[r] * q1 : 0.f) + sB[r] * tw - kt;
+          sRowG[wv * C + r] += (ok ? gam * Rq4[e] * q1 : 0.f) + B4[e] * tw - kt;
           sRowB[wv * C + r] += tw;
         }
         last += kt;
 #pragma unroll
         for (int i = 0; i < SCK; ++i) {
           dq[i][e] = gam * dQg[i][e];
-          dk[i][e] = kap * dKt[i][e] + sB[r] * gam * TdW[i][e];
+          dk[i][e] = kap * dKt[i][e] + B4[e] * gam * TdW[i][e];
         }
       }
       last = group4_sum(last);
@@ -499,42 +510,51 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     lds_barrier();
 
     // ---- dA (strictly lower): dbeta, dG and the Dk tiles
+    {
+      f32x4 rowB = zero4(), rowG = zero4();
 #pragma unroll
-    for (int i = 0; i < SCC; ++i) {
-      const int b = wv + NW * i, cb = b / NRB;
-      if (b >= NBC) continue;
-      f32x4 kk = zero4();
-      if (cb <= rb) {
+      for (int i = 0; i < SCC; ++i) {
+        const int b = wv + NW * i, cb = b / NRB;
+        if (b >= NBC) continue;
+        const int m = 16 * cb + r16;
+        f32x4 d1v = zero4(), d2v = zero4();
+        if (cb <= rb) {
+          f32x4 kk = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KSK; ++ks)
-          mma(kk, ld8(&sK[(16 * rb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sK[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
+          for (int ks = 0; ks < KSK; ++ks)
+            mma(kk, ld8(&sK[(16 * rb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sK[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
+          const float Gm = sG[m], Rkm = sRk[m];
+          float colsum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = r4 + e;
+            const bool ok = m < t && t < L;
+            const float da = -dA[i][e];
+            const float ex = ok ? __expf(Gr4[e] - Gm) : 0.f;
+            const float abar = Rk4[e] * Rkm * kk[e] * ex;
+            const float dbp = ok ? da * abar : 0.f;
+            const float dkv = ok ? B4[e] * da * ex : 0.f;
+            const float ad = B4[e] * dbp;
+            rowB[e] += dbp;
+            rowG[e] += ad;
+            colsum += ad;
+            d1v[e] = dkv * Rkm;
+            d2v[e] = dkv * Rk4[e];
+          }
+          colsum = group4_sum(colsum);
+          if (g4 == 0) sRowG[wv * C + m] -= colsum;
+        }
+        fD1.put4(m, r4, d1v);
+        fD2.put4(m, r4, d2v);
       }
-      const int m = 16 * cb + r16;
-      float colsum = 0.f;
-      f32x4 d1v, d2v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rb + 4 * g4 + e;
-        const bool ok = m < t && t < L;
-        const float da = -dA[i][e];
-        const float ex = ok ? __expf(sG[t] - sG[m]) : 0.f;
-        const float abar = sRk[t] * sRk[m] * kk[e] * ex;
-        const float dbp = ok ? da * abar : 0.f;
-        const float dkv = ok ? sB[t] * da * ex : 0.f;
-        const float ad = sB[t] * dbp;
-        const float rb1 = lanes_sum_t<16>(dbp), rg = lanes_sum_t<16>(ad);
+        const float rb1 = lanes_sum_t<16>(rowB[e]), rg = lanes_sum_t<16>(rowG[e]);
         if (r16 == 0) {
-          sRowB[wv * C + t] += rb1;
-          sRowG[wv * C + t] += rg;
+          sRowB[wv * C + r4 + e] += rb1;
+          sRowG[wv * C + r4 + e] += rg;
         }
-        colsum += ad;
-        d1v[e] = dkv * sRk[m];
-        d2v[e] = dkv * sRk[t];
       }
-      fD1.put4(m, 16 * rb + 4 * g4, d1v);
-      fD2.put4(m, 16 * rb + 4 * g4, d2v);
-      colsum = group4_sum(colsum);
-      if (g4 == 0) sRowG[wv * C + m] -= colsum;
     }
     lds_barrier();
 
@@ -589,54 +609,53 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   }
 
   // ---- group sums, L2-norm backward, dq / dk through LDS as 16-byte rows
+  // (rows r4 + e of every slot: the raw q / k values in one transposed read per
+  // slot and tile, the row factors in one read each)
   auto finish = [&](const f32x4 (&DQ)[SCK], const f32x4 (&DK)[SCK]) {
+    const int r4 = 16 * rb + 4 * g4;
     if (a.l2norm) {
       f32x4 qd = zero4(), kd = zero4();
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
+        const int b = wv + NW * i, db = b / NRB;
         if (b >= NBK) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * g4 + e;
-          qd[e] += to_float(sQ[r * PK + d]) * DQ[i][e];
-          kd[e] += to_float(sK[r * PK + d]) * DK[i][e];
-        }
+        qd += lds_rows4(sQ, PK, r4, 16 * db, lane) * DQ[i];
+        kd += lds_rows4(sK, PK, r4, 16 * db, lane) * DK[i];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
         const float q1 = lanes_sum_t<16>(qd[e]), k1 = lanes_sum_t<16>(kd[e]);
         if (r16 == 0) {
-          sDotQ[wv * C + r] = q1;
-          sDotK[wv * C + r] = k1;
+          sDotQ[wv * C + r4 + e] = q1;
+          sDotK[wv * C + r4 + e] = k1;
         }
       }
       lds_barrier();
     }
+    const f32x4 rq = *reinterpret_cast<const f32x4*>(&sRq[r4]), rk = *reinterpret_cast<const f32x4*>(&sRk[r4]);
+    f32x4 cq = zero4(), ck = zero4();
+    if (a.l2norm) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * rb + 4 * g4 + e;
-      float cq = 0.f, ck = 0.f;
-      const float rq = sRq[r], rk = sRk[r];
+      for (int w = 0; w < NW; ++w) {
+        cq += *reinterpret_cast<const f32x4*>(&sDotQ[w * C + r4]);
+        ck += *reinterpret_cast<const f32x4*>(&sDotK[w * C + r4]);
+      }
+      cq *= rq * rq;
+      ck *= rk * rk;
+    }
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) {
+      const int b = wv + NW * i, db = b / NRB, d = 16 * db + r16;
+      if (b >= NBK) continue;
+      f32x4 oq = DQ[i], okv = DK[i];
       if (a.l2norm) {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          cq += sDotQ[w * C + r];
-          ck += sDotK[w * C + r];
-        }
-        cq *= rq * rq;
-        ck *= rk * rk;
+        oq = rq * (DQ[i] - cq * lds_rows4(sQ, PK, r4, 16 * db, lane));
+        okv = rk * (DK[i] - ck * lds_rows4(sK, PK, r4, 16 * db, lane));
       }
 #pragma unroll
-      for (int i = 0; i < SCK; ++i) {
-        const int b = wv + NW * i, d = 16 * (b / NRB) + r16;
-        if (b >= NBK) continue;
-        const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
-        const float oq = a.l2norm ? rq * (DQ[i][e] - cq * qv) : DQ[i][e];
-        const float okv = a.l2norm ? rk * (DK[i][e] - ck * kv) : DK[i][e];
-        sOq[r * PK + d] = (T)oq;
-        sOk[r * PK + d] = (T)okv;
+      for (int e = 0; e < 4; ++e) {
+        sOq[(r4 + e) * PK + d] = (T)oq[e];
+        sOk[(r4 + e) * PK + d] = (T)okv[e];
       }
     }
     lds_barrier();

@@ -175,6 +175,14 @@ GDR_DEV Frag<T> lds_tr_frag(const T* tile, int pitch, int row_lo, int row_hi, in
   return Frag<T>::raw(cat8(lds_tr4(tile, pitch, row_lo, col0, lane), lds_tr4(tile, pitch, row_hi, col0, lane)));
 }
 
+// Rows r0 .. r0 + 3 of column c0 + l % 16 in fp32 -- the accumulator layout of
+// a 16 x 16 block -- in one transposed read (r0 and c0 the same across each
+// 16-lane group).
+template <typename T>
+GDR_DEV f32x4 lds_rows4(const T* tile, int pitch, int r0, int c0, int lane) {
+  return to_f32<T>(lds_tr4(tile, pitch, r0, c0, lane));
+}
+
 GDR_DEV float to_float(bf16 x) { return (float)x; }
 GDR_DEV float to_float(float x) { return x; }
 
@@ -244,6 +252,12 @@ template <typename T> struct FTile {
   GDR_DEV float get(int r, int c) const {
     float x = to_float(hi[r * pitch + c]);
     if constexpr (kSplit) x += to_float(lo[r * pitch + c]);
+    return x;
+  }
+  // rows r0 .. r0 + 3 of column c0 + l % 16 (the accumulator layout)
+  GDR_DEV f32x4 get4(int r0, int c0, int lane) const {
+    f32x4 x = lds_rows4(hi, pitch, r0, c0, lane);
+    if constexpr (kSplit) x += lds_rows4(lo, pitch, r0, c0, lane);
     return x;
   }
   // row r, contraction columns c0 + 8 g .. + 7
