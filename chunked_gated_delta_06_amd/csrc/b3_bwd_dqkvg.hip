@@ -32,8 +32,9 @@
 // accumulates the C x K and C x C products above in registers; a wave owns a
 // fixed set of 16 x 16 output blocks (one row block) for the whole chunk.  The
 // next head's T tile, gate and beta are fetched into registers while the
-// current head's last value tile is computed; dq and dk leave through an LDS
-// tile as 16-byte row pieces.  Cross-lane sums use DPP row permutations.
+// current head's last value tile is computed, and (one workgroup per CU) each
+// value tile while the previous one is; dq and dk leave through an LDS tile
+// as 16-byte row pieces.  Cross-lane sums use DPP row permutations.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -226,6 +227,14 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   };
 
   HeadRegs HR;
+  // The value tile's registers.  When the LDS already holds the CU to one
+  // workgroup (whose four waves then have 512 registers each), each tile's
+  // loads are issued one tile ahead -- the first head's first tile with the
+  // q / k rows -- so their latency overlaps the previous tile's products
+  // instead of stalling every tile; otherwise a tile is fetched where it is
+  // staged, keeping two workgroups per CU.
+  constexpr bool PF = 2 * Cfg::total > 160 * 1024;
+  TileRegs TN;
   {
     // q, k tiles (rows past L are zero) and their row norms, with the first
     // head's T tile, gate and beta already on the way
@@ -238,6 +247,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       kr[i] = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
     }
     fetch_head(HR, h * ng);
+    if constexpr (PF) fetch_tile(TN, h * ng, 0);
 #pragma unroll
     for (int i = 0; i < NPQ; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -291,26 +301,36 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     lds_barrier();
     const float GL = sG[L - 1];
 
-    // ---- P tile, P[r][t] (norms, gate, causal mask applied)
+    // ---- P tile, P[r][t] (norms, gate, causal mask applied).  Slot i's block
+    //      has key rows t in the wave's row block rb (tb = b % NRB = rb) and
+    //      query rows r in block cb: the key fragments and the factors of the
+    //      rows t are read once; blocks with rb > cb are zero.
+    {
+      const int r4 = 16 * rb + 4 * g4;
+      const f32x4 Gt4 = *reinterpret_cast<const f32x4*>(&sG[r4]);
+      const f32x4 Rkt4 = *reinterpret_cast<const f32x4*>(&sRk[r4]);
+      Frag<T> kr[KSK];
 #pragma unroll
-    for (int i = 0; i < SCC; ++i) {
-      const int b = wv + NW * i, tb = b % NRB, cb = b / NRB;
-      if (b >= NBC) continue;
-      f32x4 acc = zero4();
-      if (tb <= cb) {
+      for (int ks = 0; ks < KSK; ++ks) kr[ks] = ld8(&sK[(16 * rb + r16) * PK + 32 * ks + 8 * g4]);
 #pragma unroll
-        for (int ks = 0; ks < KSK; ++ks)
-          mma(acc, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), ld8(&sQ[(16 * cb + r16) * PK + 32 * ks + 8 * g4]));
+      for (int i = 0; i < SCC; ++i) {
+        const int b = wv + NW * i, cb = b / NRB;
+        if (b >= NBC) continue;
+        const int r = 16 * cb + r16;
+        f32x4 pv = zero4();
+        if (rb <= cb) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) mma(acc, kr[ks], ld8(&sQ[r * PK + 32 * ks + 8 * g4]));
+          const float Gr = sG[r], Rqr = sRq[r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = r4 + e <= r && r < L;
+            pv[e] = ok ? acc[e] * Rqr * Rkt4[e] * __expf(Gr - Gt4[e]) : 0.f;
+          }
+        }
+        fP.put4(r, r4, pv);
       }
-      const int r = 16 * cb + r16;
-      f32x4 pv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * tb + 4 * g4 + e;
-        const float f = (t <= r && r < L) ? sRq[r] * sRk[t] * __expf(sG[r] - sG[t]) : 0.f;
-        pv[e] = acc[e] * f;
-      }
-      fP.put4(r, 16 * tb + 4 * g4, pv);
     }
 
     f32x4 dQg[SCK], TdW[SCK], dKt[SCK], dP[SCC], dA[SCC];
@@ -320,16 +340,17 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     for (int i = 0; i < SCC; ++i) dP[i] = dA[i] = zero4();
 
     for (int64_t v0 = 0; v0 < V; v0 += VT) {
-      {
-        // all of the tile's loads are issued before the first LDS store; a
-        // register prefetch of the next tile across the compute phases would
-        // not fit the register budget (about 500 live registers per lane)
-        TileRegs TR;
-        fetch_tile(TR, j, v0);
-        stage_tile(TR);
-      }
+      if constexpr (!PF) fetch_tile(TN, j, v0);
+      stage_tile(TN);
       lds_barrier();
       if (v0 + VT >= V && jj + 1 < ng) fetch_head(HR, j + 1);
+      if constexpr (PF) {
+        if (v0 + VT < V) {
+          fetch_tile(TN, j, v0 + VT);
+        } else if (jj + 1 < ng) {
+          fetch_tile(TN, j + 1, 0);
+        }
+      }
 
       // ---- dE[t][v] = scale (P^T dO)[t][v] + kappa_t rk_t (K dS1)[t][v]
 #pragma unroll
