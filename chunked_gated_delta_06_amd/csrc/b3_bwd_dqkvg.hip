@@ -92,6 +92,13 @@ struct B3 {
   static constexpr size_t total = oRows + rows_floats * 4;
   static_assert(oRows % 16 == 0, "row factors start 16-byte aligned");
   static constexpr bool fits = total <= 160 * 1024;
+  // the LDS holds the CU to one workgroup (four waves with 512 registers each)
+  static constexpr bool one_per_cu = 2 * total > 160 * 1024;
+  // Persistent workgroups (one per CU, each looping over items and requesting
+  // the next item's rows during the current one's finish) where one workgroup
+  // per CU runs anyway and no GVA group's registers compete; otherwise one
+  // workgroup per item.
+  template <bool GVA> static constexpr bool persistent() { return one_per_cu && !GVA; }
 };
 
 template <typename T, int C, int K, bool GVA, int NW>
@@ -109,12 +116,29 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   // fold, so the MFMA loops unroll without runtime branches
   auto body = [&](auto wvc) {
   constexpr int wv = decltype(wvc)::value;
-  const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
-  const int64_t c = blockIdx.x, h = blockIdx.y;
-  if (c >= a.chunk_off[a.N]) return;
-  const int64_t t0 = a.chunk_idx[4 * c + 1];
-  const int L = a.chunk_idx[4 * c + 2];
+  // lane indices are re-read opaquely at the top of every item (below), so the
+  // compiler recomputes addresses per item instead of hoisting them all out of
+  // the item loop, where they would stay live across the whole item
+  int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
   const int64_t H = a.H, HV = a.HV, V = a.V;
+  // Persistent workgroups: items (chunk, q/k head) blockIdx.x, blockIdx.x +
+  // gridDim.x, ...; item i is chunk i / H, head i % H.
+  struct Item {
+    int64_t c, h, t0;
+    int L;
+  };
+  const int64_t nitems = (int64_t)a.chunk_off[a.N] * H;
+  auto item_at = [&](int64_t i) {
+    Item it;
+    it.c = i / H;
+    it.h = i % H;
+    it.t0 = a.chunk_idx[4 * it.c + 1];
+    it.L = a.chunk_idx[4 * it.c + 2];
+    return it;
+  };
+  int64_t item = blockIdx.x;
+  if (item >= nitems) return;
+  Item cur = item_at(item);
   const int ng = (int)(HV / H);
   const float scale = a.scale;
 
@@ -162,7 +186,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     Frag<T> h[NPH], o[NPO], v[NPO], e[NPE];
     Frag<float> dh[NPH];     // dS1 (fp32)
   };
-  auto fetch_head = [&](HeadRegs& R, int64_t j) {
+  auto fetch_head = [&](HeadRegs& R, const Item& I, int64_t j) {
+    const int64_t c = I.c, t0 = I.t0;
+    const int L = I.L;
     const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
@@ -172,7 +198,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     R.g = (tid < L) ? a.g[(t0 + tid) * HV + j] : 0.f;
     R.b = (tid < L) ? beta_value(a.beta[(t0 + tid) * HV + j], a.beta_logits) : 0.f;
   };
-  auto fetch_tile = [&](TileRegs& R, int64_t j, int64_t v0) {
+  auto fetch_tile = [&](TileRegs& R, const Item& I, int64_t j, int64_t v0) {
+    const int64_t c = I.c, t0 = I.t0;
+    const int L = I.L;
     const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
     const float* dhb = static_cast<const float*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
     const T* eb = static_cast<const T*>(a.v_new) + ((c * HV + j) * V + v0) * (int64_t)C;
@@ -233,21 +261,21 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   // q / k rows -- so their latency overlaps the previous tile's products
   // instead of stalling every tile; otherwise a tile is fetched where it is
   // staged, keeping two workgroups per CU.
-  constexpr bool PF = 2 * Cfg::total > 160 * 1024;
+  constexpr bool PF = Cfg::one_per_cu;
   TileRegs TN;
-  {
-    // q, k tiles (rows past L are zero) and their row norms, with the first
-    // head's T tile, gate and beta already on the way
-    Frag<T> qr[NPQ], kr[NPQ];
+  // q, k rows of item I (rows past L are zero), and their staging with the
+  // row norms
+  Frag<T> qr[NPQ], kr[NPQ];
+  auto fetch_qk = [&](const Item& I) {
 #pragma unroll
     for (int i = 0; i < NPQ; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
-      const bool in = idx < C * CPR && t < L;
-      qr[i] = in ? ld8(qp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
-      kr[i] = in ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
+      const bool in = idx < C * CPR && t < I.L;
+      qr[i] = in ? ld8(qp + ((I.t0 + t) * H + I.h) * K + d8) : frag_zero<T>();
+      kr[i] = in ? ld8(kp + ((I.t0 + t) * H + I.h) * K + d8) : frag_zero<T>();
     }
-    fetch_head(HR, h * ng);
-    if constexpr (PF) fetch_tile(TN, h * ng, 0);
+  };
+  auto stage_qk = [&]() {
 #pragma unroll
     for (int i = 0; i < NPQ; ++i) {
       const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -270,13 +298,24 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       }
     }
     for (int i = tid; i < 2 * NW * C; i += NT) sDotQ[i] = 0.f;   // sDotQ and sDotK
-  }
+  };
+  // the first item's rows, with its first head's T tile, gate and beta (and
+  // first value tile) already on the way
+  fetch_qk(cur);
+  fetch_head(HR, cur, cur.h * ng);
+  if constexpr (PF) fetch_tile(TN, cur, cur.h * ng, 0);
 
   // a wave's fixed output blocks: slot i of a product is block b = wv + NW i,
   // row block b % NRB (= wv % NRB), column block b / NRB
   const int rb = wv % NRB;
   f32x4 dq[SCK], dk[SCK];          // dq^, dk^ of the current value head
   f32x4 sq_[GVA ? SCK : 1], sk_[GVA ? SCK : 1];
+
+  for (;;) {
+  asm volatile("" : "+v"(tid), "+v"(lane), "+v"(r16), "+v"(g4));
+  const int64_t h = cur.h, t0 = cur.t0;
+  const int L = cur.L;
+  stage_qk();
   if constexpr (GVA) {
 #pragma unroll
     for (int i = 0; i < SCK; ++i) sq_[i] = sk_[i] = zero4();
@@ -340,15 +379,15 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     for (int i = 0; i < SCC; ++i) dP[i] = dA[i] = zero4();
 
     for (int64_t v0 = 0; v0 < V; v0 += VT) {
-      if constexpr (!PF) fetch_tile(TN, j, v0);
+      if constexpr (!PF) fetch_tile(TN, cur, j, v0);
       stage_tile(TN);
       lds_barrier();
-      if (v0 + VT >= V && jj + 1 < ng) fetch_head(HR, j + 1);
+      if (v0 + VT >= V && jj + 1 < ng) fetch_head(HR, cur, j + 1);
       if constexpr (PF) {
         if (v0 + VT < V) {
-          fetch_tile(TN, j, v0 + VT);
+          fetch_tile(TN, cur, j, v0 + VT);
         } else if (jj + 1 < ng) {
-          fetch_tile(TN, j + 1, 0);
+          fetch_tile(TN, cur, j + 1, 0);
         }
       }
 
@@ -691,11 +730,28 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       }
     }
   };
+  // the next item's rows, T tile, gate and beta are requested before this
+  // item's finish, which hides their latency
+  const int64_t next = item + gridDim.x;
+  const bool more = Cfg::template persistent<GVA>() && next < nitems;
+  Item nx = cur;
+  if (more) {
+    nx = item_at(next);
+    fetch_qk(nx);
+    fetch_head(HR, nx, nx.h * ng);
+  }
   if constexpr (GVA) {
     finish(sq_, sk_);
   } else {
     finish(dq, dk);
   }
+  if constexpr (!Cfg::template persistent<GVA>()) break;
+  if (!more) break;
+  item = next;
+  cur = nx;
+  fetch_tile(TN, cur, cur.h * ng, 0);
+  lds_barrier();      // the finish's LDS reads end before the next item's staging
+  }   // items
   };
   with_wave_index<NW>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), body);
 }
@@ -714,7 +770,11 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
   if constexpr (!B3<T, C, K, NW>::fits) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
-    const dim3 grid((unsigned)a.NTmax, (unsigned)a.H);
+    // one workgroup per CU that loops over the items, or one per item
+    using Cfg = B3<T, C, K, NW>;
+    const int64_t items = a.NTmax * a.H;
+    const bool pers = a.HV == a.H ? Cfg::template persistent<false>() : Cfg::template persistent<true>();
+    const dim3 grid((unsigned)(pers && items > kNumCUs ? kNumCUs : items));
     if (a.HV == a.H)
       hipLaunchKernelGGL((b3_bwd_dqkvg<T, C, K, false, NW>), grid, dim3(64 * NW), 0, s, a);
     else
