@@ -62,6 +62,19 @@ struct B2S {
       ((size_t)C * (KR + 2 * KP) + (size_t)C * OP + (size_t)BV * EP) * sizeof(T) + KSN * 4;
   static constexpr int NBUF = 2 * buf_bytes <= 160 * 1024 ? 2 : 1;
   static constexpr bool fits = NBUF * buf_bytes <= 160 * 1024 && NKS <= NTL;
+  // dh staging: the compute waves leave each step's dh (fp32, one row of K
+  // features per value column) in one of two LDS buffers and the loader waves
+  // store it during the next step, so the compute waves issue no
+  // vector-memory instructions (stores behind the loaders' loads would stall
+  // their MFMA chains).  Used for 16-bit inputs when both buffers fit beside
+  // the tiles (the fp32 loaders have no registers to spare for it).
+  // staged dh rows: K floats, unpadded; the 16-byte chunk c of row v sits at
+  // chunk c ^ (v % 8), so the compute waves' 16-byte writes of 16 rows spread
+  // over the banks
+  static constexpr int HSP = K;
+  static constexpr size_t stg_bytes = (size_t)BV * HSP * 4;
+  static constexpr bool STG = sizeof(T) == 2 && NBUF == 2 && 2 * (buf_bytes + stg_bytes) <= 160 * 1024;
+  static constexpr int NDH = (BV * K / 4 + NTL - 1) / NTL;   // staged float4 pieces per loader thread
 
   struct Regs {
     Frag<T> k[NLD], q[NLD], w[NLD];
@@ -78,6 +91,7 @@ struct B2S {
     T o[NBUF][C * OP];
     T e[NBUF][BV * EP];
     float ks[NBUF][KSN];
+    __attribute__((aligned(16))) float hs[STG ? 2 : 1][STG ? BV * HSP : 4];
   };
 };
 
@@ -89,6 +103,8 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
   constexpr int KSK = Cfg::KSK, KSC = Cfg::KSC, CPR = Cfg::CPR, NLD = Cfg::NLD, NLO = Cfg::NLO;
   constexpr int NLE = Cfg::NLE, NKS = Cfg::NKS, NPW = Cfg::NPW, NPO = Cfg::NPO, NPE = Cfg::NPE;
   constexpr int KR = Cfg::KR, KP = Cfg::KP, OP = Cfg::OP, EP = Cfg::EP, NBUF = Cfg::NBUF;
+  constexpr bool STG = Cfg::STG;
+  constexpr int HSP = Cfg::HSP, NDH = Cfg::NDH;
   __shared__ __attribute__((aligned(16))) typename Cfg::Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
@@ -185,10 +201,29 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
     if (tl < NKS) *reinterpret_cast<f32x4*>(&sm.ks[b][4 * tl]) = R.ks;
   };
 
+  // staged dh of step x (buffer x % 2) to global memory: the workgroup's BV
+  // rows of K features are contiguous in dh[c]
+  auto drain = [&](int x) {
+    float* hp = dhbase + ((chunk_at(x) * HV + j) * V + vw) * (int64_t)K;
+    f32x4 hv[NDH];
+#pragma unroll
+    for (int i = 0; i < NDH; ++i) {
+      const int idx = tl + NTL * i, v = idx / (K / 4), c4 = idx % (K / 4);
+      if ((BV * K / 4) % NTL == 0 || idx < BV * K / 4)
+        hv[i] = *reinterpret_cast<const f32x4*>(&sm.hs[x & 1][v * HSP + 4 * (c4 ^ (v & 7))]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDH; ++i) {
+      const int idx = tl + NTL * i;
+      if ((BV * K / 4) % NTL == 0 || idx < BV * K / 4) *reinterpret_cast<f32x4*>(hp + 4 * idx) = hv[i];
+    }
+  };
+
   // Loader and compute waves run separate loops with the same barrier
   // sequence.  Step x lives in register slot x % 3 and LDS buffer x % NBUF; at
   // step s the compute waves work on step s while the loaders stage step s + 1
-  // (after a second barrier when there is one buffer) and fetch step s + 4.
+  // (after a second barrier when there is one buffer), fetch step s + 4 and,
+  // with dh staging, store the dh that step s - 1 left in LDS.
   if (loader) {
     if (nc > 0) {
       Regs R0, R1, R2;
@@ -202,15 +237,26 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
         if constexpr (NBUF == 1) lds_barrier();
         stage(R1, (s0 + 1) % NBUF);
         fetch(R1, chunk_at(s0 + 4));
+        if constexpr (STG) {
+          if (s0 > 0) drain(s0 - 1);
+        }
         lds_barrier();
         if constexpr (NBUF == 1) lds_barrier();
         stage(R2, (s0 + 2) % NBUF);
         fetch(R2, chunk_at(s0 + 5));
+        if constexpr (STG) drain(s0);
         lds_barrier();
         if constexpr (NBUF == 1) lds_barrier();
         stage(R0, (s0 + 3) % NBUF);
         fetch(R0, chunk_at(s0 + 6));
+        if constexpr (STG) {
+          if (s0 + 1 < nc) drain(s0 + 1);
+        }
         lds_barrier();
+      }
+      // the last step's dh when the loop ended right after it
+      if constexpr (STG) {
+        if (nc % 3 == 0) drain(nc - 1);
       }
     }
     return;
@@ -244,10 +290,17 @@ __global__ __launch_bounds__(64 * (NWC_ + NWL)) void b2_bwd_dh(Args a) {
       dl[eb] = ld4f(erow + 16 * eb + 4 * g4);
     }
     const float gl = PC ? 1.f : sm.ks[b][C];
-    // dh[c] = dS (fp32, transposed; feature blocks paired into 16-byte stores)
-    float* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
+    // dh[c] = dS (fp32, transposed): staged for the loaders (buffer b = the
+    // step's parity), or stored with feature blocks paired into 16-byte stores
+    if constexpr (STG) {
+      float* hs = &sm.hs[b][(16 * wv + r16) * HSP];
 #pragma unroll
-    for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
+      for (int mb = 0; mb < NS; ++mb) *reinterpret_cast<f32x4*>(hs + 4 * ((4 * mb + g4) ^ (r16 & 7))) = S[mb];
+    } else {
+      float* hp = dhbase + ((c * HV + j) * V + v0) * (int64_t)K;
+#pragma unroll
+      for (int m = 0; m < NS / 2; ++m) st_pair(hp + (r16 * K + 32 * m), S[2 * m], S[2 * m + 1], lane);
+    }
     // dE = de_local + diag(kscale) K dS
     Frag<T> Sf[KSK];
 #pragma unroll
