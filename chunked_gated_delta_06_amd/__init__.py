@@ -50,7 +50,8 @@ class GdrFwdLayout(ctypes.Structure):
                 ("chunk_off", ctypes.c_size_t), ("seq_order", ctypes.c_size_t), ("Tm", ctypes.c_size_t),
                 ("w", ctypes.c_size_t),
                 ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
-                ("kscale", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+                ("kscale", ctypes.c_size_t), ("kt", ctypes.c_size_t), ("dl", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
 
 
 class GdrBwdLayout(ctypes.Structure):

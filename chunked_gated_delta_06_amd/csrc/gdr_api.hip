@@ -138,7 +138,10 @@ gdr::Args make_args(const gdr_problem& p) {
   return a;
 }
 
-gdr_fwd_layout layout_of(const gdr_problem& p) {
+// pc_regions: with a per-channel gate, reserve the WY stage's gated keys and
+// decay for the warp-specialised scan (the backward keeps its own; the
+// segmented forward runs the other per-channel scan).
+gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true) {
   gdr_fwd_layout l;
   const int64_t nt = gdr::nt_max(p);
   const size_t es = elem_size(p);
@@ -163,6 +166,11 @@ gdr_fwd_layout layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * V * C * es);
   l.kscale = off;
   off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float)));
+  const bool pcs = pc_regions && p.gate_per_channel && gdr::fwd_pc_scan_fits(p.dtype, (int)C, (int)K);
+  l.kt = off;
+  off = round_up(off + (pcs ? (size_t)nt * HV * C * K * es : 0));
+  l.dl = off;
+  off = round_up(off + (pcs ? (size_t)nt * HV * K * sizeof(float) : 0));
   l.total = off;
   return l;
 }
@@ -191,6 +199,8 @@ gdr_fwd_layout fused_layout_of(const gdr_problem& p) {
   l.v_new = off;
   l.kscale = off;
   off = round_up(off + (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float));
+  l.kt = off;
+  l.dl = off;
   l.total = off;
   return l;
 }
@@ -206,7 +216,7 @@ gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_
 
 gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
   gdr_bwd_layout l;
-  l.fwd = layout_of(p);
+  l.fwd = layout_of(p, false);
   l.chunk_size = p.chunk_size;
   const int64_t nt = l.fwd.nt_max;
   const size_t es = elem_size(p);
@@ -232,7 +242,7 @@ gdr_bwd_layout bwd_layout_of(const gdr_problem& p) {
 
 gdr_seg_layout seg_layout_of(const gdr_problem& p) {
   gdr_seg_layout l;
-  l.fwd = layout_of(p);
+  l.fwd = layout_of(p, false);
   const int64_t nt = l.fwd.nt_max;
   const size_t es = elem_size(p);
   const size_t C = (size_t)p.chunk_size, HV = (size_t)p.HV, K = (size_t)p.K, V = (size_t)p.V, N = (size_t)p.N;
@@ -334,6 +344,11 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.h = ws + l.h;
   a.v_new = ws + l.v_new;
   a.kscale = p.gate_per_channel ? nullptr : reinterpret_cast<float*>(ws + l.kscale);
+  if (p.gate_per_channel && l.dl > l.kt) {
+    // the WY stage writes the gated keys and decay the scan reads
+    a.kt = ws + l.kt;
+    a.dl = reinterpret_cast<float*>(ws + l.dl);
+  }
   a.o = o;
   a.ht = ht;
   hipError_t e = hipSuccess;
@@ -507,7 +522,7 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
 
 extern "C" {
 
-int gdr_abi_version(void) { return 4; }
+int gdr_abi_version(void) { return 5; }
 
 gdr_status gdr_stage_timing(int enable) {
   t_timer.on = enable != 0;

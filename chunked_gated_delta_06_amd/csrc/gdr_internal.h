@@ -116,6 +116,8 @@ hipError_t launch_bwd_dqkvg_pc(const Args& a, hipStream_t s);
 // reverse scan; a per-channel gate at chunk 32).
 bool bwd_shape_ok(const gdr_problem& p);
 bool bwd_scan_fits(int dtype, int C, int K);
+// per-channel gate: the warp-specialised scan on the WY stage's gated keys fits
+bool fwd_pc_scan_fits(int dtype, int C, int K);
 bool bwd_scan_pc_fits(int dtype, int K);   // per-channel reverse scan at chunk 32
 bool bwd_fused_fits(int dtype, int C, int K);
 bool bwd_pc_fits(int dtype, int K);        // per-channel B3 at chunk 32

@@ -20,7 +20,10 @@
 //    value column (an 8-byte store into the per-chunk transposed u);
 //  * with a scalar gate the per-token factor s_t = beta_t exp(G_t) / |k_t|
 //    multiplies the columns of Tm, leaving the raw keys exact; a per-channel
-//    gate multiplies the key tile element-wise by exp(G_td) <= 1;
+//    gate multiplies the key tile element-wise by exp(G_td) <= 1, and (when
+//    the caller gives a.kt / a.dl) the stage also writes the state scan's
+//    gated keys exp(G_L - G_t) k^_t and decay exp(G_L), so the scan does not
+//    form the chunk's gate cumsum in each of its workgroups;
 //  * blocks above the diagonal of Tm are skipped (Tm is lower triangular);
 //  * every global load of a chunk (keys, the first value pass, Tm rows, g,
 //    beta) is issued before the first wait, so a workgroup pays one memory
@@ -119,7 +122,10 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     lds_barrier();
   }
 
-  // key tile (token-major), row norms of the raw keys
+  // key tile (token-major), row norms of the raw keys; with a per-channel gate
+  // (and a.kt set) also the state scan's gated key rows exp(G_L - G_t) k^_t
+  // (zero past L) and the decay exp(G_L), one float per feature
+  T* __restrict__ ktp = (PC && a.kt != nullptr) ? static_cast<T*>(a.kt) + (c * HV + j) * (int64_t)(C * K) : nullptr;
 #pragma unroll
   for (int i = 0; i < NKP; ++i) {
     const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -129,15 +135,26 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
     sq = lanes_sum_t<CPR>(sq);
     if (idx < C * CPR) {
-      if (d8 == 0) sRn[t] = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+      const float rn = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
+      if (d8 == 0) sRn[t] = rn;
       Frag<T> f = kr[i];
       if constexpr (PC) {
+        if (ktp != nullptr) {
+          f32x8 y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = x[e] * rn * __expf(sGc[(L - 1) * GP + d8 + e] - sGc[t * GP + d8 + e]);
+          st8(ktp + t * K + d8, Frag<T>::make(y));
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[t * GP + d8 + e]);
         f = Frag<T>::make(x);
       }
       st8(&sK[t * KP + d8], f);
     }
+  }
+  if constexpr (PC) {
+    if (a.dl != nullptr)
+      for (int d = tid; d < K; d += NT) a.dl[(c * HV + j) * K + d] = __expf(sGc[(L - 1) * GP + d]);
   }
   lds_barrier();
   if (wv == 0) {

@@ -316,7 +316,7 @@ __global__ __launch_bounds__(64 * NW) void k3_fwd_h(Args a) {
 // other, and meet the compute waves at one LDS-only barrier per step.  The
 // compute waves therefore carry no prefetch registers, so the state and the
 // e tiles stay in architectural VGPRs next to the MFMAs.
-template <typename T, int C, int K, int NWC, int NWL, int NWO = 0, typename UT = T>
+template <typename T, int C, int K, int NWC, int NWL, int NWO = 0, typename UT = T, bool PC = false>
 struct K3S {
   static constexpr int NTL = 64 * NWL;          // loader threads
   static constexpr int BV = 16 * NWC;           // value columns per workgroup
@@ -326,11 +326,13 @@ struct K3S {
   static constexpr int NPU = BV * C / 8;        // 8-element pieces of the u tile
   static constexpr int NLD = (NPW + NTL - 1) / NTL;   // w and k pieces per loader thread
   static constexpr int NLU = (NPU + NTL - 1) / NTL;   // u pieces per loader thread
-  static constexpr int NKS = (C + 4) / 4;       // float4 pieces of a kscale row
+  // float4 pieces of a kscale row, or (per-channel gate) of the decay exp(G_L)
+  static constexpr int KSN = PC ? K : C + 4;
+  static constexpr int NKS = KSN / 4;
   static constexpr int WP = K + 16 / sizeof(T);
   static constexpr int KP = K + 32 / sizeof(T);
   static constexpr int UP = C + 16 / sizeof(UT); // u rows (one per value column), +16 B
-  static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(UT) + (C + 4) * 4;
+  static constexpr size_t buf_bytes = (size_t)C * (WP + KP) * sizeof(T) + (size_t)BV * UP * sizeof(UT) + KSN * 4;
   static constexpr bool fits = 2 * buf_bytes <= 160 * 1024 && NKS <= NTL;
   // Output staging: the compute waves leave h and e of a step in LDS and the
   // loader waves store them during the next step, so the compute waves issue
@@ -366,7 +368,7 @@ struct K3S {
     T w[2][C * WP];
     T k[2][C * KP];
     UT u[2][BV * UP];
-    float ks[2][C + 4];
+    __attribute__((aligned(16))) float ks[2][KSN];
     T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
     T es[STG ? 2 : 1][STG ? BV * VSP : 8];
     T q[OUT ? 2 : 1][OUT ? C * QP : 8];
@@ -383,9 +385,14 @@ struct K3S {
 // pre-process) writes neither h nor v_new.  ZU: u is zero (the transition
 // scan), so it is neither read nor staged.  UT: u's storage type (fp32 from
 // the separate WY stage, the input dtype from the fused K1 + K2 stage).
-template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T>
+// PC: per-channel gate, with the chunk's gated keys exp(G_L - G_t) k^_t and
+// decay exp(G_L) from the WY stage in place of the raw keys and the token
+// factors: S <- diag(exp(G_L)) S + Kt^T e.
+template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T,
+          bool PC = false>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
-  using Cfg = K3S<T, C, K, NWC, NWL, NWO, UT>;
+  using Cfg = K3S<T, C, K, NWC, NWL, NWO, UT, PC>;
+  static_assert(!PC || NWO == 0, "the fused output takes a scalar gate");
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
   constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
@@ -433,7 +440,9 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     R.t0 = seq_t0 + (c - c_begin) * C;
     R.L = (int)((seq_end - R.t0) < C ? (seq_end - R.t0) : C);
     const T* wp = wbase + (c * HV + j) * (int64_t)(C * K);
-    const T* krow = kp + (R.t0 * H + h) * K;
+    // scalar gate: the raw key rows of the input; per-channel: the chunk's gated rows
+    const T* krow = PC ? static_cast<const T*>(a.kt) + (c * HV + j) * (int64_t)(C * K) : kp + (R.t0 * H + h) * K;
+    const int kstride = PC ? K : (int)(H * K);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int idx = tl + NTL * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       // Rows past L load row L-1 (a valid address) and are zeroed when staged;
       // pieces past the tile load piece 0 and are never staged.
       const int tc = t < R.L ? t : R.L - 1;
-      R.k[i] = ld8(krow + (tc * (int)(H * K) + d8));
+      R.k[i] = ld8(krow + (tc * kstride + d8));
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
       if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
     }
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         R.u[i] = ld8(up + 8 * (((NPU % NTL == 0) || idx < NPU) ? idx : 0));
       }
     }
-    const float* ksp = a.kscale + (c * HV + j) * kscale_pitch(C);
+    const float* ksp = PC ? a.dl + (c * HV + j) * (int64_t)K : a.kscale + (c * HV + j) * kscale_pitch(C);
     R.ks = *reinterpret_cast<const f32x4*>(ksp + 4 * (tl < NKS ? tl : 0));
     // fused output: G_t and 1 / |k_t| of the chunk (K1's token factors), and
     // for the column factor G at the end of t's key block (the chunk's last
@@ -790,8 +799,9 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     for (int eb = 0; eb < NE; ++eb) E[eb] = ZU ? zero4() : ld4f(urow + 16 * eb + 4 * g4);
     f32x4 sc[NE];
 #pragma unroll
-    for (int eb = 0; eb < NE; ++eb) sc[eb] = *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
-    const float gl = sm.ks[b][C];
+    for (int eb = 0; eb < NE; ++eb)
+      sc[eb] = PC ? f32x4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * eb + 4 * g4]);
+    const float gl = PC ? 1.f : sm.ks[b][C];
     // h[c] = S (transposed): staged in LDS for the loaders, or stored directly
     // with feature blocks paired into 16-byte stores
     if constexpr (STG && (OUT || KEEP)) {
@@ -823,8 +833,14 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     }
     // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e: e as a hi + lo
     // pair except in the fused scan + output stage
+    if constexpr (PC) {
+      // row d of S decays by exp(G_L,d)
 #pragma unroll
-    for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+      for (int mb = 0; mb < NS; ++mb) S[mb] *= *reinterpret_cast<const f32x4*>(&sm.ks[b][16 * mb + 4 * g4]);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
+    }
     if constexpr (OUT) {
       Frag<T> Ef[KSC];
 #pragma unroll
@@ -899,8 +915,37 @@ hipError_t launch_keep(const Args& a, hipStream_t s) {
   }
 }
 
+// Per-channel gate with the WY stage's gated keys and decay (a.kt, a.dl): the
+// warp-specialised scan in its per-channel mode, u in fp32.
+// (K = 256 keeps the other per-channel scan: its loaders' payload would spill)
+template <typename T, int C, int K>
+constexpr bool pc_scan_fits() {
+  return K <= 128 && K3S<T, C, K, 2, scan_loaders<T, C, K, float>(), 0, float, true>::fits &&
+         K3S<T, C, K, 1, scan_loaders<T, C, K, float>(), 0, float, true>::fits;
+}
+
+template <typename T, int C, int K>
+hipError_t launch_keep_pc(const Args& a, hipStream_t s) {
+  constexpr int NWL = scan_loaders<T, C, K, float>();
+  if constexpr (!pc_scan_fits<T, C, K>()) {
+    return hipErrorInvalidValue;
+  } else {
+    const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+    if (nblk32 < kNumCUs)
+      hipLaunchKernelGGL((k3_scan<T, C, K, 1, NWL, 0, true, false, float, true>), dim3((unsigned)(2 * nblk32)),
+                         dim3(64 * (1 + NWL)), 0, s, a);
+    else
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 0, true, false, float, true>), dim3((unsigned)nblk32),
+                         dim3(64 * (2 + NWL)), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
 template <typename T, int C, int K, bool PC>
 hipError_t launch_t(const Args& a, hipStream_t s) {
+  if constexpr (PC && pc_scan_fits<T, C, K>()) {
+    if (a.kt != nullptr && a.dl != nullptr && a.h != nullptr && a.u_f32) return launch_keep_pc<T, C, K>(a, s);
+  }
   if constexpr (!PC) {
     // warp-specialised scan: 2 compute + 2 loader waves (4 loader waves when
     // elements are fp32 or K = 256, to keep each loader's payload in registers)
@@ -1027,6 +1072,23 @@ bool specialised_k(int64_t K) {
   return false;
 }
 }  // namespace
+
+bool fwd_pc_scan_fits(int dtype, int C, int K) {
+  auto k = [&](auto tc, auto cc) {
+    using TT = decltype(tc);
+    constexpr int CC = decltype(cc)::value;
+    switch (K) {
+      case 32: return pc_scan_fits<TT, CC, 32>();
+      case 64: return pc_scan_fits<TT, CC, 64>();
+      case 128: return pc_scan_fits<TT, CC, 128>();
+      case 256: return pc_scan_fits<TT, CC, 256>();
+    }
+    return false;
+  };
+  if (dtype == GDR_BF16)
+    return C == 32 ? k(bf16{}, std::integral_constant<int, 32>{}) : k(bf16{}, std::integral_constant<int, 64>{});
+  return C == 32 ? k(float{}, std::integral_constant<int, 32>{}) : k(float{}, std::integral_constant<int, 64>{});
+}
 
 bool fwd_h_states_optional(const Args& a) {
   if (a.per_channel) return false;

@@ -114,10 +114,14 @@ typedef struct {
  *                                         and 3 zeros, then G_t (chunk-local gate cumsum),
  *                                         then 1 / |k_t| (1 without the in-kernel norm);
  *                                         0 past L
+ *   kt         dtype [NT_max][HV][C][K]   per-channel gate, written by the full forward's
+ *                                         WY stage for its state scan: exp(G_L - G_t) k^_t
+ *                                         per row t (zero past L); no bytes otherwise
+ *   dl         f32   [NT_max][HV][K]      per-channel gate: exp(G_L) per feature
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;
-  size_t chunk_idx, chunk_off, seq_order, Tm, w, u, h, v_new, kscale, total;
+  size_t chunk_idx, chunk_off, seq_order, Tm, w, u, h, v_new, kscale, kt, dl, total;
 } gdr_fwd_layout;
 
 /* ABI version of this header (bumped on incompatible changes). */

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdr_abi_version() == 4
+    assert L.gdr_abi_version() == 5
 
 
 def test_status_strings():
@@ -101,9 +101,15 @@ def test_workspace_layout():
     assert f.u - f.w >= nt * HV * C * K * 2 and f.kscale - f.u >= nt * HV * V * C * 2
     assert f.kscale - f.u < nt * HV * V * C * 4
     assert f.total < lay.total // 2
-    # a shape without the fused scan + output stage (per-channel gate) keeps the full layout
+    # a shape without the fused scan + output stage (per-channel gate) keeps the full layout,
+    # plus the WY stage's gated keys and decay for the state scan
     pc = gdr.fwd_layout(problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1))
     assert pc.w - pc.Tm >= nt * HV * C * C * 2 and pc.v_new > pc.h
+    assert pc.dl - pc.kt >= nt * HV * C * K * 2 and pc.total - pc.dl >= nt * HV * K * 4
+    assert lay.kt == lay.dl == lay.total and f.kt == f.dl == f.total
+    # the backward keeps its own gated rows: its forward part reserves none
+    bl = gdr.bwd_layout(problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1, chunk_size=32))
+    assert bl.fwd.kt == bl.fwd.dl and bl.dl > bl.kt
     # varlen bound floor(T / C) + N
     pv = problem(B=1, T=25344, H=16, HV=32, K=128, V=128, N=24)
     assert gdr.fwd_layout(pv).nt_max == 25344 // 64 + 24
