@@ -49,16 +49,33 @@ PEAK_MFMA_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def stage_bytes_per_token_head(w, T_seq):
+def stage_bytes_per_token_head(w, T_seq, pc_fused=False):
     """Algorithmic HBM bytes per (token, value head) of each forward stage:
     every tensor counted once when written and once per reading stage, at the
     library's storage dtypes (q/k/v/o and the intermediates in the input dtype,
     except the separate WY stage's u, which is fp32; g and beta in fp32, h0/ht
-    fp32)."""
+    fp32).  ``pc_fused``: the per-channel forward whose K1 also writes aqk,
+    K2 the gated query pair, read by the per-channel fused scan + output."""
     e = 2 if w.dtype == "bf16" else 4
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
     gb = 4 * K if w.per_channel_gate else 4
+    if w.per_channel_gate and K <= 128:
+        # the WY stage also writes the scan's gated keys kt and decay dl, which
+        # the scan reads in place of k and g
+        kt_dl = e * K + 4 * K / C
+        d = {
+            "kkt_solve": r * K * e + gb + 4 + e * C,
+            "wy": r * K * e + V * e + e * C + gb + 4 + e * K + 4 * V + kt_dl,
+            "fwd_h": e * K + 4 * V + kt_dl + e * V + e * K * V / C + 8 * K * V / T_seq,
+            "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
+        }
+        if pc_fused:
+            d["kkt_solve"] += r * K * e + 4 * C      # + q read, aqk (fp32) written
+            d["wy"] += r * K * e + 2 * e * K         # + q read, the hi + lo query pair written
+            # w, u, kt, dl, the query pair, aqk -> o, ht (h and v_new stay on chip)
+            d["fwd_h_o"] = e * K + 4 * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
+        return d
     # K1's per-chunk token factors (scalar gate): 3C + 4 floats per chunk and
     # value head, of which the separate scan reads the first C + 4
     kf_row = 0 if w.per_channel_gate else 4 * (3 * C + 4) / C
@@ -505,7 +522,8 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     fwd_ms = call_stage_ms(gdr, fwd_call, reps)
     T_seq = inp["B"] * inp["T"] / inp["N"]
     units = tokens * w.HV
-    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq).items() if k in fwd_ms}
+    pc_fused = not backward and gdr.chunk_fwd_fused(p) == 2
+    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq, pc_fused).items() if k in fwd_ms}
     rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
            "timing": {**timing, "what": "HIP events around each whole call on the launch stream; "
                                         "ms_per_step = median_ms; wall_ms = wall clock per step"},

@@ -51,7 +51,7 @@ class GdrFwdLayout(ctypes.Structure):
                 ("w", ctypes.c_size_t),
                 ("u", ctypes.c_size_t), ("h", ctypes.c_size_t), ("v_new", ctypes.c_size_t),
                 ("kscale", ctypes.c_size_t), ("kt", ctypes.c_size_t), ("dl", ctypes.c_size_t),
-                ("total", ctypes.c_size_t)]
+                ("aqk", ctypes.c_size_t), ("qgs", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 class GdrBwdLayout(ctypes.Structure):
@@ -316,13 +316,16 @@ def stage_times(max_stages: int = 8192) -> list:
 
 def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout] = None) -> dict:
     """Typed views of the forward intermediates inside a workspace tensor (of
-    the layout ``lay``, by default the one gdr_chunk_fwd uses for ``p``).  The
-    compact layout of the fused stages has no Tm, h or v_new and keeps u in the
-    input dtype: those views are None there."""
+    the layout ``lay``, by default the one gdr_chunk_fwd uses for ``p``).  A
+    region the layout gives no bytes has a None view: the compact layout of the
+    scalar-gate fused stages has no Tm, h or v_new and keeps u in the input
+    dtype; the per-channel fused forward has no h or v_new but aqk and qgs."""
     if lay is None:
         lay = fwd_layout(p)
     nt, C, HV, K, V = lay.nt_max, p.chunk_size, p.HV, p.K, p.V
     compact = nt > 0 and lay.Tm == lay.w
+    no_states = nt > 0 and lay.h == lay.v_new
+    pc_fused = nt > 0 and lay.qgs > lay.aqk
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 
@@ -342,9 +345,13 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
         # fused K1 + K2 stage writes it (input dtype)
         u=None if compact else view(lay.u, (nt, HV, V, C), torch.float32, 4),
         u_fused=view(lay.u, (nt, HV, V, C), dt, es),
-        h=None if compact else view(lay.h, (nt, HV, V, K), dt, es),
-        v_new=None if compact else view(lay.v_new, (nt, HV, V, C), dt, es),
+        h=None if no_states else view(lay.h, (nt, HV, V, K), dt, es),
+        v_new=None if no_states else view(lay.v_new, (nt, HV, V, C), dt, es),
         kscale=None if p.gate_per_channel else view(lay.kscale, (nt, HV, 3 * C + 4), torch.float32, 4),
+        kt=view(lay.kt, (nt, HV, C, K), dt, es) if lay.dl > lay.kt else None,
+        dl=view(lay.dl, (nt, HV, K), torch.float32, 4) if lay.aqk > lay.dl else None,
+        aqk=view(lay.aqk, (nt, HV, C, C), torch.float32, 4) if pc_fused else None,
+        qgs=view(lay.qgs, (nt, HV, 2, C, K), dt, es) if pc_fused else None,
     )
 
 
@@ -386,9 +393,11 @@ def fwd_h_o_supported(p) -> bool:
     return bool(lib().gdr_fwd_h_o_supported(ctypes.byref(p)))
 
 
-def chunk_fwd_fused(p) -> bool:
-    """Whether gdr_chunk_fwd runs the fused scan + output stage for ``p``."""
-    return bool(lib().gdr_chunk_fwd_fused(ctypes.byref(p)))
+def chunk_fwd_fused(p) -> int:
+    """Which fused scan + output stage gdr_chunk_fwd runs for ``p``: 1 with the
+    fused K1 + K2 stage (scalar gate), 2 the per-channel one after separate K1
+    and K2, 0 none (separate stages)."""
+    return int(lib().gdr_chunk_fwd_fused(ctypes.byref(p)))
 
 
 def fwd_h_o(p, q, k, w, u, g, kscale, chunk_idx, chunk_off, h0, o, ht):

@@ -140,8 +140,10 @@ gdr::Args make_args(const gdr_problem& p) {
 
 // pc_regions: with a per-channel gate, reserve the WY stage's gated keys and
 // decay for the warp-specialised scan (the backward keeps its own; the
-// segmented forward runs the other per-channel scan).
-gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true) {
+// segmented forward runs the other per-channel scan).  pc_fused: the
+// per-channel fused scan + output runs, so h and v_new get no bytes and the
+// aqk and gated-query regions it reads do.
+gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_fused = false) {
   gdr_fwd_layout l;
   const int64_t nt = gdr::nt_max(p);
   const size_t es = elem_size(p);
@@ -161,16 +163,20 @@ gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true) {
   l.u = off;   // fp32 from the separate WY stage, input dtype from the fused K1 + K2 stage
   off = round_up(off + (size_t)nt * HV * V * C * sizeof(float));
   l.h = off;
-  off = round_up(off + (size_t)nt * HV * V * K * es);
+  off = round_up(off + (pc_fused ? 0 : (size_t)nt * HV * V * K * es));
   l.v_new = off;
-  off = round_up(off + (size_t)nt * HV * V * C * es);
+  off = round_up(off + (pc_fused ? 0 : (size_t)nt * HV * V * C * es));
   l.kscale = off;
   off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float)));
   const bool pcs = pc_regions && p.gate_per_channel && gdr::fwd_pc_scan_fits(p.dtype, (int)C, (int)K);
   l.kt = off;
-  off = round_up(off + (pcs ? (size_t)nt * HV * C * K * es : 0));
+  off = round_up(off + (pcs || pc_fused ? (size_t)nt * HV * C * K * es : 0));
   l.dl = off;
-  off = round_up(off + (pcs ? (size_t)nt * HV * K * sizeof(float) : 0));
+  off = round_up(off + (pcs || pc_fused ? (size_t)nt * HV * K * sizeof(float) : 0));
+  l.aqk = off;
+  off = round_up(off + (pc_fused ? (size_t)nt * HV * C * C * sizeof(float) : 0));
+  l.qgs = off;
+  off = round_up(off + (pc_fused ? (size_t)nt * HV * 2 * C * K * es : 0));
   l.total = off;
   return l;
 }
@@ -201,15 +207,32 @@ gdr_fwd_layout fused_layout_of(const gdr_problem& p) {
   off = round_up(off + (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float));
   l.kt = off;
   l.dl = off;
+  l.aqk = off;
+  l.qgs = off;
   l.total = off;
   return l;
 }
 
+// Which fused forward gdr_chunk_fwd runs for the (padded) problem: 1 = fused
+// K1 + K2 and fused scan + output (scalar gate), 2 = separate K1 and K2 and
+// the per-channel fused scan + output, 0 = the separate stages.
+int fused_kind(const gdr_problem& pp) {
+  if (pp.keep_states) return 0;
+  const Args a = make_args(pp);
+  if (gdr::fwd_h_o_preferred(a)) return 1;
+  if (gdr::fwd_h_o_pc_preferred(a)) return 2;
+  return 0;
+}
+
 // The layout gdr_chunk_fwd works in: the compact one when the fused stages run
-// (no keep_states and a shape with the fused scan + output stage), else the
+// (no keep_states and a shape with a fused scan + output stage), else the
 // full one with Tm, h and v_new.
 gdr_fwd_layout fwd_layout_for(const gdr_problem& pp) {
-  return (!pp.keep_states && gdr::fwd_h_o_preferred(make_args(pp))) ? fused_layout_of(pp) : layout_of(pp);
+  switch (fused_kind(pp)) {
+    case 1: return fused_layout_of(pp);
+    case 2: return layout_of(pp, true, true);
+  }
+  return layout_of(pp);
 }
 
 gdr_status hip_status(hipError_t e) { return e == hipSuccess ? GDR_OK : GDR_ERR_HIP; }
@@ -352,7 +375,24 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   a.o = o;
   a.ht = ht;
   hipError_t e = hipSuccess;
-  if (!p.keep_states && gdr::fwd_h_o_preferred(a)) {
+  const int kind = fused_kind(p);
+  if (kind == 2 && l.qgs > l.aqk) {
+    // per-channel gate: K1 also writes aqk and K2 the gated query pair, and
+    // the fused scan + output reads them (h and v_new stay on chip)
+    a.u_f32 = 1;
+    a.h = nullptr;
+    a.v_new = nullptr;
+    a.aqk = reinterpret_cast<float*>(ws + l.aqk);
+    a.qgs = ws + l.qgs;
+    e = gdr::launch_chunk_table(a, s);
+    timer_mark(e, "chunk_table", s);
+    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+    timer_mark(e, "kkt_solve", s);
+    if (e == hipSuccess) e = gdr::launch_wy(a, s);
+    timer_mark(e, "wy", s);
+    if (e == hipSuccess) e = gdr::launch_fwd_h_o_pc(a, s);
+    timer_mark(e, "fwd_h_o", s);
+  } else if (kind == 1) {
     // fused K1 + K2 (Tm stays on chip) and fused scan + output (h and v_new
     // stay on chip); for a dense batch the first writes the chunk table too
     if (cu_seqlens == nullptr && a.NTmax > 0) {
@@ -522,7 +562,7 @@ gdr_status chunk_fwd_run(const gdr_problem& p0, const void* q, const void* k, co
 
 extern "C" {
 
-int gdr_abi_version(void) { return 5; }
+int gdr_abi_version(void) { return 6; }
 
 gdr_status gdr_stage_timing(int enable) {
   t_timer.on = enable != 0;
@@ -736,7 +776,7 @@ gdr_status gdr_fwd_h(const gdr_problem* p, const void* k, const void* w, const v
 
 int gdr_chunk_fwd_fused(const gdr_problem* p) {
   if (check(p, p ? p->N != p->B : false, true) != GDR_OK) return 0;
-  return !p->keep_states && gdr::fwd_h_o_preferred(make_args(padded_problem(*p))) ? 1 : 0;
+  return fused_kind(padded_problem(*p));
 }
 
 int gdr_fwd_h_o_supported(const gdr_problem* p) {

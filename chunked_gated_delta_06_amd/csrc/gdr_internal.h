@@ -73,6 +73,13 @@ struct Args {
   void* kt;
   void* qg;
   float* dl;
+  // forward with a per-channel gate and the fused scan + output: the chunk's
+  // intra attention aqk[r][t] = scale sum_d q^_rd k^_td exp(G_rd - G_td) for
+  // t <= r (fp32 [NT][HV][C][C], zero above the diagonal and past L), written
+  // by K1, and its gated queries scale exp(G_t) q^_t as a bf16 hi + lo pair
+  // (qgs [NT][HV][2][C][K]: the hi tile, then the lo tile), written by K2
+  float* aqk;
+  void* qgs;
 };
 
 int64_t nt_max(const gdr_problem& p);
@@ -93,6 +100,12 @@ bool fwd_h_o_supported(const Args& a);
 bool fwd_h_o_preferred(const Args& a);   // the full forward's choice
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
+// per-channel gate: the fused scan + output on K2's gated keys / decay and the
+// aqk / qgs tiles (bf16, chunk 32, K <= 128); *_preferred is the full
+// forward's choice
+bool fwd_h_o_pc_supported(const Args& a);
+bool fwd_h_o_pc_preferred(const Args& a);
+hipError_t launch_fwd_h_o_pc(const Args& a, hipStream_t s);
 // token-by-token forward (no chunk table, no workspace)
 hipError_t launch_recurrent(const Args& a, hipStream_t s);
 hipError_t launch_bwd_intra(const Args& a, hipStream_t s);

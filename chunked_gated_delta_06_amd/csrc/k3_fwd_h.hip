@@ -348,15 +348,23 @@ struct K3S {
   static constexpr bool STG = 2 * (buf_bytes + stg_bytes) <= 160 * 1024;
   static constexpr int NDH = (BV * K / 8 + NTL - 1) / NTL;   // staged h pieces per loader thread
   static constexpr int NDV = (BV * C / 8 + NTL - 1) / NTL;   // staged e pieces per loader thread
-  // fused output: the loaders also stage each chunk's q tile and gates
+  // fused output: the loaders also stage each chunk's q tile and gates, or
+  // (per-channel gate) the gated queries as a hi + lo pair of tiles and the
+  // intra attention aqk (fp32 rows)
   static constexpr bool OUT = NWO > 0;
+  static constexpr bool PCO = OUT && PC;
   static constexpr int QP = K + (sizeof(T) == 2 ? 32 : 16) / sizeof(T);   // staged q rows, padded as h
-  static constexpr size_t q_bytes = OUT ? (size_t)C * QP * sizeof(T) + 3 * C * 4 : 0;
+  static constexpr int NQT = PCO ? 2 : 1;       // staged query tiles
+  static constexpr int AP = C + 4;              // staged aqk rows
+  static constexpr int NLA = PCO ? (C * C / 4 + NTL - 1) / NTL : 1;   // float4 pieces of aqk per loader thread
+  static constexpr size_t q_bytes =
+      OUT ? (size_t)NQT * C * QP * sizeof(T) + (PCO ? (size_t)C * AP * 4 : 3 * C * 4) : 0;
   static constexpr bool fits_out = STG && 2 * (buf_bytes + stg_bytes + q_bytes) <= 160 * 1024;
 
   struct Regs {
     Frag<T> w[NLD], k[NLD];
-    Frag<T> q[OUT ? NLD : 1];
+    Frag<T> q[OUT ? NQT * NLD : 1];
+    f32x4 pa[NLA];            // aqk pieces (per-channel fused output)
     Frag<UT> u[NLU];
     f32x4 ks;
     float g2;                 // G_t (threads < C) or 1 / |k_t| (threads C .. 2C - 1)
@@ -371,13 +379,14 @@ struct K3S {
     __attribute__((aligned(16))) float ks[2][KSN];
     T hs[STG ? 2 : 1][STG ? BV * HSP : 8];
     T es[STG ? 2 : 1][STG ? BV * VSP : 8];
-    T q[OUT ? 2 : 1][OUT ? C * QP : 8];
+    T q[OUT ? 2 : 1][OUT ? NQT * C * QP : 8];
     // per token of the staged chunk: gate cumsum G_t in log2 units, 1 / |k_t|
     // and the column factor exp(G_e - G_t) / |k_t|, e the last token of t's
     // key block (zero past L)
-    __attribute__((aligned(16))) float gq[OUT ? 2 : 1][OUT ? C : 4];
-    __attribute__((aligned(16))) float rk[OUT ? 2 : 1][OUT ? C : 4];
-    __attribute__((aligned(16))) float cf[OUT ? 2 : 1][OUT ? C : 4];
+    __attribute__((aligned(16))) float gq[OUT && !PC ? 2 : 1][OUT && !PC ? C : 4];
+    __attribute__((aligned(16))) float rk[OUT && !PC ? 2 : 1][OUT && !PC ? C : 4];
+    __attribute__((aligned(16))) float cf[OUT && !PC ? 2 : 1][OUT && !PC ? C : 4];
+    __attribute__((aligned(16))) float pa[PCO ? 2 : 1][PCO ? C * AP : 4];
   };
 };
 
@@ -387,12 +396,14 @@ struct K3S {
 // the separate WY stage, the input dtype from the fused K1 + K2 stage).
 // PC: per-channel gate, with the chunk's gated keys exp(G_L - G_t) k^_t and
 // decay exp(G_L) from the WY stage in place of the raw keys and the token
-// factors: S <- diag(exp(G_L)) S + Kt^T e.
+// factors: S <- diag(exp(G_L)) S + Kt^T e.  With output waves as well (bf16),
+// o = (scale exp(G) q^) h + aqk e from K2's gated query pair and K1's aqk, so
+// the output waves apply no gate factor themselves.
 template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T,
           bool PC = false>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   using Cfg = K3S<T, C, K, NWC, NWL, NWO, UT, PC>;
-  static_assert(!PC || NWO == 0, "the fused output takes a scalar gate");
+  static_assert(!PC || NWO == 0 || sizeof(T) == 2, "the per-channel fused output stages bf16 query pairs");
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
   constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   // fused output: NWO output waves compute o from the staged h / e, and
   // neither h nor v_new is written
   constexpr bool OUT = Cfg::OUT;
-  constexpr int QP = Cfg::QP;
+  constexpr int QP = Cfg::QP, AP = Cfg::AP, NLA = Cfg::NLA;
   static_assert(!OUT || (Cfg::fits_out && Cfg::NTL >= 2 * C), "the fused output reads the staged h / e / q");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const bool loader = wv >= NWC + NWO;
@@ -454,7 +465,22 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       const int tc = t < R.L ? t : R.L - 1;
       R.k[i] = ld8(krow + (tc * kstride + d8));
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
-      if constexpr (OUT) R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
+      if constexpr (OUT && PC) {
+        // the chunk's gated query tiles (hi, then lo), zero past L
+        const T* qs = static_cast<const T*>(a.qgs) + (c * HV + j) * (int64_t)(2 * C * K);
+        R.q[i] = ld8(qs + 8 * (in ? idx : 0));
+        R.q[NLD + i] = ld8(qs + C * K + 8 * (in ? idx : 0));
+      } else if constexpr (OUT) {
+        R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
+      }
+    }
+    if constexpr (OUT && PC) {
+      const float* ap = a.aqk + (c * HV + j) * (int64_t)(C * C);
+#pragma unroll
+      for (int i = 0; i < NLA; ++i) {
+        const int idx = tl + NTL * i;
+        R.pa[i] = *reinterpret_cast<const f32x4*>(ap + 4 * (((C * C / 4) % NTL == 0 || idx < C * C / 4) ? idx : 0));
+      }
     }
     if constexpr (!ZU) {
       const UT* up = ubase + ((c * HV + j) * V + vw) * (int64_t)C;
@@ -469,7 +495,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
     // fused output: G_t and 1 / |k_t| of the chunk (K1's token factors), and
     // for the column factor G at the end of t's key block (the chunk's last
     // token when the block runs past it)
-    if constexpr (OUT) {
+    if constexpr (OUT && !PC) {
       R.g2 = ksp[C + 4 + (tl < 2 * C ? tl : 0)];
       const int tc = tl < C ? tl : 0;
       const int te = (tc | 15) < R.L - 1 ? (tc | 15) : R.L - 1;
@@ -484,10 +510,21 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       if ((NPW % NTL == 0) || idx < NPW) {
         st8(&sm.w[b][t * WP + d8], R.w[i]);
         st8(&sm.k[b][t * KP + d8], t < R.L ? R.k[i] : frag_zero<T>());
-        if constexpr (OUT) st8(&sm.q[b][t * QP + d8], t < R.L ? R.q[i] : frag_zero<T>());
+        if constexpr (OUT && PC) {
+          st8(&sm.q[b][t * QP + d8], R.q[i]);
+          st8(&sm.q[b][(C + t) * QP + d8], R.q[NLD + i]);
+        } else if constexpr (OUT) {
+          st8(&sm.q[b][t * QP + d8], t < R.L ? R.q[i] : frag_zero<T>());
+        }
       }
     }
-    if constexpr (OUT) {
+    if constexpr (OUT && PC) {
+#pragma unroll
+      for (int i = 0; i < NLA; ++i) {
+        const int idx = tl + NTL * i, r = idx / (C / 4), t4 = (idx % (C / 4)) * 4;
+        if ((C * C / 4) % NTL == 0 || idx < C * C / 4) *reinterpret_cast<f32x4*>(&sm.pa[b][r * AP + t4]) = R.pa[i];
+      }
+    } else if constexpr (OUT) {
       if (tl < C) {
         // past L: G of the chunk's last token, so every staged factor stays finite
         sm.gq[b][tl] = (tl < R.L ? R.g2 : R.gref) * kLog2e;
@@ -608,9 +645,10 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       T* __restrict__ op = static_cast<T*>(a.o);
       // operands of one chunk's output, carried from its P^T step to its o step
       struct ORegs {
-        Frag<T> q[TPW][KSK];        // q rows of this wave's token blocks
+        Frag<T> q[TPW][KSK];        // q rows of this wave's token blocks (per-channel: gated, hi part)
+        Frag<T> ql[PC ? TPW : 1][PC ? KSK : 1];   // per-channel: lo part of the gated rows
         SplitFrag<T> f[TPW][KSC];   // P^T as the chained B operand
-        float isc[TPW];             // scale exp(G_r) / |q_r|
+        float isc[TPW];             // scale exp(G_r) / |q_r| (scalar gate)
       };
       auto chunk_t0 = [&](int x) { return seq_t0 + (int64_t)x * C; };
       auto chunk_L = [&](int x) {
@@ -625,7 +663,31 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       // most 1).  |q_r|^2 is the diagonal of the block's Q Q^T product, and the
       // output scale rides on the row factors.  A column r >= L of P^T only
       // reaches row r of o, which is never stored.
-      auto pphase = [&](ORegs& P, int x) {
+      // Per-channel gate: the gated query pair and the aqk rows come staged,
+      // so the phase only reads them into operand registers (aqk rows are zero
+      // above the diagonal and past L).
+      auto pphase_pc = [&](ORegs& P, int x) {
+        const int b = x & 1;
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          const int rr = 16 * tbk(m) + r16;
+#pragma unroll
+          for (int ks = 0; ks < KSK; ++ks) {
+            P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
+            P.ql[m][ks] = ld8(&sm.q[b][(C + rr) * QP + 32 * ks + 8 * g4]);
+          }
+          const float* prow = &sm.pa[b][rr * AP];
+#pragma unroll
+          for (int kt = 0; kt < KSC; ++kt) {
+            if (2 * kt > tbk(m)) continue;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(prow + 32 * kt + 4 * g4);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(prow + 32 * kt + 16 + 4 * g4);
+            P.f[m][kt] = SplitFrag<T>::make(cat8(lo, hi));
+          }
+          P.isc[m] = 1.f;
+        }
+      };
+      auto pphase_sc = [&](ORegs& P, int x) {
         const int b = x & 1;
         float rs[TPW], Gr[TPW];      // scale / |q_r| and G_r (log2 units)
 #pragma unroll
@@ -695,6 +757,13 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
           P.isc[m] = rs[m] * exp2_fast(Gr[m]);
         }
       };
+      auto pphase = [&](ORegs& P, int x) {
+        if constexpr (PC) {
+          pphase_pc(P, x);
+        } else {
+          pphase_sc(P, x);
+        }
+      };
       // o of chunk x from the staged h / e (buffer x % 2) and its P^T step's operands
       auto ophase = [&](const ORegs& P, int x) {
         const int64_t t0 = chunk_t0(x);
@@ -712,8 +781,11 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
           for (int m = 0; m < TPW; ++m) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KSK; ++ks) mma(acc, hf[ks], P.q[m][ks]);
-            acc *= P.isc[m];
+            for (int ks = 0; ks < KSK; ++ks) {
+              mma(acc, hf[ks], P.q[m][ks]);
+              if constexpr (PC) mma(acc, hf[ks], P.ql[m][ks]);
+            }
+            if constexpr (!PC) acc *= P.isc[m];
 #pragma unroll
             for (int kt = 0; kt < KSC; ++kt) {
               if (2 * kt > tbk(m)) continue;
@@ -832,7 +904,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
     }
     // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e: e as a hi + lo
-    // pair except in the fused scan + output stage
+    // pair except in the scalar-gate fused scan + output stage
     if constexpr (PC) {
       // row d of S decays by exp(G_L,d)
 #pragma unroll
@@ -841,7 +913,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
       for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
     }
-    if constexpr (OUT) {
+    if constexpr (OUT && !PC) {
       Frag<T> Ef[KSC];
 #pragma unroll
       for (int kt = 0; kt < KSC; ++kt) Ef[kt] = frag_from_halves<T>(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]);
@@ -1052,6 +1124,45 @@ hipError_t launch_fused_k(const Args& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// ---- fused state scan + output, per-channel gate (bf16, chunk 32): the
+// per-channel scan's compute and loader waves (u in fp32) plus 2 output waves
+// on K1's aqk and K2's gated query pair.  64 value columns (4 compute waves)
+// per workgroup when that grid still gives every compute unit a workgroup,
+// else 32.
+template <typename T, int C, int K>
+constexpr bool pc_out_ok() {
+  constexpr int NWL = scan_loaders<T, C, K, float>();
+  return sizeof(T) == 2 && C == 32 && K <= 128 && K3S<T, C, K, 4, NWL, 2, float, true>::fits_out &&
+         K3S<T, C, K, 2, NWL, 2, float, true>::fits_out;
+}
+
+template <typename T, int C, int K>
+hipError_t launch_pc_out_t(const Args& a, hipStream_t s) {
+  if constexpr (pc_out_ok<T, C, K>()) {
+    constexpr int NWL = scan_loaders<T, C, K, float>();
+    const int64_t nblk64 = a.N * a.HV * (a.V / 64);
+    if (a.V % 64 == 0 && nblk64 >= kNumCUs) {
+      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, false, false, float, true>), dim3((unsigned)nblk64),
+                         dim3(64 * (6 + NWL)), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, false, false, float, true>),
+                         dim3((unsigned)(a.N * a.HV * (a.V / 32))), dim3(64 * (4 + NWL)), 0, s, a);
+    }
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+bool pc_out_ok_k(int64_t K) {
+  switch (K) {
+    case 32: return pc_out_ok<bf16, 32, 32>();
+    case 64: return pc_out_ok<bf16, 32, 64>();
+    case 128: return pc_out_ok<bf16, 32, 128>();
+  }
+  return false;
+}
+
 }  // namespace
 
 namespace {
@@ -1112,6 +1223,25 @@ bool fwd_h_o_preferred(const Args& a) {
   // shapes (one 16-column compute wave per workgroup on few long sequences:
   // 1.78 vs 1.95 ms; two compute waves on 4 x 16 heads: 145 vs 222 us)
   return fwd_h_o_supported(a);
+}
+
+bool fwd_h_o_pc_supported(const Args& a) {
+  return a.per_channel && a.dtype == GDR_BF16 && a.C == 32 && pc_out_ok_k(a.K) && a.V % 32 == 0;
+}
+
+bool fwd_h_o_pc_preferred(const Args& a) { return fwd_h_o_pc_supported(a); }
+
+hipError_t launch_fwd_h_o_pc(const Args& a, hipStream_t s) {
+  if (a.N == 0) return hipSuccess;
+  if (!fwd_h_o_pc_supported(a) || a.kt == nullptr || a.dl == nullptr || a.aqk == nullptr || a.qgs == nullptr ||
+      a.u == nullptr || !a.u_f32)
+    return hipErrorInvalidValue;
+  switch (a.K) {
+    case 32: return launch_pc_out_t<bf16, 32, 32>(a, s);
+    case 64: return launch_pc_out_t<bf16, 32, 64>(a, s);
+    case 128: return launch_pc_out_t<bf16, 32, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s) {

@@ -81,8 +81,9 @@ typedef struct {
   float scale;               /* output scale */
   int32_t keep_states;       /* gdr_chunk_fwd: 1 = run the separate K1..K4 stages and leave
                                 Tm, h and v_new in the workspace; 0 = use the fused stages
-                                where gdr_fwd_h_o_supported (Tm, h and v_new are then not
-                                written).  gdr_chunk_bwd: 1 = take those intermediates
+                                where gdr_chunk_fwd_fused reports them (h and v_new, and
+                                with a scalar gate Tm, are then not written).
+                                gdr_chunk_bwd: 1 = take those intermediates
                                 from its workspace instead of recomputing them (see
                                 gdr_chunk_bwd) */
   int32_t beta_logits;       /* 1: beta holds logits and every kernel uses sigmoid(beta) (the
@@ -94,9 +95,11 @@ typedef struct {
 /* Offsets (bytes from the workspace base) of the forward intermediates that
  * gdr_chunk_fwd keeps in its workspace; NT_max = B * ceil(T / C) for a dense
  * batch and floor(T / C) + N for a varlen batch.  When the forward takes the
- * fused stages (keep_states = 0 and a shape gdr_chunk_fwd_fused reports), the
- * layout is the compact one those stages use: Tm, h and v_new get no bytes
- * (their offsets equal the next region's) and u is in `dtype`.
+ * fused stages (keep_states = 0 and gdr_chunk_fwd_fused(p) != 0), the layout is
+ * the compact one those stages use: h and v_new get no bytes (their offsets
+ * equal the next region's); with a scalar gate (kind 1) neither does Tm, and u
+ * is in `dtype`; with a per-channel gate (kind 2) the aqk and qgs regions
+ * below get bytes.  Regions a layout does not use have no bytes.
  *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
  *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
  *   seq_order  int32 [N]           varlen batches of at most 1024 sequences: the sequences
@@ -118,10 +121,20 @@ typedef struct {
  *                                         WY stage for its state scan: exp(G_L - G_t) k^_t
  *                                         per row t (zero past L); no bytes otherwise
  *   dl         f32   [NT_max][HV][K]      per-channel gate: exp(G_L) per feature
+ *   aqk        f32   [NT_max][HV][C][C]   per-channel fused forward only, written by K1:
+ *                                         the chunk's intra attention, row r, column t:
+ *                                         scale sum_d q^_rd k^_td exp(G_rd - G_td) for
+ *                                         t <= r (the Q K^T o M term of the chunk form's
+ *                                         output, coverage-matrix page, section 2), zero
+ *                                         above the diagonal and in rows past L
+ *   qgs        dtype [NT_max][HV][2][C][K] per-channel fused forward only, written by K2:
+ *                                         the gated queries scale exp(G_t) q^_t as a bf16
+ *                                         hi tile then a lo tile (hi + lo = the fp32 value
+ *                                         to about 16 mantissa bits)
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;
-  size_t chunk_idx, chunk_off, seq_order, Tm, w, u, h, v_new, kscale, kt, dl, total;
+  size_t chunk_idx, chunk_off, seq_order, Tm, w, u, h, v_new, kscale, kt, dl, aqk, qgs, total;
 } gdr_fwd_layout;
 
 /* ABI version of this header (bumped on incompatible changes). */
@@ -176,11 +189,15 @@ gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout
  * intermediates of gdr_fwd_layout / gdr_bwd_layout then have the padded dims. */
 
 /* Full forward: K0 chunk table -> K1 kkt + triangular inverse -> K2 WY w/u ->
- * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0 and a
- * shape that gdr_fwd_h_o_supported accepts, K1 and K2 run as the one fused
- * stage gdr_fwd_kkt_wy and K3 and K4 as the one fused stage gdr_fwd_h_o, and
- * the Tm, h and v_new regions of the workspace are left untouched;
- * gdr_chunk_fwd_fused(p) returns 1 exactly then.
+ * K3 state scan -> K4 output, all on `stream`.  With p->keep_states == 0:
+ *  - scalar gate, a shape that gdr_fwd_h_o_supported accepts: K1 and K2 run as
+ *    the one fused stage gdr_fwd_kkt_wy and K3 and K4 as the one fused stage
+ *    gdr_fwd_h_o, and the Tm, h and v_new regions are left untouched;
+ *    gdr_chunk_fwd_fused(p) returns 1 exactly then;
+ *  - per-channel gate, bf16, chunk 32, K <= 128: K1 also writes aqk, K2 also
+ *    writes qgs (layout above), and K3 and K4 run as one fused scan + output
+ *    stage that reads them, so h and v_new are not written;
+ *    gdr_chunk_fwd_fused(p) returns 2 exactly then (0 otherwise).
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
@@ -201,8 +218,8 @@ gdr_status gdr_chunk_fwd(const gdr_problem* p, const void* q, const void* k, con
  * workspace), kernels and results as gdr_chunk_fwd; the intermediates live in
  * a fixed scratch array of GDR_NOALLOC_SCRATCH_BYTES per device, part of the
  * library's code object (allocated when the library is loaded on a device and
- * held until the process ends).  With the fused stages (gdr_chunk_fwd_fused)
- * the scratch holds the chunk tables, w, u and kscale (about 524 bytes per
+ * held until the process ends).  With the scalar-gate fused stages
+ * (gdr_chunk_fwd_fused(p) == 1) the scratch holds the chunk tables, w, u and kscale (about 524 bytes per
  * token and value head for bf16 with K = V = 128 at chunk 64), so such a
  * problem fits up to about 500 k (token, value head) pairs (4 x 4096 tokens x
  * 16 heads take half); a larger problem returns GDR_ERR_SCRATCH_LIMIT before

@@ -128,7 +128,8 @@ def _chunk(qc, kc, vc, Gc, bc, S0, scale, per_channel):
     E = U - W @ S0
     O = scale * (q_in @ S0 + qk @ E)           # qk already holds j <= r only
     S1 = decay_L[:, :, None] * S0 + np.transpose(k_out, (0, 2, 1)) @ E
-    return dict(A=A, T=Tm, W=W, U=U, E=E, O=O, S_next=S1)
+    return dict(A=A, T=Tm, W=W, U=U, E=E, O=O, S_next=S1, QK=scale * qk, QG=scale * q_in, KT=k_out,
+                DL=decay_L)
 
 
 def chunked_fwd(q, k, v, g, beta, *, scale=1.0, h0=None, cu_seqlens=None,
@@ -139,7 +140,10 @@ def chunked_fwd(q, k, v, g, beta, *, scale=1.0, h0=None, cu_seqlens=None,
     global chunk number of ``chunk_table``:
       G [NT,HV,C(,K)], A and T [NT,HV,C,C], W [NT,HV,C,K], U and E
       [NT,HV,C,V] (rows past a partial chunk's end are zero) and
-      h [NT,HV,K,V] (the state entering each chunk)."""
+      h [NT,HV,K,V] (the state entering each chunk); also the output's own
+      operands QK = scale (Q K^T o decay mask) [NT,HV,C,C], QG = scale
+      exp(G) q [NT,HV,C,K], and the state update's KT = exp(G_L - G) k
+      [NT,HV,C,K] and DL = exp(G_L) [NT,HV,K]."""
     q, k, v, g, beta, h0 = (_np64(x) for x in (q, k, v, g, beta, h0))
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
@@ -163,7 +167,9 @@ def chunked_fwd(q, k, v, g, beta, *, scale=1.0, h0=None, cu_seqlens=None,
         gshape = (NT, HV, C, K) if per_channel else (NT, HV, C)
         inter = dict(G=np.zeros(gshape), A=np.zeros((NT, HV, C, C)), T=np.zeros((NT, HV, C, C)),
                      W=np.zeros((NT, HV, C, K)), U=np.zeros((NT, HV, C, V)),
-                     E=np.zeros((NT, HV, C, V)), h=np.zeros((NT, HV, K, V)))
+                     E=np.zeros((NT, HV, C, V)), h=np.zeros((NT, HV, K, V)),
+                     QK=np.zeros((NT, HV, C, C)), QG=np.zeros((NT, HV, C, K)), KT=np.zeros((NT, HV, C, K)),
+                     DL=np.zeros((NT, HV, K)))
     for n in range(N):
         S = h0[n].copy() if h0 is not None else np.zeros((HV, K, V))
         for c in range(off[n], off[n + 1]):
@@ -179,6 +185,10 @@ def chunked_fwd(q, k, v, g, beta, *, scale=1.0, h0=None, cu_seqlens=None,
                 inter["W"][c, :, :L] = r["W"]
                 inter["U"][c, :, :L] = r["U"]
                 inter["E"][c, :, :L] = r["E"]
+                inter["QK"][c, :, :L, :L] = r["QK"]
+                inter["QG"][c, :, :L] = r["QG"]
+                inter["KT"][c, :, :L] = r["KT"]
+                inter["DL"][c] = r["DL"]
             o[sl] = np.transpose(r["O"], (1, 0, 2))
             S = r["S_next"]
         ht[n] = S

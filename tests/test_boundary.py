@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
     assert "gdr_chunk_bwd" in names and "gdr_bwd_dqkvg" in names
     for n in names:
         assert hasattr(L, n), n
-    assert L.gdr_abi_version() == 5
+    assert L.gdr_abi_version() == 6
 
 
 def test_status_strings():
@@ -107,6 +107,24 @@ def test_workspace_layout():
     assert pc.w - pc.Tm >= nt * HV * C * C * 2 and pc.v_new > pc.h
     assert pc.dl - pc.kt >= nt * HV * C * K * 2 and pc.total - pc.dl >= nt * HV * K * 4
     assert lay.kt == lay.dl == lay.total and f.kt == f.dl == f.total
+    # per-channel gate, bf16, chunk 32, K <= 128: the per-channel fused scan + output, so no
+    # h / v_new, and K1's aqk and K2's gated query pair for it
+    p32 = problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1, chunk_size=32)
+    assert gdr.lib().gdr_chunk_fwd_fused(ctypes.byref(p32)) == 2
+    q = gdr.fwd_layout(p32)
+    n32 = 4 * 128
+    offs = [q.chunk_idx, q.Tm, q.w, q.u, q.h, q.kt, q.dl, q.aqk, q.qgs, q.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert q.h == q.v_new == q.kscale == q.kt and q.w - q.Tm >= n32 * HV * 32 * 32 * 2
+    assert q.h - q.u >= n32 * HV * V * 32 * 4
+    assert q.dl - q.kt >= n32 * HV * 32 * K * 2 and q.aqk - q.dl >= n32 * HV * K * 4
+    assert q.qgs - q.aqk >= n32 * HV * 32 * 32 * 4 and q.total - q.qgs >= n32 * HV * 2 * 32 * K * 2
+    for kw in (dict(keep_states=1), dict(dtype=gdr.GDR_FP32), dict(K=256), dict(chunk_size=64)):
+        other = problem(**{**dict(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1,
+                                  chunk_size=32), **kw})
+        assert gdr.lib().gdr_chunk_fwd_fused(ctypes.byref(other)) == 0, kw
+        o = gdr.fwd_layout(other)
+        assert o.aqk == o.qgs == o.total and o.v_new > o.h, kw
     # the backward keeps its own gated rows: its forward part reserves none
     bl = gdr.bwd_layout(problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1, chunk_size=32))
     assert bl.fwd.kt == bl.fwd.dl and bl.dl > bl.kt
@@ -180,6 +198,8 @@ def test_fused_stage_support_and_host_rejections():
     assert fused(B=4, N=4, HV=16, H=16, K=128, V=128, keep_states=1) == 0
     assert fused(B=1, N=1, HV=32, H=32, K=128, V=128) == 1     # 16-column workgroups
     assert fused(B=4, N=4, HV=16, H=16, K=256, V=128) == 0
+    assert fused(B=4, N=4, HV=16, H=16, K=128, V=128, gate_per_channel=1, chunk_size=32) == 2
+    assert fused(B=4, N=4, HV=16, H=16, K=128, V=128, gate_per_channel=1) == 0   # chunk 64
     P = ctypes.c_void_p
     args = [P(0x1000)] * 11
     p = problem()

@@ -101,6 +101,63 @@ def test_stage_intermediates(cfg):
     check("ht", f64(ht), rht, tol)
 
 
+# ------------------------------------------------------------------ per-channel fused scan + output
+
+PC_FUSED_CASES = [
+    # the per-channel workload's head dims (K = 128, V = 256), host-normalised q / k
+    dict(K=128, V=256, pc=True, l2=False, host_l2=True),
+    # in-kernel L2 norm, GVA
+    dict(K=64, V=64, pc=True, H=1, HV=4),
+    dict(K=32, V=128, pc=True),
+]
+
+
+@pytest.mark.parametrize("cfg", PC_FUSED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_per_channel_fused_forward_intermediates(cfg):
+    """Per-channel gate, bf16, chunk 32: the default forward runs K1 (which
+    also writes aqk), K2 (also the gated query pair qgs and the scan's kt /
+    dl) and the per-channel fused scan + output.  Each of those regions
+    against the oracle's per-chunk operands, h / v_new absent, o / ht against
+    the oracle, on a ragged dense batch with slow decay and h0."""
+    w, inp = mk(T=150, C=32, slow=True, scale=0.75, **cfg)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, use_qk_l2norm=inp["use_qk_l2norm"])
+    assert gdr.chunk_fwd_fused(p) == 2
+    o, ht, ws = gpu_fwd(inp)
+    ro, rht, it = oracle_fwd(inp, intermediates=True)
+    NT = int(it["off"][-1])
+    assert ws["h"] is None and ws["v_new"] is None
+    # aqk and the hi + lo query pair carry ~16 mantissa bits
+    check("aqk", f64(ws["aqk"][:NT]), it["QK"], 1e-4)
+    check("qgs", f64(ws["qgs"][:NT, :, 0]) + f64(ws["qgs"][:NT, :, 1]), it["QG"], 1e-4)
+    check("kt", f64(ws["kt"][:NT]), it["KT"], TOL["bf16"])
+    check("dl", f64(ws["dl"][:NT]), it["DL"], 1e-5)
+    check("Tm", f64(ws["Tm"][:NT]), it["T"], TOL["bf16"])
+    check("o", f64(o), ro, TOL["bf16"])
+    check("ht", f64(ht), rht, TOL["bf16"])
+    # the separate stages on the same inputs agree with it within the tolerance
+    o2, ht2, _ = gpu_fwd(inp, keep_states=True)
+    check("o (separate stages)", f64(o2), f64(o), TOL["bf16"])
+    check("ht (separate stages)", f64(ht2), f64(ht), TOL["bf16"])
+
+
+def test_per_channel_fused_forward_extreme_gate_span():
+    """Per-channel gates of -9 (about 144 of decay inside a 16-token block,
+    above K1's exponential-safety limit, so its diagonal blocks take the
+    per-element path for aqk as for A) with a few near-zero gates, on the
+    per-channel fused forward (bf16, chunk 32, ragged tail)."""
+    w, inp = mk(B=1, T=90, H=1, HV=2, K=64, V=64, C=32, pc=True)
+    inp["g"] = inp["g"] * 0.0 - 9.0
+    inp["g"][0, 1::3] = -0.01
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, use_qk_l2norm=True)
+    assert gdr.chunk_fwd_fused(p) == 2
+    o, ht, ws = gpu_fwd(inp)
+    ro, rht, it = oracle_fwd(inp, intermediates=True)
+    NT = int(it["off"][-1])
+    check("aqk", f64(ws["aqk"][:NT]), it["QK"], 1e-4)
+    check("o", f64(o), ro, TOL["bf16"])
+    check("ht", f64(ht), rht, TOL["bf16"])
+
+
 # ------------------------------------------------------------------ fused scan + output
 
 FUSED_CASES = [
@@ -226,7 +283,7 @@ for dtype in ("bf16", "fp32"):
                 if dtype == "fp32" and pc and K == 256 and C == 64:
                     continue
                 SWEEP.append(dict(dtype=dtype, C=C, K=K, V=V, pc=pc))
-                if not pc:
+                if not pc or (dtype == "bf16" and C == 32 and K <= 128):
                     # the separate scan and output stages too (the default is the
                     # fused stage wherever the shape has one)
                     SWEEP.append(dict(dtype=dtype, C=C, K=K, V=V, pc=pc, keep=True))
