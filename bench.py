@@ -67,12 +67,14 @@ def stage_bytes_per_token_head(w, T_seq, pc_fused=False):
         d = {
             "kkt_solve": r * K * e + gb + 4 + e * C,
             "wy": r * K * e + V * e + e * C + gb + 4 + e * K + 4 * V + kt_dl,
+            # fused K1 + K2 (chunk 32): k, v, g, beta -> Tm, w, u, kt, dl
+            "kkt_wy": r * K * e + V * e + gb + 4 + e * C + e * K + 4 * V + kt_dl,
             "fwd_h": e * K + 4 * V + kt_dl + e * V + e * K * V / C + 8 * K * V / T_seq,
             "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
         }
         if pc_fused:
-            d["kkt_solve"] += r * K * e + 4 * C      # + q read, aqk (fp32) written
-            d["wy"] += r * K * e + 2 * e * K         # + q read, the hi + lo query pair written
+            # + q read; aqk (fp32) and the hi + lo query pair written, Tm not
+            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - e * C
             # w, u, kt, dl, the query pair, aqk -> o, ht (h and v_new stay on chip)
             d["fwd_h_o"] = e * K + 4 * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
         return d
@@ -159,6 +161,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
         return {
             "kkt_solve": fwd["kkt_solve"],
             "wy": fwd["wy"],
+            "kkt_wy": fwd["kkt_wy"],
             "fwd_h": fwd["fwd_h"] - 4 * K * V / T_seq,
             # q, k, g, dO -> de_local, the gated rows kt, qg and the decay dl
             "bwd_intra": 2 * r * K * e + 4 * K + V * e + V * e + 2 * K * e + 4 * K / C,

@@ -319,13 +319,14 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
     the layout ``lay``, by default the one gdr_chunk_fwd uses for ``p``).  A
     region the layout gives no bytes has a None view: the compact layout of the
     scalar-gate fused stages has no Tm, h or v_new and keeps u in the input
-    dtype; the per-channel fused forward has no h or v_new but aqk and qgs."""
+    dtype; the per-channel fused forward has no Tm, h or v_new but aqk and qgs."""
     if lay is None:
         lay = fwd_layout(p)
     nt, C, HV, K, V = lay.nt_max, p.chunk_size, p.HV, p.K, p.V
-    compact = nt > 0 and lay.Tm == lay.w
+    no_tm = nt > 0 and lay.Tm == lay.w
     no_states = nt > 0 and lay.h == lay.v_new
     pc_fused = nt > 0 and lay.qgs > lay.aqk
+    compact = no_tm and not pc_fused       # the scalar-gate fused stages: u in the input dtype
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 
@@ -339,7 +340,7 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
         chunk_idx=view(lay.chunk_idx, (nt, 4), torch.int32, 4),
         chunk_off=view(lay.chunk_off, (p.N + 1,), torch.int32, 4),
         seq_order=view(lay.seq_order, (p.N,), torch.int32, 4),
-        Tm=None if compact else view(lay.Tm, (nt, HV, C, C), dt, es),
+        Tm=None if no_tm else view(lay.Tm, (nt, HV, C, C), dt, es),
         w=view(lay.w, (nt, HV, C, K), dt, es),
         # u as the separate WY stage writes it (fp32), and the same region as the
         # fused K1 + K2 stage writes it (input dtype)

@@ -141,8 +141,8 @@ gdr::Args make_args(const gdr_problem& p) {
 // pc_regions: with a per-channel gate, reserve the WY stage's gated keys and
 // decay for the warp-specialised scan (the backward keeps its own; the
 // segmented forward runs the other per-channel scan).  pc_fused: the
-// per-channel fused scan + output runs, so h and v_new get no bytes and the
-// aqk and gated-query regions it reads do.
+// per-channel fused K1 + K2 and fused scan + output run, so Tm, h and v_new
+// get no bytes and the aqk and gated-query regions do.
 gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_fused = false) {
   gdr_fwd_layout l;
   const int64_t nt = gdr::nt_max(p);
@@ -157,7 +157,7 @@ gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_f
   l.seq_order = off;
   off = round_up(off + (size_t)p.N * sizeof(int32_t));
   l.Tm = off;
-  off = round_up(off + (size_t)nt * HV * C * C * es);
+  off = round_up(off + (pc_fused ? 0 : (size_t)nt * HV * C * C * es));
   l.w = off;
   off = round_up(off + (size_t)nt * HV * C * K * es);
   l.u = off;   // fp32 from the separate WY stage, input dtype from the fused K1 + K2 stage
@@ -214,13 +214,13 @@ gdr_fwd_layout fused_layout_of(const gdr_problem& p) {
 }
 
 // Which fused forward gdr_chunk_fwd runs for the (padded) problem: 1 = fused
-// K1 + K2 and fused scan + output (scalar gate), 2 = separate K1 and K2 and
-// the per-channel fused scan + output, 0 = the separate stages.
+// K1 + K2 and fused scan + output (scalar gate), 2 = the per-channel fused
+// K1 + K2 and fused scan + output, 0 = the separate stages.
 int fused_kind(const gdr_problem& pp) {
   if (pp.keep_states) return 0;
   const Args a = make_args(pp);
   if (gdr::fwd_h_o_preferred(a)) return 1;
-  if (gdr::fwd_h_o_pc_preferred(a)) return 2;
+  if (gdr::fwd_h_o_pc_preferred(a) && gdr::kkt_wy_pc_supported(a)) return 2;
   return 0;
 }
 
@@ -345,6 +345,22 @@ PadLayout pad_layout(const gdr_problem& p, size_t base, bool bwd) {
   return l;
 }
 
+// K1 and K2 into Tm, w and u (fp32), and with a per-channel gate the scan's
+// kt / dl when a.kt / a.dl are set: one fused stage where the per-channel
+// shape has it, else the two stages.
+hipError_t kkt_and_wy(const Args& a, hipError_t e, hipStream_t s) {
+  if (a.per_channel && a.kt != nullptr && a.dl != nullptr && gdr::kkt_wy_pc_supported(a)) {
+    if (e == hipSuccess) e = gdr::launch_kkt_wy_pc(a, s);
+    timer_mark(e, "kkt_wy", s);
+    return e;
+  }
+  if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
+  timer_mark(e, "kkt_solve", s);
+  if (e == hipSuccess) e = gdr::launch_wy(a, s);
+  timer_mark(e, "wy", s);
+  return e;
+}
+
 // The forward's launch sequence for a problem with instantiated head dims;
 // the intermediates go to the workspace at the offsets of l.
 hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const void* v, const float* g,
@@ -377,19 +393,19 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   hipError_t e = hipSuccess;
   const int kind = fused_kind(p);
   if (kind == 2 && l.qgs > l.aqk) {
-    // per-channel gate: K1 also writes aqk and K2 the gated query pair, and
-    // the fused scan + output reads them (h and v_new stay on chip)
+    // per-channel gate: the fused K1 + K2 also writes aqk and the gated query
+    // pair, and the fused scan + output reads them (Tm, h and v_new stay on
+    // chip)
     a.u_f32 = 1;
+    a.Tm = nullptr;
     a.h = nullptr;
     a.v_new = nullptr;
     a.aqk = reinterpret_cast<float*>(ws + l.aqk);
     a.qgs = ws + l.qgs;
     e = gdr::launch_chunk_table(a, s);
     timer_mark(e, "chunk_table", s);
-    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-    timer_mark(e, "kkt_solve", s);
-    if (e == hipSuccess) e = gdr::launch_wy(a, s);
-    timer_mark(e, "wy", s);
+    if (e == hipSuccess) e = gdr::launch_kkt_wy_pc(a, s);
+    timer_mark(e, "kkt_wy", s);
     if (e == hipSuccess) e = gdr::launch_fwd_h_o_pc(a, s);
     timer_mark(e, "fwd_h_o", s);
   } else if (kind == 1) {
@@ -410,10 +426,7 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
     a.u_f32 = 1;   // the separate WY stage writes u in fp32
     e = gdr::launch_chunk_table(a, s);
     timer_mark(e, "chunk_table", s);
-    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-    timer_mark(e, "kkt_solve", s);
-    if (e == hipSuccess) e = gdr::launch_wy(a, s);
-    timer_mark(e, "wy", s);
+    e = kkt_and_wy(a, e, s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
     timer_mark(e, "fwd_h", s);
     if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
@@ -469,10 +482,7 @@ hipError_t bwd_run(const gdr_problem& p, const void* q, const void* k, const voi
     // recompute the forward's chunk tables, Tm, w, u, kscale, h and v_new
     e = gdr::launch_chunk_table(a, s);
     timer_mark(e, "chunk_table", s);
-    if (e == hipSuccess) e = gdr::launch_kkt_solve(a, s);
-    timer_mark(e, "kkt_solve", s);
-    if (e == hipSuccess) e = gdr::launch_wy(a, s);
-    timer_mark(e, "wy", s);
+    e = kkt_and_wy(a, e, s);
     if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
     timer_mark(e, "fwd_h", s);
   }

@@ -75,9 +75,10 @@ struct Args {
   float* dl;
   // forward with a per-channel gate and the fused scan + output: the chunk's
   // intra attention aqk[r][t] = scale sum_d q^_rd k^_td exp(G_rd - G_td) for
-  // t <= r (fp32 [NT][HV][C][C], zero above the diagonal and past L), written
-  // by K1, and its gated queries scale exp(G_t) q^_t as a bf16 hi + lo pair
-  // (qgs [NT][HV][2][C][K]: the hi tile, then the lo tile), written by K2
+  // t <= r (fp32 [NT][HV][C][C], zero above the diagonal and past L) and its
+  // gated queries scale exp(G_t) q^_t as a bf16 hi + lo pair (qgs
+  // [NT][HV][2][C][K]: the hi tile, then the lo tile), both written by the
+  // fused per-channel K1 + K2
   float* aqk;
   void* qgs;
 };
@@ -90,6 +91,10 @@ hipError_t launch_kkt_solve(const Args& a, hipStream_t s);
 hipError_t launch_wy(const Args& a, hipStream_t s);
 // K1 + K2 fused (scalar gate; w, u and kscale, no Tm)
 hipError_t launch_kkt_wy(const Args& a, hipStream_t s);
+// K1 + K2 fused, per-channel gate (bf16, chunk 32, K <= 128): w, u (fp32),
+// kt, dl, Tm when a.Tm is set, aqk and qgs when both are set
+bool kkt_wy_pc_supported(const Args& a);
+hipError_t launch_kkt_wy_pc(const Args& a, hipStream_t s);
 hipError_t launch_fwd_h(const Args& a, hipStream_t s);
 // whether launch_fwd_h takes h = v_new = NULL (then writes neither) and, with
 // them, u = NULL for u = 0: the scalar-gate warp-specialised scan
@@ -100,7 +105,7 @@ bool fwd_h_o_supported(const Args& a);
 bool fwd_h_o_preferred(const Args& a);   // the full forward's choice
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
-// per-channel gate: the fused scan + output on K2's gated keys / decay and the
+// per-channel gate: the fused scan + output on the gated keys / decay and the
 // aqk / qgs tiles (bf16, chunk 32, K <= 128); *_preferred is the full
 // forward's choice
 bool fwd_h_o_pc_supported(const Args& a);

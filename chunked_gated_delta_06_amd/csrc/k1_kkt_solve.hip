@@ -19,12 +19,6 @@
 //    (off-diagonal: m = last row of the column block).  Diagonal blocks use
 //    m = the block's middle row when the block's gate span keeps every factor
 //    below e^80; otherwise that block falls back to per-element exponentials.
-//  * Per-channel gate with a.aqk set (the fused per-channel scan + output
-//    runs next): the same blocks also give the chunk's intra attention
-//    aqk[r][t] = scale sum_d q^_rd k^_td exp(G_rd - G_td), t <= r, the q row
-//    sharing the k row's factor exp(G_r - G_m).  Both gated operands go in as
-//    bf16 hi + lo pairs, computed as the transposed product so that each lane
-//    holds four consecutive t of one row r (16-byte stores of fp32 aqk rows).
 //  * (I + A)^-1 in fp32: the 16x16 diagonal blocks by forward substitution
 //    (one lane per column, four blocks in parallel), then block forward
 //    substitution T_ib = -T_ii sum_m A_im T_mb on fp32 MFMA, in place in LDS.
@@ -57,9 +51,6 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   // block (rb, cb) base; element (i, k) of a block at base + 17 i + k
   auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * (16 * 17); };
   __shared__ float sG[C], sBeta[C], sRn[C];
-  // intra attention for the fused per-channel output (bf16 only)
-  constexpr bool AQK = PC && sizeof(T) == 2;
-  __shared__ float sRq[AQK ? C : 1];
 
   const int lane = threadIdx.x, r16 = lane & 15, g4 = lane >> 4;
   const int64_t NG = PC ? a.HV : a.H;    // workgroups per chunk
@@ -79,11 +70,6 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
 
   auto krow = [&](int row, int ks) -> Frag<T> {
     if (row < L) return ld8(kp + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
-    return frag_zero<T>();
-  };
-  const bool want_aqk = AQK && a.aqk != nullptr;
-  auto qrow = [&](int row, int ks) -> Frag<T> {
-    if (row < L) return ld8(static_cast<const T*>(a.q) + ((t0 + row) * H + h) * K + 32 * ks + 8 * g4);
     return frag_zero<T>();
   };
 
@@ -109,11 +95,9 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   f32x4 acc[NLB];
 #pragma unroll
   for (int i = 0; i < NLB; ++i) acc[i] = zero4();
-  float ss[NB], sq[AQK ? NB : 1];
+  float ss[NB];
 #pragma unroll
   for (int rb = 0; rb < NB; ++rb) ss[rb] = 0.f;
-#pragma unroll
-  for (int rb = 0; rb < (AQK ? NB : 1); ++rb) sq[rb] = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     Frag<T> f[NB];
@@ -127,13 +111,6 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
       const f32x8 x = f[rb].f32();
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss[rb] += x[e] * x[e];
-      if constexpr (AQK) {
-        if (want_aqk) {
-          const f32x8 y = qrow(16 * rb + r16, ks).f32();
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sq[rb] += y[e] * y[e];
-        }
-      }
     }
     if constexpr (!PC) {
 #pragma unroll
@@ -146,10 +123,6 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
   for (int rb = 0; rb < NB; ++rb) {
     const float tot = group4_sum(ss[rb]);
     if (g4 == 0) sRn[16 * rb + r16] = a.l2norm ? 1.f / sqrtf(tot + kL2Eps) : 1.f;
-    if constexpr (AQK) {
-      const float tq = group4_sum(sq[rb]);
-      if (g4 == 0) sRq[16 * rb + r16] = a.l2norm ? 1.f / sqrtf(tq + kL2Eps) : 1.f;
-    }
   }
 
   for (int64_t jj = 0; jj < jcount; ++jj) {
@@ -181,13 +154,12 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
         for (int t = 0; t < C; ++t) sGc[t * GP + d] = col[t];
       }
       lds_barrier();
-      // gated kk^T (and q k^T), block by block, with a reference row per block
-      f32x4 accq[AQK ? NLB : 1];
+      // gated kk^T, block by block, with a reference row per block
 #pragma unroll
       for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
         for (int cb = 0; cb <= rb; ++cb) {
-          f32x4 s = zero4(), sqk = zero4();
+          f32x4 s = zero4();
           bool direct = false;
           int m = 16 * cb + 15;
           if (cb == rb) {
@@ -203,26 +175,15 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
               f32x8 xa = krow(16 * rb + r16, ks).f32(), xb = krow(16 * cb + r16, ks).f32();
-              f32x8 xq = {};
-              if constexpr (AQK) {
-                if (want_aqk) xq = qrow(16 * rb + r16, ks).f32();
-              }
               const int ra = 16 * rb + r16, rbw = 16 * cb + r16;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int d = 32 * ks + 8 * g4 + e;
                 const float gm = sGc[m * GP + d];
-                const float fa = __expf(sGc[ra * GP + d] - gm);
-                xa[e] *= fa;
-                if constexpr (AQK) xq[e] *= fa;
+                xa[e] *= __expf(sGc[ra * GP + d] - gm);
                 xb[e] *= __expf(gm - sGc[rbw * GP + d]);
               }
               mma(s, Frag<T>::make(xa), Frag<T>::make(xb));
-              // q k^T transposed: element i of lane (r16, g4) is row 16 rb + r16,
-              // column 16 cb + 4 g4 + i
-              if constexpr (AQK) {
-                if (want_aqk) mma_split(sqk, SplitFrag<T>::make(xb), SplitFrag<T>::make(xq));
-              }
             }
           } else {
             // per-element exponentials for a block whose gate span is too wide
@@ -237,49 +198,8 @@ __global__ __launch_bounds__(64) void k1_kkt_solve(Args a) {
               }
               s[i] = sum;
             }
-            if constexpr (AQK) {
-              if (want_aqk) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int r = 16 * rb + r16, tc = 16 * cb + 4 * g4 + i;
-                  float sum = 0.f;
-                  if (tc <= r && r < L) {
-                    for (int d = 0; d < K; ++d)
-                      sum += to_float(static_cast<const T*>(a.q)[((t0 + r) * H + h) * K + d]) *
-                             to_float(kp[((t0 + tc) * H + h) * K + d]) * __expf(sGc[r * GP + d] - sGc[tc * GP + d]);
-                  }
-                  sqk[i] = sum;
-                }
-              }
-            }
           }
           acc[rb * (rb + 1) / 2 + cb] = s;
-          if constexpr (AQK) accq[rb * (rb + 1) / 2 + cb] = sqk;
-        }
-      }
-      // aqk rows: scale / (|q_r| |k_t|) on t <= r < L, zero elsewhere (blocks
-      // above the diagonal included)
-      if constexpr (AQK) {
-        if (want_aqk) {
-          float* dst = a.aqk + (c * HV + j) * (int64_t)(C * C);
-#pragma unroll
-          for (int rb = 0; rb < NB; ++rb) {
-            const int r = 16 * rb + r16;
-            const float fr = (r < L) ? a.scale * sRq[r] : 0.f;
-#pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-              f32x4 o4 = zero4();
-              if (cb <= rb) {
-                const f32x4 v4 = accq[rb * (rb + 1) / 2 + cb];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int tc = 16 * cb + 4 * g4 + i;
-                  o4[i] = tc <= r ? v4[i] * fr * sRn[tc] : 0.f;
-                }
-              }
-              *reinterpret_cast<f32x4*>(dst + r * C + 16 * cb + 4 * g4) = o4;
-            }
-          }
         }
       }
     }

@@ -23,10 +23,7 @@
 //    gate multiplies the key tile element-wise by exp(G_td) <= 1, and (when
 //    the caller gives a.kt / a.dl) the stage also writes the state scan's
 //    gated keys exp(G_L - G_t) k^_t and decay exp(G_L), so the scan does not
-//    form the chunk's gate cumsum in each of its workgroups; with a.qgs set
-//    (bf16, the fused per-channel scan + output runs next) it also writes the
-//    gated queries scale exp(G_t) q^_t as a bf16 hi + lo pair, reusing the
-//    keys' exponentials;
+//    form the chunk's gate cumsum in each of its workgroups;
 //  * blocks above the diagonal of Tm are skipped (Tm is lower triangular);
 //  * every global load of a chunk (keys, the first value pass, Tm rows, g,
 //    beta) is issued before the first wait, so a workgroup pays one memory
@@ -91,20 +88,6 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
     const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
     kr[i] = (idx < C * CPR && t < L) ? ld8(kp + ((t0 + t) * H + h) * K + d8) : frag_zero<T>();
   }
-  // gated queries for the fused per-channel output (bf16 only)
-  constexpr bool QG = PC && sizeof(T) == 2;
-  const bool want_qg = QG && a.qgs != nullptr;
-  Frag<T> qr[QG ? NKP : 1];
-  if constexpr (QG) {
-    if (want_qg) {
-#pragma unroll
-      for (int i = 0; i < NKP; ++i) {
-        const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
-        qr[i] = (idx < C * CPR && t < L) ? ld8(static_cast<const T*>(a.q) + ((t0 + t) * H + h) * K + d8)
-                                         : frag_zero<T>();
-      }
-    }
-  }
   fetch_v(0);
   // rows of Tm this lane feeds: row 16 rb + r16, tokens 32 ks + 8 g4 + e
   Frag<T> tf[NB][KSC];
@@ -143,7 +126,6 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
   // (and a.kt set) also the state scan's gated key rows exp(G_L - G_t) k^_t
   // (zero past L) and the decay exp(G_L), one float per feature
   T* __restrict__ ktp = (PC && a.kt != nullptr) ? static_cast<T*>(a.kt) + (c * HV + j) * (int64_t)(C * K) : nullptr;
-  T* __restrict__ qgp = want_qg ? static_cast<T*>(a.qgs) + (c * HV + j) * (int64_t)(2 * C * K) : nullptr;
 #pragma unroll
   for (int i = 0; i < NKP; ++i) {
     const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -152,16 +134,6 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
     sq = lanes_sum_t<CPR>(sq);
-    f32x8 y = {};
-    float sqq = 0.f;
-    if constexpr (QG) {
-      if (want_qg) {
-        y = qr[i].f32();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sqq += y[e] * y[e];
-        sqq = lanes_sum_t<CPR>(sqq);
-      }
-    }
     if (idx < C * CPR) {
       const float rn = a.l2norm ? 1.f / sqrtf(sq + kL2Eps) : 1.f;
       if (d8 == 0) sRn[t] = rn;
@@ -173,19 +145,9 @@ __global__ __launch_bounds__(256) void k2_wy(Args a) {
           for (int e = 0; e < 8; ++e) y[e] = x[e] * rn * __expf(sGc[(L - 1) * GP + d8 + e] - sGc[t * GP + d8 + e]);
           st8(ktp + t * K + d8, Frag<T>::make(y));
         }
-        f32x8 ex;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ex[e] = __expf(sGc[t * GP + d8 + e]);
-        x *= ex;
+        for (int e = 0; e < 8; ++e) x[e] *= __expf(sGc[t * GP + d8 + e]);
         f = Frag<T>::make(x);
-        if constexpr (QG) {
-          if (want_qg) {
-            const float fq = a.scale * (a.l2norm ? 1.f / sqrtf(sqq + kL2Eps) : 1.f);
-            const SplitFrag<T> sp = SplitFrag<T>::make(y * ex * fq);
-            st8(qgp + t * K + d8, sp.hi);
-            st8(qgp + (C + t) * K + d8, sp.lo);
-          }
-        }
       }
       st8(&sK[t * KP + d8], f);
     }

@@ -397,8 +397,9 @@ struct K3S {
 // PC: per-channel gate, with the chunk's gated keys exp(G_L - G_t) k^_t and
 // decay exp(G_L) from the WY stage in place of the raw keys and the token
 // factors: S <- diag(exp(G_L)) S + Kt^T e.  With output waves as well (bf16),
-// o = (scale exp(G) q^) h + aqk e from K2's gated query pair and K1's aqk, so
-// the output waves apply no gate factor themselves.
+// o = (scale exp(G) q^) h + aqk e from the gated query pair and aqk of the
+// fused per-channel K1 + K2, so the output waves apply no gate factor
+// themselves.
 template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T,
           bool PC = false>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
@@ -1126,7 +1127,7 @@ hipError_t launch_fused_k(const Args& a, hipStream_t s) {
 
 // ---- fused state scan + output, per-channel gate (bf16, chunk 32): the
 // per-channel scan's compute and loader waves (u in fp32) plus 2 output waves
-// on K1's aqk and K2's gated query pair.  64 value columns (4 compute waves)
+// on the aqk and gated query pair of the fused per-channel K1 + K2.  64 value columns (4 compute waves)
 // per workgroup when that grid still gives every compute unit a workgroup,
 // else 32.
 template <typename T, int C, int K>

@@ -96,10 +96,11 @@ typedef struct {
  * gdr_chunk_fwd keeps in its workspace; NT_max = B * ceil(T / C) for a dense
  * batch and floor(T / C) + N for a varlen batch.  When the forward takes the
  * fused stages (keep_states = 0 and gdr_chunk_fwd_fused(p) != 0), the layout is
- * the compact one those stages use: h and v_new get no bytes (their offsets
- * equal the next region's); with a scalar gate (kind 1) neither does Tm, and u
- * is in `dtype`; with a per-channel gate (kind 2) the aqk and qgs regions
- * below get bytes.  Regions a layout does not use have no bytes.
+ * the compact one those stages use: Tm, h and v_new get no bytes (their
+ * offsets equal the next region's); with a scalar gate (kind 1) u is in
+ * `dtype`; with a per-channel gate (kind 2) u stays fp32 and the kt, dl, aqk
+ * and qgs regions below get bytes.  Regions a layout does not use have no
+ * bytes.
  *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
  *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
  *   seq_order  int32 [N]           varlen batches of at most 1024 sequences: the sequences
@@ -121,13 +122,13 @@ typedef struct {
  *                                         WY stage for its state scan: exp(G_L - G_t) k^_t
  *                                         per row t (zero past L); no bytes otherwise
  *   dl         f32   [NT_max][HV][K]      per-channel gate: exp(G_L) per feature
- *   aqk        f32   [NT_max][HV][C][C]   per-channel fused forward only, written by K1:
+ *   aqk        f32   [NT_max][HV][C][C]   per-channel fused forward only (fused K1 + K2):
  *                                         the chunk's intra attention, row r, column t:
  *                                         scale sum_d q^_rd k^_td exp(G_rd - G_td) for
  *                                         t <= r (the Q K^T o M term of the chunk form's
  *                                         output, coverage-matrix page, section 2), zero
  *                                         above the diagonal and in rows past L
- *   qgs        dtype [NT_max][HV][2][C][K] per-channel fused forward only, written by K2:
+ *   qgs        dtype [NT_max][HV][2][C][K] per-channel fused forward only (fused K1 + K2):
  *                                         the gated queries scale exp(G_t) q^_t as a bf16
  *                                         hi tile then a lo tile (hi + lo = the fp32 value
  *                                         to about 16 mantissa bits)
@@ -194,10 +195,10 @@ gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout
  *    the one fused stage gdr_fwd_kkt_wy and K3 and K4 as the one fused stage
  *    gdr_fwd_h_o, and the Tm, h and v_new regions are left untouched;
  *    gdr_chunk_fwd_fused(p) returns 1 exactly then;
- *  - per-channel gate, bf16, chunk 32, K <= 128: K1 also writes aqk, K2 also
- *    writes qgs (layout above), and K3 and K4 run as one fused scan + output
- *    stage that reads them, so h and v_new are not written;
- *    gdr_chunk_fwd_fused(p) returns 2 exactly then (0 otherwise).
+ *  - per-channel gate, bf16, chunk 32, K <= 128: K1 and K2 run as one fused
+ *    stage that also writes kt, dl, aqk and qgs (layout above), and K3 and K4
+ *    as one fused scan + output stage that reads them, so Tm, h and v_new are
+ *    not written; gdr_chunk_fwd_fused(p) returns 2 exactly then (0 otherwise).
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch

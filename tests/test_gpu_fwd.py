@@ -114,24 +114,25 @@ PC_FUSED_CASES = [
 
 @pytest.mark.parametrize("cfg", PC_FUSED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_per_channel_fused_forward_intermediates(cfg):
-    """Per-channel gate, bf16, chunk 32: the default forward runs K1 (which
-    also writes aqk), K2 (also the gated query pair qgs and the scan's kt /
-    dl) and the per-channel fused scan + output.  Each of those regions
-    against the oracle's per-chunk operands, h / v_new absent, o / ht against
-    the oracle, on a ragged dense batch with slow decay and h0."""
+    """Per-channel gate, bf16, chunk 32: the default forward runs the fused
+    K1 + K2 (w, u, the scan's kt / dl, aqk and the gated query pair qgs) and
+    the per-channel fused scan + output.  Each of those regions against the
+    oracle's per-chunk operands, Tm / h / v_new absent, o / ht against the
+    oracle, on a ragged dense batch with slow decay and h0."""
     w, inp = mk(T=150, C=32, slow=True, scale=0.75, **cfg)
     p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, use_qk_l2norm=inp["use_qk_l2norm"])
     assert gdr.chunk_fwd_fused(p) == 2
     o, ht, ws = gpu_fwd(inp)
     ro, rht, it = oracle_fwd(inp, intermediates=True)
     NT = int(it["off"][-1])
-    assert ws["h"] is None and ws["v_new"] is None
+    assert ws["Tm"] is None and ws["h"] is None and ws["v_new"] is None
     # aqk and the hi + lo query pair carry ~16 mantissa bits
     check("aqk", f64(ws["aqk"][:NT]), it["QK"], 1e-4)
     check("qgs", f64(ws["qgs"][:NT, :, 0]) + f64(ws["qgs"][:NT, :, 1]), it["QG"], 1e-4)
     check("kt", f64(ws["kt"][:NT]), it["KT"], TOL["bf16"])
     check("dl", f64(ws["dl"][:NT]), it["DL"], 1e-5)
-    check("Tm", f64(ws["Tm"][:NT]), it["T"], TOL["bf16"])
+    check("w", f64(ws["w"][:NT]), it["W"], TOL["bf16"])
+    check("u", f64(ws["u"][:NT]).transpose(0, 1, 3, 2), it["U"], TOL["bf16"])
     check("o", f64(o), ro, TOL["bf16"])
     check("ht", f64(ht), rht, TOL["bf16"])
     # the separate stages on the same inputs agree with it within the tolerance
