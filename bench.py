@@ -49,17 +49,20 @@ PEAK_MFMA_FLOPS = {"bf16": 2.5e15, "fp32": 157.3e12}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def stage_bytes_per_token_head(w, T_seq, pc_fused=False):
+def stage_bytes_per_token_head(w, T_seq, pc_fused=False, keep=False):
     """Algorithmic HBM bytes per (token, value head) of each forward stage:
     every tensor counted once when written and once per reading stage, at the
     library's storage dtypes (q/k/v/o and the intermediates in the input dtype,
     except the separate WY stage's u, which is fp32; g and beta in fp32, h0/ht
-    fp32).  ``pc_fused``: the per-channel forward whose K1 also writes aqk,
-    K2 the gated query pair, read by the per-channel fused scan + output."""
+    fp32).  ``pc_fused``: the per-channel fused forward (its fused K1 + K2 also
+    writes aqk and the gated query pair, read by the fused scan + output).
+    ``keep``: a forward that keeps its states (its fused stages also write Tm,
+    u in fp32, h and v_new)."""
     e = 2 if w.dtype == "bf16" else 4
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
     gb = 4 * K if w.per_channel_gate else 4
+    states = e * K * V / C + e * V          # h (per chunk) and v_new
     if w.per_channel_gate and K <= 128:
         # the WY stage also writes the scan's gated keys kt and decay dl, which
         # the scan reads in place of k and g
@@ -72,25 +75,29 @@ def stage_bytes_per_token_head(w, T_seq, pc_fused=False):
             "fwd_h": e * K + 4 * V + kt_dl + e * V + e * K * V / C + 8 * K * V / T_seq,
             "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
         }
-        if pc_fused:
-            # + q read; aqk (fp32) and the hi + lo query pair written, Tm not
-            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - e * C
-            # w, u, kt, dl, the query pair, aqk -> o, ht (h and v_new stay on chip)
-            d["fwd_h_o"] = e * K + 4 * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
+        if pc_fused or keep:
+            # + q read; aqk (fp32) and the hi + lo query pair written (Tm only
+            # when the states are kept)
+            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - (0 if keep else e * C)
+            # w, u, kt, dl, the query pair, aqk -> o, ht (+ h, v_new when kept)
+            d["fwd_h_o"] = (e * K + 4 * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
+                            + (states if keep else 0))
         return d
     # K1's per-chunk token factors (scalar gate): 3C + 4 floats per chunk and
     # value head, of which the separate scan reads the first C + 4
     kf_row = 0 if w.per_channel_gate else 4 * (3 * C + 4) / C
     kf_scan = gb if w.per_channel_gate else 4 * (C + 4) / C
+    ue = 4 if keep else e                   # u: fp32 when the states are kept
     return {
         "kkt_solve": r * K * e + gb + 4 + e * C + kf_row,
         "wy": r * K * e + V * e + e * C + gb + 4 + e * K + 4 * V,
         "fwd_h": e * K + 4 * V + r * K * e + kf_scan + e * V + e * K * V / C + 8 * K * V / T_seq,
         "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
-        # fused K1 + K2: k, v, g, beta -> w, u, token factors (Tm stays on chip)
-        "kkt_wy": r * K * e + V * e + gb + 4 + e * K + e * V + kf_row,
-        # fused scan + output: w, u, k, q, token factors -> o, ht (h and v_new stay on chip)
-        "fwd_h_o": e * K + e * V + r * K * e + r * K * e + kf_row + e * V + 8 * K * V / T_seq,
+        # fused K1 + K2: k, v, g, beta -> w, u, token factors (+ Tm when kept)
+        "kkt_wy": r * K * e + V * e + gb + 4 + e * K + ue * V + kf_row + (e * C if keep else 0),
+        # fused scan + output: w, u, k, q, token factors -> o, ht (+ h, v_new when kept)
+        "fwd_h_o": e * K + ue * V + r * K * e + r * K * e + kf_row + e * V + 8 * K * V / T_seq
+                   + (states if keep else 0),
     }
 
 
@@ -156,7 +163,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
     e = 2 if w.dtype == "bf16" else 4
     r = w.H / w.HV
     K, V, C = w.K, w.V, w.chunk_size
-    fwd = stage_bytes_per_token_head(w, T_seq)
+    fwd = stage_bytes_per_token_head(w, T_seq, keep=True)
     if w.per_channel_gate:
         return {
             "kkt_solve": fwd["kkt_solve"],
@@ -173,6 +180,7 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
     return {
         "kkt_solve": fwd["kkt_solve"],
         "wy": fwd["wy"],
+        "kkt_wy": fwd["kkt_wy"],
         "fwd_h": fwd["fwd_h"] - 4 * K * V / T_seq,
         # q, k, g, dO -> de_local, qscale
         "bwd_intra": 2 * r * K * e + 4 + V * e + V * e + 4,
@@ -184,11 +192,13 @@ def bwd_stage_bytes_per_token_head(w, T_seq):
 
 
 def kernel_source_hash(stage):
-    fname = {"kkt_solve": "k1_kkt_solve.hip", "wy": "k2_wy.hip", "fwd_h": "k3_fwd_h.hip",
-             "fwd_o": "k4_fwd_o.hip", "fwd_h_o": "k3_fwd_h.hip", "kkt_wy": "k12_kkt_wy.hip", "bwd_intra": "b1_bwd_intra.hip", "bwd_dh": "b2_bwd_dh.hip",
-             "bwd_dqkvg": "b3_bwd_dqkvg.hip", "recurrent": "k5_recurrent.hip"}[stage]
+    fname = {"kkt_solve": ("k1_kkt_solve.hip",), "wy": ("k2_wy.hip",), "fwd_h": ("k3_fwd_h.hip",),
+             "fwd_o": ("k4_fwd_o.hip",), "fwd_h_o": ("k3_fwd_h.hip",),
+             "kkt_wy": ("k12_kkt_wy.hip", "k12pc_kkt_wy.hip"), "bwd_intra": ("b1_bwd_intra.hip",),
+             "bwd_dh": ("b2_bwd_dh.hip",), "bwd_dqkvg": ("b3_bwd_dqkvg.hip", "b3pc_bwd_dqkvg.hip"),
+             "recurrent": ("k5_recurrent.hip",)}[stage]
     h = hashlib.sha256()
-    for f in (fname, "gdr_device.h"):
+    for f in (*fname, "gdr_device.h"):
         with open(os.path.join(ROOT, "chunked_gated_delta_06_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -526,7 +536,8 @@ def measure(gdr, w, steps, warmup, breakdown, label):
     T_seq = inp["B"] * inp["T"] / inp["N"]
     units = tokens * w.HV
     pc_fused = not backward and gdr.chunk_fwd_fused(p) == 2
-    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq, pc_fused).items() if k in fwd_ms}
+    per_unit = {k: v for k, v in stage_bytes_per_token_head(w, T_seq, pc_fused, keep=backward).items()
+                if k in fwd_ms}
     rec = {"value": value, "ms_per_step": ms_per_step, "tokens": tokens,
            "timing": {**timing, "what": "HIP events around each whole call on the launch stream; "
                                         "ms_per_step = median_ms; wall_ms = wall clock per step"},

@@ -169,14 +169,18 @@ gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_f
   l.kscale = off;
   off = round_up(off + (p.gate_per_channel ? 0 : (size_t)nt * HV * gdr::kscale_pitch(C) * sizeof(float)));
   const bool pcs = pc_regions && p.gate_per_channel && gdr::fwd_pc_scan_fits(p.dtype, (int)C, (int)K);
+  // the fused per-channel K1 + K2 and scan + output (the kept-states forward
+  // runs them too, storing h and v_new as well)
+  const Args pa = make_args(p);
+  const bool pco = pc_fused || (pcs && gdr::kkt_wy_pc_supported(pa) && gdr::fwd_h_o_pc_supported(pa));
   l.kt = off;
   off = round_up(off + (pcs || pc_fused ? (size_t)nt * HV * C * K * es : 0));
   l.dl = off;
   off = round_up(off + (pcs || pc_fused ? (size_t)nt * HV * K * sizeof(float) : 0));
   l.aqk = off;
-  off = round_up(off + (pc_fused ? (size_t)nt * HV * C * C * sizeof(float) : 0));
+  off = round_up(off + (pco ? (size_t)nt * HV * C * C * sizeof(float) : 0));
   l.qgs = off;
-  off = round_up(off + (pc_fused ? (size_t)nt * HV * 2 * C * K * es : 0));
+  off = round_up(off + (pco ? (size_t)nt * HV * 2 * C * K * es : 0));
   l.total = off;
   return l;
 }
@@ -346,9 +350,16 @@ PadLayout pad_layout(const gdr_problem& p, size_t base, bool bwd) {
 }
 
 // K1 and K2 into Tm, w and u (fp32), and with a per-channel gate the scan's
-// kt / dl when a.kt / a.dl are set: one fused stage where the per-channel
-// shape has it, else the two stages.
+// kt / dl when a.kt / a.dl are set: one fused stage (the scalar gate's
+// kept-states fused K1 + K2, or the per-channel one where the shape has it),
+// else the two stages.  The kept-states forward and the backward's recompute
+// both come here, so they produce the same Tm, w and u.
 hipError_t kkt_and_wy(const Args& a, hipError_t e, hipStream_t s) {
+  if (!a.per_channel && a.u_f32 && !a.gla) {
+    if (e == hipSuccess) e = gdr::launch_kkt_wy(a, s);
+    timer_mark(e, "kkt_wy", s);
+    return e;
+  }
   if (a.per_channel && a.kt != nullptr && a.dl != nullptr && gdr::kkt_wy_pc_supported(a)) {
     if (e == hipSuccess) e = gdr::launch_kkt_wy_pc(a, s);
     timer_mark(e, "kkt_wy", s);
@@ -423,14 +434,32 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
     if (e == hipSuccess) e = gdr::launch_fwd_h_o(a, s);
     timer_mark(e, "fwd_h_o", s);
   } else {
-    a.u_f32 = 1;   // the separate WY stage writes u in fp32
+    a.u_f32 = 1;   // u in fp32 (what the backward reads)
     e = gdr::launch_chunk_table(a, s);
     timer_mark(e, "chunk_table", s);
-    e = kkt_and_wy(a, e, s);
-    if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
-    timer_mark(e, "fwd_h", s);
-    if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
-    timer_mark(e, "fwd_o", s);
+    if (p.keep_states && !p.gate_per_channel && gdr::fwd_h_o_keep_supported(a)) {
+      // kept states, scalar gate: the fused K1 + K2 writing Tm and an fp32 u,
+      // and the fused scan + output storing h and v_new as well
+      e = kkt_and_wy(a, e, s);
+      if (e == hipSuccess) e = gdr::launch_fwd_h_o_keep(a, s);
+      timer_mark(e, "fwd_h_o", s);
+    } else if (p.keep_states && l.qgs > l.aqk && a.kt != nullptr && gdr::kkt_wy_pc_supported(a) &&
+               gdr::fwd_h_o_pc_supported(a)) {
+      // kept states, per-channel gate: the fused K1 + K2 writing Tm and the
+      // output's operands, and the fused scan + output storing h and v_new
+      a.aqk = reinterpret_cast<float*>(ws + l.aqk);
+      a.qgs = ws + l.qgs;
+      if (e == hipSuccess) e = gdr::launch_kkt_wy_pc(a, s);
+      timer_mark(e, "kkt_wy", s);
+      if (e == hipSuccess) e = gdr::launch_fwd_h_o_pc(a, s);
+      timer_mark(e, "fwd_h_o", s);
+    } else {
+      e = kkt_and_wy(a, e, s);
+      if (e == hipSuccess) e = gdr::launch_fwd_h(a, s);
+      timer_mark(e, "fwd_h", s);
+      if (e == hipSuccess) e = gdr::launch_fwd_o(a, s);
+      timer_mark(e, "fwd_o", s);
+    }
   }
   return e;
 }

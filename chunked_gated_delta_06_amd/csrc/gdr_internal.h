@@ -89,7 +89,8 @@ constexpr int64_t kMaxOrdered = 1024;
 hipError_t launch_chunk_table(const Args& a, hipStream_t s);
 hipError_t launch_kkt_solve(const Args& a, hipStream_t s);
 hipError_t launch_wy(const Args& a, hipStream_t s);
-// K1 + K2 fused (scalar gate; w, u and kscale, no Tm)
+// K1 + K2 fused (scalar gate): w, u and kscale, no Tm; with a.u_f32 set (kept
+// states) also Tm, and u in fp32 as the separate WY stage writes it
 hipError_t launch_kkt_wy(const Args& a, hipStream_t s);
 // K1 + K2 fused, per-channel gate (bf16, chunk 32, K <= 128): w, u (fp32),
 // kt, dl, Tm when a.Tm is set, aqk and qgs when both are set
@@ -104,10 +105,14 @@ bool fwd_h_states_optional(const Args& a);
 bool fwd_h_o_supported(const Args& a);
 bool fwd_h_o_preferred(const Args& a);   // the full forward's choice
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s);
+// the fused scan + output of a kept-states forward (scalar gate): u in fp32 from
+// the kept-states fused K1 + K2, h and v_new written as the separate scan does
+bool fwd_h_o_keep_supported(const Args& a);
+hipError_t launch_fwd_h_o_keep(const Args& a, hipStream_t s);
 hipError_t launch_fwd_o(const Args& a, hipStream_t s);
 // per-channel gate: the fused scan + output on the gated keys / decay and the
-// aqk / qgs tiles (bf16, chunk 32, K <= 128); *_preferred is the full
-// forward's choice
+// aqk / qgs tiles (bf16, chunk 32, K <= 128), also storing h and v_new when
+// both are set; *_preferred is the full forward's choice
 bool fwd_h_o_pc_supported(const Args& a);
 bool fwd_h_o_pc_preferred(const Args& a);
 hipError_t launch_fwd_h_o_pc(const Args& a, hipStream_t s);

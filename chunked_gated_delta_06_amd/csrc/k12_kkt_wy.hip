@@ -9,8 +9,10 @@
 // the WY construction of the DeltaNet chunk form P^r = I - sum_i k^i w^i^T on
 // the coverage-matrix page ("FLA operator-kernel correctness testing and
 // coverage matrix", section 2) with the gate folded in.  Same results as the
-// K1 and K2 stages, except that Tm is not written (the forward does not need
-// it; the backward runs the separate stages, whose Tm it reads).  For simple
+// K1 and K2 stages up to rounding (Tm feeds w and u in fp32 here, not through
+// its bf16 copy).  The fused forward's variant writes neither Tm nor a wide u;
+// the kept-states variant (KEEP) writes Tm for the backward and u in fp32, its
+// operand Tm diag(beta) as a hi + lo pair, as the separate WY stage does.  For simple
 // GLA (no delta correction) it yields Tm = I, w = 0 and u = v, so the same scan
 // and output stages evaluate S_t = exp(g_t) S_{t-1} + k_t v_t^T.
 //
@@ -31,6 +33,8 @@
 //    before the first value pass is staged, so with bf16 and chunk 64 a
 //    workgroup holds 35 KB of LDS and 128 registers per lane, and four
 //    workgroups share a CU (a dense batch's chunks run in whole rounds).
+#include <type_traits>
+
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -38,8 +42,9 @@ namespace gdr {
 
 namespace {
 
-template <typename T, int C, int K>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a) {
+template <typename T, int C, int K, bool KEEP>
+__global__ __launch_bounds__(256, sizeof(T) == 2 && !KEEP ? 4 : 1) void k12_kkt_wy(Args a) {
+  using UT = typename std::conditional<KEEP, float, T>::type;   // u's storage type
   constexpr int NW = 4;
   constexpr int NT = 256;
   constexpr int NB = C / 16;                        // 16-row blocks per chunk
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
   const T* __restrict__ kp = static_cast<const T*>(a.k);
   const T* __restrict__ vp = static_cast<const T*>(a.v);
   T* __restrict__ wp = static_cast<T*>(a.w) + (c * HV + j) * (int64_t)(C * K);
-  T* __restrict__ up = static_cast<T*>(a.u) + (c * HV + j) * (int64_t)C * V;
+  UT* __restrict__ up = static_cast<UT*>(a.u) + (c * HV + j) * (int64_t)C * V;
 
   // ---- every global load of the chunk up front: key rows, the first value
   //      pass, g and beta
@@ -243,6 +248,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
     lds_barrier();
   }
 
+  // ---- Tm itself (kept-states variant; rows / cols past L and the upper
+  //      triangle zero)
+  if constexpr (KEEP) {
+    T* dst = static_cast<T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
+    for (int idx = tid; idx < C * C / 8; idx += NT) {
+      const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cc = c8 + e;
+        x[e] = (r < L && cc <= r) ? sM[blk(r >> 4, cc >> 4) + (r & 15) * MP + (cc & 15)] : 0.f;
+      }
+      st8(dst + r * C + c8, Frag<T>::make(x));
+    }
+  }
+
   // ---- rows of Tm this lane feeds (fp32, from LDS): row 16 rb + r16, tokens
   //      32 ks + 8 g4 + e; blocks above the diagonal are zero
   f32x8 tf[NB][KSC];
@@ -324,7 +345,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
 #pragma unroll
           for (int e = 0; e < 8; ++e) sc[e] = sB[32 * ks + 8 * g4 + e];
           const Frag<T> vbf = lds_tr_frag(sV, VP, 32 * ks + 8 * g4, 32 * ks + 8 * g4 + 4, 16 * vb, lane);
-          mma(acc[rb], Frag<T>::make(tf[rb][ks] * sc), vbf);
+          if constexpr (KEEP) {
+            mma_split(acc[rb], SplitFrag<T>::make(tf[rb][ks] * sc), vbf);
+          } else {
+            mma(acc[rb], Frag<T>::make(tf[rb][ks] * sc), vbf);
+          }
         }
       }
       // token blocks paired into 16-byte stores of the transposed u rows
@@ -337,7 +362,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 1) void k12_kkt_wy(Args a
 
 template <typename T, int C, int K>
 hipError_t launch_t(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k12_kkt_wy<T, C, K>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
+  if (a.u_f32)
+    hipLaunchKernelGGL((k12_kkt_wy<T, C, K, true>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k12_kkt_wy<T, C, K, false>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

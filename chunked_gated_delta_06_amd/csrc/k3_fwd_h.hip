@@ -391,7 +391,11 @@ struct K3S {
 };
 
 // KEEP = false: a scan that only needs the end states (the segment hand-off's
-// pre-process) writes neither h nor v_new.  ZU: u is zero (the transition
+// pre-process), or the fused scan + output of a forward that keeps no states,
+// writes neither h nor v_new.  With output waves and KEEP, the staged h / e
+// are stored one step later while the output waves read them: by the loaders
+// (scalar gate) or by the output waves themselves (per-channel gate, whose
+// output work is light and whose loaders carry the larger payload).  ZU: u is zero (the transition
 // scan), so it is neither read nor staged.  UT: u's storage type (fp32 from
 // the separate WY stage, the input dtype from the fused K1 + K2 stage).
 // PC: per-channel gate, with the chunk's gated keys exp(G_L - G_t) k^_t and
@@ -593,25 +597,25 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       for (int s0 = 0; s0 < nc; s0 += 3) {
         stage(R1, (s0 + 1) & 1);
         fetch(R1, cl(c_begin + s0 + 4));
-        if constexpr (STG && !OUT && KEEP) {
+        if constexpr (STG && KEEP && !(OUT && PC)) {
           if (s0 > 0) drain(s0 - 1);
         }
         lds_barrier();
         stage(R2, (s0 + 2) & 1);
         fetch(R2, cl(c_begin + s0 + 5));
-        if constexpr (STG && !OUT && KEEP) {
+        if constexpr (STG && KEEP && !(OUT && PC)) {
           if (s0 < nc) drain(s0);
         }
         lds_barrier();
         stage(R0, (s0 + 3) & 1);
         fetch(R0, cl(c_begin + s0 + 6));
-        if constexpr (STG && !OUT && KEEP) {
+        if constexpr (STG && KEEP && !(OUT && PC)) {
           if (s0 + 1 < nc) drain(s0 + 1);
         }
         lds_barrier();
       }
       // the last step's output when the loop ended right after it
-      if constexpr (STG && !OUT && KEEP) {
+      if constexpr (STG && KEEP && !(OUT && PC)) {
         if (nc % 3 == 0) drain(nc - 1);
       }
     }
@@ -771,6 +775,11 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         const int L = chunk_L(x);
         const T* hsb = sm.hs[x & 1];
         const T* esb = sm.es[x & 1];
+        // kept states with a per-channel gate: output wave 0 stores the staged
+        // h^T rows and wave 1 the e^T rows as it reads them (the loaders'
+        // registers have no room for the stores there)
+        constexpr bool KEEP_H = PC && KEEP && OW == 0, KEEP_E = PC && KEEP && OW == 1;
+        const int64_t cx = c_begin + x;
         f32x4 O[TPW][NVB];
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
@@ -778,6 +787,20 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) hf[ks] = ld8(&hsb[(16 * vb + r16) * HSP + 32 * ks + 8 * g4]);
           const T* erow = &esb[(16 * vb + r16) * VSP];
+          if constexpr (KEEP_H) {
+            T* hrow = hbase + ((cx * HV + j) * V + vw + 16 * vb + r16) * (int64_t)K;
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) st8(hrow + 32 * ks + 8 * g4, hf[ks]);
+          }
+          if constexpr (KEEP_E) {
+            T* vrow = vnbase + ((cx * HV + j) * V + vw + 16 * vb + r16) * (int64_t)C;
+#pragma unroll
+            for (int kt = 0; kt < KSC; ++kt) {
+              using V4 = typename Vec<T>::v4;
+              *reinterpret_cast<V4*>(vrow + 32 * kt + 4 * g4) = ld4raw(erow + 32 * kt + 4 * g4);
+              *reinterpret_cast<V4*>(vrow + 32 * kt + 16 + 4 * g4) = ld4raw(erow + 32 * kt + 16 + 4 * g4);
+            }
+          }
 #pragma unroll
           for (int m = 0; m < TPW; ++m) {
             f32x4 acc = zero4();
@@ -905,7 +928,8 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       for (int m = 0; m < NE / 2; ++m) st_pair(vnp + (r16 * C + 32 * m), E[2 * m], E[2 * m + 1], lane);
     }
     // S <- exp(G_L) S + k^T diag(exp(G_L - G_t) / |k_t|) e: e as a hi + lo
-    // pair except in the scalar-gate fused scan + output stage
+    // pair except in the scalar-gate fused scan + output stage that keeps no
+    // states
     if constexpr (PC) {
       // row d of S decays by exp(G_L,d)
 #pragma unroll
@@ -914,7 +938,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
       for (int mb = 0; mb < NS; ++mb) S[mb] *= gl;
     }
-    if constexpr (OUT && !PC) {
+    if constexpr (OUT && !PC && !KEEP) {
       Frag<T> Ef[KSC];
 #pragma unroll
       for (int kt = 0; kt < KSC; ++kt) Ef[kt] = frag_from_halves<T>(E[2 * kt] * sc[2 * kt], E[2 * kt + 1] * sc[2 * kt + 1]);
@@ -1087,15 +1111,25 @@ constexpr bool fused_ok() {
   return K3S<T, C, K, 2, 4, 2>::fits && K3S<T, C, K, 2, 4, 2>::fits_out && K3S<T, C, K, 1, 4, 2>::fits_out &&
          K <= 128;
 }
-
+// the kept-states variant: u in fp32 from the kept-states fused K1 + K2, e as
+// a hi + lo pair in the state update, h and v_new stored
 template <typename T, int C, int K>
+constexpr bool fused_keep_ok() {
+  return K <= 128 && K3S<T, C, K, 2, 4, 2, float>::fits_out && K3S<T, C, K, 1, 4, 2, float>::fits_out;
+}
+
+template <typename T, int C, int K, bool KEEP>
 hipError_t launch_fused_t(const Args& a, hipStream_t s) {
-  if constexpr (fused_ok<T, C, K>()) {
+  using UT = typename std::conditional<KEEP, float, T>::type;
+  constexpr bool ok = KEEP ? fused_keep_ok<T, C, K>() : fused_ok<T, C, K>();
+  if constexpr (ok) {
     const int64_t nblk32 = a.N * a.HV * (a.V / 32);
     if (nblk32 < kNumCUs) {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 1, 4, 2>), dim3((unsigned)(2 * nblk32)), dim3(64 * 7), 0, s, a);
+      hipLaunchKernelGGL((k3_scan<T, C, K, 1, 4, 2, KEEP, false, UT>), dim3((unsigned)(2 * nblk32)), dim3(64 * 7),
+                         0, s, a);
     } else {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 2, 4, 2>), dim3((unsigned)nblk32), dim3(64 * 8), 0, s, a);
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, 4, 2, KEEP, false, UT>), dim3((unsigned)nblk32), dim3(64 * 8), 0, s,
+                         a);
     }
     return hipGetLastError();
   } else {
@@ -1103,24 +1137,24 @@ hipError_t launch_fused_t(const Args& a, hipStream_t s) {
   }
 }
 
-template <typename T, int C>
+template <typename T, int C, bool KEEP>
 bool fused_ok_k(int64_t K) {
   switch (K) {
-    case 32: return fused_ok<T, C, 32>();
-    case 64: return fused_ok<T, C, 64>();
-    case 128: return fused_ok<T, C, 128>();
-    case 256: return fused_ok<T, C, 256>();
+    case 32: return KEEP ? fused_keep_ok<T, C, 32>() : fused_ok<T, C, 32>();
+    case 64: return KEEP ? fused_keep_ok<T, C, 64>() : fused_ok<T, C, 64>();
+    case 128: return KEEP ? fused_keep_ok<T, C, 128>() : fused_ok<T, C, 128>();
+    case 256: return KEEP ? fused_keep_ok<T, C, 256>() : fused_ok<T, C, 256>();
   }
   return false;
 }
 
-template <typename T, int C>
+template <typename T, int C, bool KEEP>
 hipError_t launch_fused_k(const Args& a, hipStream_t s) {
   switch (a.K) {
-    case 32: return launch_fused_t<T, C, 32>(a, s);
-    case 64: return launch_fused_t<T, C, 64>(a, s);
-    case 128: return launch_fused_t<T, C, 128>(a, s);
-    case 256: return launch_fused_t<T, C, 256>(a, s);
+    case 32: return launch_fused_t<T, C, 32, KEEP>(a, s);
+    case 64: return launch_fused_t<T, C, 64, KEEP>(a, s);
+    case 128: return launch_fused_t<T, C, 128, KEEP>(a, s);
+    case 256: return launch_fused_t<T, C, 256, KEEP>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1137,16 +1171,17 @@ constexpr bool pc_out_ok() {
          K3S<T, C, K, 2, NWL, 2, float, true>::fits_out;
 }
 
-template <typename T, int C, int K>
+// KEEP: the loaders also store h and v_new (kept states)
+template <typename T, int C, int K, bool KEEP>
 hipError_t launch_pc_out_t(const Args& a, hipStream_t s) {
   if constexpr (pc_out_ok<T, C, K>()) {
     constexpr int NWL = scan_loaders<T, C, K, float>();
     const int64_t nblk64 = a.N * a.HV * (a.V / 64);
     if (a.V % 64 == 0 && nblk64 >= kNumCUs) {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, false, false, float, true>), dim3((unsigned)nblk64),
+      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, KEEP, false, float, true>), dim3((unsigned)nblk64),
                          dim3(64 * (6 + NWL)), 0, s, a);
     } else {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, false, false, float, true>),
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, KEEP, false, float, true>),
                          dim3((unsigned)(a.N * a.HV * (a.V / 32))), dim3(64 * (4 + NWL)), 0, s, a);
     }
     return hipGetLastError();
@@ -1215,8 +1250,8 @@ hipError_t launch_fwd_h(const Args& a, hipStream_t s) {
 
 bool fwd_h_o_supported(const Args& a) {
   if (a.per_channel) return false;
-  if (a.dtype == GDR_BF16) return a.C == 32 ? fused_ok_k<bf16, 32>(a.K) : fused_ok_k<bf16, 64>(a.K);
-  return a.C == 32 ? fused_ok_k<float, 32>(a.K) : fused_ok_k<float, 64>(a.K);
+  if (a.dtype == GDR_BF16) return a.C == 32 ? fused_ok_k<bf16, 32, false>(a.K) : fused_ok_k<bf16, 64, false>(a.K);
+  return a.C == 32 ? fused_ok_k<float, 32, false>(a.K) : fused_ok_k<float, 64, false>(a.K);
 }
 
 bool fwd_h_o_preferred(const Args& a) {
@@ -1237,18 +1272,35 @@ hipError_t launch_fwd_h_o_pc(const Args& a, hipStream_t s) {
   if (!fwd_h_o_pc_supported(a) || a.kt == nullptr || a.dl == nullptr || a.aqk == nullptr || a.qgs == nullptr ||
       a.u == nullptr || !a.u_f32)
     return hipErrorInvalidValue;
+  const bool keep = a.h != nullptr && a.v_new != nullptr;
   switch (a.K) {
-    case 32: return launch_pc_out_t<bf16, 32, 32>(a, s);
-    case 64: return launch_pc_out_t<bf16, 32, 64>(a, s);
-    case 128: return launch_pc_out_t<bf16, 32, 128>(a, s);
+    case 32: return keep ? launch_pc_out_t<bf16, 32, 32, true>(a, s) : launch_pc_out_t<bf16, 32, 32, false>(a, s);
+    case 64: return keep ? launch_pc_out_t<bf16, 32, 64, true>(a, s) : launch_pc_out_t<bf16, 32, 64, false>(a, s);
+    case 128:
+      return keep ? launch_pc_out_t<bf16, 32, 128, true>(a, s) : launch_pc_out_t<bf16, 32, 128, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
+bool fwd_h_o_keep_supported(const Args& a) {
+  if (a.per_channel) return false;
+  if (a.dtype == GDR_BF16) return a.C == 32 ? fused_ok_k<bf16, 32, true>(a.K) : fused_ok_k<bf16, 64, true>(a.K);
+  return a.C == 32 ? fused_ok_k<float, 32, true>(a.K) : fused_ok_k<float, 64, true>(a.K);
+}
+
+hipError_t launch_fwd_h_o_keep(const Args& a, hipStream_t s) {
+  if (a.N == 0) return hipSuccess;
+  if (!fwd_h_o_keep_supported(a) || a.h == nullptr || a.v_new == nullptr || !a.u_f32) return hipErrorInvalidValue;
+  if (a.dtype == GDR_BF16)
+    return a.C == 32 ? launch_fused_k<bf16, 32, true>(a, s) : launch_fused_k<bf16, 64, true>(a, s);
+  return a.C == 32 ? launch_fused_k<float, 32, true>(a, s) : launch_fused_k<float, 64, true>(a, s);
+}
+
 hipError_t launch_fwd_h_o(const Args& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
-  if (a.dtype == GDR_BF16) return a.C == 32 ? launch_fused_k<bf16, 32>(a, s) : launch_fused_k<bf16, 64>(a, s);
-  return a.C == 32 ? launch_fused_k<float, 32>(a, s) : launch_fused_k<float, 64>(a, s);
+  if (a.dtype == GDR_BF16)
+    return a.C == 32 ? launch_fused_k<bf16, 32, false>(a, s) : launch_fused_k<bf16, 64, false>(a, s);
+  return a.C == 32 ? launch_fused_k<float, 32, false>(a, s) : launch_fused_k<float, 64, false>(a, s);
 }
 
 }  // namespace gdr
