@@ -46,6 +46,10 @@ namespace gdr {
 
 namespace {
 
+// largest 16-row gate span (max over features of G at the block's first row
+// minus its last) for which the gated pair sums take the MFMA form
+constexpr float kPairSpan = 40.f;
+
 template <typename T, int K>
 struct B3P {
   static constexpr int C = 32, NW = 4, NT = 256, VT = 32;
@@ -191,8 +195,41 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
 #pragma unroll
   for (int i = 0; i < SCK; ++i) sq_[i] = sk_[i] = zero4();
 
+  // value tiles: each tile's loads are issued one tile ahead, into
+  // registers, and staged when the previous tile's products are done
+  Frag<T> hr[NPH], orr[NPO], vr[NPO], er[NPE], dlr[NPE];
+  Frag<float> dhr[NPH];
+  auto fetch_tile = [&](int64_t j, int64_t v0) {
+    const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
+    const float* dhb = static_cast<const float*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
+    const T* eb = static_cast<const T*>(a.v_new) + ((c * HV + j) * V + v0) * (int64_t)C;
+    const T* db = static_cast<const T*>(a.de_local) + ((c * HV + j) * V + v0) * (int64_t)C;
+#pragma unroll
+    for (int i = 0; i < NPH; ++i) {
+      const int idx = tid + NT * i;
+      const bool in = idx < VT * CPR;
+      hr[i] = in ? ld8(hb + 8 * idx) : frag_zero<T>();
+      dhr[i] = in ? ld8(dhb + 8 * idx) : frag_zero<float>();
+    }
+#pragma unroll
+    for (int i = 0; i < NPO; ++i) {
+      const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
+      // rows past L load row 0 (a valid address) and are zeroed when staged
+      const int tc = (idx < C * VT / 8 && t < L) ? t : 0;
+      orr[i] = ld8(dop + ((t0 + tc) * HV + j) * V + v0 + v8);
+      vr[i] = ld8(vp + ((t0 + tc) * HV + j) * V + v0 + v8);
+    }
+#pragma unroll
+    for (int i = 0; i < NPE; ++i) {
+      const int idx = tid + NT * i;
+      const int ic = idx < VT * C / 8 ? idx : 0;
+      er[i] = ld8(eb + 8 * ic);
+      dlr[i] = ld8(db + 8 * ic);
+    }
+  };
   for (int jj = 0; jj < ng; ++jj) {
     const int64_t j = h * ng + jj;
+    fetch_tile(j, 0);   // with this head's T, kt, gate and beta
     // ---- per-head tiles: T, kt, the gate (cumsum below), beta
     {
       const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
@@ -238,40 +275,20 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int t = 0; t < C; ++t) sG[t * GP + d] = col[t];
     }
-    float lr = 0.f;     // sum_v S0[d][v] dS1[d][v] for feature d = tid (tid < K)
+    // sum_v S0[d][v] dS1[d][v] per feature, accumulated in the products phase
+    // by the waves of row block 0 (their slots cover every feature once):
+    // slot i, feature 16 db + r16, the 8 value rows of lane group g4
+    float lrp[SCK];
+#pragma unroll
+    for (int i = 0; i < SCK; ++i) lrp[i] = 0.f;
 
     f32x4 dQg[SCK], TdW[SCK], dKt[SCK], dP = zero4(), dA = zero4();
 #pragma unroll
     for (int i = 0; i < SCK; ++i) dQg[i] = TdW[i] = dKt[i] = zero4();
 
+
     for (int64_t v0 = 0; v0 < V; v0 += VT) {
       {
-        const T* hb = static_cast<const T*>(a.h) + ((c * HV + j) * V + v0) * (int64_t)K;
-        const float* dhb = static_cast<const float*>(a.dh) + ((c * HV + j) * V + v0) * (int64_t)K;
-        const T* eb = static_cast<const T*>(a.v_new) + ((c * HV + j) * V + v0) * (int64_t)C;
-        const T* db = static_cast<const T*>(a.de_local) + ((c * HV + j) * V + v0) * (int64_t)C;
-        Frag<T> hr[NPH], orr[NPO], vr[NPO], er[NPE], dlr[NPE];
-        Frag<float> dhr[NPH];
-#pragma unroll
-        for (int i = 0; i < NPH; ++i) {
-          const int idx = tid + NT * i;
-          const bool in = idx < VT * CPR;
-          hr[i] = in ? ld8(hb + 8 * idx) : frag_zero<T>();
-          dhr[i] = in ? ld8(dhb + 8 * idx) : frag_zero<float>();
-        }
-#pragma unroll
-        for (int i = 0; i < NPO; ++i) {
-          const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
-          const bool in = idx < C * VT / 8 && t < L;
-          orr[i] = in ? ld8(dop + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
-          vr[i] = in ? ld8(vp + ((t0 + t) * HV + j) * V + v0 + v8) : frag_zero<T>();
-        }
-#pragma unroll
-        for (int i = 0; i < NPE; ++i) {
-          const int idx = tid + NT * i;
-          er[i] = (idx < VT * C / 8) ? ld8(eb + 8 * idx) : frag_zero<T>();
-          dlr[i] = (idx < VT * C / 8) ? ld8(db + 8 * idx) : frag_zero<T>();
-        }
 #pragma unroll
         for (int i = 0; i < NPH; ++i) {
           const int idx = tid + NT * i, v = idx / CPR, d8 = (idx % CPR) * 8;
@@ -287,8 +304,8 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
         for (int i = 0; i < NPO; ++i) {
           const int idx = tid + NT * i, t = idx / (VT / 8), v8 = (idx % (VT / 8)) * 8;
           if (idx < C * VT / 8) {
-            st8(&sDO[t * PV + v8], orr[i]);
-            st8(&sV[t * PV + v8], vr[i]);
+            st8(&sDO[t * PV + v8], t < L ? orr[i] : frag_zero<T>());
+            st8(&sV[t * PV + v8], t < L ? vr[i] : frag_zero<T>());
           }
         }
 #pragma unroll
@@ -300,12 +317,8 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
           }
         }
       }
+      if (v0 + VT < V) fetch_tile(j, v0 + VT);
       lds_barrier();
-      // S0 . dS1 per feature (fp32 dS1 from its hi + lo pair)
-      if (tid < K) {
-#pragma unroll 8
-        for (int v = 0; v < VT; ++v) lr += to_float(sH[v * PK + tid]) * fDH.get(v, tid);
-      }
 
       // ---- dE^T[v][t] = de_local^T[v][t] + (Kt dS1)[t][v]; one 16 x 16 block per wave
       {
@@ -342,9 +355,15 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
         for (int i = 0; i < SCK; ++i) {
           const int db = (wv + NW * i) / NRB;
           const Frag<T> bS = lds_col8(sH, PK, 0, 16 * db, lane);
+          const SplitFrag<T> bD = fDH.col(0, 16 * db, lane);
           mma(dQg[i], aO, bS);
           mma_split(TdW[i], aY, bS);
-          mma_split(dKt[i], aE, fDH.col(0, 16 * db, lane));
+          mma_split(dKt[i], aE, bD);
+          if constexpr (rb == 0) {
+            const f32x8 hs = bS.f32(), ds = bD.hi.f32() + (FTile<T>::kSplit ? bD.lo.f32() : zero8());
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lrp[i] += hs[e] * ds[e];
+          }
         }
         constexpr int cb = wv / NRB;
         const Frag<T> bE = lds_col8(sE, PCC, 0, 16 * cb, lane);
@@ -365,7 +384,13 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
         sDA[r * CP + t] = (t < r && r < L) ? -dA[e] : 0.f;
       }
     }
-    if (tid < K) sLr[tid] = lr;
+    if constexpr (rb == 0) {
+#pragma unroll
+      for (int i = 0; i < SCK; ++i) {
+        const float x = group4_sum(lrp[i]);
+        if (g4 == 0) sLr[16 * ((wv + NW * i) / NRB) + r16] = x;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
       dQg[i] *= scale;
@@ -373,7 +398,17 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
     }
     lds_barrier();
 
-    // ---- the gated pair sums, one pass over the chunk's rows x
+    // ---- the gated pair sums.  With every 16-row block's gate span below
+    //      kPairSpan they run on MFMA with a reference row per block: for the
+    //      wave's rows r (block R = rb) m = 16 R, for its rows t (block T = rb)
+    //      m' = 16 T + 15, so that
+    //        dqP[r]  = exp(G_r - G_m)   sum_t dP[r][t] (k^_t exp(G_m - G_t))
+    //        dkP[t]  = exp(G_m' - G_t)  sum_r dP[r][t] (q^_r exp(G_r - G_m'))
+    //      (dkA1, dkA2 alike with dA and beta dA^T): every outer factor is
+    //      <= 1 and every inner one <= exp(span); rows outside the causal
+    //      range are zeroed before their factor could overflow.  Operands go
+    //      in as bf16 hi + lo pairs.  A wider span takes one pass over the
+    //      chunk's rows x with the exact difference per term.
     f32x4 dqP[SCK], dkP[SCK], dkA1[SCK], dkA2[SCK], Gr[SCK];
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
@@ -382,34 +417,88 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) Gr[i][e] = sG[(16 * rb + 4 * g4 + e) * GP + d];
     }
-    for (int x = 0; x < L; ++x) {
-      const float bx = sB[x], rqx = sRq[x], rkx = sRk[x];
-      float dpa[4], dpb[4], daa[4], dab[4];
+    float span = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
-        dpa[e] = sDP[r * CP + x];     // dP[r][x], x <= r
-        daa[e] = sDA[r * CP + x];     // dA[r][x], x < r
-        dpb[e] = sDP[x * CP + r];     // dP[x][r], x >= r
-        dab[e] = bx * sDA[x * CP + r];
+    for (int b = 0; b < NRB; ++b)
+      for (int d = lane; d < K; d += 64) span = fmaxf(span, sG[(16 * b) * GP + d] - sG[(16 * b + 15) * GP + d]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+    if (span <= kPairSpan) {
+      const int ra = 16 * rb + r16;
+      f32x8 xp, xa, xpt, xat;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int x = 8 * g4 + e;
+        xp[e] = sDP[ra * CP + x];
+        xa[e] = sDA[ra * CP + x];
+        xpt[e] = sDP[x * CP + ra];
+        xat[e] = sB[x] * sDA[x * CP + ra];
       }
+      const SplitFrag<T> aP = SplitFrag<T>::make(xp), aA = SplitFrag<T>::make(xa);
+      const SplitFrag<T> aPT = SplitFrag<T>::make(xpt), aAT = SplitFrag<T>::make(xat);
+      const int mR = 16 * rb, mT = 16 * rb + 15;
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int d = 16 * ((wv + NW * i) / NRB) + r16;
-        const float kx = to_float(sK[x * PK + d]) * rkx, qx = to_float(sQ[x * PK + d]) * rqx;
-        const float gx = sG[x * GP + d];
+        const int db = (wv + NW * i) / NRB, d = 16 * db + r16;
+        const float GmR = sG[mR * GP + d], GmT = sG[mT * GP + d];
+        const f32x8 kc = lds_col8(sK, PK, 0, 16 * db, lane).f32(), qc = lds_col8(sQ, PK, 0, 16 * db, lane).f32();
+        f32x8 bK, bQ, bK2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int x = 8 * g4 + e;
+          const float Gx = sG[x * GP + d];
+          const float f = x <= mT ? __expf(GmR - Gx) : 0.f;     // t up to the end of block R
+          const float hh = x >= mR ? __expf(Gx - GmT) : 0.f;    // r from the start of block T
+          const float kx = kc[e] * sRk[x];
+          bK[e] = kx * f;
+          bQ[e] = qc[e] * sRq[x] * hh;
+          bK2[e] = kx * hh;
+        }
+        const SplitFrag<T> fK = SplitFrag<T>::make(bK);
+        f32x4 c1 = zero4(), c2 = zero4(), c3 = zero4(), c4 = zero4();
+        mma_split(c1, aP, fK);
+        mma_split(c2, aA, fK);
+        mma_split(c3, aPT, SplitFrag<T>::make(bQ));
+        mma_split(c4, aAT, SplitFrag<T>::make(bK2));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float e2 = __expf(Gr[i][e] - GmR), e1 = __expf(GmT - Gr[i][e]);
+          dqP[i][e] = e2 * c1[e];
+          dkA1[i][e] = e2 * c2[e];
+          dkP[i][e] = e1 * c3[e];
+          dkA2[i][e] = e1 * c4[e];
+        }
+      }
+    } else {
+      for (int x = 0; x < L; ++x) {
+        const float bx = sB[x], rqx = sRq[x], rkx = sRk[x];
+        float dpa[4], dpb[4], daa[4], dab[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rb + 4 * g4 + e;
-          // exp(G_r - G_x) below the diagonal, exp(G_x - G_r) above it
-          const float ex = __expf(x <= r ? Gr[i][e] - gx : gx - Gr[i][e]);
-          if (x <= r) {
-            dqP[i][e] += dpa[e] * kx * ex;
-            dkA1[i][e] += daa[e] * kx * ex;
-          }
-          if (x >= r) {
-            dkP[i][e] += dpb[e] * qx * ex;
-            dkA2[i][e] += dab[e] * kx * ex;
+          dpa[e] = sDP[r * CP + x];     // dP[r][x], x <= r
+          daa[e] = sDA[r * CP + x];     // dA[r][x], x < r
+          dpb[e] = sDP[x * CP + r];     // dP[x][r], x >= r
+          dab[e] = bx * sDA[x * CP + r];
+        }
+#pragma unroll
+        for (int i = 0; i < SCK; ++i) {
+          const int d = 16 * ((wv + NW * i) / NRB) + r16;
+          const float kx = to_float(sK[x * PK + d]) * rkx, qx = to_float(sQ[x * PK + d]) * rqx;
+          const float gx = sG[x * GP + d];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * g4 + e;
+            // exp(G_r - G_x) below the diagonal, exp(G_x - G_r) above it
+            const float ex = __expf(x <= r ? Gr[i][e] - gx : gx - Gr[i][e]);
+            if (x <= r) {
+              dqP[i][e] += dpa[e] * kx * ex;
+              dkA1[i][e] += daa[e] * kx * ex;
+            }
+            if (x >= r) {
+              dkP[i][e] += dpb[e] * qx * ex;
+              dkA2[i][e] += dab[e] * kx * ex;
+            }
           }
         }
       }

@@ -457,6 +457,24 @@ def test_bwd_per_channel_intermediates():
     compare(got, ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_per_channel_wide_gate_span(dtype):
+    """Per-channel gates of -9 per token on some channels (about 144 of decay
+    inside a 16-row block, past the span below which the gated pair sums run
+    on matrix cores, so those chunks take the exact per-term pass) and mild
+    gates elsewhere in the batch, on a ragged dense batch: every gradient
+    against the oracle."""
+    w, inp = mk(dtype=dtype, B=2, T=100, H=2, HV=2, K=64, V=64, C=32, pc=True, seed=14)
+    g = inp["g"].clone()
+    g[0, :, :, ::3] = -9.0           # row 0: wide spans on every third channel
+    g[0, 1::5, :, ::3] = -0.01
+    inp["g"] = g.contiguous()
+    got, _, _ = gpu_bwd(inp)
+    for n in GRADS:
+        assert bool(torch.isfinite(torch.as_tensor(got[n])).all()), n
+    compare(got, oracle_bwd(inp), TOL[dtype])
+
+
 def test_bwd_per_channel_gate_equal_channels_is_scalar():
     """A per-channel gate whose channels are all equal is the scalar gate: its
     dg summed over the channels equals the scalar backward's dg, and the other

@@ -554,6 +554,12 @@ def test_config_kda_bf16():
     _run_config("kda_bf16", rows=slice(1, 2))
 
 
+def test_config_kda_bf16_first_row():
+    """The per-channel workload's other row (the two tests together check
+    every output of the full-size forward)."""
+    _run_config("kda_bf16", rows=slice(0, 1))
+
+
 def test_config_long_bf16_forward():
     _run_config("long_bf16", heads=[0, 21])
 
