@@ -26,6 +26,9 @@ namespace gdr {
 
 namespace {
 
+// largest diagonal-block gate span for the reference-row form of P
+constexpr float kSpanLimit = 80.f;
+
 template <typename T, int C, int K>
 __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   constexpr int NB = C / 16;
@@ -161,9 +164,9 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
 
 // Per-channel gate (chunk 32): the same de_local, with
 //   P[r][t] = sum_d q^_rd k^_td exp(G_rd - G_td)        (t <= r)
-// formed on the vector ALU with the exact exponent of every difference
-// (G_rd - G_td <= 0 for a decay gate: no overflow, no reference row needed),
-// and, for the reverse scan, the chunk's gated operand rows and decay
+// formed on MFMA with a reference row per 16 x 16 block (as the forward's
+// per-channel K1 forms kk^T), and, for the reverse scan, the chunk's gated
+// operand rows and decay
 //   kt[t][d] = exp(G_Ld - G_td) k^_td      qg[t][d] = scale exp(G_td) q^_td
 //   dl[d]    = exp(G_Ld)
 // ([NT][HV][C][K] in the input dtype, zero past L; [NT][HV][K] fp32), which
@@ -286,26 +289,70 @@ __global__ __launch_bounds__(256) void b1_bwd_intra_pc(Args a) {
   for (int d = tid; d < K; d += NT) dlp[d] = __expf(GL[d]);
 
   // ---- P^T[t][r] = rq_r rk_t sum_d q_rd k_td exp(G_rd - G_td), t <= r < L:
-  //      thread (r = tid / 8, token group tid % 8) owns t = group + 8 m
+  //      the lower-triangular 16 x 16 blocks (r block rb, t block cb <= rb)
+  //      on MFMA, one per wave, with a reference row m per block so that both
+  //      gated operands carry factors exp(+-(G - G_m)) <= 1 (off-diagonal: the
+  //      last row of the t block; diagonal: the middle row while the block's
+  //      gate span keeps every factor below e^80, else per-element
+  //      exponentials); operands as bf16 hi + lo pairs.  The block above the
+  //      diagonal is zero.
   {
-    const int r = tid >> 3, tg = tid & 7;
-    float acc[C / 8];
+    constexpr int NB = C / 16, KS = K / 32;
+    int bi = 0;
 #pragma unroll
-    for (int m = 0; m < C / 8; ++m) acc[m] = 0.f;
-    if (r < L) {
-      for (int d = 0; d < K; ++d) {
-        const float qv = to_float(sQ[r * KP + d]), gr = sG[r * GP + d];
+    for (int rb = 0; rb < NB; ++rb) {
 #pragma unroll
-        for (int m = 0; m < C / 8; ++m) {
-          const int t = tg + 8 * m;
-          if (t <= r) acc[m] += qv * to_float(sK[t * KP + d]) * __expf(gr - sG[t * GP + d]);
+      for (int cb = 0; cb < NB; ++cb, ++bi) {
+        if (bi % 4 != wv) continue;
+        f32x4 sp = zero4();
+        if (cb <= rb) {
+          bool direct = false;
+          int m = 16 * cb + 15;
+          if (cb == rb) {
+            m = 16 * rb + 8;
+            float span = 0.f;
+            for (int d = lane; d < K; d += 64)
+              span = fmaxf(span, sG[(16 * rb) * GP + d] - sG[(16 * rb + 15) * GP + d]);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) span = fmaxf(span, __shfl_xor(span, o, 64));
+            direct = span > kSpanLimit;
+          }
+          const int ra = 16 * rb + r16, rc = 16 * cb + r16;
+          if (!direct) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              const int d0 = 32 * ks + 8 * g4;
+              f32x8 xq = ld8(&sQ[ra * KP + d0]).f32(), xk = ld8(&sK[rc * KP + d0]).f32();
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float gm = sG[m * GP + d0 + e];
+                xq[e] *= __expf(sG[ra * GP + d0 + e] - gm);
+                xk[e] *= __expf(gm - sG[rc * GP + d0 + e]);
+              }
+              // element i of lane (r16, g4): row r = 16 rb + 4 g4 + i, token t = 16 cb + r16
+              mma_split(sp, SplitFrag<T>::make(xq), SplitFrag<T>::make(xk));
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * rb + 4 * g4 + i, t = 16 * cb + r16;
+              float sum = 0.f;
+              if (t <= r && r < L) {
+                for (int d = 0; d < K; ++d)
+                  sum += to_float(sQ[r * KP + d]) * to_float(sK[t * KP + d]) * __expf(sG[r * GP + d] - sG[t * GP + d]);
+              }
+              sp[i] = sum;
+            }
+          }
+          const int t = 16 * cb + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rb + 4 * g4 + i;
+            sp[i] = (t <= r && r < L) ? sp[i] * sRq[r] * sRk[t] : 0.f;
+          }
         }
+        fPT.put4(16 * cb + r16, 16 * rb + 4 * g4, sp);
       }
-    }
-#pragma unroll
-    for (int m = 0; m < C / 8; ++m) {
-      const int t = tg + 8 * m;
-      fPT.put(t, r, (t <= r && r < L) ? acc[m] * sRq[r] * sRk[t] : 0.f);
     }
   }
 
