@@ -374,8 +374,18 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
     return hipErrorInvalidValue;    // rejected on the host before any launch
   } else {
     // 32 value columns per workgroup, or 16 when the 32-column grid would
-    // leave compute units idle (as the forward scan)
+    // leave compute units idle (as the forward scan), or 64 (four compute and
+    // four loader waves, 16-bit inputs) when the 64-column grid still gives
+    // every compute unit a workgroup and its tiles fit: the 32-column grid
+    // would then run in two rounds of one workgroup per compute unit
     const int64_t nblk32 = a.N * a.HV * (a.V / 32);
+    if constexpr (sizeof(T) == 2 && B2S<T, C, K, 4, 4, PC>::STG) {
+      if (a.V % 64 == 0 && nblk32 / 2 >= kNumCUs && 2 * B2S<T, C, K, 2, NWL, PC>::buf_bytes +
+                                                          2 * B2S<T, C, K, 2, NWL, PC>::stg_bytes > 80 * 1024) {
+        hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 4, 4, PC>), dim3((unsigned)(nblk32 / 2)), dim3(64 * 8), 0, s, a);
+        return hipGetLastError();
+      }
+    }
     if (nblk32 < kNumCUs) {
       hipLaunchKernelGGL((b2_bwd_dh<T, C, K, 1, NWL, PC>), dim3((unsigned)(2 * nblk32)), dim3(64 * (1 + NWL)), 0, s,
                          a);

@@ -457,6 +457,22 @@ def test_bwd_per_channel_intermediates():
     compare(got, ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("pc", [False, True])
+def test_bwd_reverse_scan_four_wave_grid(pc):
+    """N * HV * V / 64 = 256 at chunk 32, K = 128, bf16: the reverse scan runs
+    four compute waves (64 value columns) per workgroup.  A ragged tail, h0
+    and slow decay, every gradient against the oracle on three heads."""
+    w, inp = mk(B=2, T=77, H=32, HV=32, K=128, V=256, C=32, pc=pc, slow=True, seed=21, scale=128 ** -0.5)
+    assert w.B * w.HV * (w.V // 64) >= 256
+    heads = [0, 17, 31]
+    res = gdr.chunk_bwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                        dev(inp["do"]), dev(inp["dht"]), scale=inp["scale"], chunk_size=32,
+                        initial_state=dev(inp["h0"]), use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    got = {n: f64(t[:, :, heads] if n != "dh0" else t[:, heads]) for n, t in zip(GRADS, res)}
+    compare(got, oracle_bwd(slice_inputs(inp, heads=heads)), TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_bwd_per_channel_wide_gate_span(dtype):
     """Per-channel gates of -9 per token on some channels (about 144 of decay
