@@ -141,6 +141,29 @@ def test_per_channel_fused_forward_intermediates(cfg):
     check("ht (separate stages)", f64(ht2), f64(ht), TOL["bf16"])
 
 
+@pytest.mark.parametrize("keep", [False, True])
+def test_per_channel_fused_forward_varlen_gva(keep):
+    """The per-channel fused forward (and its kept-states form) on a varlen
+    GVA batch at chunk 32: empty, one-token, chunk-aligned and ragged
+    sequences, 2 value heads per q/k head, in-kernel L2 norm, h0; o and ht
+    against the oracle, every sequence on its own."""
+    lengths = [0, 1, 31, 32, 33, 100, 0, 7, 130]
+    w, inp = mk(B=1, H=2, HV=4, K=128, V=128, C=32, pc=True, lengths=lengths, slow=True, scale=0.5)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, cu_seqlens=inp["cu_seqlens"],
+                         use_qk_l2norm=True, keep_states=keep)
+    assert gdr.chunk_fwd_fused(p) == (0 if keep else 2)
+    o, ht, ws = gpu_fwd(inp, keep_states=keep)
+    ro, rht = oracle_fwd(inp)
+    check("o", f64(o), ro, TOL["bf16"])
+    check("ht", f64(ht), rht, TOL["bf16"])
+    cu = inp["cu_seqlens"].tolist()
+    for n in range(len(lengths)):
+        if lengths[n]:
+            check(f"o[seq {n}]", f64(o)[:, cu[n]:cu[n + 1]], ro[:, cu[n]:cu[n + 1]], TOL["bf16"])
+    if keep:
+        assert ws["h"] is not None and ws["Tm"] is not None
+
+
 def test_per_channel_fused_forward_extreme_gate_span():
     """Per-channel gates of -9 (about 144 of decay inside a 16-token block,
     above K1's exponential-safety limit, so its diagonal blocks take the
