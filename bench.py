@@ -77,10 +77,11 @@ def stage_bytes_per_token_head(w, T_seq, pc_fused=False, keep=False):
         }
         if pc_fused or keep:
             # + q read; aqk (fp32) and the hi + lo query pair written (Tm only
-            # when the states are kept)
-            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - (0 if keep else e * C)
+            # when the states are kept; u in the input dtype otherwise)
+            ue = 4 if keep else e
+            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - (0 if keep else e * C) - (4 - ue) * V
             # w, u, kt, dl, the query pair, aqk -> o, ht (+ h, v_new when kept)
-            d["fwd_h_o"] = (e * K + 4 * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
+            d["fwd_h_o"] = (e * K + ue * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
                             + (states if keep else 0))
         return d
     # K1's per-chunk token factors (scalar gate): 3C + 4 floats per chunk and

@@ -326,7 +326,7 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
     no_tm = nt > 0 and lay.Tm == lay.w
     no_states = nt > 0 and lay.h == lay.v_new
     pc_fused = nt > 0 and lay.qgs > lay.aqk
-    compact = no_tm and not pc_fused       # the scalar-gate fused stages: u in the input dtype
+    compact = no_tm                        # the fused stages: u in the input dtype
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 

@@ -160,8 +160,8 @@ gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_f
   off = round_up(off + (pc_fused ? 0 : (size_t)nt * HV * C * C * es));
   l.w = off;
   off = round_up(off + (size_t)nt * HV * C * K * es);
-  l.u = off;   // fp32 from the separate WY stage, input dtype from the fused K1 + K2 stage
-  off = round_up(off + (size_t)nt * HV * V * C * sizeof(float));
+  l.u = off;   // fp32 from the separate WY stage, input dtype from the fused stages
+  off = round_up(off + (size_t)nt * HV * V * C * (pc_fused ? es : sizeof(float)));
   l.h = off;
   off = round_up(off + (pc_fused ? 0 : (size_t)nt * HV * V * K * es));
   l.v_new = off;
@@ -406,8 +406,8 @@ hipError_t fwd_run(const gdr_problem& p, const void* q, const void* k, const voi
   if (kind == 2 && l.qgs > l.aqk) {
     // per-channel gate: the fused K1 + K2 also writes aqk and the gated query
     // pair, and the fused scan + output reads them (Tm, h and v_new stay on
-    // chip)
-    a.u_f32 = 1;
+    // chip; u in the input dtype, as in the scalar-gate fused stages)
+    a.u_f32 = 0;
     a.Tm = nullptr;
     a.h = nullptr;
     a.v_new = nullptr;

@@ -17,7 +17,8 @@
 //   qgs_t     = scale exp(G_t) q^_t   as a bf16 hi + lo pair   (the output's two terms)
 // Same results as the K1 and K2 stages up to rounding (Tm feeds w and u here
 // in fp32 instead of through its bf16 copy); Tm itself is written only when
-// a.Tm is set (the backward reads it).
+// a.Tm is set (the backward reads it), and u is written in fp32 when a.u_f32
+// is set (kept states), else in the input dtype (the fused forward).
 //
 // gfx950 mapping (4 waves per chunk and value head):
 //  * every global load of the chunk (key and query rows, the gate tile as
@@ -71,7 +72,7 @@ struct K12P {
   static constexpr bool fits = lds_bytes <= 64 * 1024;
 };
 
-template <typename T, int C, int K>
+template <typename T, int C, int K, typename UT>
 __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
   using Cfg = K12P<T, C, K>;
   constexpr int NW = Cfg::NW, NT = Cfg::NT, NB = Cfg::NB, NLB = Cfg::NLB, KSC = Cfg::KSC, KS = Cfg::KS;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
   const T* __restrict__ qp = static_cast<const T*>(a.q);
   const T* __restrict__ vp = static_cast<const T*>(a.v);
   T* __restrict__ wp = static_cast<T*>(a.w) + (c * HV + j) * (int64_t)(C * K);
-  float* __restrict__ up = static_cast<float*>(a.u) + (c * HV + j) * (int64_t)C * V;
+  UT* __restrict__ up = static_cast<UT*>(a.u) + (c * HV + j) * (int64_t)C * V;
   // intra attention and gated queries for the fused scan + output (bf16 only)
   const bool want_q = sizeof(T) == 2 && a.aqk != nullptr && a.qgs != nullptr;
 
@@ -473,7 +474,13 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
 template <typename T, int C, int K>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   if constexpr (K12P<T, C, K>::fits) {
-    hipLaunchKernelGGL((k12pc_kkt_wy<T, C, K>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
+    // u in fp32 (kept states, which the backward reads) or in the input dtype
+    // (the fused forward, whose scan + output takes it as the scalar-gate fused
+    // stage does)
+    if (a.u_f32)
+      hipLaunchKernelGGL((k12pc_kkt_wy<T, C, K, float>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k12pc_kkt_wy<T, C, K, T>), dim3((unsigned)(a.NTmax * a.HV)), dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

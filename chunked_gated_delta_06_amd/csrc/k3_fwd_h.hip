@@ -1171,17 +1171,19 @@ constexpr bool pc_out_ok() {
          K3S<T, C, K, 2, NWL, 2, float, true>::fits_out;
 }
 
-// KEEP: the loaders also store h and v_new (kept states)
+// KEEP: h and v_new are stored as well (kept states), and u is the fp32 of
+// the kept-states K1 + K2; otherwise u is in the input dtype
 template <typename T, int C, int K, bool KEEP>
 hipError_t launch_pc_out_t(const Args& a, hipStream_t s) {
   if constexpr (pc_out_ok<T, C, K>()) {
+    using UT = typename std::conditional<KEEP, float, T>::type;
     constexpr int NWL = scan_loaders<T, C, K, float>();
     const int64_t nblk64 = a.N * a.HV * (a.V / 64);
     if (a.V % 64 == 0 && nblk64 >= kNumCUs) {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, KEEP, false, float, true>), dim3((unsigned)nblk64),
+      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, KEEP, false, UT, true>), dim3((unsigned)nblk64),
                          dim3(64 * (6 + NWL)), 0, s, a);
     } else {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, KEEP, false, float, true>),
+      hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, KEEP, false, UT, true>),
                          dim3((unsigned)(a.N * a.HV * (a.V / 32))), dim3(64 * (4 + NWL)), 0, s, a);
     }
     return hipGetLastError();
@@ -1269,10 +1271,10 @@ bool fwd_h_o_pc_preferred(const Args& a) { return fwd_h_o_pc_supported(a); }
 
 hipError_t launch_fwd_h_o_pc(const Args& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
-  if (!fwd_h_o_pc_supported(a) || a.kt == nullptr || a.dl == nullptr || a.aqk == nullptr || a.qgs == nullptr ||
-      a.u == nullptr || !a.u_f32)
-    return hipErrorInvalidValue;
   const bool keep = a.h != nullptr && a.v_new != nullptr;
+  if (!fwd_h_o_pc_supported(a) || a.kt == nullptr || a.dl == nullptr || a.aqk == nullptr || a.qgs == nullptr ||
+      a.u == nullptr || (a.u_f32 != 0) != keep)
+    return hipErrorInvalidValue;
   switch (a.K) {
     case 32: return keep ? launch_pc_out_t<bf16, 32, 32, true>(a, s) : launch_pc_out_t<bf16, 32, 32, false>(a, s);
     case 64: return keep ? launch_pc_out_t<bf16, 32, 64, true>(a, s) : launch_pc_out_t<bf16, 32, 64, false>(a, s);

@@ -116,7 +116,7 @@ def test_workspace_layout():
     offs = [q.chunk_idx, q.Tm, q.w, q.u, q.h, q.kt, q.dl, q.aqk, q.qgs, q.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert q.h == q.v_new == q.kscale == q.kt and q.Tm == q.w
-    assert q.h - q.u >= n32 * HV * V * 32 * 4
+    assert n32 * HV * V * 32 * 2 <= q.h - q.u < n32 * HV * V * 32 * 4     # u in the input dtype
     assert q.dl - q.kt >= n32 * HV * 32 * K * 2 and q.aqk - q.dl >= n32 * HV * K * 4
     assert q.qgs - q.aqk >= n32 * HV * 32 * 32 * 4 and q.total - q.qgs >= n32 * HV * 2 * 32 * K * 2
     for kw in (dict(keep_states=1), dict(dtype=gdr.GDR_FP32), dict(K=256), dict(chunk_size=64)):

@@ -132,7 +132,8 @@ def test_per_channel_fused_forward_intermediates(cfg):
     check("kt", f64(ws["kt"][:NT]), it["KT"], TOL["bf16"])
     check("dl", f64(ws["dl"][:NT]), it["DL"], 1e-5)
     check("w", f64(ws["w"][:NT]), it["W"], TOL["bf16"])
-    check("u", f64(ws["u"][:NT]).transpose(0, 1, 3, 2), it["U"], TOL["bf16"])
+    assert ws["u"] is None      # u in the input dtype
+    check("u", f64(ws["u_fused"][:NT]).transpose(0, 1, 3, 2), it["U"], TOL["bf16"])
     check("o", f64(o), ro, TOL["bf16"])
     check("ht", f64(ht), rht, TOL["bf16"])
     # the separate stages on the same inputs agree with it within the tolerance
