@@ -55,7 +55,7 @@ def stage_bytes_per_token_head(w, T_seq, pc_fused=False, keep=False):
     library's storage dtypes (q/k/v/o and the intermediates in the input dtype,
     except the separate WY stage's u, which is fp32; g and beta in fp32, h0/ht
     fp32).  ``pc_fused``: the per-channel fused forward (its fused K1 + K2 also
-    writes aqk and the gated query pair, read by the fused scan + output).
+    writes aqk and the gated queries, read by the fused scan + output).
     ``keep``: a forward that keeps its states (its fused stages also write Tm,
     u in fp32, h and v_new)."""
     e = 2 if w.dtype == "bf16" else 4
@@ -76,12 +76,12 @@ def stage_bytes_per_token_head(w, T_seq, pc_fused=False, keep=False):
             "fwd_o": 2 * r * K * e + gb + e * V + e * K * V / C + V * e,
         }
         if pc_fused or keep:
-            # + q read; aqk (fp32) and the hi + lo query pair written (Tm only
-            # when the states are kept; u in the input dtype otherwise)
+            # + q read; aqk (fp32) and the gated queries written (Tm only when
+            # the states are kept; u in the input dtype otherwise)
             ue = 4 if keep else e
-            d["kkt_wy"] += r * K * e + 4 * C + 2 * e * K - (0 if keep else e * C) - (4 - ue) * V
-            # w, u, kt, dl, the query pair, aqk -> o, ht (+ h, v_new when kept)
-            d["fwd_h_o"] = (e * K + ue * V + kt_dl + 2 * e * K + 4 * C + e * V + 8 * K * V / T_seq
+            d["kkt_wy"] += r * K * e + 4 * C + e * K - (0 if keep else e * C) - (4 - ue) * V
+            # w, u, kt, dl, the gated queries, aqk -> o, ht (+ h, v_new when kept)
+            d["fwd_h_o"] = (e * K + ue * V + kt_dl + e * K + 4 * C + e * V + 8 * K * V / T_seq
                             + (states if keep else 0))
         return d
     # K1's per-chunk token factors (scalar gate): 3C + 4 floats per chunk and

@@ -327,6 +327,8 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
     no_states = nt > 0 and lay.h == lay.v_new
     pc_fused = nt > 0 and lay.qgs > lay.aqk
     compact = no_tm                        # the fused stages: u in the input dtype
+    qg_tiles = max(1, (lay.total - lay.qgs) // max(1, nt * HV * C * K * (2 if p.dtype == GDR_BF16 else 4))) \
+        if pc_fused else 0
     dt = torch.bfloat16 if p.dtype == GDR_BF16 else torch.float32
     es = 2 if p.dtype == GDR_BF16 else 4
 
@@ -352,7 +354,8 @@ def workspace_views(p: GdrProblem, ws: torch.Tensor, lay: Optional[GdrFwdLayout]
         kt=view(lay.kt, (nt, HV, C, K), dt, es) if lay.dl > lay.kt else None,
         dl=view(lay.dl, (nt, HV, K), torch.float32, 4) if lay.aqk > lay.dl else None,
         aqk=view(lay.aqk, (nt, HV, C, C), torch.float32, 4) if pc_fused else None,
-        qgs=view(lay.qgs, (nt, HV, 2, C, K), dt, es) if pc_fused else None,
+        # the gated queries: one tile in the input dtype, or a hi + lo pair
+        qgs=view(lay.qgs, (nt, HV, qg_tiles, C, K), dt, es) if pc_fused else None,
     )
 
 

@@ -180,7 +180,7 @@ gdr_fwd_layout layout_of(const gdr_problem& p, bool pc_regions = true, bool pc_f
   l.aqk = off;
   off = round_up(off + (pco ? (size_t)nt * HV * C * C * sizeof(float) : 0));
   l.qgs = off;
-  off = round_up(off + (pco ? (size_t)nt * HV * 2 * C * K * es : 0));
+  off = round_up(off + (pco ? (size_t)nt * HV * gdr::kQgsTiles * C * K * es : 0));
   l.total = off;
   return l;
 }

@@ -76,12 +76,17 @@ struct Args {
   // forward with a per-channel gate and the fused scan + output: the chunk's
   // intra attention aqk[r][t] = scale sum_d q^_rd k^_td exp(G_rd - G_td) for
   // t <= r (fp32 [NT][HV][C][C], zero above the diagonal and past L) and its
-  // gated queries scale exp(G_t) q^_t as a bf16 hi + lo pair (qgs
-  // [NT][HV][2][C][K]: the hi tile, then the lo tile), both written by the
+  // gated queries scale exp(G_t) q^_t (qgs [NT][HV][kQgsTiles][C][K]: one
+  // tile in the input dtype, or a hi tile and a lo tile), both written by the
   // fused per-channel K1 + K2
   float* aqk;
   void* qgs;
 };
+
+// Tiles of the gated queries of the per-channel fused forward: 1 (rounded once
+// to the input dtype; the output's inter term then carries the same rounding
+// as its bf16 state h) or 2 (a bf16 hi + lo pair).
+constexpr int kQgsTiles = 1;
 
 int64_t nt_max(const gdr_problem& p);
 constexpr int64_t kMaxOrdered = 1024;

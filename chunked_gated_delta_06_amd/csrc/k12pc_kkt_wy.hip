@@ -14,7 +14,8 @@
 //   kt_t = exp(G_L - G_t) k^_t,  dl = exp(G_L)                (the state update)
 // and, for the fused scan + output (a.aqk / a.qgs set, bf16),
 //   aqk[r][t] = scale sum_d q^_rd k^_td exp(G_rd - G_td)       t <= r
-//   qgs_t     = scale exp(G_t) q^_t   as a bf16 hi + lo pair   (the output's two terms)
+//   qgs_t     = scale exp(G_t) q^_t   (the output's inter term; one tile in the
+//                                      input dtype, or a bf16 hi + lo pair)
 // Same results as the K1 and K2 stages up to rounding (Tm feeds w and u here
 // in fp32 instead of through its bf16 copy); Tm itself is written only when
 // a.Tm is set (the backward reads it), and u is written in fp32 when a.u_f32
@@ -33,7 +34,7 @@
 //    middle row while the block's gate span keeps every factor below e^80,
 //    else per-element exponentials); kk^T takes single-rounded bf16 operands,
 //    q k^T hi + lo pairs;
-//  * the element-wise operands (k exp(G) for w, kt, the gated query pair) come
+//  * the element-wise operands (k exp(G) for w, kt, the gated queries) come
 //    from each thread's own key / query pieces, still in registers, with one
 //    exponential per element shared between them;
 //  * (I + A)^-1 in fp32 in LDS as in the fused scalar-gate stage; w and u as in
@@ -181,9 +182,9 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
   lds_barrier();
 
   // ---- element-wise operands from this thread's own pieces: k exp(G) (the w
-  //      products' tile), kt = exp(G_L - G_t) k^_t, the gated query pair, dl
+  //      products' tile), kt = exp(G_L - G_t) k^_t, the gated queries, dl
   T* __restrict__ ktp = a.kt != nullptr ? static_cast<T*>(a.kt) + (c * HV + j) * (int64_t)(C * K) : nullptr;
-  T* __restrict__ qgp = want_q ? static_cast<T*>(a.qgs) + (c * HV + j) * (int64_t)(2 * C * K) : nullptr;
+  T* __restrict__ qgp = want_q ? static_cast<T*>(a.qgs) + (c * HV + j) * (int64_t)(kQgsTiles * C * K) : nullptr;
 #pragma unroll
   for (int i = 0; i < NKP; ++i) {
     const int idx = tid + NT * i, t = idx / CPR, d8 = (idx % CPR) * 8;
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
       if (qgp != nullptr) {
         const SplitFrag<T> sp = SplitFrag<T>::make(qr[i].f32() * ex * (a.scale * rq[i]));
         st8(qgp + t * K + d8, sp.hi);
-        st8(qgp + (C + t) * K + d8, sp.lo);
+        if constexpr (kQgsTiles == 2) st8(qgp + (C + t) * K + d8, sp.lo);
       }
     }
   }

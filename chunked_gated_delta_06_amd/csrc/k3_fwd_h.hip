@@ -349,12 +349,12 @@ struct K3S {
   static constexpr int NDH = (BV * K / 8 + NTL - 1) / NTL;   // staged h pieces per loader thread
   static constexpr int NDV = (BV * C / 8 + NTL - 1) / NTL;   // staged e pieces per loader thread
   // fused output: the loaders also stage each chunk's q tile and gates, or
-  // (per-channel gate) the gated queries as a hi + lo pair of tiles and the
-  // intra attention aqk (fp32 rows)
+  // (per-channel gate) the gated query tile(s) and the intra attention aqk
+  // (fp32 rows)
   static constexpr bool OUT = NWO > 0;
   static constexpr bool PCO = OUT && PC;
   static constexpr int QP = K + (sizeof(T) == 2 ? 32 : 16) / sizeof(T);   // staged q rows, padded as h
-  static constexpr int NQT = PCO ? 2 : 1;       // staged query tiles
+  static constexpr int NQT = PCO ? kQgsTiles : 1;   // staged query tiles
   static constexpr int AP = C + 4;              // staged aqk rows
   static constexpr int NLA = PCO ? (C * C / 4 + NTL - 1) / NTL : 1;   // float4 pieces of aqk per loader thread
   static constexpr size_t q_bytes =
@@ -401,14 +401,14 @@ struct K3S {
 // PC: per-channel gate, with the chunk's gated keys exp(G_L - G_t) k^_t and
 // decay exp(G_L) from the WY stage in place of the raw keys and the token
 // factors: S <- diag(exp(G_L)) S + Kt^T e.  With output waves as well (bf16),
-// o = (scale exp(G) q^) h + aqk e from the gated query pair and aqk of the
+// o = (scale exp(G) q^) h + aqk e from the gated queries and aqk of the
 // fused per-channel K1 + K2, so the output waves apply no gate factor
 // themselves.
 template <typename T, int C, int K, int NWC, int NWL, int NWO, bool KEEP = true, bool ZU = false, typename UT = T,
           bool PC = false>
 __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   using Cfg = K3S<T, C, K, NWC, NWL, NWO, UT, PC>;
-  static_assert(!PC || NWO == 0 || sizeof(T) == 2, "the per-channel fused output stages bf16 query pairs");
+  static_assert(!PC || NWO == 0 || sizeof(T) == 2, "the per-channel fused output takes bf16 gated queries");
   using Regs = typename Cfg::Regs;
   constexpr int NTL = Cfg::NTL, BV = Cfg::BV, NE = Cfg::NE, NS = Cfg::NS, KSK = Cfg::KSK, KSC = Cfg::KSC;
   constexpr int CPR = Cfg::CPR, NLD = Cfg::NLD, NLU = Cfg::NLU, NKS = Cfg::NKS, NPW = Cfg::NPW, NPU = Cfg::NPU;
@@ -472,9 +472,9 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       R.w[i] = ld8(wp + 8 * (in ? idx : 0));
       if constexpr (OUT && PC) {
         // the chunk's gated query tiles (hi, then lo), zero past L
-        const T* qs = static_cast<const T*>(a.qgs) + (c * HV + j) * (int64_t)(2 * C * K);
+        const T* qs = static_cast<const T*>(a.qgs) + (c * HV + j) * (int64_t)(kQgsTiles * C * K);
         R.q[i] = ld8(qs + 8 * (in ? idx : 0));
-        R.q[NLD + i] = ld8(qs + C * K + 8 * (in ? idx : 0));
+        if constexpr (kQgsTiles == 2) R.q[NLD + i] = ld8(qs + C * K + 8 * (in ? idx : 0));
       } else if constexpr (OUT) {
         R.q[i] = ld8(static_cast<const T*>(a.q) + (R.t0 * H + h) * K + (tc * (int)(H * K) + d8));
       }
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         st8(&sm.k[b][t * KP + d8], t < R.L ? R.k[i] : frag_zero<T>());
         if constexpr (OUT && PC) {
           st8(&sm.q[b][t * QP + d8], R.q[i]);
-          st8(&sm.q[b][(C + t) * QP + d8], R.q[NLD + i]);
+          if constexpr (kQgsTiles == 2) st8(&sm.q[b][(C + t) * QP + d8], R.q[NLD + i]);
         } else if constexpr (OUT) {
           st8(&sm.q[b][t * QP + d8], t < R.L ? R.q[i] : frag_zero<T>());
         }
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       // operands of one chunk's output, carried from its P^T step to its o step
       struct ORegs {
         Frag<T> q[TPW][KSK];        // q rows of this wave's token blocks (per-channel: gated, hi part)
-        Frag<T> ql[PC ? TPW : 1][PC ? KSK : 1];   // per-channel: lo part of the gated rows
+        Frag<T> ql[PC && kQgsTiles == 2 ? TPW : 1][PC && kQgsTiles == 2 ? KSK : 1];   // lo part of a gated-row pair
         SplitFrag<T> f[TPW][KSC];   // P^T as the chained B operand
         float isc[TPW];             // scale exp(G_r) / |q_r| (scalar gate)
       };
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       // most 1).  |q_r|^2 is the diagonal of the block's Q Q^T product, and the
       // output scale rides on the row factors.  A column r >= L of P^T only
       // reaches row r of o, which is never stored.
-      // Per-channel gate: the gated query pair and the aqk rows come staged,
+      // Per-channel gate: the gated query rows and the aqk rows come staged,
       // so the phase only reads them into operand registers (aqk rows are zero
       // above the diagonal and past L).
       auto pphase_pc = [&](ORegs& P, int x) {
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) {
             P.q[m][ks] = ld8(&sm.q[b][rr * QP + 32 * ks + 8 * g4]);
-            P.ql[m][ks] = ld8(&sm.q[b][(C + rr) * QP + 32 * ks + 8 * g4]);
+            if constexpr (kQgsTiles == 2) P.ql[m][ks] = ld8(&sm.q[b][(C + rr) * QP + 32 * ks + 8 * g4]);
           }
           const float* prow = &sm.pa[b][rr * AP];
 #pragma unroll
@@ -807,7 +807,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
 #pragma unroll
             for (int ks = 0; ks < KSK; ++ks) {
               mma(acc, hf[ks], P.q[m][ks]);
-              if constexpr (PC) mma(acc, hf[ks], P.ql[m][ks]);
+              if constexpr (PC && kQgsTiles == 2) mma(acc, hf[ks], P.ql[m][ks]);
             }
             if constexpr (!PC) acc *= P.isc[m];
 #pragma unroll
@@ -1161,7 +1161,7 @@ hipError_t launch_fused_k(const Args& a, hipStream_t s) {
 
 // ---- fused state scan + output, per-channel gate (bf16, chunk 32): the
 // per-channel scan's compute and loader waves (u in fp32) plus 2 output waves
-// on the aqk and gated query pair of the fused per-channel K1 + K2.  64 value columns (4 compute waves)
+// on the aqk and gated queries of the fused per-channel K1 + K2.  64 value columns (4 compute waves)
 // per workgroup when that grid still gives every compute unit a workgroup,
 // else 32.
 template <typename T, int C, int K>

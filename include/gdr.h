@@ -109,8 +109,8 @@ typedef struct {
  *   Tm         dtype [NT_max][HV][C][C]   (I + A)^-1 of each chunk, row-major
  *   w          dtype [NT_max][HV][C][K]   WY keys, token-major
  *   u          f32   [NT_max][HV][V][C]   WY values, transposed per chunk, as gdr_fwd_wy
- *                                         writes them (fp32 for every dtype); the fused
- *                                         stage gdr_fwd_kkt_wy writes them in `dtype`
+ *                                         writes them (fp32 for every dtype); in the
+ *                                         fused forwards' layouts (kinds 1 and 2) in `dtype`
  *   h          dtype [NT_max][HV][V][K]   state entering each chunk, transposed (h^T)
  *   v_new      dtype [NT_max][HV][V][C]   corrected values e, transposed per chunk
  *   kscale     f32   [NT_max][HV][3C + 4] scalar gate only, per chunk token factors:
@@ -128,10 +128,9 @@ typedef struct {
  *                                         t <= r (the Q K^T o M term of the chunk form's
  *                                         output, coverage-matrix page, section 2), zero
  *                                         above the diagonal and in rows past L
- *   qgs        dtype [NT_max][HV][2][C][K] per-channel fused forward only (fused K1 + K2):
- *                                         the gated queries scale exp(G_t) q^_t as a bf16
- *                                         hi tile then a lo tile (hi + lo = the fp32 value
- *                                         to about 16 mantissa bits)
+ *   qgs        dtype [NT_max][HV][C][K] per-channel fused forward only (fused K1 + K2):
+ *                                         the gated queries scale exp(G_t) q^_t, the
+ *                                         output's inter-term operand
  * Rows past the end of a partial chunk hold zeros. */
 typedef struct {
   int64_t nt_max;

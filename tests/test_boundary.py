@@ -108,7 +108,7 @@ def test_workspace_layout():
     assert pc.dl - pc.kt >= nt * HV * C * K * 2 and pc.total - pc.dl >= nt * HV * K * 4
     assert lay.kt == lay.dl == lay.total and f.kt == f.dl == f.total
     # per-channel gate, bf16, chunk 32, K <= 128: the per-channel fused scan + output, so no
-    # Tm / h / v_new, and the fused K1 + K2's aqk and gated query pair for it
+    # Tm / h / v_new, and the fused K1 + K2's aqk and gated queries for it
     p32 = problem(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1, chunk_size=32)
     assert gdr.lib().gdr_chunk_fwd_fused(ctypes.byref(p32)) == 2
     q = gdr.fwd_layout(p32)
@@ -118,7 +118,7 @@ def test_workspace_layout():
     assert q.h == q.v_new == q.kscale == q.kt and q.Tm == q.w
     assert n32 * HV * V * 32 * 2 <= q.h - q.u < n32 * HV * V * 32 * 4     # u in the input dtype
     assert q.dl - q.kt >= n32 * HV * 32 * K * 2 and q.aqk - q.dl >= n32 * HV * K * 4
-    assert q.qgs - q.aqk >= n32 * HV * 32 * 32 * 4 and q.total - q.qgs >= n32 * HV * 2 * 32 * K * 2
+    assert q.qgs - q.aqk >= n32 * HV * 32 * 32 * 4 and q.total - q.qgs >= n32 * HV * 32 * K * 2
     for kw in (dict(keep_states=1), dict(dtype=gdr.GDR_FP32), dict(K=256), dict(chunk_size=64)):
         other = problem(**{**dict(B=4, T=4096, H=16, HV=16, K=128, V=128, N=4, gate_per_channel=1,
                                   chunk_size=32), **kw})

@@ -115,7 +115,7 @@ PC_FUSED_CASES = [
 @pytest.mark.parametrize("cfg", PC_FUSED_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
 def test_per_channel_fused_forward_intermediates(cfg):
     """Per-channel gate, bf16, chunk 32: the default forward runs the fused
-    K1 + K2 (w, u, the scan's kt / dl, aqk and the gated query pair qgs) and
+    K1 + K2 (w, u, the scan's kt / dl, aqk and the gated queries qgs) and
     the per-channel fused scan + output.  Each of those regions against the
     oracle's per-chunk operands, Tm / h / v_new absent, o / ht against the
     oracle, on a ragged dense batch with slow decay and h0."""
@@ -126,9 +126,11 @@ def test_per_channel_fused_forward_intermediates(cfg):
     ro, rht, it = oracle_fwd(inp, intermediates=True)
     NT = int(it["off"][-1])
     assert ws["Tm"] is None and ws["h"] is None and ws["v_new"] is None
-    # aqk and the hi + lo query pair carry ~16 mantissa bits
+    # aqk carries ~16 mantissa bits (hi + lo operands); the gated queries are
+    # one bf16 rounding (or a hi + lo pair)
     check("aqk", f64(ws["aqk"][:NT]), it["QK"], 1e-4)
-    check("qgs", f64(ws["qgs"][:NT, :, 0]) + f64(ws["qgs"][:NT, :, 1]), it["QG"], 1e-4)
+    qg_tol = 1e-4 if ws["qgs"].shape[2] == 2 else 2e-3
+    check("qgs", f64(ws["qgs"][:NT]).sum(2), it["QG"], qg_tol)
     check("kt", f64(ws["kt"][:NT]), it["KT"], TOL["bf16"])
     check("dl", f64(ws["dl"][:NT]), it["DL"], 1e-5)
     check("w", f64(ws["w"][:NT]), it["W"], TOL["bf16"])
