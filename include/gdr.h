@@ -79,10 +79,11 @@ typedef struct {
   int32_t use_qk_l2norm;     /* 1: normalise q, k rows in the kernels */
   int32_t dtype;             /* gdr_dtype */
   float scale;               /* output scale */
-  int32_t keep_states;       /* gdr_chunk_fwd: 1 = run the separate K1..K4 stages and leave
-                                Tm, h and v_new in the workspace; 0 = use the fused stages
-                                where gdr_chunk_fwd_fused reports them (h and v_new, and
-                                with a scalar gate Tm, are then not written).
+  int32_t keep_states;       /* gdr_chunk_fwd: 1 = leave Tm, h, v_new and an fp32 u in the
+                                workspace (fused stages that also store them where the
+                                shape has them, else the separate K1..K4 stages); 0 = use
+                                the fused stages where gdr_chunk_fwd_fused reports them
+                                (Tm, h and v_new are then not written).
                                 gdr_chunk_bwd: 1 = take those intermediates
                                 from its workspace instead of recomputing them (see
                                 gdr_chunk_bwd) */
@@ -97,10 +98,11 @@ typedef struct {
  * batch and floor(T / C) + N for a varlen batch.  When the forward takes the
  * fused stages (keep_states = 0 and gdr_chunk_fwd_fused(p) != 0), the layout is
  * the compact one those stages use: Tm, h and v_new get no bytes (their
- * offsets equal the next region's); with a scalar gate (kind 1) u is in
- * `dtype`; with a per-channel gate (kind 2) u stays fp32 and the kt, dl, aqk
- * and qgs regions below get bytes.  Regions a layout does not use have no
- * bytes.
+ * offsets equal the next region's) and u is in `dtype`; with a per-channel
+ * gate (kind 2) the kt, dl, aqk and qgs regions below get bytes.  The
+ * kept-states layout of a per-channel chunk-32 bf16 problem with K <= 128
+ * keeps aqk and qgs too (its forward runs the same fused stages).  Regions a
+ * layout does not use have no bytes.
  *   chunk_idx  int32 [NT_max][4]   (sequence, first token (flattened), length, chunk-in-sequence)
  *   chunk_off  int32 [N + 1]       first chunk of each sequence; chunk_off[N] = NT
  *   seq_order  int32 [N]           varlen batches of at most 1024 sequences: the sequences
@@ -198,6 +200,10 @@ gdr_status gdr_fwd_workspace_layout(const gdr_problem* p, gdr_fwd_layout* layout
  *    stage that also writes kt, dl, aqk and qgs (layout above), and K3 and K4
  *    as one fused scan + output stage that reads them, so Tm, h and v_new are
  *    not written; gdr_chunk_fwd_fused(p) returns 2 exactly then (0 otherwise).
+ * With keep_states == 1 the same fused stages run where the shape has them,
+ * writing Tm, an fp32 u, h and v_new as well (the scalar gate's kept-states
+ * fused K1 + K2; the scan + output storing its staged h and e), else the
+ * separate stages.
  *   q, k  dtype [B,T,H,K]      v  dtype [B,T,HV,V]
  *   g     f32 [B,T,HV] (or [B,T,HV,K] when gate_per_channel)   beta f32 [B,T,HV]
  *   cu_seqlens  int32 [N+1] device, or NULL for a dense batch
