@@ -632,9 +632,14 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
   if (outw) {
     if constexpr (OUT) {
       constexpr int NB = C / 16;                 // token blocks of a chunk
-      constexpr int TPW = NB / NWO;              // token blocks per output wave (1 or 2)
-      constexpr int NVB = BV / 16;               // value blocks of the workgroup
-      static_assert(TPW >= 1 && TPW <= 2 && TPW * NWO == NB, "output-wave token split");
+      // Output waves split the chunk's token blocks into NTS groups and, when
+      // there are more waves than token blocks, the value columns into NCS parts.
+      constexpr int NTS = NWO < NB ? NWO : NB;
+      constexpr int NCS = NWO / NTS;
+      constexpr int TPW = NB / NTS;              // token blocks per output wave (1 or 2)
+      constexpr int NVW = BV / 16 / NCS;         // value blocks per output wave
+      static_assert(TPW >= 1 && TPW <= 2 && TPW * NTS == NB && NTS * NCS == NWO && NVW * NCS * 16 == BV,
+                    "output-wave token / column split");
       // The wave index is a compile-time constant inside `run` (one
       // instantiation per output wave, selected by a scalar branch): every
       // causal-block condition below folds away, so the loops unroll without
@@ -643,8 +648,10 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
       // a vector register it would become a lane mask, which an MFMA ignores.)
       auto run = [&](auto owc) {
       constexpr int OW = decltype(owc)::value;
-      // token blocks {OW, NB - 1 - OW}: equal causal work for both waves
-      constexpr int TB0 = OW, TB1 = NB - 1 - OW;
+      constexpr int OT = OW % NTS, OC = OW / NTS;   // token group, column part
+      constexpr int VB0 = OC * NVW;                 // first value block of the wave
+      // token blocks {OT, NB - 1 - OT}: equal causal work for both groups
+      constexpr int TB0 = OT, TB1 = NB - 1 - OT;
       auto tbk = [](int m) constexpr { return m == 0 ? TB0 : TB1; };
       constexpr int tbmax = TPW == 1 ? TB0 : TB1;
       T* __restrict__ op = static_cast<T*>(a.o);
@@ -775,14 +782,16 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         const int L = chunk_L(x);
         const T* hsb = sm.hs[x & 1];
         const T* esb = sm.es[x & 1];
-        // kept states with a per-channel gate: output wave 0 stores the staged
-        // h^T rows and wave 1 the e^T rows as it reads them (the loaders'
-        // registers have no room for the stores there)
-        constexpr bool KEEP_H = PC && KEEP && OW == 0, KEEP_E = PC && KEEP && OW == 1;
+        // kept states with a per-channel gate: the waves of token group 0 store
+        // the staged h^T rows of their value blocks and those of group 1 the
+        // e^T rows, as they read them (the loaders' registers have no room for
+        // the stores there)
+        constexpr bool KEEP_H = PC && KEEP && OT == 0, KEEP_E = PC && KEEP && OT == 1;
         const int64_t cx = c_begin + x;
-        f32x4 O[TPW][NVB];
+        f32x4 O[TPW][NVW];
 #pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
+        for (int vw_ = 0; vw_ < NVW; ++vw_) {
+          const int vb = VB0 + vw_;
           Frag<T> hf[KSK];
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) hf[ks] = ld8(&hsb[(16 * vb + r16) * HSP + 32 * ks + 8 * g4]);
@@ -815,20 +824,20 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
               if (2 * kt > tbk(m)) continue;
               mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), P.f[m][kt]);
             }
-            O[m][vb] = acc;
+            O[m][vw_] = acc;
           }
         }
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
           const int rr = 16 * tbk(m) + r16;
-          T* orow = op + ((t0 + rr) * HV + j) * V + vw;
+          T* orow = op + ((t0 + rr) * HV + j) * V + vw + 16 * VB0;
           if (rr < L) {
-            if constexpr (NVB % 2 == 0) {
+            if constexpr (NVW % 2 == 0) {
 #pragma unroll
-              for (int pb = 0; pb < NVB / 2; ++pb) st_pair(orow + 32 * pb, O[m][2 * pb], O[m][2 * pb + 1], lane);
+              for (int pb = 0; pb < NVW / 2; ++pb) st_pair(orow + 32 * pb, O[m][2 * pb], O[m][2 * pb + 1], lane);
             } else {
 #pragma unroll
-              for (int vb = 0; vb < NVB; ++vb) st4(orow + 16 * vb + 4 * g4, O[m][vb]);
+              for (int vb = 0; vb < NVW; ++vb) st4(orow + 16 * vb + 4 * g4, O[m][vb]);
             }
           }
         }
@@ -852,10 +861,24 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         if (nsteps == nc) ophase(P, nc - 1);
       }
       };
-      if (__builtin_amdgcn_readfirstlane(oi) == 0) {
-        run(std::integral_constant<int, 0>{});
+      const int oiu = __builtin_amdgcn_readfirstlane(oi);
+      if constexpr (NWO == 2) {
+        if (oiu == 0) {
+          run(std::integral_constant<int, 0>{});
+        } else {
+          run(std::integral_constant<int, 1>{});
+        }
       } else {
-        run(std::integral_constant<int, 1>{});
+        static_assert(NWO == 4, "two or four output waves");
+        if (oiu == 0) {
+          run(std::integral_constant<int, 0>{});
+        } else if (oiu == 1) {
+          run(std::integral_constant<int, 1>{});
+        } else if (oiu == 2) {
+          run(std::integral_constant<int, 2>{});
+        } else {
+          run(std::integral_constant<int, 3>{});
+        }
       }
     }
     return;
@@ -1160,14 +1183,15 @@ hipError_t launch_fused_k(const Args& a, hipStream_t s) {
 }
 
 // ---- fused state scan + output, per-channel gate (bf16, chunk 32): the
-// per-channel scan's compute and loader waves (u in fp32) plus 2 output waves
-// on the aqk and gated queries of the fused per-channel K1 + K2.  64 value columns (4 compute waves)
-// per workgroup when that grid still gives every compute unit a workgroup,
-// else 32.
+// per-channel scan's compute and loader waves plus output waves on the aqk and
+// gated queries of the fused per-channel K1 + K2.  64 value columns (4 compute
+// waves, and 4 output waves that split the chunk's two token blocks and the
+// columns in halves) per workgroup when that grid still gives every compute
+// unit a workgroup, else 32 (2 compute and 2 output waves).
 template <typename T, int C, int K>
 constexpr bool pc_out_ok() {
   constexpr int NWL = scan_loaders<T, C, K, float>();
-  return sizeof(T) == 2 && C == 32 && K <= 128 && K3S<T, C, K, 4, NWL, 2, float, true>::fits_out &&
+  return sizeof(T) == 2 && C == 32 && K <= 128 && K3S<T, C, K, 4, NWL, 4, float, true>::fits_out &&
          K3S<T, C, K, 2, NWL, 2, float, true>::fits_out;
 }
 
@@ -1180,8 +1204,8 @@ hipError_t launch_pc_out_t(const Args& a, hipStream_t s) {
     constexpr int NWL = scan_loaders<T, C, K, float>();
     const int64_t nblk64 = a.N * a.HV * (a.V / 64);
     if (a.V % 64 == 0 && nblk64 >= kNumCUs) {
-      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 2, KEEP, false, UT, true>), dim3((unsigned)nblk64),
-                         dim3(64 * (6 + NWL)), 0, s, a);
+      hipLaunchKernelGGL((k3_scan<T, C, K, 4, NWL, 4, KEEP, false, UT, true>), dim3((unsigned)nblk64),
+                         dim3(64 * (8 + NWL)), 0, s, a);
     } else {
       hipLaunchKernelGGL((k3_scan<T, C, K, 2, NWL, 2, KEEP, false, UT, true>),
                          dim3((unsigned)(a.N * a.HV * (a.V / 32))), dim3(64 * (4 + NWL)), 0, s, a);

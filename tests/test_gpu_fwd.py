@@ -670,6 +670,26 @@ def test_per_channel_scan_four_wave_grid(dtype):
     check("ht", f64(ht), rht, TOL[dtype])
 
 
+def test_per_channel_fused_four_wave_grid_kept_states():
+    """The per-channel fused scan + output on its four-compute-wave grid
+    (N * HV * V / 64 = 256, bf16, chunk 32), whose four output waves split the
+    chunk's token blocks and the 64 value columns: o and ht, and with kept
+    states the h and v_new tiles those output waves store, against the oracle
+    on a ragged GVA batch."""
+    w, inp = mk(B=2, T=77, H=8, HV=64, K=64, V=128, C=32, pc=True, slow=True, scale=0.5)
+    p = gdr.make_problem(inp["q"], inp["v"], inp["g"], chunk_size=32, use_qk_l2norm=True)
+    assert gdr.chunk_fwd_fused(p) == 2
+    ro, rht, it = oracle_fwd(inp, intermediates=True)
+    NT = int(it["off"][-1])
+    for keep in (False, True):
+        o, ht, ws = gpu_fwd(inp, keep_states=keep)
+        check(f"o (keep {keep})", f64(o), ro, TOL["bf16"])
+        check(f"ht (keep {keep})", f64(ht), rht, TOL["bf16"])
+        if keep:
+            check("h", f64(ws["h"][:NT]).transpose(0, 1, 3, 2), it["h"], TOL["bf16"])
+            check("v_new", f64(ws["v_new"][:NT]).transpose(0, 1, 3, 2), it["E"], TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_per_channel_scan_four_wave_grid_k32(dtype):
     """Per-channel gate, K = 32 at chunk 32 on a four-wave grid (B = 2, HV = 32,
