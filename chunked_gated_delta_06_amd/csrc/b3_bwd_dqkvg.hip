@@ -196,7 +196,10 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       R.t[i] = (idx < C * C / 8) ? ld8(tp + 8 * idx) : frag_zero<T>();
     }
     R.g = (tid < L) ? a.g[(t0 + tid) * HV + j] : 0.f;
-    R.b = (tid < L) ? beta_value(a.beta[(t0 + tid) * HV + j], a.beta_logits) : 0.f;
+    // raw beta (or logit): the sigmoid is taken where the row is staged, so
+    // no instruction needs the loaded value (and waits for it and for every
+    // load issued before it) while the fetch is in flight
+    R.b = (tid < L) ? a.beta[(t0 + tid) * HV + j] : 0.f;
   };
   auto fetch_tile = [&](TileRegs& R, const Item& I, int64_t j, int64_t v0) {
     const int64_t c = I.c, t0 = I.t0;
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     {
       const float G = wave_incl_scan(HR.g, lane);
       if (wv == 0 && lane < C) sG[lane] = G;
-      if (tid < C) sB[tid] = HR.b;
+      if (tid < C) sB[tid] = tid < L ? beta_value(HR.b, a.beta_logits) : 0.f;
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int idx = tid + NT * i, r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
@@ -730,8 +733,9 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       }
     }
   };
-  // the next item's rows, T tile, gate and beta are requested before this
-  // item's finish, which hides their latency
+  // the next item's rows, T tile, gate, beta and first value tile are
+  // requested before this item's finish, which hides their latency (the value
+  // tile's registers are free once this item's last tile is staged)
   const int64_t next = item + gridDim.x;
   const bool more = Cfg::template persistent<GVA>() && next < nitems;
   Item nx = cur;
@@ -739,6 +743,7 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     nx = item_at(next);
     fetch_qk(nx);
     fetch_head(HR, nx, nx.h * ng);
+    fetch_tile(TN, nx, nx.h * ng, 0);
   }
   if constexpr (GVA) {
     finish(sq_, sk_);
@@ -749,7 +754,6 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
   if (!more) break;
   item = next;
   cur = nx;
-  fetch_tile(TN, cur, cur.h * ng, 0);
   lds_barrier();      // the finish's LDS reads end before the next item's staging
   }   // items
   };

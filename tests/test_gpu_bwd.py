@@ -364,6 +364,23 @@ def test_beta_logits_mode():
     compare({n: f64(t) for n, t in zip(GRADS, grads)}, ref, TOL["bf16"])
 
 
+def test_beta_logits_persistent_backward():
+    """beta as logits on the backward's persistent grid (bf16, chunk 64,
+    K = 128, H = HV: one workgroup per compute unit looping over 260 (chunk,
+    head) items, each fetching the next item's rows and beta during its own
+    finish), ragged tail; every gradient against the oracle on sigmoid(logits)."""
+    w, inp = mk(B=1, T=64 * 129 + 17, H=2, HV=2, K=128, V=128, slow=True)
+    x = torch.logit(inp["beta"])
+    b = torch.sigmoid(x.double())
+    d = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "do", "dht", "h0")}
+    grads = gdr.chunk_bwd(d["q"], d["k"], d["v"], d["g"], dev(x.contiguous()), d["do"], d["dht"],
+                          initial_state=d["h0"], use_qk_l2norm_in_kernel=True, beta_logits=True)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(dict(inp, beta=b))
+    ref["dbeta"] = ref["dbeta"] * (b * (1 - b)).numpy()
+    compare({n: f64(t) for n, t in zip(GRADS, grads)}, ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("cfg", [dict(B=2, T=512, H=2, HV=4, K=60, V=60),
                                  dict(B=1, T=130, H=1, HV=2, K=60, V=36, C=32, dtype="fp32"),
                                  dict(B=1, T=100, H=2, HV=2, K=100, V=20, C=32),
