@@ -381,6 +381,49 @@ def test_beta_logits_persistent_backward():
     compare({n: f64(t) for n, t in zip(GRADS, grads)}, ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("pc", [False, True], ids=["scalar", "per_channel"])
+def test_bwd_int64_offsets(pc):
+    """The backward on a varlen batch whose last sequence sits past 2^31
+    elements of q / k / v / do, of the gradients and of the per-chunk state
+    and state-gradient tensors (bf16, 16 heads; scalar gate at chunk 64 on the
+    persistent B3, per-channel gate at chunk 32); only that sequence's
+    gradients are checked, against the oracle on it alone."""
+    H = HV = 16
+    K = V = 128
+    tail = 192
+    s = (1 << 20) + 64          # the checked sequence starts past 2^31 elements
+    T = s + tail
+    assert s * H * K > 2 ** 31
+    gen = torch.Generator().manual_seed(5)
+    qt = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    kt = torch.randn(1, tail, H, K, generator=gen).bfloat16()
+    vt = torch.randn(1, tail, HV, V, generator=gen).bfloat16()
+    dot = torch.randn(1, tail, HV, V, generator=gen).bfloat16()
+    gw = (HV, K) if pc else (HV,)
+    C = 32 if pc else 64
+    gt = torch.nn.functional.logsigmoid(torch.randn(1, tail, *gw, generator=gen) + 4)
+    bt = torch.sigmoid(torch.randn(1, tail, HV, generator=gen))
+    h0 = 0.1 * torch.randn(2, HV, K, V, generator=gen)
+    dht = torch.randn(2, HV, K, V, generator=gen)
+
+    def full(x, width):
+        y = torch.zeros(1, T, *width, dtype=x.dtype, device="cuda")
+        y[:, s:] = x.cuda()
+        return y
+
+    cu = torch.tensor([0, s, T], dtype=torch.int32)
+    grads = gdr.chunk_bwd(full(qt, (H, K)), full(kt, (H, K)), full(vt, (HV, V)), full(gt, gw),
+                          full(bt, (HV,)), full(dot, (HV, V)), dev(dht), scale=1.0, chunk_size=C,
+                          cu_seqlens=dev(cu), initial_state=dev(h0), use_qk_l2norm_in_kernel=True)
+    torch.cuda.synchronize()
+    got = {n: f64(t[1:2] if n == "dh0" else t[:, s:]) for n, t in zip(GRADS, grads)}
+    del grads
+    torch.cuda.empty_cache()
+    sub = dict(q=qt, k=kt, v=vt, g=gt, beta=bt, do=dot, dht=dht[1:2], h0=h0[1:2], cu_seqlens=None,
+               scale=1.0, use_qk_l2norm=True, chunk_size=C)
+    compare(got, oracle_bwd(sub), TOL["bf16"])
+
+
 @pytest.mark.parametrize("cfg", [dict(B=2, T=512, H=2, HV=4, K=60, V=60),
                                  dict(B=1, T=130, H=1, HV=2, K=60, V=36, C=32, dtype="fp32"),
                                  dict(B=1, T=100, H=2, HV=2, K=100, V=20, C=32),
