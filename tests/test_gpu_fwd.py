@@ -503,31 +503,34 @@ def test_deterministic_and_nan_poison_and_canaries():
     assert (ws_full[:pad] == 0xFF).all() and (ws_full[pad + lay.total:] == 0xFF).all()
 
 
-def test_int64_offsets():
+@pytest.mark.parametrize("pc", [False, True], ids=["scalar", "per_channel"])
+def test_int64_offsets(pc):
     """A varlen batch whose last sequence sits past 2^31 elements of q / k / v
-    and of the per-chunk state tensor; only that sequence is checked."""
+    and of the per-chunk state tensor (per-channel gate: of g too, at chunk
+    32); only that sequence is checked."""
     H = HV = 16
     K = V = 128
     tail = 192
-    T_big = (1 << 20) + 64
+    T_big = (1 << 20) + 64 + tail       # the checked sequence starts past 2^31 elements
     lengths = [T_big - tail, tail]
     gen = torch.Generator().manual_seed(3)
     T = T_big
     q = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
     k = torch.zeros(1, T, H, K, dtype=torch.bfloat16)
     v = torch.zeros(1, T, HV, V, dtype=torch.bfloat16)
-    g = torch.zeros(1, T, HV)
+    gw = (HV, K) if pc else (HV,)
+    g = torch.zeros(1, T, *gw)
     beta = torch.zeros(1, T, HV)
     s = T - tail
     q[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
     k[:, s:] = torch.randn(1, tail, H, K, generator=gen).bfloat16()
     v[:, s:] = torch.randn(1, tail, HV, V, generator=gen).bfloat16()
-    g[:, s:] = torch.nn.functional.logsigmoid(torch.randn(1, tail, HV, generator=gen) + 4)
+    g[:, s:] = torch.nn.functional.logsigmoid(torch.randn(1, tail, *gw, generator=gen) + 4)
     beta[:, s:] = torch.sigmoid(torch.randn(1, tail, HV, generator=gen))
     h0 = 0.1 * torch.randn(2, HV, K, V, generator=gen)
-    assert (T - 1) * H * K > 2 ** 31
+    assert s * H * K > 2 ** 31
     cu = torch.tensor([0, lengths[0], T], dtype=torch.int32)
-    inp = dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, scale=1.0, chunk_size=64,
+    inp = dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, cu_seqlens=cu, scale=1.0, chunk_size=32 if pc else 64,
                use_qk_l2norm=True)
     sub = dict(inp, cu_seqlens=None, h0=h0[1:2])
     for key in ("q", "k", "v", "g", "beta"):
