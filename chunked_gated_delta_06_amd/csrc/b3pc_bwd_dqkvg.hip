@@ -229,9 +229,21 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
   };
   for (int jj = 0; jj < ng; ++jj) {
     const int64_t j = h * ng + jj;
-    fetch_tile(j, 0);   // with this head's T, kt, gate and beta
-    // ---- per-head tiles: T, kt, the gate (cumsum below), beta
+    // ---- per-head tiles: the gate (cumsum below), beta, T, kt, then the
+    //      head's first value tile.  The gate pieces are requested first and
+    //      all at once, so staging them waits for nothing younger, and beta's
+    //      sigmoid is taken after the last request, so no instruction needs a
+    //      loaded value while the others are in flight.
     {
+      constexpr int NPG = (C * K / 4 + NT - 1) / NT;   // float4 gate pieces per thread
+      f32x4 gr[NPG];
+#pragma unroll
+      for (int i = 0; i < NPG; ++i) {
+        const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+        gr[i] = (idx < C * K / 4 && t < L) ? *reinterpret_cast<const f32x4*>(a.g + ((t0 + t) * HV + j) * K + d4)
+                                           : zero4();
+      }
+      const float braw = (tid < L) ? a.beta[(t0 + tid) * HV + j] : 0.f;
       const T* tp = static_cast<const T*>(a.Tm) + (c * HV + j) * (int64_t)(C * C);
       const T* ktp = static_cast<const T*>(a.kt) + (c * HV + j) * (int64_t)(C * K);
       Frag<T> tr[NPT], ktr[NPQ];
@@ -245,13 +257,16 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
         const int idx = tid + NT * i;
         ktr[i] = (idx < C * CPR) ? ld8(ktp + 8 * idx) : frag_zero<T>();
       }
-      for (int idx = tid; idx < C * K / 4; idx += NT) {
-        const int t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
-        const f32x4 gv = (t < L) ? *reinterpret_cast<const f32x4*>(a.g + ((t0 + t) * HV + j) * K + d4) : zero4();
+      fetch_tile(j, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sG[t * GP + d4 + e] = gv[e];
+      for (int i = 0; i < NPG; ++i) {
+        const int idx = tid + NT * i, t = idx / (K / 4), d4 = (idx % (K / 4)) * 4;
+        if (idx < C * K / 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sG[t * GP + d4 + e] = gr[i][e];
+        }
       }
-      const float bv = (tid < L) ? beta_value(a.beta[(t0 + tid) * HV + j], a.beta_logits) : 0.f;
+      const float bv = (tid < L) ? beta_value(braw, a.beta_logits) : 0.f;
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const int idx = tid + NT * i, r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
