@@ -342,6 +342,16 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
     lr = 0.f;
     lds_barrier();
     const float GL = sG[L - 1];
+    // dE's row factors kappa_t rk_t for the wave's rows t = 16 rb + 4 g4 + e
+    // (every dE slot of a wave has row block rb), formed once per head
+    f32x4 kapE;
+    {
+      const int t4 = 16 * rb + 4 * g4;
+      const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sG[t4]);
+      const f32x4 K4 = *reinterpret_cast<const f32x4*>(&sRk[t4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kapE[e] = (t4 + e < L) ? __expf(GL - G4[e]) * K4[e] : 0.f;
+    }
 
     // ---- P tile, P[r][t] (norms, gate, causal mask applied).  Slot i's block
     //      has key rows t in the wave's row block rb (tb = b % NRB = rb) and
@@ -408,13 +418,8 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
 #pragma unroll
         for (int ks = 0; ks < KSK; ++ks)
           mma_split(a2, ld8(&sK[(16 * tb + r16) * PK + 32 * ks + 8 * g4]), fDH.row(16 * vb + r16, 32 * ks, lane));
-        f32x4 dv4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * tb + 4 * g4 + e;
-          const float ks = (t < L) ? __expf(GL - sG[t]) * sRk[t] : 0.f;
-          dv4[e] = scale * a1[e] + ks * a2[e];
-        }
+        static_assert(NW % NRB == 0, "every dE slot of a wave has row block rb");
+        const f32x4 dv4 = scale * a1 + kapE * a2;
         fDE.put4(16 * vb + r16, 16 * tb + 4 * g4, dv4);
       }
       lds_barrier();
@@ -660,6 +665,8 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
       }
       const float y = wave_incl_scan(x, lane);
       if (lane < C && tr < L) a.dg[(t0 + tr) * HV + j] = y;
+    }
+    if (wv == 1) {      // dbeta beside wave 0's dg
       if (lane < L) {
         float db = 0.f;
 #pragma unroll
