@@ -95,8 +95,8 @@ struct B3P {
                               : (post_bytes > fin_bytes ? post_bytes : fin_bytes);
   static constexpr size_t oRows = oLoop + ((region + 15) & ~size_t(15));
   // rows: rq, rk, beta; per-wave dbeta, q.dq, k.dk partials; last-row column
-  // extras per row block; lr per feature
-  static constexpr size_t rows_floats = 3 * C + 3 * NW * C + NRB * K + K;
+  // extras per row block; lr per feature and its per-wave partials
+  static constexpr size_t rows_floats = 3 * C + 3 * NW * C + NRB * K + K + NW * K;
   static constexpr size_t total = oRows + rows_floats * 4;
   static constexpr bool fits = total <= 160 * 1024;
 };
@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
   float* sDotK = sDotQ + NW * C;       // [NW][C]
   float* sLast = sDotK + NW * C;       // [NRB][K]
   float* sLr = sLast + NRB * K;        // [K]
+  float* sLrW = sLr + K;               // [NW][K]
 
   const T* __restrict__ qp = static_cast<const T*>(a.q);
   const T* __restrict__ kp = static_cast<const T*>(a.k);
@@ -290,12 +291,12 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
 #pragma unroll
       for (int t = 0; t < C; ++t) sG[t * GP + d] = col[t];
     }
-    // sum_v S0[d][v] dS1[d][v] per feature, accumulated in the products phase
-    // by the waves of row block 0 (their slots cover every feature once):
-    // slot i, feature 16 db + r16, the 8 value rows of lane group g4
-    float lrp[SCK];
+    // sum_v S0[d][v] dS1[d][v] per feature, accumulated where the h and dh
+    // pieces are staged: a thread's pieces all hold features d8 .. d8 + 7
+    // (d8 = 8 (tid % CPR)), from the fp32 dh
+    float lr8[8];
 #pragma unroll
-    for (int i = 0; i < SCK; ++i) lrp[i] = 0.f;
+    for (int e = 0; e < 8; ++e) lr8[e] = 0.f;
 
     f32x4 dQg[SCK], TdW[SCK], dKt[SCK], dP = zero4(), dA = zero4();
 #pragma unroll
@@ -313,6 +314,9 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
             const Frag<T> hi = Frag<T>::make(fy);
             st8(&fDH.hi[v * PK + d8], hi);
             if constexpr (FTile<T>::kSplit) st8(&fDH.lo[v * PK + d8], Frag<T>::make(fy - hi.f32()));
+            const f32x8 hx = hr[i].f32();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lr8[e] += hx[e] * fy[e];
           }
         }
 #pragma unroll
@@ -374,11 +378,6 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
           mma(dQg[i], aO, bS);
           mma_split(TdW[i], aY, bS);
           mma_split(dKt[i], aE, bD);
-          if constexpr (rb == 0) {
-            const f32x8 hs = bS.f32(), ds = bD.hi.f32() + (FTile<T>::kSplit ? bD.lo.f32() : zero8());
-#pragma unroll
-            for (int e = 0; e < 8; ++e) lrp[i] += hs[e] * ds[e];
-          }
         }
         constexpr int cb = wv / NRB;
         const Frag<T> bE = lds_col8(sE, PCC, 0, 16 * cb, lane);
@@ -399,12 +398,18 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
         sDA[r * CP + t] = (t < r && r < L) ? -dA[e] : 0.f;
       }
     }
-    if constexpr (rb == 0) {
+    // lr: the lanes holding the same features are CPR apart in a wave; one
+    // partial per wave, summed in wave order below
 #pragma unroll
-      for (int i = 0; i < SCK; ++i) {
-        const float x = group4_sum(lrp[i]);
-        if (g4 == 0) sLr[16 * ((wv + NW * i) / NRB) + r16] = x;
-      }
+    for (int e = 0; e < 8; ++e) {
+      float x = lr8[e];
+#pragma unroll
+      for (int off = CPR; off < 64; off *= 2) x += __shfl_xor(x, off, 64);
+      lr8[e] = x;
+    }
+    if (lane < CPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sLrW[wv * K + 8 * lane + e] = lr8[e];
     }
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
@@ -412,6 +417,12 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
       TdW[i] = -TdW[i];
     }
     lds_barrier();
+    for (int d = tid; d < K; d += NT) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) x += sLrW[w * K + d];
+      sLr[d] = x;
+    }
 
     // ---- the gated pair sums.  With every 16-row block's gate span below
     //      kPairSpan they run on MFMA with a reference row per block: for the
