@@ -533,19 +533,28 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
     // ---- per element: dq^, dk^ (group sums), dG; dbeta row parts; last-row extras
     {
       f32x4 rowb = zero4();
+      // the wave's rows t = 16 rb + 4 g4 + e are the same in every slot: their
+      // factors in one 16-byte read each, the raw q / k values in one
+      // transposed read per slot
+      const int r4 = 16 * rb + 4 * g4;
+      const f32x4 B4 = *reinterpret_cast<const f32x4*>(&sB[r4]);
+      const f32x4 RK4 = *reinterpret_cast<const f32x4*>(&sRk[r4]);
+      const f32x4 RQ4 = *reinterpret_cast<const f32x4*>(&sRq[r4]);
 #pragma unroll
       for (int i = 0; i < SCK; ++i) {
-        const int d = 16 * ((wv + NW * i) / NRB) + r16;
+        const int db = (wv + NW * i) / NRB, d = 16 * db + r16;
         const float gl = sG[(L - 1) * GP + d];
+        const f32x4 K4 = lds_rows4(sK, PK, r4, 16 * db, lane) * RK4;
+        const f32x4 Q4 = lds_rows4(sQ, PK, r4, 16 * db, lane) * RQ4;
         float last = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 16 * rb + 4 * g4 + e;
+          const int t = r4 + e;
           const bool ok = t < L;
           const float gt = sG[t * GP + d];
           const float gam = ok ? __expf(gt) : 0.f, kap = ok ? __expf(gl - gt) : 0.f;
-          const float bt = sB[t];
-          const float kv = to_float(sK[t * PK + d]) * sRk[t], qv = to_float(sQ[t * PK + d]) * sRq[t];
+          const float bt = B4[e];
+          const float kv = K4[e], qv = Q4[e];
           const float dq = dqP[i][e] + gam * dQg[i][e];
           const float dk = bt * dkA1[i][e] + dkA2[i][e] + dkP[i][e] + bt * gam * TdW[i][e] + kap * dKt[i][e];
           const float dg = qv * dqP[i][e] - kv * dkP[i][e] + kv * bt * dkA1[i][e] - kv * dkA2[i][e] +
@@ -595,13 +604,9 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
     f32x4 qd = zero4(), kd = zero4();
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
-      const int d = 16 * ((wv + NW * i) / NRB) + r16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * g4 + e;
-        qd[e] += to_float(sQ[r * PK + d]) * sq_[i][e];
-        kd[e] += to_float(sK[r * PK + d]) * sk_[i][e];
-      }
+      const int db = (wv + NW * i) / NRB;
+      qd += lds_rows4(sQ, PK, 16 * rb + 4 * g4, 16 * db, lane) * sq_[i];
+      kd += lds_rows4(sK, PK, 16 * rb + 4 * g4, 16 * db, lane) * sk_[i];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -614,30 +619,34 @@ __global__ __launch_bounds__(256) void b3pc_bwd_dqkvg(Args a) {
     }
     lds_barrier();
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = 16 * rb + 4 * g4 + e;
-    float cq = 0.f, ck = 0.f;
-    const float rq = sRq[r], rk = sRk[r];
+  {
+    const int r4 = 16 * rb + 4 * g4;
+    const f32x4 rq = *reinterpret_cast<const f32x4*>(&sRq[r4]), rk = *reinterpret_cast<const f32x4*>(&sRk[r4]);
+    f32x4 cq = zero4(), ck = zero4();
     if (a.l2norm) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         if (w % NRB != rb) continue;
-        cq += sDotQ[w * C + r];
-        ck += sDotK[w * C + r];
+        cq += *reinterpret_cast<const f32x4*>(&sDotQ[w * C + r4]);
+        ck += *reinterpret_cast<const f32x4*>(&sDotK[w * C + r4]);
       }
       cq *= rq * rq;
       ck *= rk * rk;
     }
 #pragma unroll
     for (int i = 0; i < SCK; ++i) {
-      const int d = 16 * ((wv + NW * i) / NRB) + r16;
-      const float qv = to_float(sQ[r * PK + d]), kv = to_float(sK[r * PK + d]);
+      const int db = (wv + NW * i) / NRB, d = 16 * db + r16;
       // dq^ is with respect to q^ = q rq; with the norm off rq = 1
-      const float oq = a.l2norm ? rq * (sq_[i][e] - cq * qv) : sq_[i][e];
-      const float okv = a.l2norm ? rk * (sk_[i][e] - ck * kv) : sk_[i][e];
-      sOq[r * PK + d] = (T)oq;
-      sOk[r * PK + d] = (T)okv;
+      f32x4 oq = sq_[i], okv = sk_[i];
+      if (a.l2norm) {
+        oq = rq * (sq_[i] - cq * lds_rows4(sQ, PK, r4, 16 * db, lane));
+        okv = rk * (sk_[i] - ck * lds_rows4(sK, PK, r4, 16 * db, lane));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sOq[(r4 + e) * PK + d] = (T)oq[e];
+        sOk[(r4 + e) * PK + d] = (T)okv[e];
+      }
     }
   }
   lds_barrier();
