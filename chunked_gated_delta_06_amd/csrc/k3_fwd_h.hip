@@ -790,8 +790,8 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
         const int64_t cx = c_begin + x;
         f32x4 O[TPW][NVW];
 #pragma unroll
-        for (int vw_ = 0; vw_ < NVW; ++vw_) {
-          const int vb = VB0 + vw_;
+        for (int ib = 0; ib < NVW; ++ib) {
+          const int vb = VB0 + ib;
           Frag<T> hf[KSK];
 #pragma unroll
           for (int ks = 0; ks < KSK; ++ks) hf[ks] = ld8(&hsb[(16 * vb + r16) * HSP + 32 * ks + 8 * g4]);
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(64 * (NWC + NWO + NWL)) void k3_scan(Args a) {
               if (2 * kt > tbk(m)) continue;
               mma_split(acc, ld_chain(erow + 32 * kt + 4 * g4, erow + 32 * kt + 16 + 4 * g4), P.f[m][kt]);
             }
-            O[m][vw_] = acc;
+            O[m][ib] = acc;
           }
         }
 #pragma unroll
