@@ -73,7 +73,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && !KEEP ? 4 : 1) void k12_kkt_
   T* const sV = reinterpret_cast<T*>(sVM);
   float* const sM = reinterpret_cast<float*>(sVM);
   auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * MB; };
-  __shared__ float sS[C], sB[C], sRn[C], sG[C];
+  __shared__ __attribute__((aligned(16))) float sS[C];
+  __shared__ __attribute__((aligned(16))) float sB[C];
+  __shared__ __attribute__((aligned(16))) float sRn[C];
+  __shared__ __attribute__((aligned(16))) float sG[C];
 
   // the wave index is read into a scalar register, so every per-wave choice
   // below is a scalar branch around whole MFMA sequences
@@ -180,10 +183,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && !KEEP ? 4 : 1) void k12_kkt_
         const Frag<T> fb = Frag<T>::raw(*reinterpret_cast<const v8_t<T>*>(&sK[(16 * cb + r16) * KP + 32 * ks + 8 * g4]));
         mma(s, fa, fb);
       }
+      // the block's rows r = 16 rb + 4 g4 + i: their factors in one 16-byte
+      // read each; the column's once
+      const int r4 = 16 * rb + 4 * g4, cc = 16 * cb + r16;
+      const f32x4 B4 = *reinterpret_cast<const f32x4*>(&sB[r4]);
+      const f32x4 N4 = *reinterpret_cast<const f32x4*>(&sRn[r4]);
+      const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sG[r4]);
+      const float nc = sRn[cc], gc = sG[cc];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + 4 * g4 + i, cc = 16 * cb + r16;
-        const float val = (!a.gla && cc < r && r < L) ? sB[r] * s[i] * sRn[r] * sRn[cc] * __expf(sG[r] - sG[cc]) : 0.f;
+        const int r = r4 + i;
+        const float val = (!a.gla && cc < r && r < L) ? B4[i] * s[i] * N4[i] * nc * __expf(G4[i] - gc) : 0.f;
         sM[blk(rb, cb) + (4 * g4 + i) * MP + r16] = val;
       }
     }
