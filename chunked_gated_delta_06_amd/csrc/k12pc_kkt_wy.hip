@@ -88,7 +88,10 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
   float* const sGc = reinterpret_cast<float*>(sGV);
   T* const sV = reinterpret_cast<T*>(sGV);
   __shared__ __attribute__((aligned(16))) float sM[NLB * MB];
-  __shared__ float sB[C], sRn[C], sRq[C], sS[C];
+  __shared__ __attribute__((aligned(16))) float sB[C];
+  __shared__ __attribute__((aligned(16))) float sRn[C];
+  __shared__ __attribute__((aligned(16))) float sRq[C];
+  __shared__ __attribute__((aligned(16))) float sS[C];
   auto blk = [](int rb, int cb) { return (rb * (rb + 1) / 2 + cb) * MB; };
 
   const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, g4 = lane >> 4;
@@ -276,20 +279,28 @@ __global__ __launch_bounds__(256) void k12pc_kkt_wy(Args a) {
           sqk[i] = sq;
         }
       }
-      // A (strictly lower, fp32) into LDS
+      // A (strictly lower, fp32) into LDS; the factors of the lane's four
+      // consecutive rows in one 16-byte read each, the column's once
+      {
+        const int r4 = 16 * rb + 4 * g4, cc = 16 * cb + r16;
+        const f32x4 B4 = *reinterpret_cast<const f32x4*>(&sB[r4]);
+        const f32x4 N4 = *reinterpret_cast<const f32x4*>(&sRn[r4]);
+        const float nc = sRn[cc];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rb + 4 * g4 + i, cc = 16 * cb + r16;
-        sM[blk(rb, cb) + (4 * g4 + i) * MP + r16] = (cc < r && r < L) ? sB[r] * s[i] * sRn[r] * sRn[cc] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int r = r4 + i;
+          sM[blk(rb, cb) + (4 * g4 + i) * MP + r16] = (cc < r && r < L) ? B4[i] * s[i] * N4[i] * nc : 0.f;
+        }
       }
       // aqk row ra: scale / (|q_r| |k_t|) on t <= r < L
       if (want_q) {
         const float fr = (ra < L) ? a.scale * sRq[ra] : 0.f;
+        const f32x4 T4 = *reinterpret_cast<const f32x4*>(&sRn[16 * cb + 4 * g4]);
         f32x4 o4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tc = 16 * cb + 4 * g4 + i;
-          o4[i] = tc <= ra ? sqk[i] * fr * sRn[tc] : 0.f;
+          o4[i] = tc <= ra ? sqk[i] * fr * T4[i] : 0.f;
         }
         *reinterpret_cast<f32x4*>(a.aqk + (c * HV + j) * (int64_t)(C * C) + ra * C + 16 * cb + 4 * g4) = o4;
       }
