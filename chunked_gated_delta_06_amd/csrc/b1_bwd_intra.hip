@@ -42,7 +42,9 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
   constexpr int NPD = VT * C / 8 / NT;            // 8-element dO pieces per thread (= 1)
   constexpr int NPK = (C * CPR + NT - 1) / NT;     // 8-element q / k pieces per thread
   static_assert(NPD * NT * 8 == VT * C, "dO tile pieces");
-  __shared__ float sG[C], sRq[C], sRk[C];
+  __shared__ __attribute__((aligned(16))) float sG[C];
+  __shared__ __attribute__((aligned(16))) float sRq[C];
+  __shared__ __attribute__((aligned(16))) float sRk[C];
   __shared__ __attribute__((aligned(16))) T sDO[C * DP];
   __shared__ __attribute__((aligned(16))) T sQ[C * KP];
   __shared__ __attribute__((aligned(16))) T sK[C * KP];
@@ -130,10 +132,13 @@ __global__ __launch_bounds__(C * 4) void b1_bwd_intra(Args a) {
 #pragma unroll
     for (int ks = 0; ks < KSK; ++ks)
       mma(Pa[rb], ld8(&sQ[(16 * rb + r16) * KP + 32 * ks + 8 * g4]), ld8(&sK[tt * KP + 32 * ks + 8 * g4]));
+    // the factors of the lane's four consecutive rows in one 16-byte read each
+    const f32x4 Rq4 = *reinterpret_cast<const f32x4*>(&sRq[16 * rb + 4 * g4]);
+    const f32x4 G4 = *reinterpret_cast<const f32x4*>(&sG[16 * rb + 4 * g4]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * rb + 4 * g4 + i;
-      Pa[rb][i] *= (tt <= r && r < L) ? sRq[r] * rkt * __expf(sG[r] - Gt) : 0.f;
+      Pa[rb][i] *= (tt <= r && r < L) ? Rq4[i] * rkt * __expf(G4[i] - Gt) : 0.f;
     }
   }
   // P^T rows t as A operands over the chained r map, as hi + lo pairs
