@@ -722,10 +722,26 @@ __global__ __launch_bounds__(64 * NW) void b3_bwd_dqkvg(Args a) {
         oq = rq * (DQ[i] - cq * lds_rows4(sQ, PK, r4, 16 * db, lane));
         okv = rk * (DK[i] - ck * lds_rows4(sK, PK, r4, 16 * db, lane));
       }
+      if constexpr (sizeof(T) == 2) {
+        // adjacent columns pair up (DPP lane swap within each lane pair): the
+        // even lane writes rows r4, r4 + 1 and the odd lane rows r4 + 2, r4 + 3,
+        // each as one 4-byte (two-column) LDS write instead of four 2-byte ones
+        const bool odd = r16 & 1;
+        const int row0 = r4 + (odd ? 2 : 0), col = d - (odd ? 1 : 0);
+        auto pair_store = [&](T* tile, const f32x4 x) {
+          const float p0 = dpp_f<0xB1>(odd ? x[0] : x[2]), p1 = dpp_f<0xB1>(odd ? x[1] : x[3]);
+          using P2 = T __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<P2*>(&tile[row0 * PK + col]) = P2{(T)(odd ? p0 : x[0]), (T)(odd ? x[2] : p0)};
+          *reinterpret_cast<P2*>(&tile[(row0 + 1) * PK + col]) = P2{(T)(odd ? p1 : x[1]), (T)(odd ? x[3] : p1)};
+        };
+        pair_store(sOq, oq);
+        pair_store(sOk, okv);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sOq[(r4 + e) * PK + d] = (T)oq[e];
-        sOk[(r4 + e) * PK + d] = (T)okv[e];
+        for (int e = 0; e < 4; ++e) {
+          sOq[(r4 + e) * PK + d] = (T)oq[e];
+          sOk[(r4 + e) * PK + d] = (T)okv[e];
+        }
       }
     }
     lds_barrier();
